@@ -1,0 +1,368 @@
+"""CPU oracle for the VSA2 attention layer -- TEST INFRASTRUCTURE ONLY.
+
+Only the tests, the smoke check and the benchmark's CPU-baseline leg may import
+this module.  The HIP library never calls it and shares no code with it.
+
+Everything is plain numpy in float64, one (batch, head) at a time, written
+from the equations of "Improving Video Sparse Attention with Fine-grained
+Router and Sparse Rebasing" (arXiv 2609.32882, §2.1-§2.2, App. B).  Where the
+paper leaves a step open, the plain reading is taken and noted at the function.
+
+Conventions shared with the library interface:
+  * tokens of one head are in cube-tiled order (§2.2 "Permutation"): the 64
+    tokens of a 4x4x4 cube are contiguous, cube-major over the cube grid;
+    inside a cube, the eight 2x2x2 sub-cubes in raster order, each holding its
+    8 tokens in raster order.  The oracle does not rely on the inner order: it
+    rebuilds every token's (t, y, x) from the grid and pools by coordinates.
+  * block size B = 64 (4x4x4), router pool R = 8 (2x2x2), G = B/R = 8.
+  * softmax scale 1/sqrt(d) unless given.
+
+Parity pins: every function here is checked in tests/test_oracle.py against
+closed forms, special cases that reduce to textbook routines (dense softmax
+attention, autograd), brute force on tiny inputs and finite differences.
+"""
+
+import numpy as np
+
+CUBE_SHAPE = (4, 4, 4)
+SUB_SHAPE = (2, 2, 2)
+
+
+# ----------------------------------------------------------------------------
+# layout
+# ----------------------------------------------------------------------------
+def token_coords(grid):
+    """(t, y, x) of every token slot in cube-tiled order, shape [L, 3].
+
+    Cube-major order over the (T/4, Y/4, X/4) cube grid (§2.2 "Permutation");
+    inside a cube the reading taken here is sub-cube-major: slot 64c + 8s + u
+    holds sub-cube s (raster over the 2x2x2 sub-cube grid of the cube) and
+    position u (raster inside the 2x2x2 sub-cube).
+    """
+    T, Y, X = grid
+    ct, cy, cx = T // 4, Y // 4, X // 4
+    coords = np.empty((T * Y * X, 3), dtype=np.int64)
+    slot = 0
+    for a in range(ct):
+        for b in range(cy):
+            for c in range(cx):
+                for st in range(2):
+                    for sy in range(2):
+                        for sx in range(2):
+                            for ut in range(2):
+                                for uy in range(2):
+                                    for ux in range(2):
+                                        coords[slot] = (4 * a + 2 * st + ut, 4 * b + 2 * sy + uy, 4 * c + 2 * sx + ux)
+                                        slot += 1
+    return coords
+
+
+def pool_groups(grid, pool):
+    """Token slots of each pooling window, ordered cube-major then window raster
+    inside the cube.  Returns int array [L / prod(pool), prod(pool)].
+
+    The windows tile every 4x4x4 cube (pool in {1,2,4}^3), so a pooled token
+    index a belongs to cube a // (64 / prod(pool)).
+    """
+    T, Y, X = grid
+    pt, py, px = pool
+    coords = token_coords(grid)
+    slot_of = np.empty((T, Y, X), dtype=np.int64)
+    slot_of[coords[:, 0], coords[:, 1], coords[:, 2]] = np.arange(T * Y * X)
+    groups = []
+    for a in range(T // 4):
+        for b in range(Y // 4):
+            for c in range(X // 4):
+                for wt in range(4 // pt):
+                    for wy in range(4 // py):
+                        for wx in range(4 // px):
+                            t0, y0, x0 = 4 * a + wt * pt, 4 * b + wy * py, 4 * c + wx * px
+                            members = slot_of[t0:t0 + pt, y0:y0 + py, x0:x0 + px].reshape(-1)
+                            groups.append(members)
+    return np.asarray(groups, dtype=np.int64)
+
+
+def mean_pool(x, grid, pool):
+    """MeanPool over windows of shape ``pool`` (Eq.(1) with the cube, Eq.(5)
+    with the router window).  x: [L, d] -> [L / prod(pool), d]."""
+    grp = pool_groups(grid, pool)
+    return x[grp].mean(axis=1)
+
+
+def round_bf16(x):
+    """Round to the nearest bfloat16 (ties to even), returned as float64."""
+    f = np.asarray(x, dtype=np.float32)
+    u = f.view(np.uint32).astype(np.uint64)
+    lsb = (u >> 16) & 1
+    u = ((u + 0x7FFF + lsb) >> 16) << 16
+    return u.astype(np.uint32).view(np.float32).astype(np.float64)
+
+
+def _softmax_rows(s):
+    m = s.max(axis=1, keepdims=True)
+    e = np.exp(s - m)
+    return e / e.sum(axis=1, keepdims=True)
+
+
+def _scale(d, scale):
+    return 1.0 / np.sqrt(d) if not scale else float(scale)
+
+
+# ----------------------------------------------------------------------------
+# router: pool - softmax - pool, Eq.(5)-(7)
+# ----------------------------------------------------------------------------
+def router_scores(q, k, grid, pool=SUB_SHAPE, scale=None, bf16_pooled=False, rows=None):
+    """Block scores P_r [nb, nb] of one head (Eq.(5)-(7)).
+
+    Eq.(5): Q_r, K_r = MeanPool_R(Q, K).  With ``bf16_pooled`` the pooled
+    operands are rounded to bf16 before the product (the precision the bf16
+    kernels work in; the paper does not state one).
+    Eq.(6): P_hat = softmax over all pooled keys of Q_r K_r^T / sqrt(d).
+    Eq.(7): P_r[i, j] = mean of the G x G entries of P_hat between cube i and
+    cube j (the paper's MeanPool_{GxG}; the sum would be G^2 times this).
+    ``rows`` restricts the output to some query cubes (rows are independent).
+    """
+    d = q.shape[1]
+    qr = mean_pool(np.asarray(q, np.float64), grid, pool)
+    kr = mean_pool(np.asarray(k, np.float64), grid, pool)
+    if bf16_pooled:
+        qr, kr = round_bf16(qr), round_bf16(kr)
+    g = 64 // (pool[0] * pool[1] * pool[2])
+    nb = qr.shape[0] // g
+    rows = np.arange(nb) if rows is None else np.asarray(rows)
+    out = np.empty((len(rows), nb))
+    for n, i in enumerate(rows):
+        s = qr[i * g:(i + 1) * g] @ kr.T * _scale(d, scale)       # [G, L/R]
+        p_hat = _softmax_rows(s)
+        out[n] = p_hat.reshape(g, nb, g).mean(axis=(0, 2))
+    return out
+
+
+def oracle_block_scores(q, k, grid, scale=None):
+    """P_oracle (Eq.(10)-(11)): token-level softmax, then the mean over each
+    (B x B) tile.  Output rows are cubes in cube-major order."""
+    d = q.shape[1]
+    p = _softmax_rows(np.asarray(q, np.float64) @ np.asarray(k, np.float64).T * _scale(d, scale))
+    nb = q.shape[0] // 64
+    return p.reshape(nb, 64, nb, 64).mean(axis=(1, 3))
+
+
+# ----------------------------------------------------------------------------
+# per-sequence TopK, Eq.(8)-(9)
+# ----------------------------------------------------------------------------
+def topk_per_sequence(scores, topk):
+    """Keep the nb*topk largest entries of the flattened nb x nb block scores of
+    one head (Eq.(8)-(9); the budget is capped at nb^2).  Ties are broken
+    toward the lower flat index i*nb + j (the paper leaves ties open).
+
+    Returns (mask [nb, nb] bool, row_ptr [nb+1], col_idx [k], col_ptr [nb+1],
+    row_idx [k]) with columns ascending in each row and rows ascending in each
+    column.
+    """
+    scores = np.asarray(scores, np.float64)
+    nb = scores.shape[0]
+    k = min(nb * topk, nb * nb)
+    flat = scores.reshape(-1)
+    order = np.lexsort((np.arange(nb * nb), -flat))     # score desc, then index asc
+    mask = np.zeros(nb * nb, dtype=bool)
+    mask[order[:k]] = True
+    mask = mask.reshape(nb, nb)
+    return (mask,) + mask_to_csr_csc(mask)
+
+
+def mask_to_csr_csc(mask):
+    nb = mask.shape[0]
+    rows, cols = np.nonzero(mask)                        # row-major: cols ascending per row
+    row_ptr = np.zeros(nb + 1, dtype=np.int64)
+    np.add.at(row_ptr, rows + 1, 1)
+    row_ptr = np.cumsum(row_ptr)
+    cols_t, rows_t = np.nonzero(mask.T)                  # column-major: rows ascending per column
+    col_ptr = np.zeros(nb + 1, dtype=np.int64)
+    np.add.at(col_ptr, cols_t + 1, 1)
+    col_ptr = np.cumsum(col_ptr)
+    return row_ptr, cols.astype(np.int64), col_ptr, rows_t.astype(np.int64)
+
+
+def csr_to_mask(row_ptr, col_idx, nb):
+    mask = np.zeros((nb, nb), dtype=bool)
+    for i in range(nb):
+        mask[i, col_idx[row_ptr[i]:row_ptr[i + 1]]] = True
+    return mask
+
+
+# ----------------------------------------------------------------------------
+# fine branch, Eq.(12)
+# ----------------------------------------------------------------------------
+def _tokens_of(cubes):
+    return (np.asarray(cubes)[:, None] * 64 + np.arange(64)[None, :]).reshape(-1)
+
+
+def fine_forward(q, k, v, mask, scale=None, rows=None):
+    """Block-sparse attention of one head (Eq.(12), with the -inf mask of §2.1
+    outside the selected (64 x 64) tiles).
+
+    Returns O_f [L, d] and the natural-log LSE [L].  A query cube with no
+    selected KV cube has O_f = 0 and LSE = -inf (the paper does not treat empty
+    rows).  ``rows`` limits the work to some query cubes; other rows are NaN.
+    """
+    q, k, v = (np.asarray(t, np.float64) for t in (q, k, v))
+    L, d = q.shape
+    nb = L // 64
+    sc = _scale(d, scale)
+    o = np.full((L, v.shape[1]), np.nan)
+    lse = np.full(L, np.nan)
+    for i in (range(nb) if rows is None else rows):
+        sl = slice(64 * i, 64 * i + 64)
+        cols = np.nonzero(mask[i])[0]
+        if len(cols) == 0:
+            o[sl], lse[sl] = 0.0, -np.inf
+            continue
+        toks = _tokens_of(cols)
+        s = q[sl] @ k[toks].T * sc
+        m = s.max(axis=1, keepdims=True)
+        e = np.exp(s - m)
+        z = e.sum(axis=1, keepdims=True)
+        o[sl] = (e / z) @ v[toks]
+        lse[sl] = (m + np.log(z))[:, 0]
+    return o, lse
+
+
+def fine_backward(q, k, v, mask, d_o, scale=None):
+    """Gradients of Eq.(12) with the mask held fixed (the router takes no
+    gradient, §2.1-§2.2).  Returns dQ, dK, dV [L, d]."""
+    q, k, v, d_o = (np.asarray(t, np.float64) for t in (q, k, v, d_o))
+    L, d = q.shape
+    nb = L // 64
+    sc = _scale(d, scale)
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    for i in range(nb):
+        cols = np.nonzero(mask[i])[0]
+        if len(cols) == 0:
+            continue
+        sl = slice(64 * i, 64 * i + 64)
+        toks = _tokens_of(cols)
+        s = q[sl] @ k[toks].T * sc
+        p = _softmax_rows(s)                       # [64, n]
+        o = p @ v[toks]
+        dp = d_o[sl] @ v[toks].T
+        ds = p * (dp - (d_o[sl] * o).sum(axis=1, keepdims=True))
+        dq[sl] += ds @ k[toks] * sc
+        dk[toks] += ds.T @ q[sl] * sc
+        dv[toks] += p.T @ d_o[sl]
+    return dq, dk, dv
+
+
+# ----------------------------------------------------------------------------
+# coarse branch, Eq.(1)-(4), and gated merge, Eq.(13)-(14)
+# ----------------------------------------------------------------------------
+def coarse_forward(q, k, v, grid, scale=None):
+    """Eq.(1)-(3): cube mean-pooling, dense softmax attention over the nb cube
+    tokens.  Returns (O_hat_c [nb, d], lse_c [nb], (q_c, k_c, v_c))."""
+    d = q.shape[1]
+    qc, kc, vc = (mean_pool(np.asarray(t, np.float64), grid, CUBE_SHAPE) for t in (q, k, v))
+    s = qc @ kc.T * _scale(d, scale)
+    m = s.max(axis=1, keepdims=True)
+    z = np.exp(s - m).sum(axis=1, keepdims=True)
+    p = np.exp(s - m) / z
+    return p @ vc, (m + np.log(z))[:, 0], (qc, kc, vc)
+
+
+def repeat_cubes(oc):
+    """Eq.(4): broadcast each cube row back to its 64 tokens (cube-tiled order)."""
+    return np.repeat(np.asarray(oc, np.float64), 64, axis=0)
+
+
+def gate(x, w_g):
+    """Eq.(13): G = tanh(X W_g), one gate per token and head.
+    x [L, Dm], w_g [Dm, H] -> [L, H]."""
+    return np.tanh(np.asarray(x, np.float64) @ np.asarray(w_g, np.float64))
+
+
+def merge(g_h, oc_hat, o_f):
+    """Eq.(14) for one head: O = G (.) Repeat(O_hat_c) + O_f."""
+    return g_h[:, None] * repeat_cubes(oc_hat) + np.asarray(o_f, np.float64)
+
+
+def coarse_gate_backward(q, k, v, grid, x, w_g, d_o, scale=None):
+    """Gradients of Eq.(1)-(4) and (13)-(14) for one batch element.
+
+    q, k, v, d_o: [H, L, d]; x [L, Dm]; w_g [Dm, H].
+    Returns (dq_c, dk_c, dv_c [H, nb, d] -- the coarse-branch gradients w.r.t.
+    the pooled tensors --, dq, dk, dv [H, L, d] of the coarse branch alone,
+    i.e. the pooled gradients spread back with weight 1/64, dx [L, Dm],
+    dw_g [Dm, H]).  dO_f = dO because Eq.(14) adds O_f with weight one.
+    """
+    H, L, d = q.shape
+    sc = _scale(d, scale)
+    g = gate(x, w_g)                                    # [L, H]
+    dpre = np.zeros_like(g)
+    dqc, dkc, dvc = [], [], []
+    for h in range(H):
+        oc_hat, lse_c, (qc, kc, vc) = coarse_forward(q[h], k[h], v[h], grid, scale)
+        oc = repeat_cubes(oc_hat)
+        doh = np.asarray(d_o[h], np.float64)
+        dg = (doh * oc).sum(axis=1)
+        dpre[:, h] = dg * (1.0 - g[:, h] ** 2)
+        doc_hat = (g[:, h, None] * doh).reshape(-1, 64, d).sum(axis=1)   # Repeat^T
+        p = np.exp(qc @ kc.T * sc - lse_c[:, None])
+        dvc.append(p.T @ doc_hat)
+        dp = doc_hat @ vc.T
+        ds = p * (dp - (doc_hat * oc_hat).sum(axis=1, keepdims=True))
+        dqc.append(ds @ kc * sc)
+        dkc.append(ds.T @ qc * sc)
+    dqc, dkc, dvc = np.stack(dqc), np.stack(dkc), np.stack(dvc)
+    spread = lambda t: np.repeat(t, 64, axis=1) / 64.0                  # MeanPool^T
+    dx = dpre @ np.asarray(w_g, np.float64).T
+    dw = np.asarray(x, np.float64).T @ dpre
+    return dqc, dkc, dvc, spread(dqc), spread(dkc), spread(dvc), dx, dw
+
+
+# ----------------------------------------------------------------------------
+# the whole layer
+# ----------------------------------------------------------------------------
+def vsa2_forward(q, k, v, grid, topk, x, w_g, scale=None, bf16_pooled=False, mask=None):
+    """One batch element, all heads: router -> TopK -> fine + coarse -> merge.
+
+    q, k, v: [H, L, d]; x [L, Dm]; w_g [Dm, H].  ``mask`` [H, nb, nb] skips the
+    router and uses a given selection.  Returns a dict of every intermediate.
+    """
+    H = q.shape[0]
+    g = gate(x, w_g)
+    res = {"scores": [], "mask": [], "o_f": [], "lse": [], "oc_hat": [], "lse_c": [], "o": [], "g": g}
+    for h in range(H):
+        if mask is None:
+            p_r = router_scores(q[h], k[h], grid, scale=scale, bf16_pooled=bf16_pooled)
+            m = topk_per_sequence(p_r, topk)[0]
+            res["scores"].append(p_r)
+        else:
+            m = mask[h]
+        o_f, lse = fine_forward(q[h], k[h], v[h], m, scale)
+        oc_hat, lse_c, _ = coarse_forward(q[h], k[h], v[h], grid, scale)
+        res["mask"].append(m)
+        res["o_f"].append(o_f)
+        res["lse"].append(lse)
+        res["oc_hat"].append(oc_hat)
+        res["lse_c"].append(lse_c)
+        res["o"].append(merge(g[:, h], oc_hat, o_f))
+    return {n: (np.stack(t) if isinstance(t, list) and t else t) for n, t in res.items()}
+
+
+def vsa2_backward(q, k, v, grid, mask, x, w_g, d_o, scale=None):
+    """Gradients of the whole layer (router excluded) for one batch element.
+    Returns dq, dk, dv [H, L, d], dx [L, Dm], dw_g [Dm, H]."""
+    H = q.shape[0]
+    dq, dk, dv = [], [], []
+    for h in range(H):
+        a, b, c = fine_backward(q[h], k[h], v[h], mask[h], d_o[h], scale)
+        dq.append(a); dk.append(b); dv.append(c)
+    _, _, _, cq, ck, cv, dx, dw = coarse_gate_backward(q, k, v, grid, x, w_g, d_o, scale)
+    return np.stack(dq) + cq, np.stack(dk) + ck, np.stack(dv) + cv, dx, dw
+
+
+# ----------------------------------------------------------------------------
+# cost model, App. B Eq.(15)-(16)
+# ----------------------------------------------------------------------------
+def sparsity(L, block, pool, topk):
+    """Eq.(16): sparsity ~= 1 - (1/R^2 + K*B/L) (router two GEMMs + fine branch;
+    coarse branch omitted as in App. B)."""
+    return 1.0 - (1.0 / pool ** 2 + topk * block / L)

@@ -1,0 +1,85 @@
+"""Workload registry: the five video-shaped VSA2 problems.
+
+Grids are (T, Y, X) latent cells; tokens L = T*Y*X are stored in cube-tiled
+order (4x4x4 cubes of 64 tokens, each made of eight 2x2x2 sub-cubes of 8
+tokens).  ``topk`` is the average number of KV cubes per query cube, so the
+per-head budget is nb * topk selected (query cube, KV cube) pairs
+(paper "Improving Video Sparse Attention with Fine-grained Router and Sparse
+Rebasing", §2.2 Eq.(8)-(9)).
+"""
+
+from dataclasses import dataclass, field
+
+CUBE = 64          # tokens per 4x4x4 cube (block size of the block-sparse attention)
+SUB = 8            # tokens per 2x2x2 router pooling sub-cube
+G = CUBE // SUB    # pooled tokens per cube
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    cfg_id: int
+    grid: tuple            # (T, Y, X)
+    batch: int
+    heads: int
+    head_dim: int
+    dtype: str             # "f32" or "bf16"
+    topk: int
+    gen: str               # "sinusoid" or "lowrank"
+    alpha: float = 0.5     # weight of the structured component
+    skew: bool = False     # heavy-tailed per-query-cube scale
+    train: bool = False    # forward + backward
+    extra_topk: tuple = field(default_factory=tuple)
+
+    @property
+    def L(self):
+        t, y, x = self.grid
+        return t * y * x
+
+    @property
+    def nb(self):
+        return self.L // CUBE
+
+    @property
+    def d_model(self):
+        return self.heads * self.head_dim
+
+    def budget(self, topk=None):
+        k = self.topk if topk is None else topk
+        return min(self.nb * k, self.nb * self.nb)
+
+
+WORKLOADS = {
+    w.name: w
+    for w in [
+        Workload("tiny", 1, (8, 16, 16), 1, 2, 64, "f32", 8, "sinusoid", alpha=1.0),
+        Workload("short", 2, (16, 32, 64), 1, 20, 128, "bf16", 64, "lowrank"),
+        Workload("train480", 3, (28, 32, 52), 1, 20, 128, "bf16", 64, "lowrank", train=True),
+        Workload("infer720", 4, (44, 48, 104), 1, 20, 128, "bf16", 64, "lowrank", extra_topk=(128,)),
+        Workload("train720", 5, (44, 48, 104), 1, 20, 128, "bf16", 64, "lowrank", skew=True, train=True),
+    ]
+}
+
+
+def flops(w: Workload, topk=None):
+    """Algorithmic FLOPs of one call of each op, counting selected blocks only.
+
+    Fine branch: 4 * 64^2 * d per selected pair forward (QK^T and PV), 2.5x that
+    backward (five 64x64xd GEMMs).  Router: two pooled GEMMs (LSE pass and score
+    pass), each 2 * (L/8)^2 * d, as in the paper's App. B cost model.  Coarse:
+    dense attention over nb pooled tokens, 4 * nb^2 * d forward.
+    """
+    k = w.budget(topk)
+    bh = w.batch * w.heads
+    d = w.head_dim
+    lr = w.L // SUB
+    pair = 4 * CUBE * CUBE * d
+    return {
+        "fine_fwd": bh * k * pair,
+        "fine_bwd": bh * k * pair * 5 // 2,
+        "router": bh * 2 * 2 * lr * lr * d,
+        "coarse_fwd": bh * 4 * w.nb * w.nb * d,
+        "coarse_bwd": bh * 10 * w.nb * w.nb * d,
+        "gate_fwd": 2 * w.batch * w.L * w.d_model * w.heads,
+        "gate_bwd": 4 * w.batch * w.L * w.d_model * w.heads,
+    }
