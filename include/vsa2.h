@@ -1,0 +1,189 @@
+/* vsa2.h -- C interface of the VSA2 sparse-attention layer for MI355X (gfx950).
+ *
+ * The method is the attention layer of "Improving Video Sparse Attention with
+ * Fine-grained Router and Sparse Rebasing" (arXiv 2609.32882): a fine-grained
+ * router (§2.2 Eq.(5)-(7)), a per-sequence TopK (Eq.(8)-(9)), a block-sparse
+ * fine branch (Eq.(12)), a cube-pooled coarse branch (Eq.(1)-(4)) and a tanh
+ * gate (Eq.(13)-(14)); the router takes no gradient (§2.1).
+ *
+ * Conventions (all entry points):
+ *  - Every tensor argument is DEVICE memory owned by the caller, contiguous,
+ *    row-major, 16-byte aligned.  The library never allocates or frees; the
+ *    scratch it needs comes from a caller workspace `ws` of at least the size
+ *    vsa2_workspace_size() reports (its contents need not be initialised).
+ *  - Q, K, V, O_f, O, dO, dQ, dK, dV are [batch, heads, L, head_dim] in the
+ *    storage dtype of vsa2_problem.dtype, tokens in cube-tiled order (§2.2
+ *    "Permutation"): the 64 tokens of each 4x4x4 cube are contiguous (cubes in
+ *    raster order over the (T/4, Y/4, X/4) cube grid); inside a cube the eight
+ *    2x2x2 sub-cubes follow in raster order, each holding its 8 tokens in
+ *    raster order.  Router pooling windows are therefore the contiguous groups
+ *    of 8 tokens and the attention blocks the contiguous groups of 64.
+ *  - Block size B = 64 (4x4x4) and router pool R = 8 (2x2x2), so G = 8.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Every call only
+ *    enqueues work on it and returns without synchronising.
+ *  - Errors: argument and shape errors are reported before anything is
+ *    enqueued and leave outputs untouched (VSA2_E_ARG / VSA2_E_SHAPE /
+ *    VSA2_E_WORKSPACE / VSA2_E_UNSUPPORTED); a failed kernel launch returns
+ *    VSA2_E_HIP.  Numerical outputs are bitwise deterministic for identical
+ *    inputs on the same device (no floating-point atomics).
+ */
+#ifndef VSA2_H
+#define VSA2_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum vsa2_status {
+  VSA2_OK = 0,
+  VSA2_E_ARG = 1,         /* NULL pointer, misaligned pointer, bad scalar argument   */
+  VSA2_E_SHAPE = 2,       /* grid not a multiple of 4, head_dim not 64/128, sizes    */
+  VSA2_E_WORKSPACE = 3,   /* workspace smaller than vsa2_workspace_size() reports     */
+  VSA2_E_HIP = 4,         /* a HIP call or kernel launch failed                       */
+  VSA2_E_UNSUPPORTED = 5  /* valid request this build does not implement              */
+};
+
+enum vsa2_dtype { VSA2_F32 = 0, VSA2_BF16 = 1 };
+
+/* Operations, for vsa2_workspace_size(). */
+enum vsa2_op {
+  VSA2_OP_POOL = 0,
+  VSA2_OP_ROUTE = 1,
+  VSA2_OP_TOPK = 2,
+  VSA2_OP_PLAN = 3,
+  VSA2_OP_FWD = 4,
+  VSA2_OP_BWD = 5,
+  VSA2_OP_COARSE = 6,
+  VSA2_OP_COARSE_BWD = 7
+};
+
+typedef struct vsa2_problem {
+  int32_t batch;          /* >= 1                                                     */
+  int32_t heads;          /* >= 1 (multi-head attention: as many K/V heads as Q heads)*/
+  int32_t head_dim;       /* d: 64 or 128                                             */
+  int32_t lat_t, lat_y, lat_x; /* latent grid; L = lat_t*lat_y*lat_x; each a multiple of 4 */
+  int32_t dtype;          /* vsa2_dtype of Q, K, V, O_f, O, dO, dQ, dK, dV, X, dX     */
+  float softmax_scale;    /* <= 0 selects 1/sqrt(head_dim)                            */
+} vsa2_problem;
+
+/* Human-readable name of a status code (static string). */
+const char* vsa2_status_string(int status);
+
+/* Bytes of workspace `op` needs for problem `p` (topk: average KV cubes per
+ * query cube; d_model: width of X for the coarse/gate ops, else ignored).
+ * Pure host computation; enqueues nothing. */
+int vsa2_workspace_size(const vsa2_problem* p, int32_t op, int32_t topk, int32_t d_model, size_t* bytes);
+
+/* Bytes of the `pooled` buffer written by vsa2_pool (see there). */
+int vsa2_pooled_size(const vsa2_problem* p, size_t* bytes);
+
+/* Bytes of the `saved` buffer written by vsa2_coarse_gate (see there). */
+int vsa2_saved_size(const vsa2_problem* p, size_t* bytes);
+
+/* Per-sequence budget k = min(nb * topk, nb^2) selected pairs per (batch, head),
+ * nb = L / 64 (paper §2.2 Eq.(9): N*K blocks per sequence). */
+int vsa2_budget(const vsa2_problem* p, int32_t topk, int64_t* k);
+
+/* Mean pooling of the router (Eq.(5), windows of 8 tokens) and of the coarse
+ * branch (Eq.(1), cubes of 64 tokens), one read of Q, K, V.
+ *   pooled (written), in order, each [batch, heads, rows, d] in the storage dtype:
+ *     Q_r, K_r    rows = L/8   (router operands; bf16 storage rounds the fp32 mean
+ *                               to nearest-even, the router's stated precision)
+ *     Q_c, K_c, V_c rows = nbp = nb rounded up to a multiple of 64; rows >= nb are 0
+ *   Size from vsa2_pooled_size(). */
+int vsa2_pool(const vsa2_problem* p, const void* q, const void* k, const void* v,
+              void* pooled, void* stream);
+
+/* Fine-grained router, Eq.(6)-(7), fused: two passes over the pooled keys
+ * (log-sum-exp, then softmax + G x G mean pooling), P_hat_r never stored.
+ *   pooled: from vsa2_pool.
+ *   scores (written): fp32 [batch, heads, nb, nb], P_r[i][j] = mean over the
+ *     8 x 8 pooled (query, key) pairs of cubes i, j of softmax_b(q_a.k_b*scale).
+ *     Every row sums to 1/8.
+ *   ws: vsa2_workspace_size(VSA2_OP_ROUTE). */
+int vsa2_route(const vsa2_problem* p, const void* pooled, float* scores,
+               void* ws, size_t ws_bytes, void* stream);
+
+/* Per-sequence TopK, Eq.(8)-(9): for every (batch, head) keep the k largest of
+ * the nb*nb block scores (k from vsa2_budget; ties at the cut-off go to the
+ * lower flat index i*nb + j).  Exact radix select on the fp32 bit patterns.
+ *   scores: fp32 [batch, heads, nb, nb], finite and >= 0.
+ *   row_ptr (written) int32 [batch, heads, nb+1]; col_idx (written) int32
+ *     [batch, heads, k]: selected KV cubes of query cube i are
+ *     col_idx[row_ptr[i] .. row_ptr[i+1]), ascending.  row_ptr[nb] = k.
+ *   col_ptr, row_idx (written): the same selection by KV cube (CSC), query
+ *     cubes ascending; used by the backward pass.
+ *   ws: vsa2_workspace_size(VSA2_OP_TOPK). */
+int vsa2_topk_per_seq(const vsa2_problem* p, const float* scores, int32_t topk,
+                      int32_t* row_ptr, int32_t* col_idx, int32_t* col_ptr, int32_t* row_idx,
+                      void* ws, size_t ws_bytes, void* stream);
+
+/* CSC form (col_ptr, row_idx) of a caller-chosen selection given as CSR
+ * (row_ptr, col_idx, same layout as vsa2_topk_per_seq, exactly k entries per
+ * (batch, head), columns ascending and distinct in each row).
+ *   ws: vsa2_workspace_size(VSA2_OP_PLAN). */
+int vsa2_plan_from_csr(const vsa2_problem* p, int32_t topk, const int32_t* row_ptr, const int32_t* col_idx,
+                       int32_t* col_ptr, int32_t* row_idx, void* ws, size_t ws_bytes, void* stream);
+
+/* Fine branch forward, Eq.(12): block-sparse attention of every query cube
+ * over its selected KV cubes only (-inf mask elsewhere, §2.1).
+ *   row_ptr, col_idx: the selection (CSR as above, k = vsa2_budget(topk)).
+ *   o_f (written): storage dtype [batch, heads, L, d].
+ *   lse (written): fp32 [batch, heads, L], natural-log log-sum-exp of the scaled
+ *     scores of each query over its selected keys (kept for the backward).
+ *   A query cube with no selected KV cube gets o_f = 0 and lse = -inf.
+ *   ws: vsa2_workspace_size(VSA2_OP_FWD). */
+int vsa2_sparse_attn_fwd(const vsa2_problem* p, int32_t topk, const void* q, const void* k, const void* v,
+                         const int32_t* row_ptr, const int32_t* col_idx, void* o_f, float* lse,
+                         void* ws, size_t ws_bytes, void* stream);
+
+/* Fine branch backward with the selection held fixed (the router takes no
+ * gradient, §2.1-§2.2), plus the coarse-branch gradients spread back to the
+ * tokens.
+ *   q, k, v, o_f, lse: as in / out of vsa2_sparse_attn_fwd; d_o = dL/dO (the
+ *     gate adds O_f with weight one, Eq.(14), so dL/dO_f = dL/dO).
+ *   row_ptr, col_idx, col_ptr, row_idx: the selection in CSR and CSC form.
+ *   dqkv_c: fp32 [3, batch, heads, nb, d] gradients w.r.t. the pooled Q_c, K_c,
+ *     V_c (from vsa2_coarse_gate_bwd) or NULL; each token of cube c receives
+ *     1/64 of row c (the adjoint of the mean pooling).
+ *   dq, dk, dv (written, overwritten): storage dtype [batch, heads, L, d].
+ *   dK and dV are accumulated per KV cube over its query list in a fixed order
+ *   (no atomics), so results are bitwise reproducible.
+ *   ws: vsa2_workspace_size(VSA2_OP_BWD). */
+int vsa2_sparse_attn_bwd(const vsa2_problem* p, int32_t topk, const void* q, const void* k, const void* v,
+                         const void* o_f, const float* lse, const void* d_o,
+                         const int32_t* row_ptr, const int32_t* col_idx,
+                         const int32_t* col_ptr, const int32_t* row_idx, const float* dqkv_c,
+                         void* dq, void* dk, void* dv, void* ws, size_t ws_bytes, void* stream);
+
+/* Coarse branch, Eq.(1)-(4), and gated merge, Eq.(13)-(14).
+ *   pooled: from vsa2_pool.  x: storage dtype [batch, L, d_model] hidden states
+ *   in the same token order.  w_g: fp32 [d_model, heads], one gate column per
+ *   head (zero at initialisation gives O = O_f).  o_f: fine-branch output.
+ *   o (written): storage dtype [batch, heads, L, d], O = tanh(X W_g) * O_c + O_f.
+ *   saved (written, fp32, for the backward; size vsa2_saved_size):
+ *     O_hat_c [batch, heads, nb, d] | lse_c [batch, heads, nb] | G [batch, heads, L]
+ *   ws: vsa2_workspace_size(VSA2_OP_COARSE, d_model). */
+int vsa2_coarse_gate(const vsa2_problem* p, const void* pooled, const void* x, int32_t d_model,
+                     const float* w_g, const void* o_f, void* o, float* saved,
+                     void* ws, size_t ws_bytes, void* stream);
+
+/* Backward of vsa2_coarse_gate.
+ *   d_o: dL/dO.  saved: as written by vsa2_coarse_gate for the same inputs.
+ *   dqkv_c (written): fp32 [3, batch, heads, nb, d], gradients w.r.t. Q_c, K_c, V_c
+ *     (pass it to vsa2_sparse_attn_bwd).
+ *   dx (written): storage dtype [batch, L, d_model]; dw_g (written): fp32
+ *     [d_model, heads], reduced over tokens in a fixed order.
+ *   ws: vsa2_workspace_size(VSA2_OP_COARSE_BWD, d_model). */
+int vsa2_coarse_gate_bwd(const vsa2_problem* p, const void* pooled, const void* x, int32_t d_model,
+                         const float* w_g, const float* saved, const void* d_o,
+                         float* dqkv_c, void* dx, float* dw_g, void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VSA2_H */

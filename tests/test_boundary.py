@@ -1,0 +1,106 @@
+"""The C-ABI library loads, exports every entry point of include/vsa2.h and
+rejects bad arguments before touching the GPU (host logic only, runs on CPU)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from video_dit_trainable_amd import vsa2
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "vsa2.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(vsa2.LIB_PATH), reason="libvsa2.so not built")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(vsa2_[a-z0-9_]+)\s*\(", text)))
+
+
+def _prob(**kw):
+    base = dict(batch=1, heads=2, head_dim=64, grid=(8, 16, 16), dtype="f32")
+    base.update(kw)
+    return vsa2.problem(base["batch"], base["heads"], base["head_dim"], base["grid"], base["dtype"])
+
+
+def test_every_declared_symbol_is_exported():
+    names = _declared()
+    assert len(names) >= 12
+    h = ctypes.CDLL(vsa2.LIB_PATH)
+    for n in names:
+        assert hasattr(h, n), n
+    assert set(names) <= set(vsa2._SIGS), "binding misses a declared entry point"
+
+
+def test_status_strings():
+    L = vsa2.lib()
+    for code in range(6):
+        assert L.vsa2_status_string(code)
+    assert b"unknown" in L.vsa2_status_string(99)
+
+
+def test_sizes_and_budget():
+    p = _prob()
+    assert vsa2.budget(p, 8) == 32 * 8
+    assert vsa2.budget(p, 100) == 32 * 32           # capped at nb^2
+    L, nb, nbp = 2048, 32, 64
+    assert vsa2.pooled_size(p) == 2 * (2 * (L // 8) + 3 * nbp) * 64 * 4
+    assert vsa2.saved_size(p) == (2 * nb * 64 + 2 * nb + 2 * L) * 4
+    assert vsa2.workspace_size(p, vsa2.OP_ROUTE) >= 2 * (L // 8) * 4
+    assert vsa2.workspace_size(p, vsa2.OP_FWD) == 0
+    assert vsa2.workspace_size(p, vsa2.OP_COARSE_BWD, 8, 128) > 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(head_dim=96), vsa2.VSA2_E_SHAPE),
+    (dict(grid=(6, 16, 16)), vsa2.VSA2_E_SHAPE),
+    (dict(grid=(8, 16, 0)), vsa2.VSA2_E_SHAPE),
+    (dict(batch=0), vsa2.VSA2_E_SHAPE),
+])
+def test_bad_problem_rejected(kw, code):
+    with pytest.raises(vsa2.Vsa2Error) as e:
+        vsa2.workspace_size(_prob(**kw), vsa2.OP_TOPK)
+    assert e.value.code == code
+
+
+def test_bad_dtype_and_null_problem():
+    p = _prob()
+    p.dtype = 7
+    out = ctypes.c_size_t()
+    assert vsa2.lib().vsa2_workspace_size(ctypes.byref(p), 1, 1, 0, ctypes.byref(out)) == vsa2.VSA2_E_ARG
+    assert vsa2.lib().vsa2_workspace_size(None, 1, 1, 0, ctypes.byref(out)) == vsa2.VSA2_E_ARG
+
+
+# Fake, never-dereferenced addresses: every call below must fail validation
+# before any kernel is enqueued.
+A, B, C, D = 0x10000, 0x20000, 0x30000, 0x40000
+
+
+def test_null_and_misaligned_pointers():
+    L, p = vsa2.lib(), _prob()
+    assert L.vsa2_pool(ctypes.byref(p), A, B, None, D, None) == vsa2.VSA2_E_ARG
+    assert L.vsa2_pool(ctypes.byref(p), A + 4, B, C, D, None) == vsa2.VSA2_E_ARG
+    assert L.vsa2_route(ctypes.byref(p), None, B, C, 1 << 30, None) == vsa2.VSA2_E_ARG
+
+
+def test_workspace_checks():
+    L, p = vsa2.lib(), _prob()
+    need = vsa2.workspace_size(p, vsa2.OP_ROUTE)
+    assert L.vsa2_route(ctypes.byref(p), A, B, C, need - 1, None) == vsa2.VSA2_E_WORKSPACE
+    assert L.vsa2_route(ctypes.byref(p), A, B, None, need, None) == vsa2.VSA2_E_WORKSPACE
+    assert L.vsa2_route(ctypes.byref(p), A, B, C + 16, need, None) == vsa2.VSA2_E_ARG   # ws not 256-aligned
+    need = vsa2.workspace_size(p, vsa2.OP_TOPK)
+    assert L.vsa2_topk_per_seq(ctypes.byref(p), A, 8, B, C, D, A, B, need - 256, None) == vsa2.VSA2_E_WORKSPACE
+
+
+def test_scalar_arguments():
+    L, p = vsa2.lib(), _prob()
+    assert L.vsa2_topk_per_seq(ctypes.byref(p), A, 0, B, C, D, A, B, 1 << 30, None) == vsa2.VSA2_E_ARG
+    assert L.vsa2_sparse_attn_fwd(ctypes.byref(p), 0, A, B, C, D, A, B, C, None, 0, None) == vsa2.VSA2_E_ARG
+    assert L.vsa2_coarse_gate(ctypes.byref(p), A, B, 100, C, D, A, B, C, 1 << 30, None) == vsa2.VSA2_E_SHAPE
+    many = _prob(heads=65)
+    assert L.vsa2_coarse_gate(ctypes.byref(many), A, B, 128, C, D, A, B, C, 1 << 30, None) == vsa2.VSA2_E_UNSUPPORTED

@@ -1,0 +1,289 @@
+"""GPU (HIP, gfx950) vs CPU oracle parity through the C-ABI library.
+
+Tolerances: fp32 storage within 1e-4 (max-abs and rel-L2); bf16 outputs
+within max-abs 2e-2 and rel-L2 1e-2; gradients within rel-L2 2e-2; selected
+index sets exact outside a relative 1e-3 band around the oracle's cut-off
+score, with the count exact.  Output parity runs on the oracle's own
+selection, fed to the GPU through vsa2_plan_from_csr.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import gpu_util as gu
+from oracle import vsa2_oracle as orc
+from video_dit_trainable_amd import vsa2
+from video_dit_trainable_amd.configs import WORKLOADS, Workload
+from video_dit_trainable_amd.inputs import make_gate_inputs, make_grad_out, make_qkv, make_selection
+
+pytestmark = pytest.mark.gpu
+
+TINY = WORKLOADS["tiny"]
+SHORT = WORKLOADS["short"]
+TINY_TRAIN = Workload("tiny-train", 11, (8, 16, 16), 1, 2, 64, "f32", 8, "sinusoid", alpha=1.0, train=True)
+MID = Workload("mid", 12, (8, 16, 32), 1, 4, 128, "bf16", 8, "lowrank", train=True)          # nb = 64
+RAGGED = Workload("ragged", 13, (4, 8, 20), 1, 3, 64, "bf16", 3, "lowrank", train=True)      # nb = 10
+RAGGED32 = Workload("ragged32", 14, (4, 12, 20), 1, 2, 128, "f32", 5, "lowrank", skew=True, train=True)  # nb = 15
+SMALL = [TINY_TRAIN, MID, RAGGED, RAGGED32]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    vsa2.lib()
+
+
+def _dev():
+    return torch.device("cuda:0")
+
+
+def _setup(w, zero_gate=False, heads=None):
+    q, k, v = make_qkv(w)
+    x, w_g = make_gate_inputs(w, zero_gate=zero_gate)
+    p = vsa2.problem(w.batch, w.heads, w.head_dim, w.grid, w.dtype)
+    layer = vsa2.Layer(p, w.topk, w.d_model, device=_dev())
+    dev = [t.to(_dev()) for t in (q, k, v, x, w_g)]
+    return (q, k, v, x, w_g), dev, layer
+
+
+def _oracle_masks(w, q, k, heads):
+    bf = w.dtype == "bf16"
+    scores = np.stack([orc.router_scores(gu.f64(q[0, h]), gu.f64(k[0, h]), w.grid, bf16_pooled=bf) for h in heads])
+    masks = np.stack([orc.topk_per_sequence(s, w.topk)[0] for s in scores])
+    return scores, masks
+
+
+def _close(w, got, want, what):
+    if w.dtype == "f32":
+        gu.assert_close_f32(got, want, what)
+    else:
+        gu.assert_close_bf16(got, want, what)
+
+
+# ----------------------------------------------------------------------------- pooling
+@pytest.mark.parametrize("w", [TINY, MID, RAGGED], ids=lambda w: w.name)
+def test_pool(w):
+    (q, k, v, x, w_g), (qd, kd, vd, xd, wd), layer = _setup(w)
+    vsa2.vsa2_pool(layer.p, qd, kd, vd, layer.pooled)
+    torch.cuda.synchronize()
+    qr, kr, qc, kc, vc = layer.pooled_views()
+    rnd = orc.round_bf16 if w.dtype == "bf16" else (lambda a: a)
+    for h in range(w.heads):
+        for src, gr, gc in ((q, qr, qc), (k, kr, kc), (v, None, vc)):
+            a = gu.f64(src[0, h])
+            if gr is not None:
+                want = rnd(orc.mean_pool(a, w.grid, (2, 2, 2)))
+                np.testing.assert_allclose(gu.f64(gr[0, h]), want, rtol=8e-3 if w.dtype == "bf16" else 1e-6, atol=1e-6)
+            want = rnd(orc.mean_pool(a, w.grid, (4, 4, 4)))
+            got = gu.f64(gc[0, h])
+            np.testing.assert_allclose(got[: w.nb], want, rtol=8e-3 if w.dtype == "bf16" else 1e-6, atol=1e-6)
+            assert np.all(got[w.nb:] == 0)
+
+
+# ----------------------------------------------------------------------------- router
+@pytest.mark.parametrize("w", [TINY, MID, RAGGED, RAGGED32], ids=lambda w: w.name)
+def test_router_scores(w):
+    (q, k, v, x, w_g), (qd, kd, vd, xd, wd), layer = _setup(w)
+    vsa2.vsa2_pool(layer.p, qd, kd, vd, layer.pooled)
+    vsa2.vsa2_route(layer.p, layer.pooled, layer.scores, layer.ws)
+    torch.cuda.synchronize()
+    got = gu.f64(layer.scores[0])
+    np.testing.assert_allclose(got.sum(axis=2), 1.0 / 8.0, rtol=2e-5)       # Eq.(7) rows sum to 1/G
+    for h in range(w.heads):
+        want = orc.router_scores(gu.f64(q[0, h]), gu.f64(k[0, h]), w.grid, bf16_pooled=w.dtype == "bf16")
+        np.testing.assert_allclose(got[h], want, rtol=1e-4, atol=1e-4 * want.mean())
+
+
+# ----------------------------------------------------------------------------- topk
+def _topk_on(scores_np, topk, grid_nb):
+    """GPU TopK on given scores [H, nb, nb] (generator-made, same for both)."""
+    H, nb, _ = scores_np.shape
+    T = 4
+    Y = 4
+    X = 4 * nb
+    p = vsa2.problem(1, H, 64, (T, Y, X), "f32")
+    assert p.lat_t * p.lat_y * p.lat_x // 64 == nb
+    k = vsa2.budget(p, topk)
+    dev = _dev()
+    s = torch.tensor(scores_np, dtype=torch.float32, device=dev)[None].contiguous()
+    rp = torch.empty((1, H, nb + 1), dtype=torch.int32, device=dev)
+    ci = torch.empty((1, H, k), dtype=torch.int32, device=dev)
+    cp = torch.empty_like(rp)
+    ri = torch.empty_like(ci)
+    ws = torch.empty(vsa2.workspace_size(p, vsa2.OP_TOPK), dtype=torch.uint8, device=dev)
+    vsa2.vsa2_topk_per_seq(p, s, topk, rp, ci, cp, ri, ws)
+    torch.cuda.synchronize()
+    return rp[0], ci[0], cp[0], ri[0], k
+
+
+@pytest.mark.parametrize("nb,topk,levels", [(32, 8, 5), (64, 3, 3), (10, 4, 2), (200, 17, 7), (15, 15, 4),
+                                           (33, 40, 3), (130, 1, 1000)])
+def test_topk_exact_with_ties(nb, topk, levels):
+    rng = np.random.default_rng(nb * 1000 + topk)
+    H = 3
+    scores = rng.integers(0, levels, size=(H, nb, nb)).astype(np.float32) / np.float32(levels)
+    scores[0, :, :3] = 0.0                               # exact zeros take part
+    rp, ci, cp, ri, k = _topk_on(scores, topk, nb)
+    gu.check_csr_csc(rp, ci, cp, ri, nb, k)
+    got = gu.masks_from_csr(rp, ci, nb)
+    for h in range(H):
+        want = orc.topk_per_sequence(scores[h].astype(np.float64), topk)[0]
+        assert np.array_equal(got[h], want), f"head {h}: {np.sum(got[h] != want)} mismatches"
+
+
+def test_topk_distinct_scores_large():
+    rng = np.random.default_rng(7)
+    nb, topk = 728, 64
+    scores = rng.random((2, nb, nb), dtype=np.float32) ** 4
+    rp, ci, cp, ri, k = _topk_on(scores, topk, nb)
+    gu.check_csr_csc(rp, ci, cp, ri, nb, k)
+    got = gu.masks_from_csr(rp, ci, nb)
+    for h in range(2):
+        assert np.array_equal(got[h], orc.topk_per_sequence(scores[h].astype(np.float64), topk)[0])
+
+
+@pytest.mark.parametrize("w", [TINY, MID, RAGGED32], ids=lambda w: w.name)
+def test_route_and_topk_selection(w):
+    (q, k, v, x, w_g), (qd, kd, vd, xd, wd), layer = _setup(w)
+    vsa2.vsa2_pool(layer.p, qd, kd, vd, layer.pooled)
+    vsa2.vsa2_route(layer.p, layer.pooled, layer.scores, layer.ws)
+    vsa2.vsa2_topk_per_seq(layer.p, layer.scores, w.topk, layer.row_ptr, layer.col_idx, layer.col_ptr,
+                           layer.row_idx, layer.ws)
+    torch.cuda.synchronize()
+    gu.check_csr_csc(layer.row_ptr[0], layer.col_idx[0], layer.col_ptr[0], layer.row_idx[0], w.nb, layer.k)
+    got = gu.masks_from_csr(layer.row_ptr[0], layer.col_idx[0], w.nb)
+    scores, _ = _oracle_masks(w, q, k, range(w.heads))
+    for h in range(w.heads):
+        outside, band, inside = gu.band_compare(got[h], scores[h], layer.k)
+        assert outside == 0, f"head {h}: {outside} selection mismatches outside the 1e-3 band ({band} contested)"
+
+
+# ----------------------------------------------------------------------------- fine forward
+@pytest.mark.parametrize("w", [TINY, MID, RAGGED, RAGGED32], ids=lambda w: w.name)
+def test_fine_forward(w):
+    (q, k, v, x, w_g), (qd, kd, vd, xd, wd), layer = _setup(w)
+    _, masks = _oracle_masks(w, q, k, range(w.heads))
+    masks[0] = gu.empty_rows(masks[0], [1, w.nb - 1])      # empty query rows, budget kept exact
+    assert masks[0].sum() == layer.k
+    layer.set_selection(*gu.csr_tensors(masks, _dev()))
+    vsa2.vsa2_sparse_attn_fwd(layer.p, w.topk, qd, kd, vd, layer.row_ptr, layer.col_idx, layer.o_f, layer.lse)
+    torch.cuda.synchronize()
+    for h in range(w.heads):
+        o, lse = orc.fine_forward(gu.f64(q[0, h]), gu.f64(k[0, h]), gu.f64(v[0, h]), masks[h])
+        _close(w, gu.f64(layer.o_f[0, h]), o, f"O_f head {h}")
+        live = np.isfinite(lse)
+        got_lse = gu.f64(layer.lse[0, h])
+        assert np.all(np.isneginf(got_lse[~live]))
+        np.testing.assert_allclose(got_lse[live], lse[live], atol=1e-4 if w.dtype == "f32" else 1e-3)
+        assert np.all(gu.f64(layer.o_f[0, h])[~live] == 0)
+
+
+def test_fine_forward_full_budget_is_dense_attention():
+    w = Workload("full", 15, (4, 8, 16), 1, 2, 128, "bf16", 8, "lowrank")     # nb = 8, topk = nb
+    (q, k, v, x, w_g), (qd, kd, vd, xd, wd), layer = _setup(w)
+    vsa2.vsa2_pool(layer.p, qd, kd, vd, layer.pooled)
+    vsa2.vsa2_route(layer.p, layer.pooled, layer.scores, layer.ws)
+    vsa2.vsa2_topk_per_seq(layer.p, layer.scores, w.topk, layer.row_ptr, layer.col_idx, layer.col_ptr,
+                           layer.row_idx, layer.ws)
+    vsa2.vsa2_sparse_attn_fwd(layer.p, w.topk, qd, kd, vd, layer.row_ptr, layer.col_idx, layer.o_f, layer.lse)
+    torch.cuda.synchronize()
+    assert gu.masks_from_csr(layer.row_ptr[0], layer.col_idx[0], w.nb).all()
+    for h in range(w.heads):
+        want = torch.nn.functional.scaled_dot_product_attention(
+            torch.tensor(gu.f64(q[0, h]))[None], torch.tensor(gu.f64(k[0, h]))[None],
+            torch.tensor(gu.f64(v[0, h]))[None])[0].numpy()
+        gu.assert_close_bf16(gu.f64(layer.o_f[0, h]), want, f"dense O head {h}")
+
+
+# ----------------------------------------------------------------------------- coarse + gate
+@pytest.mark.parametrize("zero_gate", [True, False])
+@pytest.mark.parametrize("w", [TINY, MID, RAGGED, RAGGED32], ids=lambda w: w.name)
+def test_coarse_gate(w, zero_gate):
+    (q, k, v, x, w_g), (qd, kd, vd, xd, wd), layer = _setup(w, zero_gate=zero_gate)
+    masks = gu.masks_from_csr(*[t.view(w.heads, -1) for t in make_selection(w)], w.nb)
+    layer.set_selection(*gu.csr_tensors(masks, _dev()))
+    o = layer.forward(qd, kd, vd, xd, wd, route=False)
+    torch.cuda.synchronize()
+    oc_hat, lse_c, g = layer.saved_views()
+    gate = orc.gate(gu.f64(x[0]), gu.f64(w_g))
+    for h in range(w.heads):
+        want_oc, want_lse, _ = orc.coarse_forward(gu.f64(q[0, h]), gu.f64(k[0, h]), gu.f64(v[0, h]), w.grid)
+        _close(w, gu.f64(oc_hat[0, h]), want_oc, f"O_hat_c head {h}")
+        np.testing.assert_allclose(gu.f64(lse_c[0, h]), want_lse, atol=1e-4 if w.dtype == "f32" else 2e-3)
+        np.testing.assert_allclose(gu.f64(g[0, h]), gate[:, h], atol=1e-5 if w.dtype == "f32" else 1e-4)
+        want_o = orc.merge(gate[:, h], want_oc, gu.f64(layer.o_f[0, h]))
+        _close(w, gu.f64(o[0, h]), want_o, f"O head {h}")
+    if zero_gate:
+        assert torch.equal(o, layer.o_f), "W_g = 0 must give O = O_f exactly"
+
+
+# ----------------------------------------------------------------------------- backward
+@pytest.mark.parametrize("w", SMALL, ids=lambda w: w.name)
+def test_backward(w):
+    (q, k, v, x, w_g), (qd, kd, vd, xd, wd), layer = _setup(w)
+    d_o = make_grad_out(w)
+    _, masks = _oracle_masks(w, q, k, range(w.heads))
+    layer.set_selection(*gu.csr_tensors(masks, _dev()))
+    layer.forward(qd, kd, vd, xd, wd, route=False)
+    grads = layer.backward(qd, kd, vd, xd, wd, d_o.to(_dev()))
+    torch.cuda.synchronize()
+    a = [gu.f64(t[0]) for t in (q, k, v)]
+    dq, dk, dv, dx, dw = orc.vsa2_backward(*a, w.grid, masks, gu.f64(x[0]), gu.f64(w_g), gu.f64(d_o[0]))
+    cq, ck, cv = orc.coarse_gate_backward(*a, w.grid, gu.f64(x[0]), gu.f64(w_g), gu.f64(d_o[0]))[:3]
+    tol = 1e-4 if w.dtype == "f32" else 2e-2
+    for name, want in (("dq", dq), ("dk", dk), ("dv", dv), ("dx", dx), ("dw_g", dw)):
+        got = gu.f64(grads[name][0] if name != "dw_g" else grads[name])
+        r = gu.rel_l2(got, want.reshape(got.shape))
+        assert r <= tol, f"{name}: rel-L2 {r:.3g} > {tol}"
+    for i, want in enumerate((cq, ck, cv)):
+        r = gu.rel_l2(gu.f64(grads["dqkv_c"][i, 0]), want)
+        assert r <= tol, f"dqkv_c[{i}]: rel-L2 {r:.3g}"
+
+
+def test_backward_is_bitwise_deterministic():
+    w = MID
+    (q, k, v, x, w_g), (qd, kd, vd, xd, wd), layer = _setup(w)
+    d_o = make_grad_out(w).to(_dev())
+    outs = []
+    for _ in range(2):
+        layer.forward(qd, kd, vd, xd, wd)
+        g = layer.backward(qd, kd, vd, xd, wd, d_o)
+        torch.cuda.synchronize()
+        outs.append([t.clone() for t in (layer.o, layer.col_idx, g["dq"], g["dk"], g["dv"], g["dx"], g["dw_g"])])
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
+
+
+# ----------------------------------------------------------------------------- the Short workload
+def test_short_forward_pipeline():
+    """Short 480p-like shape (16x32x64, 20 heads, d128, bf16, top64): the whole
+    forward on all heads; oracle checks on heads 0 and 7."""
+    w = SHORT
+    (q, k, v, x, w_g), (qd, kd, vd, xd, wd), layer = _setup(w, zero_gate=False)
+    layer.forward(qd, kd, vd, xd, wd)
+    torch.cuda.synchronize()
+    heads = [0, 7]
+    scores, masks = _oracle_masks(w, q, k, heads)
+    got_scores = gu.f64(layer.scores[0])
+    gpu_masks = gu.masks_from_csr(layer.row_ptr[0], layer.col_idx[0], w.nb)
+    gu.check_csr_csc(layer.row_ptr[0], layer.col_idx[0], layer.col_ptr[0], layer.row_idx[0], w.nb, layer.k)
+    for n, h in enumerate(heads):
+        np.testing.assert_allclose(got_scores[h], scores[n], rtol=1e-4, atol=1e-4 * scores[n].mean())
+        outside, band, inside = gu.band_compare(gpu_masks[h], scores[n], layer.k)
+        assert outside == 0, f"head {h}: {outside} mismatches outside the band"
+    # outputs on the oracle selection for the checked heads
+    rp, ci = layer.row_ptr.clone(), layer.col_idx.clone()
+    orp, oci = gu.csr_tensors(masks, _dev())
+    for n, h in enumerate(heads):
+        rp[0, h], ci[0, h] = orp[0, n], oci[0, n]
+    layer.set_selection(rp, ci)
+    o = layer.forward(qd, kd, vd, xd, wd, route=False)
+    torch.cuda.synchronize()
+    gate = orc.gate(gu.f64(x[0]), gu.f64(w_g))
+    for n, h in enumerate(heads):
+        o_f, _ = orc.fine_forward(gu.f64(q[0, h]), gu.f64(k[0, h]), gu.f64(v[0, h]), masks[n])
+        gu.assert_close_bf16(gu.f64(layer.o_f[0, h]), o_f, f"O_f head {h}")
+        oc, _, _ = orc.coarse_forward(gu.f64(q[0, h]), gu.f64(k[0, h]), gu.f64(v[0, h]), w.grid)
+        gu.assert_close_bf16(gu.f64(o[0, h]), orc.merge(gate[:, h], oc, o_f), f"O head {h}")

@@ -1,0 +1,423 @@
+// C-ABI entry points of libvsa2 (declared in include/vsa2.h): argument
+// validation, workspace carving and kernel launches.  No allocation, no
+// synchronisation; every call enqueues on the caller's stream.
+#include <cmath>
+#include <cstring>
+
+#include "../../include/vsa2.h"
+#include "launch.h"
+
+using namespace vsa2;
+
+namespace {
+
+constexpr size_t ALIGN = 256;
+constexpr int DW_TC = 4096;  // tokens per dW_g partial (matches gate.hip)
+
+size_t up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
+
+struct Dims {
+  int batch, heads, bh, d, L, nb, nbp, Lr;
+  bool bf16;
+  size_t esz;
+  float scale;
+};
+
+int check_problem(const vsa2_problem* p, Dims& o) {
+  if (!p) return VSA2_E_ARG;
+  if (p->batch < 1 || p->heads < 1) return VSA2_E_SHAPE;
+  if (p->head_dim != 64 && p->head_dim != 128) return VSA2_E_SHAPE;
+  if (p->lat_t < 4 || p->lat_y < 4 || p->lat_x < 4) return VSA2_E_SHAPE;
+  if (p->lat_t % 4 || p->lat_y % 4 || p->lat_x % 4) return VSA2_E_SHAPE;
+  if (p->dtype != VSA2_F32 && p->dtype != VSA2_BF16) return VSA2_E_ARG;
+  const int64_t L = (int64_t)p->lat_t * p->lat_y * p->lat_x;
+  const int64_t nb = L / 64;
+  if (nb > 46340) return VSA2_E_SHAPE;  // nb^2 and all indices fit int32
+  if ((int64_t)p->batch * p->heads > (1 << 20)) return VSA2_E_SHAPE;
+  if (std::isnan(p->softmax_scale) || std::isinf(p->softmax_scale)) return VSA2_E_ARG;
+  o.batch = p->batch;
+  o.heads = p->heads;
+  o.bh = p->batch * p->heads;
+  o.d = p->head_dim;
+  o.L = (int)L;
+  o.nb = (int)nb;
+  o.nbp = (int)((nb + 63) / 64 * 64);
+  o.Lr = (int)(L / 8);
+  o.bf16 = p->dtype == VSA2_BF16;
+  o.esz = o.bf16 ? 2 : 4;
+  o.scale = p->softmax_scale > 0.f ? p->softmax_scale : 1.0f / std::sqrt((float)p->head_dim);
+  return VSA2_OK;
+}
+
+bool aligned(const void* ptr) { return ptr && ((uintptr_t)ptr % 16 == 0); }
+
+int64_t budget(const Dims& d, int32_t topk) {
+  const int64_t all = (int64_t)d.nb * d.nb;
+  const int64_t k = (int64_t)d.nb * topk;
+  return k < all ? k : all;
+}
+
+int bitmap_words(const Dims& d) { return 2 * ((d.nb + 63) / 64); }
+
+// Workspace layouts --------------------------------------------------------
+size_t ws_route(const Dims& d) { return up((size_t)d.bh * d.Lr * 4); }
+
+size_t ws_topk(const Dims& d, TopkWs* w, void* base) {
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += up(bytes);
+    return o;
+  };
+  const size_t o_hist = take((size_t)d.bh * 4096 * 4);
+  const size_t o_state = take((size_t)d.bh * 16);
+  const size_t o_row = take((size_t)d.bh * 2 * d.nb * 4);
+  const size_t o_take = take((size_t)d.bh * d.nb * 4);
+  const size_t o_col = take((size_t)d.bh * d.nb * 4);
+  const size_t o_bm = take((size_t)d.bh * d.nb * bitmap_words(d) * 4);
+  if (w) {
+    char* b = (char*)base;
+    w->hist = (uint32_t*)(b + o_hist);
+    w->state = (uint32_t*)(b + o_state);
+    w->rowcnt = (uint32_t*)(b + o_row);
+    w->take = (uint32_t*)(b + o_take);
+    w->colcnt = (uint32_t*)(b + o_col);
+    w->bitmap = (uint32_t*)(b + o_bm);
+    w->words = bitmap_words(d);
+  }
+  return off;
+}
+
+size_t ws_plan(const Dims& d, TopkWs* w, void* base) {
+  const size_t o_col = 0;
+  const size_t o_bm = up((size_t)d.bh * d.nb * 4);
+  if (w) {
+    char* b = (char*)base;
+    *w = TopkWs{};
+    w->colcnt = (uint32_t*)(b + o_col);
+    w->bitmap = (uint32_t*)(b + o_bm);
+    w->words = bitmap_words(d);
+  }
+  return o_bm + up((size_t)d.bh * d.nb * bitmap_words(d) * 4);
+}
+
+size_t ws_bwd(const Dims& d) { return up((size_t)d.bh * d.L * 4); }
+
+int pad16(int x) { return (x + 15) / 16 * 16; }
+int pad32(int x) { return (x + 31) / 32 * 32; }
+
+size_t wt_bytes(const Dims& d, int dm) { return up((size_t)(2 * pad16(d.heads) + 2 * pad32(d.heads)) * dm * d.esz); }
+
+int nchunk_of(const Dims& d) { return (d.L + DW_TC - 1) / DW_TC; }
+
+struct CoarseBwdWs {
+  void* wt;
+  float* dpre;
+  void* doc;
+  float* delta_c;
+  float* dw_part;
+};
+
+size_t ws_coarse_bwd(const Dims& d, int dm, CoarseBwdWs* w, void* base) {
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += up(bytes);
+    return o;
+  };
+  const size_t o_wt = take(wt_bytes(d, dm));
+  const size_t o_dpre = take((size_t)d.bh * d.L * 4);
+  const size_t o_doc = take((size_t)d.bh * d.nbp * d.d * d.esz);
+  const size_t o_dc = take((size_t)d.bh * d.nbp * 4);
+  const size_t o_dw = take((size_t)d.batch * nchunk_of(d) * dm * d.heads * 4);
+  if (w) {
+    char* b = (char*)base;
+    w->wt = b + o_wt;
+    w->dpre = (float*)(b + o_dpre);
+    w->doc = b + o_doc;
+    w->delta_c = (float*)(b + o_dc);
+    w->dw_part = (float*)(b + o_dw);
+  }
+  return off;
+}
+
+int check_dm(const Dims& d, int32_t dm) {
+  if (dm < 64 || dm % 64) return VSA2_E_SHAPE;
+  if (d.heads > 64) return VSA2_E_UNSUPPORTED;
+  return VSA2_OK;
+}
+
+int check_ws(void* ws, size_t have, size_t need) {
+  if (need == 0) return VSA2_OK;
+  if (!ws || ((uintptr_t)ws % ALIGN)) return ws ? VSA2_E_ARG : VSA2_E_WORKSPACE;
+  return have >= need ? VSA2_OK : VSA2_E_WORKSPACE;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? VSA2_OK : VSA2_E_HIP; }
+
+struct Pooled {
+  const void *qr, *kr, *qc, *kc, *vc;
+};
+Pooled pooled_ptrs(const Dims& d, const void* base) {
+  const char* b = (const char*)base;
+  const size_t r = (size_t)d.bh * d.Lr * d.d * d.esz;
+  const size_t c = (size_t)d.bh * d.nbp * d.d * d.esz;
+  return Pooled{b, b + r, b + 2 * r, b + 2 * r + c, b + 2 * r + 2 * c};
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* vsa2_status_string(int s) {
+  switch (s) {
+    case VSA2_OK: return "ok";
+    case VSA2_E_ARG: return "invalid argument (NULL/misaligned pointer or bad scalar)";
+    case VSA2_E_SHAPE: return "unsupported shape (grid must be multiples of 4, head_dim 64 or 128)";
+    case VSA2_E_WORKSPACE: return "workspace too small";
+    case VSA2_E_HIP: return "HIP launch failed";
+    case VSA2_E_UNSUPPORTED: return "unsupported request";
+    default: return "unknown status";
+  }
+}
+
+int vsa2_budget(const vsa2_problem* p, int32_t topk, int64_t* k) {
+  Dims d;
+  int s = check_problem(p, d);
+  if (s) return s;
+  if (!k || topk < 1) return VSA2_E_ARG;
+  *k = budget(d, topk);
+  return VSA2_OK;
+}
+
+int vsa2_pooled_size(const vsa2_problem* p, size_t* bytes) {
+  Dims d;
+  int s = check_problem(p, d);
+  if (s) return s;
+  if (!bytes) return VSA2_E_ARG;
+  *bytes = (size_t)d.bh * (2 * (size_t)d.Lr + 3 * (size_t)d.nbp) * d.d * d.esz;
+  return VSA2_OK;
+}
+
+int vsa2_saved_size(const vsa2_problem* p, size_t* bytes) {
+  Dims d;
+  int s = check_problem(p, d);
+  if (s) return s;
+  if (!bytes) return VSA2_E_ARG;
+  *bytes = ((size_t)d.bh * d.nb * d.d + (size_t)d.bh * d.nb + (size_t)d.bh * d.L) * 4;
+  return VSA2_OK;
+}
+
+int vsa2_workspace_size(const vsa2_problem* p, int32_t op, int32_t topk, int32_t d_model, size_t* bytes) {
+  Dims d;
+  int s = check_problem(p, d);
+  if (s) return s;
+  if (!bytes) return VSA2_E_ARG;
+  switch (op) {
+    case VSA2_OP_POOL: *bytes = 0; break;
+    case VSA2_OP_ROUTE: *bytes = ws_route(d); break;
+    case VSA2_OP_TOPK: *bytes = ws_topk(d, nullptr, nullptr); break;
+    case VSA2_OP_PLAN: *bytes = ws_plan(d, nullptr, nullptr); break;
+    case VSA2_OP_FWD: *bytes = 0; break;
+    case VSA2_OP_BWD: *bytes = ws_bwd(d); break;
+    case VSA2_OP_COARSE:
+      if ((s = check_dm(d, d_model))) return s;
+      *bytes = wt_bytes(d, d_model);
+      break;
+    case VSA2_OP_COARSE_BWD:
+      if ((s = check_dm(d, d_model))) return s;
+      *bytes = ws_coarse_bwd(d, d_model, nullptr, nullptr);
+      break;
+    default: return VSA2_E_ARG;
+  }
+  (void)topk;
+  return VSA2_OK;
+}
+
+int vsa2_pool(const vsa2_problem* p, const void* q, const void* k, const void* v, void* pooled, void* stream) {
+  Dims d;
+  int s = check_problem(p, d);
+  if (s) return s;
+  if (!aligned(q) || !aligned(k) || !aligned(v) || !aligned(pooled)) return VSA2_E_ARG;
+  Pooled pp = pooled_ptrs(d, pooled);
+  PoolArgs a{q, k, v, (void*)pp.qr, (void*)pp.kr, (void*)pp.qc, (void*)pp.kc, (void*)pp.vc, d.bh, d.nb, d.nbp, d.d,
+             d.bf16};
+  return hip_status(launch_pool(a, (hipStream_t)stream));
+}
+
+int vsa2_route(const vsa2_problem* p, const void* pooled, float* scores, void* ws, size_t ws_bytes, void* stream) {
+  Dims d;
+  int s = check_problem(p, d);
+  if (s) return s;
+  if (!aligned(pooled) || !aligned(scores)) return VSA2_E_ARG;
+  if ((s = check_ws(ws, ws_bytes, ws_route(d)))) return s;
+  Pooled pp = pooled_ptrs(d, pooled);
+  RouteArgs a{pp.qr, pp.kr, (float*)ws, scores, d.bh, d.nb, d.d, d.bf16, d.scale * 1.4426950408889634f};
+  return hip_status(launch_route(a, (hipStream_t)stream));
+}
+
+int vsa2_topk_per_seq(const vsa2_problem* p, const float* scores, int32_t topk, int32_t* row_ptr, int32_t* col_idx,
+                      int32_t* col_ptr, int32_t* row_idx, void* ws, size_t ws_bytes, void* stream) {
+  Dims d;
+  int s = check_problem(p, d);
+  if (s) return s;
+  if (topk < 1) return VSA2_E_ARG;
+  if (!aligned(scores) || !aligned(row_ptr) || !aligned(col_idx) || !aligned(col_ptr) || !aligned(row_idx))
+    return VSA2_E_ARG;
+  if ((s = check_ws(ws, ws_bytes, ws_topk(d, nullptr, nullptr)))) return s;
+  TopkArgs a{};
+  a.scores = scores;
+  a.row_ptr = row_ptr;
+  a.col_idx = col_idx;
+  a.col_ptr = col_ptr;
+  a.row_idx = row_idx;
+  a.bh = d.bh;
+  a.nb = d.nb;
+  a.k = budget(d, topk);
+  ws_topk(d, &a.ws, ws);
+  return hip_status(launch_topk(a, (hipStream_t)stream));
+}
+
+int vsa2_plan_from_csr(const vsa2_problem* p, int32_t topk, const int32_t* row_ptr, const int32_t* col_idx,
+                       int32_t* col_ptr, int32_t* row_idx, void* ws, size_t ws_bytes, void* stream) {
+  Dims d;
+  int s = check_problem(p, d);
+  if (s) return s;
+  if (topk < 1) return VSA2_E_ARG;
+  if (!aligned(row_ptr) || !aligned(col_idx) || !aligned(col_ptr) || !aligned(row_idx)) return VSA2_E_ARG;
+  if ((s = check_ws(ws, ws_bytes, ws_plan(d, nullptr, nullptr)))) return s;
+  TopkArgs a{};
+  a.row_ptr = const_cast<int32_t*>(row_ptr);
+  a.col_idx = const_cast<int32_t*>(col_idx);
+  a.col_ptr = col_ptr;
+  a.row_idx = row_idx;
+  a.bh = d.bh;
+  a.nb = d.nb;
+  a.k = budget(d, topk);
+  ws_plan(d, &a.ws, ws);
+  return hip_status(launch_plan(a, (hipStream_t)stream));
+}
+
+int vsa2_sparse_attn_fwd(const vsa2_problem* p, int32_t topk, const void* q, const void* k, const void* v,
+                         const int32_t* row_ptr, const int32_t* col_idx, void* o_f, float* lse, void* ws,
+                         size_t ws_bytes, void* stream) {
+  Dims d;
+  int s = check_problem(p, d);
+  if (s) return s;
+  if (topk < 1) return VSA2_E_ARG;
+  if (!aligned(q) || !aligned(k) || !aligned(v) || !aligned(row_ptr) || !aligned(col_idx) || !aligned(o_f) ||
+      !aligned(lse))
+    return VSA2_E_ARG;
+  (void)ws;
+  (void)ws_bytes;
+  AttnArgs a{};
+  a.q = q; a.k = k; a.v = v;
+  a.row_ptr = row_ptr; a.col_idx = col_idx;
+  a.o = o_f; a.lse = lse;
+  a.bh = d.bh; a.nq = d.nb; a.nkv = d.nb; a.seq = d.L; a.ld = d.L; a.out_rows = d.L;
+  a.kph = budget(d, topk);
+  a.d = d.d; a.bf16 = d.bf16; a.dense = false;
+  a.scale_log2 = d.scale * 1.4426950408889634f;
+  return hip_status(launch_attn_fwd(a, (hipStream_t)stream));
+}
+
+int vsa2_sparse_attn_bwd(const vsa2_problem* p, int32_t topk, const void* q, const void* k, const void* v,
+                         const void* o_f, const float* lse, const void* d_o, const int32_t* row_ptr,
+                         const int32_t* col_idx, const int32_t* col_ptr, const int32_t* row_idx, const float* dqkv_c,
+                         void* dq, void* dk, void* dv, void* ws, size_t ws_bytes, void* stream) {
+  Dims d;
+  int s = check_problem(p, d);
+  if (s) return s;
+  if (topk < 1) return VSA2_E_ARG;
+  if (!aligned(q) || !aligned(k) || !aligned(v) || !aligned(o_f) || !aligned(lse) || !aligned(d_o) ||
+      !aligned(row_ptr) || !aligned(col_idx) || !aligned(col_ptr) || !aligned(row_idx) || !aligned(dq) ||
+      !aligned(dk) || !aligned(dv))
+    return VSA2_E_ARG;
+  if (dqkv_c && !aligned(dqkv_c)) return VSA2_E_ARG;
+  if ((s = check_ws(ws, ws_bytes, ws_bwd(d)))) return s;
+  const hipStream_t st = (hipStream_t)stream;
+  AttnBwdArgs a{};
+  a.q = q; a.k = k; a.v = v; a.o = o_f; a.d_o = d_o;
+  a.lse = lse;
+  a.delta = (const float*)ws;
+  a.row_ptr = row_ptr; a.col_idx = col_idx; a.col_ptr = col_ptr; a.row_idx = row_idx;
+  const size_t cstride = (size_t)d.bh * d.nb * d.d;
+  a.dq_add = dqkv_c;
+  a.dk_add = dqkv_c ? dqkv_c + cstride : nullptr;
+  a.dv_add = dqkv_c ? dqkv_c + 2 * cstride : nullptr;
+  a.dq = dq; a.dk = dk; a.dv = dv;
+  a.bh = d.bh; a.nq = d.nb; a.nkv = d.nb; a.seq = d.L; a.ld = d.L; a.out_rows = d.L; a.lse_rows = d.L;
+  a.kph = budget(d, topk);
+  a.d = d.d; a.bf16 = d.bf16; a.dense = false;
+  a.scale = d.scale;
+  a.scale_log2 = d.scale * 1.4426950408889634f;
+  hipError_t e = launch_bwd_delta(a, (float*)ws, st);
+  if (e != hipSuccess) return VSA2_E_HIP;
+  return hip_status(launch_attn_bwd(a, st));
+}
+
+int vsa2_coarse_gate(const vsa2_problem* p, const void* pooled, const void* x, int32_t d_model, const float* w_g,
+                     const void* o_f, void* o, float* saved, void* ws, size_t ws_bytes, void* stream) {
+  Dims d;
+  int s = check_problem(p, d);
+  if (s) return s;
+  if ((s = check_dm(d, d_model))) return s;
+  if (!aligned(pooled) || !aligned(x) || !aligned(w_g) || !aligned(o_f) || !aligned(o) || !aligned(saved))
+    return VSA2_E_ARG;
+  if ((s = check_ws(ws, ws_bytes, wt_bytes(d, d_model)))) return s;
+  const hipStream_t st = (hipStream_t)stream;
+  Pooled pp = pooled_ptrs(d, pooled);
+  float* oc_hat = saved;
+  float* lse_c = oc_hat + (size_t)d.bh * d.nb * d.d;
+  float* g = lse_c + (size_t)d.bh * d.nb;
+  AttnArgs a{};
+  a.q = pp.qc; a.k = pp.kc; a.v = pp.vc;
+  a.o = oc_hat; a.lse = lse_c;
+  a.bh = d.bh; a.nq = d.nbp / 64; a.nkv = d.nbp / 64; a.seq = d.nb; a.ld = d.nbp; a.out_rows = d.nb;
+  a.kph = 0;
+  a.d = d.d; a.bf16 = d.bf16; a.dense = true;
+  a.scale_log2 = d.scale * 1.4426950408889634f;
+  hipError_t e = launch_attn_fwd(a, st);
+  if (e != hipSuccess) return VSA2_E_HIP;
+  GateArgs ga{x, w_g, ws, oc_hat, o_f, o, g, d.batch, d.heads, d.nb, d.d, d_model, d.bf16};
+  return hip_status(launch_gate_fwd(ga, st));
+}
+
+int vsa2_coarse_gate_bwd(const vsa2_problem* p, const void* pooled, const void* x, int32_t d_model, const float* w_g,
+                         const float* saved, const void* d_o, float* dqkv_c, void* dx, float* dw_g, void* ws,
+                         size_t ws_bytes, void* stream) {
+  Dims d;
+  int s = check_problem(p, d);
+  if (s) return s;
+  if ((s = check_dm(d, d_model))) return s;
+  if (!aligned(pooled) || !aligned(x) || !aligned(w_g) || !aligned(saved) || !aligned(d_o) || !aligned(dqkv_c) ||
+      !aligned(dx) || !aligned(dw_g))
+    return VSA2_E_ARG;
+  if ((s = check_ws(ws, ws_bytes, ws_coarse_bwd(d, d_model, nullptr, nullptr)))) return s;
+  const hipStream_t st = (hipStream_t)stream;
+  CoarseBwdWs w{};
+  ws_coarse_bwd(d, d_model, &w, ws);
+  Pooled pp = pooled_ptrs(d, pooled);
+  const float* oc_hat = saved;
+  const float* lse_c = oc_hat + (size_t)d.bh * d.nb * d.d;
+  const float* g = lse_c + (size_t)d.bh * d.nb;
+  GateBwdArgs ga{x, w_g, w.wt, oc_hat, g, d_o, w.dpre, w.doc, w.delta_c, w.dw_part, dx, dw_g,
+                 d.batch, d.heads, d.nb, d.nbp, d.d, d_model, nchunk_of(d), d.bf16};
+  hipError_t e = launch_gate_bwd(ga, st);
+  if (e != hipSuccess) return VSA2_E_HIP;
+  AttnBwdArgs a{};
+  a.q = pp.qc; a.k = pp.kc; a.v = pp.vc; a.o = nullptr; a.d_o = w.doc;
+  a.lse = lse_c;
+  a.delta = w.delta_c;
+  const size_t cstride = (size_t)d.bh * d.nb * d.d;
+  a.dq = dqkv_c; a.dk = dqkv_c + cstride; a.dv = dqkv_c + 2 * cstride;
+  a.bh = d.bh; a.nq = d.nbp / 64; a.nkv = d.nbp / 64; a.seq = d.nb; a.ld = d.nbp; a.out_rows = d.nb;
+  a.lse_rows = d.nb;
+  a.kph = 0;
+  a.d = d.d; a.bf16 = d.bf16; a.dense = true;
+  a.scale = d.scale;
+  a.scale_log2 = d.scale * 1.4426950408889634f;
+  return hip_status(launch_attn_bwd(a, st));
+}
+
+}  // extern "C"

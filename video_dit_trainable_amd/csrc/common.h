@@ -1,0 +1,270 @@
+// Device-side building blocks shared by the VSA2 kernels (gfx950 / CDNA4).
+//
+// MFMA fragment convention used everywhere (wave64, 16x16 output tiles):
+//   * a "k-step" contracts 32 values.  For bf16 it is one
+//     v_mfma_f32_16x16x32_bf16; for fp32 it is eight v_mfma_f32_16x16x4_f32
+//     issued on the eight elements of the same fragment, so both element types
+//     share one fragment layout.
+//   * lane l = 16*g + c (g = 0..3, c = 0..15).  The A operand row and the B
+//     operand column are c; the 8 values a lane supplies belong to the k-slots
+//     (g, e), e = 0..7.  The hardware pairs A slot (g, e) with B slot (g, e), so
+//     any bijection between the 32 slots and the 32 contracted indices gives
+//     the same product as long as A and B use the same one.
+//   * the accumulator of a 16x16 tile: lane l holds rows 4g + r (r = 0..3) of
+//     column c.
+// The accumulator of S^T = K Q^T therefore holds, per lane, four keys of one
+// query; fed back as the B operand of O^T = V^T P^T it needs the key<->slot map
+//   pi(g, e) = 4g + e (e < 4),  16 + 4g + (e - 4) (e >= 4)
+// within each 32-key chunk, and the V^T operand is read with the same map.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace vsa2 {
+
+typedef __bf16 bf16;
+typedef bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+
+constexpr int CUBE = 64;   // tokens per 4x4x4 cube = rows of one attention tile
+constexpr int SUBC = 8;    // tokens per 2x2x2 router sub-cube
+constexpr float LOG2E = 1.4426950408889634f;
+constexpr float LN2 = 0.6931471805599453f;
+
+template <typename T> struct Frag;
+template <> struct Frag<bf16> { bf16x8 v; };
+template <> struct Frag<float> { f32x8 v; };
+
+__device__ __forceinline__ void mma(f32x4& c, const Frag<bf16>& a, const Frag<bf16>& b) {
+  c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, b.v, c, 0, 0, 0);
+}
+__device__ __forceinline__ void mma(f32x4& c, const Frag<float>& a, const Frag<float>& b) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[e], b.v[e], c, 0, 0, 0);
+}
+
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16 x) { return (float)x; }
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// 8 consecutive elements in registers (16 B of bf16 or 32 B of fp32)
+template <typename T> struct Vec8 { T v[8]; };
+
+template <typename T>
+__device__ __forceinline__ Vec8<T> load8(const T* p) {
+  Vec8<T> r;
+  if constexpr (sizeof(T) == 2) {
+    uint4 u = *reinterpret_cast<const uint4*>(p);
+    __builtin_memcpy(&r, &u, 16);
+  } else {
+    uint4 u0 = reinterpret_cast<const uint4*>(p)[0];
+    uint4 u1 = reinterpret_cast<const uint4*>(p)[1];
+    __builtin_memcpy(&r, &u0, 16);
+    __builtin_memcpy(reinterpret_cast<char*>(&r) + 16, &u1, 16);
+  }
+  return r;
+}
+
+template <typename T>
+__device__ __forceinline__ void store8(T* p, const Vec8<T>& r) {
+  if constexpr (sizeof(T) == 2) {
+    uint4 u;
+    __builtin_memcpy(&u, &r, 16);
+    *reinterpret_cast<uint4*>(p) = u;
+  } else {
+    uint4 u0, u1;
+    __builtin_memcpy(&u0, &r, 16);
+    __builtin_memcpy(&u1, reinterpret_cast<const char*>(&r) + 16, 16);
+    reinterpret_cast<uint4*>(p)[0] = u0;
+    reinterpret_cast<uint4*>(p)[1] = u1;
+  }
+}
+
+// 4 consecutive elements (8 B of bf16 / 16 B of fp32)
+template <typename T> struct Vec4 { T v[4]; };
+template <typename T>
+__device__ __forceinline__ Vec4<T> load4(const T* p) {
+  Vec4<T> r;
+  if constexpr (sizeof(T) == 2) {
+    uint2 u = *reinterpret_cast<const uint2*>(p);
+    __builtin_memcpy(&r, &u, 8);
+  } else {
+    uint4 u = *reinterpret_cast<const uint4*>(p);
+    __builtin_memcpy(&r, &u, 16);
+  }
+  return r;
+}
+template <typename T>
+__device__ __forceinline__ void store4(T* p, const Vec4<T>& r) {
+  if constexpr (sizeof(T) == 2) {
+    uint2 u;
+    __builtin_memcpy(&u, &r, 8);
+    *reinterpret_cast<uint2*>(p) = u;
+  } else {
+    uint4 u;
+    __builtin_memcpy(&u, &r, 16);
+    *reinterpret_cast<uint4*>(p) = u;
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ Frag<T> frag_from8(const Vec8<T>& a) {
+  Frag<T> f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) f.v[e] = a.v[e];
+  return f;
+}
+
+// Fragment from two 4-element runs (the pi map: slots e<4 from lo, e>=4 from hi).
+template <typename T>
+__device__ __forceinline__ Frag<T> frag_from44(const Vec4<T>& lo, const Vec4<T>& hi) {
+  Frag<T> f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) { f.v[e] = lo.v[e]; f.v[4 + e] = hi.v[e]; }
+  return f;
+}
+
+// Fragment from two accumulator tiles (the pi map) converted to T.
+template <typename T>
+__device__ __forceinline__ Frag<T> frag_from_acc(const f32x4& lo, const f32x4& hi) {
+  Frag<T> f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) { f.v[e] = from_f32<T>(lo[e]); f.v[4 + e] = from_f32<T>(hi[e]); }
+  return f;
+}
+
+// ---------------------------------------------------------------------------
+// 64 x D tile movement between global memory and LDS.
+// A "unit" is 4 rows x 8 columns; thread t owns units t, t + NT, ...
+// Row-major LDS tiles have row stride D + RPAD, transposed ones (D rows of 64
+// tokens) have row stride 64 + TPAD; the pads (16 B) spread LDS banks.
+// ---------------------------------------------------------------------------
+template <typename T> struct Pad {
+  static constexpr int R = 16 / sizeof(T);
+  static constexpr int TR = 16 / sizeof(T);
+};
+
+template <typename T, int D> struct TileGeom {
+  static constexpr int UNITS = (CUBE / 4) * (D / 8);
+  static constexpr int RS = D + Pad<T>::R;      // row-major row stride (elements)
+  static constexpr int TS = CUBE + Pad<T>::TR;  // transposed row stride (elements)
+  static constexpr int RM_ELEMS = CUBE * RS;
+  static constexpr int TR_ELEMS = D * TS;
+};
+
+template <typename T, int D, int NT>
+struct TileRegs {
+  static constexpr int NU = (TileGeom<T, D>::UNITS + NT - 1) / NT;
+  Vec8<T> r[NU][4];
+};
+
+// Load a 64 x D tile (row stride ld elements); rows >= valid_rows are zero.
+template <typename T, int D, int NT>
+__device__ __forceinline__ void tile_load(TileRegs<T, D, NT>& R, const T* __restrict__ src, int tid, int valid_rows,
+                                          size_t ld = D) {
+#pragma unroll
+  for (int n = 0; n < TileRegs<T, D, NT>::NU; ++n) {
+    const int u = tid + n * NT;
+    if (u < TileGeom<T, D>::UNITS) {
+      const int rg = u / (D / 8), cg = u % (D / 8);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = 4 * rg + r;
+        if (row < valid_rows) {
+          R.r[n][r] = load8(src + (size_t)row * ld + 8 * cg);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) R.r[n][r].v[e] = from_f32<T>(0.f);
+        }
+      }
+    }
+  }
+}
+
+template <typename T, int D, int NT>
+__device__ __forceinline__ void tile_store_rm(const TileRegs<T, D, NT>& R, T* lds, int tid) {
+  constexpr int RS = TileGeom<T, D>::RS;
+#pragma unroll
+  for (int n = 0; n < TileRegs<T, D, NT>::NU; ++n) {
+    const int u = tid + n * NT;
+    if (u < TileGeom<T, D>::UNITS) {
+      const int rg = u / (D / 8), cg = u % (D / 8);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) store8(lds + (4 * rg + r) * RS + 8 * cg, R.r[n][r]);
+    }
+  }
+}
+
+template <typename T, int D, int NT>
+__device__ __forceinline__ void tile_store_tr(const TileRegs<T, D, NT>& R, T* lds, int tid) {
+  constexpr int TS = TileGeom<T, D>::TS;
+#pragma unroll
+  for (int n = 0; n < TileRegs<T, D, NT>::NU; ++n) {
+    const int u = tid + n * NT;
+    if (u < TileGeom<T, D>::UNITS) {
+      const int rg = u / (D / 8), cg = u % (D / 8);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        Vec4<T> c;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) c.v[r] = R.r[n][r].v[e];
+        store4(lds + (8 * cg + e) * TS + 4 * rg, c);
+      }
+    }
+  }
+}
+
+// A/B fragment of a row-major LDS tile: row `row`, k-step ks, slot group g.
+template <typename T, int D>
+__device__ __forceinline__ Frag<T> frag_rm(const T* lds, int row, int ks, int g) {
+  return frag_from8(load8(lds + row * TileGeom<T, D>::RS + 32 * ks + 8 * g));
+}
+
+// A fragment of a transposed LDS tile (row = feature d, k = token) with the pi
+// map over token chunk c (32 tokens).
+template <typename T, int D>
+__device__ __forceinline__ Frag<T> frag_tr(const T* lds, int drow, int c, int g) {
+  const T* p = lds + drow * TileGeom<T, D>::TS + 32 * c + 4 * g;
+  return frag_from44(load4(p), load4(p + 16));
+}
+
+// Fragment straight from global memory: row `row` of a row-major [*, D] array.
+template <typename T, int D>
+__device__ __forceinline__ Frag<T> frag_global(const T* __restrict__ base, int row, int ks, int g) {
+  return frag_from8(load8(base + (size_t)row * D + 32 * ks + 8 * g));
+}
+
+// Butterfly reductions over the four slot groups (lanes c, c+16, c+32, c+48).
+__device__ __forceinline__ float group_max(float x) {
+  x = fmaxf(x, __shfl_xor(x, 16));
+  x = fmaxf(x, __shfl_xor(x, 32));
+  return x;
+}
+__device__ __forceinline__ float group_sum(float x) {
+  x += __shfl_xor(x, 16);
+  x += __shfl_xor(x, 32);
+  return x;
+}
+
+// Block -> work-item map that gives each XCD a contiguous slice of every
+// (batch, head): consecutive block ids go round-robin over the 8 XCDs, so
+// block b runs on XCD b % 8.  Returns false for the padding blocks.
+__device__ __forceinline__ bool xcd_work(int bid, int items_per_bh, int& bh, int& item) {
+  const int per = (items_per_bh + 7) >> 3;
+  const int xcd = bid & 7, s = bid >> 3;
+  bh = s / per;
+  item = xcd * per + (s - bh * per);
+  return item < items_per_bh;
+}
+__host__ __device__ inline int xcd_grid(int items_per_bh, int bh_total) {
+  return 8 * ((items_per_bh + 7) >> 3) * bh_total;
+}
+
+}  // namespace vsa2

@@ -1,0 +1,344 @@
+// Gated merge of VSA2 (paper §2.2 Eq.(13)-(14)): G = tanh(X W_g), one gate per
+// token and head, O = G * Repeat(O_hat_c) + O_f (Eq.(4) broadcast fused), and
+// its backward (dW_g, dX, dO_hat_c).
+//
+// X W_g and dpre W_g^T are skinny GEMMs run on MFMA; in bf16 mode the fp32
+// operands W_g and dpre are split into a bf16 high part and a bf16 remainder
+// (x = hi + lo to ~16 mantissa bits) so the products keep near-fp32 accuracy.
+// dW_g = X^T dpre is reduced over token chunks into per-chunk partials that a
+// second kernel adds in a fixed order (no float atomics).
+#include <cmath>
+
+#include "common.h"
+#include "launch.h"
+
+namespace vsa2 {
+
+constexpr int HMAX = 64;   // heads supported by the gate kernels
+constexpr int DW_TC = 4096;  // tokens per dW_g partial
+
+struct GateGeom {
+  int hp, hk;  // heads padded to 16 (forward N) and 32 (backward K)
+  size_t f_elems() const { return 0; }
+};
+
+__host__ __device__ inline int pad_up(int x, int m) { return (x + m - 1) / m * m; }
+
+// Repack W_g [dm, H] fp32 into MFMA operands: F = W_g^T [hp, dm] (hi, lo) and
+// Bk = W_g [dm, hk] (hi, lo), zero-padded.
+template <typename T>
+__global__ void k_gate_prep(const float* __restrict__ w, T* __restrict__ wt, int dm, int H, int hp, int hk) {
+  T* fhi = wt;
+  T* flo = fhi + (size_t)hp * dm;
+  T* bhi = flo + (size_t)hp * dm;
+  T* blo = bhi + (size_t)dm * hk;
+  const size_t nf = (size_t)hp * dm, nbk = (size_t)dm * hk;
+  for (size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x; idx < nf + nbk; idx += (size_t)gridDim.x * blockDim.x) {
+    int h, m;
+    T *dhi, *dlo;
+    size_t o;
+    if (idx < nf) {
+      h = (int)(idx / dm); m = (int)(idx % dm); dhi = fhi; dlo = flo; o = idx;
+    } else {
+      const size_t r = idx - nf;
+      m = (int)(r / hk); h = (int)(r % hk); dhi = bhi; dlo = blo; o = r;
+    }
+    const float x = h < H ? w[(size_t)m * H + h] : 0.f;
+    const T hi = from_f32<T>(x);
+    dhi[o] = hi;
+    dlo[o] = from_f32<T>(x - to_f32(hi));
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ void split8(const float* x, Frag<T>& hi, Frag<T>& lo) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const T h = from_f32<T>(x[e]);
+    hi.v[e] = h;
+    lo.v[e] = from_f32<T>(x[e] - to_f32(h));
+  }
+}
+
+// One block per (cube, batch): gates of its 64 tokens for every head, then the merge.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void k_gate_fwd(const T* __restrict__ x, const T* __restrict__ wt,
+                                                  const float* __restrict__ oc_hat, const T* __restrict__ o_f,
+                                                  T* __restrict__ o, float* __restrict__ gout, int H, int nb, int dm,
+                                                  int hp) {
+  constexpr bool SPLIT = sizeof(T) == 2;
+  __shared__ float gs[64][HMAX + 1];
+  const int c = blockIdx.x, b = blockIdx.y, tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4,
+            cc = lane & 15;
+  const size_t L = (size_t)nb * CUBE;
+  const T* fhi = wt;
+  const T* flo = wt + (size_t)hp * dm;
+  const int nhb = hp / 16;
+  const size_t t0 = (size_t)c * CUBE + 16 * w;
+  f32x4 acc[HMAX / 16];
+#pragma unroll
+  for (int hb = 0; hb < HMAX / 16; ++hb) acc[hb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const T* xrow = x + ((size_t)b * L + t0 + cc) * dm;
+  for (int s = 0; s < dm / 32; ++s) {
+    const Frag<T> a = frag_from8(load8(xrow + 32 * s + 8 * g));
+#pragma unroll
+    for (int hb = 0; hb < HMAX / 16; ++hb) {
+      if (hb < nhb) {
+        mma(acc[hb], a, frag_from8(load8(fhi + (size_t)(16 * hb + cc) * dm + 32 * s + 8 * g)));
+        if constexpr (SPLIT) mma(acc[hb], a, frag_from8(load8(flo + (size_t)(16 * hb + cc) * dm + 32 * s + 8 * g)));
+      }
+    }
+  }
+#pragma unroll
+  for (int hb = 0; hb < HMAX / 16; ++hb) {
+    if (hb < nhb) {
+      const int h = 16 * hb + cc;
+      float4 gv;
+      gv.x = tanhf(acc[hb][0]); gv.y = tanhf(acc[hb][1]); gv.z = tanhf(acc[hb][2]); gv.w = tanhf(acc[hb][3]);
+      gs[16 * w + 4 * g + 0][h] = gv.x;
+      gs[16 * w + 4 * g + 1][h] = gv.y;
+      gs[16 * w + 4 * g + 2][h] = gv.z;
+      gs[16 * w + 4 * g + 3][h] = gv.w;
+      if (h < H) *reinterpret_cast<float4*>(gout + ((size_t)b * H + h) * L + t0 + 4 * g) = gv;
+    }
+  }
+  __syncthreads();
+  constexpr int UPR = D / 8;  // units per token row
+  for (int h = 0; h < H; ++h) {
+    const size_t bh = (size_t)b * H + h;
+    const float* oc = oc_hat + (bh * nb + c) * D;
+    for (int u = tid; u < 64 * UPR; u += 256) {
+      const int t = u / UPR, dg = u % UPR;
+      const float gv = gs[t][h];
+      const size_t off = (bh * L + (size_t)c * CUBE + t) * D + 8 * dg;
+      const Vec8<T> f = load8(o_f + off);
+      const float4 a0 = *reinterpret_cast<const float4*>(oc + 8 * dg);
+      const float4 a1 = *reinterpret_cast<const float4*>(oc + 8 * dg + 4);
+      const float ocv[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+      Vec8<T> r;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) r.v[e] = from_f32<T>(fmaf(gv, ocv[e], to_f32(f.v[e])));
+      store8(o + off, r);
+    }
+  }
+}
+
+// One block per (cube, batch): dgate, dpre = dg (1 - g^2), dO_hat_c and its
+// rowsum against O_hat_c for every head, then dX = dpre W_g^T.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void k_gate_bwd(const T* __restrict__ wt, const float* __restrict__ oc_hat,
+                                                  const float* __restrict__ gin, const T* __restrict__ d_o,
+                                                  float* __restrict__ dpre, T* __restrict__ doc,
+                                                  float* __restrict__ delta_c, T* __restrict__ dx, int H, int nb,
+                                                  int nbp, int dm, int hp, int hk) {
+  constexpr bool SPLIT = sizeof(T) == 2;
+  constexpr int UPR = D / 8;
+  constexpr int RROWS = 256 / UPR;
+  __shared__ float dps[64][HMAX + 4];
+  __shared__ float red[RROWS][D];
+  __shared__ float wsum[4];
+  const int c = blockIdx.x, b = blockIdx.y, tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4,
+            cc = lane & 15;
+  const size_t L = (size_t)nb * CUBE;
+  for (int u = tid; u < 64 * (HMAX + 4); u += 256) dps[u / (HMAX + 4)][u % (HMAX + 4)] = 0.f;
+  __syncthreads();
+  const int dg = tid % UPR;
+  for (int h = 0; h < H; ++h) {
+    const size_t bh = (size_t)b * H + h;
+    const float* oc = oc_hat + (bh * nb + c) * D;
+    const float4 a0 = *reinterpret_cast<const float4*>(oc + 8 * dg);
+    const float4 a1 = *reinterpret_cast<const float4*>(oc + 8 * dg + 4);
+    const float ocv[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+    float pacc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int t = tid / UPR; t < 64; t += RROWS) {
+      const size_t tok = (size_t)c * CUBE + t;
+      const Vec8<T> x = load8(d_o + (bh * L + tok) * D + 8 * dg);
+      const float gv = gin[bh * L + tok];
+      float part = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float xv = to_f32(x.v[e]);
+        part = fmaf(xv, ocv[e], part);
+        pacc[e] = fmaf(gv, xv, pacc[e]);
+      }
+#pragma unroll
+      for (int s = 1; s < UPR; s <<= 1) part += __shfl_xor(part, s);
+      if (dg == 0) {
+        const float dp = part * (1.f - gv * gv);
+        dps[t][h] = dp;
+        dpre[bh * L + tok] = dp;
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) red[tid / UPR][8 * dg + e] = pacc[e];
+    __syncthreads();
+    float prod = 0.f;
+    if (tid < D) {
+      float s = 0.f;
+      for (int r = 0; r < RROWS; ++r) s += red[r][tid];
+      doc[(bh * nbp + c) * D + tid] = from_f32<T>(s);
+      prod = s * oc[tid];
+    }
+    for (int s = 1; s < 64; s <<= 1) prod += __shfl_xor(prod, s);
+    if (lane == 0) wsum[w] = prod;
+    __syncthreads();
+    if (tid == 0) delta_c[bh * nbp + c] = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+  }
+  // zero the padding rows of dO_hat_c / delta_c
+  for (int row = nb + c; row < nbp; row += nb)
+    for (int h = 0; h < H; ++h) {
+      const size_t bh = (size_t)b * H + h;
+      for (int d = tid; d < D; d += 256) doc[(bh * nbp + row) * D + d] = from_f32<T>(0.f);
+      if (tid == 0) delta_c[bh * nbp + row] = 0.f;
+    }
+  __syncthreads();
+  // dX^T[m][t] = sum_h W_g[m][h] dpre[t][h]
+  const T* bhi = wt + 2 * (size_t)hp * dm;
+  const T* blo = bhi + (size_t)dm * hk;
+  Frag<T> phi[HMAX / 32], plo[HMAX / 32];
+#pragma unroll
+  for (int s = 0; s < HMAX / 32; ++s) {
+    if (32 * s < hk) {
+      float v8[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v8[e] = dps[16 * w + cc][32 * s + 8 * g + e];
+      split8<T>(v8, phi[s], plo[s]);
+    }
+  }
+  T* dxb = dx + ((size_t)b * L + (size_t)c * CUBE + 16 * w + cc) * dm;
+  for (int mb = 0; mb < dm / 16; ++mb) {
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < HMAX / 32; ++s) {
+      if (32 * s < hk) {
+        const Frag<T> ahi = frag_from8(load8(bhi + (size_t)(16 * mb + cc) * hk + 32 * s + 8 * g));
+        mma(acc, ahi, phi[s]);
+        if constexpr (SPLIT) {
+          const Frag<T> alo = frag_from8(load8(blo + (size_t)(16 * mb + cc) * hk + 32 * s + 8 * g));
+          mma(acc, ahi, plo[s]);
+          mma(acc, alo, phi[s]);
+        }
+      }
+    }
+    Vec4<T> r4;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) r4.v[r] = from_f32<T>(acc[r]);
+    store4(dxb + 16 * mb + 4 * g, r4);
+  }
+}
+
+// dW_g partial over one token chunk: dW[m][h] = sum_t X[t][m] dpre[h][t].
+// Block = (64 columns of X, token chunk, batch); X tiles transposed in LDS.
+template <typename T>
+__global__ __launch_bounds__(256) void k_dwg_part(const T* __restrict__ x, const float* __restrict__ dpre,
+                                                  float* __restrict__ part, int H, int nb, int dm, int nchunk) {
+  constexpr bool SPLIT = sizeof(T) == 2;
+  using G = TileGeom<T, 64>;
+  __shared__ T xt[G::TR_ELEMS];
+  const int mblk = blockIdx.x, chunk = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, cc = lane & 15;
+  const size_t L = (size_t)nb * CUBE;
+  const int nhb = (H + 15) / 16;
+  f32x4 acc[HMAX / 16];
+#pragma unroll
+  for (int hb = 0; hb < HMAX / 16; ++hb) acc[hb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  TileRegs<T, 64, 256> regs;
+  for (size_t t0 = (size_t)chunk * DW_TC; t0 < L && t0 < (size_t)(chunk + 1) * DW_TC; t0 += 64) {
+    tile_load<T, 64, 256>(regs, x + ((size_t)b * L + t0) * dm + 64 * mblk, tid, 64, (size_t)dm);
+    __syncthreads();
+    tile_store_tr<T, 64, 256>(regs, xt, tid);
+    __syncthreads();
+#pragma unroll
+    for (int c2 = 0; c2 < 2; ++c2) {
+      const Frag<T> a = frag_tr<T, 64>(xt, 16 * w + cc, c2, g);
+#pragma unroll
+      for (int hb = 0; hb < HMAX / 16; ++hb) {
+        if (hb < nhb) {
+          const int h = 16 * hb + cc;
+          float v8[8];
+          if (h < H) {
+            const float* src = dpre + ((size_t)b * H + h) * L + t0 + 32 * c2 + 4 * g;
+            const float4 lo = *reinterpret_cast<const float4*>(src);
+            const float4 hi = *reinterpret_cast<const float4*>(src + 16);
+            v8[0] = lo.x; v8[1] = lo.y; v8[2] = lo.z; v8[3] = lo.w;
+            v8[4] = hi.x; v8[5] = hi.y; v8[6] = hi.z; v8[7] = hi.w;
+          } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v8[e] = 0.f;
+          }
+          Frag<T> bhi, blo;
+          split8<T>(v8, bhi, blo);
+          mma(acc[hb], a, bhi);
+          if constexpr (SPLIT) mma(acc[hb], a, blo);
+        }
+      }
+    }
+  }
+  float* out = part + (((size_t)b * nchunk + chunk) * dm + 64 * mblk) * H;
+#pragma unroll
+  for (int hb = 0; hb < HMAX / 16; ++hb) {
+    const int h = 16 * hb + cc;
+    if (hb < nhb && h < H) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) out[(size_t)(16 * w + 4 * g + r) * H + h] = acc[hb][r];
+    }
+  }
+}
+
+__global__ void k_dwg_reduce(const float* __restrict__ part, float* __restrict__ dw, int n, int parts) {
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= n) return;
+  float s = 0.f;
+  for (int p = 0; p < parts; ++p) s += part[(size_t)p * n + idx];
+  dw[idx] = s;
+}
+
+template <typename T>
+static hipError_t gate_prep(const float* w_g, void* wt, int dm, int H, hipStream_t st) {
+  const int hp = pad_up(H, 16), hk = pad_up(H, 32);
+  const size_t n = (size_t)(hp + hk) * dm;
+  unsigned blocks = (unsigned)((n + 255) / 256);
+  if (blocks > 2048) blocks = 2048;
+  hipLaunchKernelGGL((k_gate_prep<T>), dim3(blocks), dim3(256), 0, st, w_g, (T*)wt, dm, H, hp, hk);
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t launch_gate_fwd_t(const GateArgs& a, hipStream_t st) {
+  hipError_t e = gate_prep<T>(a.w_g, a.wt, a.dm, a.heads, st);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((k_gate_fwd<T, D>), dim3(a.nb, a.batch), dim3(256), 0, st, (const T*)a.x, (const T*)a.wt,
+                     a.oc_hat, (const T*)a.o_f, (T*)a.o, a.g, a.heads, a.nb, a.dm, pad_up(a.heads, 16));
+  return hipGetLastError();
+}
+
+hipError_t launch_gate_fwd(const GateArgs& a, hipStream_t st) {
+  if (a.bf16) return a.d == 128 ? launch_gate_fwd_t<bf16, 128>(a, st) : launch_gate_fwd_t<bf16, 64>(a, st);
+  return a.d == 128 ? launch_gate_fwd_t<float, 128>(a, st) : launch_gate_fwd_t<float, 64>(a, st);
+}
+
+template <typename T, int D>
+hipError_t launch_gate_bwd_t(const GateBwdArgs& a, hipStream_t st) {
+  hipError_t e = gate_prep<T>(a.w_g, a.wt, a.dm, a.heads, st);
+  if (e != hipSuccess) return e;
+  const int hp = pad_up(a.heads, 16), hk = pad_up(a.heads, 32);
+  hipLaunchKernelGGL((k_gate_bwd<T, D>), dim3(a.nb, a.batch), dim3(256), 0, st, (const T*)a.wt, a.oc_hat, a.g,
+                     (const T*)a.d_o, a.dpre, (T*)a.doc, a.delta_c, (T*)a.dx, a.heads, a.nb, a.nbp, a.dm, hp, hk);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((k_dwg_part<T>), dim3(a.dm / 64, a.nchunk, a.batch), dim3(256), 0, st, (const T*)a.x, a.dpre,
+                     a.dw_part, a.heads, a.nb, a.dm, a.nchunk);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int n = a.dm * a.heads;
+  hipLaunchKernelGGL(k_dwg_reduce, dim3((n + 255) / 256), dim3(256), 0, st, a.dw_part, a.dw_g, n,
+                     a.batch * a.nchunk);
+  return hipGetLastError();
+}
+
+hipError_t launch_gate_bwd(const GateBwdArgs& a, hipStream_t st) {
+  if (a.bf16) return a.d == 128 ? launch_gate_bwd_t<bf16, 128>(a, st) : launch_gate_bwd_t<bf16, 64>(a, st);
+  return a.d == 128 ? launch_gate_bwd_t<float, 128>(a, st) : launch_gate_bwd_t<float, 64>(a, st);
+}
+
+}  // namespace vsa2

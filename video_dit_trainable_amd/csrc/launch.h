@@ -1,0 +1,115 @@
+// Internal launch interface between the C-ABI layer (api.cpp) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace vsa2 {
+
+struct PoolArgs {
+  const void *q, *k, *v;
+  void *qr, *kr, *qc, *kc, *vc;
+  int bh, nb, nbp, d;
+  bool bf16;
+};
+hipError_t launch_pool(const PoolArgs& a, hipStream_t st);
+
+struct RouteArgs {
+  const void *qr, *kr;
+  float* lse2;        // workspace [bh, 8*nb], log2-domain LSE of each pooled query
+  float* scores;      // [bh, nb, nb]
+  int bh, nb, d;
+  bool bf16;
+  float scale_log2;   // softmax scale * log2(e)
+};
+hipError_t launch_route(const RouteArgs& a, hipStream_t st);
+
+struct TopkWs {       // carved from the caller workspace
+  uint32_t* hist;     // [bh, 4096]
+  uint32_t* state;    // [bh, 4]: prefix, need, count above, pad
+  uint32_t* rowcnt;   // [bh, 2, nb]: (> tau, == tau) per row
+  uint32_t* take;     // [bh, nb] ties taken per row
+  uint32_t* colcnt;   // [bh, nb]
+  uint32_t* bitmap;   // [bh, nb, words]
+  int words;          // 32-bit words per bitmap row (multiple of 2)
+};
+struct TopkArgs {
+  const float* scores;
+  int32_t *row_ptr, *col_idx, *col_ptr, *row_idx;
+  int bh, nb;
+  int64_t k;
+  TopkWs ws;
+};
+hipError_t launch_topk(const TopkArgs& a, hipStream_t st);
+// CSC from a caller CSR (uses ws.colcnt and ws.bitmap)
+hipError_t launch_plan(const TopkArgs& a, hipStream_t st);
+
+struct AttnArgs {
+  const void *q, *k, *v;
+  const int32_t *row_ptr, *col_idx;   // CSR (ignored when dense)
+  void* o;                            // storage dtype (fine) or fp32 (dense)
+  float* lse;                         // [bh, out_rows] natural log
+  int bh;
+  int nq;                             // query cubes per (batch, head)
+  int nkv;                            // kv cubes per (batch, head) (dense)
+  int seq;                            // valid tokens per head (rows >= seq are padding)
+  int ld;                             // token rows per head in q/k/v buffers
+  int out_rows;                       // token rows per head in o / lse
+  int64_t kph;                        // col_idx entries per (batch, head)
+  int d;
+  bool bf16, dense;
+  float scale_log2;
+};
+hipError_t launch_attn_fwd(const AttnArgs& a, hipStream_t st);
+
+struct AttnBwdArgs {
+  const void *q, *k, *v, *o, *d_o;
+  const float* lse;                   // [bh, lse_rows]
+  const float* delta;                 // [bh, ld] rowsum(dO * O), made by launch_bwd_delta
+  const int32_t *row_ptr, *col_idx, *col_ptr, *row_idx;
+  const float *dq_add, *dk_add, *dv_add;  // [bh, nkv, d] per-cube terms added as row/64 (or NULL)
+  void *dq, *dk, *dv;                 // storage dtype (fine) or fp32 (dense)
+  int bh, nq, nkv, seq, ld, out_rows, lse_rows;
+  int64_t kph;
+  int d;
+  bool bf16, dense;
+  float scale;
+  float scale_log2;
+};
+hipError_t launch_bwd_delta(const AttnBwdArgs& a, float* delta, hipStream_t st);
+hipError_t launch_attn_bwd(const AttnBwdArgs& a, hipStream_t st);
+
+struct GateArgs {
+  const void* x;          // [batch, L, dm]
+  const float* w_g;       // [dm, heads]
+  void* wt;               // workspace: gate weights repacked for the MFMA operands
+  const float* oc_hat;    // [bh, nb, d] fp32
+  const void* o_f;
+  void* o;
+  float* g;               // [bh, L]
+  int batch, heads, nb, d, dm;
+  bool bf16;
+};
+hipError_t launch_gate_fwd(const GateArgs& a, hipStream_t st);
+
+struct GateBwdArgs {
+  const void* x;
+  const float* w_g;
+  void* wt;               // workspace repack (as forward)
+  const float* oc_hat;    // [bh, nb, d]
+  const float* g;         // [bh, L]
+  const void* d_o;        // [bh, L, d]
+  float* dpre;            // workspace [bh, L]
+  void* doc;              // workspace [bh, nbp, d] storage dtype: dO_hat_c
+  float* delta_c;         // workspace [bh, nbp]: rowsum(dO_hat_c * O_hat_c)
+  float* dw_part;         // workspace [nchunk, dm, heads]
+  void* dx;
+  float* dw_g;
+  int batch, heads, nb, nbp, d, dm, nchunk;
+  bool bf16;
+};
+hipError_t launch_gate_bwd(const GateBwdArgs& a, hipStream_t st);
+
+hipError_t launch_fill_u32(uint32_t* p, uint32_t val, size_t n, hipStream_t st);
+
+}  // namespace vsa2

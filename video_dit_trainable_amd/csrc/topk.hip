@@ -1,0 +1,321 @@
+// Per-sequence TopK of VSA2 (paper §2.2 Eq.(8)-(9)): for each (batch, head)
+// keep the k = nb*K largest of the nb*nb block scores; each query cube then
+// holds a variable number of KV cubes.
+//
+// Exact selection without sorting.  Non-negative fp32 values order like their
+// uint32 bit patterns, so the k-th largest pattern tau is found by a 3-pass
+// radix select (digits of 12, 12 and 8 bits; per-head histograms with integer
+// atomics, whose totals do not depend on ordering).  Then every row counts
+// its entries > tau and == tau, a per-head scan hands the ties at tau to the
+// lowest flat indices, and each row is compacted in ascending column order
+// (wave ballots), which also records a selection bitmap and column counts.
+// The CSC form is built from the bitmap with no atomics: 4 waves split the
+// rows of a 64-column strip, count, offset by an exclusive scan, and write.
+#include <cmath>
+
+#include "common.h"
+#include "launch.h"
+
+namespace vsa2 {
+
+__device__ __forceinline__ uint32_t score_bits(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return (u & 0x80000000u) ? 0u : u;  // scores are >= 0; -0.0 ranks as +0.0
+}
+
+__device__ __forceinline__ uint64_t lanemask_lt(int lane) { return (lane == 0) ? 0ull : (~0ull >> (64 - lane)); }
+
+__global__ void k_fill_u32(uint32_t* __restrict__ p, uint32_t val, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) p[i] = val;
+}
+
+hipError_t launch_fill_u32(uint32_t* p, uint32_t val, size_t n, hipStream_t st) {
+  if (n == 0) return hipSuccess;
+  size_t blocks = (n + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(k_fill_u32, dim3((unsigned)blocks), dim3(256), 0, st, p, val, n);
+  return hipGetLastError();
+}
+
+// Histogram of digit (u >> SHIFT) & (2^BITS - 1) over the entries whose bits
+// above SHIFT+BITS equal the prefix found by the previous passes.
+template <int SHIFT, int BITS>
+__global__ __launch_bounds__(256) void k_hist(const float* __restrict__ scores, uint32_t* __restrict__ hist,
+                                              const uint32_t* __restrict__ state, size_t n) {
+  constexpr int NBIN = 1 << BITS;
+  __shared__ uint32_t h[NBIN];
+  const int bh = blockIdx.y, tid = threadIdx.x;
+  for (int b = tid; b < NBIN; b += 256) h[b] = 0;
+  __syncthreads();
+  const uint32_t prefix = (SHIFT + BITS < 32) ? state[bh * 4 + 0] : 0u;
+  const float* s = scores + (size_t)bh * n;
+  for (size_t i = (size_t)blockIdx.x * 256 + tid; i < n; i += (size_t)gridDim.x * 256) {
+    const uint32_t u = score_bits(s[i]);
+    bool ok = true;
+    if constexpr (SHIFT + BITS < 32) ok = (u >> (SHIFT + BITS)) == (prefix >> (SHIFT + BITS));
+    if (ok) atomicAdd(&h[(u >> SHIFT) & (NBIN - 1)], 1u);
+  }
+  __syncthreads();
+  for (int b = tid; b < NBIN; b += 256)
+    if (h[b]) atomicAdd(&hist[(size_t)bh * 4096 + b], h[b]);
+}
+
+// Pick the digit holding the `need`-th largest remaining entry.
+// state = {prefix, need, count strictly above the prefix region, -}.
+template <int SHIFT, int BITS>
+__global__ __launch_bounds__(256) void k_select(const uint32_t* __restrict__ hist, uint32_t* __restrict__ state,
+                                                uint32_t k_first) {
+  constexpr int NBIN = 1 << BITS, PER = NBIN / 256;
+  __shared__ uint32_t part[256];
+  const int bh = blockIdx.x, tid = threadIdx.x;
+  const uint32_t* hb = hist + (size_t)bh * 4096;
+  uint32_t s = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) s += hb[tid * PER + i];
+  part[tid] = s;
+  __syncthreads();
+  if (tid == 0) {
+    const bool first = (SHIFT + BITS == 32);
+    uint32_t need = first ? k_first : state[bh * 4 + 1];
+    uint32_t above = first ? 0u : state[bh * 4 + 2];
+    uint32_t prefix = first ? 0u : state[bh * 4 + 0];
+    uint32_t acc = 0;
+    int t = 255;
+    for (; t > 0; --t) {
+      if (acc + part[t] >= need) break;
+      acc += part[t];
+    }
+    int b = t * PER + PER - 1;
+    for (; b > t * PER; --b) {
+      if (acc + hb[b] >= need) break;
+      acc += hb[b];
+    }
+    state[bh * 4 + 0] = prefix | ((uint32_t)b << SHIFT);
+    state[bh * 4 + 1] = need - acc;
+    state[bh * 4 + 2] = above + acc;
+  }
+}
+
+// Per row: entries > tau and == tau (one wave per row).
+__global__ __launch_bounds__(256) void k_rowcount(const float* __restrict__ scores, const uint32_t* __restrict__ state,
+                                                  uint32_t* __restrict__ rowcnt, int nb) {
+  const int bh = blockIdx.y, row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (row >= nb) return;
+  const uint32_t tau = state[bh * 4 + 0];
+  const float* s = scores + ((size_t)bh * nb + row) * nb;
+  uint32_t gt = 0, eq = 0;
+  for (int j0 = 0; j0 < nb; j0 += 64) {
+    const int j = j0 + lane;
+    const uint32_t u = j < nb ? score_bits(s[j]) : 0u;
+    gt += __popcll(__ballot(j < nb && u > tau));
+    eq += __popcll(__ballot(j < nb && u == tau));
+  }
+  if (lane == 0) {
+    rowcnt[((size_t)bh * 2 + 0) * nb + row] = gt;
+    rowcnt[((size_t)bh * 2 + 1) * nb + row] = eq;
+  }
+}
+
+// Block-wide exclusive scan of one value per thread (1024 threads); returns
+// the exclusive prefix and sets `total`.
+__device__ uint32_t block_scan_1024(uint32_t x, uint32_t& total, uint32_t* sh) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  uint32_t inc = x;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t y = __shfl_up(inc, o);
+    if (lane >= o) inc += y;
+  }
+  if (lane == 63) sh[w] = inc;
+  __syncthreads();
+  if (tid == 0) {
+    uint32_t a = 0;
+    for (int i = 0; i < 16; ++i) {
+      const uint32_t t = sh[i];
+      sh[i] = a;
+      a += t;
+    }
+    sh[16] = a;
+  }
+  __syncthreads();
+  const uint32_t r = sh[w] + inc - x;
+  total = sh[16];
+  __syncthreads();
+  return r;
+}
+
+// Ties at tau go to the lowest flat indices: row i takes
+// clamp(need - (ties in rows < i), 0, ties in row i).  Builds row_ptr.
+__global__ __launch_bounds__(1024) void k_rowalloc(const uint32_t* __restrict__ rowcnt,
+                                                   const uint32_t* __restrict__ state, uint32_t* __restrict__ take,
+                                                   int32_t* __restrict__ row_ptr, int nb) {
+  __shared__ uint32_t sh[17];
+  const int bh = blockIdx.x, tid = threadIdx.x;
+  const uint32_t need = state[bh * 4 + 1];
+  const uint32_t* gt = rowcnt + (size_t)bh * 2 * nb;
+  const uint32_t* eq = gt + nb;
+  uint32_t carry_eq = 0, carry_sel = 0;
+  for (int i0 = 0; i0 < nb; i0 += 1024) {
+    const int i = i0 + tid;
+    const uint32_t e = i < nb ? eq[i] : 0u;
+    uint32_t tot;
+    const uint32_t before = carry_eq + block_scan_1024(e, tot, sh);
+    carry_eq += tot;
+    const uint32_t tk = need > before ? min(need - before, e) : 0u;
+    const uint32_t sel = i < nb ? gt[i] + tk : 0u;
+    const uint32_t pos = carry_sel + block_scan_1024(sel, tot, sh);
+    carry_sel += tot;
+    if (i < nb) {
+      take[(size_t)bh * nb + i] = tk;
+      row_ptr[(size_t)bh * (nb + 1) + i] = (int32_t)pos;
+    }
+  }
+  if (tid == 0) row_ptr[(size_t)bh * (nb + 1) + nb] = (int32_t)carry_sel;
+}
+
+// Compact each row in ascending column order; record bitmap and column counts.
+__global__ __launch_bounds__(256) void k_compact(const float* __restrict__ scores, const uint32_t* __restrict__ state,
+                                                 const uint32_t* __restrict__ take, const int32_t* __restrict__ row_ptr,
+                                                 int32_t* __restrict__ col_idx, uint32_t* __restrict__ bitmap,
+                                                 uint32_t* __restrict__ colcnt, int nb, int64_t kph, int words) {
+  const int bh = blockIdx.y, row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (row >= nb) return;
+  const uint32_t tau = state[bh * 4 + 0];
+  const uint32_t tk = take[(size_t)bh * nb + row];
+  const float* s = scores + ((size_t)bh * nb + row) * nb;
+  int32_t* out = col_idx + (size_t)bh * kph + row_ptr[(size_t)bh * (nb + 1) + row];
+  uint32_t* bm = bitmap + ((size_t)bh * nb + row) * words;
+  uint32_t eq_seen = 0, written = 0;
+  const uint64_t lt = lanemask_lt(lane);
+  for (int j0 = 0; j0 < nb; j0 += 64) {
+    const int j = j0 + lane;
+    const uint32_t u = j < nb ? score_bits(s[j]) : 0u;
+    const bool is_eq = j < nb && u == tau;
+    const uint64_t eqm = __ballot(is_eq);
+    const uint32_t rank = eq_seen + __popcll(eqm & lt);
+    const bool sel = j < nb && (u > tau || (is_eq && rank < tk));
+    const uint64_t selm = __ballot(sel);
+    const int64_t slot = (int64_t)row_ptr[(size_t)bh * (nb + 1) + row] + written + __popcll(selm & lt);
+    if (sel && slot < kph) {
+      out[written + __popcll(selm & lt)] = j;
+      atomicAdd(&colcnt[(size_t)bh * nb + j], 1u);
+    }
+    if (lane < 2) bm[(j0 >> 5) + lane] = (uint32_t)(selm >> (32 * lane));
+    eq_seen += __popcll(eqm);
+    written += __popcll(selm);
+  }
+}
+
+// Selection given as CSR: bitmap + column counts.
+__global__ __launch_bounds__(256) void k_csr_scatter(const int32_t* __restrict__ row_ptr,
+                                                     const int32_t* __restrict__ col_idx, uint32_t* __restrict__ bitmap,
+                                                     uint32_t* __restrict__ colcnt, int nb, int64_t kph, int words) {
+  const int bh = blockIdx.y, row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (row >= nb) return;
+  const int32_t* rp = row_ptr + (size_t)bh * (nb + 1);
+  const int32_t* ci = col_idx + (size_t)bh * kph;
+  const int64_t n0 = min<int64_t>(max(rp[row], 0), kph), n1 = min<int64_t>(max<int64_t>(rp[row + 1], n0), kph);
+  for (int64_t n = n0 + lane; n < n1; n += 64) {
+    const int j = ci[n];
+    if ((unsigned)j >= (unsigned)nb) continue;   // corrupt entry: ignored
+    atomicOr(&bitmap[((size_t)bh * nb + row) * words + (j >> 5)], 1u << (j & 31));
+    atomicAdd(&colcnt[(size_t)bh * nb + j], 1u);
+  }
+}
+
+__global__ __launch_bounds__(1024) void k_colptr(const uint32_t* __restrict__ colcnt, int32_t* __restrict__ col_ptr,
+                                                 int nb) {
+  __shared__ uint32_t sh[17];
+  const int bh = blockIdx.x, tid = threadIdx.x;
+  uint32_t carry = 0;
+  for (int i0 = 0; i0 < nb; i0 += 1024) {
+    const int i = i0 + tid;
+    uint32_t tot;
+    const uint32_t pos = carry + block_scan_1024(i < nb ? colcnt[(size_t)bh * nb + i] : 0u, tot, sh);
+    carry += tot;
+    if (i < nb) col_ptr[(size_t)bh * (nb + 1) + i] = (int32_t)pos;
+  }
+  if (tid == 0) col_ptr[(size_t)bh * (nb + 1) + nb] = (int32_t)carry;
+}
+
+// CSC rows in ascending order from the bitmap: block = (64-column strip, bh),
+// wave w scans rows [w*R, (w+1)*R), lane = column.
+__global__ __launch_bounds__(256) void k_csc_fill(const uint32_t* __restrict__ bitmap, const int32_t* __restrict__ col_ptr,
+                                                  int32_t* __restrict__ row_idx, int nb, int64_t kph, int words) {
+  __shared__ uint32_t cnt[4][64];
+  const int bh = blockIdx.y, strip = blockIdx.x, w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int j = strip * 64 + lane;
+  const int R = (nb + 3) / 4;
+  const int r0 = w * R, r1 = min(nb, r0 + R);
+  const uint32_t* bm = bitmap + (size_t)bh * nb * words + 2 * strip + (lane >> 5);
+  const uint32_t bit = 1u << (lane & 31);
+  uint32_t c = 0;
+  for (int i = r0; i < r1; ++i) c += (bm[(size_t)i * words] & bit) ? 1u : 0u;
+  cnt[w][lane] = c;
+  __syncthreads();
+  if (j >= nb) return;
+  uint32_t base = col_ptr[(size_t)bh * (nb + 1) + j];
+  for (int ww = 0; ww < w; ++ww) base += cnt[ww][lane];
+  int32_t* out = row_idx + (size_t)bh * kph;
+  for (int i = r0; i < r1; ++i)
+    if ((bm[(size_t)i * words] & bit) && base < kph) out[base++] = i;
+}
+
+static hipError_t csc_from_bitmap(const TopkArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL(k_colptr, dim3(a.bh), dim3(1024), 0, st, a.ws.colcnt, a.col_ptr, a.nb);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_csc_fill, dim3(a.ws.words / 2, a.bh), dim3(256), 0, st, a.ws.bitmap, a.col_ptr, a.row_idx,
+                     a.nb, a.k, a.ws.words);
+  return hipGetLastError();
+}
+
+#define VSA2_CHECK(x)                      \
+  do {                                     \
+    hipError_t e_ = (x);                   \
+    if (e_ != hipSuccess) return e_;       \
+  } while (0)
+
+hipError_t launch_topk(const TopkArgs& a, hipStream_t st) {
+  const size_t n = (size_t)a.nb * a.nb;
+  int chunks = (int)((n + 256 * 64 - 1) / (256 * 64));
+  if (chunks > 128) chunks = 128;
+  if (chunks < 1) chunks = 1;
+  const dim3 hgrid(chunks, a.bh);
+  const dim3 rgrid((a.nb + 3) / 4, a.bh);
+  VSA2_CHECK(launch_fill_u32(a.ws.hist, 0u, (size_t)a.bh * 4096, st));
+  hipLaunchKernelGGL((k_hist<20, 12>), hgrid, dim3(256), 0, st, a.scores, a.ws.hist, a.ws.state, n);
+  VSA2_CHECK(hipGetLastError());
+  hipLaunchKernelGGL((k_select<20, 12>), dim3(a.bh), dim3(256), 0, st, a.ws.hist, a.ws.state, (uint32_t)a.k);
+  VSA2_CHECK(hipGetLastError());
+  VSA2_CHECK(launch_fill_u32(a.ws.hist, 0u, (size_t)a.bh * 4096, st));
+  hipLaunchKernelGGL((k_hist<8, 12>), hgrid, dim3(256), 0, st, a.scores, a.ws.hist, a.ws.state, n);
+  VSA2_CHECK(hipGetLastError());
+  hipLaunchKernelGGL((k_select<8, 12>), dim3(a.bh), dim3(256), 0, st, a.ws.hist, a.ws.state, 0u);
+  VSA2_CHECK(hipGetLastError());
+  VSA2_CHECK(launch_fill_u32(a.ws.hist, 0u, (size_t)a.bh * 4096, st));
+  hipLaunchKernelGGL((k_hist<0, 8>), hgrid, dim3(256), 0, st, a.scores, a.ws.hist, a.ws.state, n);
+  VSA2_CHECK(hipGetLastError());
+  hipLaunchKernelGGL((k_select<0, 8>), dim3(a.bh), dim3(256), 0, st, a.ws.hist, a.ws.state, 0u);
+  VSA2_CHECK(hipGetLastError());
+  hipLaunchKernelGGL(k_rowcount, rgrid, dim3(256), 0, st, a.scores, a.ws.state, a.ws.rowcnt, a.nb);
+  VSA2_CHECK(hipGetLastError());
+  hipLaunchKernelGGL(k_rowalloc, dim3(a.bh), dim3(1024), 0, st, a.ws.rowcnt, a.ws.state, a.ws.take, a.row_ptr, a.nb);
+  VSA2_CHECK(hipGetLastError());
+  VSA2_CHECK(launch_fill_u32(a.ws.colcnt, 0u, (size_t)a.bh * a.nb, st));
+  hipLaunchKernelGGL(k_compact, rgrid, dim3(256), 0, st, a.scores, a.ws.state, a.ws.take, a.row_ptr, a.col_idx,
+                     a.ws.bitmap, a.ws.colcnt, a.nb, a.k, a.ws.words);
+  VSA2_CHECK(hipGetLastError());
+  return csc_from_bitmap(a, st);
+}
+
+hipError_t launch_plan(const TopkArgs& a, hipStream_t st) {
+  VSA2_CHECK(launch_fill_u32(a.ws.colcnt, 0u, (size_t)a.bh * a.nb, st));
+  VSA2_CHECK(launch_fill_u32(a.ws.bitmap, 0u, (size_t)a.bh * a.nb * a.ws.words, st));
+  hipLaunchKernelGGL(k_csr_scatter, dim3((a.nb + 3) / 4, a.bh), dim3(256), 0, st, a.row_ptr, a.col_idx, a.ws.bitmap,
+                     a.ws.colcnt, a.nb, a.k, a.ws.words);
+  VSA2_CHECK(hipGetLastError());
+  return csc_from_bitmap(a, st);
+}
+
+}  // namespace vsa2
