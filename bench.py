@@ -1,0 +1,203 @@
+"""Benchmark of the VSA2 attention layer on one MI355X.
+
+One step = the whole hot path on the 720p training shape (latent 44x48x104 =
+219,648 tokens, B=1, 20 heads, d=128, bf16, per-sequence top64, skewed
+query-cube scales): pooling, fused router, per-sequence TopK, fine-branch
+forward, coarse branch + gate, coarse/gate backward and fine-branch backward,
+all through the C-ABI library on device-resident inputs.
+
+The JSON line reports effective TFLOP/s of the step (algorithmic FLOPs,
+selected blocks only), per-call times, the roofline of the dominant kernel and
+the CPU oracle timed on a bounded sample.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from video_dit_trainable_amd import vsa2  # noqa: E402
+from video_dit_trainable_amd.configs import WORKLOADS, flops  # noqa: E402
+from video_dit_trainable_amd.inputs import (make_gate_inputs, make_grad_out, make_qkv,  # noqa: E402
+                                            make_selection)
+
+PEAK_BF16 = 2.5e15      # MI355X dense bf16 MFMA, FLOP/s
+PEAK_HBM = 8.0e12       # MI355X HBM3E, B/s
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def cpu_baseline(w, q, k, v, d_o, budget_s=20.0):
+    """The oracle on a bounded sample of the same workload (head 0): router
+    rows of 32 query cubes, then fine forward + backward of 16 query cubes on a
+    seeded selection with the workload's budget.  FLOPs use the GPU's
+    algorithmic accounting; the rate is scaled to TFLOP/s."""
+    from threadpoolctl import threadpool_info
+
+    from oracle import vsa2_oracle as orc
+
+    f64 = lambda t: t.float().cpu().double().numpy()
+    qh, kh, vh, doh = f64(q[0, 0]), f64(k[0, 0]), f64(v[0, 0]), f64(d_o[0, 0])
+    rows = np.arange(32) * (w.nb // 32)
+    t0 = time.perf_counter()
+    orc.router_scores(qh, kh, w.grid, bf16_pooled=True, rows=rows)
+    t_router = time.perf_counter() - t0
+    lr = w.L // 8
+    fl = len(rows) * 8 * 2 * 2 * lr * w.head_dim
+    rp, ci = make_selection(w)
+    mask = orc.csr_to_mask(rp[0, 0].numpy(), ci[0, 0].numpy(), w.nb)
+    cubes = [i for i in range(w.nb) if mask[i].any()][:: max(1, w.nb // 16)][:16]
+    sub = np.zeros_like(mask)
+    sub[cubes] = mask[cubes]
+    t0 = time.perf_counter()
+    orc.fine_forward(qh, kh, vh, sub, rows=cubes)
+    orc.fine_backward(qh, kh, vh, sub, doh)
+    t_fine = time.perf_counter() - t0
+    fl += int(sub.sum()) * 4 * 64 * 64 * w.head_dim * 7 // 2
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    secs = t_router + t_fine
+    return {"value": fl / secs / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"head 0 of the same inputs: router rows of {len(rows)} query cubes + fine fwd+bwd of "
+                      f"{len(cubes)} query cubes ({int(sub.sum())} selected pairs); {secs:.1f} s on the host",
+            "seconds": round(secs, 2)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="train720")
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the layer shards by head "
+              "across GPUs, which this build does not implement", file=sys.stderr)
+        sys.exit(2)
+    w = WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log(f"generating inputs for {w.name} on the GPU")
+    q, k, v = make_qkv(w, device=dev)
+    d_o = make_grad_out(w, device=dev)
+    x, w_g = make_gate_inputs(w, device=dev, zero_gate=False)
+    p = vsa2.problem(w.batch, w.heads, w.head_dim, w.grid, w.dtype)
+    layer = vsa2.Layer(p, w.topk, w.d_model, device=dev)
+    torch.cuda.synchronize()
+
+    st = torch.cuda.current_stream()
+    names = ["pool", "route", "topk", "fine_fwd", "coarse_gate", "coarse_gate_bwd", "fine_bwd"]
+
+    # allocate gradient buffers once (outside the timed region)
+    layer.backward(q, k, v, x, w_g, d_o)
+    torch.cuda.synchronize()
+
+    def step_full(ev=None):
+        def mark(i):
+            if ev is not None:
+                ev[i].record(st)
+        gr = layer._grads
+        mark(0)
+        vsa2.vsa2_pool(p, q, k, v, layer.pooled)
+        mark(1)
+        vsa2.vsa2_route(p, layer.pooled, layer.scores, layer.ws)
+        mark(2)
+        vsa2.vsa2_topk_per_seq(p, layer.scores, w.topk, layer.row_ptr, layer.col_idx, layer.col_ptr,
+                               layer.row_idx, layer.ws)
+        mark(3)
+        vsa2.vsa2_sparse_attn_fwd(p, w.topk, q, k, v, layer.row_ptr, layer.col_idx, layer.o_f, layer.lse, layer.ws)
+        mark(4)
+        vsa2.vsa2_coarse_gate(p, layer.pooled, x, w.d_model, w_g, layer.o_f, layer.o, layer.saved, layer.ws)
+        mark(5)
+        if w.train:
+            vsa2.vsa2_coarse_gate_bwd(p, layer.pooled, x, w.d_model, w_g, layer.saved, d_o, gr["dqkv_c"], gr["dx"],
+                                      gr["dw_g"], layer.ws)
+        mark(6)
+        if w.train:
+            vsa2.vsa2_sparse_attn_bwd(p, w.topk, q, k, v, layer.o_f, layer.lse, d_o, layer.row_ptr, layer.col_idx,
+                                      layer.col_ptr, layer.row_idx, gr["dqkv_c"], gr["dq"], gr["dk"], gr["dv"],
+                                      layer.ws)
+        mark(7)
+
+    log(f"warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        step_full()
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(8)] for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(st)
+    for s in range(args.steps):
+        step_full(evs[s])
+    t_stop.record(st)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_stop)
+    ms_step = total_ms / args.steps
+    per = {n: float(np.median([evs[s][i].elapsed_time(evs[s][i + 1]) for s in range(args.steps)]))
+           for i, n in enumerate(names)}
+    log("per-call ms: " + ", ".join(f"{n} {t:.3f}" for n, t in per.items()))
+
+    fl = flops(w)
+    step_flops = fl["router"] + fl["fine_fwd"] + fl["coarse_fwd"] + fl["gate_fwd"]
+    if w.train:
+        step_flops += fl["fine_bwd"] + fl["coarse_bwd"] + fl["gate_bwd"]
+    value = step_flops / (ms_step * 1e-3) / 1e12
+
+    # roofline of the fine-branch forward kernel (one launch per vsa2_sparse_attn_fwd call)
+    fwd_ms = per["fine_fwd"]
+    achieved = fl["fine_fwd"] / (fwd_ms * 1e-3) / 1e12
+    roof = {"kernel": "k_attn_fwd (fine branch forward)", "bound": "mfma", "achieved": round(achieved, 2),
+            "peak": PEAK_BF16 / 1e12, "unit": "TFLOP/s", "frac": round(achieved / (PEAK_BF16 / 1e12), 4),
+            "traffic": None}
+
+    ops = {n: {"ms": round(t, 4)} for n, t in per.items()}
+    for n, key in (("fine_fwd", "fine_fwd"), ("fine_bwd", "fine_bwd"), ("route", "router")):
+        ops[n]["tflops"] = round(fl[key] / (per[n] * 1e-3) / 1e12, 2)
+        ops[n]["pct_bf16_peak"] = round(100 * fl[key] / (per[n] * 1e-3) / PEAK_BF16, 2)
+    nbytes_scores = w.batch * w.heads * w.nb * w.nb * 4
+    ops["topk"]["gbps_scores_pass"] = round(nbytes_scores / (per["topk"] * 1e-3) / 1e9, 1)
+
+    cpu = None
+    if not args.no_cpu:
+        log("timing the CPU oracle on a bounded sample")
+        cpu = cpu_baseline(w, q, k, v, d_o)
+
+    out = {
+        "metric": "ms/call + effective TFLOP/s (% bf16 MFMA peak), 220K tok, 20 heads, d128, top64",
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "720p training shape: latent 44x48x104 = 219648 tokens, B=1, 20 heads, d=128, "
+                               "bf16, router pool 2x2x2, 4x4x4 cubes, per-sequence top64, skewed query-cube "
+                               "scales; full forward + backward of router, TopK, fine, coarse and gate",
+                   "global_batch": w.batch, "seq_len": w.L, "heads": w.heads, "head_dim": w.head_dim,
+                   "topk": w.topk, "parallelism": "single GPU"},
+        "step_flops": step_flops,
+        "ops": ops,
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -36,6 +36,15 @@ def test_every_declared_symbol_is_exported():
     assert set(names) <= set(vsa2._SIGS), "binding misses a declared entry point"
 
 
+def test_binding_arity_matches_header():
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    for name, (_, args) in vsa2._SIGS.items():
+        m = re.search(r"\b" + name + r"\s*\(([^;]*?)\)\s*;", text, flags=re.S)
+        assert m, name
+        params = [a for a in m.group(1).split(",") if a.strip() and a.strip() != "void"]
+        assert len(params) == len(args), f"{name}: header has {len(params)} parameters, binding {len(args)}"
+
+
 def test_status_strings():
     L = vsa2.lib()
     for code in range(6):

@@ -48,7 +48,7 @@ _SIGS = {
     "vsa2_topk_per_seq": (ctypes.c_int, [_PP, _P, _I32, _P, _P, _P, _P, _P, _SZ, _P]),
     "vsa2_plan_from_csr": (ctypes.c_int, [_PP, _I32, _P, _P, _P, _P, _P, _SZ, _P]),
     "vsa2_sparse_attn_fwd": (ctypes.c_int, [_PP, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
-    "vsa2_sparse_attn_bwd": (ctypes.c_int, [_PP, _I32] + [_P] * 13 + [_P, _P, _P, _P, _SZ, _P]),
+    "vsa2_sparse_attn_bwd": (ctypes.c_int, [_PP, _I32] + [_P] * 15 + [_SZ, _P]),
     "vsa2_coarse_gate": (ctypes.c_int, [_PP, _P, _P, _I32, _P, _P, _P, _P, _P, _SZ, _P]),
     "vsa2_coarse_gate_bwd": (ctypes.c_int, [_PP, _P, _P, _I32, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
 }
