@@ -168,7 +168,7 @@ def test_fine_forward(w):
     masks[0] = gu.empty_rows(masks[0], [1, w.nb - 1])      # empty query rows, budget kept exact
     assert masks[0].sum() == layer.k
     layer.set_selection(*gu.csr_tensors(masks, _dev()))
-    vsa2.vsa2_sparse_attn_fwd(layer.p, w.topk, qd, kd, vd, layer.row_ptr, layer.col_idx, layer.o_f, layer.lse)
+    vsa2.vsa2_sparse_attn_fwd(layer.p, w.topk, qd, kd, vd, layer.row_ptr, layer.col_idx, layer.o_f, layer.lse, layer.ws)
     torch.cuda.synchronize()
     for h in range(w.heads):
         o, lse = orc.fine_forward(gu.f64(q[0, h]), gu.f64(k[0, h]), gu.f64(v[0, h]), masks[h])
@@ -187,7 +187,7 @@ def test_fine_forward_full_budget_is_dense_attention():
     vsa2.vsa2_route(layer.p, layer.pooled, layer.scores, layer.ws)
     vsa2.vsa2_topk_per_seq(layer.p, layer.scores, w.topk, layer.row_ptr, layer.col_idx, layer.col_ptr,
                            layer.row_idx, layer.ws)
-    vsa2.vsa2_sparse_attn_fwd(layer.p, w.topk, qd, kd, vd, layer.row_ptr, layer.col_idx, layer.o_f, layer.lse)
+    vsa2.vsa2_sparse_attn_fwd(layer.p, w.topk, qd, kd, vd, layer.row_ptr, layer.col_idx, layer.o_f, layer.lse, layer.ws)
     torch.cuda.synchronize()
     assert gu.masks_from_csr(layer.row_ptr[0], layer.col_idx[0], w.nb).all()
     for h in range(w.heads):

@@ -3,14 +3,21 @@
 // The same kernel in "dense" mode runs the coarse branch's attention over the
 // nb pooled cube tokens (Eq.(2)-(3)), with a ragged last tile.
 //
-// One block = one query cube (64 queries) of one (batch, head), 4 waves of 16
-// queries.  Q stays in registers as B fragments; the selected K/V cubes are
-// gathered through the CSR list into a double-buffered LDS stage (K row-major,
-// V transposed so both products read 16-byte runs), with the next cube's loads
-// in flight while the current one is computed.  S^T = K Q^T puts the 16 keys
-// of a lane group against one query per lane, so the online softmax is
-// lane-local except a 4-way max across the slot groups, and the exponentials
-// feed O^T += V^T P^T directly from the accumulator registers.
+// Work split: one block (2 waves) per query cube; each wave owns 32 queries as
+// MFMA B fragments in registers, so every K/V byte read from LDS feeds two
+// 16-query MFMA blocks.  The selected K cubes and the pre-transposed V cubes
+// are gathered through the CSR list into chunk-swizzled LDS tiles; the next
+// cube's loads are in flight (in registers) while the current one is
+// computed.  S^T = K Q^T leaves, per lane, 4 keys of one query per 16-key
+// block, so the online softmax is lane-local apart from a 4-lane max, and the
+// exponentials feed O^T += V^T P^T straight from the accumulators.  The O
+// rescale is lazy: the running max is only moved when a tile exceeds it by
+// more than 2^8, which keeps every exponential <= 256 and the result exact.
+//
+// V is read as V^T: a pre-pass writes each 64-token cube of V transposed to
+// [d][64] with the tokens of every 32-token half reordered to the MFMA
+// k-slot order pi(g, e) = 4g + e (e < 4), 16 + 4g + e - 4 (e >= 4), so one
+// 16-byte LDS read yields a whole A fragment.
 #include <cmath>
 
 #include "common.h"
@@ -18,23 +25,42 @@
 
 namespace vsa2 {
 
+// V [bh][rows][D] -> VT [bh][rows/64][D][64] (k-slot order inside each 32-token half).
+template <typename T, int D>
+__global__ __launch_bounds__(256) void k_vt_perm(const T* __restrict__ v, T* __restrict__ vt, int tiles) {
+  __shared__ T s[64][D + 8];
+  const int t = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
+  const T* src = v + ((size_t)bh * tiles + t) * 64 * D;
+  for (int u = tid; u < 64 * D / 8; u += 256) {
+    const int r = u / (D / 8), c8 = u % (D / 8);
+    store8(&s[r][8 * c8], load8(src + (size_t)r * D + 8 * c8));
+  }
+  __syncthreads();
+  T* dst = vt + ((size_t)bh * tiles + t) * 64 * D;
+  for (int u = tid; u < D * 8; u += 256) {      // output chunk: row d, 8 positions 8u'..8u'+7
+    const int d = u / 8, p0 = 8 * (u % 8);
+    const int half = p0 >> 5, g = (p0 >> 3) & 3;
+    Vec8<T> o;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o.v[e] = s[32 * half + (e < 4 ? 4 * g + e : 16 + 4 * g + e - 4)][d];
+    store8(dst + (size_t)d * 64 + p0, o);
+  }
+}
+
 template <typename T, typename TO, int D, bool DENSE>
-__global__ __launch_bounds__(256) void k_attn_fwd(const T* __restrict__ q, const T* __restrict__ k,
-                                                  const T* __restrict__ v, const int32_t* __restrict__ row_ptr,
+__global__ __launch_bounds__(128, 2) void k_attn_fwd(const T* __restrict__ q, const T* __restrict__ k,
+                                                  const T* __restrict__ vt, const int32_t* __restrict__ row_ptr,
                                                   const int32_t* __restrict__ col_idx, TO* __restrict__ o,
                                                   float* __restrict__ lse, int nq, int nkv, int seq, int ld,
                                                   int out_rows, int64_t kph, float c) {
-  using G = TileGeom<T, D>;
-  __shared__ T ksm[2][G::RM_ELEMS];
-  __shared__ T vsm[2][G::TR_ELEMS];
+  __shared__ __align__(16) T ks[64 * D];
+  __shared__ __align__(16) T vs[D * 64];
   int bh, i;
   if (!xcd_work(blockIdx.x, nq, bh, i)) return;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, cc = lane & 15;
-  const int qrow = i * 64 + 16 * w + cc;
   const size_t hoff = (size_t)bh * ld * D;
-  const T* qb = q + hoff;
   const T* kbase = k + hoff;
-  const T* vbase = v + hoff;
+  const T* vbase = vt + hoff;
 
   int cnt;
   const int32_t* cols = nullptr;
@@ -58,111 +84,139 @@ __global__ __launch_bounds__(256) void k_attn_fwd(const T* __restrict__ q, const
     return jj >= 0 ? 64 : 0;
   };
 
-  Frag<T> qf[D / 32];
+  Frag<T> qf[2][D / 32];
 #pragma unroll
-  for (int s = 0; s < D / 32; ++s) qf[s] = frag_global<T, D>(qb, qrow, s, g);
+  for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+    for (int s = 0; s < D / 32; ++s) qf[qb][s] = frag_global<T, D>(q + hoff, i * 64 + 32 * w + 16 * qb + cc, s, g);
 
-  f32x4 oacc[D / 16];
+  f32x4 oacc[D / 16][2];
 #pragma unroll
-  for (int db = 0; db < D / 16; ++db) oacc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m = -INFINITY, l = 0.f;
+  for (int db = 0; db < D / 16; ++db) oacc[db][0] = oacc[db][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};
 
   if (cnt > 0) {
-    TileRegs<T, D, 256> kr, vr;
+    SwRegs<64, D, T, 128> kr;
+    SwRegs<D, 64, T, 128> vr;
     int j = cube_at(0);
-    tile_load<T, D, 256>(kr, kbase + (size_t)max(j, 0) * 64 * D, tid, kv_limit(j));
-    tile_load<T, D, 256>(vr, vbase + (size_t)max(j, 0) * 64 * D, tid, kv_limit(j));
-    tile_store_rm<T, D, 256>(kr, ksm[0], tid);
-    tile_store_tr<T, D, 256>(vr, vsm[0], tid);
-    __syncthreads();
+    sw_load(kr, kbase + (size_t)max(j, 0) * 64 * D, tid, kv_limit(j));
+    sw_load(vr, vbase + (size_t)max(j, 0) * 64 * D, tid, j >= 0 ? D : 0);
     for (int n = 0; n < cnt; ++n) {
-      const int buf = n & 1;
-      int jn = 0;
+      sw_store(kr, ks, tid);
+      sw_store(vr, vs, tid);
+      __syncthreads();
+      const int lim = kv_limit(j);
       if (n + 1 < cnt) {
-        jn = cube_at(n + 1);
-        tile_load<T, D, 256>(kr, kbase + (size_t)max(jn, 0) * 64 * D, tid, kv_limit(jn));
-        tile_load<T, D, 256>(vr, vbase + (size_t)max(jn, 0) * 64 * D, tid, kv_limit(jn));
+        j = cube_at(n + 1);
+        sw_load(kr, kbase + (size_t)max(j, 0) * 64 * D, tid, kv_limit(j));
+        sw_load(vr, vbase + (size_t)max(j, 0) * 64 * D, tid, j >= 0 ? D : 0);
       }
-      f32x4 acc[4];
+      // S^T = K Q^T: acc[kb][qb] holds keys 16kb + 4g + r of query 16qb + cc (of this wave)
+      f32x4 acc[4][2];
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) acc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int kb = 0; kb < 4; ++kb) acc[kb][0] = acc[kb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < D / 32; ++s)
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) mma(acc[kb], frag_rm<T, D>(ksm[buf], 16 * kb + cc, s, g), qf[s]);
-      const int lim = kv_limit(j);
+        for (int kb = 0; kb < 4; ++kb) {
+          const Frag<T> a = sw_frag<T, D>(ks, 16 * kb + cc, s, g);
+          mma(acc[kb][0], a, qf[0][s]);
+          mma(acc[kb][1], a, qf[1][s]);
+        }
       if (lim < 64) {
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
           for (int r = 0; r < 4; ++r)
-            if (16 * kb + 4 * g + r >= lim) acc[kb][r] = -INFINITY;
+            if (16 * kb + 4 * g + r >= lim) acc[kb][0][r] = acc[kb][1][r] = -INFINITY;
       }
-      float mt = acc[0][0];
+      float mt[2];
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
+      for (int qb = 0; qb < 2; ++qb) {
+        float x = acc[0][qb][0];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) mt = fmaxf(mt, acc[kb][r]);
-      mt = group_max(mt);
-      const float mnew = fmaxf(m, mt);
-      if (mnew != -INFINITY) {
-        const float alpha = fast_exp2((m - mnew) * c);
-        m = mnew;
-        l *= alpha;
+        for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-        for (int db = 0; db < D / 16; ++db) oacc[db] *= alpha;
-        const float mc = -m * c;
+          for (int r = 0; r < 4; ++r) x = fmaxf(x, acc[kb][qb][r]);
+        mt[qb] = group_max(x);
+      }
+      // lazy rescale: move the reference max only when the tile exceeds it by > 2^8
+      const bool up0 = mt[0] * c > m[0] * c + 8.f, up1 = mt[1] * c > m[1] * c + 8.f;
+      if (__ballot(up0 || up1)) {
+        const float n0 = up0 ? mt[0] : m[0], n1 = up1 ? mt[1] : m[1];
+        const float a0 = fast_exp2((m[0] - n0) * c), a1 = fast_exp2((m[1] - n1) * c);
+        m[0] = n0;
+        m[1] = n1;
+        l[0] *= a0;
+        l[1] *= a1;
+#pragma unroll
+        for (int db = 0; db < D / 16; ++db) {
+          oacc[db][0] *= a0;
+          oacc[db][1] *= a1;
+        }
+      }
+      Frag<T> pf[2][2];
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        const float mc = m[qb] == -INFINITY ? 0.f : -m[qb] * c;
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const float p = fast_exp2(fmaf(acc[kb][r], c, mc));
-            acc[kb][r] = p;
-            l += p;
+            const float p = fast_exp2(fmaf(acc[kb][qb][r], c, mc));
+            acc[kb][qb][r] = p;
+            l[qb] += p;
           }
-        const Frag<T> p0 = frag_from_acc<T>(acc[0], acc[1]);
-        const Frag<T> p1 = frag_from_acc<T>(acc[2], acc[3]);
+        pf[qb][0] = frag_from_acc<T>(acc[0][qb], acc[1][qb]);
+        pf[qb][1] = frag_from_acc<T>(acc[2][qb], acc[3][qb]);
+      }
+      // O^T += V^T P^T
 #pragma unroll
-        for (int db = 0; db < D / 16; ++db) {
-          mma(oacc[db], frag_tr<T, D>(vsm[buf], 16 * db + cc, 0, g), p0);
-          mma(oacc[db], frag_tr<T, D>(vsm[buf], 16 * db + cc, 1, g), p1);
+      for (int db = 0; db < D / 16; ++db)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const Frag<T> a = sw_frag<T, 64>(vs, 16 * db + cc, h, g);
+          mma(oacc[db][0], a, pf[0][h]);
+          mma(oacc[db][1], a, pf[1][h]);
         }
-      }
-      if (n + 1 < cnt) {
-        tile_store_rm<T, D, 256>(kr, ksm[buf ^ 1], tid);
-        tile_store_tr<T, D, 256>(vr, vsm[buf ^ 1], tid);
-      }
       __syncthreads();
-      j = jn;
     }
   }
 
-  const float lt = group_sum(l);
-  const float inv = lt > 0.f ? 1.0f / lt : 0.f;
-  const bool live = DENSE ? (qrow < seq && qrow < out_rows) : (qrow < out_rows);
-  if (live) {
-    TO* orow = o + ((size_t)bh * out_rows + qrow) * D;
 #pragma unroll
-    for (int db = 0; db < D / 16; ++db) {
-      Vec4<TO> r4;
+  for (int qb = 0; qb < 2; ++qb) {
+    const int qrow = i * 64 + 32 * w + 16 * qb + cc;
+    const float lt = group_sum(l[qb]);
+    const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+    const bool live = DENSE ? (qrow < seq && qrow < out_rows) : (qrow < out_rows);
+    if (live) {
+      TO* orow = o + ((size_t)bh * out_rows + qrow) * D;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) r4.v[r] = from_f32<TO>(oacc[db][r] * inv);
-      store4(orow + 16 * db + 4 * g, r4);
+      for (int db = 0; db < D / 16; ++db) {
+        Vec4<TO> r4;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) r4.v[r] = from_f32<TO>(oacc[db][qb][r] * inv);
+        store4(orow + 16 * db + 4 * g, r4);
+      }
+      if (g == 0) lse[(size_t)bh * out_rows + qrow] = lt > 0.f ? (m[qb] * c + __log2f(lt)) * LN2 : -INFINITY;
     }
-    if (g == 0) lse[(size_t)bh * out_rows + qrow] = lt > 0.f ? (m * c + __log2f(lt)) * LN2 : -INFINITY;
   }
 }
 
 template <typename T, int D>
 hipError_t launch_fwd_t(const AttnArgs& a, hipStream_t st) {
+  const int tiles = a.ld / 64;
+  hipLaunchKernelGGL((k_vt_perm<T, D>), dim3(tiles, a.bh), dim3(256), 0, st, (const T*)a.v, (T*)a.vt, tiles);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   dim3 grid(xcd_grid(a.nq, a.bh));
   if (a.dense) {
-    hipLaunchKernelGGL((k_attn_fwd<T, float, D, true>), grid, dim3(256), 0, st, (const T*)a.q, (const T*)a.k,
-                       (const T*)a.v, nullptr, nullptr, (float*)a.o, a.lse, a.nq, a.nkv, a.seq, a.ld, a.out_rows,
+    hipLaunchKernelGGL((k_attn_fwd<T, float, D, true>), grid, dim3(128), 0, st, (const T*)a.q, (const T*)a.k,
+                       (const T*)a.vt, nullptr, nullptr, (float*)a.o, a.lse, a.nq, a.nkv, a.seq, a.ld, a.out_rows,
                        a.kph, a.scale_log2);
   } else {
-    hipLaunchKernelGGL((k_attn_fwd<T, T, D, false>), grid, dim3(256), 0, st, (const T*)a.q, (const T*)a.k,
-                       (const T*)a.v, a.row_ptr, a.col_idx, (T*)a.o, a.lse, a.nq, a.nkv, a.seq, a.ld, a.out_rows,
+    hipLaunchKernelGGL((k_attn_fwd<T, T, D, false>), grid, dim3(128), 0, st, (const T*)a.q, (const T*)a.k,
+                       (const T*)a.vt, a.row_ptr, a.col_idx, (T*)a.o, a.lse, a.nq, a.nkv, a.seq, a.ld, a.out_rows,
                        a.kph, a.scale_log2);
   }
   return hipGetLastError();

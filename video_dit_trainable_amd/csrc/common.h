@@ -143,20 +143,23 @@ __device__ __forceinline__ Frag<T> frag_from_acc(const f32x4& lo, const f32x4& h
 // ---------------------------------------------------------------------------
 // 64 x D tile movement between global memory and LDS.
 // A "unit" is 4 rows x 8 columns; thread t owns units t, t + NT, ...
-// Row-major LDS tiles have row stride D + RPAD, transposed ones (D rows of 64
-// tokens) have row stride 64 + TPAD; the pads (16 B) spread LDS banks.
+// Row-major LDS tiles have row stride RS = D + 8 elements (the pad spreads the
+// 16 rows a fragment read touches over all banks).  Transposed tiles hold D
+// rows of 64 tokens; the 4-token runs of row d are XOR-swizzled by sw(d), so
+// the scatter of a unit (8 rows, one 4-token run each) and the fragment reads
+// (16 rows, one run each) both spread over the banks:
+//   element (d, t) lives at d*TS + 4*((t >> 2) ^ sw(d)) + (t & 3).
+// The stride/swizzle pairs were chosen with a bank model (32- and 64-bank LDS)
+// over the exact access patterns of tile_store_tr and frag_tr.
 // ---------------------------------------------------------------------------
-template <typename T> struct Pad {
-  static constexpr int R = 16 / sizeof(T);
-  static constexpr int TR = 16 / sizeof(T);
-};
-
 template <typename T, int D> struct TileGeom {
+  static constexpr bool WIDE = (sizeof(T) == 2 && D == 128);
   static constexpr int UNITS = (CUBE / 4) * (D / 8);
-  static constexpr int RS = D + Pad<T>::R;      // row-major row stride (elements)
-  static constexpr int TS = CUBE + Pad<T>::TR;  // transposed row stride (elements)
+  static constexpr int RS = D + 8;              // row-major row stride (elements)
+  static constexpr int TS = WIDE ? 72 : 64;     // transposed row stride (elements)
   static constexpr int RM_ELEMS = CUBE * RS;
   static constexpr int TR_ELEMS = D * TS;
+  __device__ static constexpr int sw(int d) { return WIDE ? ((d >> 3) & 15) : (((d >> 3) ^ d) & 15); }
 };
 
 template <typename T, int D, int NT>
@@ -215,7 +218,8 @@ __device__ __forceinline__ void tile_store_tr(const TileRegs<T, D, NT>& R, T* ld
         Vec4<T> c;
 #pragma unroll
         for (int r = 0; r < 4; ++r) c.v[r] = R.r[n][r].v[e];
-        store4(lds + (8 * cg + e) * TS + 4 * rg, c);
+        const int d = 8 * cg + e;
+        store4(lds + d * TS + 4 * (rg ^ TileGeom<T, D>::sw(d)), c);
       }
     }
   }
@@ -231,14 +235,79 @@ __device__ __forceinline__ Frag<T> frag_rm(const T* lds, int row, int ks, int g)
 // map over token chunk c (32 tokens).
 template <typename T, int D>
 __device__ __forceinline__ Frag<T> frag_tr(const T* lds, int drow, int c, int g) {
-  const T* p = lds + drow * TileGeom<T, D>::TS + 32 * c + 4 * g;
-  return frag_from44(load4(p), load4(p + 16));
+  const T* row = lds + drow * TileGeom<T, D>::TS;
+  const int s = TileGeom<T, D>::sw(drow);
+  return frag_from44(load4(row + 4 * ((8 * c + g) ^ s)), load4(row + 4 * ((8 * c + 4 + g) ^ s)));
 }
 
 // Fragment straight from global memory: row `row` of a row-major [*, D] array.
 template <typename T, int D>
 __device__ __forceinline__ Frag<T> frag_global(const T* __restrict__ base, int row, int ks, int g) {
   return frag_from8(load8(base + (size_t)row * D + 32 * ks + 8 * g));
+}
+
+// ---------------------------------------------------------------------------
+// Chunk-swizzled LDS tiles (R rows x W elements, stored as a contiguous R*W
+// block in global memory).  Thread t loads the 16-byte chunks t + NT*n of the
+// tile (coalesced) and stores logical chunk ch of row r at physical chunk
+// ch ^ f(r) of that row; a wave's stores cover whole rows, so they never
+// conflict.  f spreads
+// the 16 rows of a fragment read over all banks (checked with a 32- and a
+// 64-bank model for every tile shape used):
+//   f(r) = r & 15 when a row has >= 16 chunks, else (r & 7) ^ ((r >> 3) & 1).
+// ---------------------------------------------------------------------------
+template <typename T, int W> struct SwTile {
+  static constexpr int NCH = W * (int)sizeof(T) / 16;  // 16-byte chunks per row
+  static constexpr int EPC = 16 / (int)sizeof(T);      // elements per chunk
+  __device__ static constexpr int f(int r) { return NCH >= 16 ? (r & 15) : ((r & 7) ^ ((r >> 3) & 1)); }
+  __device__ static constexpr int off(int r, int ch) { return r * W + EPC * (ch ^ (f(r) & (NCH - 1))); }
+};
+
+template <int R, int W, typename T, int NT> struct SwRegs {
+  static constexpr int N = R * SwTile<T, W>::NCH / NT;
+  static_assert(N * NT == R * SwTile<T, W>::NCH, "tile chunks must split evenly over the block");
+  uint4 c[N];
+};
+
+// Global -> registers, linear chunk order (chunk p = tid + NT*n, fully
+// coalesced); rows >= valid_rows read as zero.
+template <int R, int W, typename T, int NT>
+__device__ __forceinline__ void sw_load(SwRegs<R, W, T, NT>& g, const T* __restrict__ src, int tid, int valid_rows) {
+  using S = SwTile<T, W>;
+  constexpr int RSTEP = NT / S::NCH;
+  static_assert(NT % S::NCH == 0, "a block must cover whole rows");
+  const int r0 = tid / S::NCH;
+  const uint4* s4 = reinterpret_cast<const uint4*>(src) + tid;
+#pragma unroll
+  for (int n = 0; n < SwRegs<R, W, T, NT>::N; ++n)
+    g.c[n] = (r0 + RSTEP * n) < valid_rows ? s4[NT * n] : make_uint4(0, 0, 0, 0);
+}
+// Registers -> LDS at the swizzled position of each chunk.
+template <int R, int W, typename T, int NT>
+__device__ __forceinline__ void sw_store(const SwRegs<R, W, T, NT>& g, T* lds, int tid) {
+  using S = SwTile<T, W>;
+  constexpr int RSTEP = NT / S::NCH;
+  const int r0 = tid / S::NCH, ch = tid % S::NCH;
+#pragma unroll
+  for (int n = 0; n < SwRegs<R, W, T, NT>::N; ++n) {
+    const int r = r0 + RSTEP * n;
+    *reinterpret_cast<uint4*>(lds + r * W + S::EPC * (ch ^ (S::f(r) & (S::NCH - 1)))) = g.c[n];
+  }
+}
+// MFMA fragment (8 elements = k-slots (g, 0..7)) of row r, k-step s of a swizzled tile.
+template <typename T, int W>
+__device__ __forceinline__ Frag<T> sw_frag(const T* lds, int r, int s, int g) {
+  using S = SwTile<T, W>;
+  if constexpr (sizeof(T) == 2) {
+    return frag_from8(load8(lds + S::off(r, 4 * s + g)));
+  } else {
+    Vec8<T> v;
+    const Vec4<T> a = load4(lds + S::off(r, 8 * s + 2 * g));
+    const Vec4<T> b = load4(lds + S::off(r, 8 * s + 2 * g + 1));
+#pragma unroll
+    for (int e = 0; e < 4; ++e) { v.v[e] = a.v[e]; v.v[4 + e] = b.v[e]; }
+    return frag_from8(v);
+  }
 }
 
 // Butterfly reductions over the four slot groups (lanes c, c+16, c+32, c+48).
