@@ -321,6 +321,7 @@ int vsa2_sparse_attn_fwd(const vsa2_problem* p, int32_t topk, const void* q, con
   a.kph = budget(d, topk);
   a.d = d.d; a.bf16 = d.bf16; a.dense = false;
   a.scale_log2 = d.scale * 1.4426950408889634f;
+  a.ct = p->lat_t / 4; a.cy = p->lat_y / 4; a.cx = p->lat_x / 4;
   return hip_status(launch_attn_fwd(a, (hipStream_t)stream));
 }
 
@@ -354,6 +355,7 @@ int vsa2_sparse_attn_bwd(const vsa2_problem* p, int32_t topk, const void* q, con
   a.d = d.d; a.bf16 = d.bf16; a.dense = false;
   a.scale = d.scale;
   a.scale_log2 = d.scale * 1.4426950408889634f;
+  a.ct = p->lat_t / 4; a.cy = p->lat_y / 4; a.cx = p->lat_x / 4;
   hipError_t e = launch_bwd_delta(a, (float*)ws, st);
   if (e != hipSuccess) return VSA2_E_HIP;
   return hip_status(launch_attn_bwd(a, st));

@@ -52,11 +52,12 @@ __global__ __launch_bounds__(128, 2) void k_attn_fwd(const T* __restrict__ q, co
                                                   const T* __restrict__ vt, const int32_t* __restrict__ row_ptr,
                                                   const int32_t* __restrict__ col_idx, TO* __restrict__ o,
                                                   float* __restrict__ lse, int nq, int nkv, int seq, int ld,
-                                                  int out_rows, int64_t kph, float c) {
+                                                  int out_rows, int64_t kph, float c, int ct, int cy, int cx) {
   __shared__ __align__(16) T ks[64 * D];
   __shared__ __align__(16) T vs[D * 64];
   int bh, i;
   if (!xcd_work(blockIdx.x, nq, bh, i)) return;
+  if (ct > 0) i = blocked_cube(i, ct, cy, cx);
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, cc = lane & 15;
   const size_t hoff = (size_t)bh * ld * D;
   const T* kbase = k + hoff;
@@ -99,8 +100,8 @@ __global__ __launch_bounds__(128, 2) void k_attn_fwd(const T* __restrict__ q, co
     SwRegs<64, D, T, 128> kr;
     SwRegs<D, 64, T, 128> vr;
     int j = cube_at(0);
-    sw_load(kr, kbase + (size_t)max(j, 0) * 64 * D, tid, kv_limit(j));
-    sw_load(vr, vbase + (size_t)max(j, 0) * 64 * D, tid, j >= 0 ? D : 0);
+    sw_load(kr, kbase + (size_t)max(j, 0) * 64 * D, tid);
+    sw_load(vr, vbase + (size_t)max(j, 0) * 64 * D, tid);
     for (int n = 0; n < cnt; ++n) {
       sw_store(kr, ks, tid);
       sw_store(vr, vs, tid);
@@ -108,15 +109,19 @@ __global__ __launch_bounds__(128, 2) void k_attn_fwd(const T* __restrict__ q, co
       const int lim = kv_limit(j);
       if (n + 1 < cnt) {
         j = cube_at(n + 1);
-        sw_load(kr, kbase + (size_t)max(j, 0) * 64 * D, tid, kv_limit(j));
-        sw_load(vr, vbase + (size_t)max(j, 0) * 64 * D, tid, j >= 0 ? D : 0);
+        sw_load(kr, kbase + (size_t)max(j, 0) * 64 * D, tid);
+        sw_load(vr, vbase + (size_t)max(j, 0) * 64 * D, tid);
       }
       // S^T = K Q^T: acc[kb][qb] holds keys 16kb + 4g + r of query 16qb + cc (of this wave)
       f32x4 acc[4][2];
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) acc[kb][0] = acc[kb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int kb = 0; kb < 4; ++kb) {
+        const Frag<T> a = sw_frag<T, D>(ks, 16 * kb + cc, 0, g);
+        acc[kb][0] = mma0(a, qf[0][0]);
+        acc[kb][1] = mma0(a, qf[1][0]);
+      }
 #pragma unroll
-      for (int s = 0; s < D / 32; ++s)
+      for (int s = 1; s < D / 32; ++s)
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
           const Frag<T> a = sw_frag<T, D>(ks, 16 * kb + cc, s, g);
@@ -130,6 +135,8 @@ __global__ __launch_bounds__(128, 2) void k_attn_fwd(const T* __restrict__ q, co
           for (int r = 0; r < 4; ++r)
             if (16 * kb + 4 * g + r >= lim) acc[kb][0][r] = acc[kb][1][r] = -INFINITY;
       }
+      // lane-local maxima; the 4-lane reduction only runs when a lane asks to
+      // move its reference maximum (lazy rescale, exponentials stay <= 2^8)
       float mt[2];
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
@@ -138,21 +145,19 @@ __global__ __launch_bounds__(128, 2) void k_attn_fwd(const T* __restrict__ q, co
         for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
           for (int r = 0; r < 4; ++r) x = fmaxf(x, acc[kb][qb][r]);
-        mt[qb] = group_max(x);
+        mt[qb] = x;
       }
-      // lazy rescale: move the reference max only when the tile exceeds it by > 2^8
-      const bool up0 = mt[0] * c > m[0] * c + 8.f, up1 = mt[1] * c > m[1] * c + 8.f;
-      if (__ballot(up0 || up1)) {
-        const float n0 = up0 ? mt[0] : m[0], n1 = up1 ? mt[1] : m[1];
-        const float a0 = fast_exp2((m[0] - n0) * c), a1 = fast_exp2((m[1] - n1) * c);
-        m[0] = n0;
-        m[1] = n1;
-        l[0] *= a0;
-        l[1] *= a1;
+      if (__ballot(mt[0] * c > m[0] * c + 8.f || mt[1] * c > m[1] * c + 8.f)) {
 #pragma unroll
-        for (int db = 0; db < D / 16; ++db) {
-          oacc[db][0] *= a0;
-          oacc[db][1] *= a1;
+        for (int qb = 0; qb < 2; ++qb) {
+          const float gm = group_max(mt[qb]);
+          if (gm * c > m[qb] * c + 8.f) {
+            const float alpha = fast_exp2((m[qb] - gm) * c);
+            m[qb] = gm;
+            l[qb] *= alpha;
+#pragma unroll
+            for (int db = 0; db < D / 16; ++db) oacc[db][qb] *= alpha;
+          }
         }
       }
       Frag<T> pf[2][2];
@@ -213,11 +218,11 @@ hipError_t launch_fwd_t(const AttnArgs& a, hipStream_t st) {
   if (a.dense) {
     hipLaunchKernelGGL((k_attn_fwd<T, float, D, true>), grid, dim3(128), 0, st, (const T*)a.q, (const T*)a.k,
                        (const T*)a.vt, nullptr, nullptr, (float*)a.o, a.lse, a.nq, a.nkv, a.seq, a.ld, a.out_rows,
-                       a.kph, a.scale_log2);
+                       a.kph, a.scale_log2, 0, 0, 0);
   } else {
     hipLaunchKernelGGL((k_attn_fwd<T, T, D, false>), grid, dim3(128), 0, st, (const T*)a.q, (const T*)a.k,
                        (const T*)a.vt, a.row_ptr, a.col_idx, (T*)a.o, a.lse, a.nq, a.nkv, a.seq, a.ld, a.out_rows,
-                       a.kph, a.scale_log2);
+                       a.kph, a.scale_log2, a.ct, a.cy, a.cx);
   }
   return hipGetLastError();
 }

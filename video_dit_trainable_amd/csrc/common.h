@@ -46,6 +46,17 @@ __device__ __forceinline__ void mma(f32x4& c, const Frag<float>& a, const Frag<f
   for (int e = 0; e < 8; ++e) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[e], b.v[e], c, 0, 0, 0);
 }
 
+// product with a zero accumulator (lets the compiler use the inline constant)
+__device__ __forceinline__ f32x4 mma0(const Frag<bf16>& a, const Frag<bf16>& b) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, b.v, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma0(const Frag<float>& a, const Frag<float>& b) {
+  f32x4 c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[0], b.v[0], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+#pragma unroll
+  for (int e = 1; e < 8; ++e) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[e], b.v[e], c, 0, 0, 0);
+  return c;
+}
+
 template <typename T> __device__ __forceinline__ T from_f32(float x);
 template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
 template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }
@@ -251,36 +262,41 @@ __device__ __forceinline__ Frag<T> frag_global(const T* __restrict__ base, int r
 // block in global memory).  Thread t loads the 16-byte chunks t + NT*n of the
 // tile (coalesced) and stores logical chunk ch of row r at physical chunk
 // ch ^ f(r) of that row; a wave's stores cover whole rows, so they never
-// conflict.  f spreads
-// the 16 rows of a fragment read over all banks (checked with a 32- and a
-// 64-bank model for every tile shape used):
-//   f(r) = r & 15 when a row has >= 16 chunks, else (r & 7) ^ ((r >> 3) & 1).
+// conflict.  f spreads both fragment reads over the banks: the 16-byte reads
+// of 16 consecutive rows (one chunk each) and the 8-byte transposing reads of
+// 4 rows x 4 runs (ds_read_b64_tr_b16).  With a 32- and a 64-bank model both
+// are conflict-free for every tile shape used (bf16 rows of 64 elements:
+// transposing reads 2-way under the 32-bank model only):
+//   16+ chunks per row: f(r) = (((r & 3) << 1) | 9 * ((r >> 2) & 1)) ^ ((r >> 3) & 1)
+//   8 chunks per row:   f(r) = (r & 7) ^ ((r >> 3) & 1)
 // ---------------------------------------------------------------------------
 template <typename T, int W> struct SwTile {
   static constexpr int NCH = W * (int)sizeof(T) / 16;  // 16-byte chunks per row
   static constexpr int EPC = 16 / (int)sizeof(T);      // elements per chunk
-  __device__ static constexpr int f(int r) { return NCH >= 16 ? (r & 15) : ((r & 7) ^ ((r >> 3) & 1)); }
+  __device__ static constexpr int f(int r) {
+    return NCH >= 16 ? ((((r & 3) << 1) | (((r >> 2) & 1) * 9)) ^ ((r >> 3) & 1)) : ((r & 7) ^ ((r >> 3) & 1));
+  }
   __device__ static constexpr int off(int r, int ch) { return r * W + EPC * (ch ^ (f(r) & (NCH - 1))); }
 };
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 template <int R, int W, typename T, int NT> struct SwRegs {
   static constexpr int N = R * SwTile<T, W>::NCH / NT;
   static_assert(N * NT == R * SwTile<T, W>::NCH, "tile chunks must split evenly over the block");
-  uint4 c[N];
+  u32x4 c[N];
 };
 
 // Global -> registers, linear chunk order (chunk p = tid + NT*n, fully
-// coalesced); rows >= valid_rows read as zero.
+// coalesced).  The whole tile is always read: callers point masked tiles at
+// valid memory and mask their scores instead.
 template <int R, int W, typename T, int NT>
-__device__ __forceinline__ void sw_load(SwRegs<R, W, T, NT>& g, const T* __restrict__ src, int tid, int valid_rows) {
+__device__ __forceinline__ void sw_load(SwRegs<R, W, T, NT>& g, const T* __restrict__ src, int tid) {
   using S = SwTile<T, W>;
-  constexpr int RSTEP = NT / S::NCH;
   static_assert(NT % S::NCH == 0, "a block must cover whole rows");
-  const int r0 = tid / S::NCH;
-  const uint4* s4 = reinterpret_cast<const uint4*>(src) + tid;
+  const u32x4* s4 = reinterpret_cast<const u32x4*>(src) + tid;
 #pragma unroll
-  for (int n = 0; n < SwRegs<R, W, T, NT>::N; ++n)
-    g.c[n] = (r0 + RSTEP * n) < valid_rows ? s4[NT * n] : make_uint4(0, 0, 0, 0);
+  for (int n = 0; n < SwRegs<R, W, T, NT>::N; ++n) g.c[n] = s4[NT * n];
 }
 // Registers -> LDS at the swizzled position of each chunk.
 template <int R, int W, typename T, int NT>
@@ -291,7 +307,7 @@ __device__ __forceinline__ void sw_store(const SwRegs<R, W, T, NT>& g, T* lds, i
 #pragma unroll
   for (int n = 0; n < SwRegs<R, W, T, NT>::N; ++n) {
     const int r = r0 + RSTEP * n;
-    *reinterpret_cast<uint4*>(lds + r * W + S::EPC * (ch ^ (S::f(r) & (S::NCH - 1)))) = g.c[n];
+    *reinterpret_cast<u32x4*>(lds + r * W + S::EPC * (ch ^ (S::f(r) & (S::NCH - 1)))) = g.c[n];
   }
 }
 // MFMA fragment (8 elements = k-slots (g, 0..7)) of row r, k-step s of a swizzled tile.
@@ -308,6 +324,41 @@ __device__ __forceinline__ Frag<T> sw_frag(const T* lds, int r, int s, int g) {
     for (int e = 0; e < 4; ++e) { v.v[e] = a.v[e]; v.v[4 + e] = b.v[e]; }
     return frag_from8(v);
   }
+}
+
+// Transposed MFMA fragment from a swizzled row-major tile: lane (g, c) gets
+// tile[r0 + pi(g, e)][col0 + c] for the 8 slots e, i.e. the A operand whose
+// rows are tile columns and whose contraction runs over 32 tile rows r0.. .
+// bf16: two ds_read_b64_tr_b16.  Within each 16-lane group that instruction
+// returns to lane i, element e, the element i % 4 of the 8 bytes addressed by
+// lane 4e + i / 4; so lane j addresses row r0 + 4g + j / 4 (+16 for the upper
+// 4 slots), columns col0 + 4 (j % 4) .. +3.  fp32: eight scalar reads.
+#define VSA2_LDS __attribute__((address_space(3)))
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+template <typename T, int W>
+__device__ __forceinline__ Frag<T> sw_frag_tr(const T* lds, int r0, int col0, int g, int c) {
+  using S = SwTile<T, W>;
+  Frag<T> f;
+  if constexpr (sizeof(T) == 2) {
+    const int col = col0 + 4 * (c & 3);
+    const int ra = r0 + 4 * g + (c >> 2), rb = ra + 16;
+    const T* pa = lds + S::off(ra, col / S::EPC) + (col % S::EPC);
+    const T* pb = lds + S::off(rb, col / S::EPC) + (col % S::EPC);
+    const s16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((VSA2_LDS s16x4*)(pa));
+    const s16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((VSA2_LDS s16x4*)(pb));
+    Vec8<T> v;
+    __builtin_memcpy(&v.v[0], &va, 8);
+    __builtin_memcpy(&v.v[4], &vb, 8);
+    f = frag_from8(v);
+  } else {
+    const int col = col0 + c;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int r = r0 + (e < 4 ? 4 * g + e : 16 + 4 * g + e - 4);
+      f.v[e] = lds[S::off(r, col / S::EPC) + (col % S::EPC)];
+    }
+  }
+  return f;
 }
 
 // Butterfly reductions over the four slot groups (lanes c, c+16, c+32, c+48).
@@ -332,6 +383,40 @@ __device__ __forceinline__ bool xcd_work(int bid, int items_per_bh, int& bh, int
   item = xcd * per + (s - bh * per);
   return item < items_per_bh;
 }
+// Visiting order of the cubes of one head: 4x4x4 blocks of cubes in raster
+// order, cubes inside a block in raster order (edge blocks are smaller).
+// Maps position p in [0, ct*cy*cx) to a cube index (c_t * cy + c_y) * cx + c_x,
+// so consecutive positions are spatial neighbours in all three axes.
+__host__ __device__ inline int blocked_cube(int p, int ct, int cy, int cx) {
+  constexpr int B = 4;
+  int t0 = 0;
+  for (;;) {  // t-slab
+    const int st = min(B, ct - t0), slab = st * cy * cx;
+    if (p < slab || t0 + st >= ct) break;
+    p -= slab;
+    t0 += st;
+  }
+  const int st = min(B, ct - t0);
+  int y0 = 0;
+  for (;;) {  // y-row of blocks inside the slab
+    const int sy = min(B, cy - y0), row = st * sy * cx;
+    if (p < row || y0 + sy >= cy) break;
+    p -= row;
+    y0 += sy;
+  }
+  const int sy = min(B, cy - y0);
+  int x0 = 0;
+  for (;;) {  // block inside the row
+    const int sx = min(B, cx - x0), blk = st * sy * sx;
+    if (p < blk || x0 + sx >= cx) break;
+    p -= blk;
+    x0 += sx;
+  }
+  const int sx = min(B, cx - x0);
+  const int dx = p % sx, dy = (p / sx) % sy, dt = p / (sx * sy);
+  return ((t0 + dt) * cy + (y0 + dy)) * cx + (x0 + dx);
+}
+
 __host__ __device__ inline int xcd_grid(int items_per_bh, int bh_total) {
   return 8 * ((items_per_bh + 7) >> 3) * bh_total;
 }

@@ -60,6 +60,7 @@ struct AttnArgs {
   int d;
   bool bf16, dense;
   float scale_log2;
+  int ct, cy, cx;                     // cube grid for the blocked visiting order (0 = linear)
 };
 hipError_t launch_attn_fwd(const AttnArgs& a, hipStream_t st);
 
@@ -76,6 +77,7 @@ struct AttnBwdArgs {
   bool bf16, dense;
   float scale;
   float scale_log2;
+  int ct, cy, cx;                     // cube grid for the blocked visiting order (0 = linear)
 };
 hipError_t launch_bwd_delta(const AttnBwdArgs& a, float* delta, hipStream_t st);
 hipError_t launch_attn_bwd(const AttnBwdArgs& a, hipStream_t st);
