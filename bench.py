@@ -24,12 +24,21 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 from video_dit_trainable_amd import vsa2  # noqa: E402
-from video_dit_trainable_amd.configs import WORKLOADS, flops  # noqa: E402
+from video_dit_trainable_amd.configs import WORKLOADS, flops, kernel_flops  # noqa: E402
 from video_dit_trainable_amd.inputs import (make_gate_inputs, make_grad_out, make_qkv,  # noqa: E402
                                             make_selection)
 
 PEAK_BF16 = 2.5e15      # MI355X dense bf16 MFMA, FLOP/s
 PEAK_HBM = 8.0e12       # MI355X HBM3E, B/s
+
+# kernels timed live with the library's event hooks, and their symbol names
+TIMED = {"fine_fwd": (vsa2.K_FINE_FWD, "k_attn_fwd"), "bwd_dkdv": (vsa2.K_BWD_DKDV, "k_bwd_dkdv"),
+         "bwd_dq": (vsa2.K_BWD_DQ, "k_bwd_dq"), "router_lse": (vsa2.K_ROUTER_LSE, "k_router (pass 1)"),
+         "router_scores": (vsa2.K_ROUTER_SCORES, "k_router (pass 2)")}
+# kernel source each timed kernel is built from (hashed to tell whether stored counters are current)
+SOURCES = {"fine_fwd": "attn_fwd.hip", "bwd_dkdv": "attn_bwd.hip", "bwd_dq": "attn_bwd.hip",
+           "router_lse": "router.hip", "router_scores": "router.hip"}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 
 
 def log(msg):
@@ -38,37 +47,81 @@ def log(msg):
 
 def cpu_baseline(w, q, k, v, d_o, budget_s=20.0):
     """The oracle on a bounded sample of the same workload (head 0): router
-    rows of 32 query cubes, then fine forward + backward of 16 query cubes on a
-    seeded selection with the workload's budget.  FLOPs use the GPU's
-    algorithmic accounting; the rate is scaled to TFLOP/s."""
+    rows of spread-out query cubes, then fine forward + backward of query cubes
+    on a seeded selection with the workload's budget, each part grown in
+    batches until it has used about half of `budget_s`.  FLOPs use the GPU's
+    algorithmic accounting (router pass + fine forward + backward of the
+    sampled rows); the rate is in TFLOP/s."""
     from threadpoolctl import threadpool_info
 
     from oracle import vsa2_oracle as orc
 
     f64 = lambda t: t.float().cpu().double().numpy()
     qh, kh, vh, doh = f64(q[0, 0]), f64(k[0, 0]), f64(v[0, 0]), f64(d_o[0, 0])
-    rows = np.arange(32) * (w.nb // 32)
-    t0 = time.perf_counter()
-    orc.router_scores(qh, kh, w.grid, bf16_pooled=True, rows=rows)
-    t_router = time.perf_counter() - t0
     lr = w.L // 8
-    fl = len(rows) * 8 * 2 * 2 * lr * w.head_dim
+    order = np.random.default_rng(0).permutation(w.nb)
+    n_router, t_router = 0, 0.0
+    while t_router < budget_s / 2 and n_router < w.nb:
+        rows = np.sort(order[n_router:n_router + 32])
+        t0 = time.perf_counter()
+        orc.router_scores(qh, kh, w.grid, bf16_pooled=True, rows=rows)
+        t_router += time.perf_counter() - t0
+        n_router += len(rows)
+    fl = n_router * 8 * 2 * 2 * lr * w.head_dim
     rp, ci = make_selection(w)
     mask = orc.csr_to_mask(rp[0, 0].numpy(), ci[0, 0].numpy(), w.nb)
-    cubes = [i for i in range(w.nb) if mask[i].any()][:: max(1, w.nb // 16)][:16]
-    sub = np.zeros_like(mask)
-    sub[cubes] = mask[cubes]
-    t0 = time.perf_counter()
-    orc.fine_forward(qh, kh, vh, sub, rows=cubes)
-    orc.fine_backward(qh, kh, vh, sub, doh)
-    t_fine = time.perf_counter() - t0
-    fl += int(sub.sum()) * 4 * 64 * 64 * w.head_dim * 7 // 2
+    live = [int(i) for i in order if mask[i].any()]
+    n_fine, pairs, t_fine = 0, 0, 0.0
+    while t_fine < budget_s / 2 and n_fine < len(live):
+        cubes = sorted(live[n_fine:n_fine + 16])
+        sub = np.zeros_like(mask)
+        sub[cubes] = mask[cubes]
+        t0 = time.perf_counter()
+        orc.fine_forward(qh, kh, vh, sub, rows=cubes)
+        orc.fine_backward(qh, kh, vh, sub, doh)
+        t_fine += time.perf_counter() - t0
+        n_fine += len(cubes)
+        pairs += int(sub.sum())
+    fl += pairs * 4 * 64 * 64 * w.head_dim * 7 // 2
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     secs = t_router + t_fine
     return {"value": fl / secs / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"head 0 of the same inputs: router rows of {len(rows)} query cubes + fine fwd+bwd of "
-                      f"{len(cubes)} query cubes ({int(sub.sum())} selected pairs); {secs:.1f} s on the host",
+            "sample": f"head 0 of the same inputs: router rows of {n_router} query cubes ({t_router:.1f} s) + "
+                      f"fine fwd+bwd of {n_fine} query cubes, {pairs} selected pairs ({t_fine:.1f} s); fp64 numpy",
             "seconds": round(secs, 2)}
+
+
+def source_hash(kernel):
+    import hashlib
+    h = hashlib.sha256()
+    for name in (SOURCES[kernel], "common.h"):
+        with open(os.path.join(ROOT, "video_dit_trainable_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(kernel, workload):
+    """HBM bytes per launch of `kernel` from the committed counter summary, or
+    None when there is none or the kernel's source has changed since."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f).get(f"{kernel}/{workload}")
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_sha256_16") != source_hash(kernel):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def copy_calibration(dev):
+    """A plain device copy of known size (256 MiB read + 256 MiB written), for
+    scaling the FETCH_SIZE / WRITE_SIZE counters to bytes."""
+    n = 64 << 20
+    a = torch.randn(n, device=dev)
+    b = torch.empty_like(a)
+    torch.neg(a, out=b)
+    torch.cuda.synchronize()
+    log(f"copy calibration: torch.neg over {n * 4} bytes read and {n * 4} bytes written")
 
 
 def main():
@@ -78,6 +131,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="train720")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one plain copy kernel of known size (for counter scaling)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the layer shards by head "
@@ -97,15 +152,13 @@ def main():
     st = torch.cuda.current_stream()
     names = ["pool", "route", "topk", "fine_fwd", "coarse_gate", "coarse_gate_bwd", "fine_bwd"]
 
-    # allocate gradient buffers once (outside the timed region)
-    layer.backward(q, k, v, x, w_g, d_o)
+    gr = layer.grads()      # allocated once, outside the timed region
     torch.cuda.synchronize()
 
     def step_full(ev=None):
         def mark(i):
             if ev is not None:
                 ev[i].record(st)
-        gr = layer._grads
         mark(0)
         vsa2.vsa2_pool(p, q, k, v, layer.pooled)
         mark(1)
@@ -137,11 +190,19 @@ def main():
     t_start = torch.cuda.Event(enable_timing=True)
     t_stop = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
+    for kid, _ in TIMED.values():
+        vsa2.kernel_timer_start(kid, args.steps)
     t_start.record(st)
     for s in range(args.steps):
         step_full(evs[s])
     t_stop.record(st)
     torch.cuda.synchronize()
+    kern = {}
+    for name, (kid, _) in TIMED.items():
+        ms, n = vsa2.kernel_timer_stop(kid)
+        if n:
+            kern[name] = ms / n
+    log("per-kernel ms: " + ", ".join(f"{n} {t:.3f}" for n, t in kern.items()))
     total_ms = t_start.elapsed_time(t_stop)
     ms_step = total_ms / args.steps
     per = {n: float(np.median([evs[s][i].elapsed_time(evs[s][i + 1]) for s in range(args.steps)]))
@@ -154,12 +215,16 @@ def main():
         step_flops += fl["fine_bwd"] + fl["coarse_bwd"] + fl["gate_bwd"]
     value = step_flops / (ms_step * 1e-3) / 1e12
 
-    # roofline of the fine-branch forward kernel (one launch per vsa2_sparse_attn_fwd call)
-    fwd_ms = per["fine_fwd"]
-    achieved = fl["fine_fwd"] / (fwd_ms * 1e-3) / 1e12
-    roof = {"kernel": "k_attn_fwd (fine branch forward)", "bound": "mfma", "achieved": round(achieved, 2),
+    # roofline of the dominant kernel: the timed kernel with the longest average launch
+    kfl = kernel_flops(w)
+    dom = max(kern, key=kern.get)
+    achieved = kfl[dom] / (kern[dom] * 1e-3) / 1e12
+    roof = {"kernel": TIMED[dom][1], "bound": "mfma", "achieved": round(achieved, 2),
             "peak": PEAK_BF16 / 1e12, "unit": "TFLOP/s", "frac": round(achieved / (PEAK_BF16 / 1e12), 4),
-            "traffic": None}
+            "traffic": stored_traffic(dom, w.name), "avg_launch_ms": round(kern[dom], 4),
+            "flops_per_launch": kfl[dom]}
+    kernels = {n: {"ms": round(t, 4), "tflops": round(kfl[n] / (t * 1e-3) / 1e12, 2),
+                   "pct_bf16_peak": round(100 * kfl[n] / (t * 1e-3) / PEAK_BF16, 2)} for n, t in kern.items()}
 
     ops = {n: {"ms": round(t, 4)} for n, t in per.items()}
     for n, key in (("fine_fwd", "fine_fwd"), ("fine_bwd", "fine_bwd"), ("route", "router")):
@@ -167,6 +232,9 @@ def main():
         ops[n]["pct_bf16_peak"] = round(100 * fl[key] / (per[n] * 1e-3) / PEAK_BF16, 2)
     nbytes_scores = w.batch * w.heads * w.nb * w.nb * 4
     ops["topk"]["gbps_scores_pass"] = round(nbytes_scores / (per["topk"] * 1e-3) / 1e9, 1)
+
+    if args.copy_calibration:
+        copy_calibration(dev)
 
     cpu = None
     if not args.no_cpu:
@@ -193,6 +261,7 @@ def main():
                    "topk": w.topk, "parallelism": "single GPU"},
         "step_flops": step_flops,
         "ops": ops,
+        "kernels": kernels,
         "roofline": roof,
         "cpu_baseline": cpu,
     }

@@ -182,6 +182,29 @@ int vsa2_coarse_gate_bwd(const vsa2_problem* p, const void* pooled, const void* 
                          const float* w_g, const float* saved, const void* d_o,
                          float* dqkv_c, void* dx, float* dw_g, void* ws, size_t ws_bytes, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * Diagnostic kernel timer (for benchmarks and tests, not for production use).
+ * vsa2_kernel_timer_start(kernel, capacity): from now on every launch of the
+ * given kernel records one HIP event on its launch stream right before the
+ * launch and one right after, for at most `capacity` launches (capacity in
+ * 1..4096; events are created once and reused).  Several kernels may be
+ * armed at the same time.
+ * vsa2_kernel_timer_stop(kernel, ms, launches): waits for the last recorded
+ * event of that kernel, writes the summed launch durations in milliseconds
+ * and the number of launches timed, and disarms it.
+ * Not thread-safe: arm, run and stop from one host thread.
+ * ------------------------------------------------------------------------- */
+enum vsa2_kernel {
+  VSA2_K_FINE_FWD = 0,        /* block-sparse attention forward (fine branch)         */
+  VSA2_K_BWD_DKDV = 1,        /* fine-branch dK/dV (KV-cube major)                    */
+  VSA2_K_BWD_DQ = 2,          /* fine-branch dQ (query-cube major)                    */
+  VSA2_K_ROUTER_LSE = 3,      /* router pass 1: log-sum-exp of every pooled query     */
+  VSA2_K_ROUTER_SCORES = 4,   /* router pass 2: softmax + 8x8 block mean              */
+  VSA2_K_COUNT = 5
+};
+int vsa2_kernel_timer_start(int32_t kernel, int32_t capacity);
+int vsa2_kernel_timer_stop(int32_t kernel, float* ms, int32_t* launches);
+
 #ifdef __cplusplus
 }
 #endif

@@ -113,3 +113,14 @@ def test_scalar_arguments():
     assert L.vsa2_coarse_gate(ctypes.byref(p), A, B, 100, C, D, A, B, C, 1 << 30, None) == vsa2.VSA2_E_SHAPE
     many = _prob(heads=65)
     assert L.vsa2_coarse_gate(ctypes.byref(many), A, B, 128, C, D, A, B, C, 1 << 30, None) == vsa2.VSA2_E_UNSUPPORTED
+
+
+def test_kernel_timer_arguments():
+    lib = vsa2.lib()
+    assert lib.vsa2_kernel_timer_start(-1, 4) == vsa2.VSA2_E_ARG
+    assert lib.vsa2_kernel_timer_start(vsa2.K_FINE_FWD, 0) == vsa2.VSA2_E_ARG
+    assert lib.vsa2_kernel_timer_start(vsa2.K_FINE_FWD, 5000) == vsa2.VSA2_E_ARG
+    assert lib.vsa2_kernel_timer_start(99, 4) == vsa2.VSA2_E_ARG
+    # armed but never launched: stopping reads no event and reports nothing timed
+    assert lib.vsa2_kernel_timer_start(vsa2.K_BWD_DKDV, 4) == vsa2.VSA2_OK
+    assert vsa2.kernel_timer_stop(vsa2.K_BWD_DKDV) == (0.0, 0)

@@ -197,6 +197,19 @@ def test_fine_forward_full_budget_is_dense_attention():
         gu.assert_close_bf16(gu.f64(layer.o_f[0, h]), want, f"dense O head {h}")
 
 
+def test_kernel_timer_counts_launches():
+    w = MID
+    (q, k, v, x, w_g), (qd, kd, vd, xd, wd), layer = _setup(w)
+    layer.set_selection(*make_selection(w, device=_dev()))
+    vsa2.kernel_timer_start(vsa2.K_FINE_FWD, 2)
+    for _ in range(3):      # the third launch is past the capacity and is not timed
+        vsa2.vsa2_sparse_attn_fwd(layer.p, w.topk, qd, kd, vd, layer.row_ptr, layer.col_idx, layer.o_f, layer.lse,
+                                  layer.ws)
+    ms, n = vsa2.kernel_timer_stop(vsa2.K_FINE_FWD)
+    assert n == 2 and ms > 0
+    assert vsa2.kernel_timer_stop(vsa2.K_FINE_FWD) == (0.0, 0)     # disarmed
+
+
 # ----------------------------------------------------------------------------- coarse + gate
 @pytest.mark.parametrize("zero_gate", [True, False])
 @pytest.mark.parametrize("w", [TINY, MID, RAGGED, RAGGED32], ids=lambda w: w.name)

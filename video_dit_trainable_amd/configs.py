@@ -83,3 +83,26 @@ def flops(w: Workload, topk=None):
         "gate_fwd": 2 * w.batch * w.L * w.d_model * w.heads,
         "gate_bwd": 4 * w.batch * w.L * w.d_model * w.heads,
     }
+
+
+def kernel_flops(w: Workload, topk=None):
+    """Algorithmic FLOPs credited to each timed kernel of one call.
+
+    The fine backward's five GEMMs per selected pair are split between its two
+    kernels: the dK/dV kernel computes S^T, dP^T, dV and dK (four of them, 8 *
+    64^2 * d); the dQ kernel is credited with the dQ GEMM only (2 * 64^2 * d),
+    its recomputation of S and dP is not counted.  Each router pass is one
+    pooled GEMM of 2 * (L/8)^2 * d per (batch, head).
+    """
+    k = w.budget(topk)
+    bh = w.batch * w.heads
+    d = w.head_dim
+    lr = w.L // SUB
+    gemm = 2 * CUBE * CUBE * d
+    return {
+        "fine_fwd": bh * k * 2 * gemm,
+        "bwd_dkdv": bh * k * 4 * gemm,
+        "bwd_dq": bh * k * gemm,
+        "router_lse": bh * 2 * lr * lr * d,
+        "router_scores": bh * 2 * lr * lr * d,
+    }

@@ -169,9 +169,64 @@ Pooled pooled_ptrs(const Dims& d, const void* base) {
   return Pooled{b, b + r, b + 2 * r, b + 2 * r + c, b + 2 * r + 2 * c};
 }
 
+// Diagnostic kernel timer ----------------------------------------------------
+struct KernelTimer {
+  bool armed = false;
+  int capacity = 0, used = 0;
+  hipEvent_t ev[2 * 4096];
+  int created = 0;
+};
+KernelTimer g_timer[VSA2_K_COUNT];
+
 }  // namespace
 
+namespace vsa2 {
+void timer_before(int kid, hipStream_t st) {
+  KernelTimer& t = g_timer[kid];
+  if (!t.armed || t.used >= t.capacity) return;
+  const int i = 2 * t.used;
+  while (t.created < i + 2) {
+    if (hipEventCreate(&t.ev[t.created]) != hipSuccess) { t.armed = false; return; }
+    ++t.created;
+  }
+  (void)hipEventRecord(t.ev[i], st);
+}
+void timer_after(int kid, hipStream_t st) {
+  KernelTimer& t = g_timer[kid];
+  if (!t.armed || t.used >= t.capacity) return;
+  (void)hipEventRecord(t.ev[2 * t.used + 1], st);
+  ++t.used;
+}
+}  // namespace vsa2
+
 extern "C" {
+
+int vsa2_kernel_timer_start(int32_t kernel, int32_t capacity) {
+  if (kernel < 0 || kernel >= VSA2_K_COUNT || capacity < 1 || capacity > 4096) return VSA2_E_ARG;
+  KernelTimer& t = g_timer[kernel];
+  t.armed = true;
+  t.capacity = capacity;
+  t.used = 0;
+  return VSA2_OK;
+}
+
+int vsa2_kernel_timer_stop(int32_t kernel, float* ms, int32_t* launches) {
+  if (kernel < 0 || kernel >= VSA2_K_COUNT || !ms || !launches) return VSA2_E_ARG;
+  KernelTimer& t = g_timer[kernel];
+  float sum = 0.f;
+  int status = VSA2_OK;
+  if (t.used > 0 && hipEventSynchronize(t.ev[2 * t.used - 1]) != hipSuccess) status = VSA2_E_HIP;
+  for (int i = 0; status == VSA2_OK && i < t.used; ++i) {
+    float x = 0.f;
+    if (hipEventElapsedTime(&x, t.ev[2 * i], t.ev[2 * i + 1]) != hipSuccess) status = VSA2_E_HIP;
+    sum += x;
+  }
+  *ms = sum;
+  *launches = t.used;
+  t.armed = false;
+  t.used = 0;
+  return status;
+}
 
 const char* vsa2_status_string(int s) {
   switch (s) {

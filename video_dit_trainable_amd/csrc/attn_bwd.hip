@@ -396,16 +396,20 @@ hipError_t launch_bwd_delta(const AttnBwdArgs& a, float* delta, hipStream_t st) 
 
 template <typename T, typename TO, int D, bool DENSE>
 hipError_t launch_bwd_tt(const AttnBwdArgs& a, hipStream_t st) {
+  if (!DENSE) timer_before(TK_BWD_DKDV, st);
   hipLaunchKernelGGL((k_bwd_dkdv<T, TO, D, DENSE>), dim3(xcd_grid(a.nkv, a.bh)), dim3(128), 0, st, (const T*)a.q,
                      (const T*)a.k, (const T*)a.v, (const T*)a.d_o, a.lse, a.delta, a.col_ptr, a.row_idx, a.dk_add,
                      a.dv_add, (TO*)a.dk, (TO*)a.dv, a.nq, a.nkv, a.seq, a.ld, a.out_rows, a.lse_rows, a.kph, a.scale,
                      a.scale_log2, 0, 0, 0);
+  if (!DENSE) timer_after(TK_BWD_DKDV, st);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (!DENSE) timer_before(TK_BWD_DQ, st);
   hipLaunchKernelGGL((k_bwd_dq<T, TO, D, DENSE>), dim3(xcd_grid(a.nq, a.bh)), dim3(128), 0, st, (const T*)a.q,
                      (const T*)a.k, (const T*)a.v, (const T*)a.d_o, a.lse, a.delta, a.row_ptr, a.col_idx, a.dq_add,
                      (TO*)a.dq, a.nq, a.nkv, a.seq, a.ld, a.out_rows, a.lse_rows, a.kph, a.scale, a.scale_log2, a.ct,
                      a.cy, a.cx);
+  if (!DENSE) timer_after(TK_BWD_DQ, st);
   return hipGetLastError();
 }
 

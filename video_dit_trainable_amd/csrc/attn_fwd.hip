@@ -220,9 +220,11 @@ hipError_t launch_fwd_t(const AttnArgs& a, hipStream_t st) {
                        (const T*)a.vt, nullptr, nullptr, (float*)a.o, a.lse, a.nq, a.nkv, a.seq, a.ld, a.out_rows,
                        a.kph, a.scale_log2, 0, 0, 0);
   } else {
+    timer_before(TK_FINE_FWD, st);
     hipLaunchKernelGGL((k_attn_fwd<T, T, D, false>), grid, dim3(128), 0, st, (const T*)a.q, (const T*)a.k,
                        (const T*)a.vt, a.row_ptr, a.col_idx, (T*)a.o, a.lse, a.nq, a.nkv, a.seq, a.ld, a.out_rows,
                        a.kph, a.scale_log2, a.ct, a.cy, a.cx);
+    timer_after(TK_FINE_FWD, st);
   }
   return hipGetLastError();
 }

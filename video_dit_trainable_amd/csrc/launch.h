@@ -115,4 +115,9 @@ hipError_t launch_gate_bwd(const GateBwdArgs& a, hipStream_t st);
 
 hipError_t launch_fill_u32(uint32_t* p, uint32_t val, size_t n, hipStream_t st);
 
+// Diagnostic timer hooks (api.hip): bracket one launch of kernel `kid`.
+enum TimerKernel { TK_FINE_FWD = 0, TK_BWD_DKDV = 1, TK_BWD_DQ = 2, TK_ROUTER_LSE = 3, TK_ROUTER_SCORES = 4 };
+void timer_before(int kid, hipStream_t st);
+void timer_after(int kid, hipStream_t st);
+
 }  // namespace vsa2

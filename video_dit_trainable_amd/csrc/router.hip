@@ -119,12 +119,16 @@ template <typename T, int D>
 hipError_t launch_route_t(const RouteArgs& a, hipStream_t st) {
   const int ntile = (8 * a.nb + 63) / 64;
   dim3 grid(xcd_grid(ntile, a.bh));
+  timer_before(TK_ROUTER_LSE, st);
   hipLaunchKernelGGL((k_router<T, D, false>), grid, dim3(256), 0, st, (const T*)a.qr, (const T*)a.kr, a.lse2,
                      a.scores, a.nb, a.scale_log2);
+  timer_after(TK_ROUTER_LSE, st);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  timer_before(TK_ROUTER_SCORES, st);
   hipLaunchKernelGGL((k_router<T, D, true>), grid, dim3(256), 0, st, (const T*)a.qr, (const T*)a.kr, a.lse2,
                      a.scores, a.nb, a.scale_log2);
+  timer_after(TK_ROUTER_SCORES, st);
   return hipGetLastError();
 }
 

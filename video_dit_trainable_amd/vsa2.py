@@ -17,6 +17,7 @@ LIB_PATH = os.path.join(_HERE, "libvsa2.so")
 VSA2_OK, VSA2_E_ARG, VSA2_E_SHAPE, VSA2_E_WORKSPACE, VSA2_E_HIP, VSA2_E_UNSUPPORTED = range(6)
 VSA2_F32, VSA2_BF16 = 0, 1
 OP_POOL, OP_ROUTE, OP_TOPK, OP_PLAN, OP_FWD, OP_BWD, OP_COARSE, OP_COARSE_BWD = range(8)
+K_FINE_FWD, K_BWD_DKDV, K_BWD_DQ, K_ROUTER_LSE, K_ROUTER_SCORES = range(5)
 
 
 class Problem(ctypes.Structure):
@@ -51,6 +52,8 @@ _SIGS = {
     "vsa2_sparse_attn_bwd": (ctypes.c_int, [_PP, _I32] + [_P] * 15 + [_SZ, _P]),
     "vsa2_coarse_gate": (ctypes.c_int, [_PP, _P, _P, _I32, _P, _P, _P, _P, _P, _SZ, _P]),
     "vsa2_coarse_gate_bwd": (ctypes.c_int, [_PP, _P, _P, _I32, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "vsa2_kernel_timer_start": (ctypes.c_int, [_I32, _I32]),
+    "vsa2_kernel_timer_stop": (ctypes.c_int, [_I32, ctypes.POINTER(ctypes.c_float), ctypes.POINTER(_I32)]),
 }
 
 _lib = None
@@ -175,6 +178,17 @@ def vsa2_coarse_gate_bwd(p, pooled, x, d_model, w_g, saved, d_o, dqkv_c, dx, dw_
         _ptr(dx), _ptr(dw_g), _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
 
 
+def kernel_timer_start(kernel, capacity=256):
+    _check("vsa2_kernel_timer_start", lib().vsa2_kernel_timer_start(kernel, capacity))
+
+
+def kernel_timer_stop(kernel):
+    """(summed milliseconds, launches) of the timed launches of `kernel`."""
+    ms, n = ctypes.c_float(0.0), _I32(0)
+    _check("vsa2_kernel_timer_stop", lib().vsa2_kernel_timer_stop(kernel, ctypes.byref(ms), ctypes.byref(n)))
+    return ms.value, n.value
+
+
 # ---------------------------------------------------------------------------
 # buffer bookkeeping for a full layer call (allocation + the call sequence)
 # ---------------------------------------------------------------------------
@@ -229,7 +243,8 @@ class Layer:
         self.col_idx.copy_(col_idx)
         vsa2_plan_from_csr(self.p, self.topk, self.row_ptr, self.col_idx, self.col_ptr, self.row_idx, self.ws, stream)
 
-    def backward(self, q, k, v, x, w_g, d_o, stream=None):
+    def grads(self):
+        """Gradient buffers (allocated on first use): dq, dk, dv, dx, dw_g, dqkv_c."""
         p = self.p
         if self._grads is None:
             shp = (p.batch, p.heads, self.L, p.head_dim)
@@ -242,7 +257,11 @@ class Layer:
                 dqkv_c=torch.empty((3, p.batch, p.heads, self.nb, p.head_dim), dtype=torch.float32,
                                    device=self.device),
             )
-        g = self._grads
+        return self._grads
+
+    def backward(self, q, k, v, x, w_g, d_o, stream=None):
+        p = self.p
+        g = self.grads()
         vsa2_coarse_gate_bwd(p, self.pooled, x, self.d_model, w_g, self.saved, d_o, g["dqkv_c"], g["dx"],
                              g["dw_g"], self.ws, stream)
         vsa2_sparse_attn_bwd(p, self.topk, q, k, v, self.o_f, self.lse, d_o, self.row_ptr, self.col_idx,
