@@ -101,7 +101,7 @@ size_t ws_plan(const Dims& d, TopkWs* w, void* base) {
   return o_bm + up((size_t)d.bh * d.nb * bitmap_words(d) * 4);
 }
 
-size_t ws_bwd(const Dims& d) { return up((size_t)d.bh * d.L * 4); }
+size_t ws_bwd(const Dims& d) { return up((size_t)d.bh * d.L * 8); }      // (lse2, delta) per token
 
 size_t ws_fwd(const Dims& d) { return up((size_t)d.bh * d.L * d.d * d.esz); }      // V^T per cube
 
@@ -118,7 +118,7 @@ struct CoarseBwdWs {
   void* wt;
   float* dpre;
   void* doc;
-  float* delta_c;
+  float* stats_c;
   float* dw_part;
 };
 
@@ -132,14 +132,14 @@ size_t ws_coarse_bwd(const Dims& d, int dm, CoarseBwdWs* w, void* base) {
   const size_t o_wt = take(wt_bytes(d, dm));
   const size_t o_dpre = take((size_t)d.bh * d.L * 4);
   const size_t o_doc = take((size_t)d.bh * d.nbp * d.d * d.esz);
-  const size_t o_dc = take((size_t)d.bh * d.nbp * 4);
+  const size_t o_dc = take((size_t)d.bh * d.nbp * 8);
   const size_t o_dw = take((size_t)d.batch * nchunk_of(d) * dm * d.heads * 4);
   if (w) {
     char* b = (char*)base;
     w->wt = b + o_wt;
     w->dpre = (float*)(b + o_dpre);
     w->doc = b + o_doc;
-    w->delta_c = (float*)(b + o_dc);
+    w->stats_c = (float*)(b + o_dc);
     w->dw_part = (float*)(b + o_dw);
   }
   return off;
@@ -398,14 +398,14 @@ int vsa2_sparse_attn_bwd(const vsa2_problem* p, int32_t topk, const void* q, con
   AttnBwdArgs a{};
   a.q = q; a.k = k; a.v = v; a.o = o_f; a.d_o = d_o;
   a.lse = lse;
-  a.delta = (const float*)ws;
+  a.stats = (const float*)ws;
   a.row_ptr = row_ptr; a.col_idx = col_idx; a.col_ptr = col_ptr; a.row_idx = row_idx;
   const size_t cstride = (size_t)d.bh * d.nb * d.d;
   a.dq_add = dqkv_c;
   a.dk_add = dqkv_c ? dqkv_c + cstride : nullptr;
   a.dv_add = dqkv_c ? dqkv_c + 2 * cstride : nullptr;
   a.dq = dq; a.dk = dk; a.dv = dv;
-  a.bh = d.bh; a.nq = d.nb; a.nkv = d.nb; a.seq = d.L; a.ld = d.L; a.out_rows = d.L; a.lse_rows = d.L;
+  a.bh = d.bh; a.nq = d.nb; a.nkv = d.nb; a.seq = d.L; a.ld = d.L; a.out_rows = d.L;
   a.kph = budget(d, topk);
   a.d = d.d; a.bf16 = d.bf16; a.dense = false;
   a.scale = d.scale;
@@ -461,18 +461,17 @@ int vsa2_coarse_gate_bwd(const vsa2_problem* p, const void* pooled, const void* 
   const float* oc_hat = saved;
   const float* lse_c = oc_hat + (size_t)d.bh * d.nb * d.d;
   const float* g = lse_c + (size_t)d.bh * d.nb;
-  GateBwdArgs ga{x, w_g, w.wt, oc_hat, g, d_o, w.dpre, w.doc, w.delta_c, w.dw_part, dx, dw_g,
+  GateBwdArgs ga{x, w_g, w.wt, oc_hat, g, d_o, w.dpre, w.doc, lse_c, w.stats_c, w.dw_part, dx, dw_g,
                  d.batch, d.heads, d.nb, d.nbp, d.d, d_model, nchunk_of(d), d.bf16};
   hipError_t e = launch_gate_bwd(ga, st);
   if (e != hipSuccess) return VSA2_E_HIP;
   AttnBwdArgs a{};
   a.q = pp.qc; a.k = pp.kc; a.v = pp.vc; a.o = nullptr; a.d_o = w.doc;
-  a.lse = lse_c;
-  a.delta = w.delta_c;
+  a.lse = nullptr;
+  a.stats = w.stats_c;
   const size_t cstride = (size_t)d.bh * d.nb * d.d;
   a.dq = dqkv_c; a.dk = dqkv_c + cstride; a.dv = dqkv_c + 2 * cstride;
   a.bh = d.bh; a.nq = d.nbp / 64; a.nkv = d.nbp / 64; a.seq = d.nb; a.ld = d.nbp; a.out_rows = d.nb;
-  a.lse_rows = d.nb;
   a.kph = 0;
   a.d = d.d; a.bf16 = d.bf16; a.dense = true;
   a.scale = d.scale;

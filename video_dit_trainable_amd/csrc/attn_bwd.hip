@@ -22,9 +22,13 @@
 
 namespace vsa2 {
 
+// Row statistics of the fine branch for the backward kernels: stats[2t] =
+// lse_t * log2(e) (+inf for a row with no selected key, so its P is 0) and
+// stats[2t + 1] = delta_t = dO_t . O_t.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void k_bwd_delta(const T* __restrict__ o, const T* __restrict__ d_o,
-                                                   float* __restrict__ delta, size_t rows) {
+                                                   const float* __restrict__ lse, float* __restrict__ stats,
+                                                   size_t rows) {
   constexpr int LPT = D / 8;  // lanes per row
   const size_t row = ((size_t)blockIdx.x * 256 + threadIdx.x) / LPT;
   const int part = threadIdx.x % LPT;
@@ -37,26 +41,120 @@ __global__ __launch_bounds__(256) void k_bwd_delta(const T* __restrict__ o, cons
   }
 #pragma unroll
   for (int x = 1; x < LPT; x <<= 1) s += __shfl_xor(s, x);
-  if (row < rows && part == 0) delta[row] = s;
+  if (row < rows && part == 0) {
+    const float l = lse[row];
+    stats[2 * row] = l == -INFINITY ? INFINITY : l * LOG2E;
+    stats[2 * row + 1] = s;
+  }
 }
 
+// One (query cube, KV cube) pair of the dK/dV kernel for one wave: keys 32kh..
+// (K, V fragments kf, vf in registers) against queries 32qh.. of the Q / dO
+// tiles qs, dos and their row statistics sts (pairs lse2, delta) in LDS.
+// Fragment reads of a swizzled 64 x D tile: row-major (row r, k-step s) and
+// transposed (rows r0 .., columns col0 ..).  bf16 takes the per-lane bases
+// (sw_row_base for row 16qb + cc of the wave's half, sw_tr_base for rows r0);
+// fp32 (test precision) computes each address in full.
+template <typename T, int D>
+__device__ __forceinline__ Frag<T> rd_row(const T* t, int base, int r, int s, int g) {
+  if constexpr (sizeof(T) == 2) return sw_frag_at<T>(t, base + (r & ~15) * D, s);
+  else return sw_frag<T, D>(t, r, s, g);
+}
+template <typename T, int D>
+__device__ __forceinline__ Frag<T> rd_tr(const T* t, int base, int r0, int col0, int g, int c) {
+  if constexpr (sizeof(T) == 2) return sw_frag_tr_at<T, D>(t, base, col0);
+  else return sw_frag_tr<T, D>(t, r0, col0, g, c);
+}
+
+// One (query cube, KV cube) pair of the dK/dV kernel for one wave: keys 32kh..
+// (K, V fragments kf, vf in registers) against queries 32qh.. of the Q / dO
+// tiles qs, dos and their row statistics sts (pairs lse2, delta) in LDS.
+// Query rows 32qh + 16qb + 4g + r (qb = 0, 1 in turn) meet keys 32kh + 16kb + cc;
+// P and dS of each 16-query block go straight into the low (qb = 0) or high
+// (qb = 1) half of the bf16 B fragments of the dV and dK products, so only one
+// 16 x 32 block of S and dP is live at a time.
+template <typename T, int D, bool DENSE>
+__device__ __forceinline__ void dkdv_pair(const T* qs, const T* dos, const float* sts, int brow, int btr,
+                                          const Frag<T> (&kf)[2][D / 32], const Frag<T> (&vf)[2][D / 32],
+                                          const bool (&kv_ok)[2], f32x4 (&dka)[D / 16][2], f32x4 (&dva)[D / 16][2],
+                                          int qh, int g, int cc, float c) {
+  opaque(brow);
+  opaque(btr);
+  Frag<T> pf[2], sf[2];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const int row = 32 * qh + 16 * qb + cc;
+    f32x4 p[2], dp[2];
+    {
+      const Frag<T> a = rd_row<T, D>(qs, brow, row, 0, g);
+      p[0] = mma0(a, kf[0][0]);
+      p[1] = mma0(a, kf[1][0]);
+      const Frag<T> b = rd_row<T, D>(dos, brow, row, 0, g);
+      dp[0] = mma0(b, vf[0][0]);
+      dp[1] = mma0(b, vf[1][0]);
+    }
+#pragma unroll
+    for (int s = 1; s < D / 32; ++s) {
+      const Frag<T> a = rd_row<T, D>(qs, brow, row, s, g);
+      mma(p[0], a, kf[0][s]);
+      mma(p[1], a, kf[1][s]);
+      const Frag<T> b = rd_row<T, D>(dos, brow, row, s, g);
+      mma(dp[0], b, vf[0][s]);
+      mma(dp[1], b, vf[1][s]);
+    }
+    // P = exp2(S c - lse2), dS = P (dP - delta)
+    const float* sp = sts + 2 * (32 * qh + 16 * qb + 4 * g);
+    const f32x4 s01 = *reinterpret_cast<const f32x4*>(sp);
+    const f32x4 s23 = *reinterpret_cast<const f32x4*>(sp + 4);
+    const float l2[4] = {s01[0], s01[2], s23[0], s23[2]};
+    const float dl[4] = {s01[1], s01[3], s23[1], s23[3]};
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float pe = kv_ok[kb] ? fast_exp2(fmaf(p[kb][r], c, -l2[r])) : 0.f;
+        pf[kb].v[4 * qb + r] = from_f32<T>(pe);
+        sf[kb].v[4 * qb + r] = from_f32<T>(pe * (dp[kb][r] - dl[r]));
+      }
+  }
+  // dV^T += dO^T P, dK^T += Q^T dS over these 32 queries
+#pragma unroll
+  for (int db = 0; db < D / 16; ++db) {
+    const Frag<T> ao = rd_tr<T, D>(dos, btr, 32 * qh, 16 * db, g, cc);
+    mma(dva[db][0], ao, pf[0]);
+    mma(dva[db][1], ao, pf[1]);
+    const Frag<T> aq = rd_tr<T, D>(qs, btr, 32 * qh, 16 * db, g, cc);
+    mma(dka[db][0], aq, sf[0]);
+    mma(dka[db][1], aq, sf[1]);
+  }
+}
+
+// dK, dV: one 256-thread block per KV cube j over its CSC list of query cubes.
+// Wave w takes keys 32 (w & 1) .. and queries 32 (w >> 1) .. of every pair;
+// the two query halves are summed through LDS at the end (fixed order).  The
+// Q / dO tiles and row statistics of the next pair are copied LDS-direct into
+// the other of two stages while the current pair is computed; the stages are
+// distinct arrays and the loop is unrolled by two, so the compiler can tell
+// the copy into one stage from the reads of the other.
 template <typename T, typename TO, int D, bool DENSE>
-__global__ __launch_bounds__(128) void k_bwd_dkdv(const T* __restrict__ q, const T* __restrict__ k,
-                                                  const T* __restrict__ v, const T* __restrict__ d_o,
-                                                  const float* __restrict__ lse, const float* __restrict__ delta,
-                                                  const int32_t* __restrict__ col_ptr,
-                                                  const int32_t* __restrict__ row_idx,
-                                                  const float* __restrict__ dk_add, const float* __restrict__ dv_add,
-                                                  TO* __restrict__ dk, TO* __restrict__ dv, int nq, int nkv, int seq,
-                                                  int ld, int out_rows, int lse_rows, int64_t kph, float scale,
-                                                  float c, int ct, int cy, int cx) {
-  __shared__ __align__(16) T qs[64 * D];
-  __shared__ __align__(16) T dos[64 * D];
-  __shared__ float lse_s[64], del_s[64];
+__global__ __launch_bounds__(256, 2) void k_bwd_dkdv(const T* __restrict__ q, const T* __restrict__ k,
+                                                     const T* __restrict__ v, const T* __restrict__ d_o,
+                                                     const float* __restrict__ stats,
+                                                     const int32_t* __restrict__ col_ptr,
+                                                     const int32_t* __restrict__ row_idx,
+                                                     const float* __restrict__ dk_add,
+                                                     const float* __restrict__ dv_add, TO* __restrict__ dk,
+                                                     TO* __restrict__ dv, int nq, int nkv, int seq, int ld,
+                                                     int out_rows, int64_t kph, float scale, float c) {
+  constexpr int TILE = 64 * D;
+  __shared__ __align__(16) T tA[2 * TILE];  // stage A: Q tile | dO tile
+  __shared__ __align__(16) T tB[2 * TILE];  // stage B
+  __shared__ __align__(16) float sA[128];   // stage A row statistics: [row][lse2, delta]
+  __shared__ __align__(16) float sB[128];
   int bh, j;
   if (!xcd_work(blockIdx.x, nkv, bh, j)) return;
-  if (ct > 0) j = blocked_cube(j, ct, cy, cx);
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, cc = lane & 15;
+  const int kh = w & 1, qh = w >> 1;
   const size_t hoff = (size_t)bh * ld * D;
 
   int cnt;
@@ -70,30 +168,47 @@ __global__ __launch_bounds__(128) void k_bwd_dkdv(const T* __restrict__ q, const
     cnt = (int)(end - start);
     rows = row_idx + (size_t)bh * kph + start;
   }
-  // query cube of list entry n (-1 = corrupt entry, masked tile) and its valid rows
-  auto cube_at = [&](int n) -> int {
+  // list entry n (DENSE: the query tile n); read one step before its copy is
+  // started, so the load is complete at the wait that precedes the copy
+  auto entry = [&](int n) -> int {
     if constexpr (DENSE) return n;
-    const int ii = rows[n];
-    return (unsigned)ii < (unsigned)nq ? ii : -1;
+    else return rows[n];
   };
-  auto q_limit = [&](int ii) -> int {
-    if constexpr (DENSE) return min(64, seq - ii * 64);
-    return ii >= 0 ? 64 : 0;
+  // a corrupt sparse entry is fetched as cube 0 and skipped.  The entry stays
+  // in a vector register until here (opaque), so its load is only waited for
+  // after the copies issued behind it have been waited for anyway.
+  auto cube_of = [&](int raw, bool& ok) -> int {
+    if constexpr (!DENSE) opaque(raw);
+    raw = __builtin_amdgcn_readfirstlane(raw);
+    ok = (unsigned)raw < (unsigned)nq;
+    return ok ? raw : 0;
   };
+  const float* stats_bh = stats + 2 * (size_t)bh * ld;
+#define VSA2_FETCH_QDO(ii, tbuf, sbuf)                                                             \
+  {                                                                                                \
+    dma_tile<64, D, T, 256>(q + hoff + (size_t)(ii) * TILE, tbuf, tid);                            \
+    dma_tile<64, D, T, 256>(d_o + hoff + (size_t)(ii) * TILE, tbuf + TILE, tid);                   \
+    if (tid < 32) {                                                                                \
+      int so_ = 16 * tid;                                                                          \
+      opaque(so_);                                                                                 \
+      lds_copy16(reinterpret_cast<const char*>(stats_bh + (size_t)(ii) * 128) + (uint32_t)so_,     \
+                 (VSA2_LDS void*)(sbuf));                                                          \
+    }                                                                                              \
+  }
 
-  // K, V rows of this wave as B fragments: key 32w + 16kb + cc
   Frag<T> kf[2][D / 32], vf[2][D / 32];
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-    for (int s = 0; s < D / 32; ++s) {
-      kf[kb][s] = frag_global<T, D>(k + hoff, j * 64 + 32 * w + 16 * kb + cc, s, g);
-      vf[kb][s] = frag_global<T, D>(v + hoff, j * 64 + 32 * w + 16 * kb + cc, s, g);
-    }
   bool kv_ok[2];
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb) kv_ok[kb] = !DENSE || (j * 64 + 32 * w + 16 * kb + cc < seq);
-
+  for (int kb = 0; kb < 2; ++kb) {
+    const int key = j * 64 + 32 * kh + 16 * kb + cc;
+    kv_ok[kb] = !DENSE || key < seq;
+#pragma unroll
+    for (int s = 0; s < D / 32; ++s) {
+      kf[kb][s] = frag_global<T, D>(k + hoff, key, s, g);
+      vf[kb][s] = frag_global<T, D>(v + hoff, key, s, g);
+    }
+  }
+  // dK^T, dV^T partial sums over this wave's query half: rows d = 16db + 4g + r, column key 16kb + cc
   f32x4 dka[D / 16][2], dva[D / 16][2];
 #pragma unroll
   for (int db = 0; db < D / 16; ++db) {
@@ -101,128 +216,99 @@ __global__ __launch_bounds__(128) void k_bwd_dkdv(const T* __restrict__ q, const
     dva[db][0] = dva[db][1] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
+  int brow = 0, btr = 0;  // per-lane parts of the bf16 fragment addresses
+  if constexpr (sizeof(T) == 2) {
+    brow = sw_row_base<T, D>(cc, g);  // rows 16m + cc add 16m D (the swizzle sees only r & 15)
+    btr = sw_tr_base<T, D>(32 * qh, g, cc);
+  }
+  bool ok_a = false, ok_b = false;
+  int raw = 0;  // list entry whose copy starts next
   if (cnt > 0) {
-    SwRegs<64, D, T, 128> qr, dr;
-    float lse_n = 0.f, del_n = 0.f;
-    auto fetch = [&](int n) {
-      const int ii = cube_at(n);
-      const int valid = q_limit(ii);
-      sw_load(qr, q + hoff + (size_t)max(ii, 0) * 64 * D, tid);
-      sw_load(dr, d_o + hoff + (size_t)max(ii, 0) * 64 * D, tid);
-      if (tid < 64) {
-        const bool ok = tid < valid;
-        const size_t t = (size_t)max(ii, 0) * 64 + tid;
-        lse_n = ok ? lse[(size_t)bh * lse_rows + t] * LOG2E : INFINITY;
-        del_n = ok ? delta[(size_t)bh * ld + t] : 0.f;
-      }
-    };
-    fetch(0);
-    for (int n = 0; n < cnt; ++n) {
-      sw_store(qr, qs, tid);
-      sw_store(dr, dos, tid);
-      if (tid < 64) {
-        lse_s[tid] = lse_n;
-        del_s[tid] = del_n;
-      }
-      __syncthreads();
-      if (n + 1 < cnt) fetch(n + 1);
+    const int ii0 = cube_of(entry(0), ok_a);
+    VSA2_FETCH_QDO(ii0, tA, sA);
+    if (cnt > 1) raw = entry(1);
+  }
+  for (int n = 0; n < cnt; n += 2) {
+    wait_vm0();
+    __syncthreads();  // stage A holds entry n; every wave is done with stage B
+    if (n + 1 < cnt) {
+      const int ii = cube_of(raw, ok_b);
+      if (n + 2 < cnt) raw = entry(n + 2);
+      VSA2_FETCH_QDO(ii, tB, sB);
+    }
+    if (ok_a) dkdv_pair<T, D, DENSE>(tA, tA + TILE, sA, brow, btr, kf, vf, kv_ok, dka, dva, qh, g, cc, c);
+    if (n + 1 >= cnt) break;
+    wait_vm0();
+    __syncthreads();  // stage B holds entry n + 1; every wave is done with stage A
+    if (n + 2 < cnt) {
+      const int ii = cube_of(raw, ok_a);
+      if (n + 3 < cnt) raw = entry(n + 3);
+      VSA2_FETCH_QDO(ii, tA, sA);
+    }
+    if (ok_b) dkdv_pair<T, D, DENSE>(tB, tB + TILE, sB, brow, btr, kf, vf, kv_ok, dka, dva, qh, g, cc, c);
+  }
+#undef VSA2_FETCH_QDO
 
-      // S[q][kv]: p[qb][kb] holds queries 16qb + 4g + r against key 32w + 16kb + cc
-      f32x4 p[4][2];
+  // sum the two query halves: waves with qh = 1 hand their partials to qh = 0 through LDS
+  __syncthreads();
+  constexpr int PART = (D / 16) * 2 * 4 * 64;  // floats per wave and tensor
+  static_assert(2 * PART * sizeof(float) <= sizeof(tA), "reduction buffer must fit a stage");
+  float* mine = reinterpret_cast<float*>(kh ? tB : tA);  // [dK | dV][db][kb][r][lane]
+  if (qh == 1) {
 #pragma unroll
-      for (int qb = 0; qb < 4; ++qb) {
-        const Frag<T> a = sw_frag<T, D>(qs, 16 * qb + cc, 0, g);
-        p[qb][0] = mma0(a, kf[0][0]);
-        p[qb][1] = mma0(a, kf[1][0]);
-      }
+    for (int db = 0; db < D / 16; ++db)
 #pragma unroll
-      for (int s = 1; s < D / 32; ++s)
-#pragma unroll
-        for (int qb = 0; qb < 4; ++qb) {
-          const Frag<T> a = sw_frag<T, D>(qs, 16 * qb + cc, s, g);
-          mma(p[qb][0], a, kf[0][s]);
-          mma(p[qb][1], a, kf[1][s]);
-        }
-#pragma unroll
-      for (int qb = 0; qb < 4; ++qb)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const float l2 = lse_s[16 * qb + 4 * g + r];
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb) {
-            const float pe = fast_exp2(fmaf(p[qb][kb][r], c, -l2));
-            p[qb][kb][r] = kv_ok[kb] ? pe : 0.f;
-          }
+          const int o = ((db * 2 + kb) * 4 + r) * 64 + lane;
+          mine[o] = dka[db][kb][r];
+          mine[PART + o] = dva[db][kb][r];
         }
-      // dV^T += dO^T P
+  }
+  __syncthreads();
+  if (qh == 1) return;
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const Frag<T> f0 = frag_from_acc<T>(p[2 * h][0], p[2 * h + 1][0]);
-        const Frag<T> f1 = frag_from_acc<T>(p[2 * h][1], p[2 * h + 1][1]);
+  for (int db = 0; db < D / 16; ++db)
 #pragma unroll
-        for (int db = 0; db < D / 16; ++db) {
-          const Frag<T> a = sw_frag_tr<T, D>(dos, 32 * h, 16 * db, g, cc);
-          mma(dva[db][0], a, f0);
-          mma(dva[db][1], a, f1);
-        }
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int o = ((db * 2 + kb) * 4 + r) * 64 + lane;
+        dka[db][kb][r] = (dka[db][kb][r] + mine[o]) * scale;
+        dva[db][kb][r] += mine[PART + o];
       }
-      // dP = dO V^T, dS = P (dP - delta)
-      f32x4 dp[4][2];
+  // the coarse branch's per-cube gradient rows, 1/64 to every token of the cube
+  if (dk_add) {
+    const float* ka = dk_add + ((size_t)bh * nkv + j) * D;
+    const float* va = dv_add + ((size_t)bh * nkv + j) * D;
 #pragma unroll
-      for (int qb = 0; qb < 4; ++qb) {
-        const Frag<T> a = sw_frag<T, D>(dos, 16 * qb + cc, 0, g);
-        dp[qb][0] = mma0(a, vf[0][0]);
-        dp[qb][1] = mma0(a, vf[1][0]);
-      }
+    for (int db = 0; db < D / 16; ++db) {
+      const f32x4 a4 = *reinterpret_cast<const f32x4*>(ka + 16 * db + 4 * g);
+      const f32x4 b4 = *reinterpret_cast<const f32x4*>(va + 16 * db + 4 * g);
 #pragma unroll
-      for (int s = 1; s < D / 32; ++s)
-#pragma unroll
-        for (int qb = 0; qb < 4; ++qb) {
-          const Frag<T> a = sw_frag<T, D>(dos, 16 * qb + cc, s, g);
-          mma(dp[qb][0], a, vf[0][s]);
-          mma(dp[qb][1], a, vf[1][s]);
-        }
-#pragma unroll
-      for (int qb = 0; qb < 4; ++qb)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const float dl = del_s[16 * qb + 4 * g + r];
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb) dp[qb][kb][r] = p[qb][kb][r] * (dp[qb][kb][r] - dl);
+          dka[db][kb][r] += a4[r] * (1.0f / 64.0f);
+          dva[db][kb][r] += b4[r] * (1.0f / 64.0f);
         }
-      // dK^T += Q^T dS
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const Frag<T> f0 = frag_from_acc<T>(dp[2 * h][0], dp[2 * h + 1][0]);
-        const Frag<T> f1 = frag_from_acc<T>(dp[2 * h][1], dp[2 * h + 1][1]);
-#pragma unroll
-        for (int db = 0; db < D / 16; ++db) {
-          const Frag<T> a = sw_frag_tr<T, D>(qs, 32 * h, 16 * db, g, cc);
-          mma(dka[db][0], a, f0);
-          mma(dka[db][1], a, f1);
-        }
-      }
-      __syncthreads();
     }
   }
-
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
-    const int kvrow = j * 64 + 32 * w + 16 * kb + cc;
+    const int kvrow = j * 64 + 32 * kh + 16 * kb + cc;
     const bool live = DENSE ? (kvrow < seq && kvrow < out_rows) : (kvrow < out_rows);
     if (!live) continue;
     TO* krow = dk + ((size_t)bh * out_rows + kvrow) * D;
     TO* vrow = dv + ((size_t)bh * out_rows + kvrow) * D;
-    const float* ka = dk_add ? dk_add + ((size_t)bh * nkv + j) * D : nullptr;
-    const float* va = dv_add ? dv_add + ((size_t)bh * nkv + j) * D : nullptr;
 #pragma unroll
     for (int db = 0; db < D / 16; ++db) {
       Vec4<TO> a4, b4;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int d = 16 * db + 4 * g + r;
-        a4.v[r] = from_f32<TO>(dka[db][kb][r] * scale + (ka ? ka[d] * (1.0f / 64.0f) : 0.f));
-        b4.v[r] = from_f32<TO>(dva[db][kb][r] + (va ? va[d] * (1.0f / 64.0f) : 0.f));
+        a4.v[r] = from_f32<TO>(dka[db][kb][r]);
+        b4.v[r] = from_f32<TO>(dva[db][kb][r]);
       }
       store4(krow + 16 * db + 4 * g, a4);
       store4(vrow + 16 * db + 4 * g, b4);
@@ -230,22 +316,81 @@ __global__ __launch_bounds__(128) void k_bwd_dkdv(const T* __restrict__ q, const
   }
 }
 
+// One (query cube, KV cube) pair of the dQ kernel for one wave: queries 32qh..
+// (Q, dO fragments qf, of in registers, row statistics l2, dl) against keys
+// 32kh.. of the K / V tiles ks, vs in LDS; keys at or beyond lim are masked.
+template <typename T, int D>
+__device__ __forceinline__ void dq_pair(const T* ks, const T* vs, int brow, int btr, int lim,
+                                        const Frag<T> (&qf)[2][D / 32], const Frag<T> (&of)[2][D / 32],
+                                        const float (&l2)[2], const float (&dl)[2], f32x4 (&dqa)[D / 16][2], int kh,
+                                        int g, int cc, float c) {
+  opaque(brow);
+  opaque(btr);
+  // S^T = K Q^T, dP^T = V dO^T: [kb][qb] holds keys 32kh + 16kb + 4g + r against query 32qh + 16qb + cc
+  Frag<T> sf[2];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    const int row = 32 * kh + 16 * kb + cc;
+    f32x4 p[2], dp[2];
+    {
+      const Frag<T> a = rd_row<T, D>(ks, brow, row, 0, g);
+      p[0] = mma0(a, qf[0][0]);
+      p[1] = mma0(a, qf[1][0]);
+      const Frag<T> b = rd_row<T, D>(vs, brow, row, 0, g);
+      dp[0] = mma0(b, of[0][0]);
+      dp[1] = mma0(b, of[1][0]);
+    }
+#pragma unroll
+    for (int s = 1; s < D / 32; ++s) {
+      const Frag<T> a = rd_row<T, D>(ks, brow, row, s, g);
+      mma(p[0], a, qf[0][s]);
+      mma(p[1], a, qf[1][s]);
+      const Frag<T> b = rd_row<T, D>(vs, brow, row, s, g);
+      mma(dp[0], b, of[0][s]);
+      mma(dp[1], b, of[1][s]);
+    }
+    // dS^T = P^T (dP^T - delta) straight into the low (kb = 0) / high (kb = 1) half of the B fragments
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const bool kin = 32 * kh + 16 * kb + 4 * g + r < lim;
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        const float pe = kin ? fast_exp2(fmaf(p[qb][r], c, -l2[qb])) : 0.f;
+        sf[qb].v[4 * kb + r] = from_f32<T>(pe * (dp[qb][r] - dl[qb]));
+      }
+    }
+  }
+  // dQ^T += K^T dS^T over these 32 keys
+#pragma unroll
+  for (int db = 0; db < D / 16; ++db) {
+    const Frag<T> a = rd_tr<T, D>(ks, btr, 32 * kh, 16 * db, g, cc);
+    mma(dqa[db][0], a, sf[0]);
+    mma(dqa[db][1], a, sf[1]);
+  }
+}
+
+// dQ: one 256-thread block per query cube i over its CSR list of KV cubes.
+// Wave w takes queries 32 (w & 1) .. and keys 32 (w >> 1) .. of every pair; the
+// key halves are summed through LDS at the end.  K / V tiles of the next pair
+// are copied LDS-direct into the other stage while the current pair runs
+// (distinct stage arrays, loop unrolled by two, as in the dK/dV kernel).
 template <typename T, typename TO, int D, bool DENSE>
-__global__ __launch_bounds__(128) void k_bwd_dq(const T* __restrict__ q, const T* __restrict__ k,
+__global__ __launch_bounds__(256, 2) void k_bwd_dq(const T* __restrict__ q, const T* __restrict__ k,
                                                    const T* __restrict__ v, const T* __restrict__ d_o,
-                                                   const float* __restrict__ lse, const float* __restrict__ delta,
+                                                   const float* __restrict__ stats,
                                                    const int32_t* __restrict__ row_ptr,
                                                    const int32_t* __restrict__ col_idx,
                                                    const float* __restrict__ dq_add, TO* __restrict__ dq, int nq,
-                                                   int nkv, int seq, int ld, int out_rows, int lse_rows, int64_t kph,
-                                                   float scale, float c, int ct, int cy, int cx) {
-  __shared__ __align__(16) T ks[64 * D];
-  __shared__ __align__(16) T vs[64 * D];
-  __shared__ __align__(16) T dos[64 * D];
+                                                   int nkv, int seq, int ld, int out_rows, int64_t kph, float scale,
+                                                   float c, int ct, int cy, int cx) {
+  constexpr int TILE = 64 * D;
+  __shared__ __align__(16) T tA[2 * TILE];  // stage A: K tile | V tile
+  __shared__ __align__(16) T tB[2 * TILE];  // stage B
   int bh, i;
   if (!xcd_work(blockIdx.x, nq, bh, i)) return;
   if (ct > 0) i = blocked_cube(i, ct, cy, cx);
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, cc = lane & 15;
+  const int qh = w & 1, kh = w >> 1;
   const size_t hoff = (size_t)bh * ld * D;
 
   int cnt;
@@ -259,156 +404,159 @@ __global__ __launch_bounds__(128) void k_bwd_dq(const T* __restrict__ q, const T
     cnt = (int)(end - start);
     cols = col_idx + (size_t)bh * kph + start;
   }
-  auto cube_at = [&](int n) -> int {
+  // list entry n (DENSE: the KV tile n), read one step before its copy starts
+  auto entry = [&](int n) -> int {
     if constexpr (DENSE) return n;
-    const int jj = cols[n];
-    return (unsigned)jj < (unsigned)nkv ? jj : -1;
+    else return cols[n];
   };
-  auto kv_limit = [&](int jj) -> int {
-    if constexpr (DENSE) return min(64, seq - jj * 64);
-    return jj >= 0 ? 64 : 0;
+  // KV cube of an entry and how many of its keys are valid (0 for a corrupt entry)
+  auto cube_of = [&](int raw, int& lim) -> int {
+    if constexpr (DENSE) {
+      lim = min(64, seq - raw * 64);
+      return raw;
+    } else {
+      opaque(raw);
+      raw = __builtin_amdgcn_readfirstlane(raw);
+      const bool ok = (unsigned)raw < (unsigned)nkv;
+      lim = ok ? 64 : 0;
+      return ok ? raw : 0;
+    }
   };
-
-  // this cube's dO tile (B fragments of dP^T = V dO^T come from LDS)
-  {
-    SwRegs<64, D, T, 128> r;
-    sw_load(r, d_o + hoff + (size_t)i * 64 * D, tid);
-    sw_store(r, dos, tid);
+#define VSA2_FETCH_KV(jj, tbuf)                                                       \
+  {                                                                                   \
+    dma_tile<64, D, T, 256>(k + hoff + (size_t)(jj) * TILE, tbuf, tid);               \
+    dma_tile<64, D, T, 256>(v + hoff + (size_t)(jj) * TILE, tbuf + TILE, tid);        \
   }
-  Frag<T> qf[2][D / 32];
-  float lse2[2], del[2];
+
+  // this wave's 32 queries: Q and dO rows as B fragments (column = query 32qh + 16qb + cc)
+  Frag<T> qf[2][D / 32], of[2][D / 32];
+  float l2[2], dl[2];
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
-    const int qrow = i * 64 + 32 * w + 16 * qb + cc;
+    const int qrow = i * 64 + 32 * qh + 16 * qb + cc;
 #pragma unroll
-    for (int s = 0; s < D / 32; ++s) qf[qb][s] = frag_global<T, D>(q + hoff, qrow, s, g);
-    const bool ok = !DENSE || qrow < seq;
-    lse2[qb] = ok ? lse[(size_t)bh * lse_rows + qrow] * LOG2E : INFINITY;
-    del[qb] = ok ? delta[(size_t)bh * ld + qrow] : 0.f;
+    for (int s = 0; s < D / 32; ++s) {
+      qf[qb][s] = frag_global<T, D>(q + hoff, qrow, s, g);
+      of[qb][s] = frag_global<T, D>(d_o + hoff, qrow, s, g);
+    }
+    l2[qb] = stats[2 * ((size_t)bh * ld + qrow)];
+    dl[qb] = stats[2 * ((size_t)bh * ld + qrow) + 1];
   }
+  // dQ^T partial over this wave's key half: rows d = 16db + 4g + r, column query 16qb + cc
   f32x4 dqa[D / 16][2];
 #pragma unroll
   for (int db = 0; db < D / 16; ++db) dqa[db][0] = dqa[db][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  int brow = 0, btr = 0;
+  if constexpr (sizeof(T) == 2) {
+    brow = sw_row_base<T, D>(cc, g);  // rows 16m + cc add 16m D (the swizzle sees only r & 15)
+    btr = sw_tr_base<T, D>(32 * kh, g, cc);
+  }
+  int lim_a = 0, lim_b = 0, raw = 0;
   if (cnt > 0) {
-    SwRegs<64, D, T, 128> kr, vr;
-    int j = cube_at(0);
-    sw_load(kr, k + hoff + (size_t)max(j, 0) * 64 * D, tid);
-    sw_load(vr, v + hoff + (size_t)max(j, 0) * 64 * D, tid);
-    for (int n = 0; n < cnt; ++n) {
-      sw_store(kr, ks, tid);
-      sw_store(vr, vs, tid);
-      __syncthreads();
-      const int lim = kv_limit(j);
-      if (n + 1 < cnt) {
-        j = cube_at(n + 1);
-        sw_load(kr, k + hoff + (size_t)max(j, 0) * 64 * D, tid);
-        sw_load(vr, v + hoff + (size_t)max(j, 0) * 64 * D, tid);
-      }
-      f32x4 p[4][2], dp[4][2];
-      {
-        const Frag<T> o0 = sw_frag<T, D>(dos, 32 * w + cc, 0, g);
-        const Frag<T> o1 = sw_frag<T, D>(dos, 32 * w + 16 + cc, 0, g);
+    const int j0 = cube_of(entry(0), lim_a);
+    VSA2_FETCH_KV(j0, tA);
+    if (cnt > 1) raw = entry(1);
+  }
+  for (int n = 0; n < cnt; n += 2) {
+    wait_vm0();
+    __syncthreads();  // stage A holds entry n; every wave is done with stage B
+    if (n + 1 < cnt) {
+      const int jj = cube_of(raw, lim_b);
+      if (n + 2 < cnt) raw = entry(n + 2);
+      VSA2_FETCH_KV(jj, tB);
+    }
+    if (lim_a > 32 * kh) dq_pair<T, D>(tA, tA + TILE, brow, btr, lim_a, qf, of, l2, dl, dqa, kh, g, cc, c);
+    if (n + 1 >= cnt) break;
+    wait_vm0();
+    __syncthreads();  // stage B holds entry n + 1; every wave is done with stage A
+    if (n + 2 < cnt) {
+      const int jj = cube_of(raw, lim_a);
+      if (n + 3 < cnt) raw = entry(n + 3);
+      VSA2_FETCH_KV(jj, tA);
+    }
+    if (lim_b > 32 * kh) dq_pair<T, D>(tB, tB + TILE, brow, btr, lim_b, qf, of, l2, dl, dqa, kh, g, cc, c);
+  }
+#undef VSA2_FETCH_KV
+
+  // sum the two key halves through LDS
+  __syncthreads();
+  constexpr int PART = (D / 16) * 2 * 4 * 64;
+  static_assert(PART * sizeof(float) <= sizeof(tA), "reduction buffer must fit a stage");
+  float* mine = reinterpret_cast<float*>(qh ? tB : tA);
+  if (kh == 1) {
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-          const Frag<T> a = sw_frag<T, D>(ks, 16 * kb + cc, 0, g);
-          p[kb][0] = mma0(a, qf[0][0]);
-          p[kb][1] = mma0(a, qf[1][0]);
-          const Frag<T> b = sw_frag<T, D>(vs, 16 * kb + cc, 0, g);
-          dp[kb][0] = mma0(b, o0);
-          dp[kb][1] = mma0(b, o1);
-        }
-      }
+    for (int db = 0; db < D / 16; ++db)
 #pragma unroll
-      for (int s = 1; s < D / 32; ++s) {
-        const Frag<T> o0 = sw_frag<T, D>(dos, 32 * w + cc, s, g);
-        const Frag<T> o1 = sw_frag<T, D>(dos, 32 * w + 16 + cc, s, g);
+      for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-          const Frag<T> a = sw_frag<T, D>(ks, 16 * kb + cc, s, g);
-          mma(p[kb][0], a, qf[0][s]);
-          mma(p[kb][1], a, qf[1][s]);
-          const Frag<T> b = sw_frag<T, D>(vs, 16 * kb + cc, s, g);
-          mma(dp[kb][0], b, o0);
-          mma(dp[kb][1], b, o1);
-        }
-      }
+        for (int r = 0; r < 4; ++r) mine[((db * 2 + qb) * 4 + r) * 64 + lane] = dqa[db][qb][r];
+  }
+  __syncthreads();
+  if (kh == 1) return;
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
+  for (int db = 0; db < D / 16; ++db)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const bool kin = 16 * kb + 4 * g + r < lim;
+    for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-          for (int qb = 0; qb < 2; ++qb) {
-            const float pe = kin ? fast_exp2(fmaf(p[kb][qb][r], c, -lse2[qb])) : 0.f;
-            dp[kb][qb][r] = pe * (dp[kb][qb][r] - del[qb]);
-          }
-        }
-      // dQ^T += K^T dS^T
+      for (int r = 0; r < 4; ++r)
+        dqa[db][qb][r] = (dqa[db][qb][r] + mine[((db * 2 + qb) * 4 + r) * 64 + lane]) * scale;
+  if (dq_add) {  // the coarse branch's per-cube gradient row, 1/64 to every token
+    const float* qa = dq_add + ((size_t)bh * nq + i) * D;
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const Frag<T> f0 = frag_from_acc<T>(dp[2 * h][0], dp[2 * h + 1][0]);
-        const Frag<T> f1 = frag_from_acc<T>(dp[2 * h][1], dp[2 * h + 1][1]);
+    for (int db = 0; db < D / 16; ++db) {
+      const f32x4 a4 = *reinterpret_cast<const f32x4*>(qa + 16 * db + 4 * g);
 #pragma unroll
-        for (int db = 0; db < D / 16; ++db) {
-          const Frag<T> a = sw_frag_tr<T, D>(ks, 32 * h, 16 * db, g, cc);
-          mma(dqa[db][0], a, f0);
-          mma(dqa[db][1], a, f1);
-        }
-      }
-      __syncthreads();
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) dqa[db][qb][r] += a4[r] * (1.0f / 64.0f);
     }
   }
-
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
-    const int qrow = i * 64 + 32 * w + 16 * qb + cc;
+    const int qrow = i * 64 + 32 * qh + 16 * qb + cc;
     const bool live = DENSE ? (qrow < seq && qrow < out_rows) : (qrow < out_rows);
     if (!live) continue;
     TO* dst = dq + ((size_t)bh * out_rows + qrow) * D;
-    const float* qa = dq_add ? dq_add + ((size_t)bh * nq + i) * D : nullptr;
 #pragma unroll
     for (int db = 0; db < D / 16; ++db) {
       Vec4<TO> a4;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int d = 16 * db + 4 * g + r;
-        a4.v[r] = from_f32<TO>(dqa[db][qb][r] * scale + (qa ? qa[d] * (1.0f / 64.0f) : 0.f));
-      }
+      for (int r = 0; r < 4; ++r) a4.v[r] = from_f32<TO>(dqa[db][qb][r]);
       store4(dst + 16 * db + 4 * g, a4);
     }
   }
 }
 
 template <typename T, int D>
-hipError_t launch_delta_t(const AttnBwdArgs& a, float* delta, hipStream_t st) {
+hipError_t launch_delta_t(const AttnBwdArgs& a, float* stats, hipStream_t st) {
   const size_t rows = (size_t)a.bh * a.ld;
   const size_t threads = rows * (D / 8);
   hipLaunchKernelGGL((k_bwd_delta<T, D>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st, (const T*)a.o,
-                     (const T*)a.d_o, delta, rows);
+                     (const T*)a.d_o, a.lse, stats, rows);
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_delta(const AttnBwdArgs& a, float* delta, hipStream_t st) {
-  if (a.bf16) return a.d == 128 ? launch_delta_t<bf16, 128>(a, delta, st) : launch_delta_t<bf16, 64>(a, delta, st);
-  return a.d == 128 ? launch_delta_t<float, 128>(a, delta, st) : launch_delta_t<float, 64>(a, delta, st);
+hipError_t launch_bwd_delta(const AttnBwdArgs& a, float* stats, hipStream_t st) {
+  if (a.bf16) return a.d == 128 ? launch_delta_t<bf16, 128>(a, stats, st) : launch_delta_t<bf16, 64>(a, stats, st);
+  return a.d == 128 ? launch_delta_t<float, 128>(a, stats, st) : launch_delta_t<float, 64>(a, stats, st);
 }
 
 template <typename T, typename TO, int D, bool DENSE>
 hipError_t launch_bwd_tt(const AttnBwdArgs& a, hipStream_t st) {
   if (!DENSE) timer_before(TK_BWD_DKDV, st);
-  hipLaunchKernelGGL((k_bwd_dkdv<T, TO, D, DENSE>), dim3(xcd_grid(a.nkv, a.bh)), dim3(128), 0, st, (const T*)a.q,
-                     (const T*)a.k, (const T*)a.v, (const T*)a.d_o, a.lse, a.delta, a.col_ptr, a.row_idx, a.dk_add,
-                     a.dv_add, (TO*)a.dk, (TO*)a.dv, a.nq, a.nkv, a.seq, a.ld, a.out_rows, a.lse_rows, a.kph, a.scale,
-                     a.scale_log2, 0, 0, 0);
+  hipLaunchKernelGGL((k_bwd_dkdv<T, TO, D, DENSE>), dim3(xcd_grid(a.nkv, a.bh)), dim3(256), 0, st, (const T*)a.q,
+                     (const T*)a.k, (const T*)a.v, (const T*)a.d_o, a.stats, a.col_ptr, a.row_idx, a.dk_add,
+                     a.dv_add, (TO*)a.dk, (TO*)a.dv, a.nq, a.nkv, a.seq, a.ld, a.out_rows, a.kph, a.scale,
+                     a.scale_log2);
   if (!DENSE) timer_after(TK_BWD_DKDV, st);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (!DENSE) timer_before(TK_BWD_DQ, st);
-  hipLaunchKernelGGL((k_bwd_dq<T, TO, D, DENSE>), dim3(xcd_grid(a.nq, a.bh)), dim3(128), 0, st, (const T*)a.q,
-                     (const T*)a.k, (const T*)a.v, (const T*)a.d_o, a.lse, a.delta, a.row_ptr, a.col_idx, a.dq_add,
-                     (TO*)a.dq, a.nq, a.nkv, a.seq, a.ld, a.out_rows, a.lse_rows, a.kph, a.scale, a.scale_log2, a.ct,
-                     a.cy, a.cx);
+  hipLaunchKernelGGL((k_bwd_dq<T, TO, D, DENSE>), dim3(xcd_grid(a.nq, a.bh)), dim3(256), 0, st, (const T*)a.q,
+                     (const T*)a.k, (const T*)a.v, (const T*)a.d_o, a.stats, a.row_ptr, a.col_idx, a.dq_add,
+                     (TO*)a.dq, a.nq, a.nkv, a.seq, a.ld, a.out_rows, a.kph, a.scale, a.scale_log2, a.ct, a.cy,
+                     a.cx);
   if (!DENSE) timer_after(TK_BWD_DQ, st);
   return hipGetLastError();
 }

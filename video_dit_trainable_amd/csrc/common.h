@@ -361,6 +361,87 @@ __device__ __forceinline__ Frag<T> sw_frag_tr(const T* lds, int r0, int col0, in
   return f;
 }
 
+// Direct global -> LDS copy of a swizzled R x W tile (global_load_lds_dwordx4,
+// no staging registers).  One instruction of a wave fills 1 KiB of LDS in lane
+// order (lane i writes bytes 16i .. 16i+15 after the wave's base), so the lane
+// that fills physical chunk pc of row r fetches logical chunk pc ^ f(r) -- the
+// same layout sw_store makes.  The copy is asynchronous: the caller waits with
+// wait_vm0() and then a barrier before any wave reads the tile.
+// Keeps the compiler from hoisting address arithmetic on x out of a loop
+// (an empty statement that claims to update the register).
+__device__ __forceinline__ void opaque(int& x) { asm volatile("" : "+v"(x)); }
+
+// one 16-byte LDS-direct load per lane (kept out of templates: the host pass
+// cannot resolve the builtin inside a dependent context)
+__device__ __forceinline__ void lds_copy16(const void* g, VSA2_LDS void* l) {
+  __builtin_amdgcn_global_load_lds(g, l, 16, 0, 0);
+}
+template <int R, int W, typename T, int NT>
+__device__ __forceinline__ void dma_tile(const T* __restrict__ src, T* lds, int tid) {
+  using S = SwTile<T, W>;
+  constexpr int CH = R * S::NCH;
+  static_assert(CH % NT == 0 && NT % 64 == 0 && NT % S::NCH == 0, "tile chunks must split evenly over whole waves");
+  // Row r = n (NT / NCH) + tid / NCH: when NT / NCH is a multiple of 16 the
+  // low four bits of r, and so the swizzle term, are the same for every n and
+  // the per-lane offset is computed once.
+  constexpr int RSTEP = NT / S::NCH;
+  const int r0 = tid / S::NCH, pc = tid % S::NCH;
+  int lane_off = (r0 * W + S::EPC * (pc ^ (S::f(r0) & (S::NCH - 1)))) * (int)sizeof(T);
+  opaque(lane_off);  // keeps "base + lane_off" from being hoisted as a 64-bit per-lane pointer
+  const int wbase = __builtin_amdgcn_readfirstlane(tid & ~63);
+#pragma unroll
+  for (int n = 0; n < CH / NT; ++n) {
+    uint32_t off;
+    if constexpr (RSTEP % 16 == 0) {
+      off = (uint32_t)lane_off + (uint32_t)(n * RSTEP * W * sizeof(T));
+    } else {
+      const int r = r0 + n * RSTEP;
+      off = (uint32_t)(r * W + S::EPC * (pc ^ (S::f(r) & (S::NCH - 1)))) * sizeof(T);
+    }
+    T* lbase = lds + (n * NT + wbase) * S::EPC;  // wave-uniform
+    lds_copy16(reinterpret_cast<const char*>(src) + off, (VSA2_LDS void*)lbase);
+  }
+}
+// Wait until every vector-memory load of this wave (including LDS-direct
+// copies) has completed: s_waitcnt vmcnt(0), other counters untouched.
+__device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// The same two fragment reads for bf16 tiles with the per-lane part of the
+// address computed once.  For a row-major swizzled tile the k-step s of
+// sw_frag(r, s, g) sits at element (base ^ 32 s) with base = sw_row_base(r, g),
+// and the columns col0 (a multiple of 16) of sw_frag_tr(r0, col0, g, c) at
+// (base ^ col0) with base = sw_tr_base(r0, g, c): the swizzle only permutes
+// 16-byte chunks inside a row, so the step's contribution is a pure XOR.
+template <typename T, int W>
+__device__ __forceinline__ int sw_row_base(int r, int g) {
+  using S = SwTile<T, W>;
+  static_assert(sizeof(T) == 2 && S::EPC == 8, "bf16 tiles only");
+  const int f = S::f(r) & (S::NCH - 1);
+  return r * W + 8 * (f & ~3) + 8 * (g ^ (f & 3));
+}
+template <typename T, int W>
+__device__ __forceinline__ int sw_tr_base(int r0, int g, int c) {
+  using S = SwTile<T, W>;
+  static_assert(sizeof(T) == 2 && S::EPC == 8, "bf16 tiles only");
+  const int ra = r0 + 4 * g + (c >> 2);
+  const int f = S::f(ra) & (S::NCH - 1);
+  return ra * W + 8 * (f & ~1) + 8 * (((c >> 1) & 1) ^ (f & 1)) + 4 * (c & 1);
+}
+template <typename T>
+__device__ __forceinline__ Frag<T> sw_frag_at(const T* lds, int base, int s) {
+  return frag_from8(load8(lds + (base ^ (32 * s))));
+}
+// rows ra (from the base) and ra + 16 of the transposed read; W = row length
+template <typename T, int W>
+__device__ __forceinline__ Frag<T> sw_frag_tr_at(const T* lds, int base, int col0) {
+  const T* pa = lds + (base ^ col0);
+  const s16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((VSA2_LDS s16x4*)(pa));
+  const s16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((VSA2_LDS s16x4*)(pa + 16 * W));
+  Vec8<T> v;
+  __builtin_memcpy(&v.v[0], &va, 8);
+  __builtin_memcpy(&v.v[4], &vb, 8);
+  return frag_from8(v);
+}
 // Butterfly reductions over the four slot groups (lanes c, c+16, c+32, c+48).
 __device__ __forceinline__ float group_max(float x) {
   x = fmaxf(x, __shfl_xor(x, 16));

@@ -129,7 +129,8 @@ template <typename T, int D>
 __global__ __launch_bounds__(256) void k_gate_bwd(const T* __restrict__ wt, const float* __restrict__ oc_hat,
                                                   const float* __restrict__ gin, const T* __restrict__ d_o,
                                                   float* __restrict__ dpre, T* __restrict__ doc,
-                                                  float* __restrict__ delta_c, T* __restrict__ dx, int H, int nb,
+                                                  const float* __restrict__ lse_c, float* __restrict__ stats_c,
+                                                  T* __restrict__ dx, int H, int nb,
                                                   int nbp, int dm, int hp, int hk) {
   constexpr bool SPLIT = sizeof(T) == 2;
   constexpr int UPR = D / 8;
@@ -182,14 +183,20 @@ __global__ __launch_bounds__(256) void k_gate_bwd(const T* __restrict__ wt, cons
     for (int s = 1; s < 64; s <<= 1) prod += __shfl_xor(prod, s);
     if (lane == 0) wsum[w] = prod;
     __syncthreads();
-    if (tid == 0) delta_c[bh * nbp + c] = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+    if (tid == 0) {
+      stats_c[2 * (bh * nbp + c)] = lse_c[bh * nb + c] * LOG2E;
+      stats_c[2 * (bh * nbp + c) + 1] = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+    }
   }
-  // zero the padding rows of dO_hat_c / delta_c
+  // zero the padding rows of dO_hat_c and mask them in the row statistics
   for (int row = nb + c; row < nbp; row += nb)
     for (int h = 0; h < H; ++h) {
       const size_t bh = (size_t)b * H + h;
       for (int d = tid; d < D; d += 256) doc[(bh * nbp + row) * D + d] = from_f32<T>(0.f);
-      if (tid == 0) delta_c[bh * nbp + row] = 0.f;
+      if (tid == 0) {
+        stats_c[2 * (bh * nbp + row)] = INFINITY;
+        stats_c[2 * (bh * nbp + row) + 1] = 0.f;
+      }
     }
   __syncthreads();
   // dX^T[m][t] = sum_h W_g[m][h] dpre[t][h]
@@ -323,7 +330,8 @@ hipError_t launch_gate_bwd_t(const GateBwdArgs& a, hipStream_t st) {
   if (e != hipSuccess) return e;
   const int hp = pad_up(a.heads, 16), hk = pad_up(a.heads, 32);
   hipLaunchKernelGGL((k_gate_bwd<T, D>), dim3(a.nb, a.batch), dim3(256), 0, st, (const T*)a.wt, a.oc_hat, a.g,
-                     (const T*)a.d_o, a.dpre, (T*)a.doc, a.delta_c, (T*)a.dx, a.heads, a.nb, a.nbp, a.dm, hp, hk);
+                     (const T*)a.d_o, a.dpre, (T*)a.doc, a.lse_c, a.stats_c, (T*)a.dx, a.heads, a.nb, a.nbp, a.dm, hp,
+                     hk);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((k_dwg_part<T>), dim3(a.dm / 64, a.nchunk, a.batch), dim3(256), 0, st, (const T*)a.x, a.dpre,
