@@ -5,11 +5,19 @@
 // averages the 8 x 8 (query sub-cube, key sub-cube) entries of each cube pair.
 // Only the nb x nb block scores reach memory.
 //
-// Work split: a block owns 64 pooled queries (8 query cubes); each of its 4
-// waves holds 16 of them as B fragments in registers and streams all pooled
-// keys, 64 at a time, through a double-buffered LDS tile.  The accumulator of
-// S^T = K_r Q_r^T gives each lane 4 keys x 1 query per 16-key block, so the
-// 8 x 8 pooling is 4 in-lane adds + one cross-group and three in-row shuffles.
+// Work split: a 256-thread block owns 128 pooled queries (16 query cubes);
+// wave w holds queries 32w .. 32w+31 as MFMA B fragments in registers and
+// streams all pooled keys of the head, 64 at a time, through two LDS stages
+// filled by LDS-direct copies (distinct arrays, loop unrolled by two, so a
+// copy into one stage never makes the reads of the other wait).
+//
+// Key order inside a staged tile: LDS row 16 kb + c holds pooled key
+//   pi(kb, c) = 32 (kb >> 1) + 4 (kb & 1) + 8 (c >> 2) + (c & 3)
+// of the 64-key tile.  The accumulator of S^T = K Q^T for 16-row block kb
+// gives lane (g, c) rows 4g .. 4g+3, i.e. keys pi(kb, 4g + r) =
+// 8 (4 (kb >> 1) + g) + 4 (kb & 1) + r: over kb = 2h, 2h+1 and r = 0..3 one lane
+// holds all 8 keys of key cube 4h + g.  The 8 x 8 pooling is then 7 in-lane
+// adds and a 3-step DPP reduction over the 8 query lanes of a query cube.
 #include <cmath>
 
 #include "common.h"
@@ -17,108 +25,193 @@
 
 namespace vsa2 {
 
+namespace {
+
+constexpr int RQ = 128;  // pooled queries per block
+constexpr int RK = 64;   // pooled keys per staged tile
+
+__device__ __forceinline__ int key_of_row(int r) {
+  const int kb = r >> 4, c = r & 15;
+  return 32 * (kb >> 1) + 4 * (kb & 1) + 8 * (c >> 2) + (c & 3);
+}
+
+// Copy keys [k0, k0 + 64) of one head's K_r (rows of D elements) into a
+// swizzled LDS tile in the order above; keys at or past nkeys read key
+// nkeys - 1 (masked by the caller).
+template <typename T, int D>
+__device__ __forceinline__ void dma_keys(const T* __restrict__ kr, int k0, int nkeys, T* lds, int tid) {
+  using S = SwTile<T, D>;
+  constexpr int RSTEP = 256 / S::NCH;
+  static_assert(RK * S::NCH % 256 == 0, "tile chunks must split evenly over the block");
+  const int wbase = __builtin_amdgcn_readfirstlane(tid & ~63);
+  const int pc = tid % S::NCH;
+#pragma unroll
+  for (int n = 0; n < RK * S::NCH / 256; ++n) {
+    const int r = n * RSTEP + tid / S::NCH;
+    const int key = min(k0 + key_of_row(r), nkeys - 1);
+    int off = (key * D + S::EPC * (pc ^ (S::f(r) & (S::NCH - 1)))) * (int)sizeof(T);
+    opaque(off);
+    lds_copy16(reinterpret_cast<const char*>(kr) + (uint32_t)off, (VSA2_LDS void*)(lds + (n * 256 + wbase) * S::EPC));
+  }
+}
+
+// Sum over the 8 lanes c, c^1, .., c^7 of a row-group of 8 (DPP, no LDS).
+__device__ __forceinline__ float sum8(float x) {
+  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, true));   // quad_perm [1,0,3,2]
+  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, true));   // quad_perm [2,3,0,1]
+  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x141, 0xF, 0xF, true));  // row_half_mirror
+  return x;
+}
+
+// One 64-key tile for one wave: acc[kb][qb] = S^T block (keys of LDS rows
+// 16kb + 4g + r, query 32w + 16qb + c), unscaled.
+template <typename T, int D>
+__device__ __forceinline__ void tile_scores(const T* ks, int brow, const Frag<T> (&qf)[2][D / 32], int g, int cc,
+                                            f32x4 (&acc)[4][2]) {
+  opaque(brow);
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+    Frag<T> a;
+    if constexpr (sizeof(T) == 2) a = sw_frag_at<T>(ks, brow + 16 * kb * D, 0);
+    else a = sw_frag<T, D>(ks, 16 * kb + cc, 0, g);
+    acc[kb][0] = mma0(a, qf[0][0]);
+    acc[kb][1] = mma0(a, qf[1][0]);
+  }
+#pragma unroll
+  for (int s = 1; s < D / 32; ++s)
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      Frag<T> a;
+      if constexpr (sizeof(T) == 2) a = sw_frag_at<T>(ks, brow + 16 * kb * D, s);
+      else a = sw_frag<T, D>(ks, 16 * kb + cc, s, g);
+      mma(acc[kb][0], a, qf[0][s]);
+      mma(acc[kb][1], a, qf[1][s]);
+    }
+}
+
+// keys of a tile at or past nkeys get -inf (only the last tile can have them)
+__device__ __forceinline__ void mask_tail(f32x4 (&acc)[4][2], int k0, int nkeys, int g) {
+  if (k0 + RK <= nkeys) return;
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (k0 + key_of_row(16 * kb + 4 * g + r) >= nkeys) acc[kb][0][r] = acc[kb][1][r] = -INFINITY;
+}
+
+}  // namespace
+
 template <typename T, int D, bool PASS2>
-__global__ __launch_bounds__(256) void k_router(const T* __restrict__ qr, const T* __restrict__ kr,
-                                                float* __restrict__ lse2, float* __restrict__ scores, int nb,
-                                                float c) {
-  using G = TileGeom<T, D>;
-  __shared__ T ks[2][G::RM_ELEMS];
+__global__ __launch_bounds__(256, 2) void k_router(const T* __restrict__ qr, const T* __restrict__ kr,
+                                                   float* __restrict__ lse2, float* __restrict__ scores, int nb,
+                                                   float c) {
+  __shared__ __align__(16) T kA[RK * D];
+  __shared__ __align__(16) T kB[RK * D];
   const int Lr = 8 * nb;
-  const int ntile = (Lr + 63) / 64;
+  const int nqt = (Lr + RQ - 1) / RQ, nkt = (Lr + RK - 1) / RK;
   int bh, qt;
-  if (!xcd_work(blockIdx.x, ntile, bh, qt)) return;
+  if (!xcd_work(blockIdx.x, nqt, bh, qt)) return;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, cc = lane & 15;
-  const int qrow = qt * 64 + 16 * w + cc;
   const T* qbase = qr + (size_t)bh * Lr * D;
   const T* kbase = kr + (size_t)bh * Lr * D;
 
-  Frag<T> qf[D / 32];
+  // this wave's 32 pooled queries as B fragments: query qt*128 + 32w + 16qb + cc
+  Frag<T> qf[2][D / 32];
+  float lse[2];
 #pragma unroll
-  for (int s = 0; s < D / 32; ++s) {
-    if (qrow < Lr) {
-      qf[s] = frag_global<T, D>(qbase, qrow, s, g);
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) qf[s].v[e] = from_f32<T>(0.f);
-    }
-  }
-
-  TileRegs<T, D, 256> regs;
-  tile_load<T, D, 256>(regs, kbase, tid, min(64, Lr));
-  tile_store_rm<T, D, 256>(regs, ks[0], tid);
-  __syncthreads();
-
-  float m = -INFINITY, l = 0.f;
-  float lse = 0.f;
-  if constexpr (PASS2) lse = qrow < Lr ? lse2[(size_t)bh * Lr + qrow] : INFINITY;
-
-  for (int t = 0; t < ntile; ++t) {
-    if (t + 1 < ntile) tile_load<T, D, 256>(regs, kbase + (size_t)(t + 1) * 64 * D, tid, min(64, Lr - (t + 1) * 64));
-    const T* kl = ks[t & 1];
-    f32x4 acc[4];
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) acc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int qb = 0; qb < 2; ++qb) {
+    const int qrow = qt * RQ + 32 * w + 16 * qb + cc;
 #pragma unroll
     for (int s = 0; s < D / 32; ++s) {
+      if (qrow < Lr) {
+        qf[qb][s] = frag_global<T, D>(qbase, qrow, s, g);
+      } else {
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) mma(acc[kb], frag_rm<T, D>(kl, 16 * kb + cc, s, g), qf[s]);
-    }
-    if (t * 64 + 64 > Lr) {
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (t * 64 + 16 * kb + 4 * g + r >= Lr) acc[kb][r] = -INFINITY;
-    }
-    if constexpr (!PASS2) {
-      float mt = acc[0][0];
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) mt = fmaxf(mt, acc[kb][r]);
-      if (mt > m) {
-        l *= fast_exp2((m - mt) * c);
-        m = mt;
+        for (int e = 0; e < 8; ++e) qf[qb][s].v[e] = from_f32<T>(0.f);
       }
-      if (m != -INFINITY) {
-        const float mc = -m * c;
+    }
+    if constexpr (PASS2) lse[qb] = qrow < Lr ? lse2[(size_t)bh * Lr + qrow] : INFINITY;
+  }
+  int brow = 0;
+  if constexpr (sizeof(T) == 2) brow = sw_row_base<T, D>(cc, g);
+
+  float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};  // pass 1: running max / sum (scaled log2 domain)
+
+  auto consume = [&](const f32x4 (&acc)[4][2], int t) {
+    if constexpr (!PASS2) {
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        float mt = acc[0][qb][0];
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) l += fast_exp2(fmaf(acc[kb][r], c, mc));
+          for (int r = 0; r < 4; ++r) mt = fmaxf(mt, acc[kb][qb][r]);
+        if (mt > m[qb]) {
+          l[qb] *= fast_exp2((m[qb] - mt) * c);
+          m[qb] = mt;
+        }
+        if (m[qb] != -INFINITY) {
+          const float mc = -m[qb] * c;
+#pragma unroll
+          for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) l[qb] += fast_exp2(fmaf(acc[kb][qb][r], c, mc));
+        }
       }
     } else {
-      const int qcube = qt * 8 + 2 * w + (cc >> 3);
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        float s4 = 0.f;
+      for (int qb = 0; qb < 2; ++qb) {
+        const int qcube = (qt * RQ + 32 * w + 16 * qb + cc) >> 3;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) s4 += fast_exp2(fmaf(acc[kb][r], c, -lse));
-        s4 += __shfl_xor(s4, 16);
-        s4 += __shfl_xor(s4, 1);
-        s4 += __shfl_xor(s4, 2);
-        s4 += __shfl_xor(s4, 4);
-        const int kcube = t * 8 + 2 * kb + (g >> 1);
-        if ((g & 1) == 0 && (cc & 7) == 0 && qcube < nb && kcube < nb)
-          scores[((size_t)bh * nb + qcube) * nb + kcube] = s4 * (1.0f / 64.0f);
+        for (int h = 0; h < 2; ++h) {
+          float s8 = 0.f;
+#pragma unroll
+          for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) s8 += fast_exp2(fmaf(acc[2 * h + kk][qb][r], c, -lse[qb]));
+          s8 = sum8(s8);
+          const int kcube = t * (RK / 8) + 4 * h + g;
+          if ((cc & 7) == 0 && qcube < nb && kcube < nb)
+            scores[((size_t)bh * nb + qcube) * nb + kcube] = s8 * (1.0f / 64.0f);
+        }
       }
     }
-    if (t + 1 < ntile) tile_store_rm<T, D, 256>(regs, ks[(t + 1) & 1], tid);
-    __syncthreads();
+  };
+
+  dma_keys<T, D>(kbase, 0, Lr, kA, tid);
+  for (int t = 0; t < nkt; t += 2) {
+    f32x4 acc[4][2];
+    wait_vm0();
+    __syncthreads();  // stage A holds tile t; every wave is done with stage B
+    if (t + 1 < nkt) dma_keys<T, D>(kbase, (t + 1) * RK, Lr, kB, tid);
+    tile_scores<T, D>(kA, brow, qf, g, cc, acc);
+    mask_tail(acc, t * RK, Lr, g);
+    consume(acc, t);
+    if (t + 1 >= nkt) break;
+    wait_vm0();
+    __syncthreads();  // stage B holds tile t + 1; every wave is done with stage A
+    if (t + 2 < nkt) dma_keys<T, D>(kbase, (t + 2) * RK, Lr, kA, tid);
+    tile_scores<T, D>(kB, brow, qf, g, cc, acc);
+    mask_tail(acc, (t + 1) * RK, Lr, g);
+    consume(acc, t + 1);
   }
 
   if constexpr (!PASS2) {
-    const float M = group_max(m);
-    const float part = (m == -INFINITY) ? 0.f : l * fast_exp2((m - M) * c);
-    const float lt = group_sum(part);
-    if (g == 0 && qrow < Lr) lse2[(size_t)bh * Lr + qrow] = M * c + __log2f(lt);
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      const int qrow = qt * RQ + 32 * w + 16 * qb + cc;
+      const float M = group_max(m[qb]);
+      const float part = (m[qb] == -INFINITY) ? 0.f : l[qb] * fast_exp2((m[qb] - M) * c);
+      const float lt = group_sum(part);
+      if (g == 0 && qrow < Lr) lse2[(size_t)bh * Lr + qrow] = M * c + __log2f(lt);
+    }
   }
 }
 
 template <typename T, int D>
 hipError_t launch_route_t(const RouteArgs& a, hipStream_t st) {
-  const int ntile = (8 * a.nb + 63) / 64;
-  dim3 grid(xcd_grid(ntile, a.bh));
+  const int nqt = (8 * a.nb + RQ - 1) / RQ;
+  dim3 grid(xcd_grid(nqt, a.bh));
   timer_before(TK_ROUTER_LSE, st);
   hipLaunchKernelGGL((k_router<T, D, false>), grid, dim3(256), 0, st, (const T*)a.qr, (const T*)a.kr, a.lse2,
                      a.scores, a.nb, a.scale_log2);
