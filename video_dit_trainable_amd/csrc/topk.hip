@@ -38,7 +38,9 @@ hipError_t launch_fill_u32(uint32_t* p, uint32_t val, size_t n, hipStream_t st) 
 }
 
 // Histogram of digit (u >> SHIFT) & (2^BITS - 1) over the entries whose bits
-// above SHIFT+BITS equal the prefix found by the previous passes.
+// above SHIFT+BITS equal the prefix found by the previous passes.  Each thread
+// reads 4 consecutive scores per step (n is a multiple of 4 for every head:
+// n = nb^2 is, or the head offset breaks alignment and the scalar path runs).
 template <int SHIFT, int BITS>
 __global__ __launch_bounds__(256) void k_hist(const float* __restrict__ scores, uint32_t* __restrict__ hist,
                                               const uint32_t* __restrict__ state, size_t n) {
@@ -49,11 +51,21 @@ __global__ __launch_bounds__(256) void k_hist(const float* __restrict__ scores, 
   __syncthreads();
   const uint32_t prefix = (SHIFT + BITS < 32) ? state[bh * 4 + 0] : 0u;
   const float* s = scores + (size_t)bh * n;
-  for (size_t i = (size_t)blockIdx.x * 256 + tid; i < n; i += (size_t)gridDim.x * 256) {
-    const uint32_t u = score_bits(s[i]);
+  auto add = [&](float x) {
+    const uint32_t u = score_bits(x);
     bool ok = true;
     if constexpr (SHIFT + BITS < 32) ok = (u >> (SHIFT + BITS)) == (prefix >> (SHIFT + BITS));
     if (ok) atomicAdd(&h[(u >> SHIFT) & (NBIN - 1)], 1u);
+  };
+  if ((n & 3) == 0) {
+    const float4* s4 = reinterpret_cast<const float4*>(s);
+    const size_t n4 = n / 4;
+    for (size_t i = (size_t)blockIdx.x * 256 + tid; i < n4; i += (size_t)gridDim.x * 256) {
+      const float4 v = s4[i];
+      add(v.x); add(v.y); add(v.z); add(v.w);
+    }
+  } else {
+    for (size_t i = (size_t)blockIdx.x * 256 + tid; i < n; i += (size_t)gridDim.x * 256) add(s[i]);
   }
   __syncthreads();
   for (int b = tid; b < NBIN; b += 256)
@@ -96,7 +108,8 @@ __global__ __launch_bounds__(256) void k_select(const uint32_t* __restrict__ his
   }
 }
 
-// Per row: entries > tau and == tau (one wave per row).
+// Per row: entries > tau and == tau (one wave per row; 4 columns per lane and
+// step when rows are 16-byte aligned, nb % 4 == 0).
 __global__ __launch_bounds__(256) void k_rowcount(const float* __restrict__ scores, const uint32_t* __restrict__ state,
                                                   uint32_t* __restrict__ rowcnt, int nb) {
   const int bh = blockIdx.y, row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
@@ -104,11 +117,31 @@ __global__ __launch_bounds__(256) void k_rowcount(const float* __restrict__ scor
   const uint32_t tau = state[bh * 4 + 0];
   const float* s = scores + ((size_t)bh * nb + row) * nb;
   uint32_t gt = 0, eq = 0;
-  for (int j0 = 0; j0 < nb; j0 += 64) {
-    const int j = j0 + lane;
-    const uint32_t u = j < nb ? score_bits(s[j]) : 0u;
-    gt += __popcll(__ballot(j < nb && u > tau));
-    eq += __popcll(__ballot(j < nb && u == tau));
+  if ((nb & 3) == 0) {
+    for (int j0 = 0; j0 < nb; j0 += 256) {
+      const int j = j0 + 4 * lane;
+      if (j < nb) {
+        const float4 v = *reinterpret_cast<const float4*>(s + j);
+        const uint32_t u[4] = {score_bits(v.x), score_bits(v.y), score_bits(v.z), score_bits(v.w)};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          gt += u[e] > tau;
+          eq += u[e] == tau;
+        }
+      }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      gt += __shfl_xor(gt, o);
+      eq += __shfl_xor(eq, o);
+    }
+  } else {
+    for (int j0 = 0; j0 < nb; j0 += 64) {
+      const int j = j0 + lane;
+      const uint32_t u = j < nb ? score_bits(s[j]) : 0u;
+      gt += __popcll(__ballot(j < nb && u > tau));
+      eq += __popcll(__ballot(j < nb && u == tau));
+    }
   }
   if (lane == 0) {
     rowcnt[((size_t)bh * 2 + 0) * nb + row] = gt;
@@ -187,22 +220,34 @@ __global__ __launch_bounds__(256) void k_compact(const float* __restrict__ score
   uint32_t* bm = bitmap + ((size_t)bh * nb + row) * words;
   uint32_t eq_seen = 0, written = 0;
   const uint64_t lt = lanemask_lt(lane);
-  for (int j0 = 0; j0 < nb; j0 += 64) {
-    const int j = j0 + lane;
-    const uint32_t u = j < nb ? score_bits(s[j]) : 0u;
-    const bool is_eq = j < nb && u == tau;
-    const uint64_t eqm = __ballot(is_eq);
-    const uint32_t rank = eq_seen + __popcll(eqm & lt);
-    const bool sel = j < nb && (u > tau || (is_eq && rank < tk));
-    const uint64_t selm = __ballot(sel);
-    const int64_t slot = (int64_t)row_ptr[(size_t)bh * (nb + 1) + row] + written + __popcll(selm & lt);
-    if (sel && slot < kph) {
-      out[written + __popcll(selm & lt)] = j;
-      atomicAdd(&colcnt[(size_t)bh * nb + j], 1u);
+  const int64_t row0 = row_ptr[(size_t)bh * (nb + 1) + row];
+  for (int j1 = 0; j1 < nb; j1 += 256) {
+    uint32_t uu[4];  // four 64-column chunks loaded together, then compacted in column order
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int j = j1 + 64 * q + lane;
+      uu[q] = j < nb ? score_bits(s[j]) : 0u;
     }
-    if (lane < 2) bm[(j0 >> 5) + lane] = (uint32_t)(selm >> (32 * lane));
-    eq_seen += __popcll(eqm);
-    written += __popcll(selm);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int j0 = j1 + 64 * q;
+      if (j0 >= nb) break;
+      const int j = j0 + lane;
+      const uint32_t u = uu[q];
+      const bool is_eq = j < nb && u == tau;
+      const uint64_t eqm = __ballot(is_eq);
+      const uint32_t rank = eq_seen + __popcll(eqm & lt);
+      const bool sel = j < nb && (u > tau || (is_eq && rank < tk));
+      const uint64_t selm = __ballot(sel);
+      const uint32_t before = __popcll(selm & lt);
+      if (sel && row0 + written + before < kph) {
+        out[written + before] = j;
+        atomicAdd(&colcnt[(size_t)bh * nb + j], 1u);
+      }
+      if (lane < 2) bm[(j0 >> 5) + lane] = (uint32_t)(selm >> (32 * lane));
+      eq_seen += __popcll(eqm);
+      written += __popcll(selm);
+    }
   }
 }
 
@@ -250,6 +295,7 @@ __global__ __launch_bounds__(256) void k_csc_fill(const uint32_t* __restrict__ b
   const uint32_t* bm = bitmap + (size_t)bh * nb * words + 2 * strip + (lane >> 5);
   const uint32_t bit = 1u << (lane & 31);
   uint32_t c = 0;
+#pragma unroll 8
   for (int i = r0; i < r1; ++i) c += (bm[(size_t)i * words] & bit) ? 1u : 0u;
   cnt[w][lane] = c;
   __syncthreads();
@@ -257,6 +303,7 @@ __global__ __launch_bounds__(256) void k_csc_fill(const uint32_t* __restrict__ b
   uint32_t base = col_ptr[(size_t)bh * (nb + 1) + j];
   for (int ww = 0; ww < w; ++ww) base += cnt[ww][lane];
   int32_t* out = row_idx + (size_t)bh * kph;
+#pragma unroll 8
   for (int i = r0; i < r1; ++i)
     if ((bm[(size_t)i * words] & bit) && base < kph) out[base++] = i;
 }
