@@ -74,36 +74,62 @@ __global__ __launch_bounds__(256) void k_gate_fwd(const T* __restrict__ x, const
   const T* fhi = wt;
   const T* flo = wt + (size_t)hp * dm;
   const int nhb = hp / 16;
-  const size_t t0 = (size_t)c * CUBE + 16 * w;
-  f32x4 acc[HMAX / 16];
+  // gate products: wave w takes k-steps [w S/4, (w+1) S/4) of X W_g for all 64
+  // tokens (4 blocks of 16), so each wave reads a quarter of W_g; the four
+  // partial sums are added through LDS (one head block at a time, fixed order)
+  __shared__ float gpart[4][4][4][64];  // [wave][token block][r][lane]
+  f32x4 acc[4][HMAX / 16];
 #pragma unroll
-  for (int hb = 0; hb < HMAX / 16; ++hb) acc[hb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const T* xrow = x + ((size_t)b * L + t0 + cc) * dm;
-  for (int s = 0; s < dm / 32; ++s) {
-    const Frag<T> a = frag_from8(load8(xrow + 32 * s + 8 * g));
+  for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+    for (int hb = 0; hb < HMAX / 16; ++hb) acc[tb][hb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int S = dm / 32, s0 = w * S / 4, s1 = (w + 1) * S / 4;
+  const T* xblk = x + ((size_t)b * L + (size_t)c * CUBE + cc) * dm;
+#pragma unroll 2
+  for (int s = s0; s < s1; ++s) {
+    Frag<T> a[4];
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) a[tb] = frag_from8(load8(xblk + (size_t)16 * tb * dm + 32 * s + 8 * g));
 #pragma unroll
     for (int hb = 0; hb < HMAX / 16; ++hb) {
       if (hb < nhb) {
-        mma(acc[hb], a, frag_from8(load8(fhi + (size_t)(16 * hb + cc) * dm + 32 * s + 8 * g)));
-        if constexpr (SPLIT) mma(acc[hb], a, frag_from8(load8(flo + (size_t)(16 * hb + cc) * dm + 32 * s + 8 * g)));
+        const Frag<T> bhi = frag_from8(load8(fhi + (size_t)(16 * hb + cc) * dm + 32 * s + 8 * g));
+        Frag<T> blo;
+        if constexpr (SPLIT) blo = frag_from8(load8(flo + (size_t)(16 * hb + cc) * dm + 32 * s + 8 * g));
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) {
+          mma(acc[tb][hb], a[tb], bhi);
+          if constexpr (SPLIT) mma(acc[tb][hb], a[tb], blo);
+        }
       }
     }
   }
+  // acc[tb][hb] lane (g, c): tokens 16 tb + 4g + r (rows), head 16 hb + c (column)
+  for (int hb = 0; hb < nhb; ++hb) {
 #pragma unroll
-  for (int hb = 0; hb < HMAX / 16; ++hb) {
-    if (hb < nhb) {
-      const int h = 16 * hb + cc;
-      float4 gv;
-      gv.x = tanhf(acc[hb][0]); gv.y = tanhf(acc[hb][1]); gv.z = tanhf(acc[hb][2]); gv.w = tanhf(acc[hb][3]);
-      gs[16 * w + 4 * g + 0][h] = gv.x;
-      gs[16 * w + 4 * g + 1][h] = gv.y;
-      gs[16 * w + 4 * g + 2][h] = gv.z;
-      gs[16 * w + 4 * g + 3][h] = gv.w;
-      if (h < H) *reinterpret_cast<float4*>(gout + ((size_t)b * H + h) * L + t0 + 4 * g) = gv;
-    }
+    for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+      for (int hb2 = 0; hb2 < HMAX / 16; ++hb2)
+        if (hb2 == hb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) gpart[w][tb][r][lane] = acc[tb][hb2][r];
+    __syncthreads();
+    const int tb = w;  // wave w finishes token block w
+    const int h = 16 * hb + cc;
+    float v[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      v[r] = tanhf(gpart[0][tb][r][lane] + gpart[1][tb][r][lane] + gpart[2][tb][r][lane] + gpart[3][tb][r][lane]);
+    const size_t t0 = (size_t)c * CUBE + 16 * tb;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) gs[16 * tb + 4 * g + r][h] = v[r];
+    if (h < H)
+      *reinterpret_cast<float4*>(gout + ((size_t)b * H + h) * L + t0 + 4 * g) = make_float4(v[0], v[1], v[2], v[3]);
+    __syncthreads();
   }
   __syncthreads();
   constexpr int UPR = D / 8;  // units per token row
+#pragma unroll 4
   for (int h = 0; h < H; ++h) {
     const size_t bh = (size_t)b * H + h;
     const float* oc = oc_hat + (bh * nb + c) * D;
@@ -144,17 +170,41 @@ __global__ __launch_bounds__(256) void k_gate_bwd(const T* __restrict__ wt, cons
   for (int u = tid; u < 64 * (HMAX + 4); u += 256) dps[u / (HMAX + 4)][u % (HMAX + 4)] = 0.f;
   __syncthreads();
   const int dg = tid % UPR;
+  constexpr int TPT = 64 / RROWS;  // tokens per thread and head
+  // dO rows and gates of the next head are loaded while the current head is reduced
+  Vec8<T> xn[TPT];
+  float gn[TPT];
+  auto fetch = [&](int h) {
+    const size_t bh = (size_t)b * H + h;
+#pragma unroll
+    for (int i = 0; i < TPT; ++i) {
+      const size_t tok = (size_t)c * CUBE + tid / UPR + RROWS * i;
+      xn[i] = load8(d_o + (bh * L + tok) * D + 8 * dg);
+      gn[i] = gin[bh * L + tok];
+    }
+  };
+  if (H > 0) fetch(0);
   for (int h = 0; h < H; ++h) {
     const size_t bh = (size_t)b * H + h;
+    Vec8<T> xc[TPT];
+    float gc[TPT];
+#pragma unroll
+    for (int i = 0; i < TPT; ++i) {
+      xc[i] = xn[i];
+      gc[i] = gn[i];
+    }
+    if (h + 1 < H) fetch(h + 1);
     const float* oc = oc_hat + (bh * nb + c) * D;
     const float4 a0 = *reinterpret_cast<const float4*>(oc + 8 * dg);
     const float4 a1 = *reinterpret_cast<const float4*>(oc + 8 * dg + 4);
     const float ocv[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
     float pacc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int t = tid / UPR; t < 64; t += RROWS) {
+#pragma unroll
+    for (int i = 0; i < TPT; ++i) {
+      const int t = tid / UPR + RROWS * i;
       const size_t tok = (size_t)c * CUBE + t;
-      const Vec8<T> x = load8(d_o + (bh * L + tok) * D + 8 * dg);
-      const float gv = gin[bh * L + tok];
+      const Vec8<T> x = xc[i];
+      const float gv = gc[i];
       float part = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -250,11 +300,14 @@ __global__ __launch_bounds__(256) void k_dwg_part(const T* __restrict__ x, const
 #pragma unroll
   for (int hb = 0; hb < HMAX / 16; ++hb) acc[hb] = f32x4{0.f, 0.f, 0.f, 0.f};
   TileRegs<T, 64, 256> regs;
-  for (size_t t0 = (size_t)chunk * DW_TC; t0 < L && t0 < (size_t)(chunk + 1) * DW_TC; t0 += 64) {
-    tile_load<T, 64, 256>(regs, x + ((size_t)b * L + t0) * dm + 64 * mblk, tid, 64, (size_t)dm);
+  const size_t t_beg = (size_t)chunk * DW_TC, t_end = min(L, (size_t)(chunk + 1) * DW_TC);
+  if (t_beg < t_end) tile_load<T, 64, 256>(regs, x + ((size_t)b * L + t_beg) * dm + 64 * mblk, tid, 64, (size_t)dm);
+  for (size_t t0 = t_beg; t0 < t_end; t0 += 64) {
     __syncthreads();
     tile_store_tr<T, 64, 256>(regs, xt, tid);
     __syncthreads();
+    if (t0 + 64 < t_end)  // next tile's loads overlap this tile's products
+      tile_load<T, 64, 256>(regs, x + ((size_t)b * L + t0 + 64) * dm + 64 * mblk, tid, 64, (size_t)dm);
 #pragma unroll
     for (int c2 = 0; c2 < 2; ++c2) {
       const Frag<T> a = frag_tr<T, 64>(xt, 16 * w + cc, c2, g);
