@@ -283,6 +283,25 @@ def merge(g_h, oc_hat, o_f):
     return g_h[:, None] * repeat_cubes(oc_hat) + np.asarray(o_f, np.float64)
 
 
+def gate_backward(x, w_g, oc_hat, d_o, tokens):
+    """Gate part of the backward of Eq.(13)-(14) for some tokens of one batch
+    element: with g = tanh(X W_g) and O_c = Repeat(O_hat_c), dL/dg = dO . O_c
+    per token and head, dpre = dL/dg (1 - g^2).
+
+    x [n, Dm] and d_o [H, n, d] hold the rows of ``tokens`` (cube-tiled
+    indices); oc_hat [H, nb, d]; w_g [Dm, H].  Returns (dpre [n, H],
+    dx [n, Dm] = dpre W_g^T, this slice's share X^T dpre [Dm, H] of dW_g).
+    """
+    x = np.asarray(x, np.float64)
+    w_g = np.asarray(w_g, np.float64)
+    g = gate(x, w_g)
+    cubes = np.asarray(tokens) // 64
+    dg = np.stack([(np.asarray(d_o[h], np.float64) * np.asarray(oc_hat[h], np.float64)[cubes]).sum(axis=1)
+                   for h in range(w_g.shape[1])], axis=1)
+    dpre = dg * (1.0 - g ** 2)
+    return dpre, dpre @ w_g.T, x.T @ dpre
+
+
 def coarse_gate_backward(q, k, v, grid, x, w_g, d_o, scale=None):
     """Gradients of Eq.(1)-(4) and (13)-(14) for one batch element.
 
@@ -295,14 +314,11 @@ def coarse_gate_backward(q, k, v, grid, x, w_g, d_o, scale=None):
     H, L, d = q.shape
     sc = _scale(d, scale)
     g = gate(x, w_g)                                    # [L, H]
-    dpre = np.zeros_like(g)
-    dqc, dkc, dvc = [], [], []
+    dqc, dkc, dvc, ochat = [], [], [], []
     for h in range(H):
         oc_hat, lse_c, (qc, kc, vc) = coarse_forward(q[h], k[h], v[h], grid, scale)
-        oc = repeat_cubes(oc_hat)
+        ochat.append(oc_hat)
         doh = np.asarray(d_o[h], np.float64)
-        dg = (doh * oc).sum(axis=1)
-        dpre[:, h] = dg * (1.0 - g[:, h] ** 2)
         doc_hat = (g[:, h, None] * doh).reshape(-1, 64, d).sum(axis=1)   # Repeat^T
         p = np.exp(qc @ kc.T * sc - lse_c[:, None])
         dvc.append(p.T @ doc_hat)
@@ -312,8 +328,7 @@ def coarse_gate_backward(q, k, v, grid, x, w_g, d_o, scale=None):
         dkc.append(ds.T @ qc * sc)
     dqc, dkc, dvc = np.stack(dqc), np.stack(dkc), np.stack(dvc)
     spread = lambda t: np.repeat(t, 64, axis=1) / 64.0                  # MeanPool^T
-    dx = dpre @ np.asarray(w_g, np.float64).T
-    dw = np.asarray(x, np.float64).T @ dpre
+    _, dx, dw = gate_backward(x, w_g, np.stack(ochat), d_o, np.arange(L))
     return dqc, dkc, dvc, spread(dqc), spread(dkc), spread(dvc), dx, dw
 
 
