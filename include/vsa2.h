@@ -135,7 +135,7 @@ int vsa2_plan_from_csr(const vsa2_problem* p, int32_t topk, const int32_t* row_p
  *   lse (written): fp32 [batch, heads, L], natural-log log-sum-exp of the scaled
  *     scores of each query over its selected keys (kept for the backward).
  *   A query cube with no selected KV cube gets o_f = 0 and lse = -inf.
- *   ws: vsa2_workspace_size(VSA2_OP_FWD). */
+ *   ws: vsa2_workspace_size(VSA2_OP_FWD), currently 0 bytes (ws may be NULL). */
 int vsa2_sparse_attn_fwd(const vsa2_problem* p, int32_t topk, const void* q, const void* k, const void* v,
                          const int32_t* row_ptr, const int32_t* col_idx, void* o_f, float* lse,
                          void* ws, size_t ws_bytes, void* stream);

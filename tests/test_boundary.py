@@ -60,7 +60,7 @@ def test_sizes_and_budget():
     assert vsa2.pooled_size(p) == 2 * (2 * (L // 8) + 3 * nbp) * 64 * 4
     assert vsa2.saved_size(p) == (2 * nb * 64 + 2 * nb + 2 * L) * 4
     assert vsa2.workspace_size(p, vsa2.OP_ROUTE) >= 2 * (L // 8) * 4
-    assert vsa2.workspace_size(p, vsa2.OP_FWD) == 2 * L * 64 * 4          # V^T per cube
+    assert vsa2.workspace_size(p, vsa2.OP_FWD) == 0                       # forward needs no scratch
     assert vsa2.workspace_size(p, vsa2.OP_COARSE_BWD, 8, 128) > 0
 
 

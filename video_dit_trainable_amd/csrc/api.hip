@@ -103,9 +103,8 @@ size_t ws_plan(const Dims& d, TopkWs* w, void* base) {
 
 size_t ws_bwd(const Dims& d) { return up((size_t)d.bh * d.L * 8); }      // (lse2, delta) per token
 
-size_t ws_fwd(const Dims& d) { return up((size_t)d.bh * d.L * d.d * d.esz); }      // V^T per cube
+size_t ws_fwd(const Dims&) { return 0; }  // the forward needs no scratch
 
-size_t ws_coarse_vt(const Dims& d) { return up((size_t)d.bh * d.nbp * d.d * d.esz); }
 
 int pad16(int x) { return (x + 15) / 16 * 16; }
 int pad32(int x) { return (x + 31) / 32 * 32; }
@@ -281,7 +280,7 @@ int vsa2_workspace_size(const vsa2_problem* p, int32_t op, int32_t topk, int32_t
     case VSA2_OP_BWD: *bytes = ws_bwd(d); break;
     case VSA2_OP_COARSE:
       if ((s = check_dm(d, d_model))) return s;
-      *bytes = wt_bytes(d, d_model) + ws_coarse_vt(d);
+      *bytes = wt_bytes(d, d_model);
       break;
     case VSA2_OP_COARSE_BWD:
       if ((s = check_dm(d, d_model))) return s;
@@ -369,7 +368,7 @@ int vsa2_sparse_attn_fwd(const vsa2_problem* p, int32_t topk, const void* q, con
     return VSA2_E_ARG;
   if ((s = check_ws(ws, ws_bytes, ws_fwd(d)))) return s;
   AttnArgs a{};
-  a.q = q; a.k = k; a.v = v; a.vt = ws;
+  a.q = q; a.k = k; a.v = v;
   a.row_ptr = row_ptr; a.col_idx = col_idx;
   a.o = o_f; a.lse = lse;
   a.bh = d.bh; a.nq = d.nb; a.nkv = d.nb; a.seq = d.L; a.ld = d.L; a.out_rows = d.L;
@@ -424,14 +423,14 @@ int vsa2_coarse_gate(const vsa2_problem* p, const void* pooled, const void* x, i
   if ((s = check_dm(d, d_model))) return s;
   if (!aligned(pooled) || !aligned(x) || !aligned(w_g) || !aligned(o_f) || !aligned(o) || !aligned(saved))
     return VSA2_E_ARG;
-  if ((s = check_ws(ws, ws_bytes, wt_bytes(d, d_model) + ws_coarse_vt(d)))) return s;
+  if ((s = check_ws(ws, ws_bytes, wt_bytes(d, d_model)))) return s;
   const hipStream_t st = (hipStream_t)stream;
   Pooled pp = pooled_ptrs(d, pooled);
   float* oc_hat = saved;
   float* lse_c = oc_hat + (size_t)d.bh * d.nb * d.d;
   float* g = lse_c + (size_t)d.bh * d.nb;
   AttnArgs a{};
-  a.q = pp.qc; a.k = pp.kc; a.v = pp.vc; a.vt = (char*)ws + wt_bytes(d, d_model);
+  a.q = pp.qc; a.k = pp.kc; a.v = pp.vc;
   a.o = oc_hat; a.lse = lse_c;
   a.bh = d.bh; a.nq = d.nbp / 64; a.nkv = d.nbp / 64; a.seq = d.nb; a.ld = d.nbp; a.out_rows = d.nb;
   a.kph = 0;

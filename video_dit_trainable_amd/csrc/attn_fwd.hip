@@ -5,19 +5,17 @@
 //
 // Work split: one block (2 waves) per query cube; each wave owns 32 queries as
 // MFMA B fragments in registers, so every K/V byte read from LDS feeds two
-// 16-query MFMA blocks.  The selected K cubes and the pre-transposed V cubes
-// are gathered through the CSR list into chunk-swizzled LDS tiles; the next
-// cube's loads are in flight (in registers) while the current one is
-// computed.  S^T = K Q^T leaves, per lane, 4 keys of one query per 16-key
-// block, so the online softmax is lane-local apart from a 4-lane max, and the
-// exponentials feed O^T += V^T P^T straight from the accumulators.  The O
+// 16-query MFMA blocks.  The selected K and V cubes are gathered through the
+// CSR list into chunk-swizzled row-major LDS tiles; the next cube's loads are
+// in flight (in registers) while the current one is computed.  S^T = K Q^T
+// leaves, per lane, 4 keys of one query per 16-key block, so the online
+// softmax is lane-local apart from a 4-lane max, and the exponentials feed
+// O^T += V^T P^T straight from the accumulators: the accumulators of key
+// blocks 2h, 2h+1 form the B operand with the k-slot order
+// pi(g, e) = 4g + e (e < 4), 16 + 4g + e - 4 (e >= 4) of keys 32h.., and the
+// V^T A operand is read in the same order by transposing LDS reads.  The O
 // rescale is lazy: the running max is only moved when a tile exceeds it by
 // more than 2^8, which keeps every exponential <= 256 and the result exact.
-//
-// V is read as V^T: a pre-pass writes each 64-token cube of V transposed to
-// [d][64] with the tokens of every 32-token half reordered to the MFMA
-// k-slot order pi(g, e) = 4g + e (e < 4), 16 + 4g + e - 4 (e >= 4), so one
-// 16-byte LDS read yields a whole A fragment.
 #include <cmath>
 
 #include "common.h"
@@ -25,43 +23,21 @@
 
 namespace vsa2 {
 
-// V [bh][rows][D] -> VT [bh][rows/64][D][64] (k-slot order inside each 32-token half).
-template <typename T, int D>
-__global__ __launch_bounds__(256) void k_vt_perm(const T* __restrict__ v, T* __restrict__ vt, int tiles) {
-  __shared__ T s[64][D + 8];
-  const int t = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
-  const T* src = v + ((size_t)bh * tiles + t) * 64 * D;
-  for (int u = tid; u < 64 * D / 8; u += 256) {
-    const int r = u / (D / 8), c8 = u % (D / 8);
-    store8(&s[r][8 * c8], load8(src + (size_t)r * D + 8 * c8));
-  }
-  __syncthreads();
-  T* dst = vt + ((size_t)bh * tiles + t) * 64 * D;
-  for (int u = tid; u < D * 8; u += 256) {      // output chunk: row d, 8 positions 8u'..8u'+7
-    const int d = u / 8, p0 = 8 * (u % 8);
-    const int half = p0 >> 5, g = (p0 >> 3) & 3;
-    Vec8<T> o;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) o.v[e] = s[32 * half + (e < 4 ? 4 * g + e : 16 + 4 * g + e - 4)][d];
-    store8(dst + (size_t)d * 64 + p0, o);
-  }
-}
-
 template <typename T, typename TO, int D, bool DENSE>
 __global__ __launch_bounds__(128, 2) void k_attn_fwd(const T* __restrict__ q, const T* __restrict__ k,
-                                                  const T* __restrict__ vt, const int32_t* __restrict__ row_ptr,
+                                                  const T* __restrict__ v, const int32_t* __restrict__ row_ptr,
                                                   const int32_t* __restrict__ col_idx, TO* __restrict__ o,
                                                   float* __restrict__ lse, int nq, int nkv, int seq, int ld,
                                                   int out_rows, int64_t kph, float c, int ct, int cy, int cx) {
   __shared__ __align__(16) T ks[64 * D];
-  __shared__ __align__(16) T vs[D * 64];
+  __shared__ __align__(16) T vs[64 * D];
   int bh, i;
   if (!xcd_work(blockIdx.x, nq, bh, i)) return;
   if (ct > 0) i = blocked_cube(i, ct, cy, cx);
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, cc = lane & 15;
   const size_t hoff = (size_t)bh * ld * D;
   const T* kbase = k + hoff;
-  const T* vbase = vt + hoff;
+  const T* vbase = v + hoff;
 
   int cnt;
   const int32_t* cols = nullptr;
@@ -97,8 +73,9 @@ __global__ __launch_bounds__(128, 2) void k_attn_fwd(const T* __restrict__ q, co
   float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};
 
   if (cnt > 0) {
-    SwRegs<64, D, T, 128> kr;
-    SwRegs<D, 64, T, 128> vr;
+    SwRegs<64, D, T, 128> kr, vr;
+    int vtr = 0;  // bf16: this lane's part of the transposed V reads (rows 4g + c/4 of key half 0)
+    if constexpr (sizeof(T) == 2) vtr = sw_tr_base<T, D>(0, g, cc);
     int j = cube_at(0);
     sw_load(kr, kbase + (size_t)max(j, 0) * 64 * D, tid);
     sw_load(vr, vbase + (size_t)max(j, 0) * 64 * D, tid);
@@ -180,7 +157,9 @@ __global__ __launch_bounds__(128, 2) void k_attn_fwd(const T* __restrict__ q, co
       for (int db = 0; db < D / 16; ++db)
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-          const Frag<T> a = sw_frag<T, 64>(vs, 16 * db + cc, h, g);
+          Frag<T> a;
+          if constexpr (sizeof(T) == 2) a = sw_frag_tr_at<T, D>(vs, vtr + 32 * h * D, 16 * db);
+          else a = sw_frag_tr<T, D>(vs, 32 * h, 16 * db, g, cc);
           mma(oacc[db][0], a, pf[0][h]);
           mma(oacc[db][1], a, pf[1][h]);
         }
@@ -210,19 +189,15 @@ __global__ __launch_bounds__(128, 2) void k_attn_fwd(const T* __restrict__ q, co
 
 template <typename T, int D>
 hipError_t launch_fwd_t(const AttnArgs& a, hipStream_t st) {
-  const int tiles = a.ld / 64;
-  hipLaunchKernelGGL((k_vt_perm<T, D>), dim3(tiles, a.bh), dim3(256), 0, st, (const T*)a.v, (T*)a.vt, tiles);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
   dim3 grid(xcd_grid(a.nq, a.bh));
   if (a.dense) {
     hipLaunchKernelGGL((k_attn_fwd<T, float, D, true>), grid, dim3(128), 0, st, (const T*)a.q, (const T*)a.k,
-                       (const T*)a.vt, nullptr, nullptr, (float*)a.o, a.lse, a.nq, a.nkv, a.seq, a.ld, a.out_rows,
+                       (const T*)a.v, nullptr, nullptr, (float*)a.o, a.lse, a.nq, a.nkv, a.seq, a.ld, a.out_rows,
                        a.kph, a.scale_log2, 0, 0, 0);
   } else {
     timer_before(TK_FINE_FWD, st);
     hipLaunchKernelGGL((k_attn_fwd<T, T, D, false>), grid, dim3(128), 0, st, (const T*)a.q, (const T*)a.k,
-                       (const T*)a.vt, a.row_ptr, a.col_idx, (T*)a.o, a.lse, a.nq, a.nkv, a.seq, a.ld, a.out_rows,
+                       (const T*)a.v, a.row_ptr, a.col_idx, (T*)a.o, a.lse, a.nq, a.nkv, a.seq, a.ld, a.out_rows,
                        a.kph, a.scale_log2, a.ct, a.cy, a.cx);
     timer_after(TK_FINE_FWD, st);
   }

@@ -47,7 +47,6 @@ hipError_t launch_plan(const TopkArgs& a, hipStream_t st);
 struct AttnArgs {
   const void *q, *k, *v;
   const int32_t *row_ptr, *col_idx;   // CSR (ignored when dense)
-  void* vt;                           // workspace [bh, ld/64, d, 64]: V per cube, transposed
   void* o;                            // storage dtype (fine) or fp32 (dense)
   float* lse;                         // [bh, out_rows] natural log
   int bh;
