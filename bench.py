@@ -24,7 +24,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 from video_dit_trainable_amd import vsa2  # noqa: E402
-from video_dit_trainable_amd.configs import WORKLOADS, flops, kernel_flops  # noqa: E402
+from video_dit_trainable_amd.configs import WORKLOADS, flops, kernel_bytes, kernel_flops  # noqa: E402
 from video_dit_trainable_amd.inputs import (make_gate_inputs, make_grad_out, make_qkv,  # noqa: E402
                                             make_selection)
 
@@ -215,16 +215,31 @@ def main():
         step_flops += fl["fine_bwd"] + fl["coarse_bwd"] + fl["gate_bwd"]
     value = step_flops / (ms_step * 1e-3) / 1e12
 
-    # roofline of the dominant kernel: the timed kernel with the longest average launch
-    kfl = kernel_flops(w)
+    # roofline of the dominant kernel (the timed kernel with the longest average
+    # launch): its bound is the one its algorithmic intensity puts it under,
+    # HBM below the ridge point PEAK_BF16 / PEAK_HBM FLOP per byte, MFMA above
+    kfl, kby = kernel_flops(w), kernel_bytes(w)
+    ridge = PEAK_BF16 / PEAK_HBM
+
+    def kernel_roof(n, ms):
+        sec = ms * 1e-3
+        tf, gbps = kfl[n] / sec / 1e12, kby[n] / sec / 1e9
+        if kfl[n] / kby[n] < ridge:
+            return "hbm", gbps, PEAK_HBM / 1e9, "GB/s", tf, gbps
+        return "mfma", tf, PEAK_BF16 / 1e12, "TFLOP/s", tf, gbps
+
     dom = max(kern, key=kern.get)
-    achieved = kfl[dom] / (kern[dom] * 1e-3) / 1e12
-    roof = {"kernel": TIMED[dom][1], "bound": "mfma", "achieved": round(achieved, 2),
-            "peak": PEAK_BF16 / 1e12, "unit": "TFLOP/s", "frac": round(achieved / (PEAK_BF16 / 1e12), 4),
-            "traffic": stored_traffic(dom, w.name), "avg_launch_ms": round(kern[dom], 4),
-            "flops_per_launch": kfl[dom]}
-    kernels = {n: {"ms": round(t, 4), "tflops": round(kfl[n] / (t * 1e-3) / 1e12, 2),
-                   "pct_bf16_peak": round(100 * kfl[n] / (t * 1e-3) / PEAK_BF16, 2)} for n, t in kern.items()}
+    bound, achieved, peak, unit, tf, gbps = kernel_roof(dom, kern[dom])
+    roof = {"kernel": TIMED[dom][1], "bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+            "frac": round(achieved / peak, 4), "traffic": stored_traffic(dom, w.name),
+            "avg_launch_ms": round(kern[dom], 4), "bytes_per_launch": kby[dom], "flops_per_launch": kfl[dom],
+            "flop_per_byte": round(kfl[dom] / kby[dom], 1), "ridge_flop_per_byte": round(ridge, 1),
+            "mfma_tflops": round(tf, 2), "mfma_frac": round(tf * 1e12 / PEAK_BF16, 4), "gbps": round(gbps, 1)}
+    kernels = {}
+    for n, t in kern.items():
+        b, a, pk, _, tf, gbps = kernel_roof(n, t)
+        kernels[n] = {"ms": round(t, 4), "bound": b, "frac": round(a / pk, 4), "tflops": round(tf, 2),
+                      "pct_bf16_peak": round(100 * tf * 1e12 / PEAK_BF16, 2), "gbps": round(gbps, 1)}
 
     ops = {n: {"ms": round(t, 4)} for n, t in per.items()}
     for n, key in (("fine_fwd", "fine_fwd"), ("fine_bwd", "fine_bwd"), ("route", "router")):

@@ -106,3 +106,31 @@ def kernel_flops(w: Workload, topk=None):
         "router_lse": bh * 2 * lr * lr * d,
         "router_scores": bh * 2 * lr * lr * d,
     }
+
+
+def kernel_bytes(w: Workload, topk=None):
+    """Algorithmic HBM bytes of one launch of each timed kernel.
+
+    The fine kernels gather one 64-row tile of two operands per selected pair
+    with no reuse assumed (K and V for the forward and the dQ kernel, Q and dO
+    plus the 64 rows' (lse, delta) pairs for the dK/dV kernel), plus the index
+    entry, and read or write the per-token tensors that stay with the block
+    once.  The dK/dV and dQ kernels also read the coarse branch's per-cube
+    gradient rows.  A router pass reads the pooled Q_r and K_r once and writes
+    the per-row LSE; the score pass also writes the nb x nb cube scores.
+    """
+    k = w.budget(topk)
+    bh = w.batch * w.heads
+    d = w.head_dim
+    esz = 2 if w.dtype == "bf16" else 4
+    tile = CUBE * d * esz
+    tok = w.L * d * esz          # one per-token tensor of one (batch, head)
+    ptr = (w.nb + 1) * 4
+    lr = w.L // SUB
+    return {
+        "fine_fwd": bh * (k * (2 * tile + 4) + 2 * tok + w.L * 4 + ptr),
+        "bwd_dkdv": bh * (k * (2 * tile + CUBE * 8 + 4) + 4 * tok + 2 * w.nb * d * 4 + ptr),
+        "bwd_dq": bh * (k * (2 * tile + 4) + 3 * tok + w.L * 8 + w.nb * d * 4 + ptr),
+        "router_lse": bh * (2 * lr * d * esz + lr * 4),
+        "router_scores": bh * (2 * lr * d * esz + lr * 4 + w.nb * w.nb * 4),
+    }

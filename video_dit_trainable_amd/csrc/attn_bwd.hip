@@ -24,7 +24,8 @@ namespace vsa2 {
 
 // Row statistics of the fine branch for the backward kernels: stats[2t] =
 // lse_t * log2(e) (+inf for a row with no selected key, so its P is 0) and
-// stats[2t + 1] = delta_t = dO_t . O_t.
+// stats[2t + 1] = -delta_t = -(dO_t . O_t), the initial value of the dP
+// accumulators, so that they end at dP - delta.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void k_bwd_delta(const T* __restrict__ o, const T* __restrict__ d_o,
                                                    const float* __restrict__ lse, float* __restrict__ stats,
@@ -44,7 +45,7 @@ __global__ __launch_bounds__(256) void k_bwd_delta(const T* __restrict__ o, cons
   if (row < rows && part == 0) {
     const float l = lse[row];
     stats[2 * row] = l == -INFINITY ? INFINITY : l * LOG2E;
-    stats[2 * row + 1] = s;
+    stats[2 * row + 1] = -s;
   }
 }
 
@@ -84,14 +85,21 @@ __device__ __forceinline__ void dkdv_pair(const T* qs, const T* dos, const float
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     const int row = 32 * qh + 16 * qb + cc;
-    f32x4 p[2], dp[2];
+    // row statistics of queries 32qh + 16qb + 4g + r: lse2 and -delta, the
+    // latter the starting value of the dP accumulators (they end at dP - delta)
+    const float* sp = sts + 2 * (32 * qh + 16 * qb + 4 * g);
+    const f32x4 s01 = *reinterpret_cast<const f32x4*>(sp);
+    const f32x4 s23 = *reinterpret_cast<const f32x4*>(sp + 4);
+    const float l2[4] = {s01[0], s01[2], s23[0], s23[2]};
+    const f32x4 ndl = {s01[1], s01[3], s23[1], s23[3]};
+    f32x4 p[2], dp[2] = {ndl, ndl};
     {
       const Frag<T> a = rd_row<T, D>(qs, brow, row, 0, g);
       p[0] = mma0(a, kf[0][0]);
       p[1] = mma0(a, kf[1][0]);
       const Frag<T> b = rd_row<T, D>(dos, brow, row, 0, g);
-      dp[0] = mma0(b, vf[0][0]);
-      dp[1] = mma0(b, vf[1][0]);
+      mma(dp[0], b, vf[0][0]);
+      mma(dp[1], b, vf[1][0]);
     }
 #pragma unroll
     for (int s = 1; s < D / 32; ++s) {
@@ -103,18 +111,13 @@ __device__ __forceinline__ void dkdv_pair(const T* qs, const T* dos, const float
       mma(dp[1], b, vf[1][s]);
     }
     // P = exp2(S c - lse2), dS = P (dP - delta)
-    const float* sp = sts + 2 * (32 * qh + 16 * qb + 4 * g);
-    const f32x4 s01 = *reinterpret_cast<const f32x4*>(sp);
-    const f32x4 s23 = *reinterpret_cast<const f32x4*>(sp + 4);
-    const float l2[4] = {s01[0], s01[2], s23[0], s23[2]};
-    const float dl[4] = {s01[1], s01[3], s23[1], s23[3]};
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const float pe = kv_ok[kb] ? fast_exp2(fmaf(p[kb][r], c, -l2[r])) : 0.f;
         pf[kb].v[4 * qb + r] = from_f32<T>(pe);
-        sf[kb].v[4 * qb + r] = from_f32<T>(pe * (dp[kb][r] - dl[r]));
+        sf[kb].v[4 * qb + r] = from_f32<T>(pe * dp[kb][r]);
       }
   }
   // dV^T += dO^T P, dK^T += Q^T dS over these 32 queries
@@ -317,12 +320,13 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(const T* __restrict__ q, co
 }
 
 // One (query cube, KV cube) pair of the dQ kernel for one wave: queries 32qh..
-// (Q, dO fragments qf, of in registers, row statistics l2, dl) against keys
+// (Q, dO fragments qf, of in registers, row statistics l2 and ndl = -delta,
+// the starting value of the dP^T accumulators) against keys
 // 32kh.. of the K / V tiles ks, vs in LDS; keys at or beyond lim are masked.
 template <typename T, int D>
 __device__ __forceinline__ void dq_pair(const T* ks, const T* vs, int brow, int btr, int lim,
                                         const Frag<T> (&qf)[2][D / 32], const Frag<T> (&of)[2][D / 32],
-                                        const float (&l2)[2], const float (&dl)[2], f32x4 (&dqa)[D / 16][2], int kh,
+                                        const float (&l2)[2], const float (&ndl)[2], f32x4 (&dqa)[D / 16][2], int kh,
                                         int g, int cc, float c) {
   opaque(brow);
   opaque(btr);
@@ -331,14 +335,14 @@ __device__ __forceinline__ void dq_pair(const T* ks, const T* vs, int brow, int 
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
     const int row = 32 * kh + 16 * kb + cc;
-    f32x4 p[2], dp[2];
+    f32x4 p[2], dp[2] = {f32x4{ndl[0], ndl[0], ndl[0], ndl[0]}, f32x4{ndl[1], ndl[1], ndl[1], ndl[1]}};
     {
       const Frag<T> a = rd_row<T, D>(ks, brow, row, 0, g);
       p[0] = mma0(a, qf[0][0]);
       p[1] = mma0(a, qf[1][0]);
       const Frag<T> b = rd_row<T, D>(vs, brow, row, 0, g);
-      dp[0] = mma0(b, of[0][0]);
-      dp[1] = mma0(b, of[1][0]);
+      mma(dp[0], b, of[0][0]);
+      mma(dp[1], b, of[1][0]);
     }
 #pragma unroll
     for (int s = 1; s < D / 32; ++s) {
@@ -356,7 +360,7 @@ __device__ __forceinline__ void dq_pair(const T* ks, const T* vs, int brow, int 
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
         const float pe = kin ? fast_exp2(fmaf(p[qb][r], c, -l2[qb])) : 0.f;
-        sf[qb].v[4 * kb + r] = from_f32<T>(pe * (dp[qb][r] - dl[qb]));
+        sf[qb].v[4 * kb + r] = from_f32<T>(pe * dp[qb][r]);
       }
     }
   }
@@ -430,7 +434,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(const T* __restrict__ q, cons
 
   // this wave's 32 queries: Q and dO rows as B fragments (column = query 32qh + 16qb + cc)
   Frag<T> qf[2][D / 32], of[2][D / 32];
-  float l2[2], dl[2];
+  float l2[2], ndl[2];
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     const int qrow = i * 64 + 32 * qh + 16 * qb + cc;
@@ -440,7 +444,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(const T* __restrict__ q, cons
       of[qb][s] = frag_global<T, D>(d_o + hoff, qrow, s, g);
     }
     l2[qb] = stats[2 * ((size_t)bh * ld + qrow)];
-    dl[qb] = stats[2 * ((size_t)bh * ld + qrow) + 1];
+    ndl[qb] = stats[2 * ((size_t)bh * ld + qrow) + 1];
   }
   // dQ^T partial over this wave's key half: rows d = 16db + 4g + r, column query 16qb + cc
   f32x4 dqa[D / 16][2];
@@ -466,7 +470,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(const T* __restrict__ q, cons
       if (n + 2 < cnt) raw = entry(n + 2);
       VSA2_FETCH_KV(jj, tB);
     }
-    if (lim_a > 32 * kh) dq_pair<T, D>(tA, tA + TILE, brow, btr, lim_a, qf, of, l2, dl, dqa, kh, g, cc, c);
+    if (lim_a > 32 * kh) dq_pair<T, D>(tA, tA + TILE, brow, btr, lim_a, qf, of, l2, ndl, dqa, kh, g, cc, c);
     if (n + 1 >= cnt) break;
     wait_vm0();
     __syncthreads();  // stage B holds entry n + 1; every wave is done with stage A
@@ -475,7 +479,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(const T* __restrict__ q, cons
       if (n + 3 < cnt) raw = entry(n + 3);
       VSA2_FETCH_KV(jj, tA);
     }
-    if (lim_b > 32 * kh) dq_pair<T, D>(tB, tB + TILE, brow, btr, lim_b, qf, of, l2, dl, dqa, kh, g, cc, c);
+    if (lim_b > 32 * kh) dq_pair<T, D>(tB, tB + TILE, brow, btr, lim_b, qf, of, l2, ndl, dqa, kh, g, cc, c);
   }
 #undef VSA2_FETCH_KV
 

@@ -335,6 +335,16 @@ __device__ __forceinline__ Frag<T> sw_frag(const T* lds, int r, int s, int g) {
 // 4 slots), columns col0 + 4 (j % 4) .. +3.  fp32: eight scalar reads.
 #define VSA2_LDS __attribute__((address_space(3)))
 typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+// the two halves of a bf16 fragment as one register quad (a plain vector
+// concatenation: element-wise copies make the compiler insert bit-field moves)
+template <typename T>
+__device__ __forceinline__ Frag<T> frag_join(s16x4 lo, s16x4 hi) {
+  static_assert(sizeof(T) == 2, "bf16 fragments only");
+  Frag<T> f;
+  f.v = __builtin_bit_cast(decltype(f.v), __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  return f;
+}
 template <typename T, int W>
 __device__ __forceinline__ Frag<T> sw_frag_tr(const T* lds, int r0, int col0, int g, int c) {
   using S = SwTile<T, W>;
@@ -346,10 +356,7 @@ __device__ __forceinline__ Frag<T> sw_frag_tr(const T* lds, int r0, int col0, in
     const T* pb = lds + S::off(rb, col / S::EPC) + (col % S::EPC);
     const s16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((VSA2_LDS s16x4*)(pa));
     const s16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((VSA2_LDS s16x4*)(pb));
-    Vec8<T> v;
-    __builtin_memcpy(&v.v[0], &va, 8);
-    __builtin_memcpy(&v.v[4], &vb, 8);
-    f = frag_from8(v);
+    f = frag_join<T>(va, vb);
   } else {
     const int col = col0 + c;
 #pragma unroll
@@ -437,10 +444,7 @@ __device__ __forceinline__ Frag<T> sw_frag_tr_at(const T* lds, int base, int col
   const T* pa = lds + (base ^ col0);
   const s16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((VSA2_LDS s16x4*)(pa));
   const s16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((VSA2_LDS s16x4*)(pa + 16 * W));
-  Vec8<T> v;
-  __builtin_memcpy(&v.v[0], &va, 8);
-  __builtin_memcpy(&v.v[4], &vb, 8);
-  return frag_from8(v);
+  return frag_join<T>(va, vb);
 }
 // Butterfly reductions over the four slot groups (lanes c, c+16, c+32, c+48).
 __device__ __forceinline__ float group_max(float x) {

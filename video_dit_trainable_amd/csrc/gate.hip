@@ -235,7 +235,7 @@ __global__ __launch_bounds__(256) void k_gate_bwd(const T* __restrict__ wt, cons
     __syncthreads();
     if (tid == 0) {
       stats_c[2 * (bh * nbp + c)] = lse_c[bh * nb + c] * LOG2E;
-      stats_c[2 * (bh * nbp + c) + 1] = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+      stats_c[2 * (bh * nbp + c) + 1] = -(wsum[0] + wsum[1] + wsum[2] + wsum[3]);
     }
   }
   // zero the padding rows of dO_hat_c and mask them in the row statistics

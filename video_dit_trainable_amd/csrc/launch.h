@@ -66,7 +66,7 @@ hipError_t launch_attn_fwd(const AttnArgs& a, hipStream_t st);
 struct AttnBwdArgs {
   const void *q, *k, *v, *o, *d_o;
   const float* lse;                   // [bh, ld] natural log (fine branch; input of launch_bwd_delta)
-  const float* stats;                 // [bh, ld] pairs (lse * log2 e, rowsum(dO * O)); +inf lse = masked row
+  const float* stats;                 // [bh, ld] pairs (lse * log2 e, -rowsum(dO * O)); +inf lse = masked row
   const int32_t *row_ptr, *col_idx, *col_ptr, *row_idx;
   const float *dq_add, *dk_add, *dv_add;  // [bh, nkv, d] per-cube terms added as row/64 (or NULL)
   void *dq, *dk, *dv;                 // storage dtype (fine) or fp32 (dense)
@@ -104,7 +104,7 @@ struct GateBwdArgs {
   float* dpre;            // workspace [bh, L]
   void* doc;              // workspace [bh, nbp, d] storage dtype: dO_hat_c
   const float* lse_c;     // [bh, nb] natural log, from the forward
-  float* stats_c;         // workspace [bh, nbp] pairs (lse_c * log2 e, rowsum(dO_hat_c * O_hat_c)); pad rows (+inf, 0)
+  float* stats_c;         // workspace [bh, nbp] pairs (lse_c * log2 e, -rowsum(dO_hat_c * O_hat_c)); pad rows (+inf, 0)
   float* dw_part;         // workspace [nchunk, dm, heads]
   void* dx;
   float* dw_g;
