@@ -120,15 +120,21 @@ __device__ __forceinline__ void dkdv_pair(const T* qs, const T* dos, const float
         sf[kb].v[4 * qb + r] = from_f32<T>(pe * dp[kb][r]);
       }
   }
-  // dV^T += dO^T P, dK^T += Q^T dS over these 32 queries
+  // dV^T += dO^T P, dK^T += Q^T dS over these 32 queries; the transposed
+  // fragments of step db + 1 are read while the products of step db run
+  Frag<T> ao[2], aq[2];
+  ao[0] = rd_tr<T, D>(dos, btr, 32 * qh, 0, g, cc);
+  aq[0] = rd_tr<T, D>(qs, btr, 32 * qh, 0, g, cc);
 #pragma unroll
   for (int db = 0; db < D / 16; ++db) {
-    const Frag<T> ao = rd_tr<T, D>(dos, btr, 32 * qh, 16 * db, g, cc);
-    mma(dva[db][0], ao, pf[0]);
-    mma(dva[db][1], ao, pf[1]);
-    const Frag<T> aq = rd_tr<T, D>(qs, btr, 32 * qh, 16 * db, g, cc);
-    mma(dka[db][0], aq, sf[0]);
-    mma(dka[db][1], aq, sf[1]);
+    if (db + 1 < D / 16) {
+      ao[(db + 1) & 1] = rd_tr<T, D>(dos, btr, 32 * qh, 16 * (db + 1), g, cc);
+      aq[(db + 1) & 1] = rd_tr<T, D>(qs, btr, 32 * qh, 16 * (db + 1), g, cc);
+    }
+    mma(dva[db][0], ao[db & 1], pf[0]);
+    mma(dva[db][1], ao[db & 1], pf[1]);
+    mma(dka[db][0], aq[db & 1], sf[0]);
+    mma(dka[db][1], aq[db & 1], sf[1]);
   }
 }
 
