@@ -264,21 +264,24 @@ __device__ __forceinline__ Frag<T> frag_global(const T* __restrict__ base, int r
 // ch ^ f(r) of that row; a wave's stores cover whole rows, so they never
 // conflict.  f spreads both fragment reads over the banks: the 16-byte reads
 // of 16 consecutive rows (one chunk each) and the 8-byte transposing reads of
-// 4 rows x 4 runs (ds_read_b64_tr_b16).  The LDS of gfx950 behaves as 128
-// banks of 4 bytes with the 16-byte reads served 32 lanes at a time (fitted to
-// the SQ_LDS_BANK_CONFLICT counter on linear and swizzled read patterns):
-// rows r and r + 1 of a 256-byte-row tile then fall on different bank halves,
-// and both reads are conflict-free when f(r) >> 1 differs between the rows of
-// one bank half (for 128-byte rows: of one residue of r mod 4):
-//   16+ chunks per row: f(r) = r & 15
-//   8 chunks per row:   f(r) = 2 ((r >> 2) & 3)
+// 4 rows x 4 runs (ds_read_b64_tr_b16).  f was chosen with the LDS bank
+// conflict counter of gfx950: on linear and swizzled read patterns it fits
+// 128 banks with the 16-byte reads served in 16-lane groups and 64 banks with
+// the transposing reads served 32 lanes at a time.  Among the swizzles that
+// are linear in the bits of r & 15, the ones below give no conflict for either
+// read under every grouping consistent with the counts (and measure zero
+// conflict cycles on both patterns):
+//   16+ chunks per row: f(r) = 2 (r & 7) ^ 15 [r & 8]
+//   8 chunks per row:   f(r) = (r & 6) ^ 7 [r & 8]
 // f depends on r & 15 only, so rows r and r + 16m share a swizzle and a
 // fragment address moves by 16m rows with a plain add.
 // ---------------------------------------------------------------------------
 template <typename T, int W> struct SwTile {
   static constexpr int NCH = W * (int)sizeof(T) / 16;  // 16-byte chunks per row
   static constexpr int EPC = 16 / (int)sizeof(T);      // elements per chunk
-  __device__ static constexpr int f(int r) { return NCH >= 16 ? (r & 15) : (((r >> 2) & 3) << 1); }
+  __device__ static constexpr int f(int r) {
+    return NCH >= 16 ? (((r & 7) << 1) ^ (((r >> 3) & 1) * 15)) : ((r & 6) ^ (((r >> 3) & 1) * 7));
+  }
   __device__ static constexpr int off(int r, int ch) { return r * W + EPC * (ch ^ (f(r) & (NCH - 1))); }
 };
 
