@@ -12,7 +12,6 @@ using namespace vsa2;
 namespace {
 
 constexpr size_t ALIGN = 256;
-constexpr int DW_TC = 4096;  // tokens per dW_g partial (matches gate.hip)
 
 size_t up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
 

@@ -15,7 +15,6 @@
 namespace vsa2 {
 
 constexpr int HMAX = 64;   // heads supported by the gate kernels
-constexpr int DW_TC = 4096;  // tokens per dW_g partial
 
 struct GateGeom {
   int hp, hk;  // heads padded to 16 (forward N) and 32 (backward K)
@@ -345,6 +344,124 @@ __global__ __launch_bounds__(256) void k_dwg_part(const T* __restrict__ x, const
   }
 }
 
+// The bf16 dW_g partial: dW^T[h][m] = sum_t dpre[h][t] X[t][m] over one token
+// chunk.  Each wave owns 64 columns of X and works alone: it copies its
+// 64-token x 64-column tiles LDS-direct (row-major, chunk-swizzled, two
+// stages in distinct arrays, the loop unrolled by two) and reads them as
+// transposed B fragments; the A operand is dpre^T, split into bf16 hi + lo
+// (fp32-accurate products), loaded one tile ahead.  NHB = 16-head blocks.
+template <int NHB>
+__global__ __launch_bounds__(256, 2) void k_dwg_part_bf16(const bf16* __restrict__ x, const float* __restrict__ dpre,
+                                                          float* __restrict__ part, int H, int nb, int dm,
+                                                          int nchunk) {
+  using T = bf16;
+  using S = SwTile<T, 64>;
+  constexpr int TT = 64 * 64;  // elements per wave tile
+  __shared__ __align__(16) T sA[4 * TT];
+  __shared__ __align__(16) T sB[4 * TT];
+  const int chunk = blockIdx.y, b = blockIdx.z, tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4,
+            cc = lane & 15;
+  const int m0 = 256 * blockIdx.x + 64 * w;
+  if (m0 >= dm) return;  // waves work alone: no barrier follows
+  const size_t L = (size_t)nb * CUBE;
+  const size_t t_beg = (size_t)chunk * DW_TC, t_end = min(L, (size_t)(chunk + 1) * DW_TC);
+  T* tA = sA + w * TT;
+  T* tB = sB + w * TT;
+  // copy n of this lane fills physical chunk lane % 8 of row 8n + lane / 8
+  // with logical chunk (lane % 8) ^ f(row); rows 8n + j share f for n and n + 2
+  const int rl = lane >> 3, pc = lane & 7;
+  int coff[2];
+#pragma unroll
+  for (int n = 0; n < 2; ++n) {
+    const int r = 8 * n + rl;
+    coff[n] = (r * dm + 8 * (pc ^ (S::f(r) & (S::NCH - 1)))) * (int)sizeof(T);
+  }
+  const char* xb = reinterpret_cast<const char*>(x + (size_t)b * L * dm + m0);
+  auto copy = [&](size_t t0, T* tile) {
+    const char* src = xb + t0 * dm * sizeof(T);
+#pragma unroll
+    for (int n = 0; n < 8; ++n) {
+      int off = coff[n & 1] + (n >> 1) * 16 * dm * (int)sizeof(T);
+      opaque(off);
+      lds_copy16(src + (uint32_t)off, (VSA2_LDS void*)(tile + n * 512));
+    }
+  };
+  float4 dp[2][NHB][2], dpn[2][NHB][2];
+  auto load_dp = [&](size_t t0, float4 (&d)[2][NHB][2]) {
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int hb = 0; hb < NHB; ++hb) {
+        const int h = 16 * hb + cc;
+        if (h < H) {
+          const float* src = dpre + ((size_t)b * H + h) * L + t0 + 32 * ks + 4 * g;
+          d[ks][hb][0] = *reinterpret_cast<const float4*>(src);
+          d[ks][hb][1] = *reinterpret_cast<const float4*>(src + 16);
+        } else {
+          d[ks][hb][0] = d[ks][hb][1] = make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+      }
+  };
+  f32x4 acc[NHB][4];
+#pragma unroll
+  for (int hb = 0; hb < NHB; ++hb)
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) acc[hb][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int btr = sw_tr_base<T, 64>(0, g, cc);
+  auto tile_products = [&](const T* tile, const float4 (&d)[2][NHB][2]) {
+    int base = btr;
+    opaque(base);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      Frag<T> ahi[NHB], alo[NHB];
+#pragma unroll
+      for (int hb = 0; hb < NHB; ++hb) {
+        const float4 lo = d[ks][hb][0], hi = d[ks][hb][1];
+        const float v8[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+        split8<T>(v8, ahi[hb], alo[hb]);
+      }
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) {
+        const Frag<T> bx = sw_frag_tr_at<T, 64>(tile, base + 32 * ks * 64, 16 * mb);
+#pragma unroll
+        for (int hb = 0; hb < NHB; ++hb) {
+          mma(acc[hb][mb], ahi[hb], bx);
+          mma(acc[hb][mb], alo[hb], bx);
+        }
+      }
+    }
+  };
+  if (t_beg < t_end) {
+    copy(t_beg, tA);
+    load_dp(t_beg, dp);
+  }
+  for (size_t t0 = t_beg; t0 < t_end; t0 += 128) {
+    wait_vm0();  // tile t0 (stage A) and its dpre values are in
+    if (t0 + 64 < t_end) {
+      copy(t0 + 64, tB);
+      load_dp(t0 + 64, dpn);
+    }
+    tile_products(tA, dp);
+    if (t0 + 64 >= t_end) break;
+    wait_vm0();  // tile t0 + 64 (stage B)
+    if (t0 + 128 < t_end) {
+      copy(t0 + 128, tA);
+      load_dp(t0 + 128, dp);
+    }
+    tile_products(tB, dpn);
+  }
+  float* out = part + (((size_t)b * nchunk + chunk) * dm + m0) * H;
+#pragma unroll
+  for (int hb = 0; hb < NHB; ++hb)
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int h = 16 * hb + 4 * g + r;
+        if (h < H) out[(size_t)(16 * mb + cc) * H + h] = acc[hb][mb][r];
+      }
+}
+
 __global__ void k_dwg_reduce(const float* __restrict__ part, float* __restrict__ dw, int n, int parts) {
   const int idx = blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= n) return;
@@ -387,8 +504,18 @@ hipError_t launch_gate_bwd_t(const GateBwdArgs& a, hipStream_t st) {
                      hk);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((k_dwg_part<T>), dim3(a.dm / 64, a.nchunk, a.batch), dim3(256), 0, st, (const T*)a.x, a.dpre,
-                     a.dw_part, a.heads, a.nb, a.dm, a.nchunk);
+  if constexpr (sizeof(T) == 2) {
+    const dim3 grid((a.dm + 255) / 256, a.nchunk, a.batch);
+    const int nhb = (a.heads + 15) / 16;
+    const bf16* xx = (const bf16*)a.x;
+    if (nhb == 1) hipLaunchKernelGGL(k_dwg_part_bf16<1>, grid, dim3(256), 0, st, xx, a.dpre, a.dw_part, a.heads, a.nb, a.dm, a.nchunk);
+    else if (nhb == 2) hipLaunchKernelGGL(k_dwg_part_bf16<2>, grid, dim3(256), 0, st, xx, a.dpre, a.dw_part, a.heads, a.nb, a.dm, a.nchunk);
+    else if (nhb == 3) hipLaunchKernelGGL(k_dwg_part_bf16<3>, grid, dim3(256), 0, st, xx, a.dpre, a.dw_part, a.heads, a.nb, a.dm, a.nchunk);
+    else hipLaunchKernelGGL(k_dwg_part_bf16<4>, grid, dim3(256), 0, st, xx, a.dpre, a.dw_part, a.heads, a.nb, a.dm, a.nchunk);
+  } else {
+    hipLaunchKernelGGL((k_dwg_part<T>), dim3(a.dm / 64, a.nchunk, a.batch), dim3(256), 0, st, (const T*)a.x, a.dpre,
+                       a.dw_part, a.heads, a.nb, a.dm, a.nchunk);
+  }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int n = a.dm * a.heads;

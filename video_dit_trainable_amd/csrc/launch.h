@@ -94,6 +94,10 @@ struct GateArgs {
 };
 hipError_t launch_gate_fwd(const GateArgs& a, hipStream_t st);
 
+// tokens per dW_g partial sum of the gate backward (the partials are then
+// reduced in a fixed order, so dW_g does not depend on the launch)
+constexpr int DW_TC = 2048;
+
 struct GateBwdArgs {
   const void* x;
   const float* w_g;
