@@ -60,7 +60,7 @@ __device__ __forceinline__ void split8(const float* x, Frag<T>& hi, Frag<T>& lo)
 }
 
 // One block per (cube, batch): gates of its 64 tokens for every head, then the merge.
-template <typename T, int D>
+template <typename T, int D, int NHB>
 __global__ __launch_bounds__(256) void k_gate_fwd(const T* __restrict__ x, const T* __restrict__ wt,
                                                   const float* __restrict__ oc_hat, const T* __restrict__ o_f,
                                                   T* __restrict__ o, float* __restrict__ gout, int H, int nb, int dm,
@@ -72,46 +72,41 @@ __global__ __launch_bounds__(256) void k_gate_fwd(const T* __restrict__ x, const
   const size_t L = (size_t)nb * CUBE;
   const T* fhi = wt;
   const T* flo = wt + (size_t)hp * dm;
-  const int nhb = hp / 16;
   // gate products: wave w takes k-steps [w S/4, (w+1) S/4) of X W_g for all 64
   // tokens (4 blocks of 16), so each wave reads a quarter of W_g; the four
   // partial sums are added through LDS (one head block at a time, fixed order)
   __shared__ float gpart[4][4][4][64];  // [wave][token block][r][lane]
-  f32x4 acc[4][HMAX / 16];
+  f32x4 acc[4][NHB];
 #pragma unroll
   for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
-    for (int hb = 0; hb < HMAX / 16; ++hb) acc[tb][hb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int hb = 0; hb < NHB; ++hb) acc[tb][hb] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int S = dm / 32, s0 = w * S / 4, s1 = (w + 1) * S / 4;
   const T* xblk = x + ((size_t)b * L + (size_t)c * CUBE + cc) * dm;
-#pragma unroll 2
+#pragma unroll 4
   for (int s = s0; s < s1; ++s) {
     Frag<T> a[4];
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb) a[tb] = frag_from8(load8(xblk + (size_t)16 * tb * dm + 32 * s + 8 * g));
 #pragma unroll
-    for (int hb = 0; hb < HMAX / 16; ++hb) {
-      if (hb < nhb) {
-        const Frag<T> bhi = frag_from8(load8(fhi + (size_t)(16 * hb + cc) * dm + 32 * s + 8 * g));
-        Frag<T> blo;
-        if constexpr (SPLIT) blo = frag_from8(load8(flo + (size_t)(16 * hb + cc) * dm + 32 * s + 8 * g));
+    for (int hb = 0; hb < NHB; ++hb) {
+      const Frag<T> bhi = frag_from8(load8(fhi + (size_t)(16 * hb + cc) * dm + 32 * s + 8 * g));
+      Frag<T> blo;
+      if constexpr (SPLIT) blo = frag_from8(load8(flo + (size_t)(16 * hb + cc) * dm + 32 * s + 8 * g));
 #pragma unroll
-        for (int tb = 0; tb < 4; ++tb) {
-          mma(acc[tb][hb], a[tb], bhi);
-          if constexpr (SPLIT) mma(acc[tb][hb], a[tb], blo);
-        }
+      for (int tb = 0; tb < 4; ++tb) {
+        mma(acc[tb][hb], a[tb], bhi);
+        if constexpr (SPLIT) mma(acc[tb][hb], a[tb], blo);
       }
     }
   }
   // acc[tb][hb] lane (g, c): tokens 16 tb + 4g + r (rows), head 16 hb + c (column)
-  for (int hb = 0; hb < nhb; ++hb) {
+#pragma unroll
+  for (int hb = 0; hb < NHB; ++hb) {
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
-      for (int hb2 = 0; hb2 < HMAX / 16; ++hb2)
-        if (hb2 == hb)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) gpart[w][tb][r][lane] = acc[tb][hb2][r];
+      for (int r = 0; r < 4; ++r) gpart[w][tb][r][lane] = acc[tb][hb][r];
     __syncthreads();
     const int tb = w;  // wave w finishes token block w
     const int h = 16 * hb + cc;
@@ -128,11 +123,14 @@ __global__ __launch_bounds__(256) void k_gate_fwd(const T* __restrict__ x, const
   }
   __syncthreads();
   constexpr int UPR = D / 8;  // units per token row
-#pragma unroll 4
+  constexpr int UPT = 64 * UPR / 256;  // units per thread and head
+#pragma unroll 2
   for (int h = 0; h < H; ++h) {
     const size_t bh = (size_t)b * H + h;
     const float* oc = oc_hat + (bh * nb + c) * D;
-    for (int u = tid; u < 64 * UPR; u += 256) {
+#pragma unroll
+    for (int i = 0; i < UPT; ++i) {
+      const int u = tid + 256 * i;
       const int t = u / UPR, dg = u % UPR;
       const float gv = gs[t][h];
       const size_t off = (bh * L + (size_t)c * CUBE + t) * D + 8 * dg;
@@ -150,7 +148,7 @@ __global__ __launch_bounds__(256) void k_gate_fwd(const T* __restrict__ x, const
 
 // One block per (cube, batch): dgate, dpre = dg (1 - g^2), dO_hat_c and its
 // rowsum against O_hat_c for every head, then dX = dpre W_g^T.
-template <typename T, int D>
+template <typename T, int D, int NS>
 __global__ __launch_bounds__(256) void k_gate_bwd(const T* __restrict__ wt, const float* __restrict__ oc_hat,
                                                   const float* __restrict__ gin, const T* __restrict__ d_o,
                                                   float* __restrict__ dpre, T* __restrict__ doc,
@@ -160,8 +158,14 @@ __global__ __launch_bounds__(256) void k_gate_bwd(const T* __restrict__ wt, cons
   constexpr bool SPLIT = sizeof(T) == 2;
   constexpr int UPR = D / 8;
   constexpr int RROWS = 256 / UPR;
-  __shared__ float dps[64][HMAX + 4];
-  __shared__ float red[RROWS][D];
+  // dps and red during the head loop; afterwards the same bytes stage the dX
+  // tiles (one 64-token x 64-column tile per wave)
+  constexpr int DPS_BYTES = 64 * (HMAX + 4) * 4, RED_BYTES = RROWS * D * 4;
+  constexpr int STAGE_BYTES = 4 * 64 * 64 * (int)sizeof(T);
+  constexpr int SMEM = DPS_BYTES + RED_BYTES > STAGE_BYTES ? DPS_BYTES + RED_BYTES : STAGE_BYTES;
+  __shared__ __align__(16) char smem[SMEM];
+  float(*dps)[HMAX + 4] = reinterpret_cast<float(*)[HMAX + 4]>(smem);
+  float(*red)[D] = reinterpret_cast<float(*)[D]>(smem + DPS_BYTES);
   __shared__ float wsum[4];
   const int c = blockIdx.x, b = blockIdx.y, tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4,
             cc = lane & 15;
@@ -248,38 +252,66 @@ __global__ __launch_bounds__(256) void k_gate_bwd(const T* __restrict__ wt, cons
       }
     }
   __syncthreads();
-  // dX^T[m][t] = sum_h W_g[m][h] dpre[t][h]
+  // dX^T[m][t] = sum_h W_g[m][h] dpre[t][h]: wave w takes the column blocks
+  // [w dm/64, (w+1) dm/64) for all 64 tokens, so each wave reads a quarter of
+  // W_g (its hi and lo parts) and reuses every fragment for 4 token blocks
   const T* bhi = wt + 2 * (size_t)hp * dm;
   const T* blo = bhi + (size_t)dm * hk;
-  Frag<T> phi[HMAX / 32], plo[HMAX / 32];
+  Frag<T> phi[4][NS], plo[4][NS];
 #pragma unroll
-  for (int s = 0; s < HMAX / 32; ++s) {
-    if (32 * s < hk) {
+  for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
       float v8[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) v8[e] = dps[16 * w + cc][32 * s + 8 * g + e];
-      split8<T>(v8, phi[s], plo[s]);
+      for (int e = 0; e < 8; ++e) v8[e] = dps[16 * tb + cc][32 * s + 8 * g + e];
+      split8<T>(v8, phi[tb][s], plo[tb][s]);
     }
-  }
-  T* dxb = dx + ((size_t)b * L + (size_t)c * CUBE + 16 * w + cc) * dm;
-  for (int mb = 0; mb < dm / 16; ++mb) {
-    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+  __syncthreads();  // every wave has its dpre fragments: dps may be overwritten
+  // Each wave stages 64 tokens x 64 columns (four column blocks) at a time and
+  // writes them as whole 128-byte row segments; dm is a multiple of 64.
+  T* stage = reinterpret_cast<T*>(smem) + w * 64 * 64;
+  T* dxt = dx + ((size_t)b * L + (size_t)c * CUBE) * dm;
+  const int nq = dm / 64, q0 = w * nq / 4, q1 = (w + 1) * nq / 4;
+  for (int qd = q0; qd < q1; ++qd) {
 #pragma unroll
-    for (int s = 0; s < HMAX / 32; ++s) {
-      if (32 * s < hk) {
+    for (int j = 0; j < 4; ++j) {
+      const int mb = 4 * qd + j;
+      f32x4 acc[4];
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb) acc[tb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
         const Frag<T> ahi = frag_from8(load8(bhi + (size_t)(16 * mb + cc) * hk + 32 * s + 8 * g));
-        mma(acc, ahi, phi[s]);
-        if constexpr (SPLIT) {
-          const Frag<T> alo = frag_from8(load8(blo + (size_t)(16 * mb + cc) * hk + 32 * s + 8 * g));
-          mma(acc, ahi, plo[s]);
-          mma(acc, alo, phi[s]);
+        Frag<T> alo;
+        if constexpr (SPLIT) alo = frag_from8(load8(blo + (size_t)(16 * mb + cc) * hk + 32 * s + 8 * g));
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) {
+          mma(acc[tb], ahi, phi[tb][s]);
+          if constexpr (SPLIT) {
+            mma(acc[tb], ahi, plo[tb][s]);
+            mma(acc[tb], alo, phi[tb][s]);
+          }
         }
       }
-    }
-    Vec4<T> r4;
+      // lane (g, c): columns 16j + 4g .. +3 of token 16tb + c; the 8-byte
+      // pieces are placed at chunk (2j + g/2) ^ (t & 7) of the token's row
 #pragma unroll
-    for (int r = 0; r < 4; ++r) r4.v[r] = from_f32<T>(acc[r]);
-    store4(dxb + 16 * mb + 4 * g, r4);
+      for (int tb = 0; tb < 4; ++tb) {
+        Vec4<T> r4;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) r4.v[r] = from_f32<T>(acc[tb][r]);
+        const int t = 16 * tb + cc;
+        store4(stage + t * 64 + 8 * ((2 * j + (g >> 1)) ^ (t & 7)) + 4 * (g & 1), r4);
+      }
+    }
+    // 8 lanes per token row: lane l writes chunk l % 8 of rows l / 8 + 8i
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int t = lane / 8 + 8 * i, ch = lane % 8;
+      const Vec8<T> v = load8(stage + t * 64 + 8 * (ch ^ (t & 7)));
+      store8(dxt + (size_t)t * dm + 64 * qd + 8 * ch, v);
+    }
   }
 }
 
@@ -484,8 +516,18 @@ template <typename T, int D>
 hipError_t launch_gate_fwd_t(const GateArgs& a, hipStream_t st) {
   hipError_t e = gate_prep<T>(a.w_g, a.wt, a.dm, a.heads, st);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((k_gate_fwd<T, D>), dim3(a.nb, a.batch), dim3(256), 0, st, (const T*)a.x, (const T*)a.wt,
-                     a.oc_hat, (const T*)a.o_f, (T*)a.o, a.g, a.heads, a.nb, a.dm, pad_up(a.heads, 16));
+  const int hp = pad_up(a.heads, 16);
+  const dim3 grid(a.nb, a.batch);
+#define VSA2_GATE_FWD(NHB)                                                                                     \
+  hipLaunchKernelGGL((k_gate_fwd<T, D, NHB>), grid, dim3(256), 0, st, (const T*)a.x, (const T*)a.wt, a.oc_hat, \
+                     (const T*)a.o_f, (T*)a.o, a.g, a.heads, a.nb, a.dm, hp)
+  switch (hp / 16) {
+    case 1: VSA2_GATE_FWD(1); break;
+    case 2: VSA2_GATE_FWD(2); break;
+    case 3: VSA2_GATE_FWD(3); break;
+    default: VSA2_GATE_FWD(4); break;
+  }
+#undef VSA2_GATE_FWD
   return hipGetLastError();
 }
 
@@ -499,9 +541,14 @@ hipError_t launch_gate_bwd_t(const GateBwdArgs& a, hipStream_t st) {
   hipError_t e = gate_prep<T>(a.w_g, a.wt, a.dm, a.heads, st);
   if (e != hipSuccess) return e;
   const int hp = pad_up(a.heads, 16), hk = pad_up(a.heads, 32);
-  hipLaunchKernelGGL((k_gate_bwd<T, D>), dim3(a.nb, a.batch), dim3(256), 0, st, (const T*)a.wt, a.oc_hat, a.g,
-                     (const T*)a.d_o, a.dpre, (T*)a.doc, a.lse_c, a.stats_c, (T*)a.dx, a.heads, a.nb, a.nbp, a.dm, hp,
-                     hk);
+  if (hk <= 32)
+    hipLaunchKernelGGL((k_gate_bwd<T, D, 1>), dim3(a.nb, a.batch), dim3(256), 0, st, (const T*)a.wt, a.oc_hat, a.g,
+                       (const T*)a.d_o, a.dpre, (T*)a.doc, a.lse_c, a.stats_c, (T*)a.dx, a.heads, a.nb, a.nbp, a.dm,
+                       hp, hk);
+  else
+    hipLaunchKernelGGL((k_gate_bwd<T, D, 2>), dim3(a.nb, a.batch), dim3(256), 0, st, (const T*)a.wt, a.oc_hat, a.g,
+                       (const T*)a.d_o, a.dpre, (T*)a.doc, a.lse_c, a.stats_c, (T*)a.dx, a.heads, a.nb, a.nbp, a.dm,
+                       hp, hk);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if constexpr (sizeof(T) == 2) {
