@@ -25,7 +25,11 @@ TINY_TRAIN = Workload("tiny-train", 11, (8, 16, 16), 1, 2, 64, "f32", 8, "sinuso
 MID = Workload("mid", 12, (8, 16, 32), 1, 4, 128, "bf16", 8, "lowrank", train=True)          # nb = 64
 RAGGED = Workload("ragged", 13, (4, 8, 20), 1, 3, 64, "bf16", 3, "lowrank", train=True)      # nb = 10
 RAGGED32 = Workload("ragged32", 14, (4, 12, 20), 1, 2, 128, "f32", 5, "lowrank", skew=True, train=True)  # nb = 15
-SMALL = [TINY_TRAIN, MID, RAGGED, RAGGED32]
+# gate-kernel shapes: 36 heads (three 16-head blocks, a 64-wide dX contraction),
+# and 5 heads with d_model = 320 (a partial 256-column block of dW_g)
+HEADS36 = Workload("heads36", 15, (4, 8, 16), 1, 36, 64, "bf16", 3, "lowrank", train=True)   # nb = 8
+COLS320 = Workload("cols320", 16, (4, 8, 16), 1, 5, 64, "bf16", 3, "lowrank", train=True)    # d_model = 320
+SMALL = [TINY_TRAIN, MID, RAGGED, RAGGED32, HEADS36, COLS320]
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -212,7 +216,7 @@ def test_kernel_timer_counts_launches():
 
 # ----------------------------------------------------------------------------- coarse + gate
 @pytest.mark.parametrize("zero_gate", [True, False])
-@pytest.mark.parametrize("w", [TINY, MID, RAGGED, RAGGED32], ids=lambda w: w.name)
+@pytest.mark.parametrize("w", [TINY, MID, RAGGED, RAGGED32, HEADS36, COLS320], ids=lambda w: w.name)
 def test_coarse_gate(w, zero_gate):
     (q, k, v, x, w_g), (qd, kd, vd, xd, wd), layer = _setup(w, zero_gate=zero_gate)
     masks = gu.masks_from_csr(*[t.view(w.heads, -1) for t in make_selection(w)], w.nb)
