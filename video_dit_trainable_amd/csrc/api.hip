@@ -396,7 +396,7 @@ int vsa2_sparse_attn_bwd(const vsa2_problem* p, int32_t topk, const void* q, con
   AttnBwdArgs a{};
   a.q = q; a.k = k; a.v = v; a.o = o_f; a.d_o = d_o;
   a.lse = lse;
-  a.stats = (const float*)ws;
+  a.stats_out = (float*)ws;
   a.row_ptr = row_ptr; a.col_idx = col_idx; a.col_ptr = col_ptr; a.row_idx = row_idx;
   const size_t cstride = (size_t)d.bh * d.nb * d.d;
   a.dq_add = dqkv_c;
@@ -409,8 +409,6 @@ int vsa2_sparse_attn_bwd(const vsa2_problem* p, int32_t topk, const void* q, con
   a.scale = d.scale;
   a.scale_log2 = d.scale * 1.4426950408889634f;
   a.ct = p->lat_t / 4; a.cy = p->lat_y / 4; a.cx = p->lat_x / 4;
-  hipError_t e = launch_bwd_delta(a, (float*)ws, st);
-  if (e != hipSuccess) return VSA2_E_HIP;
   return hip_status(launch_attn_bwd(a, st));
 }
 

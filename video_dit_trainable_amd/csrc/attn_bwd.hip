@@ -12,7 +12,9 @@
 //  * k_bwd_dq: one block (2 waves x 32 queries) per query cube i over its KV
 //    list (CSR): S^T, P^T, dP^T = V dO^T, dS^T, dQ += dS K (K^T fragments by
 //    transposing reads of the K tile).
-// delta = rowsum(dO * O) comes from k_bwd_delta.  Per-cube gradient rows
+// The row statistics (lse * log2 e, -delta) with delta = rowsum(dO * O) are
+// computed by the dQ kernel, which holds every query row's dO anyway; it runs
+// first and the dK/dV kernel reads them.  Per-cube gradient rows
 // (the coarse branch's dQ_c, dK_c, dV_c) are added as row/64 to every token of
 // the cube before the single rounding to the storage type.
 #include <cmath>
@@ -26,28 +28,6 @@ namespace vsa2 {
 // lse_t * log2(e) (+inf for a row with no selected key, so its P is 0) and
 // stats[2t + 1] = -delta_t = -(dO_t . O_t), the initial value of the dP
 // accumulators, so that they end at dP - delta.
-template <typename T, int D>
-__global__ __launch_bounds__(256) void k_bwd_delta(const T* __restrict__ o, const T* __restrict__ d_o,
-                                                   const float* __restrict__ lse, float* __restrict__ stats,
-                                                   size_t rows) {
-  constexpr int LPT = D / 8;  // lanes per row
-  const size_t row = ((size_t)blockIdx.x * 256 + threadIdx.x) / LPT;
-  const int part = threadIdx.x % LPT;
-  float s = 0.f;
-  if (row < rows) {
-    Vec8<T> a = load8(o + row * D + 8 * part);
-    Vec8<T> b = load8(d_o + row * D + 8 * part);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) s += to_f32(a.v[e]) * to_f32(b.v[e]);
-  }
-#pragma unroll
-  for (int x = 1; x < LPT; x <<= 1) s += __shfl_xor(s, x);
-  if (row < rows && part == 0) {
-    const float l = lse[row];
-    stats[2 * row] = l == -INFINITY ? INFINITY : l * LOG2E;
-    stats[2 * row + 1] = -s;
-  }
-}
 
 // One (query cube, KV cube) pair of the dK/dV kernel for one wave: keys 32kh..
 // (K, V fragments kf, vf in registers) against queries 32qh.. of the Q / dO
@@ -384,10 +364,11 @@ __device__ __forceinline__ void dq_pair(const T* ks, const T* vs, int brow, int 
 // key halves are summed through LDS at the end.  K / V tiles of the next pair
 // are copied LDS-direct into the other stage while the current pair runs
 // (distinct stage arrays, loop unrolled by two, as in the dK/dV kernel).
-template <typename T, typename TO, int D, bool DENSE>
+template <typename T, typename TO, int D, bool DENSE, bool STATS>
 __global__ __launch_bounds__(256, 2) void k_bwd_dq(const T* __restrict__ q, const T* __restrict__ k,
                                                    const T* __restrict__ v, const T* __restrict__ d_o,
-                                                   const float* __restrict__ stats,
+                                                   const T* __restrict__ o, const float* __restrict__ lse,
+                                                   float* __restrict__ stats_out, const float* __restrict__ stats,
                                                    const int32_t* __restrict__ row_ptr,
                                                    const int32_t* __restrict__ col_idx,
                                                    const float* __restrict__ dq_add, TO* __restrict__ dq, int nq,
@@ -449,8 +430,28 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(const T* __restrict__ q, cons
       qf[qb][s] = frag_global<T, D>(q + hoff, qrow, s, g);
       of[qb][s] = frag_global<T, D>(d_o + hoff, qrow, s, g);
     }
-    l2[qb] = stats[2 * ((size_t)bh * ld + qrow)];
-    ndl[qb] = stats[2 * ((size_t)bh * ld + qrow) + 1];
+    if constexpr (STATS) {
+      // delta = dO . O over the row: this lane's 4 x 8 elements, then the 4 lanes g
+      float part = 0.f;
+#pragma unroll
+      for (int s = 0; s < D / 32; ++s) {
+        const Frag<T> of8 = frag_global<T, D>(o + hoff, qrow, s, g);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) part = fmaf(to_f32(of[qb][s].v[e]), to_f32(of8.v[e]), part);
+      }
+      part += __shfl_xor(part, 16);
+      part += __shfl_xor(part, 32);
+      const float l = lse[(size_t)bh * ld + qrow];
+      l2[qb] = l == -INFINITY ? INFINITY : l * LOG2E;
+      ndl[qb] = -part;
+      if (kh == 0 && g == 0) {
+        stats_out[2 * ((size_t)bh * ld + qrow)] = l2[qb];
+        stats_out[2 * ((size_t)bh * ld + qrow) + 1] = ndl[qb];
+      }
+    } else {
+      l2[qb] = stats[2 * ((size_t)bh * ld + qrow)];
+      ndl[qb] = stats[2 * ((size_t)bh * ld + qrow) + 1];
+    }
   }
   // dQ^T partial over this wave's key half: rows d = 16db + 4g + r, column query 16qb + cc
   f32x4 dqa[D / 16][2];
@@ -538,36 +539,29 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(const T* __restrict__ q, cons
   }
 }
 
-template <typename T, int D>
-hipError_t launch_delta_t(const AttnBwdArgs& a, float* stats, hipStream_t st) {
-  const size_t rows = (size_t)a.bh * a.ld;
-  const size_t threads = rows * (D / 8);
-  hipLaunchKernelGGL((k_bwd_delta<T, D>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st, (const T*)a.o,
-                     (const T*)a.d_o, a.lse, stats, rows);
-  return hipGetLastError();
-}
-
-hipError_t launch_bwd_delta(const AttnBwdArgs& a, float* stats, hipStream_t st) {
-  if (a.bf16) return a.d == 128 ? launch_delta_t<bf16, 128>(a, stats, st) : launch_delta_t<bf16, 64>(a, stats, st);
-  return a.d == 128 ? launch_delta_t<float, 128>(a, stats, st) : launch_delta_t<float, 64>(a, stats, st);
-}
-
 template <typename T, typename TO, int D, bool DENSE>
 hipError_t launch_bwd_tt(const AttnBwdArgs& a, hipStream_t st) {
-  if (!DENSE) timer_before(TK_BWD_DKDV, st);
-  hipLaunchKernelGGL((k_bwd_dkdv<T, TO, D, DENSE>), dim3(xcd_grid(a.nkv, a.bh)), dim3(256), 0, st, (const T*)a.q,
-                     (const T*)a.k, (const T*)a.v, (const T*)a.d_o, a.stats, a.col_ptr, a.row_idx, a.dk_add,
-                     a.dv_add, (TO*)a.dk, (TO*)a.dv, a.nq, a.nkv, a.seq, a.ld, a.out_rows, a.kph, a.scale,
-                     a.scale_log2);
-  if (!DENSE) timer_after(TK_BWD_DKDV, st);
+  // dQ first: in sparse mode it writes the row statistics the dK/dV kernel reads
+  if (!DENSE) timer_before(TK_BWD_DQ, st);
+  if constexpr (DENSE)
+    hipLaunchKernelGGL((k_bwd_dq<T, TO, D, DENSE, false>), dim3(xcd_grid(a.nq, a.bh)), dim3(256), 0, st,
+                       (const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.d_o, nullptr, nullptr, nullptr,
+                       a.stats, a.row_ptr, a.col_idx, a.dq_add, (TO*)a.dq, a.nq, a.nkv, a.seq, a.ld, a.out_rows, a.kph,
+                       a.scale, a.scale_log2, a.ct, a.cy, a.cx);
+  else
+    hipLaunchKernelGGL((k_bwd_dq<T, TO, D, DENSE, true>), dim3(xcd_grid(a.nq, a.bh)), dim3(256), 0, st,
+                       (const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.d_o, (const T*)a.o, a.lse,
+                       a.stats_out, nullptr, a.row_ptr, a.col_idx, a.dq_add, (TO*)a.dq, a.nq, a.nkv, a.seq, a.ld,
+                       a.out_rows, a.kph, a.scale, a.scale_log2, a.ct, a.cy, a.cx);
+  if (!DENSE) timer_after(TK_BWD_DQ, st);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (!DENSE) timer_before(TK_BWD_DQ, st);
-  hipLaunchKernelGGL((k_bwd_dq<T, TO, D, DENSE>), dim3(xcd_grid(a.nq, a.bh)), dim3(256), 0, st, (const T*)a.q,
-                     (const T*)a.k, (const T*)a.v, (const T*)a.d_o, a.stats, a.row_ptr, a.col_idx, a.dq_add,
-                     (TO*)a.dq, a.nq, a.nkv, a.seq, a.ld, a.out_rows, a.kph, a.scale, a.scale_log2, a.ct, a.cy,
-                     a.cx);
-  if (!DENSE) timer_after(TK_BWD_DQ, st);
+  if (!DENSE) timer_before(TK_BWD_DKDV, st);
+  hipLaunchKernelGGL((k_bwd_dkdv<T, TO, D, DENSE>), dim3(xcd_grid(a.nkv, a.bh)), dim3(256), 0, st, (const T*)a.q,
+                     (const T*)a.k, (const T*)a.v, (const T*)a.d_o, DENSE ? a.stats : a.stats_out, a.col_ptr,
+                     a.row_idx, a.dk_add, a.dv_add, (TO*)a.dk, (TO*)a.dv, a.nq, a.nkv, a.seq, a.ld, a.out_rows,
+                     a.kph, a.scale, a.scale_log2);
+  if (!DENSE) timer_after(TK_BWD_DKDV, st);
   return hipGetLastError();
 }
 

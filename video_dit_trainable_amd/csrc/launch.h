@@ -65,8 +65,9 @@ hipError_t launch_attn_fwd(const AttnArgs& a, hipStream_t st);
 
 struct AttnBwdArgs {
   const void *q, *k, *v, *o, *d_o;
-  const float* lse;                   // [bh, ld] natural log (fine branch; input of launch_bwd_delta)
-  const float* stats;                 // [bh, ld] pairs (lse * log2 e, -rowsum(dO * O)); +inf lse = masked row
+  const float* lse;                   // [bh, ld] natural log (fine branch)
+  const float* stats;                 // dense: [bh, ld] pairs (lse * log2 e, -rowsum(dO * O)); +inf lse = masked row
+  float* stats_out;                   // fine: workspace for the same pairs, written by the dQ kernel
   const int32_t *row_ptr, *col_idx, *col_ptr, *row_idx;
   const float *dq_add, *dk_add, *dv_add;  // [bh, nkv, d] per-cube terms added as row/64 (or NULL)
   void *dq, *dk, *dv;                 // storage dtype (fine) or fp32 (dense)
@@ -78,7 +79,6 @@ struct AttnBwdArgs {
   float scale_log2;
   int ct, cy, cx;                     // cube grid for the blocked visiting order (0 = linear)
 };
-hipError_t launch_bwd_delta(const AttnBwdArgs& a, float* stats, hipStream_t st);
 hipError_t launch_attn_bwd(const AttnBwdArgs& a, hipStream_t st);
 
 struct GateArgs {
