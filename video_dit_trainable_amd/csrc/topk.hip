@@ -221,13 +221,19 @@ __global__ __launch_bounds__(256) void k_compact(const float* __restrict__ score
   uint32_t eq_seen = 0, written = 0;
   const uint64_t lt = lanemask_lt(lane);
   const int64_t row0 = row_ptr[(size_t)bh * (nb + 1) + row];
-  for (int j1 = 0; j1 < nb; j1 += 256) {
-    uint32_t uu[4];  // four 64-column chunks loaded together, then compacted in column order
+  // four 64-column chunks per step, compacted in column order; the next
+  // step's four are loaded while this step's are ranked
+  uint32_t uu[4], un[4];
+  auto load4 = [&](int j1, uint32_t (&d)[4]) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int j = j1 + 64 * q + lane;
-      uu[q] = j < nb ? score_bits(s[j]) : 0u;
+      d[q] = j < nb ? score_bits(s[j]) : 0u;
     }
+  };
+  load4(0, uu);
+  for (int j1 = 0; j1 < nb; j1 += 256) {
+    if (j1 + 256 < nb) load4(j1 + 256, un);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int j0 = j1 + 64 * q;
@@ -248,6 +254,8 @@ __global__ __launch_bounds__(256) void k_compact(const float* __restrict__ score
       eq_seen += __popcll(eqm);
       written += __popcll(selm);
     }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) uu[q] = un[q];
   }
 }
 
@@ -285,13 +293,14 @@ __global__ __launch_bounds__(1024) void k_colptr(const uint32_t* __restrict__ co
 
 // CSC rows in ascending order from the bitmap: block = (64-column strip, bh),
 // wave w scans rows [w*R, (w+1)*R), lane = column.
-__global__ __launch_bounds__(256) void k_csc_fill(const uint32_t* __restrict__ bitmap, const int32_t* __restrict__ col_ptr,
-                                                  int32_t* __restrict__ row_idx, int nb, int64_t kph, int words) {
-  __shared__ uint32_t cnt[4][64];
+__global__ __launch_bounds__(1024) void k_csc_fill(const uint32_t* __restrict__ bitmap, const int32_t* __restrict__ col_ptr,
+                                                   int32_t* __restrict__ row_idx, int nb, int64_t kph, int words) {
+  constexpr int NW = 16;  // waves per strip, each over nb / NW consecutive rows
+  __shared__ uint32_t cnt[NW][64];
   const int bh = blockIdx.y, strip = blockIdx.x, w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int j = strip * 64 + lane;
-  const int R = (nb + 3) / 4;
-  const int r0 = w * R, r1 = min(nb, r0 + R);
+  const int R = (nb + NW - 1) / NW;
+  const int r0 = min(nb, w * R), r1 = min(nb, r0 + R);
   const uint32_t* bm = bitmap + (size_t)bh * nb * words + 2 * strip + (lane >> 5);
   const uint32_t bit = 1u << (lane & 31);
   uint32_t c = 0;
@@ -312,7 +321,7 @@ static hipError_t csc_from_bitmap(const TopkArgs& a, hipStream_t st) {
   hipLaunchKernelGGL(k_colptr, dim3(a.bh), dim3(1024), 0, st, a.ws.colcnt, a.col_ptr, a.nb);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_csc_fill, dim3(a.ws.words / 2, a.bh), dim3(256), 0, st, a.ws.bitmap, a.col_ptr, a.row_idx,
+  hipLaunchKernelGGL(k_csc_fill, dim3(a.ws.words / 2, a.bh), dim3(1024), 0, st, a.ws.bitmap, a.col_ptr, a.row_idx,
                      a.nb, a.k, a.ws.words);
   return hipGetLastError();
 }
