@@ -152,23 +152,18 @@ __device__ __forceinline__ Frag<T> frag_from_acc(const f32x4& lo, const f32x4& h
 }
 
 // ---------------------------------------------------------------------------
-// 64 x D tile movement between global memory and LDS.
-// A "unit" is 4 rows x 8 columns; thread t owns units t, t + NT, ...
-// Row-major LDS tiles have row stride RS = D + 8 elements (the pad spreads the
-// 16 rows a fragment read touches over all banks).  Transposed tiles hold D
-// rows of 64 tokens; the 4-token runs of row d are XOR-swizzled by sw(d), so
-// the scatter of a unit (8 rows, one 4-token run each) and the fragment reads
-// (16 rows, one run each) both spread over the banks:
+// 64 x D tiles staged through registers into a transposed LDS layout (the
+// fp32-storage dW_g kernel).  A "unit" is 4 rows x 8 columns; thread t owns
+// units t, t + NT, ...  The transposed tile holds D rows of 64 tokens; the
+// 4-token runs of row d are XOR-swizzled by sw(d), so the scatter of a unit
+// (8 rows, one 4-token run each) and the fragment reads (16 rows, one run
+// each) both spread over the banks:
 //   element (d, t) lives at d*TS + 4*((t >> 2) ^ sw(d)) + (t & 3).
-// The stride/swizzle pairs were chosen with a bank model (32- and 64-bank LDS)
-// over the exact access patterns of tile_store_tr and frag_tr.
 // ---------------------------------------------------------------------------
 template <typename T, int D> struct TileGeom {
   static constexpr bool WIDE = (sizeof(T) == 2 && D == 128);
   static constexpr int UNITS = (CUBE / 4) * (D / 8);
-  static constexpr int RS = D + 8;              // row-major row stride (elements)
   static constexpr int TS = WIDE ? 72 : 64;     // transposed row stride (elements)
-  static constexpr int RM_ELEMS = CUBE * RS;
   static constexpr int TR_ELEMS = D * TS;
   __device__ static constexpr int sw(int d) { return WIDE ? ((d >> 3) & 15) : (((d >> 3) ^ d) & 15); }
 };
@@ -203,20 +198,6 @@ __device__ __forceinline__ void tile_load(TileRegs<T, D, NT>& R, const T* __rest
 }
 
 template <typename T, int D, int NT>
-__device__ __forceinline__ void tile_store_rm(const TileRegs<T, D, NT>& R, T* lds, int tid) {
-  constexpr int RS = TileGeom<T, D>::RS;
-#pragma unroll
-  for (int n = 0; n < TileRegs<T, D, NT>::NU; ++n) {
-    const int u = tid + n * NT;
-    if (u < TileGeom<T, D>::UNITS) {
-      const int rg = u / (D / 8), cg = u % (D / 8);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) store8(lds + (4 * rg + r) * RS + 8 * cg, R.r[n][r]);
-    }
-  }
-}
-
-template <typename T, int D, int NT>
 __device__ __forceinline__ void tile_store_tr(const TileRegs<T, D, NT>& R, T* lds, int tid) {
   constexpr int TS = TileGeom<T, D>::TS;
 #pragma unroll
@@ -234,12 +215,6 @@ __device__ __forceinline__ void tile_store_tr(const TileRegs<T, D, NT>& R, T* ld
       }
     }
   }
-}
-
-// A/B fragment of a row-major LDS tile: row `row`, k-step ks, slot group g.
-template <typename T, int D>
-__device__ __forceinline__ Frag<T> frag_rm(const T* lds, int row, int ks, int g) {
-  return frag_from8(load8(lds + row * TileGeom<T, D>::RS + 32 * ks + 8 * g));
 }
 
 // A fragment of a transposed LDS tile (row = feature d, k = token) with the pi

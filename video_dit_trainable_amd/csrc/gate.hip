@@ -16,11 +16,6 @@ namespace vsa2 {
 
 constexpr int HMAX = 64;   // heads supported by the gate kernels
 
-struct GateGeom {
-  int hp, hk;  // heads padded to 16 (forward N) and 32 (backward K)
-  size_t f_elems() const { return 0; }
-};
-
 __host__ __device__ inline int pad_up(int x, int m) { return (x + m - 1) / m * m; }
 
 // Repack W_g [dm, H] fp32 into MFMA operands: F = W_g^T [hp, dm] (hi, lo) and
