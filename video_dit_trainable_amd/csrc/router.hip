@@ -64,15 +64,16 @@ __device__ __forceinline__ float sum8(float x) {
 }
 
 // One 64-key tile for one wave: acc[kb][qb] = S^T block (keys of LDS rows
-// 16kb + 4g + r, query 32w + 16qb + c), unscaled.
+// 16kb + 4g + r, query 32w + 16qb + c), unscaled.  bf16: bs[s] is this lane's
+// element offset of k-step s in row cc of the tile (the swizzle XOR already
+// applied), so every read is a base register plus an immediate.
 template <typename T, int D>
-__device__ __forceinline__ void tile_scores(const T* ks, int brow, const Frag<T> (&qf)[2][D / 32], int g, int cc,
-                                            f32x4 (&acc)[4][2]) {
-  opaque(brow);
+__device__ __forceinline__ void tile_scores(const T* ks, const int (&bs)[D / 32], const Frag<T> (&qf)[2][D / 32],
+                                            int g, int cc, f32x4 (&acc)[4][2]) {
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb) {
     Frag<T> a;
-    if constexpr (sizeof(T) == 2) a = sw_frag_at<T>(ks, brow + 16 * kb * D, 0);
+    if constexpr (sizeof(T) == 2) a = frag_from8(load8(ks + bs[0] + 16 * kb * D));
     else a = sw_frag<T, D>(ks, 16 * kb + cc, 0, g);
     acc[kb][0] = mma0(a, qf[0][0]);
     acc[kb][1] = mma0(a, qf[1][0]);
@@ -82,7 +83,7 @@ __device__ __forceinline__ void tile_scores(const T* ks, int brow, const Frag<T>
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
       Frag<T> a;
-      if constexpr (sizeof(T) == 2) a = sw_frag_at<T>(ks, brow + 16 * kb * D, s);
+      if constexpr (sizeof(T) == 2) a = frag_from8(load8(ks + bs[s] + 16 * kb * D));
       else a = sw_frag<T, D>(ks, 16 * kb + cc, s, g);
       mma(acc[kb][0], a, qf[0][s]);
       mma(acc[kb][1], a, qf[1][s]);
@@ -132,8 +133,51 @@ __global__ __launch_bounds__(256, 2) void k_router(const T* __restrict__ qr, con
     }
     if constexpr (PASS2) lse[qb] = qrow < Lr ? lse2[(size_t)bh * Lr + qrow] : INFINITY;
   }
-  int brow = 0;
-  if constexpr (sizeof(T) == 2) brow = sw_row_base<T, D>(cc, g);
+  int bs[D / 32] = {};  // bf16: per-lane fragment offsets of the k-steps (see tile_scores)
+  if constexpr (sizeof(T) == 2) {
+    const int brow = sw_row_base<T, D>(cc, g);
+#pragma unroll
+    for (int s = 0; s < D / 32; ++s) {
+      bs[s] = brow ^ (32 * s);
+      opaque(bs[s]);
+    }
+  }
+  // key-tile copies: for a full tile the per-lane source offsets are fixed and
+  // only the (uniform) tile base moves; a ragged last tile takes dma_keys
+  using S = SwTile<T, D>;
+  constexpr int RSTEP = 256 / S::NCH;
+  constexpr int NCP = RK * S::NCH / 256;
+  const int nfull = Lr / RK;
+  const int wbase = __builtin_amdgcn_readfirstlane(tid & ~63);
+  int coff[NCP];
+#pragma unroll
+  for (int n = 0; n < NCP; ++n) {
+    const int r = n * RSTEP + tid / S::NCH, pc = tid % S::NCH;
+    coff[n] = (key_of_row(r) * D + S::EPC * (pc ^ (S::f(r) & (S::NCH - 1)))) * (int)sizeof(T);
+  }
+  auto copy_tile = [&](int t, T* lds) {
+    if (t < nfull) {
+      const char* src = reinterpret_cast<const char*>(kbase + (size_t)t * RK * D);
+      asm volatile("" : "+s"(src));  // keep the tile base one uniform value (scalar registers)
+#pragma unroll
+      for (int n = 0; n < NCP; ++n) {
+        int off = coff[n];
+        opaque(off);  // a 32-bit per-lane offset on a uniform base (saddr form)
+        lds_copy16(src + (uint32_t)off, (VSA2_LDS void*)(lds + (n * 256 + wbase) * S::EPC));
+      }
+    } else {
+      dma_keys<T, D>(kbase, t * RK, Lr, lds, tid);
+    }
+  };
+  // pass 2: the lane that stores a block score (the first of each 8 query lanes)
+  bool qstore[2];
+  float* srow[2];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const int qcube = (qt * RQ + 32 * w + 16 * qb + cc) >> 3;
+    qstore[qb] = (cc & 7) == 0 && qcube < nb;
+    srow[qb] = scores + ((size_t)bh * nb + min(qcube, nb - 1)) * nb;
+  }
 
   float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};  // pass 1: running max / sum (scaled log2 domain)
 
@@ -161,7 +205,6 @@ __global__ __launch_bounds__(256, 2) void k_router(const T* __restrict__ qr, con
     } else {
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
-        const int qcube = (qt * RQ + 32 * w + 16 * qb + cc) >> 3;
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           float s8 = 0.f;
@@ -171,27 +214,26 @@ __global__ __launch_bounds__(256, 2) void k_router(const T* __restrict__ qr, con
             for (int r = 0; r < 4; ++r) s8 += fast_exp2(fmaf(acc[2 * h + kk][qb][r], c, -lse[qb]));
           s8 = sum8(s8);
           const int kcube = t * (RK / 8) + 4 * h + g;
-          if ((cc & 7) == 0 && qcube < nb && kcube < nb)
-            scores[((size_t)bh * nb + qcube) * nb + kcube] = s8 * (1.0f / 64.0f);
+          if (qstore[qb] && kcube < nb) srow[qb][kcube] = s8 * (1.0f / 64.0f);
         }
       }
     }
   };
 
-  dma_keys<T, D>(kbase, 0, Lr, kA, tid);
+  copy_tile(0, kA);
   for (int t = 0; t < nkt; t += 2) {
     f32x4 acc[4][2];
     wait_vm0();
     __syncthreads();  // stage A holds tile t; every wave is done with stage B
-    if (t + 1 < nkt) dma_keys<T, D>(kbase, (t + 1) * RK, Lr, kB, tid);
-    tile_scores<T, D>(kA, brow, qf, g, cc, acc);
+    if (t + 1 < nkt) copy_tile(t + 1, kB);
+    tile_scores<T, D>(kA, bs, qf, g, cc, acc);
     mask_tail(acc, t * RK, Lr, g);
     consume(acc, t);
     if (t + 1 >= nkt) break;
     wait_vm0();
     __syncthreads();  // stage B holds tile t + 1; every wave is done with stage A
-    if (t + 2 < nkt) dma_keys<T, D>(kbase, (t + 2) * RK, Lr, kA, tid);
-    tile_scores<T, D>(kB, brow, qf, g, cc, acc);
+    if (t + 2 < nkt) copy_tile(t + 2, kA);
+    tile_scores<T, D>(kB, bs, qf, g, cc, acc);
     mask_tail(acc, (t + 1) * RK, Lr, g);
     consume(acc, t + 1);
   }
