@@ -136,7 +136,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the layer shards by head "
-              "across GPUs, which this build does not implement", file=sys.stderr)
+              "across GPUs, which this library does not implement", file=sys.stderr)
         sys.exit(2)
     w = WORKLOADS[args.workload]
     dev = torch.device("cuda:0")

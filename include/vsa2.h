@@ -43,7 +43,7 @@ enum vsa2_status {
   VSA2_E_SHAPE = 2,       /* grid not a multiple of 4, head_dim not 64/128, sizes    */
   VSA2_E_WORKSPACE = 3,   /* workspace smaller than vsa2_workspace_size() reports     */
   VSA2_E_HIP = 4,         /* a HIP call or kernel launch failed                       */
-  VSA2_E_UNSUPPORTED = 5  /* valid request this build does not implement              */
+  VSA2_E_UNSUPPORTED = 5  /* valid request the library does not implement             */
 };
 
 enum vsa2_dtype { VSA2_F32 = 0, VSA2_BF16 = 1 };
