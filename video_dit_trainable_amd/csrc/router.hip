@@ -102,7 +102,9 @@ __device__ __forceinline__ void mask_tail(f32x4 (&acc)[4][2], int k0, int nkeys,
 
 }  // namespace
 
-template <typename T, int D, bool PASS2>
+// TAIL: the pooled key count is not a multiple of 64, so the last key tile is
+// ragged (masked).  Without it no tile is, and the masking is compiled out.
+template <typename T, int D, bool PASS2, bool TAIL>
 __global__ __launch_bounds__(256, 2) void k_router(const T* __restrict__ qr, const T* __restrict__ kr,
                                                    float* __restrict__ lse2, float* __restrict__ scores, int nb,
                                                    float c) {
@@ -227,14 +229,14 @@ __global__ __launch_bounds__(256, 2) void k_router(const T* __restrict__ qr, con
     __syncthreads();  // stage A holds tile t; every wave is done with stage B
     if (t + 1 < nkt) copy_tile(t + 1, kB);
     tile_scores<T, D>(kA, bs, qf, g, cc, acc);
-    mask_tail(acc, t * RK, Lr, g);
+    if constexpr (TAIL) mask_tail(acc, t * RK, Lr, g);
     consume(acc, t);
     if (t + 1 >= nkt) break;
     wait_vm0();
     __syncthreads();  // stage B holds tile t + 1; every wave is done with stage A
     if (t + 2 < nkt) copy_tile(t + 2, kA);
     tile_scores<T, D>(kB, bs, qf, g, cc, acc);
-    mask_tail(acc, (t + 1) * RK, Lr, g);
+    if constexpr (TAIL) mask_tail(acc, (t + 1) * RK, Lr, g);
     consume(acc, t + 1);
   }
 
@@ -250,21 +252,26 @@ __global__ __launch_bounds__(256, 2) void k_router(const T* __restrict__ qr, con
   }
 }
 
-template <typename T, int D>
-hipError_t launch_route_t(const RouteArgs& a, hipStream_t st) {
+template <typename T, int D, bool TAIL>
+hipError_t launch_route_tt(const RouteArgs& a, hipStream_t st) {
   const int nqt = (8 * a.nb + RQ - 1) / RQ;
   dim3 grid(xcd_grid(nqt, a.bh));
   timer_before(TK_ROUTER_LSE, st);
-  hipLaunchKernelGGL((k_router<T, D, false>), grid, dim3(256), 0, st, (const T*)a.qr, (const T*)a.kr, a.lse2,
+  hipLaunchKernelGGL((k_router<T, D, false, TAIL>), grid, dim3(256), 0, st, (const T*)a.qr, (const T*)a.kr, a.lse2,
                      a.scores, a.nb, a.scale_log2);
   timer_after(TK_ROUTER_LSE, st);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   timer_before(TK_ROUTER_SCORES, st);
-  hipLaunchKernelGGL((k_router<T, D, true>), grid, dim3(256), 0, st, (const T*)a.qr, (const T*)a.kr, a.lse2,
+  hipLaunchKernelGGL((k_router<T, D, true, TAIL>), grid, dim3(256), 0, st, (const T*)a.qr, (const T*)a.kr, a.lse2,
                      a.scores, a.nb, a.scale_log2);
   timer_after(TK_ROUTER_SCORES, st);
   return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t launch_route_t(const RouteArgs& a, hipStream_t st) {
+  return (8 * a.nb) % RK ? launch_route_tt<T, D, true>(a, st) : launch_route_tt<T, D, false>(a, st);
 }
 
 hipError_t launch_route(const RouteArgs& a, hipStream_t st) {
