@@ -29,7 +29,10 @@ RAGGED32 = Workload("ragged32", 14, (4, 12, 20), 1, 2, 128, "f32", 5, "lowrank",
 # and 5 heads with d_model = 320 (a partial 256-column block of dW_g)
 HEADS36 = Workload("heads36", 15, (4, 8, 16), 1, 36, 64, "bf16", 3, "lowrank", train=True)   # nb = 8
 COLS320 = Workload("cols320", 16, (4, 8, 16), 1, 5, 64, "bf16", 3, "lowrank", train=True)    # d_model = 320
-SMALL = [TINY_TRAIN, MID, RAGGED, RAGGED32, HEADS36, COLS320]
+# three 64-row tiles of pooled cube tokens (nb = 160, the last one ragged) in
+# the coarse branch's dense attention
+COARSE3 = Workload("coarse3", 17, (8, 20, 64), 1, 2, 64, "bf16", 4, "lowrank", train=True)
+SMALL = [TINY_TRAIN, MID, RAGGED, RAGGED32, HEADS36, COLS320, COARSE3]
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -216,7 +219,7 @@ def test_kernel_timer_counts_launches():
 
 # ----------------------------------------------------------------------------- coarse + gate
 @pytest.mark.parametrize("zero_gate", [True, False])
-@pytest.mark.parametrize("w", [TINY, MID, RAGGED, RAGGED32, HEADS36, COLS320], ids=lambda w: w.name)
+@pytest.mark.parametrize("w", [TINY, MID, RAGGED, RAGGED32, HEADS36, COLS320, COARSE3], ids=lambda w: w.name)
 def test_coarse_gate(w, zero_gate):
     (q, k, v, x, w_g), (qd, kd, vd, xd, wd), layer = _setup(w, zero_gate=zero_gate)
     masks = gu.masks_from_csr(*[t.view(w.heads, -1) for t in make_selection(w)], w.nb)
