@@ -16,6 +16,17 @@ Conventions shared with the library interface:
     rebuilds every token's (t, y, x) from the grid and pools by coordinates.
   * block size B = 64 (4x4x4), router pool R = 8 (2x2x2), G = B/R = 8.
   * softmax scale 1/sqrt(d) unless given.
+  * a latent grid whose sides are not multiples of 4 is padded up to the next
+    multiple along each axis (§2.2 "Kernel Implementation"); tensors hold the
+    padded grid in the order above, and the pad positions are not tokens.
+    Readings taken here, where the paper only says that attention to padding
+    is masked: a pooling window averages the real tokens it holds, and a
+    window holding none does not exist (it is no router key and gives no
+    router row; every 4x4x4 cube holds at least one real token); the G x G
+    mean of Eq.(7) keeps its denominator, with missing entries counted as
+    zero; pad positions are masked as keys, and as queries or gate rows they
+    give O_f = 0, LSE = -inf, g = 0, O = 0 and zero gradients; the coarse
+    branch's gradient goes back to the n real tokens of a cube as 1/n each.
 
 Parity pins: every function here is checked in tests/test_oracle.py against
 closed forms, special cases that reduce to textbook routines (dense softmax
@@ -31,15 +42,22 @@ SUB_SHAPE = (2, 2, 2)
 # ----------------------------------------------------------------------------
 # layout
 # ----------------------------------------------------------------------------
+def padded_grid(grid):
+    """Each side rounded up to a multiple of the cube side 4."""
+    return tuple(-(-int(n) // 4) * 4 for n in grid)
+
+
 def token_coords(grid):
-    """(t, y, x) of every token slot in cube-tiled order, shape [L, 3].
+    """(t, y, x) of every token slot in cube-tiled order, shape [L, 3], L the
+    token count of the padded grid.
 
     Cube-major order over the (T/4, Y/4, X/4) cube grid (§2.2 "Permutation");
     inside a cube the reading taken here is sub-cube-major: slot 64c + 8s + u
     holds sub-cube s (raster over the 2x2x2 sub-cube grid of the cube) and
-    position u (raster inside the 2x2x2 sub-cube).
+    position u (raster inside the 2x2x2 sub-cube).  Slots whose coordinates
+    reach past ``grid`` are padding.
     """
-    T, Y, X = grid
+    T, Y, X = padded_grid(grid)
     ct, cy, cx = T // 4, Y // 4, X // 4
     coords = np.empty((T * Y * X, 3), dtype=np.int64)
     slot = 0
@@ -57,6 +75,11 @@ def token_coords(grid):
     return coords
 
 
+def token_valid(grid):
+    """True for the slots that hold a token of ``grid`` (not padding), [L]."""
+    return np.all(token_coords(grid) < np.asarray(grid, dtype=np.int64), axis=1)
+
+
 def pool_groups(grid, pool):
     """Token slots of each pooling window, ordered cube-major then window raster
     inside the cube.  Returns int array [L / prod(pool), prod(pool)].
@@ -64,7 +87,7 @@ def pool_groups(grid, pool):
     The windows tile every 4x4x4 cube (pool in {1,2,4}^3), so a pooled token
     index a belongs to cube a // (64 / prod(pool)).
     """
-    T, Y, X = grid
+    T, Y, X = padded_grid(grid)
     pt, py, px = pool
     coords = token_coords(grid)
     slot_of = np.empty((T, Y, X), dtype=np.int64)
@@ -84,9 +107,18 @@ def pool_groups(grid, pool):
 
 def mean_pool(x, grid, pool):
     """MeanPool over windows of shape ``pool`` (Eq.(1) with the cube, Eq.(5)
-    with the router window).  x: [L, d] -> [L / prod(pool), d]."""
+    with the router window).  x: [L, d] -> [L / prod(pool), d].  A window
+    averages the real tokens it holds; one holding none gives a zero row."""
     grp = pool_groups(grid, pool)
-    return x[grp].mean(axis=1)
+    ok = token_valid(grid)[grp]                               # [windows, members]
+    cnt = ok.sum(axis=1)
+    tot = np.where(ok[..., None], np.asarray(x)[grp], 0.0).sum(axis=1)
+    return np.where(cnt[:, None] > 0, tot / np.maximum(cnt, 1)[:, None], 0.0)
+
+
+def pool_exists(grid, pool):
+    """True for the pooling windows that hold at least one real token."""
+    return token_valid(grid)[pool_groups(grid, pool)].any(axis=1)
 
 
 def round_bf16(x):
@@ -121,28 +153,38 @@ def router_scores(q, k, grid, pool=SUB_SHAPE, scale=None, bf16_pooled=False, row
     Eq.(7): P_r[i, j] = mean of the G x G entries of P_hat between cube i and
     cube j (the paper's MeanPool_{GxG}; the sum would be G^2 times this).
     ``rows`` restricts the output to some query cubes (rows are independent).
+    On a padded grid a window with no real token is no key (-inf logit) and
+    its query row is left out (zero entries in the mean).
     """
     d = q.shape[1]
     qr = mean_pool(np.asarray(q, np.float64), grid, pool)
     kr = mean_pool(np.asarray(k, np.float64), grid, pool)
     if bf16_pooled:
         qr, kr = round_bf16(qr), round_bf16(kr)
+    ex = pool_exists(grid, pool)
     g = 64 // (pool[0] * pool[1] * pool[2])
     nb = qr.shape[0] // g
     rows = np.arange(nb) if rows is None else np.asarray(rows)
     out = np.empty((len(rows), nb))
     for n, i in enumerate(rows):
         s = qr[i * g:(i + 1) * g] @ kr.T * _scale(d, scale)       # [G, L/R]
+        s[:, ~ex] = -np.inf
         p_hat = _softmax_rows(s)
+        p_hat[~ex[i * g:(i + 1) * g]] = 0.0
         out[n] = p_hat.reshape(g, nb, g).mean(axis=(0, 2))
     return out
 
 
 def oracle_block_scores(q, k, grid, scale=None):
     """P_oracle (Eq.(10)-(11)): token-level softmax, then the mean over each
-    (B x B) tile.  Output rows are cubes in cube-major order."""
+    (B x B) tile.  Output rows are cubes in cube-major order.  Pad keys are
+    masked and pad query rows left out (zero entries in the mean)."""
     d = q.shape[1]
-    p = _softmax_rows(np.asarray(q, np.float64) @ np.asarray(k, np.float64).T * _scale(d, scale))
+    ok = token_valid(grid)
+    s = np.asarray(q, np.float64) @ np.asarray(k, np.float64).T * _scale(d, scale)
+    s[:, ~ok] = -np.inf
+    p = _softmax_rows(s)
+    p[~ok] = 0.0
     nb = q.shape[0] // 64
     return p.reshape(nb, 64, nb, 64).mean(axis=(1, 3))
 
@@ -197,58 +239,68 @@ def _tokens_of(cubes):
     return (np.asarray(cubes)[:, None] * 64 + np.arange(64)[None, :]).reshape(-1)
 
 
-def fine_forward(q, k, v, mask, scale=None, rows=None):
+def fine_forward(q, k, v, mask, scale=None, rows=None, valid=None):
     """Block-sparse attention of one head (Eq.(12), with the -inf mask of §2.1
     outside the selected (64 x 64) tiles).
 
     Returns O_f [L, d] and the natural-log LSE [L].  A query cube with no
     selected KV cube has O_f = 0 and LSE = -inf (the paper does not treat empty
     rows).  ``rows`` limits the work to some query cubes; other rows are NaN.
+    ``valid`` [L] marks the real tokens of a padded grid: pad keys are masked,
+    pad query rows get O_f = 0 and LSE = -inf.
     """
     q, k, v = (np.asarray(t, np.float64) for t in (q, k, v))
     L, d = q.shape
     nb = L // 64
+    ok = np.ones(L, bool) if valid is None else np.asarray(valid, bool)
     sc = _scale(d, scale)
     o = np.full((L, v.shape[1]), np.nan)
     lse = np.full(L, np.nan)
     for i in (range(nb) if rows is None else rows):
         sl = slice(64 * i, 64 * i + 64)
         cols = np.nonzero(mask[i])[0]
+        o[sl], lse[sl] = 0.0, -np.inf
         if len(cols) == 0:
-            o[sl], lse[sl] = 0.0, -np.inf
             continue
+        qt = _tokens_of([i])
+        qt = qt[ok[qt]]
         toks = _tokens_of(cols)
-        s = q[sl] @ k[toks].T * sc
+        toks = toks[ok[toks]]
+        s = q[qt] @ k[toks].T * sc
         m = s.max(axis=1, keepdims=True)
         e = np.exp(s - m)
         z = e.sum(axis=1, keepdims=True)
-        o[sl] = (e / z) @ v[toks]
-        lse[sl] = (m + np.log(z))[:, 0]
+        o[qt] = (e / z) @ v[toks]
+        lse[qt] = (m + np.log(z))[:, 0]
     return o, lse
 
 
-def fine_backward(q, k, v, mask, d_o, scale=None):
+def fine_backward(q, k, v, mask, d_o, scale=None, valid=None):
     """Gradients of Eq.(12) with the mask held fixed (the router takes no
-    gradient, §2.1-§2.2).  Returns dQ, dK, dV [L, d]."""
+    gradient, §2.1-§2.2).  Returns dQ, dK, dV [L, d]; with ``valid`` (see
+    fine_forward) pad rows take no part and get zero gradients."""
     q, k, v, d_o = (np.asarray(t, np.float64) for t in (q, k, v, d_o))
     L, d = q.shape
     nb = L // 64
+    ok = np.ones(L, bool) if valid is None else np.asarray(valid, bool)
     sc = _scale(d, scale)
     dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
     for i in range(nb):
         cols = np.nonzero(mask[i])[0]
         if len(cols) == 0:
             continue
-        sl = slice(64 * i, 64 * i + 64)
+        qt = _tokens_of([i])
+        qt = qt[ok[qt]]
         toks = _tokens_of(cols)
-        s = q[sl] @ k[toks].T * sc
-        p = _softmax_rows(s)                       # [64, n]
+        toks = toks[ok[toks]]
+        s = q[qt] @ k[toks].T * sc
+        p = _softmax_rows(s)                       # [rows, keys]
         o = p @ v[toks]
-        dp = d_o[sl] @ v[toks].T
-        ds = p * (dp - (d_o[sl] * o).sum(axis=1, keepdims=True))
-        dq[sl] += ds @ k[toks] * sc
-        dk[toks] += ds.T @ q[sl] * sc
-        dv[toks] += p.T @ d_o[sl]
+        dp = d_o[qt] @ v[toks].T
+        ds = p * (dp - (d_o[qt] * o).sum(axis=1, keepdims=True))
+        dq[qt] += ds @ k[toks] * sc
+        dk[toks] += ds.T @ q[qt] * sc
+        dv[toks] += p.T @ d_o[qt]
     return dq, dk, dv
 
 
@@ -272,10 +324,14 @@ def repeat_cubes(oc):
     return np.repeat(np.asarray(oc, np.float64), 64, axis=0)
 
 
-def gate(x, w_g):
+def gate(x, w_g, valid=None):
     """Eq.(13): G = tanh(X W_g), one gate per token and head.
-    x [L, Dm], w_g [Dm, H] -> [L, H]."""
-    return np.tanh(np.asarray(x, np.float64) @ np.asarray(w_g, np.float64))
+    x [L, Dm], w_g [Dm, H] -> [L, H]; rows that ``valid`` marks as padding
+    are 0."""
+    g = np.tanh(np.asarray(x, np.float64) @ np.asarray(w_g, np.float64))
+    if valid is not None:
+        g[~np.asarray(valid, bool)] = 0.0
+    return g
 
 
 def merge(g_h, oc_hat, o_f):
@@ -283,7 +339,7 @@ def merge(g_h, oc_hat, o_f):
     return g_h[:, None] * repeat_cubes(oc_hat) + np.asarray(o_f, np.float64)
 
 
-def gate_backward(x, w_g, oc_hat, d_o, tokens):
+def gate_backward(x, w_g, oc_hat, d_o, tokens, valid=None):
     """Gate part of the backward of Eq.(13)-(14) for some tokens of one batch
     element: with g = tanh(X W_g) and O_c = Repeat(O_hat_c), dL/dg = dO . O_c
     per token and head, dpre = dL/dg (1 - g^2).
@@ -291,6 +347,7 @@ def gate_backward(x, w_g, oc_hat, d_o, tokens):
     x [n, Dm] and d_o [H, n, d] hold the rows of ``tokens`` (cube-tiled
     indices); oc_hat [H, nb, d]; w_g [Dm, H].  Returns (dpre [n, H],
     dx [n, Dm] = dpre W_g^T, this slice's share X^T dpre [Dm, H] of dW_g).
+    ``valid`` [n] marks real tokens; pad rows get dpre = 0.
     """
     x = np.asarray(x, np.float64)
     w_g = np.asarray(w_g, np.float64)
@@ -299,6 +356,8 @@ def gate_backward(x, w_g, oc_hat, d_o, tokens):
     dg = np.stack([(np.asarray(d_o[h], np.float64) * np.asarray(oc_hat[h], np.float64)[cubes]).sum(axis=1)
                    for h in range(w_g.shape[1])], axis=1)
     dpre = dg * (1.0 - g ** 2)
+    if valid is not None:
+        dpre[~np.asarray(valid, bool)] = 0.0
     return dpre, dpre @ w_g.T, x.T @ dpre
 
 
@@ -308,12 +367,14 @@ def coarse_gate_backward(q, k, v, grid, x, w_g, d_o, scale=None):
     q, k, v, d_o: [H, L, d]; x [L, Dm]; w_g [Dm, H].
     Returns (dq_c, dk_c, dv_c [H, nb, d] -- the coarse-branch gradients w.r.t.
     the pooled tensors --, dq, dk, dv [H, L, d] of the coarse branch alone,
-    i.e. the pooled gradients spread back with weight 1/64, dx [L, Dm],
-    dw_g [Dm, H]).  dO_f = dO because Eq.(14) adds O_f with weight one.
+    i.e. the pooled gradients spread back with weight 1/n to the n real tokens
+    of each cube (n = 64 without padding), dx [L, Dm], dw_g [Dm, H]).
+    dO_f = dO because Eq.(14) adds O_f with weight one.
     """
     H, L, d = q.shape
     sc = _scale(d, scale)
-    g = gate(x, w_g)                                    # [L, H]
+    ok = token_valid(grid)
+    g = gate(x, w_g, ok)                                # [L, H]
     dqc, dkc, dvc, ochat = [], [], [], []
     for h in range(H):
         oc_hat, lse_c, (qc, kc, vc) = coarse_forward(q[h], k[h], v[h], grid, scale)
@@ -327,8 +388,9 @@ def coarse_gate_backward(q, k, v, grid, x, w_g, d_o, scale=None):
         dqc.append(ds @ kc * sc)
         dkc.append(ds.T @ qc * sc)
     dqc, dkc, dvc = np.stack(dqc), np.stack(dkc), np.stack(dvc)
-    spread = lambda t: np.repeat(t, 64, axis=1) / 64.0                  # MeanPool^T
-    _, dx, dw = gate_backward(x, w_g, np.stack(ochat), d_o, np.arange(L))
+    n = ok.reshape(-1, 64).sum(axis=1)                                  # real tokens per cube
+    spread = lambda t: np.repeat(t / n[None, :, None], 64, axis=1) * ok[None, :, None]   # MeanPool^T
+    _, dx, dw = gate_backward(x, w_g, np.stack(ochat), d_o, np.arange(L), ok)
     return dqc, dkc, dvc, spread(dqc), spread(dkc), spread(dvc), dx, dw
 
 
@@ -342,7 +404,8 @@ def vsa2_forward(q, k, v, grid, topk, x, w_g, scale=None, bf16_pooled=False, mas
     router and uses a given selection.  Returns a dict of every intermediate.
     """
     H = q.shape[0]
-    g = gate(x, w_g)
+    ok = token_valid(grid)
+    g = gate(x, w_g, ok)
     res = {"scores": [], "mask": [], "o_f": [], "lse": [], "oc_hat": [], "lse_c": [], "o": [], "g": g}
     for h in range(H):
         if mask is None:
@@ -351,7 +414,7 @@ def vsa2_forward(q, k, v, grid, topk, x, w_g, scale=None, bf16_pooled=False, mas
             res["scores"].append(p_r)
         else:
             m = mask[h]
-        o_f, lse = fine_forward(q[h], k[h], v[h], m, scale)
+        o_f, lse = fine_forward(q[h], k[h], v[h], m, scale, valid=ok)
         oc_hat, lse_c, _ = coarse_forward(q[h], k[h], v[h], grid, scale)
         res["mask"].append(m)
         res["o_f"].append(o_f)
@@ -366,9 +429,10 @@ def vsa2_backward(q, k, v, grid, mask, x, w_g, d_o, scale=None):
     """Gradients of the whole layer (router excluded) for one batch element.
     Returns dq, dk, dv [H, L, d], dx [L, Dm], dw_g [Dm, H]."""
     H = q.shape[0]
+    ok = token_valid(grid)
     dq, dk, dv = [], [], []
     for h in range(H):
-        a, b, c = fine_backward(q[h], k[h], v[h], mask[h], d_o[h], scale)
+        a, b, c = fine_backward(q[h], k[h], v[h], mask[h], d_o[h], scale, valid=ok)
         dq.append(a); dk.append(b); dv.append(c)
     _, _, _, cq, ck, cv, dx, dw = coarse_gate_backward(q, k, v, grid, x, w_g, d_o, scale)
     return np.stack(dq) + cq, np.stack(dk) + ck, np.stack(dv) + cv, dx, dw

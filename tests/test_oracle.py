@@ -298,3 +298,202 @@ def test_cost_model_reproduces_printed_sparsities():
         s = orc.sparsity(c["L"], gold["block"], gold["pool"], c["topk"])
         assert round(s, 3) == c["sparsity_3dp"]
         assert round(s, 2) == c["table2"]
+
+
+# ----------------------------------------------------------------------------- padded grids
+# A grid that is not a whole number of 4x4x4 cubes is padded up to one; the
+# brute forces below work on the real tokens alone, in raster order, with each
+# token's cube taken from its coordinates, so they share neither the tiled
+# layout nor the pad masking with the oracle.
+PGRID = (5, 6, 7)            # padded to 8 x 8 x 8: 512 slots, 210 real tokens, nb = 8
+
+
+def _padded(fields, grid, fill=None):
+    """Raster-order rows [n_real, ...] -> tiled padded slots, pad slots = fill
+    (random garbage unless given), using the generator's permutation."""
+    perm = tile_permutation(grid).numpy()
+    real = perm >= 0
+    out = []
+    for f in fields:
+        o = (7.0 + 5.0 * rng.standard_normal((len(perm),) + f.shape[1:])) if fill is None else np.full(
+            (len(perm),) + f.shape[1:], fill)
+        o[real] = f[perm[real]]
+        out.append(o)
+    return out, perm, real
+
+
+def _raster_coords(grid):
+    T, Y, X = grid
+    t, y, x = np.meshgrid(np.arange(T), np.arange(Y), np.arange(X), indexing="ij")
+    return np.stack([t.ravel(), y.ravel(), x.ravel()], axis=1)
+
+
+def _raster_cube_ids(grid):
+    """Cube of every raster-order token, numbered raster over the padded cube grid."""
+    c = _raster_coords(grid) // 4
+    ny, nx = -(-grid[1] // 4), -(-grid[2] // 4)
+    return (c[:, 0] * ny + c[:, 1]) * nx + c[:, 2]
+
+
+def test_padded_layout_marks_the_real_tokens():
+    for grid in [PGRID, (4, 4, 5), (9, 4, 4), (1, 1, 1)]:
+        c = orc.token_coords(grid)
+        Tp, Yp, Xp = orc.padded_grid(grid)
+        assert c.shape[0] == Tp * Yp * Xp and all(n % 4 == 0 for n in (Tp, Yp, Xp))
+        assert all(0 <= p - g < 4 for p, g in zip((Tp, Yp, Xp), grid))
+        ok = orc.token_valid(grid)
+        assert ok.sum() == grid[0] * grid[1] * grid[2]
+        perm = tile_permutation(grid).numpy()
+        assert np.array_equal(ok, perm >= 0)
+        T, Y, X = grid
+        assert np.array_equal(((c[:, 0] * Y + c[:, 1]) * X + c[:, 2])[ok], perm[ok])
+        assert ok.reshape(-1, 64).any(axis=1).all()          # every cube holds a real token
+
+
+@pytest.mark.parametrize("pool", [(2, 2, 2), (4, 4, 4), (1, 1, 1)])
+def test_padded_pooling_brute_force(pool):
+    qn = _rand(210, 5)
+    (q,), perm, real = _padded([qn], PGRID)
+    got = orc.mean_pool(q, PGRID, pool)
+    ex = orc.pool_exists(PGRID, pool)
+    # window of every pooled row from its first member's coordinates
+    first = orc.pool_groups(PGRID, pool)[:, 0]
+    key = orc.token_coords(PGRID)[first] // np.asarray(pool)
+    rkey = _raster_coords(PGRID) // np.asarray(pool)
+    for a in range(got.shape[0]):
+        members = np.all(rkey == key[a], axis=1)
+        assert ex[a] == members.any()
+        want = qn[members].mean(axis=0) if members.any() else np.zeros(5)
+        np.testing.assert_allclose(got[a], want, rtol=1e-13, atol=1e-15)
+
+
+def test_padded_router_r1_brute_force_and_row_sums():
+    qn, kn = _rand(210, 8), _rand(210, 8)
+    (q, k), perm, real = _padded([qn, kn], PGRID)
+    cube = _raster_cube_ids(PGRID)
+    p = torch.softmax(torch.tensor(qn @ kn.T) / np.sqrt(8), -1).numpy()
+    want = np.zeros((8, 8))
+    np.add.at(want, (cube[:, None].repeat(210, 1), cube[None, :].repeat(210, 0)), p)
+    want /= 64.0 * 64.0
+    got = orc.router_scores(q, k, PGRID, pool=(1, 1, 1))
+    np.testing.assert_allclose(got, want, rtol=1e-11, atol=1e-17)
+    # closed form: a query cube's row sums to (its real tokens) / 64^2
+    n = np.bincount(cube, minlength=8)
+    np.testing.assert_allclose(got.sum(axis=1), n / 4096.0, rtol=1e-12)
+    np.testing.assert_allclose(orc.oracle_block_scores(q, k, PGRID, scale=1 / np.sqrt(8)), want, rtol=1e-11,
+                               atol=1e-17)
+
+
+def test_padded_router_subcube_brute_force():
+    qn, kn = _rand(210, 8), _rand(210, 8)
+    (q, k), perm, real = _padded([qn, kn], PGRID)
+    sub = _raster_coords(PGRID) // 2
+    keys, inv = np.unique(sub, axis=0, return_inverse=True)        # existing windows
+    inv = inv.ravel()
+    cnt = np.bincount(inv)
+    qr = np.stack([qn[inv == a].mean(axis=0) for a in range(len(keys))])
+    kr = np.stack([kn[inv == a].mean(axis=0) for a in range(len(keys))])
+    p = torch.softmax(torch.tensor(qr @ kr.T) / np.sqrt(8), -1).numpy()
+    wc = keys // 2                                                  # window -> cube coords
+    wcube = (wc[:, 0] * 2 + wc[:, 1]) * 2 + wc[:, 2]
+    want = np.zeros((8, 8))
+    np.add.at(want, (wcube[:, None].repeat(len(keys), 1), wcube[None, :].repeat(len(keys), 0)), p)
+    want /= 64.0
+    got = orc.router_scores(q, k, PGRID)
+    np.testing.assert_allclose(got, want, rtol=1e-11, atol=1e-17)
+    assert cnt.min() >= 1 and len(keys) < 64 * 8                    # some windows do not exist
+    nq = np.bincount(wcube, minlength=8)                            # existing pooled queries per cube
+    np.testing.assert_allclose(got.sum(axis=1), nq / 64.0, rtol=1e-12)
+
+
+def _padded_token_mask(mask):
+    cube = _raster_cube_ids(PGRID)
+    return mask[cube[:, None], cube[None, :]]
+
+
+def test_padded_fine_forward_brute_force():
+    qn, kn, vn = _rand(210, 8), _rand(210, 8), _rand(210, 6)
+    (q, k, v), perm, real = _padded([qn, kn, vn], PGRID)
+    mask = rng.random((8, 8)) < 0.4
+    mask[3] = False                                                  # an empty row
+    mask[0, 0] = True
+    o, lse = orc.fine_forward(q, k, v, mask, scale=0.3, valid=real)
+    keep = _padded_token_mask(mask)
+    live = keep.any(axis=1)
+    want = _sdpa(qn, kn, vn, keep, 0.3)
+    got_r = o[real][np.argsort(perm[real])]                         # back to raster order
+    lse_r = lse[real][np.argsort(perm[real])]
+    np.testing.assert_allclose(got_r[live], want[live], rtol=1e-12, atol=1e-13)
+    assert np.all(got_r[~live] == 0) and np.all(np.isneginf(lse_r[~live]))
+    s = torch.tensor(qn @ kn.T * 0.3).masked_fill(~torch.tensor(keep), -np.inf)
+    np.testing.assert_allclose(lse_r[live], torch.logsumexp(s, -1).numpy()[live], rtol=1e-12)
+    assert np.all(o[~real] == 0) and np.all(np.isneginf(lse[~real]))
+    full, _ = orc.fine_forward(q, k, v, np.ones((8, 8), bool), scale=0.3, valid=real)
+    np.testing.assert_allclose(full[real][np.argsort(perm[real])], _sdpa(qn, kn, vn, None, 0.3), rtol=1e-12,
+                               atol=1e-13)
+
+
+def test_padded_fine_backward_autograd():
+    qn, kn, vn, don = (_rand(210, 8) for _ in range(4))
+    (q, k, v, d_o), perm, real = _padded([qn, kn, vn, don], PGRID)
+    mask = rng.random((8, 8)) < 0.5
+    mask[5] = False
+    mask[1, 7] = True
+    got = orc.fine_backward(q, k, v, mask, d_o, scale=0.3, valid=real)
+    t = [torch.tensor(a, requires_grad=True) for a in (qn, kn, vn)]
+    keep = torch.tensor(_padded_token_mask(mask))
+    s = (t[0] @ t[1].T * 0.3).masked_fill(~keep, -np.inf)
+    pr = torch.softmax(s, -1).nan_to_num(0.0)
+    (pr @ t[2] * torch.tensor(don)).sum().backward()
+    order = np.argsort(perm[real])
+    for g, w in zip(got, t):
+        np.testing.assert_allclose(g[real][order], w.grad.numpy(), rtol=1e-10, atol=1e-12)
+        assert np.all(g[~real] == 0)
+
+
+def test_padded_coarse_gate_autograd():
+    H, d, dm = 2, 6, 10
+    fields = [_rand(210, H * d) for _ in range(4)] + [_rand(210, dm)]
+    (q, k, v, d_o, x), perm, real = _padded(fields, PGRID)
+    split = lambda a: a.reshape(-1, H, d).transpose(1, 0, 2).copy()
+    q, k, v, d_o = (split(a) for a in (q, k, v, d_o))
+    w_g = _rand(dm, H) * 0.4
+    got = orc.coarse_gate_backward(q, k, v, PGRID, x, w_g, d_o)
+    # natural order: cube means over the real tokens, dense attention over the
+    # cubes, gated broadcast, loss sum(O * dO) over real tokens
+    cube = torch.tensor(_raster_cube_ids(PGRID))
+    n = torch.bincount(cube, minlength=8).double()
+    tq, tk, tv = (torch.tensor(split(f), requires_grad=True) for f in fields[:3])
+    tx, tw = torch.tensor(fields[4], requires_grad=True), torch.tensor(w_g, requires_grad=True)
+    mean = lambda t: torch.zeros(H, 8, d, dtype=torch.float64).index_add(1, cube, t) / n[None, :, None]
+    oc = torch.softmax(mean(tq) @ mean(tk).transpose(1, 2) / np.sqrt(d), -1) @ mean(tv)
+    g = torch.tanh(tx @ tw)                                         # [210, H]
+    o = g.T[:, :, None] * oc[:, cube]
+    (o * torch.tensor(split(fields[3]))).sum().backward()
+    order = np.argsort(perm[real])
+    for g_, w_ in zip(got[3:6], (tq, tk, tv)):
+        np.testing.assert_allclose(g_[:, real][:, order], w_.grad.numpy(), rtol=1e-10, atol=1e-12)
+        assert np.all(g_[:, ~real] == 0)
+    np.testing.assert_allclose(got[6][real][order], tx.grad.numpy(), rtol=1e-10, atol=1e-12)
+    assert np.all(got[6][~real] == 0)
+    np.testing.assert_allclose(got[7], tw.grad.numpy(), rtol=1e-10, atol=1e-12)
+    # forward: gate rows and merged output are zero on pad slots
+    res = orc.vsa2_forward(q, k, v, PGRID, 8, x, w_g)
+    assert np.all(res["g"][~real] == 0) and np.all(res["o"][:, ~real] == 0)
+    np.testing.assert_allclose(res["oc_hat"], oc.detach().numpy(), rtol=1e-12)
+
+
+def test_pad_values_never_reach_an_output():
+    H, d, dm = 2, 8, 12
+    fields = [_rand(210, H * d) for _ in range(4)] + [_rand(210, dm)]
+    split = lambda a: a.reshape(-1, H, d).transpose(1, 0, 2).copy()
+    w_g = _rand(dm, H) * 0.4
+    outs = []
+    for _ in range(2):                                               # two different pad fills
+        (q, k, v, d_o, x), perm, real = _padded(fields, PGRID)
+        q, k, v, d_o = (split(a) for a in (q, k, v, d_o))
+        f = orc.vsa2_forward(q, k, v, PGRID, 3, x, w_g)
+        b = orc.vsa2_backward(q, k, v, PGRID, f["mask"], x, w_g, d_o)
+        outs.append([f["scores"], f["mask"], f["o_f"], f["lse"], f["o"], f["g"], *b])
+    for a, b in zip(*outs):
+        assert np.array_equal(a, b)

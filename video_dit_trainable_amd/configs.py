@@ -1,8 +1,9 @@
 """Workload registry: the five video-shaped VSA2 problems.
 
-Grids are (T, Y, X) latent cells; tokens L = T*Y*X are stored in cube-tiled
-order (4x4x4 cubes of 64 tokens, each made of eight 2x2x2 sub-cubes of 8
-tokens).  ``topk`` is the average number of KV cubes per query cube, so the
+Grids are (T, Y, X) latent cells; tokens are stored in cube-tiled order (4x4x4
+cubes of 64 tokens, each made of eight 2x2x2 sub-cubes of 8 tokens).  A grid
+whose sides are not multiples of 4 is padded up to whole cubes; L counts the
+slots of the padded grid.  ``topk`` is the average number of KV cubes per query cube, so the
 per-head budget is nb * topk selected (query cube, KV cube) pairs
 (paper "Improving Video Sparse Attention with Fine-grained Router and Sparse
 Rebasing", §2.2 Eq.(8)-(9)).
@@ -32,7 +33,24 @@ class Workload:
     extra_topk: tuple = field(default_factory=tuple)
 
     @property
+    def pgrid(self):
+        """The grid padded up to whole 4x4x4 cubes along each axis (§2.2
+        "Kernel Implementation"); equal to ``grid`` when it divides."""
+        return tuple(-(-n // 4) * 4 for n in self.grid)
+
+    @property
+    def padded(self):
+        return self.pgrid != tuple(self.grid)
+
+    @property
     def L(self):
+        """Token slots per (batch, head): the padded grid's size."""
+        t, y, x = self.pgrid
+        return t * y * x
+
+    @property
+    def L_real(self):
+        """Real tokens per (batch, head) (pad slots excluded)."""
         t, y, x = self.grid
         return t * y * x
 
@@ -57,6 +75,9 @@ WORKLOADS = {
         Workload("train480", 3, (28, 32, 52), 1, 20, 128, "bf16", 64, "lowrank", train=True),
         Workload("infer720", 4, (44, 48, 104), 1, 20, 128, "bf16", 64, "lowrank", extra_topk=(128,)),
         Workload("train720", 5, (44, 48, 104), 1, 20, 128, "bf16", 64, "lowrank", skew=True, train=True),
+        # the 720p training problem on a grid one short of whole cubes along
+        # every axis: padded to the same 44 x 48 x 104 slots (3.5% pad slots)
+        Workload("train720pad", 6, (43, 47, 103), 1, 20, 128, "bf16", 64, "lowrank", skew=True, train=True),
     ]
 }
 

@@ -10,7 +10,11 @@ Token order.  The attention layer takes tokens in cube-tiled order (paper
 Rebasing", §2.2 "Permutation"): cube-major over the (T/4, Y/4, X/4) cube grid,
 then the eight 2x2x2 sub-cubes of a cube in raster order, then the eight tokens
 of a sub-cube in raster order.  Tensors are generated in raster (t, y, x) order
-and permuted with :func:`tile_permutation`.
+and permuted with :func:`tile_permutation`.  A grid that is not a whole number
+of cubes is padded up to one (§2.2 "Kernel Implementation"); the pad slots of
+Q, K and V are filled with seeded finite values of a different distribution
+(3 + 4 N(0,1)), and those of dO and X are drawn like their real rows, so that
+any pad value reaching an output shows.
 
 Recipes (one torch generator per (workload, batch, tensor, head)):
 
@@ -33,7 +37,7 @@ import torch
 from .configs import CUBE, Workload
 
 # tensor ids used in the seeds
-T_Q, T_K, T_V, T_DO, T_X, T_WG, T_SQK, T_SV, T_SKEW, T_SEL = range(10)
+T_Q, T_K, T_V, T_DO, T_X, T_WG, T_SQK, T_SV, T_SKEW, T_SEL, T_PAD = range(11)
 
 
 def seed_of(w: Workload, tensor: int, head: int = 0, batch: int = 0) -> int:
@@ -47,20 +51,30 @@ def _gen(seed: int, device) -> torch.Generator:
 
 
 def tile_permutation(grid, device="cpu") -> torch.Tensor:
-    """perm[j] = raster index (t*Y + y)*X + x of the token stored at tiled slot j."""
+    """perm[j] = raster index (t*Y + y)*X + x of the token stored at tiled slot
+    j of the grid padded up to whole cubes, or -1 where slot j is padding."""
     T, Y, X = grid
-    if T % 4 or Y % 4 or X % 4:
-        raise ValueError(f"grid {grid} is not a multiple of the 4x4x4 cube")
-    L = T * Y * X
+    Tp, Yp, Xp = (-(-n // 4) * 4 for n in grid)
+    L = Tp * Yp * Xp
     j = torch.arange(L, device=device, dtype=torch.int64)
     c, s, u = j // 64, (j // 8) % 8, j % 8
-    cx = c % (X // 4)
-    cy = (c // (X // 4)) % (Y // 4)
-    ct = c // ((X // 4) * (Y // 4))
+    cx = c % (Xp // 4)
+    cy = (c // (Xp // 4)) % (Yp // 4)
+    ct = c // ((Xp // 4) * (Yp // 4))
     t = 4 * ct + 2 * (s // 4) + u // 4
     y = 4 * cy + 2 * ((s // 2) % 2) + (u // 2) % 2
     x = 4 * cx + 2 * (s % 2) + u % 2
-    return (t * Y + y) * X + x
+    real = (t < T) & (y < Y) & (x < X)
+    return torch.where(real, (t * Y + y) * X + x, torch.full_like(j, -1))
+
+
+def _to_tiled(x_raster, perm, fill):
+    """Raster-order rows [L_real, d] into tiled slots [L, d]; pad slots take
+    the rows of ``fill``."""
+    real = perm >= 0
+    out = fill.clone()
+    out[real] = x_raster[perm[real]]
+    return out
 
 
 def _smooth_noise(grid, nfield, sigma, gen, device):
@@ -118,10 +132,17 @@ def make_qkv(w: Workload, device="cpu", heads=None):
         for hi, h in enumerate(heads):
             s_qk = _structure(w, T_SQK, h, b, device)
             s_v = _structure(w, T_SV, h, b, device)
-            for name, tid, s in (("q", T_Q, s_qk), ("k", T_K, s_qk), ("v", T_V, s_v)):
+            for ti, (name, tid, s) in enumerate((("q", T_Q, s_qk), ("k", T_K, s_qk), ("v", T_V, s_v))):
                 g = _gen(seed_of(w, tid, h, b), device)
-                x = torch.randn((L, d), generator=g, device=device) + w.alpha * s
-                x = x[perm]
+                x = torch.randn((w.L_real, d), generator=g, device=device) + w.alpha * s
+                if w.padded:
+                    # pad slots hold finite garbage (offset, 4x the spread) that
+                    # must not reach any output
+                    gp = _gen(seed_of(w, T_PAD, 3 * h + ti, b), device)
+                    fill = 3.0 + 4.0 * torch.randn((L, d), generator=gp, device=device)
+                    x = _to_tiled(x, perm, fill)
+                else:
+                    x = x[perm]
                 if name == "q" and w.skew:
                     gs = _gen(seed_of(w, T_SKEW, h, b), device)
                     xi = torch.randn((w.nb,), generator=gs, device=device)
