@@ -19,6 +19,15 @@
  *    raster order.  Router pooling windows are therefore the contiguous groups
  *    of 8 tokens and the attention blocks the contiguous groups of 64.
  *  - Block size B = 64 (4x4x4) and router pool R = 8 (2x2x2), so G = 8.
+ *  - Padded grids (§2.2 "Kernel Implementation"): a latent side that is not a
+ *    multiple of 4 is padded up to one, and every tensor holds the padded
+ *    grid: L = 64 nb with nb = ceil(T/4) ceil(Y/4) ceil(X/4), in the order
+ *    above.  Pad slots are not tokens.  Their input values are never read into
+ *    a result (they must be finite); pad rows of O_f, O, G, dQ, dK, dV and dX
+ *    are written as 0 and their LSE as -inf.  Pooling windows average their
+ *    real tokens; a 2x2x2 window holding none is no router key and adds no
+ *    router row; the coarse gradient of a cube goes to its n real tokens as
+ *    1/n each (1/64 without padding).
  *  - `stream` is a hipStream_t (NULL = the default stream).  Every call only
  *    enqueues work on it and returns without synchronising.
  *  - Errors: argument and shape errors are reported before anything is
@@ -40,7 +49,7 @@ extern "C" {
 enum vsa2_status {
   VSA2_OK = 0,
   VSA2_E_ARG = 1,         /* NULL pointer, misaligned pointer, bad scalar argument   */
-  VSA2_E_SHAPE = 2,       /* grid not a multiple of 4, head_dim not 64/128, sizes    */
+  VSA2_E_SHAPE = 2,       /* empty or oversized grid, head_dim not 64/128            */
   VSA2_E_WORKSPACE = 3,   /* workspace smaller than vsa2_workspace_size() reports     */
   VSA2_E_HIP = 4,         /* a HIP call or kernel launch failed                       */
   VSA2_E_UNSUPPORTED = 5  /* valid request the library does not implement             */
@@ -64,7 +73,7 @@ typedef struct vsa2_problem {
   int32_t batch;          /* >= 1                                                     */
   int32_t heads;          /* >= 1 (multi-head attention: as many K/V heads as Q heads)*/
   int32_t head_dim;       /* d: 64 or 128                                             */
-  int32_t lat_t, lat_y, lat_x; /* latent grid; L = lat_t*lat_y*lat_x; each a multiple of 4 */
+  int32_t lat_t, lat_y, lat_x; /* latent grid, each >= 1; padded up to multiples of 4 */
   int32_t dtype;          /* vsa2_dtype of Q, K, V, O_f, O, dO, dQ, dK, dV, X, dX     */
   float softmax_scale;    /* <= 0 selects 1/sqrt(head_dim)                            */
 } vsa2_problem;
@@ -84,7 +93,8 @@ int vsa2_pooled_size(const vsa2_problem* p, size_t* bytes);
 int vsa2_saved_size(const vsa2_problem* p, size_t* bytes);
 
 /* Per-sequence budget k = min(nb * topk, nb^2) selected pairs per (batch, head),
- * nb = L / 64 (paper §2.2 Eq.(9): N*K blocks per sequence). */
+ * nb = L / 64 cubes of the padded grid (paper §2.2 Eq.(9): N*K blocks per
+ * sequence). */
 int vsa2_budget(const vsa2_problem* p, int32_t topk, int64_t* k);
 
 /* Mean pooling of the router (Eq.(5), windows of 8 tokens) and of the coarse
@@ -102,7 +112,8 @@ int vsa2_pool(const vsa2_problem* p, const void* q, const void* k, const void* v
  *   pooled: from vsa2_pool.
  *   scores (written): fp32 [batch, heads, nb, nb], P_r[i][j] = mean over the
  *     8 x 8 pooled (query, key) pairs of cubes i, j of softmax_b(q_a.k_b*scale).
- *     Every row sums to 1/8.
+ *     Every row sums to 1/8 (padded grids: to the number of the cube's 2x2x2
+ *     windows that hold a real token, over 64).
  *   ws: vsa2_workspace_size(VSA2_OP_ROUTE). */
 int vsa2_route(const vsa2_problem* p, const void* pooled, float* scores,
                void* ws, size_t ws_bytes, void* stream);

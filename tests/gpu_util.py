@@ -92,3 +92,14 @@ def empty_rows(mask, rows):
                 moved -= 1
     assert moved == 0
     return m
+
+
+def coarse_lse_bound(qc, kc, scale):
+    """Per-row bound on |lse_c(GPU) - lse_c(oracle)| when the pooled coarse
+    operands Q_c, K_c are stored in bf16 (each element rounded, relative error
+    <= 2^-9) and the oracle keeps them exact.  A logit scale * q . k then moves
+    by at most scale * sum_d |q_d k_d| * (2 * 2^-9 + 2^-18), and a log-sum-exp
+    moves by at most the largest change of its logits.  1e-4 covers the fp32
+    accumulation."""
+    a = np.abs(np.asarray(qc)) @ np.abs(np.asarray(kc)).T * scale
+    return a.max(axis=1) * (2.0 ** -8 + 2.0 ** -18) + 1e-4

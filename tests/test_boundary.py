@@ -64,10 +64,25 @@ def test_sizes_and_budget():
     assert vsa2.workspace_size(p, vsa2.OP_COARSE_BWD, 8, 128) > 0
 
 
+def test_padded_grid_sizes():
+    # a grid that is not a whole number of cubes is padded up to one: 7x13x14
+    # takes the slots of 8x16x16 (nb = 32), and every size follows the padded grid
+    p, q = _prob(grid=(7, 13, 14)), _prob()
+    assert vsa2.budget(p, 8) == vsa2.budget(q, 8) == 32 * 8
+    assert vsa2.pooled_size(p) == vsa2.pooled_size(q)
+    assert vsa2.saved_size(p) == vsa2.saved_size(q)
+    # the router also keeps one existence word per 64 pooled keys
+    assert vsa2.workspace_size(p, vsa2.OP_ROUTE) == vsa2.workspace_size(q, vsa2.OP_ROUTE) + 256
+    for op in (vsa2.OP_TOPK, vsa2.OP_PLAN, vsa2.OP_FWD, vsa2.OP_BWD):
+        assert vsa2.workspace_size(p, op) == vsa2.workspace_size(q, op)
+    assert vsa2.budget(_prob(grid=(1, 1, 1)), 3) == 1        # one cube holding a single token
+
+
 @pytest.mark.parametrize("kw,code", [
     (dict(head_dim=96), vsa2.VSA2_E_SHAPE),
-    (dict(grid=(6, 16, 16)), vsa2.VSA2_E_SHAPE),
     (dict(grid=(8, 16, 0)), vsa2.VSA2_E_SHAPE),
+    (dict(grid=(-4, 16, 16)), vsa2.VSA2_E_SHAPE),
+    (dict(grid=(400, 400, 400)), vsa2.VSA2_E_SHAPE),       # nb beyond the int32 index range
     (dict(batch=0), vsa2.VSA2_E_SHAPE),
 ])
 def test_bad_problem_rejected(kw, code):

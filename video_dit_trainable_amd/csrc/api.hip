@@ -20,17 +20,20 @@ struct Dims {
   bool bf16;
   size_t esz;
   float scale;
+  PadGrid pad;
 };
 
 int check_problem(const vsa2_problem* p, Dims& o) {
   if (!p) return VSA2_E_ARG;
   if (p->batch < 1 || p->heads < 1) return VSA2_E_SHAPE;
   if (p->head_dim != 64 && p->head_dim != 128) return VSA2_E_SHAPE;
-  if (p->lat_t < 4 || p->lat_y < 4 || p->lat_x < 4) return VSA2_E_SHAPE;
-  if (p->lat_t % 4 || p->lat_y % 4 || p->lat_x % 4) return VSA2_E_SHAPE;
+  if (p->lat_t < 1 || p->lat_y < 1 || p->lat_x < 1) return VSA2_E_SHAPE;
+  if (p->lat_t > (1 << 20) || p->lat_y > (1 << 20) || p->lat_x > (1 << 20)) return VSA2_E_SHAPE;
   if (p->dtype != VSA2_F32 && p->dtype != VSA2_BF16) return VSA2_E_ARG;
-  const int64_t L = (int64_t)p->lat_t * p->lat_y * p->lat_x;
-  const int64_t nb = L / 64;
+  // a grid that is not a whole number of 4x4x4 cubes is padded up to one
+  const int64_t nt = (p->lat_t + 3) / 4, ny = (p->lat_y + 3) / 4, nx = (p->lat_x + 3) / 4;
+  const int64_t nb = nt * ny * nx;
+  const int64_t L = 64 * nb;
   if (nb > 46340) return VSA2_E_SHAPE;  // nb^2 and all indices fit int32
   if ((int64_t)p->batch * p->heads > (1 << 20)) return VSA2_E_SHAPE;
   if (std::isnan(p->softmax_scale) || std::isinf(p->softmax_scale)) return VSA2_E_ARG;
@@ -45,6 +48,15 @@ int check_problem(const vsa2_problem* p, Dims& o) {
   o.bf16 = p->dtype == VSA2_BF16;
   o.esz = o.bf16 ? 2 : 4;
   o.scale = p->softmax_scale > 0.f ? p->softmax_scale : 1.0f / std::sqrt((float)p->head_dim);
+  o.pad.on = (p->lat_t % 4) || (p->lat_y % 4) || (p->lat_x % 4);
+  o.pad.nt = (int)nt;
+  o.pad.ny = (int)ny;
+  o.pad.nx = (int)nx;
+  o.pad.et = p->lat_t - 4 * (int)(nt - 1);
+  o.pad.ey = p->lat_y - 4 * (int)(ny - 1);
+  o.pad.ex = p->lat_x - 4 * (int)(nx - 1);
+  o.pad.inv_nx = (float)(1.0 / (double)nx);
+  o.pad.inv_nyx = (float)(1.0 / (double)(ny * nx));
   return VSA2_OK;
 }
 
@@ -59,7 +71,11 @@ int64_t budget(const Dims& d, int32_t topk) {
 int bitmap_words(const Dims& d) { return 2 * ((d.nb + 63) / 64); }
 
 // Workspace layouts --------------------------------------------------------
-size_t ws_route(const Dims& d) { return up((size_t)d.bh * d.Lr * 4); }
+// per-row LSE, then (padded grids) one existence word per 64 pooled keys
+size_t ws_route_lse(const Dims& d) { return up((size_t)d.bh * d.Lr * 4); }
+size_t ws_route(const Dims& d) {
+  return ws_route_lse(d) + (d.pad.on ? up((size_t)(d.Lr + 63) / 64 * 8) : 0);
+}
 
 size_t ws_topk(const Dims& d, TopkWs* w, void* base) {
   size_t off = 0;
@@ -230,7 +246,7 @@ const char* vsa2_status_string(int s) {
   switch (s) {
     case VSA2_OK: return "ok";
     case VSA2_E_ARG: return "invalid argument (NULL/misaligned pointer or bad scalar)";
-    case VSA2_E_SHAPE: return "unsupported shape (grid must be multiples of 4, head_dim 64 or 128)";
+    case VSA2_E_SHAPE: return "unsupported shape (empty or oversized grid, head_dim not 64 or 128)";
     case VSA2_E_WORKSPACE: return "workspace too small";
     case VSA2_E_HIP: return "HIP launch failed";
     case VSA2_E_UNSUPPORTED: return "unsupported request";
@@ -298,7 +314,7 @@ int vsa2_pool(const vsa2_problem* p, const void* q, const void* k, const void* v
   if (!aligned(q) || !aligned(k) || !aligned(v) || !aligned(pooled)) return VSA2_E_ARG;
   Pooled pp = pooled_ptrs(d, pooled);
   PoolArgs a{q, k, v, (void*)pp.qr, (void*)pp.kr, (void*)pp.qc, (void*)pp.kc, (void*)pp.vc, d.bh, d.nb, d.nbp, d.d,
-             d.bf16};
+             d.bf16, d.pad};
   return hip_status(launch_pool(a, (hipStream_t)stream));
 }
 
@@ -309,7 +325,8 @@ int vsa2_route(const vsa2_problem* p, const void* pooled, float* scores, void* w
   if (!aligned(pooled) || !aligned(scores)) return VSA2_E_ARG;
   if ((s = check_ws(ws, ws_bytes, ws_route(d)))) return s;
   Pooled pp = pooled_ptrs(d, pooled);
-  RouteArgs a{pp.qr, pp.kr, (float*)ws, scores, d.bh, d.nb, d.d, d.bf16, d.scale * 1.4426950408889634f};
+  RouteArgs a{pp.qr, pp.kr, (float*)ws, scores, d.bh, d.nb, d.d, d.bf16, d.scale * 1.4426950408889634f, d.pad,
+              d.pad.on ? (uint64_t*)((char*)ws + ws_route_lse(d)) : nullptr};
   return hip_status(launch_route(a, (hipStream_t)stream));
 }
 
@@ -374,7 +391,8 @@ int vsa2_sparse_attn_fwd(const vsa2_problem* p, int32_t topk, const void* q, con
   a.kph = budget(d, topk);
   a.d = d.d; a.bf16 = d.bf16; a.dense = false;
   a.scale_log2 = d.scale * 1.4426950408889634f;
-  a.ct = p->lat_t / 4; a.cy = p->lat_y / 4; a.cx = p->lat_x / 4;
+  a.ct = d.pad.nt; a.cy = d.pad.ny; a.cx = d.pad.nx;
+  a.pad = d.pad;
   return hip_status(launch_attn_fwd(a, (hipStream_t)stream));
 }
 
@@ -408,7 +426,8 @@ int vsa2_sparse_attn_bwd(const vsa2_problem* p, int32_t topk, const void* q, con
   a.d = d.d; a.bf16 = d.bf16; a.dense = false;
   a.scale = d.scale;
   a.scale_log2 = d.scale * 1.4426950408889634f;
-  a.ct = p->lat_t / 4; a.cy = p->lat_y / 4; a.cx = p->lat_x / 4;
+  a.ct = d.pad.nt; a.cy = d.pad.ny; a.cx = d.pad.nx;
+  a.pad = d.pad;
   return hip_status(launch_attn_bwd(a, st));
 }
 
@@ -435,7 +454,7 @@ int vsa2_coarse_gate(const vsa2_problem* p, const void* pooled, const void* x, i
   a.scale_log2 = d.scale * 1.4426950408889634f;
   hipError_t e = launch_attn_fwd(a, st);
   if (e != hipSuccess) return VSA2_E_HIP;
-  GateArgs ga{x, w_g, ws, oc_hat, o_f, o, g, d.batch, d.heads, d.nb, d.d, d_model, d.bf16};
+  GateArgs ga{x, w_g, ws, oc_hat, o_f, o, g, d.batch, d.heads, d.nb, d.d, d_model, d.bf16, d.pad};
   return hip_status(launch_gate_fwd(ga, st));
 }
 
@@ -458,7 +477,7 @@ int vsa2_coarse_gate_bwd(const vsa2_problem* p, const void* pooled, const void* 
   const float* lse_c = oc_hat + (size_t)d.bh * d.nb * d.d;
   const float* g = lse_c + (size_t)d.bh * d.nb;
   GateBwdArgs ga{x, w_g, w.wt, oc_hat, g, d_o, w.dpre, w.doc, lse_c, w.stats_c, w.dw_part, dx, dw_g,
-                 d.batch, d.heads, d.nb, d.nbp, d.d, d_model, nchunk_of(d), d.bf16};
+                 d.batch, d.heads, d.nb, d.nbp, d.d, d_model, nchunk_of(d), d.bf16, d.pad};
   hipError_t e = launch_gate_bwd(ga, st);
   if (e != hipSuccess) return VSA2_E_HIP;
   AttnBwdArgs a{};

@@ -16,7 +16,10 @@
 // computed by the dQ kernel, which holds every query row's dO anyway; it runs
 // first and the dK/dV kernel reads them.  Per-cube gradient rows
 // (the coarse branch's dQ_c, dK_c, dV_c) are added as row/64 to every token of
-// the cube before the single rounding to the storage type.
+// the cube before the single rounding to the storage type.  On a padded grid
+// (§2.2 "Kernel Implementation") pad tokens take no part: as keys they are
+// masked, as queries their row statistics make P = 0, their gradient rows are
+// zero, and the per-cube rows go as row/n to the n real tokens.
 #include <cmath>
 
 #include "common.h"
@@ -125,7 +128,9 @@ __device__ __forceinline__ void dkdv_pair(const T* qs, const T* dos, const float
 // the other of two stages while the current pair is computed; the stages are
 // distinct arrays and the loop is unrolled by two, so the compiler can tell
 // the copy into one stage from the reads of the other.
-template <typename T, typename TO, int D, bool DENSE>
+// PAD (fine branch on a padded grid): the cube's pad keys get P = 0, so their
+// dK, dV rows are zero; pad query rows arrive with lse2 = +inf (P = 0).
+template <typename T, typename TO, int D, bool DENSE, bool PAD>
 __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(const T* __restrict__ q, const T* __restrict__ k,
                                                      const T* __restrict__ v, const T* __restrict__ d_o,
                                                      const float* __restrict__ stats,
@@ -134,7 +139,8 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(const T* __restrict__ q, co
                                                      const float* __restrict__ dk_add,
                                                      const float* __restrict__ dv_add, TO* __restrict__ dk,
                                                      TO* __restrict__ dv, int nq, int nkv, int seq, int ld,
-                                                     int out_rows, int64_t kph, float scale, float c) {
+                                                     int out_rows, int64_t kph, float scale, float c, PadGrid pad) {
+  static_assert(!(DENSE && PAD), "padding applies to the fine branch");
   constexpr int TILE = 64 * D;
   __shared__ __align__(16) T tA[2 * TILE];  // stage A: Q tile | dO tile
   __shared__ __align__(16) T tB[2 * TILE];  // stage B
@@ -187,10 +193,12 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(const T* __restrict__ q, co
 
   Frag<T> kf[2][D / 32], vf[2][D / 32];
   bool kv_ok[2];
+  uint64_t km = ~0ull;  // PAD: real slots of cube j
+  if constexpr (PAD) km = cube_slots(j, pad);
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
     const int key = j * 64 + 32 * kh + 16 * kb + cc;
-    kv_ok[kb] = !DENSE || key < seq;
+    kv_ok[kb] = PAD ? (bool)((km >> (32 * kh + 16 * kb + cc)) & 1) : (!DENSE || key < seq);
 #pragma unroll
     for (int s = 0; s < D / 32; ++s) {
       kf[kb][s] = frag_global<T, D>(k + hoff, key, s, g);
@@ -267,10 +275,17 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(const T* __restrict__ q, co
         dka[db][kb][r] = (dka[db][kb][r] + mine[o]) * scale;
         dva[db][kb][r] += mine[PART + o];
       }
-  // the coarse branch's per-cube gradient rows, 1/64 to every token of the cube
+  // the coarse branch's per-cube gradient rows, 1/n to each of the cube's n
+  // real tokens (n = 64 unless the grid is padded)
   if (dk_add) {
     const float* ka = dk_add + ((size_t)bh * nkv + j) * D;
     const float* va = dv_add + ((size_t)bh * nkv + j) * D;
+    float wk[2] = {1.0f / 64.0f, 1.0f / 64.0f};
+    if constexpr (PAD) {
+      const float inv_n = 1.0f / (float)__popcll(km);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) wk[kb] = kv_ok[kb] ? inv_n : 0.f;
+    }
 #pragma unroll
     for (int db = 0; db < D / 16; ++db) {
       const f32x4 a4 = *reinterpret_cast<const f32x4*>(ka + 16 * db + 4 * g);
@@ -279,8 +294,8 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(const T* __restrict__ q, co
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          dka[db][kb][r] += a4[r] * (1.0f / 64.0f);
-          dva[db][kb][r] += b4[r] * (1.0f / 64.0f);
+          dka[db][kb][r] += a4[r] * wk[kb];
+          dva[db][kb][r] += b4[r] * wk[kb];
         }
     }
   }
@@ -308,9 +323,10 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(const T* __restrict__ q, co
 // One (query cube, KV cube) pair of the dQ kernel for one wave: queries 32qh..
 // (Q, dO fragments qf, of in registers, row statistics l2 and ndl = -delta,
 // the starting value of the dP^T accumulators) against keys
-// 32kh.. of the K / V tiles ks, vs in LDS; keys at or beyond lim are masked.
-template <typename T, int D>
-__device__ __forceinline__ void dq_pair(const T* ks, const T* vs, int brow, int btr, int lim,
+// 32kh.. of the K / V tiles ks, vs in LDS; keys at or beyond lim are masked
+// (PAD: keys whose bit in km is clear).
+template <typename T, int D, bool PAD>
+__device__ __forceinline__ void dq_pair(const T* ks, const T* vs, int brow, int btr, int lim, uint64_t km,
                                         const Frag<T> (&qf)[2][D / 32], const Frag<T> (&of)[2][D / 32],
                                         const float (&l2)[2], const float (&ndl)[2], f32x4 (&dqa)[D / 16][2], int kh,
                                         int g, int cc, float c) {
@@ -342,7 +358,8 @@ __device__ __forceinline__ void dq_pair(const T* ks, const T* vs, int brow, int 
     // dS^T = P^T (dP^T - delta) straight into the low (kb = 0) / high (kb = 1) half of the B fragments
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const bool kin = 32 * kh + 16 * kb + 4 * g + r < lim;
+      const int key = 32 * kh + 16 * kb + 4 * g + r;
+      const bool kin = PAD ? (bool)((km >> key) & 1) : key < lim;
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
         const float pe = kin ? fast_exp2(fmaf(p[qb][r], c, -l2[qb])) : 0.f;
@@ -364,7 +381,9 @@ __device__ __forceinline__ void dq_pair(const T* ks, const T* vs, int brow, int 
 // key halves are summed through LDS at the end.  K / V tiles of the next pair
 // are copied LDS-direct into the other stage while the current pair runs
 // (distinct stage arrays, loop unrolled by two, as in the dK/dV kernel).
-template <typename T, typename TO, int D, bool DENSE, bool STATS>
+// PAD (fine branch on a padded grid): pad keys are masked; pad query rows get
+// the statistics (+inf, 0), so their P is 0 here and in the dK/dV kernel.
+template <typename T, typename TO, int D, bool DENSE, bool STATS, bool PAD>
 __global__ __launch_bounds__(256, 2) void k_bwd_dq(const T* __restrict__ q, const T* __restrict__ k,
                                                    const T* __restrict__ v, const T* __restrict__ d_o,
                                                    const T* __restrict__ o, const float* __restrict__ lse,
@@ -373,7 +392,8 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(const T* __restrict__ q, cons
                                                    const int32_t* __restrict__ col_idx,
                                                    const float* __restrict__ dq_add, TO* __restrict__ dq, int nq,
                                                    int nkv, int seq, int ld, int out_rows, int64_t kph, float scale,
-                                                   float c, int ct, int cy, int cx) {
+                                                   float c, int ct, int cy, int cx, PadGrid pad) {
+  static_assert(!PAD || (STATS && !DENSE), "padding applies to the fine branch");
   constexpr int TILE = 64 * D;
   __shared__ __align__(16) T tA[2 * TILE];  // stage A: K tile | V tile
   __shared__ __align__(16) T tB[2 * TILE];  // stage B
@@ -422,9 +442,13 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(const T* __restrict__ q, cons
   // this wave's 32 queries: Q and dO rows as B fragments (column = query 32qh + 16qb + cc)
   Frag<T> qf[2][D / 32], of[2][D / 32];
   float l2[2], ndl[2];
+  uint64_t qm = ~0ull;  // PAD: real slots of query cube i
+  if constexpr (PAD) qm = cube_slots(i, pad);
+  bool qreal[2];
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     const int qrow = i * 64 + 32 * qh + 16 * qb + cc;
+    qreal[qb] = !PAD || ((qm >> (32 * qh + 16 * qb + cc)) & 1);
 #pragma unroll
     for (int s = 0; s < D / 32; ++s) {
       qf[qb][s] = frag_global<T, D>(q + hoff, qrow, s, g);
@@ -442,8 +466,8 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(const T* __restrict__ q, cons
       part += __shfl_xor(part, 16);
       part += __shfl_xor(part, 32);
       const float l = lse[(size_t)bh * ld + qrow];
-      l2[qb] = l == -INFINITY ? INFINITY : l * LOG2E;
-      ndl[qb] = -part;
+      l2[qb] = (l == -INFINITY || !qreal[qb]) ? INFINITY : l * LOG2E;
+      ndl[qb] = qreal[qb] ? -part : 0.f;
       if (kh == 0 && g == 0) {
         stats_out[2 * ((size_t)bh * ld + qrow)] = l2[qb];
         stats_out[2 * ((size_t)bh * ld + qrow) + 1] = ndl[qb];
@@ -464,8 +488,14 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(const T* __restrict__ q, cons
     btr = sw_tr_base<T, D>(32 * kh, g, cc);
   }
   int lim_a = 0, lim_b = 0, raw = 0;
+  uint64_t km_a = ~0ull, km_b = ~0ull;  // PAD: real slots of the staged KV cubes
+  auto slots_of = [&](int jj, int lim) -> uint64_t {
+    if constexpr (PAD) return lim > 0 ? cube_slots(jj, pad) : 0ull;
+    else return ~0ull;
+  };
   if (cnt > 0) {
     const int j0 = cube_of(entry(0), lim_a);
+    km_a = slots_of(j0, lim_a);
     VSA2_FETCH_KV(j0, tA);
     if (cnt > 1) raw = entry(1);
   }
@@ -474,19 +504,23 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(const T* __restrict__ q, cons
     __syncthreads();  // stage A holds entry n; every wave is done with stage B
     if (n + 1 < cnt) {
       const int jj = cube_of(raw, lim_b);
+      km_b = slots_of(jj, lim_b);
       if (n + 2 < cnt) raw = entry(n + 2);
       VSA2_FETCH_KV(jj, tB);
     }
-    if (lim_a > 32 * kh) dq_pair<T, D>(tA, tA + TILE, brow, btr, lim_a, qf, of, l2, ndl, dqa, kh, g, cc, c);
+    if (lim_a > 32 * kh)
+      dq_pair<T, D, PAD>(tA, tA + TILE, brow, btr, lim_a, km_a, qf, of, l2, ndl, dqa, kh, g, cc, c);
     if (n + 1 >= cnt) break;
     wait_vm0();
     __syncthreads();  // stage B holds entry n + 1; every wave is done with stage A
     if (n + 2 < cnt) {
       const int jj = cube_of(raw, lim_a);
+      km_a = slots_of(jj, lim_a);
       if (n + 3 < cnt) raw = entry(n + 3);
       VSA2_FETCH_KV(jj, tA);
     }
-    if (lim_b > 32 * kh) dq_pair<T, D>(tB, tB + TILE, brow, btr, lim_b, qf, of, l2, ndl, dqa, kh, g, cc, c);
+    if (lim_b > 32 * kh)
+      dq_pair<T, D, PAD>(tB, tB + TILE, brow, btr, lim_b, km_b, qf, of, l2, ndl, dqa, kh, g, cc, c);
   }
 #undef VSA2_FETCH_KV
 
@@ -512,15 +546,21 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(const T* __restrict__ q, cons
 #pragma unroll
       for (int r = 0; r < 4; ++r)
         dqa[db][qb][r] = (dqa[db][qb][r] + mine[((db * 2 + qb) * 4 + r) * 64 + lane]) * scale;
-  if (dq_add) {  // the coarse branch's per-cube gradient row, 1/64 to every token
+  if (dq_add) {  // the coarse branch's per-cube gradient row, 1/n to each of the n real tokens
     const float* qa = dq_add + ((size_t)bh * nq + i) * D;
+    float wq[2] = {1.0f / 64.0f, 1.0f / 64.0f};
+    if constexpr (PAD) {
+      const float inv_n = 1.0f / (float)__popcll(qm);
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) wq[qb] = qreal[qb] ? inv_n : 0.f;
+    }
 #pragma unroll
     for (int db = 0; db < D / 16; ++db) {
       const f32x4 a4 = *reinterpret_cast<const f32x4*>(qa + 16 * db + 4 * g);
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) dqa[db][qb][r] += a4[r] * (1.0f / 64.0f);
+        for (int r = 0; r < 4; ++r) dqa[db][qb][r] += a4[r] * wq[qb];
     }
   }
 #pragma unroll
@@ -539,35 +579,36 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(const T* __restrict__ q, cons
   }
 }
 
-template <typename T, typename TO, int D, bool DENSE>
+template <typename T, typename TO, int D, bool DENSE, bool PAD>
 hipError_t launch_bwd_tt(const AttnBwdArgs& a, hipStream_t st) {
   // dQ first: in sparse mode it writes the row statistics the dK/dV kernel reads
   if (!DENSE) timer_before(TK_BWD_DQ, st);
   if constexpr (DENSE)
-    hipLaunchKernelGGL((k_bwd_dq<T, TO, D, DENSE, false>), dim3(xcd_grid(a.nq, a.bh)), dim3(256), 0, st,
+    hipLaunchKernelGGL((k_bwd_dq<T, TO, D, DENSE, false, false>), dim3(xcd_grid(a.nq, a.bh)), dim3(256), 0, st,
                        (const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.d_o, nullptr, nullptr, nullptr,
                        a.stats, a.row_ptr, a.col_idx, a.dq_add, (TO*)a.dq, a.nq, a.nkv, a.seq, a.ld, a.out_rows, a.kph,
-                       a.scale, a.scale_log2, a.ct, a.cy, a.cx);
+                       a.scale, a.scale_log2, a.ct, a.cy, a.cx, a.pad);
   else
-    hipLaunchKernelGGL((k_bwd_dq<T, TO, D, DENSE, true>), dim3(xcd_grid(a.nq, a.bh)), dim3(256), 0, st,
+    hipLaunchKernelGGL((k_bwd_dq<T, TO, D, DENSE, true, PAD>), dim3(xcd_grid(a.nq, a.bh)), dim3(256), 0, st,
                        (const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.d_o, (const T*)a.o, a.lse,
                        a.stats_out, nullptr, a.row_ptr, a.col_idx, a.dq_add, (TO*)a.dq, a.nq, a.nkv, a.seq, a.ld,
-                       a.out_rows, a.kph, a.scale, a.scale_log2, a.ct, a.cy, a.cx);
+                       a.out_rows, a.kph, a.scale, a.scale_log2, a.ct, a.cy, a.cx, a.pad);
   if (!DENSE) timer_after(TK_BWD_DQ, st);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (!DENSE) timer_before(TK_BWD_DKDV, st);
-  hipLaunchKernelGGL((k_bwd_dkdv<T, TO, D, DENSE>), dim3(xcd_grid(a.nkv, a.bh)), dim3(256), 0, st, (const T*)a.q,
-                     (const T*)a.k, (const T*)a.v, (const T*)a.d_o, DENSE ? a.stats : a.stats_out, a.col_ptr,
-                     a.row_idx, a.dk_add, a.dv_add, (TO*)a.dk, (TO*)a.dv, a.nq, a.nkv, a.seq, a.ld, a.out_rows,
-                     a.kph, a.scale, a.scale_log2);
+  hipLaunchKernelGGL((k_bwd_dkdv<T, TO, D, DENSE, PAD>), dim3(xcd_grid(a.nkv, a.bh)), dim3(256), 0, st,
+                     (const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.d_o, DENSE ? a.stats : a.stats_out,
+                     a.col_ptr, a.row_idx, a.dk_add, a.dv_add, (TO*)a.dk, (TO*)a.dv, a.nq, a.nkv, a.seq, a.ld,
+                     a.out_rows, a.kph, a.scale, a.scale_log2, a.pad);
   if (!DENSE) timer_after(TK_BWD_DKDV, st);
   return hipGetLastError();
 }
 
 template <typename T, int D>
 hipError_t launch_bwd_t(const AttnBwdArgs& a, hipStream_t st) {
-  return a.dense ? launch_bwd_tt<T, float, D, true>(a, st) : launch_bwd_tt<T, T, D, false>(a, st);
+  if (a.dense) return launch_bwd_tt<T, float, D, true, false>(a, st);
+  return a.pad.on ? launch_bwd_tt<T, T, D, false, true>(a, st) : launch_bwd_tt<T, T, D, false, false>(a, st);
 }
 
 hipError_t launch_attn_bwd(const AttnBwdArgs& a, hipStream_t st) {

@@ -1,7 +1,9 @@
 // Block-sparse flash attention forward: the fine branch of VSA2 (paper §2.2
 // Eq.(12), the -inf block mask of §2.1 applied by skipping unselected tiles).
 // The same kernel in "dense" mode runs the coarse branch's attention over the
-// nb pooled cube tokens (Eq.(2)-(3)), with a ragged last tile.
+// nb pooled cube tokens (Eq.(2)-(3)), with a ragged last tile.  On a padded
+// grid (§2.2 "Kernel Implementation") pad keys are masked and pad query rows
+// give zeros.
 //
 // Work split: one block (2 waves) per query cube; each wave owns 32 queries as
 // MFMA B fragments in registers, so every K/V byte read from LDS feeds two
@@ -23,12 +25,16 @@
 
 namespace vsa2 {
 
-template <typename T, typename TO, int D, bool DENSE>
+// PAD (fine branch on a padded grid): pad slots of a KV cube are masked like
+// keys past the end; pad query rows are written as O_f = 0, LSE = -inf.
+template <typename T, typename TO, int D, bool DENSE, bool PAD>
 __global__ __launch_bounds__(128, 2) void k_attn_fwd(const T* __restrict__ q, const T* __restrict__ k,
                                                   const T* __restrict__ v, const int32_t* __restrict__ row_ptr,
                                                   const int32_t* __restrict__ col_idx, TO* __restrict__ o,
                                                   float* __restrict__ lse, int nq, int nkv, int seq, int ld,
-                                                  int out_rows, int64_t kph, float c, int ct, int cy, int cx) {
+                                                  int out_rows, int64_t kph, float c, int ct, int cy, int cx,
+                                                  PadGrid pad) {
+  static_assert(!(DENSE && PAD), "padding applies to the fine branch");
   __shared__ __align__(16) T ks[64 * D];
   __shared__ __align__(16) T vs[64 * D];
   int bh, i;
@@ -84,6 +90,8 @@ __global__ __launch_bounds__(128, 2) void k_attn_fwd(const T* __restrict__ q, co
       sw_store(vr, vs, tid);
       __syncthreads();
       const int lim = kv_limit(j);
+      uint64_t km = ~0ull;  // PAD: real slots of cube j
+      if constexpr (PAD) km = j >= 0 ? cube_slots(j, pad) : 0ull;
       if (n + 1 < cnt) {
         j = cube_at(n + 1);
         sw_load(kr, kbase + (size_t)max(j, 0) * 64 * D, tid);
@@ -111,6 +119,16 @@ __global__ __launch_bounds__(128, 2) void k_attn_fwd(const T* __restrict__ q, co
 #pragma unroll
           for (int r = 0; r < 4; ++r)
             if (16 * kb + 4 * g + r >= lim) acc[kb][0][r] = acc[kb][1][r] = -INFINITY;
+      }
+      if constexpr (PAD) {
+        if (km != ~0ull) {
+          const uint64_t mine = km >> (4 * g);
+#pragma unroll
+          for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              if (!((mine >> (16 * kb + r)) & 1)) acc[kb][0][r] = acc[kb][1][r] = -INFINITY;
+        }
       }
       // lane-local maxima; the 4-lane reduction only runs when a lane asks to
       // move its reference maximum (lazy rescale, exponentials stay <= 2^8)
@@ -167,10 +185,14 @@ __global__ __launch_bounds__(128, 2) void k_attn_fwd(const T* __restrict__ q, co
     }
   }
 
+  uint64_t qm = ~0ull;  // PAD: real slots of query cube i
+  if constexpr (PAD) qm = cube_slots(i, pad);
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     const int qrow = i * 64 + 32 * w + 16 * qb + cc;
-    const float lt = group_sum(l[qb]);
+    const bool real = !PAD || ((qm >> (32 * w + 16 * qb + cc)) & 1);
+    const float lsum = group_sum(l[qb]);  // every lane takes part in the cross-lane sum
+    const float lt = real ? lsum : 0.f;
     const float inv = lt > 0.f ? 1.0f / lt : 0.f;
     const bool live = DENSE ? (qrow < seq && qrow < out_rows) : (qrow < out_rows);
     if (live) {
@@ -179,7 +201,7 @@ __global__ __launch_bounds__(128, 2) void k_attn_fwd(const T* __restrict__ q, co
       for (int db = 0; db < D / 16; ++db) {
         Vec4<TO> r4;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) r4.v[r] = from_f32<TO>(oacc[db][qb][r] * inv);
+        for (int r = 0; r < 4; ++r) r4.v[r] = from_f32<TO>(real ? oacc[db][qb][r] * inv : 0.f);
         store4(orow + 16 * db + 4 * g, r4);
       }
       if (g == 0) lse[(size_t)bh * out_rows + qrow] = lt > 0.f ? (m[qb] * c + __log2f(lt)) * LN2 : -INFINITY;
@@ -191,14 +213,19 @@ template <typename T, int D>
 hipError_t launch_fwd_t(const AttnArgs& a, hipStream_t st) {
   dim3 grid(xcd_grid(a.nq, a.bh));
   if (a.dense) {
-    hipLaunchKernelGGL((k_attn_fwd<T, float, D, true>), grid, dim3(128), 0, st, (const T*)a.q, (const T*)a.k,
-                       (const T*)a.v, nullptr, nullptr, (float*)a.o, a.lse, a.nq, a.nkv, a.seq, a.ld, a.out_rows,
-                       a.kph, a.scale_log2, 0, 0, 0);
+    hipLaunchKernelGGL((k_attn_fwd<T, float, D, true, false>), grid, dim3(128), 0, st, (const T*)a.q,
+                       (const T*)a.k, (const T*)a.v, nullptr, nullptr, (float*)a.o, a.lse, a.nq, a.nkv, a.seq, a.ld,
+                       a.out_rows, a.kph, a.scale_log2, 0, 0, 0, a.pad);
   } else {
     timer_before(TK_FINE_FWD, st);
-    hipLaunchKernelGGL((k_attn_fwd<T, T, D, false>), grid, dim3(128), 0, st, (const T*)a.q, (const T*)a.k,
-                       (const T*)a.v, a.row_ptr, a.col_idx, (T*)a.o, a.lse, a.nq, a.nkv, a.seq, a.ld, a.out_rows,
-                       a.kph, a.scale_log2, a.ct, a.cy, a.cx);
+    if (a.pad.on)
+      hipLaunchKernelGGL((k_attn_fwd<T, T, D, false, true>), grid, dim3(128), 0, st, (const T*)a.q, (const T*)a.k,
+                         (const T*)a.v, a.row_ptr, a.col_idx, (T*)a.o, a.lse, a.nq, a.nkv, a.seq, a.ld, a.out_rows,
+                         a.kph, a.scale_log2, a.ct, a.cy, a.cx, a.pad);
+    else
+      hipLaunchKernelGGL((k_attn_fwd<T, T, D, false, false>), grid, dim3(128), 0, st, (const T*)a.q,
+                         (const T*)a.k, (const T*)a.v, a.row_ptr, a.col_idx, (T*)a.o, a.lse, a.nq, a.nkv, a.seq,
+                         a.ld, a.out_rows, a.kph, a.scale_log2, a.ct, a.cy, a.cx, a.pad);
     timer_after(TK_FINE_FWD, st);
   }
   return hipGetLastError();

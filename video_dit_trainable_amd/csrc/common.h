@@ -21,6 +21,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "launch.h"
+
 namespace vsa2 {
 
 typedef __bf16 bf16;
@@ -481,6 +483,48 @@ __host__ __device__ inline int blocked_cube(int p, int ct, int cy, int cx) {
   const int sx = min(B, cx - x0);
   const int dx = p % sx, dy = (p / sx) % sy, dt = p / (sx * sy);
   return ((t0 + dt) * cy + (y0 + dy)) * cx + (x0 + dx);
+}
+
+// Slots of a cube (slot 8s + u: sub-cube s, position u, each raster over
+// 2x2x2) whose coordinate along `axis` (0 t, 1 y, 2 x) is below v: the
+// coordinate is 2 * bit(5 - axis) + bit(2 - axis) of the slot.
+__host__ __device__ constexpr uint64_t axis_slots(int axis, int v) {
+  uint64_t m = 0;
+  for (int s = 0; s < 64; ++s)
+    if (2 * ((s >> (5 - axis)) & 1) + ((s >> (2 - axis)) & 1) < v) m |= 1ull << s;
+  return m;
+}
+template <int AXIS>
+__device__ __forceinline__ uint64_t axis_mask(int v) {
+  constexpr uint64_t m1 = axis_slots(AXIS, 1), m2 = axis_slots(AXIS, 2), m3 = axis_slots(AXIS, 3);
+  return v >= 4 ? ~0ull : (v == 3 ? m3 : (v == 2 ? m2 : m1));
+}
+
+// Real extents of cube c.  The quotients use float reciprocals: for c < 2^16
+// (c + 0.5) / n lies at least 0.5 / n from an integer, far beyond the
+// rounding error of the two float roundings, so the truncation is exact.
+__device__ __forceinline__ void cube_extent(int c, const PadGrid& p, int& vt, int& vy, int& vx) {
+  const int a = (int)(((float)c + 0.5f) * p.inv_nyx);
+  const int rem = c - a * p.ny * p.nx;
+  const int b = (int)(((float)rem + 0.5f) * p.inv_nx);
+  const int x = rem - b * p.nx;
+  vt = a == p.nt - 1 ? p.et : 4;
+  vy = b == p.ny - 1 ? p.ey : 4;
+  vx = x == p.nx - 1 ? p.ex : 4;
+}
+
+// Bit s set for the slots of cube c that hold a real token.
+__device__ __forceinline__ uint64_t cube_slots(int c, const PadGrid& p) {
+  int vt, vy, vx;
+  cube_extent(c, p, vt, vy, vx);
+  return axis_mask<0>(vt) & axis_mask<1>(vy) & axis_mask<2>(vx);
+}
+
+// Number of real tokens of cube c.
+__device__ __forceinline__ int cube_count(int c, const PadGrid& p) {
+  int vt, vy, vx;
+  cube_extent(c, p, vt, vy, vx);
+  return vt * vy * vx;
 }
 
 __host__ __device__ inline int xcd_grid(int items_per_bh, int bh_total) {

@@ -1,6 +1,8 @@
 // Gated merge of VSA2 (paper §2.2 Eq.(13)-(14)): G = tanh(X W_g), one gate per
 // token and head, O = G * Repeat(O_hat_c) + O_f (Eq.(4) broadcast fused), and
-// its backward (dW_g, dX, dO_hat_c).
+// its backward (dW_g, dX, dO_hat_c).  On a padded grid (§2.2 "Kernel
+// Implementation") pad rows get G = 0 and O = 0 and take no part in the
+// backward (dpre = 0 there, so their dX is 0 and their X adds nothing to dW_g).
 //
 // X W_g and dpre W_g^T are skinny GEMMs run on MFMA; in bf16 mode the fp32
 // operands W_g and dpre are split into a bf16 high part and a bf16 remainder
@@ -59,11 +61,12 @@ template <typename T, int D, int NHB>
 __global__ __launch_bounds__(256) void k_gate_fwd(const T* __restrict__ x, const T* __restrict__ wt,
                                                   const float* __restrict__ oc_hat, const T* __restrict__ o_f,
                                                   T* __restrict__ o, float* __restrict__ gout, int H, int nb, int dm,
-                                                  int hp) {
+                                                  int hp, PadGrid pad) {
   constexpr bool SPLIT = sizeof(T) == 2;
   __shared__ float gs[64][HMAX + 1];
   const int c = blockIdx.x, b = blockIdx.y, tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4,
             cc = lane & 15;
+  const uint64_t real = pad.on ? cube_slots(c, pad) : ~0ull;  // padded grid: pad rows get g = 0, O = 0
   const size_t L = (size_t)nb * CUBE;
   const T* fhi = wt;
   const T* flo = wt + (size_t)hp * dm;
@@ -107,8 +110,10 @@ __global__ __launch_bounds__(256) void k_gate_fwd(const T* __restrict__ x, const
     const int h = 16 * hb + cc;
     float v[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
+    for (int r = 0; r < 4; ++r) {
       v[r] = tanhf(gpart[0][tb][r][lane] + gpart[1][tb][r][lane] + gpart[2][tb][r][lane] + gpart[3][tb][r][lane]);
+      if (!((real >> (16 * tb + 4 * g + r)) & 1)) v[r] = 0.f;
+    }
     const size_t t0 = (size_t)c * CUBE + 16 * tb;
 #pragma unroll
     for (int r = 0; r < 4; ++r) gs[16 * tb + 4 * g + r][h] = v[r];
@@ -133,9 +138,10 @@ __global__ __launch_bounds__(256) void k_gate_fwd(const T* __restrict__ x, const
       const float4 a0 = *reinterpret_cast<const float4*>(oc + 8 * dg);
       const float4 a1 = *reinterpret_cast<const float4*>(oc + 8 * dg + 4);
       const float ocv[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+      const bool tok_real = (real >> t) & 1;
       Vec8<T> r;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) r.v[e] = from_f32<T>(fmaf(gv, ocv[e], to_f32(f.v[e])));
+      for (int e = 0; e < 8; ++e) r.v[e] = from_f32<T>(tok_real ? fmaf(gv, ocv[e], to_f32(f.v[e])) : 0.f);
       store8(o + off, r);
     }
   }
@@ -149,7 +155,7 @@ __global__ __launch_bounds__(256) void k_gate_bwd(const T* __restrict__ wt, cons
                                                   float* __restrict__ dpre, T* __restrict__ doc,
                                                   const float* __restrict__ lse_c, float* __restrict__ stats_c,
                                                   T* __restrict__ dx, int H, int nb,
-                                                  int nbp, int dm, int hp, int hk) {
+                                                  int nbp, int dm, int hp, int hk, PadGrid pad) {
   constexpr bool SPLIT = sizeof(T) == 2;
   constexpr int UPR = D / 8;
   constexpr int RROWS = 256 / UPR;
@@ -165,6 +171,7 @@ __global__ __launch_bounds__(256) void k_gate_bwd(const T* __restrict__ wt, cons
   const int c = blockIdx.x, b = blockIdx.y, tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4,
             cc = lane & 15;
   const size_t L = (size_t)nb * CUBE;
+  const uint64_t real = pad.on ? cube_slots(c, pad) : ~0ull;  // padded grid: pad rows get g = 0, dpre = 0
   for (int u = tid; u < 64 * (HMAX + 4); u += 256) dps[u / (HMAX + 4)][u % (HMAX + 4)] = 0.f;
   __syncthreads();
   const int dg = tid % UPR;
@@ -202,7 +209,8 @@ __global__ __launch_bounds__(256) void k_gate_bwd(const T* __restrict__ wt, cons
       const int t = tid / UPR + RROWS * i;
       const size_t tok = (size_t)c * CUBE + t;
       const Vec8<T> x = xc[i];
-      const float gv = gc[i];
+      const bool tok_real = (real >> t) & 1;
+      const float gv = tok_real ? gc[i] : 0.f;
       float part = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -213,7 +221,7 @@ __global__ __launch_bounds__(256) void k_gate_bwd(const T* __restrict__ wt, cons
 #pragma unroll
       for (int s = 1; s < UPR; s <<= 1) part += __shfl_xor(part, s);
       if (dg == 0) {
-        const float dp = part * (1.f - gv * gv);
+        const float dp = tok_real ? part * (1.f - gv * gv) : 0.f;
         dps[t][h] = dp;
         dpre[bh * L + tok] = dp;
       }
@@ -515,7 +523,7 @@ hipError_t launch_gate_fwd_t(const GateArgs& a, hipStream_t st) {
   const dim3 grid(a.nb, a.batch);
 #define VSA2_GATE_FWD(NHB)                                                                                     \
   hipLaunchKernelGGL((k_gate_fwd<T, D, NHB>), grid, dim3(256), 0, st, (const T*)a.x, (const T*)a.wt, a.oc_hat, \
-                     (const T*)a.o_f, (T*)a.o, a.g, a.heads, a.nb, a.dm, hp)
+                     (const T*)a.o_f, (T*)a.o, a.g, a.heads, a.nb, a.dm, hp, a.pad)
   switch (hp / 16) {
     case 1: VSA2_GATE_FWD(1); break;
     case 2: VSA2_GATE_FWD(2); break;
@@ -539,11 +547,11 @@ hipError_t launch_gate_bwd_t(const GateBwdArgs& a, hipStream_t st) {
   if (hk <= 32)
     hipLaunchKernelGGL((k_gate_bwd<T, D, 1>), dim3(a.nb, a.batch), dim3(256), 0, st, (const T*)a.wt, a.oc_hat, a.g,
                        (const T*)a.d_o, a.dpre, (T*)a.doc, a.lse_c, a.stats_c, (T*)a.dx, a.heads, a.nb, a.nbp, a.dm,
-                       hp, hk);
+                       hp, hk, a.pad);
   else
     hipLaunchKernelGGL((k_gate_bwd<T, D, 2>), dim3(a.nb, a.batch), dim3(256), 0, st, (const T*)a.wt, a.oc_hat, a.g,
                        (const T*)a.d_o, a.dpre, (T*)a.doc, a.lse_c, a.stats_c, (T*)a.dx, a.heads, a.nb, a.nbp, a.dm,
-                       hp, hk);
+                       hp, hk, a.pad);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if constexpr (sizeof(T) == 2) {

@@ -6,11 +6,23 @@
 
 namespace vsa2 {
 
+// Latent grids whose sides are not multiples of 4 are padded up to whole
+// cubes (paper §2.2 "Kernel Implementation"); pad positions are not tokens.
+// PadGrid gives the cube grid and the real extent (1..4) of the last cube
+// along each axis; `on` is 0 when the grid divides.
+struct PadGrid {
+  int on;
+  int nt, ny, nx;        // cubes along t, y, x
+  int et, ey, ex;        // real positions of the last cube along t, y, x
+  float inv_nx, inv_nyx; // 1 / nx, 1 / (ny nx), rounded to nearest
+};
+
 struct PoolArgs {
   const void *q, *k, *v;
   void *qr, *kr, *qc, *kc, *vc;
   int bh, nb, nbp, d;
   bool bf16;
+  PadGrid pad;
 };
 hipError_t launch_pool(const PoolArgs& a, hipStream_t st);
 
@@ -21,6 +33,8 @@ struct RouteArgs {
   int bh, nb, d;
   bool bf16;
   float scale_log2;   // softmax scale * log2(e)
+  PadGrid pad;
+  uint64_t* kmask;    // workspace [ceil(8 nb / 64)] (padded grids): bit b of word t set when pooled key 64t + b exists
 };
 hipError_t launch_route(const RouteArgs& a, hipStream_t st);
 
@@ -60,6 +74,7 @@ struct AttnArgs {
   bool bf16, dense;
   float scale_log2;
   int ct, cy, cx;                     // cube grid for the blocked visiting order (0 = linear)
+  PadGrid pad;                        // fine branch on a padded grid: pad keys masked, pad rows zero
 };
 hipError_t launch_attn_fwd(const AttnArgs& a, hipStream_t st);
 
@@ -69,7 +84,7 @@ struct AttnBwdArgs {
   const float* stats;                 // dense: [bh, ld] pairs (lse * log2 e, -rowsum(dO * O)); +inf lse = masked row
   float* stats_out;                   // fine: workspace for the same pairs, written by the dQ kernel
   const int32_t *row_ptr, *col_idx, *col_ptr, *row_idx;
-  const float *dq_add, *dk_add, *dv_add;  // [bh, nkv, d] per-cube terms added as row/64 (or NULL)
+  const float *dq_add, *dk_add, *dv_add;  // [bh, nkv, d] per-cube terms added as row/n, n real tokens (or NULL)
   void *dq, *dk, *dv;                 // storage dtype (fine) or fp32 (dense)
   int bh, nq, nkv, seq, ld, out_rows;
   int64_t kph;
@@ -78,6 +93,7 @@ struct AttnBwdArgs {
   float scale;
   float scale_log2;
   int ct, cy, cx;                     // cube grid for the blocked visiting order (0 = linear)
+  PadGrid pad;                        // fine branch on a padded grid (per-cube terms added as row/n, n real tokens)
 };
 hipError_t launch_attn_bwd(const AttnBwdArgs& a, hipStream_t st);
 
@@ -91,6 +107,7 @@ struct GateArgs {
   float* g;               // [bh, L]
   int batch, heads, nb, d, dm;
   bool bf16;
+  PadGrid pad;            // pad rows: g = 0, O = 0
 };
 hipError_t launch_gate_fwd(const GateArgs& a, hipStream_t st);
 
@@ -114,6 +131,7 @@ struct GateBwdArgs {
   float* dw_g;
   int batch, heads, nb, nbp, d, dm, nchunk;
   bool bf16;
+  PadGrid pad;            // pad rows: dpre = 0 (so dX = 0 and X there adds nothing to dW_g)
 };
 hipError_t launch_gate_bwd(const GateBwdArgs& a, hipStream_t st);
 

@@ -3,7 +3,8 @@
 // Q_r K_r^T is computed twice on chip -- pass 1 accumulates each pooled
 // query's log-sum-exp, pass 2 recomputes the tiles, normalises them and
 // averages the 8 x 8 (query sub-cube, key sub-cube) entries of each cube pair.
-// Only the nb x nb block scores reach memory.
+// Only the nb x nb block scores reach memory.  On a padded grid (§2.2 "Kernel
+// Implementation") pooled tokens that hold no real token are masked.
 //
 // Work split: a 256-thread block owns 128 pooled queries (16 query cubes);
 // wave w holds queries 32w .. 32w+31 as MFMA B fragments in registers and
@@ -100,14 +101,46 @@ __device__ __forceinline__ void mask_tail(f32x4 (&acc)[4][2], int k0, int nkeys,
       if (k0 + key_of_row(16 * kb + 4 * g + r) >= nkeys) acc[kb][0][r] = acc[kb][1][r] = -INFINITY;
 }
 
+// Padded grids: keys whose bit in the tile's existence word tm is clear get
+// -inf (LDS row 16kb + 4g + r holds key 32 (kb >> 1) + 8g + 4 (kb & 1) + r).
+__device__ __forceinline__ void mask_keys(f32x4 (&acc)[4][2], uint64_t tm, int g) {
+  if (tm == ~0ull) return;
+  const uint64_t mine = tm >> (8 * g);
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (!((mine >> (32 * (kb >> 1) + 4 * (kb & 1) + r)) & 1)) acc[kb][0][r] = acc[kb][1][r] = -INFINITY;
+}
+
 }  // namespace
+
+// Existence words of the pooled keys of a padded grid: bit b of word t is set
+// when pooled key 64t + b (sub-cube b % 8 of cube 8t + b / 8) holds a real
+// token, i.e. when its first slot does.  Keys past the last cube are clear.
+__global__ void k_route_kmask(uint64_t* __restrict__ kmask, int nb, PadGrid pad) {
+  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= (8 * nb + RK - 1) / RK) return;
+  uint64_t m = 0;
+  for (int k = 0; k < 8; ++k) {
+    const int c = 8 * t + k;
+    if (c >= nb) break;
+    const uint64_t real = cube_slots(c, pad);
+    for (int s = 0; s < 8; ++s) m |= ((real >> (8 * s)) & 1ull) << (8 * k + s);
+  }
+  kmask[t] = m;
+}
 
 // TAIL: the pooled key count is not a multiple of 64, so the last key tile is
 // ragged (masked).  Without it no tile is, and the masking is compiled out.
-template <typename T, int D, bool PASS2, bool TAIL>
+// PAD: a padded grid; keys and queries that hold no real token are taken from
+// the existence words (which also clear the ragged tail): such keys are
+// masked, such queries get LSE +inf, so pass 2 gives them no weight.
+template <typename T, int D, bool PASS2, bool TAIL, bool PAD>
 __global__ __launch_bounds__(256, 2) void k_router(const T* __restrict__ qr, const T* __restrict__ kr,
                                                    float* __restrict__ lse2, float* __restrict__ scores, int nb,
-                                                   float c) {
+                                                   float c, const uint64_t* __restrict__ kmask) {
+  static_assert(!(TAIL && PAD), "the existence words cover the ragged tail");
   __shared__ __align__(16) T kA[RK * D];
   __shared__ __align__(16) T kB[RK * D];
   const int Lr = 8 * nb;
@@ -230,6 +263,7 @@ __global__ __launch_bounds__(256, 2) void k_router(const T* __restrict__ qr, con
     if (t + 1 < nkt) copy_tile(t + 1, kB);
     tile_scores<T, D>(kA, bs, qf, g, cc, acc);
     if constexpr (TAIL) mask_tail(acc, t * RK, Lr, g);
+    if constexpr (PAD) mask_keys(acc, kmask[t], g);
     consume(acc, t);
     if (t + 1 >= nkt) break;
     wait_vm0();
@@ -237,6 +271,7 @@ __global__ __launch_bounds__(256, 2) void k_router(const T* __restrict__ qr, con
     if (t + 2 < nkt) copy_tile(t + 2, kA);
     tile_scores<T, D>(kB, bs, qf, g, cc, acc);
     if constexpr (TAIL) mask_tail(acc, (t + 1) * RK, Lr, g);
+    if constexpr (PAD) mask_keys(acc, kmask[t + 1], g);
     consume(acc, t + 1);
   }
 
@@ -247,31 +282,40 @@ __global__ __launch_bounds__(256, 2) void k_router(const T* __restrict__ qr, con
       const float M = group_max(m[qb]);
       const float part = (m[qb] == -INFINITY) ? 0.f : l[qb] * fast_exp2((m[qb] - M) * c);
       const float lt = group_sum(part);
-      if (g == 0 && qrow < Lr) lse2[(size_t)bh * Lr + qrow] = M * c + __log2f(lt);
+      bool exists = true;
+      if constexpr (PAD) exists = qrow < Lr && ((kmask[qrow >> 6] >> (qrow & 63)) & 1);
+      if (g == 0 && qrow < Lr) lse2[(size_t)bh * Lr + qrow] = exists ? M * c + __log2f(lt) : INFINITY;
     }
   }
 }
 
-template <typename T, int D, bool TAIL>
+template <typename T, int D, bool TAIL, bool PAD>
 hipError_t launch_route_tt(const RouteArgs& a, hipStream_t st) {
   const int nqt = (8 * a.nb + RQ - 1) / RQ;
   dim3 grid(xcd_grid(nqt, a.bh));
+  if constexpr (PAD) {
+    const int nkt = (8 * a.nb + RK - 1) / RK;
+    hipLaunchKernelGGL(k_route_kmask, dim3((nkt + 255) / 256), dim3(256), 0, st, a.kmask, a.nb, a.pad);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   timer_before(TK_ROUTER_LSE, st);
-  hipLaunchKernelGGL((k_router<T, D, false, TAIL>), grid, dim3(256), 0, st, (const T*)a.qr, (const T*)a.kr, a.lse2,
-                     a.scores, a.nb, a.scale_log2);
+  hipLaunchKernelGGL((k_router<T, D, false, TAIL, PAD>), grid, dim3(256), 0, st, (const T*)a.qr, (const T*)a.kr,
+                     a.lse2, a.scores, a.nb, a.scale_log2, (const uint64_t*)a.kmask);
   timer_after(TK_ROUTER_LSE, st);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   timer_before(TK_ROUTER_SCORES, st);
-  hipLaunchKernelGGL((k_router<T, D, true, TAIL>), grid, dim3(256), 0, st, (const T*)a.qr, (const T*)a.kr, a.lse2,
-                     a.scores, a.nb, a.scale_log2);
+  hipLaunchKernelGGL((k_router<T, D, true, TAIL, PAD>), grid, dim3(256), 0, st, (const T*)a.qr, (const T*)a.kr,
+                     a.lse2, a.scores, a.nb, a.scale_log2, (const uint64_t*)a.kmask);
   timer_after(TK_ROUTER_SCORES, st);
   return hipGetLastError();
 }
 
 template <typename T, int D>
 hipError_t launch_route_t(const RouteArgs& a, hipStream_t st) {
-  return (8 * a.nb) % RK ? launch_route_tt<T, D, true>(a, st) : launch_route_tt<T, D, false>(a, st);
+  if (a.pad.on) return launch_route_tt<T, D, false, true>(a, st);
+  return (8 * a.nb) % RK ? launch_route_tt<T, D, true, false>(a, st) : launch_route_tt<T, D, false, false>(a, st);
 }
 
 hipError_t launch_route(const RouteArgs& a, hipStream_t st) {

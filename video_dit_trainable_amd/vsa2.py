@@ -205,8 +205,9 @@ class Layer:
     def __init__(self, p, topk, d_model, device="cuda"):
         self.p, self.topk, self.d_model, self.device = p, topk, d_model, device
         bh = p.batch * p.heads
-        L = p.lat_t * p.lat_y * p.lat_x
-        nb = L // 64
+        # token slots of the grid padded up to whole 4x4x4 cubes
+        nb = -(-p.lat_t // 4) * -(-p.lat_y // 4) * -(-p.lat_x // 4)
+        L = 64 * nb
         self.L, self.nb, self.bh = L, nb, bh
         self.k = budget(p, topk)
         self.sdt = torch.bfloat16 if p.dtype == VSA2_BF16 else torch.float32
