@@ -58,6 +58,7 @@ def cpu_baseline(w, q, k, v, d_o, budget_s=20.0):
 
     f64 = lambda t: t.float().cpu().double().numpy()
     qh, kh, vh, doh = f64(q[0, 0]), f64(k[0, 0]), f64(v[0, 0]), f64(d_o[0, 0])
+    real = orc.token_valid(w.grid)
     lr = w.L // 8
     order = np.random.default_rng(0).permutation(w.nb)
     n_router, t_router = 0, 0.0
@@ -77,8 +78,8 @@ def cpu_baseline(w, q, k, v, d_o, budget_s=20.0):
         sub = np.zeros_like(mask)
         sub[cubes] = mask[cubes]
         t0 = time.perf_counter()
-        orc.fine_forward(qh, kh, vh, sub, rows=cubes)
-        orc.fine_backward(qh, kh, vh, sub, doh)
+        orc.fine_forward(qh, kh, vh, sub, rows=cubes, valid=real)
+        orc.fine_backward(qh, kh, vh, sub, doh, valid=real)
         t_fine += time.perf_counter() - t0
         n_fine += len(cubes)
         pairs += int(sub.sum())
@@ -89,6 +90,21 @@ def cpu_baseline(w, q, k, v, d_o, budget_s=20.0):
             "sample": f"head 0 of the same inputs: router rows of {n_router} query cubes ({t_router:.1f} s) + "
                       f"fine fwd+bwd of {n_fine} query cubes, {pairs} selected pairs ({t_fine:.1f} s); fp64 numpy",
             "seconds": round(secs, 2)}
+
+
+def describe(w):
+    """The workload named by what it is, with its sizes."""
+    T, Y, X = w.grid
+    grid = f"latent {T}x{Y}x{X} = {w.L_real} tokens"
+    if w.padded:
+        Tp, Yp, Xp = w.pgrid
+        grid += f" (padded to whole 4x4x4 cubes: {Tp}x{Yp}x{Xp} = {w.L} slots, pad masked)"
+    what = ("full forward + backward of router, TopK, fine, coarse and gate" if w.train
+            else "forward of router, TopK, fine, coarse and gate")
+    skew = ", skewed query-cube scales" if w.skew else ""
+    return (f"{'720p training' if w.name.startswith('train720') else w.name} shape: {grid}, B={w.batch}, "
+            f"{w.heads} heads, d={w.head_dim}, {w.dtype}, router pool 2x2x2, 4x4x4 cubes, per-sequence "
+            f"top{w.topk}{skew}; {what}")
 
 
 def source_hash(kernel):
@@ -273,9 +289,7 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "720p training shape: latent 44x48x104 = 219648 tokens, B=1, 20 heads, d=128, "
-                               "bf16, router pool 2x2x2, 4x4x4 cubes, per-sequence top64, skewed query-cube "
-                               "scales; full forward + backward of router, TopK, fine, coarse and gate",
+        "config": {"workload": describe(w),
                    "global_batch": w.batch, "seq_len": w.L, "heads": w.heads, "head_dim": w.head_dim,
                    "topk": w.topk, "parallelism": "single GPU"},
         "step_flops": step_flops,

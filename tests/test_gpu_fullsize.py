@@ -9,7 +9,10 @@ one head's full score matrix, the fine outputs and gradients of sampled cubes,
 sampled rows of dX and the whole of dW_g (token chunks) -- and check the
 properties that hold at any size: every score row sums to 1/8, the selection
 is exactly the top k of the GPU's own scores with ties to the lower flat
-index, CSR/CSC are each other's transpose with columns ascending.
+index, CSR/CSC are each other's transpose with columns ascending.  The same
+checks run on the 720p training problem on a grid one short of whole cubes
+along every axis (43 x 47 x 103, padded), sampling the border cubes that hold
+pad slots; there every pad row of every output must be exactly zero.
 
 Tolerances as in test_gpu_parity: bf16 outputs max-abs 2e-2 and rel-L2 1e-2,
 gradients rel-L2 2e-2, index sets exact outside the relative 1e-3 band.
@@ -29,6 +32,7 @@ pytestmark = pytest.mark.gpu
 
 TRAIN = WORKLOADS["train720"]
 INFER = WORKLOADS["infer720"]
+TRAIN_PAD = WORKLOADS["train720pad"]    # 43 x 47 x 103, padded to the same 44 x 48 x 104 slots
 
 
 def _dev():
@@ -244,3 +248,88 @@ def test_inference_top128_sampled():
     o, _ = orc.fine_forward(gu.f64(r["q"][0, h]), gu.f64(r["k"][0, h]), gu.f64(r["v"][0, h]), mask, rows=cubes)
     toks = orc._tokens_of(cubes)
     gu.assert_close_bf16(gu.f64(layer.o_f[0, h])[toks], o[toks], f"O_f top128 head {h}")
+
+
+# ----------------------------------------------------------------------------- padded grid
+@pytest.fixture(scope="module")
+def train720pad():
+    return _run(TRAIN_PAD, TRAIN_PAD.topk, True)
+
+
+def _border_cubes(w):
+    """The corner cube (pads along t, y and x), one cube on each border face
+    (pads along one axis), and an interior cube."""
+    nt, ny, nx = (n // 4 for n in w.pgrid)
+    cube = lambda a, b, c: (a * ny + b) * nx + c
+    return [cube(nt - 1, ny - 1, nx - 1), cube(nt - 1, ny // 2, nx // 3), cube(nt // 2, ny - 1, nx // 2),
+            cube(1, 2, nx - 1), cube(nt // 3, ny // 3, nx // 3)]
+
+
+def test_padded_router_and_selection(train720pad):
+    r = train720pad
+    w, layer = r["w"], r["layer"]
+    scores = layer.scores[0]
+    nq = orc.pool_exists(w.grid, (2, 2, 2)).reshape(-1, 8).sum(axis=1)
+    np.testing.assert_allclose(scores.double().sum(dim=2).cpu().numpy(), np.broadcast_to(nq / 64.0, scores.shape[:2]),
+                               rtol=1e-4)
+    rows = np.array(_border_cubes(w))
+    for h in (0, 11):
+        want = orc.router_scores(gu.f64(r["q"][0, h]), gu.f64(r["k"][0, h]), w.grid, bf16_pooled=True, rows=rows)
+        got = scores[h].double().cpu().numpy()[rows]
+        for n in range(len(rows)):
+            assert gu.rel_l2(got[n], want[n]) <= 1e-4, f"head {h} row {rows[n]}"
+    h = 6
+    s = scores[h].cpu().numpy().reshape(-1)
+    order = np.argsort(-s, kind="stable")
+    want = np.zeros(s.size, dtype=bool)
+    want[order[:layer.k]] = True
+    rp, ci = _routed(r, h)
+    assert np.array_equal(orc.csr_to_mask(rp, ci, w.nb).reshape(-1), want)
+
+
+def test_padded_outputs_sampled(train720pad):
+    r = train720pad
+    w, layer = r["w"], r["layer"]
+    real = orc.token_valid(w.grid)
+    pad = torch.from_numpy(~real).to(_dev())
+    g = layer.grads()
+    # every pad row of every output, all heads
+    assert torch.all(layer.o_f[:, :, pad] == 0) and torch.all(layer.o[:, :, pad] == 0)
+    assert torch.all(torch.isneginf(layer.lse[:, :, pad]))
+    for name in ("dq", "dk", "dv"):
+        assert torch.all(g[name][:, :, pad] == 0), name
+    assert torch.all(g["dx"][:, pad] == 0)
+    oc_hat, _, gate_saved = layer.saved_views()
+    assert torch.all(gate_saved[:, :, pad] == 0)
+    # real rows of border cubes against the oracle
+    h = 9
+    rp, ci = _seeded(r, h)
+    mask = orc.csr_to_mask(rp, ci, w.nb)
+    cubes = [c for c in _border_cubes(w) if mask[c].any()]
+    q, k, v, d_o = (gu.f64(t[0, h]) for t in (r["q"], r["k"], r["v"], r["d_o"]))
+    o_f, lse = orc.fine_forward(q, k, v, mask, rows=cubes, valid=real)
+    toks = orc._tokens_of(cubes)
+    gu.assert_close_bf16(gu.f64(layer.o_f[0, h])[toks], o_f[toks], f"O_f head {h} cubes {cubes}")
+    live = np.isfinite(lse[toks])
+    np.testing.assert_allclose(gu.f64(layer.lse[0, h])[toks][live], lse[toks][live], atol=1e-3)
+    want_oc, _, _ = orc.coarse_forward(q, k, v, w.grid)
+    gu.assert_close_bf16(gu.f64(oc_hat[0, h]), want_oc, f"O_hat_c head {h}")
+    gate = orc.gate(gu.f64(r["x"][0][torch.from_numpy(toks).to(_dev())]), gu.f64(r["w_g"]), real[toks])[:, h]
+    want_o = gate[:, None] * want_oc[toks // 64] + o_f[toks]
+    gu.assert_close_bf16(gu.f64(layer.o[0, h])[toks], want_o, f"O head {h}", rounding=2.0 ** -8)
+    # dQ of the border query cubes, dK / dV of a border KV cube (fine branch)
+    sub = np.zeros_like(mask)
+    sub[cubes] = mask[cubes]
+    dq, _, _ = orc.fine_backward(q, k, v, sub, d_o, valid=real)
+    rr = gu.rel_l2(gu.f64(g["dq"][0, h])[toks], dq[toks])
+    assert rr <= 2e-2, f"dQ head {h}: rel-L2 {rr:.3g}"
+    j = _border_cubes(w)[0]
+    rows = np.nonzero(mask[:, j])[0]
+    if len(rows):
+        sub = np.zeros_like(mask)
+        sub[rows] = mask[rows]
+        _, dk, dv = orc.fine_backward(q, k, v, sub, d_o, valid=real)
+        tj = np.arange(64 * j, 64 * j + 64)
+        for name, got, want in (("dK", g["dk"], dk), ("dV", g["dv"], dv)):
+            rr = gu.rel_l2(gu.f64(got[0, h])[tj], want[tj])
+            assert rr <= 2e-2, f"{name} head {h} corner KV cube {j}: rel-L2 {rr:.3g}"
