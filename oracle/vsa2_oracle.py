@@ -14,7 +14,12 @@ Conventions shared with the library interface:
     inside a cube, the eight 2x2x2 sub-cubes in raster order, each holding its
     8 tokens in raster order.  The oracle does not rely on the inner order: it
     rebuilds every token's (t, y, x) from the grid and pools by coordinates.
-  * block size B = 64 (4x4x4), router pool R = 8 (2x2x2), G = B/R = 8.
+  * block size B = 64 (one 4x4x4 cube), router pool R = 8 (2x2x2), G = B/R =
+    8.  B = 128 is the blog's inferred setting for the paper's own runs (its
+    §07; the paper gives no 3D cut): here a 128-token block is two
+    x-adjacent cubes, 4x4x8, which the cube-tiled order keeps contiguous
+    (cubes 2m and 2m+1), so G = 16 and the grid's x side is padded to a
+    multiple of 8.  Blocks are numbered like the cube pairs.
   * softmax scale 1/sqrt(d) unless given.
   * a latent grid whose sides are not multiples of 4 is padded up to the next
     multiple along each axis (§2.2 "Kernel Implementation"); tensors hold the
@@ -42,12 +47,20 @@ SUB_SHAPE = (2, 2, 2)
 # ----------------------------------------------------------------------------
 # layout
 # ----------------------------------------------------------------------------
-def padded_grid(grid):
-    """Each side rounded up to a multiple of the cube side 4."""
-    return tuple(-(-int(n) // 4) * 4 for n in grid)
+def _check_block(block):
+    if block not in (64, 128):
+        raise ValueError(f"block size {block} is not 64 or 128")
+    return block // 64
 
 
-def token_coords(grid):
+def padded_grid(grid, block=64):
+    """Each side rounded up to a multiple of the cube side 4 (x to a multiple
+    of 8 for 128-token blocks)."""
+    mult = (4, 4, 4 * _check_block(block))
+    return tuple(-(-int(n) // m) * m for n, m in zip(grid, mult))
+
+
+def token_coords(grid, block=64):
     """(t, y, x) of every token slot in cube-tiled order, shape [L, 3], L the
     token count of the padded grid.
 
@@ -57,7 +70,7 @@ def token_coords(grid):
     position u (raster inside the 2x2x2 sub-cube).  Slots whose coordinates
     reach past ``grid`` are padding.
     """
-    T, Y, X = padded_grid(grid)
+    T, Y, X = padded_grid(grid, block)
     ct, cy, cx = T // 4, Y // 4, X // 4
     coords = np.empty((T * Y * X, 3), dtype=np.int64)
     slot = 0
@@ -75,21 +88,21 @@ def token_coords(grid):
     return coords
 
 
-def token_valid(grid):
+def token_valid(grid, block=64):
     """True for the slots that hold a token of ``grid`` (not padding), [L]."""
-    return np.all(token_coords(grid) < np.asarray(grid, dtype=np.int64), axis=1)
+    return np.all(token_coords(grid, block) < np.asarray(grid, dtype=np.int64), axis=1)
 
 
-def pool_groups(grid, pool):
+def pool_groups(grid, pool, block=64):
     """Token slots of each pooling window, ordered cube-major then window raster
     inside the cube.  Returns int array [L / prod(pool), prod(pool)].
 
     The windows tile every 4x4x4 cube (pool in {1,2,4}^3), so a pooled token
     index a belongs to cube a // (64 / prod(pool)).
     """
-    T, Y, X = padded_grid(grid)
+    T, Y, X = padded_grid(grid, block)
     pt, py, px = pool
-    coords = token_coords(grid)
+    coords = token_coords(grid, block)
     slot_of = np.empty((T, Y, X), dtype=np.int64)
     slot_of[coords[:, 0], coords[:, 1], coords[:, 2]] = np.arange(T * Y * X)
     groups = []
@@ -105,20 +118,32 @@ def pool_groups(grid, pool):
     return np.asarray(groups, dtype=np.int64)
 
 
-def mean_pool(x, grid, pool):
+def mean_pool(x, grid, pool, block=64):
     """MeanPool over windows of shape ``pool`` (Eq.(1) with the cube, Eq.(5)
     with the router window).  x: [L, d] -> [L / prod(pool), d].  A window
     averages the real tokens it holds; one holding none gives a zero row."""
-    grp = pool_groups(grid, pool)
-    ok = token_valid(grid)[grp]                               # [windows, members]
+    grp = pool_groups(grid, pool, block)
+    ok = token_valid(grid, block)[grp]                        # [windows, members]
     cnt = ok.sum(axis=1)
     tot = np.where(ok[..., None], np.asarray(x)[grp], 0.0).sum(axis=1)
     return np.where(cnt[:, None] > 0, tot / np.maximum(cnt, 1)[:, None], 0.0)
 
 
-def pool_exists(grid, pool):
+def pool_exists(grid, pool, block=64):
     """True for the pooling windows that hold at least one real token."""
-    return token_valid(grid)[pool_groups(grid, pool)].any(axis=1)
+    return token_valid(grid, block)[pool_groups(grid, pool, block)].any(axis=1)
+
+
+def block_mean(x, grid, block=64):
+    """Eq.(1): the mean of the real tokens of every attention block (a 4x4x4
+    cube, or a 4x4x8 pair of cubes).  Cube means come from the coordinates;
+    a pair's mean weights its two cubes by their real-token counts."""
+    cm = mean_pool(np.asarray(x, np.float64), grid, CUBE_SHAPE, block)
+    if block == 64:
+        return cm
+    n = token_valid(grid, block).reshape(-1, 64).sum(axis=1).astype(np.float64)
+    tot = (cm * n[:, None]).reshape(-1, 2, cm.shape[1]).sum(axis=1)
+    return tot / n.reshape(-1, 2).sum(axis=1)[:, None]
 
 
 def round_bf16(x):
@@ -143,26 +168,26 @@ def _scale(d, scale):
 # ----------------------------------------------------------------------------
 # router: pool - softmax - pool, Eq.(5)-(7)
 # ----------------------------------------------------------------------------
-def router_scores(q, k, grid, pool=SUB_SHAPE, scale=None, bf16_pooled=False, rows=None):
-    """Block scores P_r [nb, nb] of one head (Eq.(5)-(7)).
+def router_scores(q, k, grid, pool=SUB_SHAPE, scale=None, bf16_pooled=False, rows=None, block=64):
+    """Block scores P_r [nb, nb] of one head (Eq.(5)-(7)), nb attention blocks.
 
     Eq.(5): Q_r, K_r = MeanPool_R(Q, K).  With ``bf16_pooled`` the pooled
     operands are rounded to bf16 before the product (the precision the bf16
     kernels work in; the paper does not state one).
     Eq.(6): P_hat = softmax over all pooled keys of Q_r K_r^T / sqrt(d).
-    Eq.(7): P_r[i, j] = mean of the G x G entries of P_hat between cube i and
-    cube j (the paper's MeanPool_{GxG}; the sum would be G^2 times this).
-    ``rows`` restricts the output to some query cubes (rows are independent).
+    Eq.(7): P_r[i, j] = mean of the G x G entries of P_hat between block i and
+    block j (the paper's MeanPool_{GxG}; the sum would be G^2 times this).
+    ``rows`` restricts the output to some query blocks (rows are independent).
     On a padded grid a window with no real token is no key (-inf logit) and
     its query row is left out (zero entries in the mean).
     """
     d = q.shape[1]
-    qr = mean_pool(np.asarray(q, np.float64), grid, pool)
-    kr = mean_pool(np.asarray(k, np.float64), grid, pool)
+    qr = mean_pool(np.asarray(q, np.float64), grid, pool, block)
+    kr = mean_pool(np.asarray(k, np.float64), grid, pool, block)
     if bf16_pooled:
         qr, kr = round_bf16(qr), round_bf16(kr)
-    ex = pool_exists(grid, pool)
-    g = 64 // (pool[0] * pool[1] * pool[2])
+    ex = pool_exists(grid, pool, block)
+    g = block // (pool[0] * pool[1] * pool[2])
     nb = qr.shape[0] // g
     rows = np.arange(nb) if rows is None else np.asarray(rows)
     out = np.empty((len(rows), nb))
@@ -175,18 +200,18 @@ def router_scores(q, k, grid, pool=SUB_SHAPE, scale=None, bf16_pooled=False, row
     return out
 
 
-def oracle_block_scores(q, k, grid, scale=None):
+def oracle_block_scores(q, k, grid, scale=None, block=64):
     """P_oracle (Eq.(10)-(11)): token-level softmax, then the mean over each
-    (B x B) tile.  Output rows are cubes in cube-major order.  Pad keys are
+    (B x B) tile.  Output rows are blocks in block order.  Pad keys are
     masked and pad query rows left out (zero entries in the mean)."""
     d = q.shape[1]
-    ok = token_valid(grid)
+    ok = token_valid(grid, block)
     s = np.asarray(q, np.float64) @ np.asarray(k, np.float64).T * _scale(d, scale)
     s[:, ~ok] = -np.inf
     p = _softmax_rows(s)
     p[~ok] = 0.0
-    nb = q.shape[0] // 64
-    return p.reshape(nb, 64, nb, 64).mean(axis=(1, 3))
+    nb = q.shape[0] // block
+    return p.reshape(nb, block, nb, block).mean(axis=(1, 3))
 
 
 # ----------------------------------------------------------------------------
@@ -235,36 +260,36 @@ def csr_to_mask(row_ptr, col_idx, nb):
 # ----------------------------------------------------------------------------
 # fine branch, Eq.(12)
 # ----------------------------------------------------------------------------
-def _tokens_of(cubes):
-    return (np.asarray(cubes)[:, None] * 64 + np.arange(64)[None, :]).reshape(-1)
+def _tokens_of(blocks, block=64):
+    return (np.asarray(blocks)[:, None] * block + np.arange(block)[None, :]).reshape(-1)
 
 
-def fine_forward(q, k, v, mask, scale=None, rows=None, valid=None):
+def fine_forward(q, k, v, mask, scale=None, rows=None, valid=None, block=64):
     """Block-sparse attention of one head (Eq.(12), with the -inf mask of §2.1
-    outside the selected (64 x 64) tiles).
+    outside the selected (B x B) tiles; mask is over blocks).
 
     Returns O_f [L, d] and the natural-log LSE [L].  A query cube with no
     selected KV cube has O_f = 0 and LSE = -inf (the paper does not treat empty
-    rows).  ``rows`` limits the work to some query cubes; other rows are NaN.
+    rows).  ``rows`` limits the work to some query blocks; other rows are NaN.
     ``valid`` [L] marks the real tokens of a padded grid: pad keys are masked,
     pad query rows get O_f = 0 and LSE = -inf.
     """
     q, k, v = (np.asarray(t, np.float64) for t in (q, k, v))
     L, d = q.shape
-    nb = L // 64
+    nb = L // block
     ok = np.ones(L, bool) if valid is None else np.asarray(valid, bool)
     sc = _scale(d, scale)
     o = np.full((L, v.shape[1]), np.nan)
     lse = np.full(L, np.nan)
     for i in (range(nb) if rows is None else rows):
-        sl = slice(64 * i, 64 * i + 64)
+        sl = slice(block * i, block * i + block)
         cols = np.nonzero(mask[i])[0]
         o[sl], lse[sl] = 0.0, -np.inf
         if len(cols) == 0:
             continue
-        qt = _tokens_of([i])
+        qt = _tokens_of([i], block)
         qt = qt[ok[qt]]
-        toks = _tokens_of(cols)
+        toks = _tokens_of(cols, block)
         toks = toks[ok[toks]]
         s = q[qt] @ k[toks].T * sc
         m = s.max(axis=1, keepdims=True)
@@ -275,13 +300,13 @@ def fine_forward(q, k, v, mask, scale=None, rows=None, valid=None):
     return o, lse
 
 
-def fine_backward(q, k, v, mask, d_o, scale=None, valid=None):
+def fine_backward(q, k, v, mask, d_o, scale=None, valid=None, block=64):
     """Gradients of Eq.(12) with the mask held fixed (the router takes no
     gradient, §2.1-§2.2).  Returns dQ, dK, dV [L, d]; with ``valid`` (see
     fine_forward) pad rows take no part and get zero gradients."""
     q, k, v, d_o = (np.asarray(t, np.float64) for t in (q, k, v, d_o))
     L, d = q.shape
-    nb = L // 64
+    nb = L // block
     ok = np.ones(L, bool) if valid is None else np.asarray(valid, bool)
     sc = _scale(d, scale)
     dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
@@ -289,9 +314,9 @@ def fine_backward(q, k, v, mask, d_o, scale=None, valid=None):
         cols = np.nonzero(mask[i])[0]
         if len(cols) == 0:
             continue
-        qt = _tokens_of([i])
+        qt = _tokens_of([i], block)
         qt = qt[ok[qt]]
-        toks = _tokens_of(cols)
+        toks = _tokens_of(cols, block)
         toks = toks[ok[toks]]
         s = q[qt] @ k[toks].T * sc
         p = _softmax_rows(s)                       # [rows, keys]
@@ -307,11 +332,11 @@ def fine_backward(q, k, v, mask, d_o, scale=None, valid=None):
 # ----------------------------------------------------------------------------
 # coarse branch, Eq.(1)-(4), and gated merge, Eq.(13)-(14)
 # ----------------------------------------------------------------------------
-def coarse_forward(q, k, v, grid, scale=None):
-    """Eq.(1)-(3): cube mean-pooling, dense softmax attention over the nb cube
-    tokens.  Returns (O_hat_c [nb, d], lse_c [nb], (q_c, k_c, v_c))."""
+def coarse_forward(q, k, v, grid, scale=None, block=64):
+    """Eq.(1)-(3): block mean-pooling, dense softmax attention over the nb
+    block tokens.  Returns (O_hat_c [nb, d], lse_c [nb], (q_c, k_c, v_c))."""
     d = q.shape[1]
-    qc, kc, vc = (mean_pool(np.asarray(t, np.float64), grid, CUBE_SHAPE) for t in (q, k, v))
+    qc, kc, vc = (block_mean(t, grid, block) for t in (q, k, v))
     s = qc @ kc.T * _scale(d, scale)
     m = s.max(axis=1, keepdims=True)
     z = np.exp(s - m).sum(axis=1, keepdims=True)
@@ -319,9 +344,9 @@ def coarse_forward(q, k, v, grid, scale=None):
     return p @ vc, (m + np.log(z))[:, 0], (qc, kc, vc)
 
 
-def repeat_cubes(oc):
-    """Eq.(4): broadcast each cube row back to its 64 tokens (cube-tiled order)."""
-    return np.repeat(np.asarray(oc, np.float64), 64, axis=0)
+def repeat_cubes(oc, block=64):
+    """Eq.(4): broadcast each block row back to its tokens (cube-tiled order)."""
+    return np.repeat(np.asarray(oc, np.float64), block, axis=0)
 
 
 def gate(x, w_g, valid=None):
@@ -334,12 +359,12 @@ def gate(x, w_g, valid=None):
     return g
 
 
-def merge(g_h, oc_hat, o_f):
+def merge(g_h, oc_hat, o_f, block=64):
     """Eq.(14) for one head: O = G (.) Repeat(O_hat_c) + O_f."""
-    return g_h[:, None] * repeat_cubes(oc_hat) + np.asarray(o_f, np.float64)
+    return g_h[:, None] * repeat_cubes(oc_hat, block) + np.asarray(o_f, np.float64)
 
 
-def gate_backward(x, w_g, oc_hat, d_o, tokens, valid=None):
+def gate_backward(x, w_g, oc_hat, d_o, tokens, valid=None, block=64):
     """Gate part of the backward of Eq.(13)-(14) for some tokens of one batch
     element: with g = tanh(X W_g) and O_c = Repeat(O_hat_c), dL/dg = dO . O_c
     per token and head, dpre = dL/dg (1 - g^2).
@@ -352,7 +377,7 @@ def gate_backward(x, w_g, oc_hat, d_o, tokens, valid=None):
     x = np.asarray(x, np.float64)
     w_g = np.asarray(w_g, np.float64)
     g = gate(x, w_g)
-    cubes = np.asarray(tokens) // 64
+    cubes = np.asarray(tokens) // block
     dg = np.stack([(np.asarray(d_o[h], np.float64) * np.asarray(oc_hat[h], np.float64)[cubes]).sum(axis=1)
                    for h in range(w_g.shape[1])], axis=1)
     dpre = dg * (1.0 - g ** 2)
@@ -361,26 +386,26 @@ def gate_backward(x, w_g, oc_hat, d_o, tokens, valid=None):
     return dpre, dpre @ w_g.T, x.T @ dpre
 
 
-def coarse_gate_backward(q, k, v, grid, x, w_g, d_o, scale=None):
+def coarse_gate_backward(q, k, v, grid, x, w_g, d_o, scale=None, block=64):
     """Gradients of Eq.(1)-(4) and (13)-(14) for one batch element.
 
     q, k, v, d_o: [H, L, d]; x [L, Dm]; w_g [Dm, H].
     Returns (dq_c, dk_c, dv_c [H, nb, d] -- the coarse-branch gradients w.r.t.
     the pooled tensors --, dq, dk, dv [H, L, d] of the coarse branch alone,
     i.e. the pooled gradients spread back with weight 1/n to the n real tokens
-    of each cube (n = 64 without padding), dx [L, Dm], dw_g [Dm, H]).
+    of each block (n = B without padding), dx [L, Dm], dw_g [Dm, H]).
     dO_f = dO because Eq.(14) adds O_f with weight one.
     """
     H, L, d = q.shape
     sc = _scale(d, scale)
-    ok = token_valid(grid)
+    ok = token_valid(grid, block)
     g = gate(x, w_g, ok)                                # [L, H]
     dqc, dkc, dvc, ochat = [], [], [], []
     for h in range(H):
-        oc_hat, lse_c, (qc, kc, vc) = coarse_forward(q[h], k[h], v[h], grid, scale)
+        oc_hat, lse_c, (qc, kc, vc) = coarse_forward(q[h], k[h], v[h], grid, scale, block)
         ochat.append(oc_hat)
         doh = np.asarray(d_o[h], np.float64)
-        doc_hat = (g[:, h, None] * doh).reshape(-1, 64, d).sum(axis=1)   # Repeat^T
+        doc_hat = (g[:, h, None] * doh).reshape(-1, block, d).sum(axis=1)   # Repeat^T
         p = np.exp(qc @ kc.T * sc - lse_c[:, None])
         dvc.append(p.T @ doc_hat)
         dp = doc_hat @ vc.T
@@ -388,53 +413,53 @@ def coarse_gate_backward(q, k, v, grid, x, w_g, d_o, scale=None):
         dqc.append(ds @ kc * sc)
         dkc.append(ds.T @ qc * sc)
     dqc, dkc, dvc = np.stack(dqc), np.stack(dkc), np.stack(dvc)
-    n = ok.reshape(-1, 64).sum(axis=1)                                  # real tokens per cube
-    spread = lambda t: np.repeat(t / n[None, :, None], 64, axis=1) * ok[None, :, None]   # MeanPool^T
-    _, dx, dw = gate_backward(x, w_g, np.stack(ochat), d_o, np.arange(L), ok)
+    n = ok.reshape(-1, block).sum(axis=1)                               # real tokens per block
+    spread = lambda t: np.repeat(t / n[None, :, None], block, axis=1) * ok[None, :, None]   # MeanPool^T
+    _, dx, dw = gate_backward(x, w_g, np.stack(ochat), d_o, np.arange(L), ok, block)
     return dqc, dkc, dvc, spread(dqc), spread(dkc), spread(dvc), dx, dw
 
 
 # ----------------------------------------------------------------------------
 # the whole layer
 # ----------------------------------------------------------------------------
-def vsa2_forward(q, k, v, grid, topk, x, w_g, scale=None, bf16_pooled=False, mask=None):
+def vsa2_forward(q, k, v, grid, topk, x, w_g, scale=None, bf16_pooled=False, mask=None, block=64):
     """One batch element, all heads: router -> TopK -> fine + coarse -> merge.
 
     q, k, v: [H, L, d]; x [L, Dm]; w_g [Dm, H].  ``mask`` [H, nb, nb] skips the
     router and uses a given selection.  Returns a dict of every intermediate.
     """
     H = q.shape[0]
-    ok = token_valid(grid)
+    ok = token_valid(grid, block)
     g = gate(x, w_g, ok)
     res = {"scores": [], "mask": [], "o_f": [], "lse": [], "oc_hat": [], "lse_c": [], "o": [], "g": g}
     for h in range(H):
         if mask is None:
-            p_r = router_scores(q[h], k[h], grid, scale=scale, bf16_pooled=bf16_pooled)
+            p_r = router_scores(q[h], k[h], grid, scale=scale, bf16_pooled=bf16_pooled, block=block)
             m = topk_per_sequence(p_r, topk)[0]
             res["scores"].append(p_r)
         else:
             m = mask[h]
-        o_f, lse = fine_forward(q[h], k[h], v[h], m, scale, valid=ok)
-        oc_hat, lse_c, _ = coarse_forward(q[h], k[h], v[h], grid, scale)
+        o_f, lse = fine_forward(q[h], k[h], v[h], m, scale, valid=ok, block=block)
+        oc_hat, lse_c, _ = coarse_forward(q[h], k[h], v[h], grid, scale, block)
         res["mask"].append(m)
         res["o_f"].append(o_f)
         res["lse"].append(lse)
         res["oc_hat"].append(oc_hat)
         res["lse_c"].append(lse_c)
-        res["o"].append(merge(g[:, h], oc_hat, o_f))
+        res["o"].append(merge(g[:, h], oc_hat, o_f, block))
     return {n: (np.stack(t) if isinstance(t, list) and t else t) for n, t in res.items()}
 
 
-def vsa2_backward(q, k, v, grid, mask, x, w_g, d_o, scale=None):
+def vsa2_backward(q, k, v, grid, mask, x, w_g, d_o, scale=None, block=64):
     """Gradients of the whole layer (router excluded) for one batch element.
     Returns dq, dk, dv [H, L, d], dx [L, Dm], dw_g [Dm, H]."""
     H = q.shape[0]
-    ok = token_valid(grid)
+    ok = token_valid(grid, block)
     dq, dk, dv = [], [], []
     for h in range(H):
-        a, b, c = fine_backward(q[h], k[h], v[h], mask[h], d_o[h], scale, valid=ok)
+        a, b, c = fine_backward(q[h], k[h], v[h], mask[h], d_o[h], scale, valid=ok, block=block)
         dq.append(a); dk.append(b); dv.append(c)
-    _, _, _, cq, ck, cv, dx, dw = coarse_gate_backward(q, k, v, grid, x, w_g, d_o, scale)
+    _, _, _, cq, ck, cv, dx, dw = coarse_gate_backward(q, k, v, grid, x, w_g, d_o, scale, block)
     return np.stack(dq) + cq, np.stack(dk) + ck, np.stack(dv) + cv, dx, dw
 
 

@@ -497,3 +497,129 @@ def test_pad_values_never_reach_an_output():
         outs.append([f["scores"], f["mask"], f["o_f"], f["lse"], f["o"], f["g"], *b])
     for a, b in zip(*outs):
         assert np.array_equal(a, b)
+
+
+# ----------------------------------------------------------------------------- 128-token blocks
+# B = 128 (the blog's inferred setting; the paper gives no 3D cut): a block is
+# two x-adjacent 4x4x4 cubes (4x4x8), contiguous in the cube-tiled order.
+def test_block128_layout_and_padding():
+    grid = (4, 8, 16)
+    c = orc.token_coords(grid, 128)
+    blk = c.reshape(-1, 128, 3)
+    lo, hi = blk.min(axis=1), blk.max(axis=1)
+    assert np.all(hi - lo == [3, 3, 7]) and np.all(lo % [4, 4, 8] == 0)
+    ids = (lo[:, 0] // 4 * 2 + lo[:, 1] // 4) * 2 + lo[:, 2] // 8          # raster over the (T/4, Y/4, X/8) grid
+    assert np.array_equal(ids, np.arange(len(ids)))
+    assert orc.padded_grid((5, 6, 9), 128) == (8, 8, 16) and orc.padded_grid((5, 6, 9)) == (8, 8, 12)
+    ok = orc.token_valid((5, 6, 9), 128)
+    assert ok.sum() == 270 and np.array_equal(ok, tile_permutation((5, 6, 9), block=128).numpy() >= 0)
+
+
+def test_block128_router_r1_and_pair_means():
+    grid = (4, 8, 16)
+    q, k = _rand(512, 16), _rand(512, 16)
+    got = orc.router_scores(q, k, grid, pool=(1, 1, 1), block=128)
+    p = torch.softmax(torch.tensor(q) @ torch.tensor(k).T * 0.25, dim=-1)
+    want = torch.nn.functional.avg_pool2d(p[None, None], 128)[0, 0].numpy()   # Eq.(10)-(11) with B = 128
+    np.testing.assert_allclose(got, want, rtol=1e-11, atol=1e-16)
+    np.testing.assert_allclose(orc.oracle_block_scores(q, k, grid, block=128), want, rtol=1e-11, atol=1e-16)
+    p128 = orc.router_scores(q, k, grid, block=128)
+    np.testing.assert_allclose(p128.sum(axis=1), 1.0 / 16.0, rtol=1e-12)          # G = 16
+    # a 16 x 16 mean is the mean of the four 8 x 8 means of its cube pairs
+    p64 = orc.router_scores(q, k, grid)
+    np.testing.assert_allclose(p128, p64.reshape(4, 2, 4, 2).mean(axis=(1, 3)), rtol=1e-12)
+
+
+def test_block128_fine_branch_against_dense():
+    q, k, v, d_o = (_rand(512, 8) for _ in range(4))
+    mask = np.array([[1, 0, 1, 0], [0, 0, 0, 0], [1, 1, 0, 1], [0, 0, 0, 1]], dtype=bool)
+    keep = np.kron(mask, np.ones((128, 128), dtype=bool))
+    o, lse = orc.fine_forward(q, k, v, mask, block=128)
+    live = keep.any(axis=1)
+    np.testing.assert_allclose(o[live], _sdpa(q, k, v, keep, 1 / np.sqrt(8))[live], rtol=1e-12, atol=1e-13)
+    assert np.all(o[~live] == 0) and np.all(np.isneginf(lse[~live]))
+    got = orc.fine_backward(q, k, v, mask, d_o, block=128)
+    t = [torch.tensor(a, requires_grad=True) for a in (q, k, v)]
+    s = (t[0] @ t[1].T / np.sqrt(8)).masked_fill(~torch.tensor(keep), -np.inf)
+    (torch.softmax(s, -1).nan_to_num(0.0) @ t[2] * torch.tensor(d_o)).sum().backward()
+    for g, w in zip(got, t):
+        np.testing.assert_allclose(g, w.grad.numpy(), rtol=1e-10, atol=1e-12)
+
+
+PGRID128 = (5, 6, 9)         # padded to 8 x 8 x 16: 1024 slots, 270 tokens, 8 blocks; the last
+                             # cube along x (x = 12..15) is all padding
+
+
+def _raster_block_ids(grid):
+    c = _raster_coords(grid) // np.array([4, 4, 8])
+    ny, nx = -(-grid[1] // 4), -(-grid[2] // 8)
+    return (c[:, 0] * ny + c[:, 1]) * nx + c[:, 2]
+
+
+def _padded128(fields):
+    perm = tile_permutation(PGRID128, block=128).numpy()
+    real = perm >= 0
+    out = []
+    for f in fields:
+        o = 7.0 + 5.0 * rng.standard_normal((len(perm),) + f.shape[1:])
+        o[real] = f[perm[real]]
+        out.append(o)
+    return out, perm, real
+
+
+def test_block128_padded_router_brute_force():
+    qn, kn = _rand(270, 8), _rand(270, 8)
+    (q, k), perm, real = _padded128([qn, kn])
+    assert (~real).reshape(-1, 64).all(axis=1).any()                   # a cube with no real token
+    sub = _raster_coords(PGRID128) // 2
+    keys, inv = np.unique(sub, axis=0, return_inverse=True)
+    inv = inv.ravel()
+    qr = np.stack([qn[inv == a].mean(axis=0) for a in range(len(keys))])
+    kr = np.stack([kn[inv == a].mean(axis=0) for a in range(len(keys))])
+    p = torch.softmax(torch.tensor(qr @ kr.T) / np.sqrt(8), -1).numpy()
+    wb = keys // np.array([2, 2, 4])                                   # window -> block coords
+    wblk = (wb[:, 0] * 2 + wb[:, 1]) * 2 + wb[:, 2]
+    want = np.zeros((8, 8))
+    np.add.at(want, (wblk[:, None].repeat(len(keys), 1), wblk[None, :].repeat(len(keys), 0)), p)
+    want /= 256.0
+    np.testing.assert_allclose(orc.router_scores(q, k, PGRID128, block=128), want, rtol=1e-11, atol=1e-17)
+
+
+def test_block128_padded_fine_and_coarse_autograd():
+    H, d, dm = 2, 6, 10
+    fields = [_rand(270, H * d) for _ in range(4)] + [_rand(270, dm)]
+    (q, k, v, d_o, x), perm, real = _padded128(fields)
+    split = lambda a: a.reshape(-1, H, d).transpose(1, 0, 2).copy()
+    q, k, v, d_o = (split(a) for a in (q, k, v, d_o))
+    w_g = _rand(dm, H) * 0.4
+    blk = _raster_block_ids(PGRID128)
+    order = np.argsort(perm[real])
+    # fine branch: masked dense attention in raster order, pad tokens absent
+    mask = rng.random((8, 8)) < 0.5
+    mask[2] = False
+    mask[0, 0] = True
+    keep = mask[blk[:, None], blk[None, :]]
+    o, _ = orc.fine_forward(q[0], k[0], v[0], mask, valid=real, block=128)
+    live = keep.any(axis=1)
+    want = _sdpa(split(fields[0])[0], split(fields[1])[0], split(fields[2])[0], keep, 1 / np.sqrt(d))
+    np.testing.assert_allclose(o[real][order][live], want[live], rtol=1e-12, atol=1e-13)
+    assert np.all(o[~real] == 0)
+    # coarse branch + gate: block means over the real tokens of each 4x4x8 region
+    got = orc.coarse_gate_backward(q, k, v, PGRID128, x, w_g, d_o, block=128)
+    bt = torch.tensor(blk)
+    n = torch.bincount(bt, minlength=8).double()
+    tq, tk, tv = (torch.tensor(split(f), requires_grad=True) for f in fields[:3])
+    tx, tw = torch.tensor(fields[4], requires_grad=True), torch.tensor(w_g, requires_grad=True)
+    mean = lambda t: torch.zeros(H, 8, d, dtype=torch.float64).index_add(1, bt, t) / n[None, :, None]
+    oc = torch.softmax(mean(tq) @ mean(tk).transpose(1, 2) / np.sqrt(d), -1) @ mean(tv)
+    g = torch.tanh(tx @ tw)
+    (g.T[:, :, None] * oc[:, bt] * torch.tensor(split(fields[3]))).sum().backward()
+    for g_, w_ in zip(got[3:6], (tq, tk, tv)):
+        np.testing.assert_allclose(g_[:, real][:, order], w_.grad.numpy(), rtol=1e-10, atol=1e-12)
+        assert np.all(g_[:, ~real] == 0)
+    np.testing.assert_allclose(got[6][real][order], tx.grad.numpy(), rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(got[7], tw.grad.numpy(), rtol=1e-10, atol=1e-12)
+    res = orc.vsa2_forward(q, k, v, PGRID128, 3, x, w_g, block=128)
+    np.testing.assert_allclose(res["oc_hat"], oc.detach().numpy(), rtol=1e-12)
+    assert res["mask"].shape == (H, 8, 8) and res["mask"].sum() == H * 24
+    assert np.all(res["o"][:, ~real] == 0)

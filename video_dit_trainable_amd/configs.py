@@ -31,12 +31,14 @@ class Workload:
     skew: bool = False     # heavy-tailed per-query-cube scale
     train: bool = False    # forward + backward
     extra_topk: tuple = field(default_factory=tuple)
+    block: int = 64        # attention block: 64 (a 4x4x4 cube) or 128 (4x4x8, two x-adjacent cubes)
 
     @property
     def pgrid(self):
-        """The grid padded up to whole 4x4x4 cubes along each axis (§2.2
+        """The grid padded up to whole attention blocks along each axis (§2.2
         "Kernel Implementation"); equal to ``grid`` when it divides."""
-        return tuple(-(-n // 4) * 4 for n in self.grid)
+        mult = (4, 4, 4 * (self.block // CUBE))
+        return tuple(-(-n // m) * m for n, m in zip(self.grid, mult))
 
     @property
     def padded(self):
@@ -56,7 +58,14 @@ class Workload:
 
     @property
     def nb(self):
+        """4x4x4 cubes per (batch, head)."""
         return self.L // CUBE
+
+    @property
+    def nblk(self):
+        """Attention blocks per (batch, head): the rows and columns of the
+        router scores and of the selection."""
+        return self.L // self.block
 
     @property
     def d_model(self):
@@ -64,7 +73,7 @@ class Workload:
 
     def budget(self, topk=None):
         k = self.topk if topk is None else topk
-        return min(self.nb * k, self.nb * self.nb)
+        return min(self.nblk * k, self.nblk * self.nblk)
 
 
 WORKLOADS = {

@@ -50,11 +50,12 @@ def _gen(seed: int, device) -> torch.Generator:
     return g
 
 
-def tile_permutation(grid, device="cpu") -> torch.Tensor:
+def tile_permutation(grid, device="cpu", block=64) -> torch.Tensor:
     """perm[j] = raster index (t*Y + y)*X + x of the token stored at tiled slot
-    j of the grid padded up to whole cubes, or -1 where slot j is padding."""
+    j of the grid padded up to whole blocks (x to a multiple of 8 for
+    128-token blocks), or -1 where slot j is padding."""
     T, Y, X = grid
-    Tp, Yp, Xp = (-(-n // 4) * 4 for n in grid)
+    Tp, Yp, Xp = (-(-n // m) * m for n, m in zip(grid, (4, 4, 4 * (block // 64))))
     L = Tp * Yp * Xp
     j = torch.arange(L, device=device, dtype=torch.int64)
     c, s, u = j // 64, (j // 8) % 8, j % 8
@@ -125,7 +126,7 @@ def make_qkv(w: Workload, device="cpu", heads=None):
     """
     heads = list(range(w.heads)) if heads is None else list(heads)
     L, d = w.L, w.head_dim
-    perm = tile_permutation(w.grid, device)
+    perm = tile_permutation(w.grid, device, w.block)
     dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     out = {n: torch.empty((w.batch, len(heads), L, d), dtype=dt, device=device) for n in "qkv"}
     for b in range(w.batch):
@@ -186,7 +187,7 @@ def make_selection(w: Workload, topk=None, device="cpu", seed_offset=0):
     a row are a random subset.  Used to drive the sparse attention with a fixed,
     externally chosen mask.  Returns (row_ptr [B,H,nb+1], col_idx [B,H,k]) int32.
     """
-    nb = w.nb
+    nb = w.nblk
     k = w.budget(topk)
     bh = w.batch * w.heads
     row_ptr = torch.empty((bh, nb + 1), dtype=torch.int32)
