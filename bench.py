@@ -58,19 +58,19 @@ def cpu_baseline(w, q, k, v, d_o, budget_s=20.0):
 
     f64 = lambda t: t.float().cpu().double().numpy()
     qh, kh, vh, doh = f64(q[0, 0]), f64(k[0, 0]), f64(v[0, 0]), f64(d_o[0, 0])
-    real = orc.token_valid(w.grid)
+    real = orc.token_valid(w.grid, w.block)
     lr = w.L // 8
-    order = np.random.default_rng(0).permutation(w.nb)
+    order = np.random.default_rng(0).permutation(w.nblk)
     n_router, t_router = 0, 0.0
-    while t_router < budget_s / 2 and n_router < w.nb:
+    while t_router < budget_s / 2 and n_router < w.nblk:
         rows = np.sort(order[n_router:n_router + 32])
         t0 = time.perf_counter()
-        orc.router_scores(qh, kh, w.grid, bf16_pooled=True, rows=rows)
+        orc.router_scores(qh, kh, w.grid, bf16_pooled=True, rows=rows, block=w.block)
         t_router += time.perf_counter() - t0
         n_router += len(rows)
-    fl = n_router * 8 * 2 * 2 * lr * w.head_dim
+    fl = n_router * (w.block // 8) * 2 * 2 * lr * w.head_dim
     rp, ci = make_selection(w)
-    mask = orc.csr_to_mask(rp[0, 0].numpy(), ci[0, 0].numpy(), w.nb)
+    mask = orc.csr_to_mask(rp[0, 0].numpy(), ci[0, 0].numpy(), w.nblk)
     live = [int(i) for i in order if mask[i].any()]
     n_fine, pairs, t_fine = 0, 0, 0.0
     while t_fine < budget_s / 2 and n_fine < len(live):
@@ -78,17 +78,18 @@ def cpu_baseline(w, q, k, v, d_o, budget_s=20.0):
         sub = np.zeros_like(mask)
         sub[cubes] = mask[cubes]
         t0 = time.perf_counter()
-        orc.fine_forward(qh, kh, vh, sub, rows=cubes, valid=real)
-        orc.fine_backward(qh, kh, vh, sub, doh, valid=real)
+        orc.fine_forward(qh, kh, vh, sub, rows=cubes, valid=real, block=w.block)
+        orc.fine_backward(qh, kh, vh, sub, doh, valid=real, block=w.block)
         t_fine += time.perf_counter() - t0
         n_fine += len(cubes)
         pairs += int(sub.sum())
-    fl += pairs * 4 * 64 * 64 * w.head_dim * 7 // 2
+    fl += pairs * 4 * w.block * w.block * w.head_dim * 7 // 2
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    unit = "cubes" if w.block == 64 else "128-token blocks"
     secs = t_router + t_fine
     return {"value": fl / secs / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"head 0 of the same inputs: router rows of {n_router} query cubes ({t_router:.1f} s) + "
-                      f"fine fwd+bwd of {n_fine} query cubes, {pairs} selected pairs ({t_fine:.1f} s); fp64 numpy",
+            "sample": f"head 0 of the same inputs: router rows of {n_router} query {unit} ({t_router:.1f} s) + "
+                      f"fine fwd+bwd of {n_fine} query {unit}, {pairs} selected pairs ({t_fine:.1f} s); fp64 numpy",
             "seconds": round(secs, 2)}
 
 
@@ -102,8 +103,9 @@ def describe(w):
     what = ("full forward + backward of router, TopK, fine, coarse and gate" if w.train
             else "forward of router, TopK, fine, coarse and gate")
     skew = ", skewed query-cube scales" if w.skew else ""
+    blocks = "4x4x4 cubes" if w.block == 64 else "128-token blocks of 4x4x8 (two cubes)"
     return (f"{'720p training' if w.name.startswith('train720') else w.name} shape: {grid}, B={w.batch}, "
-            f"{w.heads} heads, d={w.head_dim}, {w.dtype}, router pool 2x2x2, 4x4x4 cubes, per-sequence "
+            f"{w.heads} heads, d={w.head_dim}, {w.dtype}, router pool 2x2x2, {blocks}, per-sequence "
             f"top{w.topk}{skew}; {what}")
 
 
@@ -161,7 +163,7 @@ def main():
     q, k, v = make_qkv(w, device=dev)
     d_o = make_grad_out(w, device=dev)
     x, w_g = make_gate_inputs(w, device=dev, zero_gate=False)
-    p = vsa2.problem(w.batch, w.heads, w.head_dim, w.grid, w.dtype)
+    p = vsa2.problem(w.batch, w.heads, w.head_dim, w.grid, w.dtype, block=w.block)
     layer = vsa2.Layer(p, w.topk, w.d_model, device=dev)
     torch.cuda.synchronize()
 
@@ -265,7 +267,7 @@ def main():
     for n, key in (("fine_fwd", "fine_fwd"), ("fine_bwd", "fine_bwd"), ("route", "router")):
         ops[n]["tflops"] = round(fl[key] / (per[n] * 1e-3) / 1e12, 2)
         ops[n]["pct_bf16_peak"] = round(100 * fl[key] / (per[n] * 1e-3) / PEAK_BF16, 2)
-    nbytes_scores = w.batch * w.heads * w.nb * w.nb * 4
+    nbytes_scores = w.batch * w.heads * w.nblk * w.nblk * 4
     ops["topk"]["gbps_scores_pass"] = round(nbytes_scores / (per["topk"] * 1e-3) / 1e9, 1)
 
     if args.copy_calibration:

@@ -18,16 +18,21 @@
  *    2x2x2 sub-cubes follow in raster order, each holding its 8 tokens in
  *    raster order.  Router pooling windows are therefore the contiguous groups
  *    of 8 tokens and the attention blocks the contiguous groups of 64.
- *  - Block size B = 64 (4x4x4) and router pool R = 8 (2x2x2), so G = 8.
+ *  - Attention block B = 64 (one 4x4x4 cube) by default, router pool R = 8
+ *    (2x2x2), so G = 8.  With block_tokens = 128 a block is two x-adjacent
+ *    cubes (4x4x8), contiguous in the order above (cubes 2m, 2m+1), G = 16;
+ *    blocks are numbered like these cube pairs.  B = 128 is the blog's
+ *    inference for the paper's own runs (its §07); the paper gives no 3D cut.
+ *    "nb" below counts blocks: nb = L / B.
  *  - Padded grids (§2.2 "Kernel Implementation"): a latent side that is not a
- *    multiple of 4 is padded up to one, and every tensor holds the padded
- *    grid: L = 64 nb with nb = ceil(T/4) ceil(Y/4) ceil(X/4), in the order
- *    above.  Pad slots are not tokens.  Their input values are never read into
+ *    multiple of the block's side (4, and 8 along x for B = 128) is padded up
+ *    to one, and every tensor holds the padded grid: L = B nb slots with
+ *    nb = ceil(T/4) ceil(Y/4) ceil(X/(B/16)), in the order above.  Pad slots are not tokens.  Their input values are never read into
  *    a result (they must be finite); pad rows of O_f, O, G, dQ, dK, dV and dX
  *    are written as 0 and their LSE as -inf.  Pooling windows average their
  *    real tokens; a 2x2x2 window holding none is no router key and adds no
- *    router row; the coarse gradient of a cube goes to its n real tokens as
- *    1/n each (1/64 without padding).
+ *    router row; the coarse gradient of a block goes to its n real tokens as
+ *    1/n each (1/B without padding).
  *  - `stream` is a hipStream_t (NULL = the default stream).  Every call only
  *    enqueues work on it and returns without synchronising.
  *  - Errors: argument and shape errors are reported before anything is
@@ -73,9 +78,10 @@ typedef struct vsa2_problem {
   int32_t batch;          /* >= 1                                                     */
   int32_t heads;          /* >= 1 (multi-head attention: as many K/V heads as Q heads)*/
   int32_t head_dim;       /* d: 64 or 128                                             */
-  int32_t lat_t, lat_y, lat_x; /* latent grid, each >= 1; padded up to multiples of 4 */
+  int32_t lat_t, lat_y, lat_x; /* latent grid, each >= 1; padded up to whole blocks   */
   int32_t dtype;          /* vsa2_dtype of Q, K, V, O_f, O, dO, dQ, dK, dV, X, dX     */
   float softmax_scale;    /* <= 0 selects 1/sqrt(head_dim)                            */
+  int32_t block_tokens;   /* attention block B: 64 (0 selects it) or 128, see above   */
 } vsa2_problem;
 
 /* Human-readable name of a status code (static string). */

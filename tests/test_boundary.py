@@ -22,9 +22,10 @@ def _declared():
 
 
 def _prob(**kw):
-    base = dict(batch=1, heads=2, head_dim=64, grid=(8, 16, 16), dtype="f32")
+    base = dict(batch=1, heads=2, head_dim=64, grid=(8, 16, 16), dtype="f32", block=64)
     base.update(kw)
-    return vsa2.problem(base["batch"], base["heads"], base["head_dim"], base["grid"], base["dtype"])
+    return vsa2.problem(base["batch"], base["heads"], base["head_dim"], base["grid"], base["dtype"],
+                        block=base["block"])
 
 
 def test_every_declared_symbol_is_exported():
@@ -78,7 +79,21 @@ def test_padded_grid_sizes():
     assert vsa2.budget(_prob(grid=(1, 1, 1)), 3) == 1        # one cube holding a single token
 
 
+def test_block128_sizes():
+    # 128-token blocks (two x-adjacent cubes): nb counts blocks, x pads to a multiple of 8
+    p = _prob(block=128)                                    # 8x16x16: 32 cubes, 16 blocks
+    assert vsa2.budget(p, 4) == 16 * 4 and vsa2.budget(p, 100) == 16 * 16
+    L, nb, nbp = 2048, 16, 64
+    assert vsa2.pooled_size(p) == 2 * (2 * (L // 8) + 3 * nbp) * 64 * 4
+    assert vsa2.saved_size(p) == (2 * nb * 64 + 2 * nb + 2 * L) * 4
+    q = _prob(grid=(8, 16, 12), block=128)                  # x padded to 16: same slots as 8x16x16
+    assert vsa2.budget(q, 4) == 16 * 4 and vsa2.saved_size(q) == vsa2.saved_size(p)
+    assert vsa2.budget(_prob(grid=(8, 16, 12)), 4) == 24 * 4  # with 64-token blocks 12 needs no padding
+    assert vsa2.workspace_size(p, vsa2.OP_COARSE_BWD, 8, 128) > vsa2.workspace_size(_prob(), vsa2.OP_COARSE_BWD, 8, 128)
+
+
 @pytest.mark.parametrize("kw,code", [
+    (dict(block=96), vsa2.VSA2_E_SHAPE),
     (dict(head_dim=96), vsa2.VSA2_E_SHAPE),
     (dict(grid=(8, 16, 0)), vsa2.VSA2_E_SHAPE),
     (dict(grid=(-4, 16, 16)), vsa2.VSA2_E_SHAPE),

@@ -87,6 +87,10 @@ WORKLOADS = {
         # the 720p training problem on a grid one short of whole cubes along
         # every axis: padded to the same 44 x 48 x 104 slots (3.5% pad slots)
         Workload("train720pad", 6, (43, 47, 103), 1, 20, 128, "bf16", 64, "lowrank", skew=True, train=True),
+        # the 720p training problem with 128-token blocks (4x4x8, two
+        # x-adjacent cubes; G = 16): the blog's inferred setting, top64
+        Workload("train720b128", 7, (44, 48, 104), 1, 20, 128, "bf16", 64, "lowrank", skew=True, train=True,
+                 block=128),
     ]
 }
 
@@ -94,22 +98,22 @@ WORKLOADS = {
 def flops(w: Workload, topk=None):
     """Algorithmic FLOPs of one call of each op, counting selected blocks only.
 
-    Fine branch: 4 * 64^2 * d per selected pair forward (QK^T and PV), 2.5x that
-    backward (five 64x64xd GEMMs).  Router: two pooled GEMMs (LSE pass and score
-    pass), each 2 * (L/8)^2 * d, as in the paper's App. B cost model.  Coarse:
-    dense attention over nb pooled tokens, 4 * nb^2 * d forward.
+    Fine branch: 4 * B^2 * d per selected block pair forward (QK^T and PV),
+    2.5x that backward (five BxBxd GEMMs).  Router: two pooled GEMMs (LSE pass
+    and score pass), each 2 * (L/8)^2 * d, as in the paper's App. B cost model.
+    Coarse: dense attention over the nb block tokens, 4 * nb^2 * d forward.
     """
     k = w.budget(topk)
     bh = w.batch * w.heads
     d = w.head_dim
     lr = w.L // SUB
-    pair = 4 * CUBE * CUBE * d
+    pair = 4 * w.block * w.block * d
     return {
         "fine_fwd": bh * k * pair,
         "fine_bwd": bh * k * pair * 5 // 2,
         "router": bh * 2 * 2 * lr * lr * d,
-        "coarse_fwd": bh * 4 * w.nb * w.nb * d,
-        "coarse_bwd": bh * 10 * w.nb * w.nb * d,
+        "coarse_fwd": bh * 4 * w.nblk * w.nblk * d,
+        "coarse_bwd": bh * 10 * w.nblk * w.nblk * d,
         "gate_fwd": 2 * w.batch * w.L * w.d_model * w.heads,
         "gate_bwd": 4 * w.batch * w.L * w.d_model * w.heads,
     }
@@ -118,17 +122,17 @@ def flops(w: Workload, topk=None):
 def kernel_flops(w: Workload, topk=None):
     """Algorithmic FLOPs credited to each timed kernel of one call.
 
-    The fine backward's five GEMMs per selected pair are split between its two
-    kernels: the dK/dV kernel computes S^T, dP^T, dV and dK (four of them, 8 *
-    64^2 * d); the dQ kernel is credited with the dQ GEMM only (2 * 64^2 * d),
-    its recomputation of S and dP is not counted.  Each router pass is one
-    pooled GEMM of 2 * (L/8)^2 * d per (batch, head).
+    The fine backward's five GEMMs per selected block pair are split between
+    its two kernels: the dK/dV kernel computes S^T, dP^T, dV and dK (four of
+    them, 8 * B^2 * d); the dQ kernel is credited with the dQ GEMM only
+    (2 * B^2 * d), its recomputation of S and dP is not counted.  Each router
+    pass is one pooled GEMM of 2 * (L/8)^2 * d per (batch, head).
     """
     k = w.budget(topk)
     bh = w.batch * w.heads
     d = w.head_dim
     lr = w.L // SUB
-    gemm = 2 * CUBE * CUBE * d
+    gemm = 2 * w.block * w.block * d
     return {
         "fine_fwd": bh * k * 2 * gemm,
         "bwd_dkdv": bh * k * 4 * gemm,
@@ -141,26 +145,26 @@ def kernel_flops(w: Workload, topk=None):
 def kernel_bytes(w: Workload, topk=None):
     """Algorithmic HBM bytes of one launch of each timed kernel.
 
-    The fine kernels gather one 64-row tile of two operands per selected pair
-    with no reuse assumed (K and V for the forward and the dQ kernel, Q and dO
-    plus the 64 rows' (lse, delta) pairs for the dK/dV kernel), plus the index
-    entry, and read or write the per-token tensors that stay with the block
-    once.  The dK/dV and dQ kernels also read the coarse branch's per-cube
-    gradient rows.  A router pass reads the pooled Q_r and K_r once and writes
+    The fine kernels gather one B-row tile of two operands per selected block
+    pair with no reuse assumed (K and V for the forward and the dQ kernel, Q
+    and dO plus the B rows' (lse, delta) pairs for the dK/dV kernel), plus the
+    index entry, and read or write the per-token tensors that stay with the
+    block once.  The dK/dV and dQ kernels also read the coarse branch's
+    per-block gradient rows.  A router pass reads the pooled Q_r and K_r once and writes
     the per-row LSE; the score pass also writes the nb x nb cube scores.
     """
     k = w.budget(topk)
     bh = w.batch * w.heads
     d = w.head_dim
     esz = 2 if w.dtype == "bf16" else 4
-    tile = CUBE * d * esz
+    tile = w.block * d * esz
     tok = w.L * d * esz          # one per-token tensor of one (batch, head)
-    ptr = (w.nb + 1) * 4
+    ptr = (w.nblk + 1) * 4
     lr = w.L // SUB
     return {
         "fine_fwd": bh * (k * (2 * tile + 4) + 2 * tok + w.L * 4 + ptr),
-        "bwd_dkdv": bh * (k * (2 * tile + CUBE * 8 + 4) + 4 * tok + 2 * w.nb * d * 4 + ptr),
-        "bwd_dq": bh * (k * (2 * tile + 4) + 3 * tok + w.L * 8 + w.nb * d * 4 + ptr),
+        "bwd_dkdv": bh * (k * (2 * tile + w.block * 8 + 4) + 4 * tok + 2 * w.nblk * d * 4 + ptr),
+        "bwd_dq": bh * (k * (2 * tile + 4) + 3 * tok + w.L * 8 + w.nblk * d * 4 + ptr),
         "router_lse": bh * (2 * lr * d * esz + lr * 4),
-        "router_scores": bh * (2 * lr * d * esz + lr * 4 + w.nb * w.nb * 4),
+        "router_scores": bh * (2 * lr * d * esz + lr * 4 + w.nblk * w.nblk * 4),
     }

@@ -15,8 +15,12 @@ constexpr size_t ALIGN = 256;
 
 size_t up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
 
+// nb counts attention blocks (the rows and columns of the router scores and
+// of the selection, the coarse tokens), nc the 4x4x4 cubes the kernels tile
+// over; nb = nc >> bs with 2^bs cubes per block.
 struct Dims {
   int batch, heads, bh, d, L, nb, nbp, Lr;
+  int nc, bs;
   bool bf16;
   size_t esz;
   float scale;
@@ -30,11 +34,15 @@ int check_problem(const vsa2_problem* p, Dims& o) {
   if (p->lat_t < 1 || p->lat_y < 1 || p->lat_x < 1) return VSA2_E_SHAPE;
   if (p->lat_t > (1 << 20) || p->lat_y > (1 << 20) || p->lat_x > (1 << 20)) return VSA2_E_SHAPE;
   if (p->dtype != VSA2_F32 && p->dtype != VSA2_BF16) return VSA2_E_ARG;
-  // a grid that is not a whole number of 4x4x4 cubes is padded up to one
-  const int64_t nt = (p->lat_t + 3) / 4, ny = (p->lat_y + 3) / 4, nx = (p->lat_x + 3) / 4;
-  const int64_t nb = nt * ny * nx;
-  const int64_t L = 64 * nb;
-  if (nb > 46340) return VSA2_E_SHAPE;  // nb^2 and all indices fit int32
+  if (p->block_tokens != 0 && p->block_tokens != 64 && p->block_tokens != 128) return VSA2_E_SHAPE;
+  const int bs = p->block_tokens == 128 ? 1 : 0;  // a 128-token block is two x-adjacent cubes
+  // a grid that is not a whole number of blocks is padded up to one
+  const int64_t xs = 4 << bs;
+  const int64_t nt = (p->lat_t + 3) / 4, ny = (p->lat_y + 3) / 4, nx = (p->lat_x + xs - 1) / xs << bs;
+  const int64_t nc = nt * ny * nx;
+  const int64_t L = 64 * nc;
+  if (nc > 46340) return VSA2_E_SHAPE;  // nc^2 and all indices fit int32
+  const int64_t nb = nc >> bs;
   if ((int64_t)p->batch * p->heads > (1 << 20)) return VSA2_E_SHAPE;
   if (std::isnan(p->softmax_scale) || std::isinf(p->softmax_scale)) return VSA2_E_ARG;
   o.batch = p->batch;
@@ -44,17 +52,19 @@ int check_problem(const vsa2_problem* p, Dims& o) {
   o.L = (int)L;
   o.nb = (int)nb;
   o.nbp = (int)((nb + 63) / 64 * 64);
+  o.nc = (int)nc;
+  o.bs = bs;
   o.Lr = (int)(L / 8);
   o.bf16 = p->dtype == VSA2_BF16;
   o.esz = o.bf16 ? 2 : 4;
   o.scale = p->softmax_scale > 0.f ? p->softmax_scale : 1.0f / std::sqrt((float)p->head_dim);
-  o.pad.on = (p->lat_t % 4) || (p->lat_y % 4) || (p->lat_x % 4);
+  o.pad.on = (p->lat_t % 4) || (p->lat_y % 4) || (p->lat_x % xs);
   o.pad.nt = (int)nt;
   o.pad.ny = (int)ny;
   o.pad.nx = (int)nx;
-  o.pad.et = p->lat_t - 4 * (int)(nt - 1);
-  o.pad.ey = p->lat_y - 4 * (int)(ny - 1);
-  o.pad.ex = p->lat_x - 4 * (int)(nx - 1);
+  o.pad.rt = p->lat_t;
+  o.pad.ry = p->lat_y;
+  o.pad.rx = p->lat_x;
   o.pad.inv_nx = (float)(1.0 / (double)nx);
   o.pad.inv_nyx = (float)(1.0 / (double)(ny * nx));
   return VSA2_OK;
@@ -134,6 +144,7 @@ struct CoarseBwdWs {
   void* doc;
   float* stats_c;
   float* dw_part;
+  float* doc_part;  // 128-token blocks: per-cube sums of dO_hat_c
 };
 
 size_t ws_coarse_bwd(const Dims& d, int dm, CoarseBwdWs* w, void* base) {
@@ -148,6 +159,7 @@ size_t ws_coarse_bwd(const Dims& d, int dm, CoarseBwdWs* w, void* base) {
   const size_t o_doc = take((size_t)d.bh * d.nbp * d.d * d.esz);
   const size_t o_dc = take((size_t)d.bh * d.nbp * 8);
   const size_t o_dw = take((size_t)d.batch * nchunk_of(d) * dm * d.heads * 4);
+  const size_t o_dp = take(d.bs ? (size_t)d.bh * d.nc * d.d * 4 : 0);
   if (w) {
     char* b = (char*)base;
     w->wt = b + o_wt;
@@ -155,6 +167,7 @@ size_t ws_coarse_bwd(const Dims& d, int dm, CoarseBwdWs* w, void* base) {
     w->doc = b + o_doc;
     w->stats_c = (float*)(b + o_dc);
     w->dw_part = (float*)(b + o_dw);
+    w->doc_part = d.bs ? (float*)(b + o_dp) : nullptr;
   }
   return off;
 }
@@ -313,8 +326,8 @@ int vsa2_pool(const vsa2_problem* p, const void* q, const void* k, const void* v
   if (s) return s;
   if (!aligned(q) || !aligned(k) || !aligned(v) || !aligned(pooled)) return VSA2_E_ARG;
   Pooled pp = pooled_ptrs(d, pooled);
-  PoolArgs a{q, k, v, (void*)pp.qr, (void*)pp.kr, (void*)pp.qc, (void*)pp.kc, (void*)pp.vc, d.bh, d.nb, d.nbp, d.d,
-             d.bf16, d.pad};
+  PoolArgs a{q, k, v, (void*)pp.qr, (void*)pp.kr, (void*)pp.qc, (void*)pp.kc, (void*)pp.vc, d.bh, d.nc, d.nbp, d.d,
+             d.bf16, d.pad, d.bs};
   return hip_status(launch_pool(a, (hipStream_t)stream));
 }
 
@@ -325,8 +338,8 @@ int vsa2_route(const vsa2_problem* p, const void* pooled, float* scores, void* w
   if (!aligned(pooled) || !aligned(scores)) return VSA2_E_ARG;
   if ((s = check_ws(ws, ws_bytes, ws_route(d)))) return s;
   Pooled pp = pooled_ptrs(d, pooled);
-  RouteArgs a{pp.qr, pp.kr, (float*)ws, scores, d.bh, d.nb, d.d, d.bf16, d.scale * 1.4426950408889634f, d.pad,
-              d.pad.on ? (uint64_t*)((char*)ws + ws_route_lse(d)) : nullptr};
+  RouteArgs a{pp.qr, pp.kr, (float*)ws, scores, d.bh, d.nc, d.d, d.bf16, d.scale * 1.4426950408889634f, d.pad,
+              d.pad.on ? (uint64_t*)((char*)ws + ws_route_lse(d)) : nullptr, d.bs};
   return hip_status(launch_route(a, (hipStream_t)stream));
 }
 
@@ -387,12 +400,13 @@ int vsa2_sparse_attn_fwd(const vsa2_problem* p, int32_t topk, const void* q, con
   a.q = q; a.k = k; a.v = v;
   a.row_ptr = row_ptr; a.col_idx = col_idx;
   a.o = o_f; a.lse = lse;
-  a.bh = d.bh; a.nq = d.nb; a.nkv = d.nb; a.seq = d.L; a.ld = d.L; a.out_rows = d.L;
+  a.bh = d.bh; a.nq = d.nc; a.nkv = d.nc; a.seq = d.L; a.ld = d.L; a.out_rows = d.L;
   a.kph = budget(d, topk);
   a.d = d.d; a.bf16 = d.bf16; a.dense = false;
   a.scale_log2 = d.scale * 1.4426950408889634f;
   a.ct = d.pad.nt; a.cy = d.pad.ny; a.cx = d.pad.nx;
   a.pad = d.pad;
+  a.bs = d.bs;
   return hip_status(launch_attn_fwd(a, (hipStream_t)stream));
 }
 
@@ -421,13 +435,14 @@ int vsa2_sparse_attn_bwd(const vsa2_problem* p, int32_t topk, const void* q, con
   a.dk_add = dqkv_c ? dqkv_c + cstride : nullptr;
   a.dv_add = dqkv_c ? dqkv_c + 2 * cstride : nullptr;
   a.dq = dq; a.dk = dk; a.dv = dv;
-  a.bh = d.bh; a.nq = d.nb; a.nkv = d.nb; a.seq = d.L; a.ld = d.L; a.out_rows = d.L;
+  a.bh = d.bh; a.nq = d.nc; a.nkv = d.nc; a.seq = d.L; a.ld = d.L; a.out_rows = d.L;
   a.kph = budget(d, topk);
   a.d = d.d; a.bf16 = d.bf16; a.dense = false;
   a.scale = d.scale;
   a.scale_log2 = d.scale * 1.4426950408889634f;
   a.ct = d.pad.nt; a.cy = d.pad.ny; a.cx = d.pad.nx;
   a.pad = d.pad;
+  a.bs = d.bs;
   return hip_status(launch_attn_bwd(a, st));
 }
 
@@ -454,7 +469,7 @@ int vsa2_coarse_gate(const vsa2_problem* p, const void* pooled, const void* x, i
   a.scale_log2 = d.scale * 1.4426950408889634f;
   hipError_t e = launch_attn_fwd(a, st);
   if (e != hipSuccess) return VSA2_E_HIP;
-  GateArgs ga{x, w_g, ws, oc_hat, o_f, o, g, d.batch, d.heads, d.nb, d.d, d_model, d.bf16, d.pad};
+  GateArgs ga{x, w_g, ws, oc_hat, o_f, o, g, d.batch, d.heads, d.nc, d.d, d_model, d.bf16, d.pad, d.bs};
   return hip_status(launch_gate_fwd(ga, st));
 }
 
@@ -477,7 +492,7 @@ int vsa2_coarse_gate_bwd(const vsa2_problem* p, const void* pooled, const void* 
   const float* lse_c = oc_hat + (size_t)d.bh * d.nb * d.d;
   const float* g = lse_c + (size_t)d.bh * d.nb;
   GateBwdArgs ga{x, w_g, w.wt, oc_hat, g, d_o, w.dpre, w.doc, lse_c, w.stats_c, w.dw_part, dx, dw_g,
-                 d.batch, d.heads, d.nb, d.nbp, d.d, d_model, nchunk_of(d), d.bf16, d.pad};
+                 d.batch, d.heads, d.nc, d.nbp, d.d, d_model, nchunk_of(d), d.bf16, d.pad, d.bs, w.doc_part};
   hipError_t e = launch_gate_bwd(ga, st);
   if (e != hipSuccess) return VSA2_E_HIP;
   AttnBwdArgs a{};

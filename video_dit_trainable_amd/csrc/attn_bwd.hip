@@ -130,7 +130,9 @@ __device__ __forceinline__ void dkdv_pair(const T* qs, const T* dos, const float
 // the copy into one stage from the reads of the other.
 // PAD (fine branch on a padded grid): the cube's pad keys get P = 0, so their
 // dK, dV rows are zero; pad query rows arrive with lse2 = +inf (P = 0).
-template <typename T, typename TO, int D, bool DENSE, bool PAD>
+// BS: 2^BS cubes per attention block; the CSC lists query blocks, and list
+// position n is query cube (entry << BS) + (n mod 2^BS).
+template <typename T, typename TO, int D, bool DENSE, bool PAD, int BS>
 __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(const T* __restrict__ q, const T* __restrict__ k,
                                                      const T* __restrict__ v, const T* __restrict__ d_o,
                                                      const float* __restrict__ stats,
@@ -141,6 +143,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(const T* __restrict__ q, co
                                                      TO* __restrict__ dv, int nq, int nkv, int seq, int ld,
                                                      int out_rows, int64_t kph, float scale, float c, PadGrid pad) {
   static_assert(!(DENSE && PAD), "padding applies to the fine branch");
+  static_assert(!DENSE || BS == 0, "the dense mode has one cube per block");
   constexpr int TILE = 64 * D;
   __shared__ __align__(16) T tA[2 * TILE];  // stage A: Q tile | dO tile
   __shared__ __align__(16) T tB[2 * TILE];  // stage B
@@ -157,24 +160,28 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(const T* __restrict__ q, co
   if constexpr (DENSE) {
     cnt = nq;
   } else {
-    const int32_t* cp = col_ptr + (size_t)bh * (nkv + 1);
-    const int64_t start = min<int64_t>(max(cp[j], 0), kph);
-    const int64_t end = min<int64_t>(max<int64_t>(cp[j + 1], start), kph);
-    cnt = (int)(end - start);
+    const int32_t* cp = col_ptr + (size_t)bh * ((nkv >> BS) + 1);
+    const int64_t start = min<int64_t>(max(cp[j >> BS], 0), kph);
+    const int64_t end = min<int64_t>(max<int64_t>(cp[(j >> BS) + 1], start), kph);
+    cnt = (int)(end - start) << BS;
     rows = row_idx + (size_t)bh * kph + start;
   }
-  // list entry n (DENSE: the query tile n); read one step before its copy is
-  // started, so the load is complete at the wait that precedes the copy
+  // list entry of position n (DENSE: the query tile n); read one step before
+  // its copy is started, so the load is complete at the wait that precedes
+  // the copy
   auto entry = [&](int n) -> int {
     if constexpr (DENSE) return n;
-    else return rows[n];
+    else return rows[n >> BS];
   };
-  // a corrupt sparse entry is fetched as cube 0 and skipped.  The entry stays
-  // in a vector register until here (opaque), so its load is only waited for
-  // after the copies issued behind it have been waited for anyway.
-  auto cube_of = [&](int raw, bool& ok) -> int {
+  // query cube of an entry at a position whose low BS bits are `sub` (stage A
+  // takes the even positions, stage B the odd ones); a corrupt sparse entry
+  // is fetched as cube 0 and skipped.  The entry stays in a vector register
+  // until here (opaque), so its load is only waited for after the copies
+  // issued behind it have been waited for anyway.
+  auto cube_of = [&](int raw, int sub, bool& ok) -> int {
     if constexpr (!DENSE) opaque(raw);
     raw = __builtin_amdgcn_readfirstlane(raw);
+    if constexpr (BS > 0) raw = (int)(((unsigned)raw << BS) | (unsigned)sub);
     ok = (unsigned)raw < (unsigned)nq;
     return ok ? raw : 0;
   };
@@ -221,7 +228,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(const T* __restrict__ q, co
   bool ok_a = false, ok_b = false;
   int raw = 0;  // list entry whose copy starts next
   if (cnt > 0) {
-    const int ii0 = cube_of(entry(0), ok_a);
+    const int ii0 = cube_of(entry(0), 0, ok_a);
     VSA2_FETCH_QDO(ii0, tA, sA);
     if (cnt > 1) raw = entry(1);
   }
@@ -229,7 +236,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(const T* __restrict__ q, co
     wait_vm0();
     __syncthreads();  // stage A holds entry n; every wave is done with stage B
     if (n + 1 < cnt) {
-      const int ii = cube_of(raw, ok_b);
+      const int ii = cube_of(raw, 1, ok_b);
       if (n + 2 < cnt) raw = entry(n + 2);
       VSA2_FETCH_QDO(ii, tB, sB);
     }
@@ -238,7 +245,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(const T* __restrict__ q, co
     wait_vm0();
     __syncthreads();  // stage B holds entry n + 1; every wave is done with stage A
     if (n + 2 < cnt) {
-      const int ii = cube_of(raw, ok_a);
+      const int ii = cube_of(raw, 0, ok_a);
       if (n + 3 < cnt) raw = entry(n + 3);
       VSA2_FETCH_QDO(ii, tA, sA);
     }
@@ -275,14 +282,15 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(const T* __restrict__ q, co
         dka[db][kb][r] = (dka[db][kb][r] + mine[o]) * scale;
         dva[db][kb][r] += mine[PART + o];
       }
-  // the coarse branch's per-cube gradient rows, 1/n to each of the cube's n
-  // real tokens (n = 64 unless the grid is padded)
+  // the coarse branch's per-block gradient rows, 1/n to each of the block's
+  // n real tokens (n = 64 2^BS unless the grid is padded)
   if (dk_add) {
-    const float* ka = dk_add + ((size_t)bh * nkv + j) * D;
-    const float* va = dv_add + ((size_t)bh * nkv + j) * D;
-    float wk[2] = {1.0f / 64.0f, 1.0f / 64.0f};
+    const float* ka = dk_add + ((size_t)bh * (nkv >> BS) + (j >> BS)) * D;
+    const float* va = dv_add + ((size_t)bh * (nkv >> BS) + (j >> BS)) * D;
+    float wk[2] = {1.0f / (float)(64 << BS), 1.0f / (float)(64 << BS)};
     if constexpr (PAD) {
-      const float inv_n = 1.0f / (float)__popcll(km);
+      const int n = __popcll(km) + (BS ? __popcll(cube_slots(j ^ 1, pad)) : 0);
+      const float inv_n = 1.0f / (float)n;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) wk[kb] = kv_ok[kb] ? inv_n : 0.f;
     }
@@ -383,7 +391,9 @@ __device__ __forceinline__ void dq_pair(const T* ks, const T* vs, int brow, int 
 // (distinct stage arrays, loop unrolled by two, as in the dK/dV kernel).
 // PAD (fine branch on a padded grid): pad keys are masked; pad query rows get
 // the statistics (+inf, 0), so their P is 0 here and in the dK/dV kernel.
-template <typename T, typename TO, int D, bool DENSE, bool STATS, bool PAD>
+// BS: 2^BS cubes per attention block; the CSR lists KV blocks, and list
+// position n is KV cube (entry << BS) + (n mod 2^BS).
+template <typename T, typename TO, int D, bool DENSE, bool STATS, bool PAD, int BS>
 __global__ __launch_bounds__(256, 2) void k_bwd_dq(const T* __restrict__ q, const T* __restrict__ k,
                                                    const T* __restrict__ v, const T* __restrict__ d_o,
                                                    const T* __restrict__ o, const float* __restrict__ lse,
@@ -394,6 +404,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(const T* __restrict__ q, cons
                                                    int nkv, int seq, int ld, int out_rows, int64_t kph, float scale,
                                                    float c, int ct, int cy, int cx, PadGrid pad) {
   static_assert(!PAD || (STATS && !DENSE), "padding applies to the fine branch");
+  static_assert(!DENSE || BS == 0, "the dense mode has one cube per block");
   constexpr int TILE = 64 * D;
   __shared__ __align__(16) T tA[2 * TILE];  // stage A: K tile | V tile
   __shared__ __align__(16) T tB[2 * TILE];  // stage B
@@ -409,25 +420,27 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(const T* __restrict__ q, cons
   if constexpr (DENSE) {
     cnt = nkv;
   } else {
-    const int32_t* rp = row_ptr + (size_t)bh * (nq + 1);
-    const int64_t start = min<int64_t>(max(rp[i], 0), kph);
-    const int64_t end = min<int64_t>(max<int64_t>(rp[i + 1], start), kph);
-    cnt = (int)(end - start);
+    const int32_t* rp = row_ptr + (size_t)bh * ((nq >> BS) + 1);
+    const int64_t start = min<int64_t>(max(rp[i >> BS], 0), kph);
+    const int64_t end = min<int64_t>(max<int64_t>(rp[(i >> BS) + 1], start), kph);
+    cnt = (int)(end - start) << BS;
     cols = col_idx + (size_t)bh * kph + start;
   }
-  // list entry n (DENSE: the KV tile n), read one step before its copy starts
+  // list entry of position n (DENSE: the KV tile n), read one step before its copy starts
   auto entry = [&](int n) -> int {
     if constexpr (DENSE) return n;
-    else return cols[n];
+    else return cols[n >> BS];
   };
-  // KV cube of an entry and how many of its keys are valid (0 for a corrupt entry)
-  auto cube_of = [&](int raw, int& lim) -> int {
+  // KV cube of an entry at a position whose low BS bits are `sub`, and how
+  // many of its keys are valid (0 for a corrupt entry)
+  auto cube_of = [&](int raw, int sub, int& lim) -> int {
     if constexpr (DENSE) {
       lim = min(64, seq - raw * 64);
       return raw;
     } else {
       opaque(raw);
       raw = __builtin_amdgcn_readfirstlane(raw);
+      if constexpr (BS > 0) raw = (int)(((unsigned)raw << BS) | (unsigned)sub);
       const bool ok = (unsigned)raw < (unsigned)nkv;
       lim = ok ? 64 : 0;
       return ok ? raw : 0;
@@ -494,7 +507,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(const T* __restrict__ q, cons
     else return ~0ull;
   };
   if (cnt > 0) {
-    const int j0 = cube_of(entry(0), lim_a);
+    const int j0 = cube_of(entry(0), 0, lim_a);
     km_a = slots_of(j0, lim_a);
     VSA2_FETCH_KV(j0, tA);
     if (cnt > 1) raw = entry(1);
@@ -503,7 +516,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(const T* __restrict__ q, cons
     wait_vm0();
     __syncthreads();  // stage A holds entry n; every wave is done with stage B
     if (n + 1 < cnt) {
-      const int jj = cube_of(raw, lim_b);
+      const int jj = cube_of(raw, 1, lim_b);
       km_b = slots_of(jj, lim_b);
       if (n + 2 < cnt) raw = entry(n + 2);
       VSA2_FETCH_KV(jj, tB);
@@ -514,7 +527,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(const T* __restrict__ q, cons
     wait_vm0();
     __syncthreads();  // stage B holds entry n + 1; every wave is done with stage A
     if (n + 2 < cnt) {
-      const int jj = cube_of(raw, lim_a);
+      const int jj = cube_of(raw, 0, lim_a);
       km_a = slots_of(jj, lim_a);
       if (n + 3 < cnt) raw = entry(n + 3);
       VSA2_FETCH_KV(jj, tA);
@@ -546,11 +559,12 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(const T* __restrict__ q, cons
 #pragma unroll
       for (int r = 0; r < 4; ++r)
         dqa[db][qb][r] = (dqa[db][qb][r] + mine[((db * 2 + qb) * 4 + r) * 64 + lane]) * scale;
-  if (dq_add) {  // the coarse branch's per-cube gradient row, 1/n to each of the n real tokens
-    const float* qa = dq_add + ((size_t)bh * nq + i) * D;
-    float wq[2] = {1.0f / 64.0f, 1.0f / 64.0f};
+  if (dq_add) {  // the coarse branch's per-block gradient row, 1/n to each of the n real tokens
+    const float* qa = dq_add + ((size_t)bh * (nq >> BS) + (i >> BS)) * D;
+    float wq[2] = {1.0f / (float)(64 << BS), 1.0f / (float)(64 << BS)};
     if constexpr (PAD) {
-      const float inv_n = 1.0f / (float)__popcll(qm);
+      const int n = __popcll(qm) + (BS ? __popcll(cube_slots(i ^ 1, pad)) : 0);
+      const float inv_n = 1.0f / (float)n;
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) wq[qb] = qreal[qb] ? inv_n : 0.f;
     }
@@ -579,17 +593,17 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(const T* __restrict__ q, cons
   }
 }
 
-template <typename T, typename TO, int D, bool DENSE, bool PAD>
+template <typename T, typename TO, int D, bool DENSE, bool PAD, int BS>
 hipError_t launch_bwd_tt(const AttnBwdArgs& a, hipStream_t st) {
   // dQ first: in sparse mode it writes the row statistics the dK/dV kernel reads
   if (!DENSE) timer_before(TK_BWD_DQ, st);
   if constexpr (DENSE)
-    hipLaunchKernelGGL((k_bwd_dq<T, TO, D, DENSE, false, false>), dim3(xcd_grid(a.nq, a.bh)), dim3(256), 0, st,
+    hipLaunchKernelGGL((k_bwd_dq<T, TO, D, DENSE, false, false, 0>), dim3(xcd_grid(a.nq, a.bh)), dim3(256), 0, st,
                        (const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.d_o, nullptr, nullptr, nullptr,
                        a.stats, a.row_ptr, a.col_idx, a.dq_add, (TO*)a.dq, a.nq, a.nkv, a.seq, a.ld, a.out_rows, a.kph,
                        a.scale, a.scale_log2, a.ct, a.cy, a.cx, a.pad);
   else
-    hipLaunchKernelGGL((k_bwd_dq<T, TO, D, DENSE, true, PAD>), dim3(xcd_grid(a.nq, a.bh)), dim3(256), 0, st,
+    hipLaunchKernelGGL((k_bwd_dq<T, TO, D, DENSE, true, PAD, BS>), dim3(xcd_grid(a.nq, a.bh)), dim3(256), 0, st,
                        (const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.d_o, (const T*)a.o, a.lse,
                        a.stats_out, nullptr, a.row_ptr, a.col_idx, a.dq_add, (TO*)a.dq, a.nq, a.nkv, a.seq, a.ld,
                        a.out_rows, a.kph, a.scale, a.scale_log2, a.ct, a.cy, a.cx, a.pad);
@@ -597,7 +611,7 @@ hipError_t launch_bwd_tt(const AttnBwdArgs& a, hipStream_t st) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (!DENSE) timer_before(TK_BWD_DKDV, st);
-  hipLaunchKernelGGL((k_bwd_dkdv<T, TO, D, DENSE, PAD>), dim3(xcd_grid(a.nkv, a.bh)), dim3(256), 0, st,
+  hipLaunchKernelGGL((k_bwd_dkdv<T, TO, D, DENSE, PAD, BS>), dim3(xcd_grid(a.nkv, a.bh)), dim3(256), 0, st,
                      (const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.d_o, DENSE ? a.stats : a.stats_out,
                      a.col_ptr, a.row_idx, a.dk_add, a.dv_add, (TO*)a.dk, (TO*)a.dv, a.nq, a.nkv, a.seq, a.ld,
                      a.out_rows, a.kph, a.scale, a.scale_log2, a.pad);
@@ -607,8 +621,10 @@ hipError_t launch_bwd_tt(const AttnBwdArgs& a, hipStream_t st) {
 
 template <typename T, int D>
 hipError_t launch_bwd_t(const AttnBwdArgs& a, hipStream_t st) {
-  if (a.dense) return launch_bwd_tt<T, float, D, true, false>(a, st);
-  return a.pad.on ? launch_bwd_tt<T, T, D, false, true>(a, st) : launch_bwd_tt<T, T, D, false, false>(a, st);
+  if (a.dense) return launch_bwd_tt<T, float, D, true, false, 0>(a, st);
+  if (a.bs)
+    return a.pad.on ? launch_bwd_tt<T, T, D, false, true, 1>(a, st) : launch_bwd_tt<T, T, D, false, false, 1>(a, st);
+  return a.pad.on ? launch_bwd_tt<T, T, D, false, true, 0>(a, st) : launch_bwd_tt<T, T, D, false, false, 0>(a, st);
 }
 
 hipError_t launch_attn_bwd(const AttnBwdArgs& a, hipStream_t st) {

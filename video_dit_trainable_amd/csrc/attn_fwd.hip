@@ -27,7 +27,10 @@ namespace vsa2 {
 
 // PAD (fine branch on a padded grid): pad slots of a KV cube are masked like
 // keys past the end; pad query rows are written as O_f = 0, LSE = -inf.
-template <typename T, typename TO, int D, bool DENSE, bool PAD>
+// BS: 2^BS cubes per attention block.  The CSR lists blocks; query cube i
+// takes the list of its block i >> BS, and list position n is cube
+// (entry << BS) + (n mod 2^BS) of the selected block.
+template <typename T, typename TO, int D, bool DENSE, bool PAD, int BS>
 __global__ __launch_bounds__(128, 2) void k_attn_fwd(const T* __restrict__ q, const T* __restrict__ k,
                                                   const T* __restrict__ v, const int32_t* __restrict__ row_ptr,
                                                   const int32_t* __restrict__ col_idx, TO* __restrict__ o,
@@ -50,17 +53,17 @@ __global__ __launch_bounds__(128, 2) void k_attn_fwd(const T* __restrict__ q, co
   if constexpr (DENSE) {
     cnt = nkv;
   } else {
-    const int32_t* rp = row_ptr + (size_t)bh * (nq + 1);
-    const int64_t start = min<int64_t>(max(rp[i], 0), kph);
-    const int64_t end = min<int64_t>(max<int64_t>(rp[i + 1], start), kph);
-    cnt = (int)(end - start);
+    const int32_t* rp = row_ptr + (size_t)bh * ((nq >> BS) + 1);
+    const int64_t start = min<int64_t>(max(rp[i >> BS], 0), kph);
+    const int64_t end = min<int64_t>(max<int64_t>(rp[(i >> BS) + 1], start), kph);
+    cnt = (int)(end - start) << BS;
     cols = col_idx + (size_t)bh * kph + start;
   }
-  // cube id of list entry n; out-of-range ids (corrupt lists) become -1 = masked tile
+  // cube id of list position n; out-of-range ids (corrupt lists) become -1 = masked tile
   auto cube_at = [&](int n) -> int {
     if constexpr (DENSE) return n;
-    const int jj = cols[n];
-    return (unsigned)jj < (unsigned)nkv ? jj : -1;
+    const int jj = cols[n >> BS];
+    return (unsigned)jj < (unsigned)(nkv >> BS) ? (jj << BS) + (n & ((1 << BS) - 1)) : -1;
   };
   auto kv_limit = [&](int jj) -> int {  // valid keys of cube jj
     if constexpr (DENSE) return min(64, seq - jj * 64);
@@ -213,19 +216,21 @@ template <typename T, int D>
 hipError_t launch_fwd_t(const AttnArgs& a, hipStream_t st) {
   dim3 grid(xcd_grid(a.nq, a.bh));
   if (a.dense) {
-    hipLaunchKernelGGL((k_attn_fwd<T, float, D, true, false>), grid, dim3(128), 0, st, (const T*)a.q,
+    hipLaunchKernelGGL((k_attn_fwd<T, float, D, true, false, 0>), grid, dim3(128), 0, st, (const T*)a.q,
                        (const T*)a.k, (const T*)a.v, nullptr, nullptr, (float*)a.o, a.lse, a.nq, a.nkv, a.seq, a.ld,
                        a.out_rows, a.kph, a.scale_log2, 0, 0, 0, a.pad);
   } else {
     timer_before(TK_FINE_FWD, st);
-    if (a.pad.on)
-      hipLaunchKernelGGL((k_attn_fwd<T, T, D, false, true>), grid, dim3(128), 0, st, (const T*)a.q, (const T*)a.k,
-                         (const T*)a.v, a.row_ptr, a.col_idx, (T*)a.o, a.lse, a.nq, a.nkv, a.seq, a.ld, a.out_rows,
-                         a.kph, a.scale_log2, a.ct, a.cy, a.cx, a.pad);
-    else
-      hipLaunchKernelGGL((k_attn_fwd<T, T, D, false, false>), grid, dim3(128), 0, st, (const T*)a.q,
-                         (const T*)a.k, (const T*)a.v, a.row_ptr, a.col_idx, (T*)a.o, a.lse, a.nq, a.nkv, a.seq,
-                         a.ld, a.out_rows, a.kph, a.scale_log2, a.ct, a.cy, a.cx, a.pad);
+#define VSA2_FWD(PAD, BS)                                                                                        \
+  hipLaunchKernelGGL((k_attn_fwd<T, T, D, false, PAD, BS>), grid, dim3(128), 0, st, (const T*)a.q, (const T*)a.k, \
+                     (const T*)a.v, a.row_ptr, a.col_idx, (T*)a.o, a.lse, a.nq, a.nkv, a.seq, a.ld, a.out_rows,     \
+                     a.kph, a.scale_log2, a.ct, a.cy, a.cx, a.pad)
+    if (a.bs) {
+      if (a.pad.on) VSA2_FWD(true, 1); else VSA2_FWD(false, 1);
+    } else {
+      if (a.pad.on) VSA2_FWD(true, 0); else VSA2_FWD(false, 0);
+    }
+#undef VSA2_FWD
     timer_after(TK_FINE_FWD, st);
   }
   return hipGetLastError();

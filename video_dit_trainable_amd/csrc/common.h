@@ -497,20 +497,20 @@ __host__ __device__ constexpr uint64_t axis_slots(int axis, int v) {
 template <int AXIS>
 __device__ __forceinline__ uint64_t axis_mask(int v) {
   constexpr uint64_t m1 = axis_slots(AXIS, 1), m2 = axis_slots(AXIS, 2), m3 = axis_slots(AXIS, 3);
-  return v >= 4 ? ~0ull : (v == 3 ? m3 : (v == 2 ? m2 : m1));
+  return v >= 4 ? ~0ull : (v == 3 ? m3 : (v == 2 ? m2 : (v == 1 ? m1 : 0ull)));
 }
 
-// Real extents of cube c.  The quotients use float reciprocals: for c < 2^16
-// (c + 0.5) / n lies at least 0.5 / n from an integer, far beyond the
-// rounding error of the two float roundings, so the truncation is exact.
+// Real extents (0..4) of cube c.  The quotients use float reciprocals: for
+// c < 2^16 (c + 0.5) / n lies at least 0.5 / n from an integer, far beyond
+// the rounding error of the two float roundings, so the truncation is exact.
 __device__ __forceinline__ void cube_extent(int c, const PadGrid& p, int& vt, int& vy, int& vx) {
   const int a = (int)(((float)c + 0.5f) * p.inv_nyx);
   const int rem = c - a * p.ny * p.nx;
   const int b = (int)(((float)rem + 0.5f) * p.inv_nx);
   const int x = rem - b * p.nx;
-  vt = a == p.nt - 1 ? p.et : 4;
-  vy = b == p.ny - 1 ? p.ey : 4;
-  vx = x == p.nx - 1 ? p.ex : 4;
+  vt = min(4, max(0, p.rt - 4 * a));
+  vy = min(4, max(0, p.ry - 4 * b));
+  vx = min(4, max(0, p.rx - 4 * x));
 }
 
 // Bit s set for the slots of cube c that hold a real token.

@@ -61,7 +61,7 @@ template <typename T, int D, int NHB>
 __global__ __launch_bounds__(256) void k_gate_fwd(const T* __restrict__ x, const T* __restrict__ wt,
                                                   const float* __restrict__ oc_hat, const T* __restrict__ o_f,
                                                   T* __restrict__ o, float* __restrict__ gout, int H, int nb, int dm,
-                                                  int hp, PadGrid pad) {
+                                                  int hp, PadGrid pad, int bs) {
   constexpr bool SPLIT = sizeof(T) == 2;
   __shared__ float gs[64][HMAX + 1];
   const int c = blockIdx.x, b = blockIdx.y, tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4,
@@ -127,7 +127,7 @@ __global__ __launch_bounds__(256) void k_gate_fwd(const T* __restrict__ x, const
 #pragma unroll 2
   for (int h = 0; h < H; ++h) {
     const size_t bh = (size_t)b * H + h;
-    const float* oc = oc_hat + (bh * nb + c) * D;
+    const float* oc = oc_hat + (bh * (nb >> bs) + (c >> bs)) * D;  // the coarse token of the cube's block
 #pragma unroll
     for (int i = 0; i < UPT; ++i) {
       const int u = tid + 256 * i;
@@ -155,7 +155,8 @@ __global__ __launch_bounds__(256) void k_gate_bwd(const T* __restrict__ wt, cons
                                                   float* __restrict__ dpre, T* __restrict__ doc,
                                                   const float* __restrict__ lse_c, float* __restrict__ stats_c,
                                                   T* __restrict__ dx, int H, int nb,
-                                                  int nbp, int dm, int hp, int hk, PadGrid pad) {
+                                                  int nbp, int dm, int hp, int hk, PadGrid pad, int bs,
+                                                  float* __restrict__ doc_part) {
   constexpr bool SPLIT = sizeof(T) == 2;
   constexpr int UPR = D / 8;
   constexpr int RROWS = 256 / UPR;
@@ -199,7 +200,7 @@ __global__ __launch_bounds__(256) void k_gate_bwd(const T* __restrict__ wt, cons
       gc[i] = gn[i];
     }
     if (h + 1 < H) fetch(h + 1);
-    const float* oc = oc_hat + (bh * nb + c) * D;
+    const float* oc = oc_hat + (bh * (nb >> bs) + (c >> bs)) * D;
     const float4 a0 = *reinterpret_cast<const float4*>(oc + 8 * dg);
     const float4 a1 = *reinterpret_cast<const float4*>(oc + 8 * dg + 4);
     const float ocv[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
@@ -233,19 +234,25 @@ __global__ __launch_bounds__(256) void k_gate_bwd(const T* __restrict__ wt, cons
     if (tid < D) {
       float s = 0.f;
       for (int r = 0; r < RROWS; ++r) s += red[r][tid];
-      doc[(bh * nbp + c) * D + tid] = from_f32<T>(s);
-      prod = s * oc[tid];
+      if (bs) {  // 128-token blocks: the pair kernel adds the two cubes' sums
+        doc_part[(bh * nb + c) * D + tid] = s;
+      } else {
+        doc[(bh * nbp + c) * D + tid] = from_f32<T>(s);
+        prod = s * oc[tid];
+      }
     }
-    for (int s = 1; s < 64; s <<= 1) prod += __shfl_xor(prod, s);
-    if (lane == 0) wsum[w] = prod;
+    if (!bs) {
+      for (int s = 1; s < 64; s <<= 1) prod += __shfl_xor(prod, s);
+      if (lane == 0) wsum[w] = prod;
+    }
     __syncthreads();
-    if (tid == 0) {
+    if (tid == 0 && !bs) {
       stats_c[2 * (bh * nbp + c)] = lse_c[bh * nb + c] * LOG2E;
       stats_c[2 * (bh * nbp + c) + 1] = -(wsum[0] + wsum[1] + wsum[2] + wsum[3]);
     }
   }
   // zero the padding rows of dO_hat_c and mask them in the row statistics
-  for (int row = nb + c; row < nbp; row += nb)
+  for (int row = nb + c; row < nbp && !bs; row += nb)
     for (int h = 0; h < H; ++h) {
       const size_t bh = (size_t)b * H + h;
       for (int d = tid; d < D; d += 256) doc[(bh * nbp + row) * D + d] = from_f32<T>(0.f);
@@ -314,6 +321,40 @@ __global__ __launch_bounds__(256) void k_gate_bwd(const T* __restrict__ wt, cons
       const int t = lane / 8 + 8 * i, ch = lane % 8;
       const Vec8<T> v = load8(stage + t * 64 + 8 * (ch ^ (t & 7)));
       store8(dxt + (size_t)t * dm + 64 * qd + 8 * ch, v);
+    }
+  }
+}
+
+// 128-token blocks: dO_hat_c of a block is the sum of its two cubes' sums,
+// and its row statistics (lse_c log2 e, -rowsum(dO_hat_c O_hat_c)) follow as
+// in k_gate_bwd; rows nb .. nbp-1 are zeroed and masked.  One workgroup per
+// (block, batch * head) and D threads.
+template <typename T, int D>
+__global__ __launch_bounds__(D) void k_coarse_pair(const float* __restrict__ doc_part,
+                                                   const float* __restrict__ oc_hat, const float* __restrict__ lse_c,
+                                                   T* __restrict__ doc, float* __restrict__ stats_c, int nblk,
+                                                   int nbp) {
+  __shared__ float wsum[D / 64];
+  const int blk = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
+  const size_t bh = blockIdx.y;
+  const float* part = doc_part + (bh * 2 * nblk + 2 * blk) * D;
+  const float s = part[tid] + part[D + tid];
+  doc[(bh * nbp + blk) * D + tid] = from_f32<T>(s);
+  float prod = s * oc_hat[(bh * nblk + blk) * D + tid];
+  for (int o = 1; o < 64; o <<= 1) prod += __shfl_xor(prod, o);
+  if (lane == 0) wsum[tid >> 6] = prod;
+  __syncthreads();
+  if (tid == 0) {
+    float t = 0.f;
+    for (int w = 0; w < D / 64; ++w) t += wsum[w];
+    stats_c[2 * (bh * nbp + blk)] = lse_c[bh * nblk + blk] * LOG2E;
+    stats_c[2 * (bh * nbp + blk) + 1] = -t;
+  }
+  for (int row = nblk + blk; row < nbp; row += nblk) {
+    doc[(bh * nbp + row) * D + tid] = from_f32<T>(0.f);
+    if (tid == 0) {
+      stats_c[2 * (bh * nbp + row)] = INFINITY;
+      stats_c[2 * (bh * nbp + row) + 1] = 0.f;
     }
   }
 }
@@ -523,7 +564,7 @@ hipError_t launch_gate_fwd_t(const GateArgs& a, hipStream_t st) {
   const dim3 grid(a.nb, a.batch);
 #define VSA2_GATE_FWD(NHB)                                                                                     \
   hipLaunchKernelGGL((k_gate_fwd<T, D, NHB>), grid, dim3(256), 0, st, (const T*)a.x, (const T*)a.wt, a.oc_hat, \
-                     (const T*)a.o_f, (T*)a.o, a.g, a.heads, a.nb, a.dm, hp, a.pad)
+                     (const T*)a.o_f, (T*)a.o, a.g, a.heads, a.nb, a.dm, hp, a.pad, a.bs)
   switch (hp / 16) {
     case 1: VSA2_GATE_FWD(1); break;
     case 2: VSA2_GATE_FWD(2); break;
@@ -547,13 +588,19 @@ hipError_t launch_gate_bwd_t(const GateBwdArgs& a, hipStream_t st) {
   if (hk <= 32)
     hipLaunchKernelGGL((k_gate_bwd<T, D, 1>), dim3(a.nb, a.batch), dim3(256), 0, st, (const T*)a.wt, a.oc_hat, a.g,
                        (const T*)a.d_o, a.dpre, (T*)a.doc, a.lse_c, a.stats_c, (T*)a.dx, a.heads, a.nb, a.nbp, a.dm,
-                       hp, hk, a.pad);
+                       hp, hk, a.pad, a.bs, a.doc_part);
   else
     hipLaunchKernelGGL((k_gate_bwd<T, D, 2>), dim3(a.nb, a.batch), dim3(256), 0, st, (const T*)a.wt, a.oc_hat, a.g,
                        (const T*)a.d_o, a.dpre, (T*)a.doc, a.lse_c, a.stats_c, (T*)a.dx, a.heads, a.nb, a.nbp, a.dm,
-                       hp, hk, a.pad);
+                       hp, hk, a.pad, a.bs, a.doc_part);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (a.bs) {
+    hipLaunchKernelGGL((k_coarse_pair<T, D>), dim3(a.nb >> 1, a.batch * a.heads), dim3(D), 0, st, a.doc_part,
+                       a.oc_hat, a.lse_c, (T*)a.doc, a.stats_c, a.nb >> 1, a.nbp);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   if constexpr (sizeof(T) == 2) {
     const dim3 grid((a.dm + 255) / 256, a.nchunk, a.batch);
     const int nhb = (a.heads + 15) / 16;

@@ -6,35 +6,39 @@
 
 namespace vsa2 {
 
-// Latent grids whose sides are not multiples of 4 are padded up to whole
-// cubes (paper §2.2 "Kernel Implementation"); pad positions are not tokens.
-// PadGrid gives the cube grid and the real extent (1..4) of the last cube
-// along each axis; `on` is 0 when the grid divides.
+// Latent grids whose sides are not multiples of the block are padded up to
+// whole blocks (paper §2.2 "Kernel Implementation"); pad positions are not
+// tokens.  PadGrid gives the cube grid and the real side lengths; a cube's
+// real extent along an axis is the side length minus its offset, clamped to
+// 0..4 (with 128-token blocks the last cube along x can hold no token).
+// `on` is 0 when the grid divides.
 struct PadGrid {
   int on;
   int nt, ny, nx;        // cubes along t, y, x
-  int et, ey, ex;        // real positions of the last cube along t, y, x
+  int rt, ry, rx;        // real side lengths of the latent grid
   float inv_nx, inv_nyx; // 1 / nx, 1 / (ny nx), rounded to nearest
 };
 
 struct PoolArgs {
   const void *q, *k, *v;
   void *qr, *kr, *qc, *kc, *vc;
-  int bh, nb, nbp, d;
+  int bh, nb, nbp, d;     // nb cubes; nbp rows of the coarse operands (blocks rounded up to 64)
   bool bf16;
   PadGrid pad;
+  int bs;                 // 2^bs cubes per attention block (coarse token)
 };
 hipError_t launch_pool(const PoolArgs& a, hipStream_t st);
 
 struct RouteArgs {
   const void *qr, *kr;
   float* lse2;        // workspace [bh, 8*nb], log2-domain LSE of each pooled query
-  float* scores;      // [bh, nb, nb]
-  int bh, nb, d;
+  float* scores;      // [bh, nb >> bs, nb >> bs]
+  int bh, nb, d;      // nb cubes
   bool bf16;
   float scale_log2;   // softmax scale * log2(e)
   PadGrid pad;
   uint64_t* kmask;    // workspace [ceil(8 nb / 64)] (padded grids): bit b of word t set when pooled key 64t + b exists
+  int bs;             // 2^bs cubes per attention block: the scores are means over block pairs
 };
 hipError_t launch_route(const RouteArgs& a, hipStream_t st);
 
@@ -75,6 +79,7 @@ struct AttnArgs {
   float scale_log2;
   int ct, cy, cx;                     // cube grid for the blocked visiting order (0 = linear)
   PadGrid pad;                        // fine branch on a padded grid: pad keys masked, pad rows zero
+  int bs;                             // fine: 2^bs cubes per block; the CSR lists blocks (nq, nkv count cubes)
 };
 hipError_t launch_attn_fwd(const AttnArgs& a, hipStream_t st);
 
@@ -84,7 +89,7 @@ struct AttnBwdArgs {
   const float* stats;                 // dense: [bh, ld] pairs (lse * log2 e, -rowsum(dO * O)); +inf lse = masked row
   float* stats_out;                   // fine: workspace for the same pairs, written by the dQ kernel
   const int32_t *row_ptr, *col_idx, *col_ptr, *row_idx;
-  const float *dq_add, *dk_add, *dv_add;  // [bh, nkv, d] per-cube terms added as row/n, n real tokens (or NULL)
+  const float *dq_add, *dk_add, *dv_add;  // [bh, nkv >> bs, d] per-block terms added as row/n, n real tokens (or NULL)
   void *dq, *dk, *dv;                 // storage dtype (fine) or fp32 (dense)
   int bh, nq, nkv, seq, ld, out_rows;
   int64_t kph;
@@ -93,7 +98,8 @@ struct AttnBwdArgs {
   float scale;
   float scale_log2;
   int ct, cy, cx;                     // cube grid for the blocked visiting order (0 = linear)
-  PadGrid pad;                        // fine branch on a padded grid (per-cube terms added as row/n, n real tokens)
+  PadGrid pad;                        // fine branch on a padded grid (per-block terms added as row/n, n real tokens)
+  int bs;                             // fine: 2^bs cubes per block; CSR / CSC and the per-block terms are per block
 };
 hipError_t launch_attn_bwd(const AttnBwdArgs& a, hipStream_t st);
 
@@ -105,9 +111,10 @@ struct GateArgs {
   const void* o_f;
   void* o;
   float* g;               // [bh, L]
-  int batch, heads, nb, d, dm;
+  int batch, heads, nb, d, dm;   // nb cubes
   bool bf16;
   PadGrid pad;            // pad rows: g = 0, O = 0
+  int bs;                 // 2^bs cubes per coarse token: O_hat_c row of cube c is c >> bs
 };
 hipError_t launch_gate_fwd(const GateArgs& a, hipStream_t st);
 
@@ -129,9 +136,11 @@ struct GateBwdArgs {
   float* dw_part;         // workspace [nchunk, dm, heads]
   void* dx;
   float* dw_g;
-  int batch, heads, nb, nbp, d, dm, nchunk;
+  int batch, heads, nb, nbp, d, dm, nchunk;   // nb cubes; nbp coarse rows (blocks rounded up to 64)
   bool bf16;
   PadGrid pad;            // pad rows: dpre = 0 (so dX = 0 and X there adds nothing to dW_g)
+  int bs;                 // 2^bs cubes per coarse token
+  float* doc_part;        // workspace [bh, nb, d] fp32 when bs > 0: per-cube sums of dO_hat_c, added in pairs
 };
 hipError_t launch_gate_bwd(const GateBwdArgs& a, hipStream_t st);
 

@@ -136,11 +136,14 @@ __global__ void k_route_kmask(uint64_t* __restrict__ kmask, int nb, PadGrid pad)
 // PAD: a padded grid; keys and queries that hold no real token are taken from
 // the existence words (which also clear the ragged tail): such keys are
 // masked, such queries get LSE +inf, so pass 2 gives them no weight.
-template <typename T, int D, bool PASS2, bool TAIL, bool PAD>
+// BS: 2^BS cubes per attention block (pass 2 averages the 8 2^BS x 8 2^BS
+// entries of each block pair; nb counts cubes).
+template <typename T, int D, bool PASS2, bool TAIL, bool PAD, int BS>
 __global__ __launch_bounds__(256, 2) void k_router(const T* __restrict__ qr, const T* __restrict__ kr,
                                                    float* __restrict__ lse2, float* __restrict__ scores, int nb,
                                                    float c, const uint64_t* __restrict__ kmask) {
   static_assert(!(TAIL && PAD), "the existence words cover the ragged tail");
+  static_assert(BS == 0 || (BS == 1 && PASS2), "128-token blocks change only the score pass");
   __shared__ __align__(16) T kA[RK * D];
   __shared__ __align__(16) T kB[RK * D];
   const int Lr = 8 * nb;
@@ -204,14 +207,16 @@ __global__ __launch_bounds__(256, 2) void k_router(const T* __restrict__ qr, con
       dma_keys<T, D>(kbase, t * RK, Lr, lds, tid);
     }
   };
-  // pass 2: the lane that stores a block score (the first of each 8 query lanes)
+  // pass 2: the lane that stores a block score (the first of each 8 2^BS
+  // query lanes; with BS = 1 only even g, whose key cube starts a pair)
+  const int nblk = nb >> BS;
   bool qstore[2];
   float* srow[2];
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     const int qcube = (qt * RQ + 32 * w + 16 * qb + cc) >> 3;
-    qstore[qb] = (cc & 7) == 0 && qcube < nb;
-    srow[qb] = scores + ((size_t)bh * nb + min(qcube, nb - 1)) * nb;
+    qstore[qb] = (cc & ((8 << BS) - 1)) == 0 && qcube < nb && (BS == 0 || (g & 1) == 0);
+    srow[qb] = scores + ((size_t)bh * nblk + (min(qcube, nb - 1) >> BS)) * nblk;
   }
 
   float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};  // pass 1: running max / sum (scaled log2 domain)
@@ -248,8 +253,12 @@ __global__ __launch_bounds__(256, 2) void k_router(const T* __restrict__ qr, con
 #pragma unroll
             for (int r = 0; r < 4; ++r) s8 += fast_exp2(fmaf(acc[2 * h + kk][qb][r], c, -lse[qb]));
           s8 = sum8(s8);
+          if constexpr (BS == 1) {
+            s8 += __shfl_xor(s8, 8);   // the other query cube of the pair (lanes c ^ 8)
+            s8 += __shfl_xor(s8, 16);  // the other key cube of the pair (lanes g ^ 1)
+          }
           const int kcube = t * (RK / 8) + 4 * h + g;
-          if (qstore[qb] && kcube < nb) srow[qb][kcube] = s8 * (1.0f / 64.0f);
+          if (qstore[qb] && kcube < nb) srow[qb][kcube >> BS] = s8 * (1.0f / (64 << (2 * BS)));
         }
       }
     }
@@ -291,6 +300,7 @@ __global__ __launch_bounds__(256, 2) void k_router(const T* __restrict__ qr, con
 
 template <typename T, int D, bool TAIL, bool PAD>
 hipError_t launch_route_tt(const RouteArgs& a, hipStream_t st) {
+  static_assert(RQ % 16 == 0 && RK % 16 == 0, "query and key tiles hold whole cube pairs");
   const int nqt = (8 * a.nb + RQ - 1) / RQ;
   dim3 grid(xcd_grid(nqt, a.bh));
   if constexpr (PAD) {
@@ -300,14 +310,18 @@ hipError_t launch_route_tt(const RouteArgs& a, hipStream_t st) {
     if (e != hipSuccess) return e;
   }
   timer_before(TK_ROUTER_LSE, st);
-  hipLaunchKernelGGL((k_router<T, D, false, TAIL, PAD>), grid, dim3(256), 0, st, (const T*)a.qr, (const T*)a.kr,
+  hipLaunchKernelGGL((k_router<T, D, false, TAIL, PAD, 0>), grid, dim3(256), 0, st, (const T*)a.qr, (const T*)a.kr,
                      a.lse2, a.scores, a.nb, a.scale_log2, (const uint64_t*)a.kmask);
   timer_after(TK_ROUTER_LSE, st);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   timer_before(TK_ROUTER_SCORES, st);
-  hipLaunchKernelGGL((k_router<T, D, true, TAIL, PAD>), grid, dim3(256), 0, st, (const T*)a.qr, (const T*)a.kr,
-                     a.lse2, a.scores, a.nb, a.scale_log2, (const uint64_t*)a.kmask);
+  if (a.bs)
+    hipLaunchKernelGGL((k_router<T, D, true, TAIL, PAD, 1>), grid, dim3(256), 0, st, (const T*)a.qr,
+                       (const T*)a.kr, a.lse2, a.scores, a.nb, a.scale_log2, (const uint64_t*)a.kmask);
+  else
+    hipLaunchKernelGGL((k_router<T, D, true, TAIL, PAD, 0>), grid, dim3(256), 0, st, (const T*)a.qr,
+                       (const T*)a.kr, a.lse2, a.scores, a.nb, a.scale_log2, (const uint64_t*)a.kmask);
   timer_after(TK_ROUTER_SCORES, st);
   return hipGetLastError();
 }

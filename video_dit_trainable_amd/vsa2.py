@@ -30,6 +30,7 @@ class Problem(ctypes.Structure):
         ("lat_x", ctypes.c_int32),
         ("dtype", ctypes.c_int32),
         ("softmax_scale", ctypes.c_float),
+        ("block_tokens", ctypes.c_int32),
     ]
 
 
@@ -85,10 +86,10 @@ def _check(fn, code):
         raise Vsa2Error(fn, code)
 
 
-def problem(batch, heads, head_dim, grid, dtype, softmax_scale=0.0):
+def problem(batch, heads, head_dim, grid, dtype, softmax_scale=0.0, block=64):
     t, y, x = grid
     dt = {"bf16": VSA2_BF16, "f32": VSA2_F32, torch.bfloat16: VSA2_BF16, torch.float32: VSA2_F32}[dtype]
-    return Problem(batch, heads, head_dim, t, y, x, dt, softmax_scale)
+    return Problem(batch, heads, head_dim, t, y, x, dt, softmax_scale, block)
 
 
 def _ptr(t):
@@ -205,10 +206,13 @@ class Layer:
     def __init__(self, p, topk, d_model, device="cuda"):
         self.p, self.topk, self.d_model, self.device = p, topk, d_model, device
         bh = p.batch * p.heads
-        # token slots of the grid padded up to whole 4x4x4 cubes
-        nb = -(-p.lat_t // 4) * -(-p.lat_y // 4) * -(-p.lat_x // 4)
-        L = 64 * nb
-        self.L, self.nb, self.bh = L, nb, bh
+        # token slots of the grid padded up to whole blocks (4x4x4 cubes, or
+        # 4x4x8 pairs of cubes for 128-token blocks); nb counts blocks
+        block = p.block_tokens or 64
+        per = block // 64
+        L = 64 * -(-p.lat_t // 4) * -(-p.lat_y // 4) * (-(-p.lat_x // (4 * per)) * per)
+        nb = L // block
+        self.L, self.nb, self.bh, self.block = L, nb, bh, block
         self.k = budget(p, topk)
         self.sdt = torch.bfloat16 if p.dtype == VSA2_BF16 else torch.float32
         i32 = dict(dtype=torch.int32, device=device)
