@@ -12,7 +12,10 @@ is exactly the top k of the GPU's own scores with ties to the lower flat
 index, CSR/CSC are each other's transpose with columns ascending.  The same
 checks run on the 720p training problem on a grid one short of whole cubes
 along every axis (43 x 47 x 103, padded), sampling the border cubes that hold
-pad slots; there every pad row of every output must be exactly zero.
+pad slots; there every pad row of every output must be exactly zero.  And
+they run on the 720p training problem with 128-token blocks (4x4x8, two
+x-adjacent cubes), where the scores, the selection and the coarse tokens are
+per block.
 
 Tolerances as in test_gpu_parity: bf16 outputs max-abs 2e-2 and rel-L2 1e-2,
 gradients rel-L2 2e-2, index sets exact outside the relative 1e-3 band.
@@ -33,6 +36,7 @@ pytestmark = pytest.mark.gpu
 TRAIN = WORKLOADS["train720"]
 INFER = WORKLOADS["infer720"]
 TRAIN_PAD = WORKLOADS["train720pad"]    # 43 x 47 x 103, padded to the same 44 x 48 x 104 slots
+TRAIN_B128 = WORKLOADS["train720b128"]  # 128-token blocks (4x4x8), 1716 blocks
 
 
 def _dev():
@@ -49,7 +53,7 @@ def _run(w, topk, train):
     dev = _dev()
     q, k, v = make_qkv(w, device=dev)
     x, w_g = make_gate_inputs(w, device=dev, zero_gate=False)
-    p = vsa2.problem(w.batch, w.heads, w.head_dim, w.grid, w.dtype)
+    p = vsa2.problem(w.batch, w.heads, w.head_dim, w.grid, w.dtype, block=w.block)
     layer = vsa2.Layer(p, topk, w.d_model, device=dev)
     vsa2.vsa2_pool(p, q, k, v, layer.pooled)
     vsa2.vsa2_route(p, layer.pooled, layer.scores, layer.ws)
@@ -333,3 +337,68 @@ def test_padded_outputs_sampled(train720pad):
         for name, got, want in (("dK", g["dk"], dk), ("dV", g["dv"], dv)):
             rr = gu.rel_l2(gu.f64(got[0, h])[tj], want[tj])
             assert rr <= 2e-2, f"{name} head {h} corner KV cube {j}: rel-L2 {rr:.3g}"
+
+
+# ----------------------------------------------------------------------------- 128-token blocks
+@pytest.fixture(scope="module")
+def train720b128():
+    return _run(TRAIN_B128, TRAIN_B128.topk, True)
+
+
+def test_block128_router_and_selection(train720b128):
+    r = train720b128
+    w, layer = r["w"], r["layer"]
+    scores = layer.scores[0]
+    assert scores.shape == (w.heads, w.nblk, w.nblk)
+    np.testing.assert_allclose(scores.double().sum(dim=2).cpu().numpy(), 1.0 / 16.0, rtol=1e-4)   # G = 16
+    rows = np.array([0, w.nblk // 3, w.nblk - 1])
+    for h in (2, 17):
+        want = orc.router_scores(gu.f64(r["q"][0, h]), gu.f64(r["k"][0, h]), w.grid, bf16_pooled=True, rows=rows,
+                                 block=128)
+        got = scores[h].double().cpu().numpy()[rows]
+        for n in range(len(rows)):
+            assert gu.rel_l2(got[n], want[n]) <= 1e-4, f"head {h} row {rows[n]}"
+    h = 8
+    s = scores[h].cpu().numpy().reshape(-1)
+    order = np.argsort(-s, kind="stable")
+    want = np.zeros(s.size, dtype=bool)
+    want[order[:layer.k]] = True
+    rp, ci = _routed(r, h)
+    assert np.array_equal(orc.csr_to_mask(rp, ci, w.nblk).reshape(-1), want)
+    gu.check_csr_csc(*[t[0, [h]] for t in r["routed"]], w.nblk, layer.k)
+
+
+def test_block128_outputs_sampled(train720b128):
+    r = train720b128
+    w, layer = r["w"], r["layer"]
+    g = layer.grads()
+    h = 4
+    rp, ci = _seeded(r, h)
+    mask = orc.csr_to_mask(rp, ci, w.nblk)
+    blocks = [b for b in _sample_cubes(rp) if mask[b].any()]
+    q, k, v, d_o = (gu.f64(t[0, h]) for t in (r["q"], r["k"], r["v"], r["d_o"]))
+    o_f, lse = orc.fine_forward(q, k, v, mask, rows=blocks, block=128)
+    toks = orc._tokens_of(blocks, 128)
+    gu.assert_close_bf16(gu.f64(layer.o_f[0, h])[toks], o_f[toks], f"O_f head {h} blocks {blocks}")
+    np.testing.assert_allclose(gu.f64(layer.lse[0, h])[toks], lse[toks], atol=1e-3)
+    oc_hat, _, gate_saved = layer.saved_views()
+    want_oc, _, _ = orc.coarse_forward(q, k, v, w.grid, block=128)
+    gu.assert_close_bf16(gu.f64(oc_hat[0, h]), want_oc, f"O_hat_c head {h}")
+    gate = orc.gate(gu.f64(r["x"][0][torch.from_numpy(toks).to(_dev())]), gu.f64(r["w_g"]))[:, h]
+    want_o = gate[:, None] * want_oc[toks // 128] + o_f[toks]
+    gu.assert_close_bf16(gu.f64(layer.o[0, h])[toks], want_o, f"O head {h}", rounding=2.0 ** -8)
+    sub = np.zeros_like(mask)
+    sub[blocks] = mask[blocks]
+    dq, _, _ = orc.fine_backward(q, k, v, sub, d_o, block=128)
+    rr = gu.rel_l2(gu.f64(g["dq"][0, h])[toks], dq[toks])
+    assert rr <= 2e-2, f"dQ head {h}: rel-L2 {rr:.3g}"
+    lens = mask.sum(axis=0)
+    j = int(np.argmin(np.where(lens > 0, lens, lens.max() + 1)))  # the shortest column keeps the oracle quick
+    rows = np.nonzero(mask[:, j])[0]
+    sub = np.zeros_like(mask)
+    sub[rows] = mask[rows]
+    _, dk, dv = orc.fine_backward(q, k, v, sub, d_o, block=128)
+    tj = np.arange(128 * j, 128 * j + 128)
+    for name, got, want in (("dK", g["dk"], dk), ("dV", g["dv"], dv)):
+        rr = gu.rel_l2(gu.f64(got[0, h])[tj], want[tj])
+        assert rr <= 2e-2, f"{name} head {h} KV block {j} ({len(rows)} query blocks): rel-L2 {rr:.3g}"
