@@ -21,6 +21,14 @@ Conventions shared with the library interface:
     (cubes 2m and 2m+1), so G = 16 and the grid's x side is padded to a
     multiple of 8.  Blocks are numbered like the cube pairs.
   * softmax scale 1/sqrt(d) unless given.
+  * MMDiT text conditioning ([VSA2] §2.2 after Eq.(12): the fine branch
+    extends to full video-to-text and text-to-video attention; the blog's
+    §06 keeps both dense): n_text text tokens follow the video slots in Q, K,
+    V, padded to the tensors' length.  Reading: the joint attention is
+    block-sparse only between video blocks; video-text, text-video and
+    text-text attention are dense (MMDiT joint attention), one softmax per
+    query row.  The router, the coarse branch and the gate see the video
+    alone; a text row's O is its O_f.
   * a latent grid whose sides are not multiples of 4 is padded up to the next
     multiple along each axis (§2.2 "Kernel Implementation"); tensors hold the
     padded grid in the order above, and the pad positions are not tokens.
@@ -264,33 +272,59 @@ def _tokens_of(blocks, block=64):
     return (np.asarray(blocks)[:, None] * block + np.arange(block)[None, :]).reshape(-1)
 
 
-def fine_forward(q, k, v, mask, scale=None, rows=None, valid=None, block=64):
-    """Block-sparse attention of one head (Eq.(12), with the -inf mask of §2.1
-    outside the selected (B x B) tiles; mask is over blocks).
+def _token_sets(L, mask, valid, block, n_text):
+    """Real-token flags of all L rows, the video length and the text tokens.
 
-    Returns O_f [L, d] and the natural-log LSE [L].  A query cube with no
-    selected KV cube has O_f = 0 and LSE = -inf (the paper does not treat empty
-    rows).  ``rows`` limits the work to some query blocks; other rows are NaN.
-    ``valid`` [L] marks the real tokens of a padded grid: pad keys are masked,
-    pad query rows get O_f = 0 and LSE = -inf.
+    Rows [0, Lv) are the video slots (Lv = nb * block), rows [Lv, Lv +
+    n_text) the text tokens of MMDiT conditioning ([VSA2] §2.2 after
+    Eq.(12)), and any rows after them text padding.
+    """
+    Lv = mask.shape[0] * block
+    ok = np.zeros(L, bool)
+    ok[:Lv] = True if valid is None else np.asarray(valid, bool)[:Lv]
+    ok[Lv:Lv + n_text] = True
+    return ok, Lv, np.arange(Lv, Lv + n_text)
+
+
+def _query_groups(mask, ok, Lv, text, block, rows):
+    """(query rows, key rows) of each softmax group: a video query block sees
+    its selected video blocks and every text token; the text queries see every
+    video token and every text token (video-text and text-text attention stay
+    dense).  Pad rows take part in neither side."""
+    nb = mask.shape[0]
+    for i in (range(nb) if rows is None else rows):
+        qt = _tokens_of([i], block)
+        toks = np.concatenate([_tokens_of(np.nonzero(mask[i])[0], block), text])
+        yield qt, qt[ok[qt]], toks[ok[toks]]
+    if len(text):
+        allv = np.arange(Lv)
+        yield text, text, np.concatenate([allv[ok[:Lv]], text])
+
+
+def fine_forward(q, k, v, mask, scale=None, rows=None, valid=None, block=64, n_text=0):
+    """Block-sparse attention of one head (Eq.(12), with the -inf mask of §2.1
+    outside the selected (B x B) tiles; mask is over the video blocks).
+
+    Returns O_f [L, d] and the natural-log LSE [L].  A query block that sees
+    no key has O_f = 0 and LSE = -inf (the paper does not treat empty rows).
+    ``rows`` limits the work to some query blocks; other video rows are NaN.
+    ``valid`` [Lv] marks the real tokens of a padded video grid: pad keys are
+    masked, pad query rows get O_f = 0 and LSE = -inf.  ``n_text`` text tokens
+    follow the video rows (MMDiT conditioning; the rows after them are text
+    padding): every video query also attends to all of them, and they attend
+    to every video and text token.
     """
     q, k, v = (np.asarray(t, np.float64) for t in (q, k, v))
     L, d = q.shape
-    nb = L // block
-    ok = np.ones(L, bool) if valid is None else np.asarray(valid, bool)
+    ok, Lv, text = _token_sets(L, mask, valid, block, n_text)
     sc = _scale(d, scale)
     o = np.full((L, v.shape[1]), np.nan)
     lse = np.full(L, np.nan)
-    for i in (range(nb) if rows is None else rows):
-        sl = slice(block * i, block * i + block)
-        cols = np.nonzero(mask[i])[0]
-        o[sl], lse[sl] = 0.0, -np.inf
-        if len(cols) == 0:
+    o[Lv:], lse[Lv:] = 0.0, -np.inf
+    for allq, qt, toks in _query_groups(mask, ok, Lv, text, block, rows):
+        o[allq], lse[allq] = 0.0, -np.inf
+        if len(toks) == 0 or len(qt) == 0:
             continue
-        qt = _tokens_of([i], block)
-        qt = qt[ok[qt]]
-        toks = _tokens_of(cols, block)
-        toks = toks[ok[toks]]
         s = q[qt] @ k[toks].T * sc
         m = s.max(axis=1, keepdims=True)
         e = np.exp(s - m)
@@ -300,24 +334,19 @@ def fine_forward(q, k, v, mask, scale=None, rows=None, valid=None, block=64):
     return o, lse
 
 
-def fine_backward(q, k, v, mask, d_o, scale=None, valid=None, block=64):
+def fine_backward(q, k, v, mask, d_o, scale=None, valid=None, block=64, n_text=0):
     """Gradients of Eq.(12) with the mask held fixed (the router takes no
-    gradient, §2.1-§2.2).  Returns dQ, dK, dV [L, d]; with ``valid`` (see
-    fine_forward) pad rows take no part and get zero gradients."""
+    gradient, §2.1-§2.2).  Returns dQ, dK, dV [L, d]; with ``valid`` and
+    ``n_text`` (see fine_forward) pad rows take no part and get zero
+    gradients."""
     q, k, v, d_o = (np.asarray(t, np.float64) for t in (q, k, v, d_o))
     L, d = q.shape
-    nb = L // block
-    ok = np.ones(L, bool) if valid is None else np.asarray(valid, bool)
+    ok, Lv, text = _token_sets(L, mask, valid, block, n_text)
     sc = _scale(d, scale)
     dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
-    for i in range(nb):
-        cols = np.nonzero(mask[i])[0]
-        if len(cols) == 0:
+    for _, qt, toks in _query_groups(mask, ok, Lv, text, block, None):
+        if len(toks) == 0 or len(qt) == 0:
             continue
-        qt = _tokens_of([i], block)
-        qt = qt[ok[qt]]
-        toks = _tokens_of(cols, block)
-        toks = toks[ok[toks]]
         s = q[qt] @ k[toks].T * sc
         p = _softmax_rows(s)                       # [rows, keys]
         o = p @ v[toks]
@@ -422,45 +451,58 @@ def coarse_gate_backward(q, k, v, grid, x, w_g, d_o, scale=None, block=64):
 # ----------------------------------------------------------------------------
 # the whole layer
 # ----------------------------------------------------------------------------
-def vsa2_forward(q, k, v, grid, topk, x, w_g, scale=None, bf16_pooled=False, mask=None, block=64):
+def vsa2_forward(q, k, v, grid, topk, x, w_g, scale=None, bf16_pooled=False, mask=None, block=64, n_text=0):
     """One batch element, all heads: router -> TopK -> fine + coarse -> merge.
 
-    q, k, v: [H, L, d]; x [L, Dm]; w_g [Dm, H].  ``mask`` [H, nb, nb] skips the
-    router and uses a given selection.  Returns a dict of every intermediate.
+    q, k, v: [H, L, d] (the video slots, then, with ``n_text``, the text rows of
+    MMDiT conditioning padded to the tensor's length); x [Lv, Dm] (video);
+    w_g [Dm, H].  ``mask`` [H, nb, nb] skips the router and uses a given
+    selection.  The router, the coarse branch and the gate see the video
+    alone; a text row's O is its O_f.  Returns a dict of every intermediate.
     """
     H = q.shape[0]
     ok = token_valid(grid, block)
+    Lv = len(ok)
     g = gate(x, w_g, ok)
     res = {"scores": [], "mask": [], "o_f": [], "lse": [], "oc_hat": [], "lse_c": [], "o": [], "g": g}
     for h in range(H):
         if mask is None:
-            p_r = router_scores(q[h], k[h], grid, scale=scale, bf16_pooled=bf16_pooled, block=block)
+            p_r = router_scores(q[h][:Lv], k[h][:Lv], grid, scale=scale, bf16_pooled=bf16_pooled, block=block)
             m = topk_per_sequence(p_r, topk)[0]
             res["scores"].append(p_r)
         else:
             m = mask[h]
-        o_f, lse = fine_forward(q[h], k[h], v[h], m, scale, valid=ok, block=block)
-        oc_hat, lse_c, _ = coarse_forward(q[h], k[h], v[h], grid, scale, block)
+        o_f, lse = fine_forward(q[h], k[h], v[h], m, scale, valid=ok, block=block, n_text=n_text)
+        oc_hat, lse_c, _ = coarse_forward(q[h][:Lv], k[h][:Lv], v[h][:Lv], grid, scale, block)
         res["mask"].append(m)
         res["o_f"].append(o_f)
         res["lse"].append(lse)
         res["oc_hat"].append(oc_hat)
         res["lse_c"].append(lse_c)
-        res["o"].append(merge(g[:, h], oc_hat, o_f, block))
+        o = o_f.copy()
+        o[:Lv] = merge(g[:, h], oc_hat, o_f[:Lv], block)
+        res["o"].append(o)
     return {n: (np.stack(t) if isinstance(t, list) and t else t) for n, t in res.items()}
 
 
-def vsa2_backward(q, k, v, grid, mask, x, w_g, d_o, scale=None, block=64):
+def vsa2_backward(q, k, v, grid, mask, x, w_g, d_o, scale=None, block=64, n_text=0):
     """Gradients of the whole layer (router excluded) for one batch element.
-    Returns dq, dk, dv [H, L, d], dx [L, Dm], dw_g [Dm, H]."""
+    Returns dq, dk, dv [H, L, d], dx [Lv, Dm], dw_g [Dm, H]; text rows (see
+    vsa2_forward) get their gradients from the fine branch alone."""
     H = q.shape[0]
     ok = token_valid(grid, block)
+    Lv = len(ok)
     dq, dk, dv = [], [], []
     for h in range(H):
-        a, b, c = fine_backward(q[h], k[h], v[h], mask[h], d_o[h], scale, valid=ok, block=block)
+        a, b, c = fine_backward(q[h], k[h], v[h], mask[h], d_o[h], scale, valid=ok, block=block, n_text=n_text)
         dq.append(a); dk.append(b); dv.append(c)
-    _, _, _, cq, ck, cv, dx, dw = coarse_gate_backward(q, k, v, grid, x, w_g, d_o, scale, block)
-    return np.stack(dq) + cq, np.stack(dk) + ck, np.stack(dv) + cv, dx, dw
+    dq, dk, dv = np.stack(dq), np.stack(dk), np.stack(dv)
+    _, _, _, cq, ck, cv, dx, dw = coarse_gate_backward(q[:, :Lv], k[:, :Lv], v[:, :Lv], grid, x, w_g,
+                                                       np.asarray(d_o)[:, :Lv], scale, block)
+    dq[:, :Lv] += cq
+    dk[:, :Lv] += ck
+    dv[:, :Lv] += cv
+    return dq, dk, dv, dx, dw
 
 
 # ----------------------------------------------------------------------------

@@ -623,3 +623,94 @@ def test_block128_padded_fine_and_coarse_autograd():
     np.testing.assert_allclose(res["oc_hat"], oc.detach().numpy(), rtol=1e-12)
     assert res["mask"].shape == (H, 8, 8) and res["mask"].sum() == H * 24
     assert np.all(res["o"][:, ~real] == 0)
+
+
+# ----------------------------------------------------------------------------- MMDiT text tokens
+# Text rows follow the video slots (padded to a multiple of 64 here); video
+# queries see their selected video blocks and every text token, text queries
+# see every video and text token.
+def _joint_keep(mask, block, n_video, n_text, n_rows):
+    """Explicit [n_rows, n_rows] token mask of the joint attention (real rows
+    only: video slots [0, n_video), text [n_video, n_video + n_text))."""
+    keep = np.zeros((n_rows, n_rows), bool)
+    keep[:n_video, :n_video] = np.kron(mask, np.ones((block, block), bool))
+    t = slice(n_video, n_video + n_text)
+    keep[:n_video, t] = True
+    keep[t, :n_video + n_text] = True
+    return keep
+
+
+@pytest.mark.parametrize("block", [64, 128])
+def test_text_joint_attention_against_dense(block):
+    nv, nt, rows = 512, 50, 576                         # text padded to 64 rows
+    q, k, v = _rand(rows, 16), _rand(rows, 16), _rand(rows, 16)
+    nbk = nv // block
+    mask = rng.random((nbk, nbk)) < 0.4
+    mask[1] = False                                     # a video block whose only keys are text
+    keep = _joint_keep(mask, block, nv, nt, rows)
+    o, lse = orc.fine_forward(q, k, v, mask, block=block, n_text=nt)
+    real = np.arange(rows) < nv + nt
+    want = _sdpa(q[real], k[real], v[real], keep[np.ix_(real, real)], 0.25)
+    np.testing.assert_allclose(o[real], want, rtol=1e-12, atol=1e-13)
+    assert np.all(o[~real] == 0) and np.all(np.isneginf(lse[~real]))
+    s = torch.tensor(q @ k.T * 0.25).masked_fill(~torch.tensor(keep), -np.inf)
+    np.testing.assert_allclose(lse[real], torch.logsumexp(s, -1).numpy()[real], rtol=1e-12)
+    # with every video block selected the joint attention is full attention over all tokens
+    full, _ = orc.fine_forward(q, k, v, np.ones((nbk, nbk), bool), block=block, n_text=nt)
+    np.testing.assert_allclose(full[real], _sdpa(q[real], k[real], v[real], None, 0.25), rtol=1e-12, atol=1e-13)
+    # and the fine backward is the gradient of it
+    d_o = _rand(rows, 16)
+    got = orc.fine_backward(q, k, v, mask, d_o, block=block, n_text=nt)
+    t = [torch.tensor(a, requires_grad=True) for a in (q, k, v)]
+    sc = (t[0] @ t[1].T * 0.25).masked_fill(~torch.tensor(keep), -np.inf)
+    (torch.softmax(sc, -1).nan_to_num(0.0) @ t[2] * torch.tensor(d_o * real[:, None])).sum().backward()
+    for g, w in zip(got, t):
+        np.testing.assert_allclose(g, w.grad.numpy(), rtol=1e-10, atol=1e-12)
+
+
+def test_text_layer_autograd_on_a_padded_grid():
+    """Whole layer with text on the padded 5x6x7 grid, against torch autograd
+    in raster order: the joint fine attention, the coarse branch and gate on
+    the video tokens, O = O_f on the text rows."""
+    H, d, dm, nt = 2, 6, 10, 37
+    fields = [_rand(210 + nt, H * d) for _ in range(4)] + [_rand(210, dm)]
+    (vq, vk, vv, vdo, x), perm, real = _padded([f[:210] for f in fields[:4]] + [fields[4]], PGRID)
+    Lv, rows = len(perm), len(perm) + 64
+    split = lambda a: a.reshape(-1, H, d).transpose(1, 0, 2).copy()
+    tiled = []
+    for f, vid in zip(fields[:4], (vq, vk, vv, vdo)):
+        a = np.concatenate([vid, f[210:], 9.0 + rng.standard_normal((64 - nt, H * d))])
+        tiled.append(split(a))
+    q, k, v, d_o = tiled
+    w_g = _rand(dm, H) * 0.4
+    mask = np.stack([rng.random((8, 8)) < 0.5 for _ in range(H)])
+    mask[0, 3] = False
+    res = orc.vsa2_forward(q, k, v, PGRID, 3, x, w_g, mask=mask, n_text=nt)
+    got = orc.vsa2_backward(q, k, v, PGRID, mask, x, w_g, d_o, n_text=nt)
+    # raster order: 210 video tokens, then the text tokens
+    cube = torch.tensor(_raster_cube_ids(PGRID))
+    n = torch.bincount(cube, minlength=8).double()
+    tq, tk, tv = (torch.tensor(split(f), requires_grad=True) for f in fields[:3])
+    tx, tw = torch.tensor(fields[4], requires_grad=True), torch.tensor(w_g, requires_grad=True)
+    keep = torch.zeros(H, 210 + nt, 210 + nt, dtype=torch.bool)
+    for h in range(H):
+        keep[h, :210, :210] = torch.tensor(mask[h])[cube[:, None], cube[None, :]]
+    keep[:, :210, 210:] = True
+    keep[:, 210:, :] = True
+    s = (tq @ tk.transpose(1, 2) / np.sqrt(d)).masked_fill(~keep, -np.inf)
+    o_f = torch.softmax(s, -1).nan_to_num(0.0) @ tv
+    mean = lambda t: torch.zeros(H, 8, d, dtype=torch.float64).index_add(1, cube, t[:, :210]) / n[None, :, None]
+    oc = torch.softmax(mean(tq) @ mean(tk).transpose(1, 2) / np.sqrt(d), -1) @ mean(tv)
+    g = torch.tanh(tx @ tw)
+    o = torch.cat([g.T[:, :, None] * oc[:, cube] + o_f[:, :210], o_f[:, 210:]], dim=1)
+    (o * torch.tensor(split(fields[3]))).sum().backward()
+    order = np.argsort(perm[real])
+    rows_v = np.nonzero(real)[0][order]                   # tiled slot of every raster video token
+    rows_all = np.concatenate([rows_v, Lv + np.arange(nt)])
+    np.testing.assert_allclose(res["o"][:, rows_all], o.detach().numpy(), rtol=1e-11, atol=1e-12)
+    assert np.all(res["o"][:, Lv + nt:] == 0) and np.all(res["o"][:, :Lv][:, ~real] == 0)
+    for g_, w_ in zip(got[:3], (tq, tk, tv)):
+        np.testing.assert_allclose(g_[:, rows_all], w_.grad.numpy(), rtol=1e-10, atol=1e-12)
+        assert np.all(g_[:, Lv + nt:] == 0)
+    np.testing.assert_allclose(got[3][real][order], tx.grad.numpy(), rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(got[4], tw.grad.numpy(), rtol=1e-10, atol=1e-12)
