@@ -24,6 +24,15 @@
  *    blocks are numbered like these cube pairs.  B = 128 is the blog's
  *    inference for the paper's own runs (its §07); the paper gives no 3D cut.
  *    "nb" below counts blocks: nb = L / B.
+ *  - MMDiT text conditioning (§2.2 after Eq.(12): the fine branch extends to
+ *    full video-to-text and text-to-video attention): with text_tokens = Nt
+ *    > 0 every per-token tensor of the attention (Q, K, V, O_f, O, dO, dQ,
+ *    dK, dV and LSE) holds L video slots followed by Lt = 64 ceil(Nt / 64)
+ *    text rows, the last Lt - Nt of them padding: [batch, heads, L + Lt, d].
+ *    Video queries attend to their selected video blocks and to every text
+ *    token; text queries attend to every video and text token (one softmax
+ *    per row).  The router, TopK, coarse branch and gate see the video alone
+ *    (X, dX, G stay [.., L, ..]); a text row's O is its O_f.
  *  - Padded grids (§2.2 "Kernel Implementation"): a latent side that is not a
  *    multiple of the block's side (4, and 8 along x for B = 128) is padded up
  *    to one, and every tensor holds the padded grid: L = B nb slots with
@@ -82,6 +91,7 @@ typedef struct vsa2_problem {
   int32_t dtype;          /* vsa2_dtype of Q, K, V, O_f, O, dO, dQ, dK, dV, X, dX     */
   float softmax_scale;    /* <= 0 selects 1/sqrt(head_dim)                            */
   int32_t block_tokens;   /* attention block B: 64 (0 selects it) or 128, see above   */
+  int32_t text_tokens;    /* MMDiT text tokens Nt >= 0 joining the fine branch, above */
 } vsa2_problem;
 
 /* Human-readable name of a status code (static string). */

@@ -32,6 +32,7 @@ class Workload:
     train: bool = False    # forward + backward
     extra_topk: tuple = field(default_factory=tuple)
     block: int = 64        # attention block: 64 (a 4x4x4 cube) or 128 (4x4x8, two x-adjacent cubes)
+    text: int = 0          # MMDiT text tokens joining the fine branch (rows after the video slots)
 
     @property
     def pgrid(self):
@@ -49,6 +50,12 @@ class Workload:
         """Token slots per (batch, head): the padded grid's size."""
         t, y, x = self.pgrid
         return t * y * x
+
+    @property
+    def rows(self):
+        """Token rows per (batch, head) of the attention tensors: the video
+        slots, then the text tokens padded to a multiple of 64."""
+        return self.L + 64 * -(-self.text // 64)
 
     @property
     def L_real(self):

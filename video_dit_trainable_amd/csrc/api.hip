@@ -21,6 +21,7 @@ size_t up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
 struct Dims {
   int batch, heads, bh, d, L, nb, nbp, Lr;
   int nc, bs;
+  int nt, ntc, ld;  // MMDiT text tokens, their 64-row cubes, token rows per head (L + 64 ntc)
   bool bf16;
   size_t esz;
   float scale;
@@ -35,6 +36,7 @@ int check_problem(const vsa2_problem* p, Dims& o) {
   if (p->lat_t > (1 << 20) || p->lat_y > (1 << 20) || p->lat_x > (1 << 20)) return VSA2_E_SHAPE;
   if (p->dtype != VSA2_F32 && p->dtype != VSA2_BF16) return VSA2_E_ARG;
   if (p->block_tokens != 0 && p->block_tokens != 64 && p->block_tokens != 128) return VSA2_E_SHAPE;
+  if (p->text_tokens < 0 || p->text_tokens > (1 << 20)) return VSA2_E_SHAPE;
   const int bs = p->block_tokens == 128 ? 1 : 0;  // a 128-token block is two x-adjacent cubes
   // a grid that is not a whole number of blocks is padded up to one
   const int64_t xs = 4 << bs;
@@ -54,6 +56,9 @@ int check_problem(const vsa2_problem* p, Dims& o) {
   o.nbp = (int)((nb + 63) / 64 * 64);
   o.nc = (int)nc;
   o.bs = bs;
+  o.nt = p->text_tokens;
+  o.ntc = (p->text_tokens + 63) / 64;
+  o.ld = o.L + 64 * o.ntc;
   o.Lr = (int)(L / 8);
   o.bf16 = p->dtype == VSA2_BF16;
   o.esz = o.bf16 ? 2 : 4;
@@ -126,7 +131,7 @@ size_t ws_plan(const Dims& d, TopkWs* w, void* base) {
   return o_bm + up((size_t)d.bh * d.nb * bitmap_words(d) * 4);
 }
 
-size_t ws_bwd(const Dims& d) { return up((size_t)d.bh * d.L * 8); }      // (lse2, delta) per token
+size_t ws_bwd(const Dims& d) { return up((size_t)d.bh * d.ld * 8); }     // (lse2, delta) per token row
 
 size_t ws_fwd(const Dims&) { return 0; }  // the forward needs no scratch
 
@@ -327,7 +332,7 @@ int vsa2_pool(const vsa2_problem* p, const void* q, const void* k, const void* v
   if (!aligned(q) || !aligned(k) || !aligned(v) || !aligned(pooled)) return VSA2_E_ARG;
   Pooled pp = pooled_ptrs(d, pooled);
   PoolArgs a{q, k, v, (void*)pp.qr, (void*)pp.kr, (void*)pp.qc, (void*)pp.kc, (void*)pp.vc, d.bh, d.nc, d.nbp, d.d,
-             d.bf16, d.pad, d.bs};
+             d.bf16, d.pad, d.bs, d.ld};
   return hip_status(launch_pool(a, (hipStream_t)stream));
 }
 
@@ -400,13 +405,14 @@ int vsa2_sparse_attn_fwd(const vsa2_problem* p, int32_t topk, const void* q, con
   a.q = q; a.k = k; a.v = v;
   a.row_ptr = row_ptr; a.col_idx = col_idx;
   a.o = o_f; a.lse = lse;
-  a.bh = d.bh; a.nq = d.nc; a.nkv = d.nc; a.seq = d.L; a.ld = d.L; a.out_rows = d.L;
+  a.bh = d.bh; a.nq = d.nc; a.nkv = d.nc; a.seq = d.ld; a.ld = d.ld; a.out_rows = d.ld;
   a.kph = budget(d, topk);
   a.d = d.d; a.bf16 = d.bf16; a.dense = false;
   a.scale_log2 = d.scale * 1.4426950408889634f;
   a.ct = d.pad.nt; a.cy = d.pad.ny; a.cx = d.pad.nx;
   a.pad = d.pad;
   a.bs = d.bs;
+  a.ntc = d.ntc; a.ntext = d.nt;
   return hip_status(launch_attn_fwd(a, (hipStream_t)stream));
 }
 
@@ -435,7 +441,7 @@ int vsa2_sparse_attn_bwd(const vsa2_problem* p, int32_t topk, const void* q, con
   a.dk_add = dqkv_c ? dqkv_c + cstride : nullptr;
   a.dv_add = dqkv_c ? dqkv_c + 2 * cstride : nullptr;
   a.dq = dq; a.dk = dk; a.dv = dv;
-  a.bh = d.bh; a.nq = d.nc; a.nkv = d.nc; a.seq = d.L; a.ld = d.L; a.out_rows = d.L;
+  a.bh = d.bh; a.nq = d.nc; a.nkv = d.nc; a.seq = d.ld; a.ld = d.ld; a.out_rows = d.ld;
   a.kph = budget(d, topk);
   a.d = d.d; a.bf16 = d.bf16; a.dense = false;
   a.scale = d.scale;
@@ -443,6 +449,7 @@ int vsa2_sparse_attn_bwd(const vsa2_problem* p, int32_t topk, const void* q, con
   a.ct = d.pad.nt; a.cy = d.pad.ny; a.cx = d.pad.nx;
   a.pad = d.pad;
   a.bs = d.bs;
+  a.ntc = d.ntc; a.ntext = d.nt;
   return hip_status(launch_attn_bwd(a, st));
 }
 
@@ -469,7 +476,7 @@ int vsa2_coarse_gate(const vsa2_problem* p, const void* pooled, const void* x, i
   a.scale_log2 = d.scale * 1.4426950408889634f;
   hipError_t e = launch_attn_fwd(a, st);
   if (e != hipSuccess) return VSA2_E_HIP;
-  GateArgs ga{x, w_g, ws, oc_hat, o_f, o, g, d.batch, d.heads, d.nc, d.d, d_model, d.bf16, d.pad, d.bs};
+  GateArgs ga{x, w_g, ws, oc_hat, o_f, o, g, d.batch, d.heads, d.nc, d.d, d_model, d.bf16, d.pad, d.bs, d.ld};
   return hip_status(launch_gate_fwd(ga, st));
 }
 
@@ -492,7 +499,7 @@ int vsa2_coarse_gate_bwd(const vsa2_problem* p, const void* pooled, const void* 
   const float* lse_c = oc_hat + (size_t)d.bh * d.nb * d.d;
   const float* g = lse_c + (size_t)d.bh * d.nb;
   GateBwdArgs ga{x, w_g, w.wt, oc_hat, g, d_o, w.dpre, w.doc, lse_c, w.stats_c, w.dw_part, dx, dw_g,
-                 d.batch, d.heads, d.nc, d.nbp, d.d, d_model, nchunk_of(d), d.bf16, d.pad, d.bs, w.doc_part};
+                 d.batch, d.heads, d.nc, d.nbp, d.d, d_model, nchunk_of(d), d.bf16, d.pad, d.bs, w.doc_part, d.ld};
   hipError_t e = launch_gate_bwd(ga, st);
   if (e != hipSuccess) return VSA2_E_HIP;
   AttnBwdArgs a{};

@@ -132,7 +132,11 @@ __device__ __forceinline__ void dkdv_pair(const T* qs, const T* dos, const float
 // dK, dV rows are zero; pad query rows arrive with lse2 = +inf (P = 0).
 // BS: 2^BS cubes per attention block; the CSC lists query blocks, and list
 // position n is query cube (entry << BS) + (n mod 2^BS).
-template <typename T, typename TO, int D, bool DENSE, bool PAD, int BS>
+// TEXT (MMDiT conditioning): ntc text cubes (ntext tokens) follow the video
+// cubes; a video KV cube's list continues with every text query cube (text
+// attends to all video), a text KV cube's list is every video and text query
+// cube.  The text KV cubes take the first blocks of the grid.
+template <typename T, typename TO, int D, bool DENSE, bool PAD, int BS, bool TEXT>
 __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(const T* __restrict__ q, const T* __restrict__ k,
                                                      const T* __restrict__ v, const T* __restrict__ d_o,
                                                      const float* __restrict__ stats,
@@ -141,44 +145,72 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(const T* __restrict__ q, co
                                                      const float* __restrict__ dk_add,
                                                      const float* __restrict__ dv_add, TO* __restrict__ dk,
                                                      TO* __restrict__ dv, int nq, int nkv, int seq, int ld,
-                                                     int out_rows, int64_t kph, float scale, float c, PadGrid pad) {
+                                                     int out_rows, int64_t kph, float scale, float c, PadGrid pad,
+                                                     int ntc, int ntext, int nbh) {
   static_assert(!(DENSE && PAD), "padding applies to the fine branch");
   static_assert(!DENSE || BS == 0, "the dense mode has one cube per block");
+  static_assert(!(DENSE && TEXT), "text rows apply to the fine branch");
   constexpr int TILE = 64 * D;
   __shared__ __align__(16) T tA[2 * TILE];  // stage A: Q tile | dO tile
   __shared__ __align__(16) T tB[2 * TILE];  // stage B
   __shared__ __align__(16) float sA[128];   // stage A row statistics: [row][lse2, delta]
   __shared__ __align__(16) float sB[128];
   int bh, j;
-  if (!xcd_work(blockIdx.x, nkv, bh, j)) return;
+  bool textk = false;  // a text KV cube
+  if constexpr (TEXT) {
+    const int tblk = (ntc * nbh + 7) & ~7;  // a multiple of 8 keeps the video blocks' XCD map
+    if ((int)blockIdx.x < tblk) {
+      if ((int)blockIdx.x >= ntc * nbh) return;
+      bh = blockIdx.x / ntc;
+      j = nkv + blockIdx.x % ntc;
+      textk = true;
+    } else {
+      if (!xcd_work(blockIdx.x - tblk, nkv, bh, j)) return;
+    }
+  } else {
+    if (!xcd_work(blockIdx.x, nkv, bh, j)) return;
+  }
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, cc = lane & 15;
   const int kh = w & 1, qh = w >> 1;
   const size_t hoff = (size_t)bh * ld * D;
 
-  int cnt;
+  int cnt, nsel = 0;  // list length; nsel = selected entries before the text query cubes
   const int32_t* rows = nullptr;
   if constexpr (DENSE) {
     cnt = nq;
+  } else if (TEXT && textk) {
+    cnt = nq + ntc;
   } else {
     const int32_t* cp = col_ptr + (size_t)bh * ((nkv >> BS) + 1);
     const int64_t start = min<int64_t>(max(cp[j >> BS], 0), kph);
     const int64_t end = min<int64_t>(max<int64_t>(cp[(j >> BS) + 1], start), kph);
     cnt = (int)(end - start) << BS;
     rows = row_idx + (size_t)bh * kph + start;
+    nsel = cnt;
+    if constexpr (TEXT) cnt += ntc;
   }
   // list entry of position n (DENSE: the query tile n); read one step before
   // its copy is started, so the load is complete at the wait that precedes
   // the copy
   auto entry = [&](int n) -> int {
     if constexpr (DENSE) return n;
-    else return rows[n >> BS];
+    if constexpr (TEXT) {
+      if (textk || n >= nsel) return 0;  // positions past the selection need no load
+    }
+    return rows[n >> BS];
   };
-  // query cube of an entry at a position whose low BS bits are `sub` (stage A
-  // takes the even positions, stage B the odd ones); a corrupt sparse entry
-  // is fetched as cube 0 and skipped.  The entry stays in a vector register
-  // until here (opaque), so its load is only waited for after the copies
-  // issued behind it have been waited for anyway.
-  auto cube_of = [&](int raw, int sub, bool& ok) -> int {
+  // query cube of an entry at list position pos (whose low BS bits are `sub`:
+  // stage A takes the even positions, stage B the odd ones); a corrupt sparse
+  // entry is fetched as cube 0 and skipped.  The entry stays in a vector
+  // register until here (opaque), so its load is only waited for after the
+  // copies issued behind it have been waited for anyway.
+  auto cube_of = [&](int raw, int sub, int pos, bool& ok) -> int {
+    if constexpr (TEXT) {
+      if (textk || pos >= nsel) {
+        ok = true;
+        return textk ? pos : nq + (pos - nsel);
+      }
+    }
     if constexpr (!DENSE) opaque(raw);
     raw = __builtin_amdgcn_readfirstlane(raw);
     if constexpr (BS > 0) raw = (int)(((unsigned)raw << BS) | (unsigned)sub);
@@ -200,12 +232,20 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(const T* __restrict__ q, co
 
   Frag<T> kf[2][D / 32], vf[2][D / 32];
   bool kv_ok[2];
-  uint64_t km = ~0ull;  // PAD: real slots of cube j
-  if constexpr (PAD) km = cube_slots(j, pad);
+  uint64_t km = ~0ull;  // PAD / TEXT: real slots of cube j
+  if constexpr (TEXT) {
+    if (textk) {
+      const int nr = ntext - 64 * (j - nkv);
+      km = nr >= 64 ? ~0ull : (1ull << nr) - 1;
+    }
+  }
+  if constexpr (PAD) {
+    if (!textk) km = cube_slots(j, pad);
+  }
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
     const int key = j * 64 + 32 * kh + 16 * kb + cc;
-    kv_ok[kb] = PAD ? (bool)((km >> (32 * kh + 16 * kb + cc)) & 1) : (!DENSE || key < seq);
+    kv_ok[kb] = (PAD || TEXT) ? (bool)((km >> (32 * kh + 16 * kb + cc)) & 1) : (!DENSE || key < seq);
 #pragma unroll
     for (int s = 0; s < D / 32; ++s) {
       kf[kb][s] = frag_global<T, D>(k + hoff, key, s, g);
@@ -228,7 +268,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(const T* __restrict__ q, co
   bool ok_a = false, ok_b = false;
   int raw = 0;  // list entry whose copy starts next
   if (cnt > 0) {
-    const int ii0 = cube_of(entry(0), 0, ok_a);
+    const int ii0 = cube_of(entry(0), 0, 0, ok_a);
     VSA2_FETCH_QDO(ii0, tA, sA);
     if (cnt > 1) raw = entry(1);
   }
@@ -236,7 +276,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(const T* __restrict__ q, co
     wait_vm0();
     __syncthreads();  // stage A holds entry n; every wave is done with stage B
     if (n + 1 < cnt) {
-      const int ii = cube_of(raw, 1, ok_b);
+      const int ii = cube_of(raw, 1, n + 1, ok_b);
       if (n + 2 < cnt) raw = entry(n + 2);
       VSA2_FETCH_QDO(ii, tB, sB);
     }
@@ -245,7 +285,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(const T* __restrict__ q, co
     wait_vm0();
     __syncthreads();  // stage B holds entry n + 1; every wave is done with stage A
     if (n + 2 < cnt) {
-      const int ii = cube_of(raw, 0, ok_a);
+      const int ii = cube_of(raw, 0, n + 2, ok_a);
       if (n + 3 < cnt) raw = entry(n + 3);
       VSA2_FETCH_QDO(ii, tA, sA);
     }
@@ -284,7 +324,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(const T* __restrict__ q, co
       }
   // the coarse branch's per-block gradient rows, 1/n to each of the block's
   // n real tokens (n = 64 2^BS unless the grid is padded)
-  if (dk_add) {
+  if (dk_add && !textk) {
     const float* ka = dk_add + ((size_t)bh * (nkv >> BS) + (j >> BS)) * D;
     const float* va = dv_add + ((size_t)bh * (nkv >> BS) + (j >> BS)) * D;
     float wk[2] = {1.0f / (float)(64 << BS), 1.0f / (float)(64 << BS)};
@@ -393,7 +433,11 @@ __device__ __forceinline__ void dq_pair(const T* ks, const T* vs, int brow, int 
 // the statistics (+inf, 0), so their P is 0 here and in the dK/dV kernel.
 // BS: 2^BS cubes per attention block; the CSR lists KV blocks, and list
 // position n is KV cube (entry << BS) + (n mod 2^BS).
-template <typename T, typename TO, int D, bool DENSE, bool STATS, bool PAD, int BS>
+// TEXT (MMDiT conditioning): ntc text cubes (ntext tokens) follow the nq video
+// cubes; a video query cube's list continues with every text cube, a text
+// query cube's list is every video and text cube.  The text query cubes take
+// the first blocks of the grid.
+template <typename T, typename TO, int D, bool DENSE, bool STATS, bool PAD, int BS, bool TEXT>
 __global__ __launch_bounds__(256, 2) void k_bwd_dq(const T* __restrict__ q, const T* __restrict__ k,
                                                    const T* __restrict__ v, const T* __restrict__ d_o,
                                                    const T* __restrict__ o, const float* __restrict__ lse,
@@ -402,42 +446,72 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(const T* __restrict__ q, cons
                                                    const int32_t* __restrict__ col_idx,
                                                    const float* __restrict__ dq_add, TO* __restrict__ dq, int nq,
                                                    int nkv, int seq, int ld, int out_rows, int64_t kph, float scale,
-                                                   float c, int ct, int cy, int cx, PadGrid pad) {
+                                                   float c, int ct, int cy, int cx, PadGrid pad, int ntc, int ntext,
+                                                   int nbh) {
   static_assert(!PAD || (STATS && !DENSE), "padding applies to the fine branch");
   static_assert(!DENSE || BS == 0, "the dense mode has one cube per block");
+  static_assert(!TEXT || (STATS && !DENSE), "text rows apply to the fine branch");
   constexpr int TILE = 64 * D;
   __shared__ __align__(16) T tA[2 * TILE];  // stage A: K tile | V tile
   __shared__ __align__(16) T tB[2 * TILE];  // stage B
   int bh, i;
-  if (!xcd_work(blockIdx.x, nq, bh, i)) return;
-  if (ct > 0) i = blocked_cube(i, ct, cy, cx);
+  bool textq = false;  // a text query cube
+  if constexpr (TEXT) {
+    const int tblk = (ntc * nbh + 7) & ~7;  // a multiple of 8 keeps the video blocks' XCD map
+    if ((int)blockIdx.x < tblk) {
+      if ((int)blockIdx.x >= ntc * nbh) return;
+      bh = blockIdx.x / ntc;
+      i = nq + blockIdx.x % ntc;
+      textq = true;
+    } else {
+      if (!xcd_work(blockIdx.x - tblk, nq, bh, i)) return;
+      if (ct > 0) i = blocked_cube(i, ct, cy, cx);
+    }
+  } else {
+    if (!xcd_work(blockIdx.x, nq, bh, i)) return;
+    if (ct > 0) i = blocked_cube(i, ct, cy, cx);
+  }
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, cc = lane & 15;
   const int qh = w & 1, kh = w >> 1;
   const size_t hoff = (size_t)bh * ld * D;
 
-  int cnt;
+  int cnt, nsel = 0;  // list length; nsel = selected entries before the text cubes
   const int32_t* cols = nullptr;
   if constexpr (DENSE) {
     cnt = nkv;
+  } else if (TEXT && textq) {
+    cnt = nkv + ntc;
   } else {
     const int32_t* rp = row_ptr + (size_t)bh * ((nq >> BS) + 1);
     const int64_t start = min<int64_t>(max(rp[i >> BS], 0), kph);
     const int64_t end = min<int64_t>(max<int64_t>(rp[(i >> BS) + 1], start), kph);
     cnt = (int)(end - start) << BS;
     cols = col_idx + (size_t)bh * kph + start;
+    nsel = cnt;
+    if constexpr (TEXT) cnt += ntc;
   }
   // list entry of position n (DENSE: the KV tile n), read one step before its copy starts
   auto entry = [&](int n) -> int {
     if constexpr (DENSE) return n;
-    else return cols[n >> BS];
+    if constexpr (TEXT) {
+      if (textq || n >= nsel) return 0;  // positions past the selection need no load
+    }
+    return cols[n >> BS];
   };
-  // KV cube of an entry at a position whose low BS bits are `sub`, and how
-  // many of its keys are valid (0 for a corrupt entry)
-  auto cube_of = [&](int raw, int sub, int& lim) -> int {
+  // KV cube of an entry at list position pos (whose low BS bits are `sub`),
+  // and how many of its keys are valid (0 for a corrupt entry)
+  auto cube_of = [&](int raw, int sub, int pos, int& lim) -> int {
     if constexpr (DENSE) {
       lim = min(64, seq - raw * 64);
       return raw;
     } else {
+      if constexpr (TEXT) {
+        if (textq || pos >= nsel) {
+          const int jj = textq ? pos : nkv + (pos - nsel);
+          lim = jj < nkv ? 64 : min(64, ntext - 64 * (jj - nkv));
+          return jj;
+        }
+      }
       opaque(raw);
       raw = __builtin_amdgcn_readfirstlane(raw);
       if constexpr (BS > 0) raw = (int)(((unsigned)raw << BS) | (unsigned)sub);
@@ -455,13 +529,21 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(const T* __restrict__ q, cons
   // this wave's 32 queries: Q and dO rows as B fragments (column = query 32qh + 16qb + cc)
   Frag<T> qf[2][D / 32], of[2][D / 32];
   float l2[2], ndl[2];
-  uint64_t qm = ~0ull;  // PAD: real slots of query cube i
-  if constexpr (PAD) qm = cube_slots(i, pad);
+  uint64_t qm = ~0ull;  // PAD / TEXT: real rows of query cube i
+  if constexpr (TEXT) {
+    if (textq) {
+      const int nr = ntext - 64 * (i - nq);
+      qm = nr >= 64 ? ~0ull : (1ull << nr) - 1;
+    }
+  }
+  if constexpr (PAD) {
+    if (!textq) qm = cube_slots(i, pad);
+  }
   bool qreal[2];
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     const int qrow = i * 64 + 32 * qh + 16 * qb + cc;
-    qreal[qb] = !PAD || ((qm >> (32 * qh + 16 * qb + cc)) & 1);
+    qreal[qb] = !(PAD || TEXT) || ((qm >> (32 * qh + 16 * qb + cc)) & 1);
 #pragma unroll
     for (int s = 0; s < D / 32; ++s) {
       qf[qb][s] = frag_global<T, D>(q + hoff, qrow, s, g);
@@ -503,11 +585,15 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(const T* __restrict__ q, cons
   int lim_a = 0, lim_b = 0, raw = 0;
   uint64_t km_a = ~0ull, km_b = ~0ull;  // PAD: real slots of the staged KV cubes
   auto slots_of = [&](int jj, int lim) -> uint64_t {
-    if constexpr (PAD) return lim > 0 ? cube_slots(jj, pad) : 0ull;
-    else return ~0ull;
+    if constexpr (PAD) {
+      if (TEXT && jj >= nkv) return lim >= 64 ? ~0ull : (1ull << lim) - 1;  // a text cube's tail
+      return lim > 0 ? cube_slots(jj, pad) : 0ull;
+    } else {
+      return ~0ull;
+    }
   };
   if (cnt > 0) {
-    const int j0 = cube_of(entry(0), 0, lim_a);
+    const int j0 = cube_of(entry(0), 0, 0, lim_a);
     km_a = slots_of(j0, lim_a);
     VSA2_FETCH_KV(j0, tA);
     if (cnt > 1) raw = entry(1);
@@ -516,7 +602,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(const T* __restrict__ q, cons
     wait_vm0();
     __syncthreads();  // stage A holds entry n; every wave is done with stage B
     if (n + 1 < cnt) {
-      const int jj = cube_of(raw, 1, lim_b);
+      const int jj = cube_of(raw, 1, n + 1, lim_b);
       km_b = slots_of(jj, lim_b);
       if (n + 2 < cnt) raw = entry(n + 2);
       VSA2_FETCH_KV(jj, tB);
@@ -527,7 +613,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(const T* __restrict__ q, cons
     wait_vm0();
     __syncthreads();  // stage B holds entry n + 1; every wave is done with stage A
     if (n + 2 < cnt) {
-      const int jj = cube_of(raw, 0, lim_a);
+      const int jj = cube_of(raw, 0, n + 2, lim_a);
       km_a = slots_of(jj, lim_a);
       if (n + 3 < cnt) raw = entry(n + 3);
       VSA2_FETCH_KV(jj, tA);
@@ -559,7 +645,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(const T* __restrict__ q, cons
 #pragma unroll
       for (int r = 0; r < 4; ++r)
         dqa[db][qb][r] = (dqa[db][qb][r] + mine[((db * 2 + qb) * 4 + r) * 64 + lane]) * scale;
-  if (dq_add) {  // the coarse branch's per-block gradient row, 1/n to each of the n real tokens
+  if (dq_add && !textq) {  // the coarse branch's per-block gradient row, 1/n to each of the n real tokens
     const float* qa = dq_add + ((size_t)bh * (nq >> BS) + (i >> BS)) * D;
     float wq[2] = {1.0f / (float)(64 << BS), 1.0f / (float)(64 << BS)};
     if constexpr (PAD) {
@@ -593,38 +679,46 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(const T* __restrict__ q, cons
   }
 }
 
-template <typename T, typename TO, int D, bool DENSE, bool PAD, int BS>
+template <typename T, typename TO, int D, bool DENSE, bool PAD, int BS, bool TEXT>
 hipError_t launch_bwd_tt(const AttnBwdArgs& a, hipStream_t st) {
   // dQ first: in sparse mode it writes the row statistics the dK/dV kernel reads
+  const int tblk = TEXT ? (a.ntc * a.bh + 7) & ~7 : 0;  // text cubes take the first blocks
   if (!DENSE) timer_before(TK_BWD_DQ, st);
   if constexpr (DENSE)
-    hipLaunchKernelGGL((k_bwd_dq<T, TO, D, DENSE, false, false, 0>), dim3(xcd_grid(a.nq, a.bh)), dim3(256), 0, st,
-                       (const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.d_o, nullptr, nullptr, nullptr,
+    hipLaunchKernelGGL((k_bwd_dq<T, TO, D, DENSE, false, false, 0, false>), dim3(xcd_grid(a.nq, a.bh)), dim3(256),
+                       0, st, (const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.d_o, nullptr, nullptr, nullptr,
                        a.stats, a.row_ptr, a.col_idx, a.dq_add, (TO*)a.dq, a.nq, a.nkv, a.seq, a.ld, a.out_rows, a.kph,
-                       a.scale, a.scale_log2, a.ct, a.cy, a.cx, a.pad);
+                       a.scale, a.scale_log2, a.ct, a.cy, a.cx, a.pad, 0, 0, a.bh);
   else
-    hipLaunchKernelGGL((k_bwd_dq<T, TO, D, DENSE, true, PAD, BS>), dim3(xcd_grid(a.nq, a.bh)), dim3(256), 0, st,
-                       (const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.d_o, (const T*)a.o, a.lse,
-                       a.stats_out, nullptr, a.row_ptr, a.col_idx, a.dq_add, (TO*)a.dq, a.nq, a.nkv, a.seq, a.ld,
-                       a.out_rows, a.kph, a.scale, a.scale_log2, a.ct, a.cy, a.cx, a.pad);
+    hipLaunchKernelGGL((k_bwd_dq<T, TO, D, DENSE, true, PAD, BS, TEXT>), dim3(tblk + xcd_grid(a.nq, a.bh)),
+                       dim3(256), 0, st, (const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.d_o, (const T*)a.o,
+                       a.lse, a.stats_out, nullptr, a.row_ptr, a.col_idx, a.dq_add, (TO*)a.dq, a.nq, a.nkv, a.seq,
+                       a.ld, a.out_rows, a.kph, a.scale, a.scale_log2, a.ct, a.cy, a.cx, a.pad, a.ntc, a.ntext, a.bh);
   if (!DENSE) timer_after(TK_BWD_DQ, st);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (!DENSE) timer_before(TK_BWD_DKDV, st);
-  hipLaunchKernelGGL((k_bwd_dkdv<T, TO, D, DENSE, PAD, BS>), dim3(xcd_grid(a.nkv, a.bh)), dim3(256), 0, st,
-                     (const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.d_o, DENSE ? a.stats : a.stats_out,
-                     a.col_ptr, a.row_idx, a.dk_add, a.dv_add, (TO*)a.dk, (TO*)a.dv, a.nq, a.nkv, a.seq, a.ld,
-                     a.out_rows, a.kph, a.scale, a.scale_log2, a.pad);
+  hipLaunchKernelGGL((k_bwd_dkdv<T, TO, D, DENSE, PAD, BS, TEXT>), dim3(tblk + xcd_grid(a.nkv, a.bh)), dim3(256),
+                     0, st, (const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.d_o,
+                     DENSE ? a.stats : a.stats_out, a.col_ptr, a.row_idx, a.dk_add, a.dv_add, (TO*)a.dk, (TO*)a.dv,
+                     a.nq, a.nkv, a.seq, a.ld, a.out_rows, a.kph, a.scale, a.scale_log2, a.pad, a.ntc, a.ntext, a.bh);
   if (!DENSE) timer_after(TK_BWD_DKDV, st);
   return hipGetLastError();
 }
 
 template <typename T, int D>
 hipError_t launch_bwd_t(const AttnBwdArgs& a, hipStream_t st) {
-  if (a.dense) return launch_bwd_tt<T, float, D, true, false, 0>(a, st);
-  if (a.bs)
-    return a.pad.on ? launch_bwd_tt<T, T, D, false, true, 1>(a, st) : launch_bwd_tt<T, T, D, false, false, 1>(a, st);
-  return a.pad.on ? launch_bwd_tt<T, T, D, false, true, 0>(a, st) : launch_bwd_tt<T, T, D, false, false, 0>(a, st);
+  if (a.dense) return launch_bwd_tt<T, float, D, true, false, 0, false>(a, st);
+#define VSA2_BWD(PAD, BS)                                                                              \
+  return a.ntc ? launch_bwd_tt<T, T, D, false, PAD, BS, true>(a, st)                                  \
+               : launch_bwd_tt<T, T, D, false, PAD, BS, false>(a, st)
+  if (a.bs) {
+    if (a.pad.on) VSA2_BWD(true, 1);
+    VSA2_BWD(false, 1);
+  }
+  if (a.pad.on) VSA2_BWD(true, 0);
+  VSA2_BWD(false, 0);
+#undef VSA2_BWD
 }
 
 hipError_t launch_attn_bwd(const AttnBwdArgs& a, hipStream_t st) {

@@ -3,7 +3,8 @@
 // The same kernel in "dense" mode runs the coarse branch's attention over the
 // nb pooled cube tokens (Eq.(2)-(3)), with a ragged last tile.  On a padded
 // grid (§2.2 "Kernel Implementation") pad keys are masked and pad query rows
-// give zeros.
+// give zeros.  MMDiT text rows (after Eq.(12)) join the fine branch as cubes
+// every video query attends to, and whose queries attend to everything.
 //
 // Work split: one block (2 waves) per query cube; each wave owns 32 queries as
 // MFMA B fragments in registers, so every K/V byte read from LDS feeds two
@@ -30,43 +31,74 @@ namespace vsa2 {
 // BS: 2^BS cubes per attention block.  The CSR lists blocks; query cube i
 // takes the list of its block i >> BS, and list position n is cube
 // (entry << BS) + (n mod 2^BS) of the selected block.
-template <typename T, typename TO, int D, bool DENSE, bool PAD, int BS>
+// TEXT (MMDiT conditioning): ntc text cubes (ntext tokens, rows past them are
+// padding) follow the nq video cubes.  A video query cube attends to its
+// selected cubes and then to every text cube; a text query cube attends to
+// every video and text cube.  The text query cubes take the first blocks of
+// the grid, so their long lists start first.
+template <typename T, typename TO, int D, bool DENSE, bool PAD, int BS, bool TEXT>
 __global__ __launch_bounds__(128, 2) void k_attn_fwd(const T* __restrict__ q, const T* __restrict__ k,
                                                   const T* __restrict__ v, const int32_t* __restrict__ row_ptr,
                                                   const int32_t* __restrict__ col_idx, TO* __restrict__ o,
                                                   float* __restrict__ lse, int nq, int nkv, int seq, int ld,
                                                   int out_rows, int64_t kph, float c, int ct, int cy, int cx,
-                                                  PadGrid pad) {
+                                                  PadGrid pad, int ntc, int ntext, int nbh) {
   static_assert(!(DENSE && PAD), "padding applies to the fine branch");
+  static_assert(!(DENSE && TEXT), "text rows apply to the fine branch");
   __shared__ __align__(16) T ks[64 * D];
   __shared__ __align__(16) T vs[64 * D];
   int bh, i;
-  if (!xcd_work(blockIdx.x, nq, bh, i)) return;
-  if (ct > 0) i = blocked_cube(i, ct, cy, cx);
+  bool textq = false;  // a text query cube
+  if constexpr (TEXT) {
+    const int tblk = (ntc * nbh + 7) & ~7;  // a multiple of 8 keeps the video blocks' XCD map
+    if ((int)blockIdx.x < tblk) {
+      if ((int)blockIdx.x >= ntc * nbh) return;
+      bh = blockIdx.x / ntc;
+      i = nq + blockIdx.x % ntc;
+      textq = true;
+    } else {
+      if (!xcd_work(blockIdx.x - tblk, nq, bh, i)) return;
+      if (ct > 0) i = blocked_cube(i, ct, cy, cx);
+    }
+  } else {
+    if (!xcd_work(blockIdx.x, nq, bh, i)) return;
+    if (ct > 0) i = blocked_cube(i, ct, cy, cx);
+  }
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, cc = lane & 15;
   const size_t hoff = (size_t)bh * ld * D;
   const T* kbase = k + hoff;
   const T* vbase = v + hoff;
 
-  int cnt;
+  int cnt, nsel = 0;  // list length; nsel = selected entries before the text cubes
   const int32_t* cols = nullptr;
   if constexpr (DENSE) {
     cnt = nkv;
+  } else if (TEXT && textq) {
+    cnt = nkv + ntc;
   } else {
     const int32_t* rp = row_ptr + (size_t)bh * ((nq >> BS) + 1);
     const int64_t start = min<int64_t>(max(rp[i >> BS], 0), kph);
     const int64_t end = min<int64_t>(max<int64_t>(rp[(i >> BS) + 1], start), kph);
     cnt = (int)(end - start) << BS;
     cols = col_idx + (size_t)bh * kph + start;
+    nsel = cnt;
+    if constexpr (TEXT) cnt += ntc;
   }
   // cube id of list position n; out-of-range ids (corrupt lists) become -1 = masked tile
   auto cube_at = [&](int n) -> int {
     if constexpr (DENSE) return n;
+    if constexpr (TEXT) {
+      if (textq) return n;
+      if (n >= nsel) return nkv + (n - nsel);
+    }
     const int jj = cols[n >> BS];
     return (unsigned)jj < (unsigned)(nkv >> BS) ? (jj << BS) + (n & ((1 << BS) - 1)) : -1;
   };
   auto kv_limit = [&](int jj) -> int {  // valid keys of cube jj
     if constexpr (DENSE) return min(64, seq - jj * 64);
+    if constexpr (TEXT) {
+      if (jj >= nkv) return min(64, ntext - 64 * (jj - nkv));
+    }
     return jj >= 0 ? 64 : 0;
   };
 
@@ -93,8 +125,8 @@ __global__ __launch_bounds__(128, 2) void k_attn_fwd(const T* __restrict__ q, co
       sw_store(vr, vs, tid);
       __syncthreads();
       const int lim = kv_limit(j);
-      uint64_t km = ~0ull;  // PAD: real slots of cube j
-      if constexpr (PAD) km = j >= 0 ? cube_slots(j, pad) : 0ull;
+      uint64_t km = ~0ull;  // PAD: real slots of cube j (text cubes: their tail goes by lim)
+      if constexpr (PAD) km = j < 0 ? 0ull : ((TEXT && j >= nkv) ? ~0ull : cube_slots(j, pad));
       if (n + 1 < cnt) {
         j = cube_at(n + 1);
         sw_load(kr, kbase + (size_t)max(j, 0) * 64 * D, tid);
@@ -188,12 +220,20 @@ __global__ __launch_bounds__(128, 2) void k_attn_fwd(const T* __restrict__ q, co
     }
   }
 
-  uint64_t qm = ~0ull;  // PAD: real slots of query cube i
-  if constexpr (PAD) qm = cube_slots(i, pad);
+  uint64_t qm = ~0ull;  // PAD / TEXT: real rows of query cube i
+  if constexpr (TEXT) {
+    if (textq) {
+      const int nr = ntext - 64 * (i - nq);
+      qm = nr >= 64 ? ~0ull : (1ull << nr) - 1;
+    }
+  }
+  if constexpr (PAD) {
+    if (!textq) qm = cube_slots(i, pad);
+  }
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     const int qrow = i * 64 + 32 * w + 16 * qb + cc;
-    const bool real = !PAD || ((qm >> (32 * w + 16 * qb + cc)) & 1);
+    const bool real = !(PAD || TEXT) || ((qm >> (32 * w + 16 * qb + cc)) & 1);
     const float lsum = group_sum(l[qb]);  // every lane takes part in the cross-lane sum
     const float lt = real ? lsum : 0.f;
     const float inv = lt > 0.f ? 1.0f / lt : 0.f;
@@ -216,20 +256,25 @@ template <typename T, int D>
 hipError_t launch_fwd_t(const AttnArgs& a, hipStream_t st) {
   dim3 grid(xcd_grid(a.nq, a.bh));
   if (a.dense) {
-    hipLaunchKernelGGL((k_attn_fwd<T, float, D, true, false, 0>), grid, dim3(128), 0, st, (const T*)a.q,
+    hipLaunchKernelGGL((k_attn_fwd<T, float, D, true, false, 0, false>), grid, dim3(128), 0, st, (const T*)a.q,
                        (const T*)a.k, (const T*)a.v, nullptr, nullptr, (float*)a.o, a.lse, a.nq, a.nkv, a.seq, a.ld,
-                       a.out_rows, a.kph, a.scale_log2, 0, 0, 0, a.pad);
+                       a.out_rows, a.kph, a.scale_log2, 0, 0, 0, a.pad, 0, 0, a.bh);
   } else {
     timer_before(TK_FINE_FWD, st);
-#define VSA2_FWD(PAD, BS)                                                                                        \
-  hipLaunchKernelGGL((k_attn_fwd<T, T, D, false, PAD, BS>), grid, dim3(128), 0, st, (const T*)a.q, (const T*)a.k, \
-                     (const T*)a.v, a.row_ptr, a.col_idx, (T*)a.o, a.lse, a.nq, a.nkv, a.seq, a.ld, a.out_rows,     \
-                     a.kph, a.scale_log2, a.ct, a.cy, a.cx, a.pad)
+    const dim3 tgrid(grid.x + ((a.ntc * a.bh + 7) & ~7));  // text query cubes first
+#define VSA2_FWD(PAD, BS, TEXT)                                                                                 \
+  hipLaunchKernelGGL((k_attn_fwd<T, T, D, false, PAD, BS, TEXT>), TEXT ? tgrid : grid, dim3(128), 0, st,          \
+                     (const T*)a.q, (const T*)a.k, (const T*)a.v, a.row_ptr, a.col_idx, (T*)a.o, a.lse, a.nq, a.nkv, \
+                     a.seq, a.ld, a.out_rows, a.kph, a.scale_log2, a.ct, a.cy, a.cx, a.pad, a.ntc, a.ntext, a.bh)
+#define VSA2_FWD_T(PAD, BS)                   \
+  if (a.ntc) VSA2_FWD(PAD, BS, true);         \
+  else VSA2_FWD(PAD, BS, false)
     if (a.bs) {
-      if (a.pad.on) VSA2_FWD(true, 1); else VSA2_FWD(false, 1);
+      if (a.pad.on) { VSA2_FWD_T(true, 1); } else { VSA2_FWD_T(false, 1); }
     } else {
-      if (a.pad.on) VSA2_FWD(true, 0); else VSA2_FWD(false, 0);
+      if (a.pad.on) { VSA2_FWD_T(true, 0); } else { VSA2_FWD_T(false, 0); }
     }
+#undef VSA2_FWD_T
 #undef VSA2_FWD
     timer_after(TK_FINE_FWD, st);
   }

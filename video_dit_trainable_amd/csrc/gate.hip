@@ -9,6 +9,7 @@
 // (x = hi + lo to ~16 mantissa bits) so the products keep near-fp32 accuracy.
 // dW_g = X^T dpre is reduced over token chunks into per-chunk partials that a
 // second kernel adds in a fixed order (no float atomics).
+#include <algorithm>
 #include <cmath>
 
 #include "common.h"
@@ -61,7 +62,7 @@ template <typename T, int D, int NHB>
 __global__ __launch_bounds__(256) void k_gate_fwd(const T* __restrict__ x, const T* __restrict__ wt,
                                                   const float* __restrict__ oc_hat, const T* __restrict__ o_f,
                                                   T* __restrict__ o, float* __restrict__ gout, int H, int nb, int dm,
-                                                  int hp, PadGrid pad, int bs) {
+                                                  int hp, PadGrid pad, int bs, int ld) {
   constexpr bool SPLIT = sizeof(T) == 2;
   __shared__ float gs[64][HMAX + 1];
   const int c = blockIdx.x, b = blockIdx.y, tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4,
@@ -133,7 +134,7 @@ __global__ __launch_bounds__(256) void k_gate_fwd(const T* __restrict__ x, const
       const int u = tid + 256 * i;
       const int t = u / UPR, dg = u % UPR;
       const float gv = gs[t][h];
-      const size_t off = (bh * L + (size_t)c * CUBE + t) * D + 8 * dg;
+      const size_t off = (bh * ld + (size_t)c * CUBE + t) * D + 8 * dg;
       const Vec8<T> f = load8(o_f + off);
       const float4 a0 = *reinterpret_cast<const float4*>(oc + 8 * dg);
       const float4 a1 = *reinterpret_cast<const float4*>(oc + 8 * dg + 4);
@@ -156,7 +157,7 @@ __global__ __launch_bounds__(256) void k_gate_bwd(const T* __restrict__ wt, cons
                                                   const float* __restrict__ lse_c, float* __restrict__ stats_c,
                                                   T* __restrict__ dx, int H, int nb,
                                                   int nbp, int dm, int hp, int hk, PadGrid pad, int bs,
-                                                  float* __restrict__ doc_part) {
+                                                  float* __restrict__ doc_part, int ld) {
   constexpr bool SPLIT = sizeof(T) == 2;
   constexpr int UPR = D / 8;
   constexpr int RROWS = 256 / UPR;
@@ -185,7 +186,7 @@ __global__ __launch_bounds__(256) void k_gate_bwd(const T* __restrict__ wt, cons
 #pragma unroll
     for (int i = 0; i < TPT; ++i) {
       const size_t tok = (size_t)c * CUBE + tid / UPR + RROWS * i;
-      xn[i] = load8(d_o + (bh * L + tok) * D + 8 * dg);
+      xn[i] = load8(d_o + (bh * ld + tok) * D + 8 * dg);
       gn[i] = gin[bh * L + tok];
     }
   };
@@ -556,6 +557,19 @@ static hipError_t gate_prep(const float* w_g, void* wt, int dm, int H, hipStream
   return hipGetLastError();
 }
 
+// MMDiT text rows (after the video slots of each head) have no coarse term:
+// O = O_f there.  One thread per 8 elements.
+template <typename T>
+__global__ __launch_bounds__(256) void k_copy_rows(const T* __restrict__ src, T* __restrict__ dst, size_t row0,
+                                                   size_t ld, size_t nrows, size_t rowlen, size_t nbh) {
+  const size_t per = nrows * rowlen / 8;
+  for (size_t u = (size_t)blockIdx.x * 256 + threadIdx.x; u < per * nbh; u += (size_t)gridDim.x * 256) {
+    const size_t bh = u / per, e = (u % per) * 8;
+    const size_t off = (bh * ld + row0) * rowlen + e;
+    store8(dst + off, load8(src + off));
+  }
+}
+
 template <typename T, int D>
 hipError_t launch_gate_fwd_t(const GateArgs& a, hipStream_t st) {
   hipError_t e = gate_prep<T>(a.w_g, a.wt, a.dm, a.heads, st);
@@ -564,7 +578,7 @@ hipError_t launch_gate_fwd_t(const GateArgs& a, hipStream_t st) {
   const dim3 grid(a.nb, a.batch);
 #define VSA2_GATE_FWD(NHB)                                                                                     \
   hipLaunchKernelGGL((k_gate_fwd<T, D, NHB>), grid, dim3(256), 0, st, (const T*)a.x, (const T*)a.wt, a.oc_hat, \
-                     (const T*)a.o_f, (T*)a.o, a.g, a.heads, a.nb, a.dm, hp, a.pad, a.bs)
+                     (const T*)a.o_f, (T*)a.o, a.g, a.heads, a.nb, a.dm, hp, a.pad, a.bs, a.ld)
   switch (hp / 16) {
     case 1: VSA2_GATE_FWD(1); break;
     case 2: VSA2_GATE_FWD(2); break;
@@ -572,6 +586,15 @@ hipError_t launch_gate_fwd_t(const GateArgs& a, hipStream_t st) {
     default: VSA2_GATE_FWD(4); break;
   }
 #undef VSA2_GATE_FWD
+  const size_t L = (size_t)a.nb * CUBE;
+  if ((size_t)a.ld > L) {
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const size_t bhn = (size_t)a.batch * a.heads, n8 = ((size_t)a.ld - L) * D / 8 * bhn;
+    const int blocks = (int)std::min<size_t>((n8 + 255) / 256, 4096);
+    hipLaunchKernelGGL((k_copy_rows<T>), dim3(blocks), dim3(256), 0, st, (const T*)a.o_f, (T*)a.o, L, (size_t)a.ld,
+                       (size_t)a.ld - L, (size_t)D, bhn);
+  }
   return hipGetLastError();
 }
 
@@ -588,11 +611,11 @@ hipError_t launch_gate_bwd_t(const GateBwdArgs& a, hipStream_t st) {
   if (hk <= 32)
     hipLaunchKernelGGL((k_gate_bwd<T, D, 1>), dim3(a.nb, a.batch), dim3(256), 0, st, (const T*)a.wt, a.oc_hat, a.g,
                        (const T*)a.d_o, a.dpre, (T*)a.doc, a.lse_c, a.stats_c, (T*)a.dx, a.heads, a.nb, a.nbp, a.dm,
-                       hp, hk, a.pad, a.bs, a.doc_part);
+                       hp, hk, a.pad, a.bs, a.doc_part, a.ld);
   else
     hipLaunchKernelGGL((k_gate_bwd<T, D, 2>), dim3(a.nb, a.batch), dim3(256), 0, st, (const T*)a.wt, a.oc_hat, a.g,
                        (const T*)a.d_o, a.dpre, (T*)a.doc, a.lse_c, a.stats_c, (T*)a.dx, a.heads, a.nb, a.nbp, a.dm,
-                       hp, hk, a.pad, a.bs, a.doc_part);
+                       hp, hk, a.pad, a.bs, a.doc_part, a.ld);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (a.bs) {

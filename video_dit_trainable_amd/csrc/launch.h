@@ -26,6 +26,7 @@ struct PoolArgs {
   bool bf16;
   PadGrid pad;
   int bs;                 // 2^bs cubes per attention block (coarse token)
+  int ld;                 // token rows per head in q/k/v (video slots, then text rows)
 };
 hipError_t launch_pool(const PoolArgs& a, hipStream_t st);
 
@@ -80,6 +81,7 @@ struct AttnArgs {
   int ct, cy, cx;                     // cube grid for the blocked visiting order (0 = linear)
   PadGrid pad;                        // fine branch on a padded grid: pad keys masked, pad rows zero
   int bs;                             // fine: 2^bs cubes per block; the CSR lists blocks (nq, nkv count cubes)
+  int ntc, ntext;                     // fine: text cubes after the nq video cubes, and their tokens (0 = none)
 };
 hipError_t launch_attn_fwd(const AttnArgs& a, hipStream_t st);
 
@@ -100,6 +102,7 @@ struct AttnBwdArgs {
   int ct, cy, cx;                     // cube grid for the blocked visiting order (0 = linear)
   PadGrid pad;                        // fine branch on a padded grid (per-block terms added as row/n, n real tokens)
   int bs;                             // fine: 2^bs cubes per block; CSR / CSC and the per-block terms are per block
+  int ntc, ntext;                     // fine: text cubes after the nq video cubes, and their tokens (0 = none)
 };
 hipError_t launch_attn_bwd(const AttnBwdArgs& a, hipStream_t st);
 
@@ -115,6 +118,7 @@ struct GateArgs {
   bool bf16;
   PadGrid pad;            // pad rows: g = 0, O = 0
   int bs;                 // 2^bs cubes per coarse token: O_hat_c row of cube c is c >> bs
+  int ld;                 // token rows per head in o_f / o (video slots, then text rows, copied O = O_f)
 };
 hipError_t launch_gate_fwd(const GateArgs& a, hipStream_t st);
 
@@ -141,6 +145,7 @@ struct GateBwdArgs {
   PadGrid pad;            // pad rows: dpre = 0 (so dX = 0 and X there adds nothing to dW_g)
   int bs;                 // 2^bs cubes per coarse token
   float* doc_part;        // workspace [bh, nb, d] fp32 when bs > 0: per-cube sums of dO_hat_c, added in pairs
+  int ld;                 // token rows per head in d_o (video slots, then text rows)
 };
 hipError_t launch_gate_bwd(const GateBwdArgs& a, hipStream_t st);
 

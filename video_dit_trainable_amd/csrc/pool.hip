@@ -18,16 +18,15 @@ template <typename T, int D>
 __global__ __launch_bounds__(256) void k_pool(const T* __restrict__ q, const T* __restrict__ k,
                                               const T* __restrict__ v, T* __restrict__ qr, T* __restrict__ kr,
                                               T* __restrict__ qc, T* __restrict__ kc, T* __restrict__ vc, int nb,
-                                              int nbp, PadGrid pad, int bs) {
+                                              int nbp, PadGrid pad, int bs, int ld) {
   __shared__ float sub[3][8][D];
   const int blk = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
   const int nblk = nb >> bs;
-  const size_t L = (size_t)nb * CUBE;
   constexpr int CG = D / 8;
   int count = 0;  // real tokens of the block
   for (int cb = 0; cb < (1 << bs); ++cb) {
     const int c = (blk << bs) + cb;
-    const size_t tok0 = (size_t)bh * L + (size_t)c * CUBE;
+    const size_t tok0 = (size_t)bh * ld + (size_t)c * CUBE;  // ld rows per head (video, then any text rows)
     const uint64_t real = pad.on ? cube_slots(c, pad) : ~0ull;
     count += __popcll(real);
     for (int u = tid; u < 3 * 8 * CG; u += 256) {
@@ -83,7 +82,7 @@ template <typename T, int D>
 hipError_t launch_pool_t(const PoolArgs& a, hipStream_t st) {
   dim3 grid(a.nb >> a.bs, a.bh);
   hipLaunchKernelGGL((k_pool<T, D>), grid, dim3(256), 0, st, (const T*)a.q, (const T*)a.k, (const T*)a.v,
-                     (T*)a.qr, (T*)a.kr, (T*)a.qc, (T*)a.kc, (T*)a.vc, a.nb, a.nbp, a.pad, a.bs);
+                     (T*)a.qr, (T*)a.kr, (T*)a.qc, (T*)a.kc, (T*)a.vc, a.nb, a.nbp, a.pad, a.bs, a.ld);
   return hipGetLastError();
 }
 

@@ -14,7 +14,9 @@ and permuted with :func:`tile_permutation`.  A grid that is not a whole number
 of cubes is padded up to one (§2.2 "Kernel Implementation"); the pad slots of
 Q, K and V are filled with seeded finite values of a different distribution
 (3 + 4 N(0,1)), and those of dO and X are drawn like their real rows, so that
-any pad value reaching an output shows.
+any pad value reaching an output shows.  MMDiT text tokens (workloads with
+``text``) follow the video slots as N(0,1) rows, padded to a multiple of 64
+with the same pad fill.
 
 Recipes (one torch generator per (workload, batch, tensor, head)):
 
@@ -37,7 +39,7 @@ import torch
 from .configs import CUBE, Workload
 
 # tensor ids used in the seeds
-T_Q, T_K, T_V, T_DO, T_X, T_WG, T_SQK, T_SV, T_SKEW, T_SEL, T_PAD = range(11)
+T_Q, T_K, T_V, T_DO, T_X, T_WG, T_SQK, T_SV, T_SKEW, T_SEL, T_PAD, T_TEXT = range(12)
 
 
 def seed_of(w: Workload, tensor: int, head: int = 0, batch: int = 0) -> int:
@@ -119,7 +121,8 @@ def _storage(t: torch.Tensor, w: Workload) -> torch.Tensor:
 
 
 def make_qkv(w: Workload, device="cpu", heads=None):
-    """Q, K, V as [B, H, L, d] in storage dtype, cube-tiled token order.
+    """Q, K, V as [B, H, rows, d] in storage dtype: the video slots in cube-tiled
+    token order, then any MMDiT text rows.
 
     ``heads`` selects a subset of heads (regenerated exactly as in the full
     tensor); the result then has that many heads.
@@ -128,7 +131,7 @@ def make_qkv(w: Workload, device="cpu", heads=None):
     L, d = w.L, w.head_dim
     perm = tile_permutation(w.grid, device, w.block)
     dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
-    out = {n: torch.empty((w.batch, len(heads), L, d), dtype=dt, device=device) for n in "qkv"}
+    out = {n: torch.empty((w.batch, len(heads), w.rows, d), dtype=dt, device=device) for n in "qkv"}
     for b in range(w.batch):
         for hi, h in enumerate(heads):
             s_qk = _structure(w, T_SQK, h, b, device)
@@ -149,18 +152,25 @@ def make_qkv(w: Workload, device="cpu", heads=None):
                     xi = torch.randn((w.nb,), generator=gs, device=device)
                     sc = torch.exp(xi).clamp(1.0 / 8.0, 8.0)
                     x = (x.view(w.nb, CUBE, d) * sc.view(w.nb, 1, 1)).view(L, d)
-                out[name][b, hi] = _storage(x, w)
+                out[name][b, hi, :L] = _storage(x, w)
+                if w.text:
+                    # MMDiT text rows: N(0,1) tokens, then padding filled like
+                    # the video pad slots
+                    gt = _gen(seed_of(w, T_TEXT, 3 * h + ti, b), device)
+                    t = torch.randn((w.text, d), generator=gt, device=device)
+                    fill = 3.0 + 4.0 * torch.randn((w.rows - L - w.text, d), generator=gt, device=device)
+                    out[name][b, hi, L:] = _storage(torch.cat([t, fill]), w)
     return out["q"], out["k"], out["v"]
 
 
 def make_grad_out(w: Workload, device="cpu", heads=None):
     heads = list(range(w.heads)) if heads is None else list(heads)
     dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
-    out = torch.empty((w.batch, len(heads), w.L, w.head_dim), dtype=dt, device=device)
+    out = torch.empty((w.batch, len(heads), w.rows, w.head_dim), dtype=dt, device=device)
     for b in range(w.batch):
         for hi, h in enumerate(heads):
             g = _gen(seed_of(w, T_DO, h, b), device)
-            out[b, hi] = _storage(torch.randn((w.L, w.head_dim), generator=g, device=device), w)
+            out[b, hi] = _storage(torch.randn((w.rows, w.head_dim), generator=g, device=device), w)
     return out
 
 

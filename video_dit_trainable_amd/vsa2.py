@@ -31,6 +31,7 @@ class Problem(ctypes.Structure):
         ("dtype", ctypes.c_int32),
         ("softmax_scale", ctypes.c_float),
         ("block_tokens", ctypes.c_int32),
+        ("text_tokens", ctypes.c_int32),
     ]
 
 
@@ -86,10 +87,10 @@ def _check(fn, code):
         raise Vsa2Error(fn, code)
 
 
-def problem(batch, heads, head_dim, grid, dtype, softmax_scale=0.0, block=64):
+def problem(batch, heads, head_dim, grid, dtype, softmax_scale=0.0, block=64, text=0):
     t, y, x = grid
     dt = {"bf16": VSA2_BF16, "f32": VSA2_F32, torch.bfloat16: VSA2_BF16, torch.float32: VSA2_F32}[dtype]
-    return Problem(batch, heads, head_dim, t, y, x, dt, softmax_scale, block)
+    return Problem(batch, heads, head_dim, t, y, x, dt, softmax_scale, block, text)
 
 
 def _ptr(t):
@@ -213,6 +214,8 @@ class Layer:
         L = 64 * -(-p.lat_t // 4) * -(-p.lat_y // 4) * (-(-p.lat_x // (4 * per)) * per)
         nb = L // block
         self.L, self.nb, self.bh, self.block = L, nb, bh, block
+        # MMDiT text rows follow the video slots of every per-token attention tensor
+        self.rows = L + 64 * -(-p.text_tokens // 64)
         self.k = budget(p, topk)
         self.sdt = torch.bfloat16 if p.dtype == VSA2_BF16 else torch.float32
         i32 = dict(dtype=torch.int32, device=device)
@@ -222,10 +225,10 @@ class Layer:
         self.col_idx = torch.empty((p.batch, p.heads, self.k), **i32)
         self.col_ptr = torch.empty((p.batch, p.heads, nb + 1), **i32)
         self.row_idx = torch.empty((p.batch, p.heads, self.k), **i32)
-        shp = (p.batch, p.heads, L, p.head_dim)
+        shp = (p.batch, p.heads, self.rows, p.head_dim)
         self.o_f = torch.empty(shp, dtype=self.sdt, device=device)
         self.o = torch.empty(shp, dtype=self.sdt, device=device)
-        self.lse = torch.empty((p.batch, p.heads, L), dtype=torch.float32, device=device)
+        self.lse = torch.empty((p.batch, p.heads, self.rows), dtype=torch.float32, device=device)
         self.saved = _ws(saved_size(p), device)
         ws_need = max(workspace_size(p, op, topk, d_model)
                       for op in (OP_ROUTE, OP_TOPK, OP_PLAN, OP_FWD, OP_BWD, OP_COARSE, OP_COARSE_BWD))
@@ -252,7 +255,7 @@ class Layer:
         """Gradient buffers (allocated on first use): dq, dk, dv, dx, dw_g, dqkv_c."""
         p = self.p
         if self._grads is None:
-            shp = (p.batch, p.heads, self.L, p.head_dim)
+            shp = (p.batch, p.heads, self.rows, p.head_dim)
             self._grads = dict(
                 dq=torch.empty(shp, dtype=self.sdt, device=self.device),
                 dk=torch.empty(shp, dtype=self.sdt, device=self.device),
