@@ -37,6 +37,7 @@ TRAIN = WORKLOADS["train720"]
 INFER = WORKLOADS["infer720"]
 TRAIN_PAD = WORKLOADS["train720pad"]    # 43 x 47 x 103, padded to the same 44 x 48 x 104 slots
 TRAIN_B128 = WORKLOADS["train720b128"]  # 128-token blocks (4x4x8), 1716 blocks
+TRAIN_TEXT = WORKLOADS["train720text"]  # plus 512 MMDiT text tokens in the fine branch
 
 
 def _dev():
@@ -53,7 +54,7 @@ def _run(w, topk, train):
     dev = _dev()
     q, k, v = make_qkv(w, device=dev)
     x, w_g = make_gate_inputs(w, device=dev, zero_gate=False)
-    p = vsa2.problem(w.batch, w.heads, w.head_dim, w.grid, w.dtype, block=w.block)
+    p = vsa2.problem(w.batch, w.heads, w.head_dim, w.grid, w.dtype, block=w.block, text=w.text)
     layer = vsa2.Layer(p, topk, w.d_model, device=dev)
     vsa2.vsa2_pool(p, q, k, v, layer.pooled)
     vsa2.vsa2_route(p, layer.pooled, layer.scores, layer.ws)
@@ -402,3 +403,24 @@ def test_block128_outputs_sampled(train720b128):
     for name, got, want in (("dK", g["dk"], dk), ("dV", g["dv"], dv)):
         rr = gu.rel_l2(gu.f64(got[0, h])[tj], want[tj])
         assert rr <= 2e-2, f"{name} head {h} KV block {j} ({len(rows)} query blocks): rel-L2 {rr:.3g}"
+
+
+# ----------------------------------------------------------------------------- MMDiT text tokens
+def test_text_rows_at_full_size():
+    """720p training with 512 text tokens: the fine outputs of sampled video
+    cubes (their keys include every text token) and of all text rows (every
+    video and text token) against the oracle; O = O_f on text rows; text
+    padding is zero."""
+    r = _run(TRAIN_TEXT, TRAIN_TEXT.topk, False)
+    w, layer = r["w"], r["layer"]
+    h = 3
+    rp, ci = _seeded(r, h)
+    mask = orc.csr_to_mask(rp, ci, w.nb)
+    cubes = _sample_cubes(rp, n_extra=1)                  # includes an empty list: text keys only
+    q, k, v = (gu.f64(t[0, h]) for t in (r["q"], r["k"], r["v"]))
+    o_f, lse = orc.fine_forward(q, k, v, mask, rows=cubes, n_text=w.text)
+    toks = np.concatenate([orc._tokens_of(cubes), w.L + np.arange(w.text)])
+    gu.assert_close_bf16(gu.f64(layer.o_f[0, h])[toks], o_f[toks], f"O_f head {h} (video cubes {cubes} + text)")
+    np.testing.assert_allclose(gu.f64(layer.lse[0, h])[toks], lse[toks], atol=1e-3)
+    assert torch.equal(layer.o[:, :, w.L:], layer.o_f[:, :, w.L:]), "text rows: O must be O_f"
+    assert torch.all(layer.o_f[:, :, w.L + w.text:] == 0) and torch.all(torch.isneginf(layer.lse[:, :, w.L + w.text:]))

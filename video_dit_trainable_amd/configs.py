@@ -98,8 +98,19 @@ WORKLOADS = {
         # x-adjacent cubes; G = 16): the blog's inferred setting, top64
         Workload("train720b128", 7, (44, 48, 104), 1, 20, 128, "bf16", 64, "lowrank", skew=True, train=True,
                  block=128),
+        # the 720p training problem with 512 MMDiT text tokens in the fine branch
+        Workload("train720text", 8, (44, 48, 104), 1, 20, 128, "bf16", 64, "lowrank", skew=True, train=True,
+                 text=512),
     ]
 }
+
+
+def text_pairs(w: Workload):
+    """64 x 64 tile pairs the MMDiT text rows add per (batch, head): every video
+    query cube against every text cube, every text query cube against every
+    video and text cube."""
+    ntc = -(-w.text // 64)
+    return 2 * w.nb * ntc + ntc * ntc
 
 
 def flops(w: Workload, topk=None):
@@ -109,15 +120,18 @@ def flops(w: Workload, topk=None):
     2.5x that backward (five BxBxd GEMMs).  Router: two pooled GEMMs (LSE pass
     and score pass), each 2 * (L/8)^2 * d, as in the paper's App. B cost model.
     Coarse: dense attention over the nb block tokens, 4 * nb^2 * d forward.
+    MMDiT text rows add their 64 x 64 tile pairs (text_pairs) to the fine
+    branch.
     """
     k = w.budget(topk)
     bh = w.batch * w.heads
     d = w.head_dim
     lr = w.L // SUB
     pair = 4 * w.block * w.block * d
+    tpair = text_pairs(w) * 4 * CUBE * CUBE * d
     return {
-        "fine_fwd": bh * k * pair,
-        "fine_bwd": bh * k * pair * 5 // 2,
+        "fine_fwd": bh * (k * pair + tpair),
+        "fine_bwd": bh * (k * pair + tpair) * 5 // 2,
         "router": bh * 2 * 2 * lr * lr * d,
         "coarse_fwd": bh * 4 * w.nblk * w.nblk * d,
         "coarse_bwd": bh * 10 * w.nblk * w.nblk * d,
@@ -140,10 +154,11 @@ def kernel_flops(w: Workload, topk=None):
     d = w.head_dim
     lr = w.L // SUB
     gemm = 2 * w.block * w.block * d
+    tg = text_pairs(w) * 2 * CUBE * CUBE * d      # text tile pairs, one GEMM each
     return {
-        "fine_fwd": bh * k * 2 * gemm,
-        "bwd_dkdv": bh * k * 4 * gemm,
-        "bwd_dq": bh * k * gemm,
+        "fine_fwd": bh * (k * 2 * gemm + 2 * tg),
+        "bwd_dkdv": bh * (k * 4 * gemm + 4 * tg),
+        "bwd_dq": bh * (k * gemm + tg),
         "router_lse": bh * 2 * lr * lr * d,
         "router_scores": bh * 2 * lr * lr * d,
     }
@@ -165,13 +180,16 @@ def kernel_bytes(w: Workload, topk=None):
     d = w.head_dim
     esz = 2 if w.dtype == "bf16" else 4
     tile = w.block * d * esz
-    tok = w.L * d * esz          # one per-token tensor of one (batch, head)
+    tok = w.rows * d * esz       # one per-token tensor of one (batch, head), text rows included
     ptr = (w.nblk + 1) * 4
     lr = w.L // SUB
+    tp = text_pairs(w)           # text tile pairs: one 64-row tile of each of two operands
+    t64 = CUBE * d * esz
     return {
-        "fine_fwd": bh * (k * (2 * tile + 4) + 2 * tok + w.L * 4 + ptr),
-        "bwd_dkdv": bh * (k * (2 * tile + w.block * 8 + 4) + 4 * tok + 2 * w.nblk * d * 4 + ptr),
-        "bwd_dq": bh * (k * (2 * tile + 4) + 3 * tok + w.L * 8 + w.nblk * d * 4 + ptr),
+        "fine_fwd": bh * (k * (2 * tile + 4) + tp * 2 * t64 + 2 * tok + w.rows * 4 + ptr),
+        "bwd_dkdv": bh * (k * (2 * tile + w.block * 8 + 4) + tp * (2 * t64 + CUBE * 8) + 4 * tok
+                          + 2 * w.nblk * d * 4 + ptr),
+        "bwd_dq": bh * (k * (2 * tile + 4) + tp * 2 * t64 + 3 * tok + w.rows * 8 + w.nblk * d * 4 + ptr),
         "router_lse": bh * (2 * lr * d * esz + lr * 4),
         "router_scores": bh * (2 * lr * d * esz + lr * 4 + w.nblk * w.nblk * 4),
     }
