@@ -245,6 +245,32 @@ def topk_per_sequence(scores, topk):
     return (mask,) + mask_to_csr_csc(mask)
 
 
+def topk_per_row(scores, topk):
+    """The VSA router's selection ([VSA2] §1, Figure 1 left; [blog] §04): every
+    query block keeps its own min(topk, nb) largest scores.  Ties go to the
+    lower column index.  Returns (mask, row_ptr, col_idx, col_ptr, row_idx)
+    as topk_per_sequence does."""
+    scores = np.asarray(scores, np.float64)
+    nb = scores.shape[0]
+    kr = min(topk, nb)
+    mask = np.zeros((nb, nb), dtype=bool)
+    for i in range(nb):
+        order = np.lexsort((np.arange(nb), -scores[i]))     # score desc, then column asc
+        mask[i, order[:kr]] = True
+    return (mask,) + mask_to_csr_csc(mask)
+
+
+def coarse_scores(q, k, grid, scale=None, bf16_pooled=False, block=64):
+    """The VSA router's block scores: P_c = softmax(Q_c K_c^T / sqrt(d)) over
+    the block means (Eq.(1)-(2)), the coarse branch's own attention map.
+    With ``bf16_pooled`` the block means are rounded to bf16 first."""
+    d = q.shape[1]
+    qc, kc = block_mean(q, grid, block), block_mean(k, grid, block)
+    if bf16_pooled:
+        qc, kc = round_bf16(qc), round_bf16(kc)
+    return _softmax_rows(qc @ kc.T * _scale(d, scale))
+
+
 def mask_to_csr_csc(mask):
     nb = mask.shape[0]
     rows, cols = np.nonzero(mask)                        # row-major: cols ascending per row

@@ -714,3 +714,41 @@ def test_text_layer_autograd_on_a_padded_grid():
         assert np.all(g_[:, Lv + nt:] == 0)
     np.testing.assert_allclose(got[3][real][order], tx.grad.numpy(), rtol=1e-10, atol=1e-12)
     np.testing.assert_allclose(got[4], tw.grad.numpy(), rtol=1e-10, atol=1e-12)
+
+
+# ----------------------------------------------------------------------------- VSA router baseline
+@pytest.mark.parametrize("nb,topk,levels", [(6, 2, 3), (9, 4, 2), (5, 7, 4)])
+def test_topk_per_row_brute_force_with_ties(nb, topk, levels):
+    s = rng.integers(0, levels, size=(nb, nb)).astype(np.float64)
+    mask, row_ptr, col_idx, col_ptr, row_idx = orc.topk_per_row(s, topk)
+    kr = min(topk, nb)
+    for i in range(nb):
+        want = sorted(sorted(range(nb), key=lambda j: (-s[i, j], j))[:kr])
+        assert list(np.nonzero(mask[i])[0]) == want
+        assert list(col_idx[row_ptr[i]:row_ptr[i + 1]]) == want
+    assert np.all(np.diff(row_ptr) == kr)
+    for j in range(nb):
+        assert list(row_idx[col_ptr[j]:col_ptr[j + 1]]) == [i for i in range(nb) if mask[i, j]]
+
+
+def test_coarse_scores_are_the_coarse_attention_map():
+    grid = (4, 8, 8)
+    q, k = _rand(256, 16), _rand(256, 16)
+    # B = 64: pooling the router over whole cubes (r = 64) gives the same map
+    np.testing.assert_allclose(orc.coarse_scores(q, k, grid), orc.router_scores(q, k, grid, pool=(4, 4, 4)),
+                               rtol=1e-12)
+    qc = torch.tensor(q).view(-1, 64, 16).mean(1)
+    kc = torch.tensor(k).view(-1, 64, 16).mean(1)
+    np.testing.assert_allclose(orc.coarse_scores(q, k, grid), torch.softmax(qc @ kc.T * 0.25, -1).numpy(),
+                               rtol=1e-12)
+    # B = 128 on the raster-order brute force of the 4x4x8 block means
+    q2, k2 = _rand(512, 16), _rand(512, 16)
+    g2 = (4, 8, 16)
+    perm = tile_permutation(g2, block=128).numpy()
+    blk = _raster_block_ids(g2)
+    qr_ = np.zeros((512, 16)); kr_ = np.zeros((512, 16))
+    qr_[perm], kr_[perm] = q2, k2                           # raster rows of the tiled inputs
+    qb = np.stack([qr_[blk == b].mean(0) for b in range(4)])
+    kb = np.stack([kr_[blk == b].mean(0) for b in range(4)])
+    want = torch.softmax(torch.tensor(qb @ kb.T * 0.25), -1).numpy()
+    np.testing.assert_allclose(orc.coarse_scores(q2, k2, g2, block=128), want, rtol=1e-12)
