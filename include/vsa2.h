@@ -80,7 +80,9 @@ enum vsa2_op {
   VSA2_OP_FWD = 4,
   VSA2_OP_BWD = 5,
   VSA2_OP_COARSE = 6,
-  VSA2_OP_COARSE_BWD = 7
+  VSA2_OP_COARSE_BWD = 7,
+  VSA2_OP_ROUTE_COARSE = 8,
+  VSA2_OP_TOPK_ROW = 9
 };
 
 typedef struct vsa2_problem {
@@ -154,6 +156,25 @@ int vsa2_topk_per_seq(const vsa2_problem* p, const float* scores, int32_t topk,
  *   ws: vsa2_workspace_size(VSA2_OP_PLAN). */
 int vsa2_plan_from_csr(const vsa2_problem* p, int32_t topk, const int32_t* row_ptr, const int32_t* col_idx,
                        int32_t* col_ptr, int32_t* row_idx, void* ws, size_t ws_bytes, void* stream);
+
+/* The VSA router the paper compares against (§1 and Figure 1 left; Eq.(1)-(2)):
+ * block scores from the coarse branch's own attention map,
+ * P_c = softmax(Q_c K_c^T * scale) over the nb block means, no G x G pooling.
+ *   pooled: from vsa2_pool (its Q_c, K_c).
+ *   scores (written): fp32 [batch, heads, nb, nb] = P_c; every row sums to 1.
+ *   ws: vsa2_workspace_size(VSA2_OP_ROUTE_COARSE). */
+int vsa2_route_coarse(const vsa2_problem* p, const void* pooled, float* scores,
+                      void* ws, size_t ws_bytes, void* stream);
+
+/* The VSA router's TopK: every query block keeps its own min(topk, nb)
+ * largest scores (ties to the lower column), instead of the per-sequence
+ * budget of Eq.(8)-(9).  Same outputs, sizes and budget (vsa2_budget) as
+ * vsa2_topk_per_seq; row_ptr[i] = i min(topk, nb).
+ *   scores: fp32 [batch, heads, nb, nb], finite and >= 0.
+ *   ws: vsa2_workspace_size(VSA2_OP_TOPK_ROW). */
+int vsa2_topk_per_row(const vsa2_problem* p, const float* scores, int32_t topk, int32_t* row_ptr,
+                      int32_t* col_idx, int32_t* col_ptr, int32_t* row_idx, void* ws, size_t ws_bytes,
+                      void* stream);
 
 /* Fine branch forward, Eq.(12): block-sparse attention of every query cube
  * over its selected KV cubes only (-inf mask elsewhere, §2.1).

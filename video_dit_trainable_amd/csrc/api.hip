@@ -319,6 +319,8 @@ int vsa2_workspace_size(const vsa2_problem* p, int32_t op, int32_t topk, int32_t
       if ((s = check_dm(d, d_model))) return s;
       *bytes = ws_coarse_bwd(d, d_model, nullptr, nullptr);
       break;
+    case VSA2_OP_ROUTE_COARSE: *bytes = up((size_t)d.bh * d.nb * 4); break;
+    case VSA2_OP_TOPK_ROW: *bytes = ws_plan(d, nullptr, nullptr); break;
     default: return VSA2_E_ARG;
   }
   (void)topk;
@@ -346,6 +348,42 @@ int vsa2_route(const vsa2_problem* p, const void* pooled, float* scores, void* w
   RouteArgs a{pp.qr, pp.kr, (float*)ws, scores, d.bh, d.nc, d.d, d.bf16, d.scale * 1.4426950408889634f, d.pad,
               d.pad.on ? (uint64_t*)((char*)ws + ws_route_lse(d)) : nullptr, d.bs};
   return hip_status(launch_route(a, (hipStream_t)stream));
+}
+
+int vsa2_route_coarse(const vsa2_problem* p, const void* pooled, float* scores, void* ws, size_t ws_bytes,
+                      void* stream) {
+  Dims d;
+  int s = check_problem(p, d);
+  if (s) return s;
+  if (!aligned(pooled) || !aligned(scores)) return VSA2_E_ARG;
+  if ((s = check_ws(ws, ws_bytes, up((size_t)d.bh * d.nb * 4)))) return s;
+  Pooled pp = pooled_ptrs(d, pooled);
+  RouteArgs a{pp.qc, pp.kc, (float*)ws, scores, d.bh, d.nb, d.d, d.bf16, d.scale * 1.4426950408889634f, PadGrid{},
+              nullptr, 0, 1, d.nbp};
+  return hip_status(launch_route(a, (hipStream_t)stream));
+}
+
+int vsa2_topk_per_row(const vsa2_problem* p, const float* scores, int32_t topk, int32_t* row_ptr,
+                      int32_t* col_idx, int32_t* col_ptr, int32_t* row_idx, void* ws, size_t ws_bytes,
+                      void* stream) {
+  Dims d;
+  int s = check_problem(p, d);
+  if (s) return s;
+  if (topk < 1) return VSA2_E_ARG;
+  if (!aligned(scores) || !aligned(row_ptr) || !aligned(col_idx) || !aligned(col_ptr) || !aligned(row_idx))
+    return VSA2_E_ARG;
+  if ((s = check_ws(ws, ws_bytes, ws_plan(d, nullptr, nullptr)))) return s;
+  TopkArgs a{};
+  a.scores = scores;
+  a.row_ptr = row_ptr;
+  a.col_idx = col_idx;
+  a.col_ptr = col_ptr;
+  a.row_idx = row_idx;
+  a.bh = d.bh;
+  a.nb = d.nb;
+  a.k = budget(d, topk);  // nb min(topk, nb)
+  ws_plan(d, &a.ws, ws);
+  return hip_status(launch_topk_rows(a, (hipStream_t)stream));
 }
 
 int vsa2_topk_per_seq(const vsa2_problem* p, const float* scores, int32_t topk, int32_t* row_ptr, int32_t* col_idx,

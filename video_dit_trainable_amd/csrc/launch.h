@@ -40,6 +40,8 @@ struct RouteArgs {
   PadGrid pad;
   uint64_t* kmask;    // workspace [ceil(8 nb / 64)] (padded grids): bit b of word t set when pooled key 64t + b exists
   int bs;             // 2^bs cubes per attention block: the scores are means over block pairs
+  int g1;             // VSA router baseline: qr, kr are the coarse operands (hstride rows per head), nb counts
+  int hstride;        //   blocks, and the scores are P_c itself
 };
 hipError_t launch_route(const RouteArgs& a, hipStream_t st);
 
@@ -60,6 +62,9 @@ struct TopkArgs {
   TopkWs ws;
 };
 hipError_t launch_topk(const TopkArgs& a, hipStream_t st);
+// Per-row TopK (the VSA router baseline): every row keeps its own k / nb largest
+// scores, CSR then CSC (uses ws.colcnt and ws.bitmap)
+hipError_t launch_topk_rows(const TopkArgs& a, hipStream_t st);
 // CSC from a caller CSR (uses ws.colcnt and ws.bitmap)
 hipError_t launch_plan(const TopkArgs& a, hipStream_t st);
 

@@ -138,21 +138,25 @@ __global__ void k_route_kmask(uint64_t* __restrict__ kmask, int nb, PadGrid pad)
 // masked, such queries get LSE +inf, so pass 2 gives them no weight.
 // BS: 2^BS cubes per attention block (pass 2 averages the 8 2^BS x 8 2^BS
 // entries of each block pair; nb counts cubes).
-template <typename T, int D, bool PASS2, bool TAIL, bool PAD, int BS>
+// G1: the VSA router baseline -- one pooled token per attention block (the
+// coarse operands Q_c, K_c, hstride rows per head; nb counts blocks), and
+// pass 2 writes the probabilities P_c themselves (Eq.(2)).
+template <typename T, int D, bool PASS2, bool TAIL, bool PAD, int BS, bool G1 = false>
 __global__ __launch_bounds__(256, 2) void k_router(const T* __restrict__ qr, const T* __restrict__ kr,
                                                    float* __restrict__ lse2, float* __restrict__ scores, int nb,
-                                                   float c, const uint64_t* __restrict__ kmask) {
+                                                   float c, const uint64_t* __restrict__ kmask, int hstride) {
   static_assert(!(TAIL && PAD), "the existence words cover the ragged tail");
   static_assert(BS == 0 || (BS == 1 && PASS2), "128-token blocks change only the score pass");
+  static_assert(!G1 || (!PAD && BS == 0), "the coarse operands have one row per block");
   __shared__ __align__(16) T kA[RK * D];
   __shared__ __align__(16) T kB[RK * D];
-  const int Lr = 8 * nb;
+  const int Lr = G1 ? nb : 8 * nb;  // pooled tokens per head
   const int nqt = (Lr + RQ - 1) / RQ, nkt = (Lr + RK - 1) / RK;
   int bh, qt;
   if (!xcd_work(blockIdx.x, nqt, bh, qt)) return;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, cc = lane & 15;
-  const T* qbase = qr + (size_t)bh * Lr * D;
-  const T* kbase = kr + (size_t)bh * Lr * D;
+  const T* qbase = qr + (size_t)bh * hstride * D;
+  const T* kbase = kr + (size_t)bh * hstride * D;
 
   // this wave's 32 pooled queries as B fragments: query qt*128 + 32w + 16qb + cc
   Frag<T> qf[2][D / 32];
@@ -222,7 +226,22 @@ __global__ __launch_bounds__(256, 2) void k_router(const T* __restrict__ qr, con
   float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};  // pass 1: running max / sum (scaled log2 domain)
 
   auto consume = [&](const f32x4 (&acc)[4][2], int t) {
-    if constexpr (!PASS2) {
+    if constexpr (PASS2 && G1) {
+      // P_c of query 16qb + cc and keys t*64 + 32 (kb >> 1) + 4 (kb & 1) + 8g + r
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        const int qrow = qt * RQ + 32 * w + 16 * qb + cc;
+        if (qrow >= Lr) continue;
+        float* dst = scores + ((size_t)bh * nb + qrow) * nb;
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+          const int key0 = t * RK + 32 * (kb >> 1) + 4 * (kb & 1) + 8 * g;
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (key0 + r < nb) dst[key0 + r] = fast_exp2(fmaf(acc[kb][qb][r], c, -lse[qb]));
+        }
+      }
+    } else if constexpr (!PASS2) {
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
         float mt = acc[0][qb][0];
@@ -311,23 +330,38 @@ hipError_t launch_route_tt(const RouteArgs& a, hipStream_t st) {
   }
   timer_before(TK_ROUTER_LSE, st);
   hipLaunchKernelGGL((k_router<T, D, false, TAIL, PAD, 0>), grid, dim3(256), 0, st, (const T*)a.qr, (const T*)a.kr,
-                     a.lse2, a.scores, a.nb, a.scale_log2, (const uint64_t*)a.kmask);
+                     a.lse2, a.scores, a.nb, a.scale_log2, (const uint64_t*)a.kmask, 8 * a.nb);
   timer_after(TK_ROUTER_LSE, st);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   timer_before(TK_ROUTER_SCORES, st);
   if (a.bs)
     hipLaunchKernelGGL((k_router<T, D, true, TAIL, PAD, 1>), grid, dim3(256), 0, st, (const T*)a.qr,
-                       (const T*)a.kr, a.lse2, a.scores, a.nb, a.scale_log2, (const uint64_t*)a.kmask);
+                       (const T*)a.kr, a.lse2, a.scores, a.nb, a.scale_log2, (const uint64_t*)a.kmask, 8 * a.nb);
   else
     hipLaunchKernelGGL((k_router<T, D, true, TAIL, PAD, 0>), grid, dim3(256), 0, st, (const T*)a.qr,
-                       (const T*)a.kr, a.lse2, a.scores, a.nb, a.scale_log2, (const uint64_t*)a.kmask);
+                       (const T*)a.kr, a.lse2, a.scores, a.nb, a.scale_log2, (const uint64_t*)a.kmask, 8 * a.nb);
   timer_after(TK_ROUTER_SCORES, st);
+  return hipGetLastError();
+}
+
+// The VSA router baseline: P_c over the nb coarse tokens (hstride rows per head).
+template <typename T, int D, bool TAIL>
+hipError_t launch_route_coarse_tt(const RouteArgs& a, hipStream_t st) {
+  const int nqt = (a.nb + RQ - 1) / RQ;
+  dim3 grid(xcd_grid(nqt, a.bh));
+  hipLaunchKernelGGL((k_router<T, D, false, TAIL, false, 0, true>), grid, dim3(256), 0, st, (const T*)a.qr,
+                     (const T*)a.kr, a.lse2, a.scores, a.nb, a.scale_log2, nullptr, a.hstride);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((k_router<T, D, true, TAIL, false, 0, true>), grid, dim3(256), 0, st, (const T*)a.qr,
+                     (const T*)a.kr, a.lse2, a.scores, a.nb, a.scale_log2, nullptr, a.hstride);
   return hipGetLastError();
 }
 
 template <typename T, int D>
 hipError_t launch_route_t(const RouteArgs& a, hipStream_t st) {
+  if (a.g1) return a.nb % RK ? launch_route_coarse_tt<T, D, true>(a, st) : launch_route_coarse_tt<T, D, false>(a, st);
   if (a.pad.on) return launch_route_tt<T, D, false, true>(a, st);
   return (8 * a.nb) % RK ? launch_route_tt<T, D, true, false>(a, st) : launch_route_tt<T, D, false, false>(a, st);
 }

@@ -365,6 +365,89 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t st) {
   return csc_from_bitmap(a, st);
 }
 
+// The VSA router baseline's selection (paper §1, Figure 1 left): every query
+// block keeps its own kr largest scores, ties to the lower column.  One
+// workgroup per (row, batch * head): a 4-pass radix select over 8-bit digits
+// of the bit patterns (LDS histogram) finds the kr-th largest pattern tau and
+// how many entries equal to tau to take; the row is then compacted in column
+// order (wave ballots, per-wave totals through LDS).  Writes the CSR.
+__global__ __launch_bounds__(256) void k_row_topk(const float* __restrict__ scores, int32_t* __restrict__ row_ptr,
+                                                  int32_t* __restrict__ col_idx, int nb, int kr) {
+  __shared__ uint32_t hist[256];
+  __shared__ uint32_t sel_state[2];
+  __shared__ uint32_t wcnt[4][2];
+  const int row = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const float* s = scores + ((size_t)bh * nb + row) * nb;
+  uint32_t prefix = 0, need = (uint32_t)kr;
+  for (int pass = 0; pass < 4; ++pass) {
+    const int shift = 24 - 8 * pass;
+    hist[tid] = 0u;
+    __syncthreads();
+    for (int j = tid; j < nb; j += 256) {
+      const uint32_t u = score_bits(s[j]);
+      if (pass == 0 || (u >> (shift + 8)) == (prefix >> (shift + 8))) atomicAdd(&hist[(u >> shift) & 255u], 1u);
+    }
+    __syncthreads();
+    if (tid == 0) {
+      uint32_t acc = 0;
+      int b = 255;
+      for (; b > 0; --b) {
+        if (acc + hist[b] >= need) break;
+        acc += hist[b];
+      }
+      sel_state[0] = prefix | ((uint32_t)b << shift);
+      sel_state[1] = need - acc;
+    }
+    __syncthreads();
+    prefix = sel_state[0];
+    need = sel_state[1];
+    __syncthreads();  // every thread has the state before the next pass clears the histogram
+  }
+  const uint32_t tau = prefix;  // take every entry above tau and the first `need` equal to it
+  const uint64_t lt = lanemask_lt(lane);
+  int32_t* out = col_idx + ((size_t)bh * nb + row) * kr;
+  uint32_t gt_seen = 0, eq_seen = 0;
+  for (int j0 = 0; j0 < nb; j0 += 256) {
+    const int j = j0 + tid;
+    const uint32_t u = j < nb ? score_bits(s[j]) : 0u;
+    const bool gt = j < nb && u > tau, eq = j < nb && u == tau;
+    const uint64_t gtm = __ballot(gt), eqm = __ballot(eq);
+    if (lane == 0) {
+      wcnt[w][0] = (uint32_t)__popcll(gtm);
+      wcnt[w][1] = (uint32_t)__popcll(eqm);
+    }
+    __syncthreads();
+    uint32_t gtb = gt_seen + (uint32_t)__popcll(gtm & lt), eqb = eq_seen + (uint32_t)__popcll(eqm & lt);
+    uint32_t gtt = 0, eqt = 0;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      if (v < w) {
+        gtb += wcnt[v][0];
+        eqb += wcnt[v][1];
+      }
+      gtt += wcnt[v][0];
+      eqt += wcnt[v][1];
+    }
+    const bool sel = gt || (eq && eqb < need);
+    const uint32_t pos = gtb + min(eqb, need);  // selected entries before column j
+    if (sel && pos < (uint32_t)kr) out[pos] = j;
+    gt_seen += gtt;
+    eq_seen += eqt;
+    __syncthreads();  // the per-wave totals are rewritten next chunk
+  }
+  if (tid == 0) {
+    row_ptr[(size_t)bh * (nb + 1) + row] = row * kr;
+    if (row == nb - 1) row_ptr[(size_t)bh * (nb + 1) + nb] = nb * kr;
+  }
+}
+
+hipError_t launch_topk_rows(const TopkArgs& a, hipStream_t st) {
+  const int kr = (int)(a.k / a.nb);
+  hipLaunchKernelGGL(k_row_topk, dim3(a.nb, a.bh), dim3(256), 0, st, a.scores, a.row_ptr, a.col_idx, a.nb, kr);
+  VSA2_CHECK(hipGetLastError());
+  return launch_plan(a, st);
+}
+
 hipError_t launch_plan(const TopkArgs& a, hipStream_t st) {
   VSA2_CHECK(launch_fill_u32(a.ws.colcnt, 0u, (size_t)a.bh * a.nb, st));
   VSA2_CHECK(launch_fill_u32(a.ws.bitmap, 0u, (size_t)a.bh * a.nb * a.ws.words, st));

@@ -16,7 +16,7 @@ LIB_PATH = os.path.join(_HERE, "libvsa2.so")
 
 VSA2_OK, VSA2_E_ARG, VSA2_E_SHAPE, VSA2_E_WORKSPACE, VSA2_E_HIP, VSA2_E_UNSUPPORTED = range(6)
 VSA2_F32, VSA2_BF16 = 0, 1
-OP_POOL, OP_ROUTE, OP_TOPK, OP_PLAN, OP_FWD, OP_BWD, OP_COARSE, OP_COARSE_BWD = range(8)
+OP_POOL, OP_ROUTE, OP_TOPK, OP_PLAN, OP_FWD, OP_BWD, OP_COARSE, OP_COARSE_BWD, OP_ROUTE_COARSE, OP_TOPK_ROW = range(10)
 K_FINE_FWD, K_BWD_DKDV, K_BWD_DQ, K_ROUTER_LSE, K_ROUTER_SCORES = range(5)
 
 
@@ -49,6 +49,8 @@ _SIGS = {
     "vsa2_pool": (ctypes.c_int, [_PP, _P, _P, _P, _P, _P]),
     "vsa2_route": (ctypes.c_int, [_PP, _P, _P, _P, _SZ, _P]),
     "vsa2_topk_per_seq": (ctypes.c_int, [_PP, _P, _I32, _P, _P, _P, _P, _P, _SZ, _P]),
+    "vsa2_route_coarse": (ctypes.c_int, [_PP, _P, _P, _P, _SZ, _P]),
+    "vsa2_topk_per_row": (ctypes.c_int, [_PP, _P, _I32, _P, _P, _P, _P, _P, _SZ, _P]),
     "vsa2_plan_from_csr": (ctypes.c_int, [_PP, _I32, _P, _P, _P, _P, _P, _SZ, _P]),
     "vsa2_sparse_attn_fwd": (ctypes.c_int, [_PP, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "vsa2_sparse_attn_bwd": (ctypes.c_int, [_PP, _I32] + [_P] * 15 + [_SZ, _P]),
@@ -148,6 +150,18 @@ def vsa2_topk_per_seq(p, scores, topk, row_ptr, col_idx, col_ptr, row_idx, ws, s
         _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
 
 
+def vsa2_route_coarse(p, pooled, scores, ws, stream=None):
+    _check("vsa2_route_coarse", lib().vsa2_route_coarse(ctypes.byref(p), _ptr(pooled), _ptr(scores), _ptr(ws),
+                                                        0 if ws is None else ws.numel() * ws.element_size(),
+                                                        _stream(stream)))
+
+
+def vsa2_topk_per_row(p, scores, topk, row_ptr, col_idx, col_ptr, row_idx, ws, stream=None):
+    _check("vsa2_topk_per_row", lib().vsa2_topk_per_row(
+        ctypes.byref(p), _ptr(scores), topk, _ptr(row_ptr), _ptr(col_idx), _ptr(col_ptr), _ptr(row_idx),
+        _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
+
+
 def vsa2_plan_from_csr(p, topk, row_ptr, col_idx, col_ptr, row_idx, ws, stream=None):
     _check("vsa2_plan_from_csr", lib().vsa2_plan_from_csr(
         ctypes.byref(p), topk, _ptr(row_ptr), _ptr(col_idx), _ptr(col_ptr), _ptr(row_idx),
@@ -231,14 +245,21 @@ class Layer:
         self.lse = torch.empty((p.batch, p.heads, self.rows), dtype=torch.float32, device=device)
         self.saved = _ws(saved_size(p), device)
         ws_need = max(workspace_size(p, op, topk, d_model)
-                      for op in (OP_ROUTE, OP_TOPK, OP_PLAN, OP_FWD, OP_BWD, OP_COARSE, OP_COARSE_BWD))
+                      for op in (OP_ROUTE, OP_TOPK, OP_PLAN, OP_FWD, OP_BWD, OP_COARSE, OP_COARSE_BWD,
+                                 OP_ROUTE_COARSE, OP_TOPK_ROW))
         self.ws = _ws(ws_need, device)
         self._grads = None
 
-    def forward(self, q, k, v, x, w_g, route=True, stream=None):
+    def forward(self, q, k, v, x, w_g, route=True, stream=None, router="vsa2"):
+        """router: "vsa2" (fine-grained router, per-sequence TopK) or "vsa"
+        (the coarse-score router with a TopK per query block)."""
         p = self.p
         vsa2_pool(p, q, k, v, self.pooled, stream)
-        if route:
+        if route and router == "vsa":
+            vsa2_route_coarse(p, self.pooled, self.scores, self.ws, stream)
+            vsa2_topk_per_row(p, self.scores, self.topk, self.row_ptr, self.col_idx, self.col_ptr,
+                              self.row_idx, self.ws, stream)
+        elif route:
             vsa2_route(p, self.pooled, self.scores, self.ws, stream)
             vsa2_topk_per_seq(p, self.scores, self.topk, self.row_ptr, self.col_idx, self.col_ptr,
                               self.row_idx, self.ws, stream)
