@@ -65,13 +65,20 @@ def cpu_baseline(w, q, k, v, d_o, budget_s=20.0):
     lr = w.L // 8
     order = np.random.default_rng(0).permutation(w.nblk)
     n_router, t_router = 0, 0.0
-    while t_router < budget_s / 2 and n_router < w.nblk:
+    if w.router == "vsa":                   # the coarse scores of the whole head at once
+        t0 = time.perf_counter()
+        orc.coarse_scores(qh, kh, w.grid, bf16_pooled=True, block=w.block)
+        t_router = time.perf_counter() - t0
+        n_router = w.nblk
+        fl = 2 * 2 * w.nblk * w.nblk * w.head_dim
+    while w.router != "vsa" and t_router < budget_s / 2 and n_router < w.nblk:
         rows = np.sort(order[n_router:n_router + 32])
         t0 = time.perf_counter()
         orc.router_scores(qh, kh, w.grid, bf16_pooled=True, rows=rows, block=w.block)
         t_router += time.perf_counter() - t0
         n_router += len(rows)
-    fl = n_router * (w.block // 8) * 2 * 2 * lr * w.head_dim
+    if w.router != "vsa":
+        fl = n_router * (w.block // 8) * 2 * 2 * lr * w.head_dim
     rp, ci = make_selection(w)
     mask = orc.csr_to_mask(rp[0, 0].numpy(), ci[0, 0].numpy(), w.nblk)
     live = [int(i) for i in order if mask[i].any()]
@@ -110,10 +117,12 @@ def describe(w):
     skew = ", skewed query-cube scales" if w.skew else ""
     if w.text:
         skew += f", {w.text} MMDiT text tokens in the fine branch (dense video-text and text-video)"
+    router = ("router pool 2x2x2" if w.router == "vsa2" else
+              "VSA router baseline (coarse block scores, TopK per query block)")
     blocks = "4x4x4 cubes" if w.block == 64 else "128-token blocks of 4x4x8 (two cubes)"
     return (f"{'720p training' if w.name.startswith('train720') else w.name} shape: {grid}, B={w.batch}, "
-            f"{w.heads} heads, d={w.head_dim}, {w.dtype}, router pool 2x2x2, {blocks}, per-sequence "
-            f"top{w.topk}{skew}; {what}")
+            f"{w.heads} heads, d={w.head_dim}, {w.dtype}, {router}, {blocks}, "
+            f"{'per-sequence ' if w.router == 'vsa2' else ''}top{w.topk}{skew}; {what}")
 
 
 def source_hash(kernel):
@@ -187,10 +196,17 @@ def main():
         mark(0)
         vsa2.vsa2_pool(p, q, k, v, layer.pooled)
         mark(1)
-        vsa2.vsa2_route(p, layer.pooled, layer.scores, layer.ws)
+        if w.router == "vsa":
+            vsa2.vsa2_route_coarse(p, layer.pooled, layer.scores, layer.ws)
+        else:
+            vsa2.vsa2_route(p, layer.pooled, layer.scores, layer.ws)
         mark(2)
-        vsa2.vsa2_topk_per_seq(p, layer.scores, w.topk, layer.row_ptr, layer.col_idx, layer.col_ptr,
-                               layer.row_idx, layer.ws)
+        if w.router == "vsa":
+            vsa2.vsa2_topk_per_row(p, layer.scores, w.topk, layer.row_ptr, layer.col_idx, layer.col_ptr,
+                                   layer.row_idx, layer.ws)
+        else:
+            vsa2.vsa2_topk_per_seq(p, layer.scores, w.topk, layer.row_ptr, layer.col_idx, layer.col_ptr,
+                                   layer.row_idx, layer.ws)
         mark(3)
         vsa2.vsa2_sparse_attn_fwd(p, w.topk, q, k, v, layer.row_ptr, layer.col_idx, layer.o_f, layer.lse, layer.ws)
         mark(4)

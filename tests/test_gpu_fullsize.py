@@ -38,6 +38,7 @@ INFER = WORKLOADS["infer720"]
 TRAIN_PAD = WORKLOADS["train720pad"]    # 43 x 47 x 103, padded to the same 44 x 48 x 104 slots
 TRAIN_B128 = WORKLOADS["train720b128"]  # 128-token blocks (4x4x8), 1716 blocks
 TRAIN_TEXT = WORKLOADS["train720text"]  # plus 512 MMDiT text tokens in the fine branch
+TRAIN_VSA = WORKLOADS["train720vsa"]    # the VSA router baseline at top128
 
 
 def _dev():
@@ -424,3 +425,35 @@ def test_text_rows_at_full_size():
     np.testing.assert_allclose(gu.f64(layer.lse[0, h])[toks], lse[toks], atol=1e-3)
     assert torch.equal(layer.o[:, :, w.L:], layer.o_f[:, :, w.L:]), "text rows: O must be O_f"
     assert torch.all(layer.o_f[:, :, w.L + w.text:] == 0) and torch.all(torch.isneginf(layer.lse[:, :, w.L + w.text:]))
+
+
+# ----------------------------------------------------------------------------- VSA router baseline
+def test_vsa_router_at_full_size():
+    """The VSA router baseline at 720p, top128: P_c rows sum to 1 and match the
+    oracle on sampled rows; every row keeps exactly the top 128 of the GPU's
+    own scores; the fine forward of sampled cubes on that selection."""
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    w = TRAIN_VSA
+    dev = _dev()
+    q, k, v = make_qkv(w, device=dev)
+    x, w_g = make_gate_inputs(w, device=dev, zero_gate=False)
+    p = vsa2.problem(w.batch, w.heads, w.head_dim, w.grid, w.dtype, block=w.block)
+    layer = vsa2.Layer(p, w.topk, w.d_model, device=dev)
+    layer.forward(q, k, v, x, w_g, router="vsa")
+    torch.cuda.synchronize()
+    scores = layer.scores[0]
+    np.testing.assert_allclose(scores.double().sum(dim=2).cpu().numpy(), 1.0, rtol=1e-4)
+    for h in (1, 16):
+        want = orc.coarse_scores(gu.f64(q[0, h]), gu.f64(k[0, h]), w.grid, bf16_pooled=True)
+        got = scores[h].double().cpu().numpy()
+        for i in (0, w.nb // 2, w.nb - 1):
+            assert gu.rel_l2(got[i], want[i]) <= 1e-4, f"head {h} row {i}"
+        sel = orc.csr_to_mask(layer.row_ptr[0, h].cpu().numpy(), layer.col_idx[0, h].cpu().numpy(), w.nb)
+        assert np.array_equal(sel, orc.topk_per_row(got, w.topk)[0]), f"head {h}: not the per-row top k"
+    h = 16
+    sel = orc.csr_to_mask(layer.row_ptr[0, h].cpu().numpy(), layer.col_idx[0, h].cpu().numpy(), w.nb)
+    cubes = [0, 1717, w.nb - 1]
+    o_f, _ = orc.fine_forward(gu.f64(q[0, h]), gu.f64(k[0, h]), gu.f64(v[0, h]), sel, rows=cubes)
+    toks = orc._tokens_of(cubes)
+    gu.assert_close_bf16(gu.f64(layer.o_f[0, h])[toks], o_f[toks], f"O_f head {h}")

@@ -33,6 +33,7 @@ class Workload:
     extra_topk: tuple = field(default_factory=tuple)
     block: int = 64        # attention block: 64 (a 4x4x4 cube) or 128 (4x4x8, two x-adjacent cubes)
     text: int = 0          # MMDiT text tokens joining the fine branch (rows after the video slots)
+    router: str = "vsa2"   # "vsa2" (fine-grained, per-sequence TopK) or "vsa" (coarse scores, TopK per row)
 
     @property
     def pgrid(self):
@@ -101,6 +102,10 @@ WORKLOADS = {
         # the 720p training problem with 512 MMDiT text tokens in the fine branch
         Workload("train720text", 8, (44, 48, 104), 1, 20, 128, "bf16", 64, "lowrank", skew=True, train=True,
                  text=512),
+        # the 720p training problem under the VSA router the paper compares
+        # against: coarse scores, top128 per query block
+        Workload("train720vsa", 9, (44, 48, 104), 1, 20, 128, "bf16", 128, "lowrank", skew=True, train=True,
+                 router="vsa"),
     ]
 }
 
@@ -129,10 +134,12 @@ def flops(w: Workload, topk=None):
     lr = w.L // SUB
     pair = 4 * w.block * w.block * d
     tpair = text_pairs(w) * 4 * CUBE * CUBE * d
+    # the VSA router's two passes run over the nb coarse tokens
+    rt = w.nblk if w.router == "vsa" else lr
     return {
         "fine_fwd": bh * (k * pair + tpair),
         "fine_bwd": bh * (k * pair + tpair) * 5 // 2,
-        "router": bh * 2 * 2 * lr * lr * d,
+        "router": bh * 2 * 2 * rt * rt * d,
         "coarse_fwd": bh * 4 * w.nblk * w.nblk * d,
         "coarse_bwd": bh * 10 * w.nblk * w.nblk * d,
         "gate_fwd": 2 * w.batch * w.L * w.d_model * w.heads,
@@ -155,12 +162,13 @@ def kernel_flops(w: Workload, topk=None):
     lr = w.L // SUB
     gemm = 2 * w.block * w.block * d
     tg = text_pairs(w) * 2 * CUBE * CUBE * d      # text tile pairs, one GEMM each
+    rt = w.nblk if w.router == "vsa" else lr
     return {
         "fine_fwd": bh * (k * 2 * gemm + 2 * tg),
         "bwd_dkdv": bh * (k * 4 * gemm + 4 * tg),
         "bwd_dq": bh * (k * gemm + tg),
-        "router_lse": bh * 2 * lr * lr * d,
-        "router_scores": bh * 2 * lr * lr * d,
+        "router_lse": bh * 2 * rt * rt * d,
+        "router_scores": bh * 2 * rt * rt * d,
     }
 
 
