@@ -136,7 +136,11 @@ __device__ __forceinline__ void dkdv_pair(const T* qs, const T* dos, const float
 // cubes; a video KV cube's list continues with every text query cube (text
 // attends to all video), a text KV cube's list is every video and text query
 // cube.  The text KV cubes take the first blocks of the grid.
-template <typename T, typename TO, int D, bool DENSE, bool PAD, int BS, bool TEXT>
+// QB = 2 (128-token blocks): a workgroup takes both KV cubes of a block (waves
+// 0, 1 the first cube, 2, 3 the second), which share the block's list; each
+// wave runs both query halves of every staged Q / dO tile itself, so the
+// tiles are staged once for 128 keys and no query-half reduction is needed.
+template <typename T, typename TO, int D, bool DENSE, bool PAD, int BS, bool TEXT, int QB = 1>
 __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(const T* __restrict__ q, const T* __restrict__ k,
                                                      const T* __restrict__ v, const T* __restrict__ d_o,
                                                      const float* __restrict__ stats,
@@ -150,6 +154,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(const T* __restrict__ q, co
   static_assert(!(DENSE && PAD), "padding applies to the fine branch");
   static_assert(!DENSE || BS == 0, "the dense mode has one cube per block");
   static_assert(!(DENSE && TEXT), "text rows apply to the fine branch");
+  static_assert(QB == 1 || (QB == 2 && BS == 1 && !TEXT && !DENSE), "whole-block workgroups for 128-token blocks");
   constexpr int TILE = 64 * D;
   __shared__ __align__(16) T tA[2 * TILE];  // stage A: Q tile | dO tile
   __shared__ __align__(16) T tB[2 * TILE];  // stage B
@@ -167,11 +172,15 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(const T* __restrict__ q, co
     } else {
       if (!xcd_work(blockIdx.x - tblk, nkv, bh, j)) return;
     }
+  } else if constexpr (QB == 2) {
+    int jb;
+    if (!xcd_work(blockIdx.x, nkv >> 1, bh, jb)) return;
+    j = (jb << 1) + ((int)threadIdx.x >> 7);  // this wave's KV cube
   } else {
     if (!xcd_work(blockIdx.x, nkv, bh, j)) return;
   }
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, cc = lane & 15;
-  const int kh = w & 1, qh = w >> 1;
+  const int kh = w & 1, qh = QB == 2 ? 0 : w >> 1;  // QB = 2: every wave runs both query halves
   const size_t hoff = (size_t)bh * ld * D;
 
   int cnt, nsel = 0;  // list length; nsel = selected entries before the text query cubes
@@ -260,10 +269,11 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(const T* __restrict__ q, co
     dva[db][0] = dva[db][1] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  int brow = 0, btr = 0;  // per-lane parts of the bf16 fragment addresses
+  int brow = 0, btr = 0, btr1 = 0;  // per-lane parts of the bf16 fragment addresses
   if constexpr (sizeof(T) == 2) {
     brow = sw_row_base<T, D>(cc, g);  // rows 16m + cc add 16m D (the swizzle sees only r & 15)
     btr = sw_tr_base<T, D>(32 * qh, g, cc);
+    if constexpr (QB == 2) btr1 = sw_tr_base<T, D>(32, g, cc);
   }
   bool ok_a = false, ok_b = false;
   int raw = 0;  // list entry whose copy starts next
@@ -280,7 +290,11 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(const T* __restrict__ q, co
       if (n + 2 < cnt) raw = entry(n + 2);
       VSA2_FETCH_QDO(ii, tB, sB);
     }
-    if (ok_a) dkdv_pair<T, D, DENSE>(tA, tA + TILE, sA, brow, btr, kf, vf, kv_ok, dka, dva, qh, g, cc, c);
+    if (ok_a) {
+      dkdv_pair<T, D, DENSE>(tA, tA + TILE, sA, brow, btr, kf, vf, kv_ok, dka, dva, qh, g, cc, c);
+      if constexpr (QB == 2)  // the other query half
+        dkdv_pair<T, D, DENSE>(tA, tA + TILE, sA, brow, btr1, kf, vf, kv_ok, dka, dva, 1, g, cc, c);
+    }
     if (n + 1 >= cnt) break;
     wait_vm0();
     __syncthreads();  // stage B holds entry n + 1; every wave is done with stage A
@@ -289,10 +303,22 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(const T* __restrict__ q, co
       if (n + 3 < cnt) raw = entry(n + 3);
       VSA2_FETCH_QDO(ii, tA, sA);
     }
-    if (ok_b) dkdv_pair<T, D, DENSE>(tB, tB + TILE, sB, brow, btr, kf, vf, kv_ok, dka, dva, qh, g, cc, c);
+    if (ok_b) {
+      dkdv_pair<T, D, DENSE>(tB, tB + TILE, sB, brow, btr, kf, vf, kv_ok, dka, dva, qh, g, cc, c);
+      if constexpr (QB == 2)
+        dkdv_pair<T, D, DENSE>(tB, tB + TILE, sB, brow, btr1, kf, vf, kv_ok, dka, dva, 1, g, cc, c);
+    }
   }
 #undef VSA2_FETCH_QDO
 
+  if constexpr (QB == 2) {  // each wave holds its keys' whole sums
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) dka[db][kb][r] *= scale;
+  } else {
   // sum the two query halves: waves with qh = 1 hand their partials to qh = 0 through LDS
   __syncthreads();
   constexpr int PART = (D / 16) * 2 * 4 * 64;  // floats per wave and tensor
@@ -322,6 +348,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(const T* __restrict__ q, co
         dka[db][kb][r] = (dka[db][kb][r] + mine[o]) * scale;
         dva[db][kb][r] += mine[PART + o];
       }
+  }
   // the coarse branch's per-block gradient rows, 1/n to each of the block's
   // n real tokens (n = 64 2^BS unless the grid is padded)
   if (dk_add && !textk) {
@@ -437,7 +464,11 @@ __device__ __forceinline__ void dq_pair(const T* ks, const T* vs, int brow, int 
 // cubes; a video query cube's list continues with every text cube, a text
 // query cube's list is every video and text cube.  The text query cubes take
 // the first blocks of the grid.
-template <typename T, typename TO, int D, bool DENSE, bool STATS, bool PAD, int BS, bool TEXT>
+// QB = 2 (128-token blocks): a workgroup takes both query cubes of a block
+// (waves 0, 1 the first cube, 2, 3 the second); each wave runs both key
+// halves of every staged K / V tile itself, so the tiles are staged once for
+// 128 query rows and no key-half reduction is needed.
+template <typename T, typename TO, int D, bool DENSE, bool STATS, bool PAD, int BS, bool TEXT, int QB = 1>
 __global__ __launch_bounds__(256, 2) void k_bwd_dq(const T* __restrict__ q, const T* __restrict__ k,
                                                    const T* __restrict__ v, const T* __restrict__ d_o,
                                                    const T* __restrict__ o, const float* __restrict__ lse,
@@ -451,6 +482,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(const T* __restrict__ q, cons
   static_assert(!PAD || (STATS && !DENSE), "padding applies to the fine branch");
   static_assert(!DENSE || BS == 0, "the dense mode has one cube per block");
   static_assert(!TEXT || (STATS && !DENSE), "text rows apply to the fine branch");
+  static_assert(QB == 1 || (QB == 2 && BS == 1 && !TEXT && !DENSE), "whole-block workgroups for 128-token blocks");
   constexpr int TILE = 64 * D;
   __shared__ __align__(16) T tA[2 * TILE];  // stage A: K tile | V tile
   __shared__ __align__(16) T tB[2 * TILE];  // stage B
@@ -467,12 +499,17 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(const T* __restrict__ q, cons
       if (!xcd_work(blockIdx.x - tblk, nq, bh, i)) return;
       if (ct > 0) i = blocked_cube(i, ct, cy, cx);
     }
+  } else if constexpr (QB == 2) {
+    int ib;
+    if (!xcd_work(blockIdx.x, nq >> 1, bh, ib)) return;
+    if (ct > 0) ib = blocked_cube(ib, ct, cy, cx >> 1);
+    i = (ib << 1) + ((int)threadIdx.x >> 7);  // this wave's query cube
   } else {
     if (!xcd_work(blockIdx.x, nq, bh, i)) return;
     if (ct > 0) i = blocked_cube(i, ct, cy, cx);
   }
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, cc = lane & 15;
-  const int qh = w & 1, kh = w >> 1;
+  const int qh = w & 1, kh = QB == 2 ? 0 : w >> 1;  // QB = 2: every wave runs both key halves
   const size_t hoff = (size_t)bh * ld * D;
 
   int cnt, nsel = 0;  // list length; nsel = selected entries before the text cubes
@@ -577,10 +614,11 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(const T* __restrict__ q, cons
 #pragma unroll
   for (int db = 0; db < D / 16; ++db) dqa[db][0] = dqa[db][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  int brow = 0, btr = 0;
+  int brow = 0, btr = 0, btr1 = 0;
   if constexpr (sizeof(T) == 2) {
     brow = sw_row_base<T, D>(cc, g);  // rows 16m + cc add 16m D (the swizzle sees only r & 15)
     btr = sw_tr_base<T, D>(32 * kh, g, cc);
+    if constexpr (QB == 2) btr1 = sw_tr_base<T, D>(32, g, cc);
   }
   int lim_a = 0, lim_b = 0, raw = 0;
   uint64_t km_a = ~0ull, km_b = ~0ull;  // PAD: real slots of the staged KV cubes
@@ -609,6 +647,9 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(const T* __restrict__ q, cons
     }
     if (lim_a > 32 * kh)
       dq_pair<T, D, PAD>(tA, tA + TILE, brow, btr, lim_a, km_a, qf, of, l2, ndl, dqa, kh, g, cc, c);
+    if constexpr (QB == 2) {  // the other key half
+      if (lim_a > 32) dq_pair<T, D, PAD>(tA, tA + TILE, brow, btr1, lim_a, km_a, qf, of, l2, ndl, dqa, 1, g, cc, c);
+    }
     if (n + 1 >= cnt) break;
     wait_vm0();
     __syncthreads();  // stage B holds entry n + 1; every wave is done with stage A
@@ -620,9 +661,20 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(const T* __restrict__ q, cons
     }
     if (lim_b > 32 * kh)
       dq_pair<T, D, PAD>(tB, tB + TILE, brow, btr, lim_b, km_b, qf, of, l2, ndl, dqa, kh, g, cc, c);
+    if constexpr (QB == 2) {
+      if (lim_b > 32) dq_pair<T, D, PAD>(tB, tB + TILE, brow, btr1, lim_b, km_b, qf, of, l2, ndl, dqa, 1, g, cc, c);
+    }
   }
 #undef VSA2_FETCH_KV
 
+  if constexpr (QB == 2) {  // each wave holds its queries' whole sums
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db)
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) dqa[db][qb][r] *= scale;
+  } else {
   // sum the two key halves through LDS
   __syncthreads();
   constexpr int PART = (D / 16) * 2 * 4 * 64;
@@ -645,6 +697,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(const T* __restrict__ q, cons
 #pragma unroll
       for (int r = 0; r < 4; ++r)
         dqa[db][qb][r] = (dqa[db][qb][r] + mine[((db * 2 + qb) * 4 + r) * 64 + lane]) * scale;
+  }
   if (dq_add && !textq) {  // the coarse branch's per-block gradient row, 1/n to each of the n real tokens
     const float* qa = dq_add + ((size_t)bh * (nq >> BS) + (i >> BS)) * D;
     float wq[2] = {1.0f / (float)(64 << BS), 1.0f / (float)(64 << BS)};
@@ -679,7 +732,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(const T* __restrict__ q, cons
   }
 }
 
-template <typename T, typename TO, int D, bool DENSE, bool PAD, int BS, bool TEXT>
+template <typename T, typename TO, int D, bool DENSE, bool PAD, int BS, bool TEXT, int QB = 1>
 hipError_t launch_bwd_tt(const AttnBwdArgs& a, hipStream_t st) {
   // dQ first: in sparse mode it writes the row statistics the dK/dV kernel reads
   const int tblk = TEXT ? (a.ntc * a.bh + 7) & ~7 : 0;  // text cubes take the first blocks
@@ -690,7 +743,7 @@ hipError_t launch_bwd_tt(const AttnBwdArgs& a, hipStream_t st) {
                        a.stats, a.row_ptr, a.col_idx, a.dq_add, (TO*)a.dq, a.nq, a.nkv, a.seq, a.ld, a.out_rows, a.kph,
                        a.scale, a.scale_log2, a.ct, a.cy, a.cx, a.pad, 0, 0, a.bh);
   else
-    hipLaunchKernelGGL((k_bwd_dq<T, TO, D, DENSE, true, PAD, BS, TEXT>), dim3(tblk + xcd_grid(a.nq, a.bh)),
+    hipLaunchKernelGGL((k_bwd_dq<T, TO, D, DENSE, true, PAD, BS, TEXT, QB>), dim3(tblk + xcd_grid(a.nq / QB, a.bh)),
                        dim3(256), 0, st, (const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.d_o, (const T*)a.o,
                        a.lse, a.stats_out, nullptr, a.row_ptr, a.col_idx, a.dq_add, (TO*)a.dq, a.nq, a.nkv, a.seq,
                        a.ld, a.out_rows, a.kph, a.scale, a.scale_log2, a.ct, a.cy, a.cx, a.pad, a.ntc, a.ntext, a.bh);
@@ -698,7 +751,7 @@ hipError_t launch_bwd_tt(const AttnBwdArgs& a, hipStream_t st) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (!DENSE) timer_before(TK_BWD_DKDV, st);
-  hipLaunchKernelGGL((k_bwd_dkdv<T, TO, D, DENSE, PAD, BS, TEXT>), dim3(tblk + xcd_grid(a.nkv, a.bh)), dim3(256),
+  hipLaunchKernelGGL((k_bwd_dkdv<T, TO, D, DENSE, PAD, BS, TEXT, QB>), dim3(tblk + xcd_grid(a.nkv / QB, a.bh)), dim3(256),
                      0, st, (const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.d_o,
                      DENSE ? a.stats : a.stats_out, a.col_ptr, a.row_idx, a.dk_add, a.dv_add, (TO*)a.dk, (TO*)a.dv,
                      a.nq, a.nkv, a.seq, a.ld, a.out_rows, a.kph, a.scale, a.scale_log2, a.pad, a.ntc, a.ntext, a.bh);
@@ -712,6 +765,9 @@ hipError_t launch_bwd_t(const AttnBwdArgs& a, hipStream_t st) {
 #define VSA2_BWD(PAD, BS)                                                                              \
   return a.ntc ? launch_bwd_tt<T, T, D, false, PAD, BS, true>(a, st)                                  \
                : launch_bwd_tt<T, T, D, false, PAD, BS, false>(a, st)
+  if (a.bs && !a.ntc)  // whole 128-token blocks per workgroup
+    return a.pad.on ? launch_bwd_tt<T, T, D, false, true, 1, false, 2>(a, st)
+                    : launch_bwd_tt<T, T, D, false, false, 1, false, 2>(a, st);
   if (a.bs) {
     if (a.pad.on) VSA2_BWD(true, 1);
     VSA2_BWD(false, 1);

@@ -36,8 +36,12 @@ namespace vsa2 {
 // selected cubes and then to every text cube; a text query cube attends to
 // every video and text cube.  The text query cubes take the first blocks of
 // the grid, so their long lists start first.
-template <typename T, typename TO, int D, bool DENSE, bool PAD, int BS, bool TEXT>
-__global__ __launch_bounds__(128, 2) void k_attn_fwd(const T* __restrict__ q, const T* __restrict__ k,
+// QB = 2 (128-token blocks): a 256-thread workgroup takes both query cubes of
+// a block (waves 0, 1 the first cube, 2, 3 the second), which share the
+// block's KV list, so every gathered K / V tile is staged once for 128 query
+// rows.
+template <typename T, typename TO, int D, bool DENSE, bool PAD, int BS, bool TEXT, int QB = 1>
+__global__ __launch_bounds__(128 * QB, 2) void k_attn_fwd(const T* __restrict__ q, const T* __restrict__ k,
                                                   const T* __restrict__ v, const int32_t* __restrict__ row_ptr,
                                                   const int32_t* __restrict__ col_idx, TO* __restrict__ o,
                                                   float* __restrict__ lse, int nq, int nkv, int seq, int ld,
@@ -45,6 +49,7 @@ __global__ __launch_bounds__(128, 2) void k_attn_fwd(const T* __restrict__ q, co
                                                   PadGrid pad, int ntc, int ntext, int nbh) {
   static_assert(!(DENSE && PAD), "padding applies to the fine branch");
   static_assert(!(DENSE && TEXT), "text rows apply to the fine branch");
+  static_assert(QB == 1 || (QB == 2 && BS == 1 && !TEXT && !DENSE), "whole-block workgroups for 128-token blocks");
   __shared__ __align__(16) T ks[64 * D];
   __shared__ __align__(16) T vs[64 * D];
   int bh, i;
@@ -60,11 +65,16 @@ __global__ __launch_bounds__(128, 2) void k_attn_fwd(const T* __restrict__ q, co
       if (!xcd_work(blockIdx.x - tblk, nq, bh, i)) return;
       if (ct > 0) i = blocked_cube(i, ct, cy, cx);
     }
+  } else if constexpr (QB == 2) {
+    if (!xcd_work(blockIdx.x, nq >> 1, bh, i)) return;  // i: the block
+    if (ct > 0) i = blocked_cube(i, ct, cy, cx >> 1);
   } else {
     if (!xcd_work(blockIdx.x, nq, bh, i)) return;
     if (ct > 0) i = blocked_cube(i, ct, cy, cx);
   }
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, cc = lane & 15;
+  const int qcube = QB == 2 ? (i << 1) + (w >> 1) : i;  // this wave's query cube
+  const int wq = QB == 2 ? (w & 1) : w;                // and its 32-row half
   const size_t hoff = (size_t)bh * ld * D;
   const T* kbase = k + hoff;
   const T* vbase = v + hoff;
@@ -76,9 +86,10 @@ __global__ __launch_bounds__(128, 2) void k_attn_fwd(const T* __restrict__ q, co
   } else if (TEXT && textq) {
     cnt = nkv + ntc;
   } else {
+    const int blk = QB == 2 ? i : (i >> BS);
     const int32_t* rp = row_ptr + (size_t)bh * ((nq >> BS) + 1);
-    const int64_t start = min<int64_t>(max(rp[i >> BS], 0), kph);
-    const int64_t end = min<int64_t>(max<int64_t>(rp[(i >> BS) + 1], start), kph);
+    const int64_t start = min<int64_t>(max(rp[blk], 0), kph);
+    const int64_t end = min<int64_t>(max<int64_t>(rp[blk + 1], start), kph);
     cnt = (int)(end - start) << BS;
     cols = col_idx + (size_t)bh * kph + start;
     nsel = cnt;
@@ -106,7 +117,8 @@ __global__ __launch_bounds__(128, 2) void k_attn_fwd(const T* __restrict__ q, co
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-    for (int s = 0; s < D / 32; ++s) qf[qb][s] = frag_global<T, D>(q + hoff, i * 64 + 32 * w + 16 * qb + cc, s, g);
+    for (int s = 0; s < D / 32; ++s)
+      qf[qb][s] = frag_global<T, D>(q + hoff, qcube * 64 + 32 * wq + 16 * qb + cc, s, g);
 
   f32x4 oacc[D / 16][2];
 #pragma unroll
@@ -114,7 +126,7 @@ __global__ __launch_bounds__(128, 2) void k_attn_fwd(const T* __restrict__ q, co
   float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};
 
   if (cnt > 0) {
-    SwRegs<64, D, T, 128> kr, vr;
+    SwRegs<64, D, T, 128 * QB> kr, vr;
     int vtr = 0;  // bf16: this lane's part of the transposed V reads (rows 4g + c/4 of key half 0)
     if constexpr (sizeof(T) == 2) vtr = sw_tr_base<T, D>(0, g, cc);
     int j = cube_at(0);
@@ -228,12 +240,12 @@ __global__ __launch_bounds__(128, 2) void k_attn_fwd(const T* __restrict__ q, co
     }
   }
   if constexpr (PAD) {
-    if (!textq) qm = cube_slots(i, pad);
+    if (!textq) qm = cube_slots(qcube, pad);
   }
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
-    const int qrow = i * 64 + 32 * w + 16 * qb + cc;
-    const bool real = !(PAD || TEXT) || ((qm >> (32 * w + 16 * qb + cc)) & 1);
+    const int qrow = qcube * 64 + 32 * wq + 16 * qb + cc;
+    const bool real = !(PAD || TEXT) || ((qm >> (32 * wq + 16 * qb + cc)) & 1);
     const float lsum = group_sum(l[qb]);  // every lane takes part in the cross-lane sum
     const float lt = real ? lsum : 0.f;
     const float inv = lt > 0.f ? 1.0f / lt : 0.f;
@@ -269,11 +281,19 @@ hipError_t launch_fwd_t(const AttnArgs& a, hipStream_t st) {
 #define VSA2_FWD_T(PAD, BS)                   \
   if (a.ntc) VSA2_FWD(PAD, BS, true);         \
   else VSA2_FWD(PAD, BS, false)
-    if (a.bs) {
+    const dim3 bgrid(xcd_grid(a.nq >> 1, a.bh));  // whole 128-token blocks per workgroup
+#define VSA2_FWD_BLOCK(PAD)                                                                                     \
+  hipLaunchKernelGGL((k_attn_fwd<T, T, D, false, PAD, 1, false, 2>), bgrid, dim3(256), 0, st, (const T*)a.q,    \
+                     (const T*)a.k, (const T*)a.v, a.row_ptr, a.col_idx, (T*)a.o, a.lse, a.nq, a.nkv, a.seq, a.ld, \
+                     a.out_rows, a.kph, a.scale_log2, a.ct, a.cy, a.cx, a.pad, 0, 0, a.bh)
+    if (a.bs && !a.ntc) {
+      if (a.pad.on) { VSA2_FWD_BLOCK(true); } else { VSA2_FWD_BLOCK(false); }
+    } else if (a.bs) {
       if (a.pad.on) { VSA2_FWD_T(true, 1); } else { VSA2_FWD_T(false, 1); }
     } else {
       if (a.pad.on) { VSA2_FWD_T(true, 0); } else { VSA2_FWD_T(false, 0); }
     }
+#undef VSA2_FWD_BLOCK
 #undef VSA2_FWD_T
 #undef VSA2_FWD
     timer_after(TK_FINE_FWD, st);
