@@ -768,9 +768,9 @@ hipError_t launch_bwd_t(const AttnBwdArgs& a, hipStream_t st) {
   if (a.bs && !a.ntc)  // whole 128-token blocks per workgroup
     return a.pad.on ? launch_bwd_tt<T, T, D, false, true, 1, false, 2>(a, st)
                     : launch_bwd_tt<T, T, D, false, false, 1, false, 2>(a, st);
-  if (a.bs) {
-    if (a.pad.on) VSA2_BWD(true, 1);
-    VSA2_BWD(false, 1);
+  if (a.bs) {  // with text rows: per-cube workgroups
+    if (a.pad.on) return launch_bwd_tt<T, T, D, false, true, 1, true>(a, st);
+    return launch_bwd_tt<T, T, D, false, false, 1, true>(a, st);
   }
   if (a.pad.on) VSA2_BWD(true, 0);
   VSA2_BWD(false, 0);

@@ -288,8 +288,8 @@ hipError_t launch_fwd_t(const AttnArgs& a, hipStream_t st) {
                      a.out_rows, a.kph, a.scale_log2, a.ct, a.cy, a.cx, a.pad, 0, 0, a.bh)
     if (a.bs && !a.ntc) {
       if (a.pad.on) { VSA2_FWD_BLOCK(true); } else { VSA2_FWD_BLOCK(false); }
-    } else if (a.bs) {
-      if (a.pad.on) { VSA2_FWD_T(true, 1); } else { VSA2_FWD_T(false, 1); }
+    } else if (a.bs) {  // with text rows: per-cube workgroups
+      if (a.pad.on) { VSA2_FWD(true, 1, true); } else { VSA2_FWD(false, 1, true); }
     } else {
       if (a.pad.on) { VSA2_FWD_T(true, 0); } else { VSA2_FWD_T(false, 0); }
     }
