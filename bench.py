@@ -177,8 +177,10 @@ def main():
     torch.cuda.set_device(dev)
     log(f"generating inputs for {w.name} on the GPU")
     q, k, v = make_qkv(w, device=dev)
+    log("Q, K, V ready")
     d_o = make_grad_out(w, device=dev)
     x, w_g = make_gate_inputs(w, device=dev, zero_gate=False)
+    log("dO, X, W_g ready")
     p = vsa2.problem(w.batch, w.heads, w.head_dim, w.grid, w.dtype, block=w.block, text=w.text)
     layer = vsa2.Layer(p, w.topk, w.d_model, device=dev)
     torch.cuda.synchronize()
