@@ -251,6 +251,23 @@ def main():
     per = {n: float(np.median([evs[s][i].elapsed_time(evs[s][i + 1]) for s in range(args.steps)]))
            for i, n in enumerate(names)}
     log("per-call ms: " + ", ".join(f"{n} {t:.3f}" for n, t in per.items()))
+    steps_ms = [evs[s][0].elapsed_time(evs[s][7]) for s in range(args.steps)]
+    step_dist = {"median": round(float(np.median(steps_ms)), 3), "min": round(float(np.min(steps_ms)), 3),
+                 "p90": round(float(np.percentile(steps_ms, 90)), 3)}
+
+    # cold steps: a 512 MiB write (larger than L2 and the 256 MB Infinity Cache)
+    # before each, outside its events
+    flush = torch.empty(128 << 20, dtype=torch.float32, device=dev)
+    cold = []
+    for _ in range(3):
+        flush.fill_(1.0)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(8)]
+        step_full(ev)
+        torch.cuda.synchronize()
+        cold.append(ev[0].elapsed_time(ev[7]))
+    del flush
+    log(f"step ms: median {step_dist['median']}, min {step_dist['min']}, p90 {step_dist['p90']}; "
+        f"cold (after a 512 MiB flush) median {float(np.median(cold)):.3f}")
 
     fl = flops(w)
     step_flops = fl["router"] + fl["fine_fwd"] + fl["coarse_fwd"] + fl["gate_fwd"]
@@ -319,6 +336,8 @@ def main():
         "config": {"workload": describe(w),
                    "global_batch": w.batch, "seq_len": w.L, "heads": w.heads, "head_dim": w.head_dim,
                    "topk": w.topk, "parallelism": "single GPU"},
+        "step_ms": step_dist,
+        "cold_ms_per_step": round(float(np.median(cold)), 3),
         "step_flops": step_flops,
         "ops": ops,
         "kernels": kernels,
