@@ -158,6 +158,39 @@ def copy_calibration(dev):
     log(f"copy calibration: torch.neg over {n * 4} bytes read and {n * 4} bytes written")
 
 
+def measured_peaks(dev):
+    """Peaks measured on this device, beside the vendor figures: a dense bf16
+    GEMM through torch (hipBLASLt), 8192^3, and a plain 2 GiB device copy
+    (bytes read + written). Medians of 10 runs each."""
+    n = 8192
+    a = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
+    b = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
+    src = torch.empty(1 << 29, dtype=torch.float32, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+
+    def med(fn):
+        for _ in range(3):
+            fn()
+        ts = []
+        for _ in range(10):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return float(np.median(ts))
+
+    gemm_ms = med(lambda: torch.mm(a, b))
+    copy_ms = med(lambda: dst.copy_(src))
+    out = {"bf16_gemm_tflops": round(2 * n ** 3 / (gemm_ms * 1e-3) / 1e12, 1),
+           "copy_gbps": round(2 * src.numel() * 4 / (copy_ms * 1e-3) / 1e9, 1),
+           "gemm": "torch.mm bf16 8192x8192x8192", "copy": "2 GiB device-to-device, read + write bytes"}
+    del a, b, src, dst
+    log(f"measured peaks: bf16 GEMM {out['bf16_gemm_tflops']} TFLOP/s, copy {out['copy_gbps']} GB/s")
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -314,6 +347,7 @@ def main():
 
     if args.copy_calibration:
         copy_calibration(dev)
+    peaks = measured_peaks(dev)
 
     cpu = None
     if not args.no_cpu:
@@ -342,6 +376,7 @@ def main():
         "ops": ops,
         "kernels": kernels,
         "roofline": roof,
+        "measured_peaks": peaks,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
