@@ -102,7 +102,18 @@ def cpu_baseline(w, q, k, v, d_o, budget_s=20.0):
             "sample": f"head 0 of the same inputs: router rows of {n_router} query {unit} ({t_router:.1f} s) + "
                       f"fine fwd+bwd of {n_fine} query {unit}, {pairs} selected pairs ({t_fine:.1f} s); fp64 numpy"
                       f"{note}",
-            "seconds": round(secs, 2)}
+            "seconds": round(secs, 2), "cpu": cpu_model(), "host_cpus": os.cpu_count()}
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def describe(w):
