@@ -63,7 +63,9 @@ extern "C" {
 enum vsa2_status {
   VSA2_OK = 0,
   VSA2_E_ARG = 1,         /* NULL pointer, misaligned pointer, bad scalar argument   */
-  VSA2_E_SHAPE = 2,       /* empty or oversized grid, head_dim not 64/128            */
+  VSA2_E_SHAPE = 2,       /* empty or oversized grid (more than 46,340 cubes, more  */
+                          /* than 65,535 batch x heads, or batch x heads x (cubes + */
+                          /* text cubes + 8) x 256 beyond 2^32), head_dim not 64/128*/
   VSA2_E_WORKSPACE = 3,   /* workspace smaller than vsa2_workspace_size() reports     */
   VSA2_E_HIP = 4,         /* a HIP call or kernel launch failed                       */
   VSA2_E_UNSUPPORTED = 5  /* valid request the library does not implement             */

@@ -99,6 +99,8 @@ def test_block128_sizes():
     (dict(grid=(-4, 16, 16)), vsa2.VSA2_E_SHAPE),
     (dict(grid=(400, 400, 400)), vsa2.VSA2_E_SHAPE),       # nb beyond the int32 index range
     (dict(batch=0), vsa2.VSA2_E_SHAPE),
+    (dict(batch=2, heads=40000), vsa2.VSA2_E_SHAPE),              # batch x heads beyond grid.y
+    (dict(heads=20000, grid=(44, 48, 104)), vsa2.VSA2_E_SHAPE),   # grid work-items beyond 2^32
 ])
 def test_bad_problem_rejected(kw, code):
     with pytest.raises(vsa2.Vsa2Error) as e:

@@ -45,7 +45,13 @@ int check_problem(const vsa2_problem* p, Dims& o) {
   const int64_t L = 64 * nc;
   if (nc > 46340) return VSA2_E_SHAPE;  // nc^2 and all indices fit int32
   const int64_t nb = nc >> bs;
-  if ((int64_t)p->batch * p->heads > (1 << 20)) return VSA2_E_SHAPE;
+  // launch limits: (batch, head) pairs index grid.y (at most 65,535), and the
+  // largest one-dimensional grid, about (cubes + text cubes + 8) workgroups of
+  // 256 threads per (batch, head), must keep its work-item count within 32 bits
+  const int64_t bh = (int64_t)p->batch * p->heads;
+  if (bh > 65535) return VSA2_E_SHAPE;
+  const int64_t ntc = ((int64_t)p->text_tokens + 63) / 64;
+  if (bh * (8 * ((nc + 7) / 8) + ntc + 8) * 256 > (int64_t)0xFFFFFFFF) return VSA2_E_SHAPE;
   if (std::isnan(p->softmax_scale) || std::isinf(p->softmax_scale)) return VSA2_E_ARG;
   o.batch = p->batch;
   o.heads = p->heads;
