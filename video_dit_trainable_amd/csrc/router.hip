@@ -242,24 +242,42 @@ __global__ __launch_bounds__(256, 2) void k_router(const T* __restrict__ qr, con
         }
       }
     } else if constexpr (!PASS2) {
+      // The tile's terms are taken against the lane's running maximum m as it
+      // stands; m moves (with the exact tile maximum, and l rescaled) only for
+      // the first tile with a key, or when the tile's sum leaves [0, 2^64]
+      // (a key more than about 58 above m in the log2 domain, or an overflow).
+      // The sum stays exact: every term is exp2(s c - m c) for the m that l
+      // is kept against, and the final merge over lanes rescales each l once.
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
-        float mt = acc[0][qb][0];
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) mt = fmaxf(mt, acc[kb][qb][r]);
-        if (mt > m[qb]) {
-          l[qb] *= fast_exp2((m[qb] - mt) * c);
-          m[qb] = mt;
-        }
+        float lt = 0.f;
         if (m[qb] != -INFINITY) {
           const float mc = -m[qb] * c;
 #pragma unroll
           for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) l[qb] += fast_exp2(fmaf(acc[kb][qb][r], c, mc));
+            for (int r = 0; r < 4; ++r) lt += fast_exp2(fmaf(acc[kb][qb][r], c, mc));
         }
+        if (m[qb] == -INFINITY || !(lt <= 0x1p64f)) {
+          float mt = acc[0][qb][0];
+#pragma unroll
+          for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) mt = fmaxf(mt, acc[kb][qb][r]);
+          lt = 0.f;
+          if (mt > m[qb]) {
+            l[qb] *= fast_exp2((m[qb] - mt) * c);
+            m[qb] = mt;
+          }
+          if (m[qb] != -INFINITY) {
+            const float mc = -m[qb] * c;
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+              for (int r = 0; r < 4; ++r) lt += fast_exp2(fmaf(acc[kb][qb][r], c, mc));
+          }
+        }
+        l[qb] += lt;
       }
     } else {
 #pragma unroll
