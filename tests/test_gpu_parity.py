@@ -103,6 +103,35 @@ def test_router_scores(w):
         np.testing.assert_allclose(got[h], want, rtol=1e-4, atol=1e-4 * want.mean())
 
 
+@pytest.mark.parametrize("jump", [30.0, 100.0])
+def test_router_late_extreme_key(jump):
+    """One pooled key of the last 64-key tile scores `jump` (log2 domain) above
+    every other key of each row. Pass 1 keeps a lane's running maximum until
+    a tile's sum leaves [0, 2^64]: at 30 the large terms are summed against
+    the stale maximum, at 100 the tile forces the exact rescale. Both must
+    give the oracle's scores and rows that sum to 1/8."""
+    w = TINY_TRAIN                                   # fp32, d = 64, 256 pooled keys = 4 tiles
+    q, k, v = make_qkv(w)
+    u = torch.ones(w.head_dim)
+    q = 0.1 * q + u                                  # every pooled query lies close to u
+    c = 1.4426950408889634 / np.sqrt(w.head_dim)     # softmax scale in the log2 domain
+    key = 250                                        # pooled key in the last tile
+    alpha = jump / (c * float(u @ u))                # pooled key alpha u: q_r . k scores about jump / c
+    k[:, :, 8 * key:8 * key + 8, :] = alpha * u      # the 8 tokens of that 2x2x2 sub-cube
+    p = vsa2.problem(w.batch, w.heads, w.head_dim, w.grid, w.dtype)
+    layer = vsa2.Layer(p, w.topk, w.d_model, device=_dev())
+    qd, kd, vd = (t.to(_dev()) for t in (q, k, v))
+    vsa2.vsa2_pool(layer.p, qd, kd, vd, layer.pooled)
+    vsa2.vsa2_route(layer.p, layer.pooled, layer.scores, layer.ws)
+    torch.cuda.synchronize()
+    got = gu.f64(layer.scores[0])
+    np.testing.assert_allclose(got.sum(axis=2), 1.0 / 8.0, rtol=2e-5)
+    for h in range(w.heads):
+        want = orc.router_scores(gu.f64(q[0, h]), gu.f64(k[0, h]), w.grid, bf16_pooled=False)
+        assert want[:, key // 8].min() > 0.124      # the planted key's cube takes almost all of each row
+        np.testing.assert_allclose(got[h], want, rtol=1e-4, atol=1e-4 * want.mean())
+
+
 # ----------------------------------------------------------------------------- topk
 def _topk_on(scores_np, topk, grid_nb):
     """GPU TopK on given scores [H, nb, nb] (generator-made, same for both)."""
