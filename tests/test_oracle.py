@@ -752,3 +752,31 @@ def test_coarse_scores_are_the_coarse_attention_map():
     kb = np.stack([kr_[blk == b].mean(0) for b in range(4)])
     want = torch.softmax(torch.tensor(qb @ kb.T * 0.25), -1).numpy()
     np.testing.assert_allclose(orc.coarse_scores(q2, k2, g2, block=128), want, rtol=1e-12)
+
+
+# ----------------------------------------------------------------------------- list formats
+def test_csr_csc_of_a_worked_mask():
+    # rows: 0 -> {1, 3}, 1 -> {}, 2 -> {0, 1}, 3 -> {3}; written out by hand
+    mask = np.zeros((4, 4), dtype=bool)
+    mask[0, [1, 3]] = mask[2, [0, 1]] = mask[3, 3] = True
+    row_ptr, col_idx, col_ptr, row_idx = orc.mask_to_csr_csc(mask)
+    assert row_ptr.tolist() == [0, 2, 2, 4, 5] and col_idx.tolist() == [1, 3, 0, 1, 3]
+    # columns: 0 <- {2}, 1 <- {0, 2}, 2 <- {}, 3 <- {0, 3}
+    assert col_ptr.tolist() == [0, 1, 3, 3, 5] and row_idx.tolist() == [2, 0, 2, 0, 3]
+    assert np.array_equal(orc.csr_to_mask(row_ptr, col_idx, 4), mask)
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_csr_csc_round_trip(seed):
+    rng = np.random.default_rng(seed)
+    nb = 13
+    mask = rng.random((nb, nb)) < 0.3
+    mask[4] = False                       # an empty row
+    mask[:, 7] = False                    # an empty column
+    row_ptr, col_idx, col_ptr, row_idx = orc.mask_to_csr_csc(mask)
+    assert row_ptr[-1] == col_ptr[-1] == mask.sum()
+    assert np.array_equal(orc.csr_to_mask(row_ptr, col_idx, nb), mask)
+    assert np.array_equal(orc.csr_to_mask(col_ptr, row_idx, nb), mask.T)   # CSC is the CSR of the transpose
+    for i in range(nb):                   # ascending within each row and column
+        assert np.all(np.diff(col_idx[row_ptr[i]:row_ptr[i + 1]]) > 0)
+        assert np.all(np.diff(row_idx[col_ptr[i]:col_ptr[i + 1]]) > 0)
