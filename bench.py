@@ -12,6 +12,7 @@ the CPU oracle timed on a bounded sample.
 """
 
 import argparse
+import dataclasses
 import json
 import os
 import sys
@@ -208,6 +209,7 @@ def main():
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="train720")
+    ap.add_argument("--topk", type=int, default=None, help="override the workload's average KV blocks per query block")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain copy kernel of known size (for counter scaling)")
@@ -217,6 +219,8 @@ def main():
               "across GPUs, which this library does not implement", file=sys.stderr)
         sys.exit(2)
     w = WORKLOADS[args.workload]
+    if args.topk is not None:
+        w = dataclasses.replace(w, name=f"{w.name}-top{args.topk}", topk=args.topk)  # no stored counters apply
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     log(f"generating inputs for {w.name} on the GPU")
