@@ -46,7 +46,7 @@ def masks_from_csr(row_ptr, col_idx, nb):
 
 
 def check_csr_csc(row_ptr, col_idx, col_ptr, row_idx, nb, k):
-    """Structural validity: counts, ascending order, and CSC == transpose of CSR."""
+    """Structural validity: counts, ascending order in every row and column, and CSC == transpose of CSR."""
     rp, ci, cp, ri = (t.cpu().numpy() for t in (row_ptr, col_idx, col_ptr, row_idx))
     for h in range(rp.shape[0]):
         assert rp[h, 0] == 0 and rp[h, -1] == k and np.all(np.diff(rp[h]) >= 0)
@@ -58,6 +58,9 @@ def check_csr_csc(row_ptr, col_idx, col_ptr, row_idx, nb, k):
             assert np.all(np.diff(row) > 0)
         mt = orc.csr_to_mask(cp[h], ri[h], nb).T
         assert np.array_equal(m, mt), "CSC is not the transpose of CSR"
+        for j in range(nb):
+            col = ri[h, cp[h, j]:cp[h, j + 1]]
+            assert np.all(np.diff(col) > 0), "rows not ascending in a CSC column"
 
 
 def band_compare(gpu_mask, oracle_scores, k, rel_band=1e-3):
