@@ -301,20 +301,45 @@ __global__ __launch_bounds__(1024) void k_csc_fill(const uint32_t* __restrict__ 
   const int j = strip * 64 + lane;
   const int R = (nb + NW - 1) / NW;
   const int r0 = min(nb, w * R), r1 = min(nb, r0 + R);
-  const uint32_t* bm = bitmap + (size_t)bh * nb * words + 2 * strip + (lane >> 5);
+  // Rows go through the wave 64 at a time: lane l loads the strip's two
+  // bitmap words of row rb + l, and readlane hands each row's words to every
+  // lane in row order. readlane reads a lane whether or not it is active, so
+  // every lane stays in both passes; only the columns past nb write nothing.
+  const uint32_t* bm = bitmap + (size_t)bh * nb * words + 2 * strip;
+  const bool hi_half = lane >= 32;
   const uint32_t bit = 1u << (lane & 31);
+  auto load_rows = [&](int rb, uint32_t& lo, uint32_t& hi) {
+    const int r = rb + lane;
+    lo = hi = 0u;
+    if (r < r1) {
+      lo = bm[(size_t)r * words];
+      hi = bm[(size_t)r * words + 1];
+    }
+  };
+  auto has = [&](uint32_t lo, uint32_t hi, int i) -> bool {  // does row rb + i select column j
+    const uint32_t a = __builtin_amdgcn_readlane(lo, i), b = __builtin_amdgcn_readlane(hi, i);
+    return ((hi_half ? b : a) & bit) != 0u;
+  };
   uint32_t c = 0;
-#pragma unroll 8
-  for (int i = r0; i < r1; ++i) c += (bm[(size_t)i * words] & bit) ? 1u : 0u;
+  for (int rb = r0; rb < r1; rb += 64) {
+    uint32_t lo, hi;
+    load_rows(rb, lo, hi);
+    const int n = min(64, r1 - rb);
+    for (int i = 0; i < n; ++i) c += has(lo, hi, i) ? 1u : 0u;
+  }
   cnt[w][lane] = c;
   __syncthreads();
-  if (j >= nb) return;
-  uint32_t base = col_ptr[(size_t)bh * (nb + 1) + j];
+  const bool live = j < nb;
+  uint32_t base = live ? (uint32_t)col_ptr[(size_t)bh * (nb + 1) + j] : 0u;
   for (int ww = 0; ww < w; ++ww) base += cnt[ww][lane];
   int32_t* out = row_idx + (size_t)bh * kph;
-#pragma unroll 8
-  for (int i = r0; i < r1; ++i)
-    if ((bm[(size_t)i * words] & bit) && base < kph) out[base++] = i;
+  for (int rb = r0; rb < r1; rb += 64) {
+    uint32_t lo, hi;
+    load_rows(rb, lo, hi);
+    const int n = min(64, r1 - rb);
+    for (int i = 0; i < n; ++i)
+      if (has(lo, hi, i) && live && base < kph) out[base++] = rb + i;
+  }
 }
 
 static hipError_t csc_from_bitmap(const TopkArgs& a, hipStream_t st) {
