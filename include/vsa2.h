@@ -154,7 +154,12 @@ int vsa2_topk_per_seq(const vsa2_problem* p, const float* scores, int32_t topk,
 
 /* CSC form (col_ptr, row_idx) of a caller-chosen selection given as CSR
  * (row_ptr, col_idx, same layout as vsa2_topk_per_seq, exactly k entries per
- * (batch, head), columns ascending and distinct in each row).
+ * (batch, head), columns ascending and distinct in each row).  Entries
+ * outside [0, nb) are ignored.  A column listed twice in one row is a caller
+ * error that stays memory-safe: the CSC holds the pair once and the unused
+ * CSC slots at the end of the list are never read (col_ptr[nb] is then below
+ * k), while the forward and the dQ pass, which read the CSR, take the KV
+ * cube's keys twice into that row's softmax.
  *   ws: vsa2_workspace_size(VSA2_OP_PLAN). */
 int vsa2_plan_from_csr(const vsa2_problem* p, int32_t topk, const int32_t* row_ptr, const int32_t* col_idx,
                        int32_t* col_ptr, int32_t* row_idx, void* ws, size_t ws_bytes, void* stream);

@@ -12,7 +12,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 sys.path.insert(0, ROOT)
 
 import bench  # noqa: E402
-from video_dit_trainable_amd.configs import WORKLOADS, kernel_bytes  # noqa: E402
+from video_dit_trainable_amd.configs import WORKLOADS, compulsory_bytes, gather_bytes, op_bytes  # noqa: E402
 
 
 def test_more_than_one_gpu_is_refused():
@@ -45,7 +45,7 @@ def test_source_hash_covers_the_shared_header():
     assert len(bench.source_hash("fine_fwd")) == 16
 
 
-def test_dkdv_algorithmic_bytes_at_720p():
+def test_dkdv_gather_bytes_at_720p():
     # the per-unit figure times the units of one launch, counted by hand:
     # 20 heads x 3,432 query cubes x top64 = 4,392,960 selected pairs, each
     # gathering a 64 x 128 bf16 Q tile and dO tile (32 KiB), the 64 rows'
@@ -57,7 +57,32 @@ def test_dkdv_algorithmic_bytes_at_720p():
     per_head = 4 * 219648 * 128 * 2 + 2 * 3432 * 128 * 4 + 3433 * 4
     want = pairs * per_pair + 20 * per_head
     assert pairs == 4_392_960
-    assert kernel_bytes(WORKLOADS["train720"])["bwd_dkdv"] == want == 150_784_233_680
+    assert gather_bytes(WORKLOADS["train720"])["bwd_dkdv"] == want == 150_784_233_680
+
+
+def test_compulsory_bytes_at_720p():
+    # forward: Q, K, V read and O_f written once (4 x 219,648 x 128 bf16 per
+    # head), the fp32 LSE of every row, the CSR (219,648 entries + 3,433 row
+    # pointers); 20 heads: the 4.52 GB floor of the fine forward
+    tok = 219648 * 128 * 2
+    idx = 219648 * 4 + 3433 * 4
+    fwd = 20 * (4 * tok + 219648 * 4 + idx)
+    cb = compulsory_bytes(WORKLOADS["train720"])
+    assert cb["fine_fwd"] == fwd
+    assert 4.5e9 < fwd < 4.55e9
+    # each backward kernel reads or writes six per-token tensors once (dK/dV:
+    # Q, K, V, dO in, dK, dV out; dQ: Q, K, V, dO, O_f in, dQ out), plus the
+    # per-row statistics, the lists and the coarse rows (under 2% more)
+    for n in ("bwd_dkdv", "bwd_dq"):
+        assert 20 * 6 * tok < cb[n] < 1.02 * 20 * 6 * tok
+
+
+def test_topk_bytes_count_every_pass():
+    # five passes over the 3,432^2 fp32 scores of each of 20 heads is most of
+    # what the per-sequence TopK moves
+    w = WORKLOADS["train720"]
+    five = 20 * 5 * 3432 * 3432 * 4
+    assert five < op_bytes(w)["topk"] < 1.05 * five
 
 
 @pytest.mark.parametrize("name", sorted(WORKLOADS))

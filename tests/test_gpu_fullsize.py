@@ -39,17 +39,20 @@ TRAIN_PAD = WORKLOADS["train720pad"]    # 43 x 47 x 103, padded to the same 44 x
 TRAIN_B128 = WORKLOADS["train720b128"]  # 128-token blocks (4x4x8), 1716 blocks
 TRAIN_TEXT = WORKLOADS["train720text"]  # plus 512 MMDiT text tokens in the fine branch
 TRAIN_VSA = WORKLOADS["train720vsa"]    # the VSA router baseline at top128
+TRAIN480 = WORKLOADS["train480"]        # 28 x 32 x 52 = 46,592 tokens, 728 cubes
 
 
 def _dev():
     return torch.device("cuda:0")
 
 
-def _run(w, topk, train):
+def _run(w, topk, train, fine_on="seeded"):
     """The layer on the GPU at full size.  Route + TopK run first and their
     scores and selection are kept for the router/TopK checks; the fine branch,
     coarse branch, gate and backward then run on a seeded selection with the
-    exact budget (make_selection), which the oracle is given as well."""
+    exact budget (make_selection, fine_on="seeded"), or, as the benchmark
+    runs them, on the router's own selection (fine_on="routed"); the oracle is
+    given the same selection."""
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     dev = _dev()
@@ -64,9 +67,12 @@ def _run(w, topk, train):
     torch.cuda.synchronize()
     out = dict(w=w, topk=topk, q=q, k=k, v=v, x=x, w_g=w_g, layer=layer,
                routed=[t.clone() for t in (layer.row_ptr, layer.col_idx, layer.col_ptr, layer.row_idx)])
-    sel_rp, sel_ci = make_selection(w, topk=topk)
-    out["sel"] = (sel_rp.numpy(), sel_ci.numpy())
-    layer.set_selection(sel_rp.to(dev), sel_ci.to(dev))
+    if fine_on == "seeded":
+        sel_rp, sel_ci = make_selection(w, topk=topk)
+        out["sel"] = (sel_rp.numpy(), sel_ci.numpy())
+        layer.set_selection(sel_rp.to(dev), sel_ci.to(dev))
+    else:
+        out["sel"] = tuple(t.cpu().numpy() for t in out["routed"][:2])
     layer.forward(q, k, v, x, w_g, route=False)
     if train:
         d_o = make_grad_out(w, device=dev)
@@ -92,7 +98,8 @@ def _routed(r, h):
 
 
 def _seeded(r, h):
-    """The seeded selection of head h that both sides run the fine branch on."""
+    """The selection of head h that both sides run the fine branch on (the
+    seeded one, or the router's own for a routed run)."""
     return r["sel"][0][0, h], r["sel"][1][0, h]
 
 
@@ -167,10 +174,12 @@ def test_fine_forward_sampled(train720, h):
 
 
 def test_merged_output_and_gate_sampled(train720):
-    r = train720
+    _check_merged_output_and_gate(train720, 5)
+
+
+def _check_merged_output_and_gate(r, h):
     w, layer = r["w"], r["layer"]
     oc_hat, _, g = layer.saved_views()
-    h = 5
     rp, ci = _seeded(r, h)
     mask = orc.csr_to_mask(rp, ci, w.nb)
     cubes = _sample_cubes(rp, n_extra=1)
@@ -217,7 +226,10 @@ def test_fine_backward_sampled(train720, h):
 
 
 def test_gate_gradients(train720):
-    r = train720
+    _check_gate_gradients(train720)
+
+
+def _check_gate_gradients(r):
     w, layer = r["w"], r["layer"]
     g = layer.grads()
     oc_hat = np.stack([orc.coarse_forward(gu.f64(r["q"][0, h]), gu.f64(r["k"][0, h]), gu.f64(r["v"][0, h]),
@@ -230,11 +242,119 @@ def test_gate_gradients(train720):
         sl = slice(int(toks[0]), int(toks[-1]) + 1)
         _, dx, part = orc.gate_backward(gu.f64(r["x"][0, sl]), w_g, oc_hat, gu.f64(r["d_o"][0, :, sl]), toks)
         dw += part
-        if t0 in (0, 8 * chunk):
+        if t0 in (0, 2 * chunk, 8 * chunk):
             rr = gu.rel_l2(gu.f64(g["dx"][0, sl]), dx)
             assert rr <= 2e-2, f"dX tokens {t0}..: rel-L2 {rr:.3g}"
     rr = gu.rel_l2(gu.f64(g["dw_g"]), dw)
     assert rr <= 2e-2, f"dW_g: rel-L2 {rr:.3g}"
+
+
+# ----------------------------------------------------------------------------- the router's own selection
+# The fine branch run on the selection the router and the per-sequence TopK
+# made (the benchmark's launch configuration), at the 480p training shape
+# (latent 28x32x52 = 46,592 tokens, 728 cubes) and at the 720p training shape.
+# Per-sequence TopK (Eq.(8)-(9)) gives the "sink" KV cubes that many query
+# cubes select long CSC columns, and the skewed query scales long CSR rows;
+# the longest of both are compared with the oracle.
+@pytest.fixture(scope="module")
+def train480():
+    return _run(TRAIN480, TRAIN480.topk, True, fine_on="routed")
+
+
+@pytest.fixture(scope="module")
+def train720_routed():
+    return _run(TRAIN, TRAIN.topk, True, fine_on="routed")
+
+
+ROUTED = ["train480", "train720_routed"]
+
+
+def test_train480_router_rows_and_selection(train480):
+    r = train480
+    w, layer = r["w"], r["layer"]
+    scores = layer.scores[0]
+    np.testing.assert_allclose(scores.double().sum(dim=2).cpu().numpy(), 1.0 / 8.0, rtol=1e-4)
+    rp0, _ = _routed(r, 0)
+    rows = np.array(sorted({0, int(np.argmax(np.diff(rp0))), w.nb // 2, w.nb - 1}))
+    for h in (0, 11):
+        want = orc.router_scores(gu.f64(r["q"][0, h]), gu.f64(r["k"][0, h]), w.grid, bf16_pooled=True, rows=rows)
+        got = scores[h].double().cpu().numpy()[rows]
+        for n in range(len(rows)):
+            assert gu.rel_l2(got[n], want[n]) <= 1e-4, f"head {h} row {rows[n]}"
+    gu.check_csr_csc(*[t[0, [0, 19]] for t in r["routed"]], w.nb, layer.k)
+    for h in (0, 19):
+        s = scores[h].cpu().numpy().reshape(-1)
+        order = np.argsort(-s, kind="stable")
+        want = np.zeros(s.size, dtype=bool)
+        want[order[:layer.k]] = True
+        rp, ci = _routed(r, h)
+        assert np.array_equal(orc.csr_to_mask(rp, ci, w.nb).reshape(-1), want), f"head {h}"
+    # one whole head against the oracle router's own top k (exact outside the band)
+    h = 7
+    want_scores = orc.router_scores(gu.f64(r["q"][0, h]), gu.f64(r["k"][0, h]), w.grid, bf16_pooled=True)
+    rp, ci = _routed(r, h)
+    outside, band, _ = gu.band_compare(orc.csr_to_mask(rp, ci, w.nb), want_scores, layer.k)
+    assert outside == 0, f"{outside} selection mismatches outside the 1e-3 band ({band} pairs in it)"
+
+
+@pytest.mark.parametrize("name", ROUTED)
+@pytest.mark.parametrize("h", [0, 13])
+def test_routed_fine_forward_longest_row(request, name, h):
+    r = request.getfixturevalue(name)
+    w, layer = r["w"], r["layer"]
+    rp, ci = _seeded(r, h)
+    mask = orc.csr_to_mask(rp, ci, w.nb)
+    cubes = _sample_cubes(rp)                             # the longest row and any empty one among them
+    o, lse = orc.fine_forward(gu.f64(r["q"][0, h]), gu.f64(r["k"][0, h]), gu.f64(r["v"][0, h]), mask, rows=cubes)
+    toks = orc._tokens_of(cubes)
+    got_o = gu.f64(layer.o_f[0, h])[toks]
+    got_lse = gu.f64(layer.lse[0, h])[toks]
+    gu.assert_close_bf16(got_o, o[toks], f"{w.name} O_f head {h} cubes {cubes} (longest list {np.diff(rp).max()})")
+    live = np.isfinite(lse[toks])
+    assert np.all(np.isneginf(got_lse[~live])) and np.all(got_o[~live] == 0)
+    np.testing.assert_allclose(got_lse[live], lse[toks][live], atol=1e-3)
+
+
+@pytest.mark.parametrize("name", ROUTED)
+@pytest.mark.parametrize("h", [0, 13])
+def test_routed_fine_backward_long_columns(request, name, h):
+    """dK, dV of the longest CSC column of the router's selection and of one
+    at the 99th percentile (every query row that selected them, whole rows),
+    and dQ of the longest CSR row."""
+    r = request.getfixturevalue(name)
+    w, layer = r["w"], r["layer"]
+    g = layer.grads()
+    rp, ci = _seeded(r, h)
+    mask = orc.csr_to_mask(rp, ci, w.nb)
+    q, k, v, d_o = (gu.f64(t[0, h]) for t in (r["q"], r["k"], r["v"], r["d_o"]))
+    lens = mask.sum(axis=0)
+    order = np.argsort(lens, kind="stable")
+    js = [int(order[-1]), int(order[int(0.99 * (len(order) - 1))])]
+    assert lens[js[0]] > 3 * w.topk, f"{w.name} head {h}: no long column ({lens[js[0]]})"
+    for j in js:
+        rows = np.nonzero(mask[:, j])[0]
+        sub = np.zeros_like(mask)
+        sub[rows] = mask[rows]
+        _, dk, dv = orc.fine_backward(q, k, v, sub, d_o)
+        tj = np.arange(64 * j, 64 * j + 64)
+        for nm, got, want in (("dK", g["dk"], dk), ("dV", g["dv"], dv)):
+            rr = gu.rel_l2(gu.f64(got[0, h])[tj], want[tj])
+            assert rr <= 2e-2, f"{w.name} {nm} head {h} KV cube {j} ({len(rows)} query cubes): rel-L2 {rr:.3g}"
+    i = int(np.argmax(mask.sum(axis=1)))
+    sub = np.zeros_like(mask)
+    sub[i] = mask[i]
+    dq, _, _ = orc.fine_backward(q, k, v, sub, d_o)
+    ti = np.arange(64 * i, 64 * i + 64)
+    rr = gu.rel_l2(gu.f64(g["dq"][0, h])[ti], dq[ti])
+    assert rr <= 2e-2, f"{w.name} dQ head {h} query cube {i} ({mask[i].sum()} KV cubes): rel-L2 {rr:.3g}"
+
+
+def test_train480_merged_output_and_gate(train480):
+    _check_merged_output_and_gate(train480, 5)
+
+
+def test_train480_gate_gradients(train480):
+    _check_gate_gradients(train480)
 
 
 def test_inference_top128_sampled():

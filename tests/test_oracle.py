@@ -290,6 +290,60 @@ def test_end_to_end_full_budget_cube_constant_is_full_attention():
     assert res["mask"].all()
 
 
+# Routed forward (mask=None): router -> per-sequence TopK -> fine branch.
+# Cube-constant Q, K with Q_i = beta e_sigma(i), K_j = e_j: every pooled key of
+# cube j equals K_j, so the 8 x 8 mean of Eq.(7) is P_r[i, j] =
+# (1/G) softmax_j(beta scale [j == sigma(i)]) -- e^x / (G (e^x + nb - 1)) at
+# j = sigma(i), 1 / (G (e^x + nb - 1)) elsewhere, x = beta * scale.  A budget
+# of one block per query cube (Eq.(9): nb pairs) keeps exactly the nb large
+# entries, so the selection is the permutation sigma, and every query of cube
+# i sees 64 equal logits: O_f = mean of V over cube sigma(i), LSE = x + ln 64.
+# sigma is no involution, so Q and K swapped (sigma^-1) changes the result.
+def test_routed_forward_closed_form_on_a_permutation():
+    grid, nb, G, d, beta = (8, 8, 8), 8, 8, 16, 4.0
+    sigmas = [np.roll(np.arange(nb), 1), np.array([3, 0, 6, 1, 7, 2, 4, 5])]
+    H = len(sigmas)
+    eye = np.eye(d)
+    q = np.stack([np.repeat(beta * eye[s], 64, axis=0) for s in sigmas])
+    k = np.stack([np.repeat(eye[:nb], 64, axis=0)] * H)
+    v = _rand(H, 64 * nb, d)
+    res = orc.vsa2_forward(q, k, v, grid, 1, _rand(64 * nb, 8), np.zeros((8, H)), bf16_pooled=True)
+    x = beta / np.sqrt(d)
+    for h, s in enumerate(sigmas):
+        want = np.full((nb, nb), 1.0 / (G * (np.exp(x) + nb - 1)))
+        want[np.arange(nb), s] = np.exp(x) / (G * (np.exp(x) + nb - 1))
+        np.testing.assert_allclose(res["scores"][h], want, rtol=1e-13)
+        assert np.array_equal(res["mask"][h], np.eye(nb, dtype=bool)[s])
+        o_want = np.repeat(v[h].reshape(nb, 64, d).mean(axis=1)[s], 64, axis=0)
+        np.testing.assert_allclose(res["o_f"][h], o_want, rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(res["lse"][h], x + np.log(64.0), rtol=1e-13)
+
+
+# The routed path is the composition of the separately pinned router (with the
+# bf16 operand rounding), per-sequence TopK and fine branch, on inputs whose
+# selection is neither everything nor one block per row.
+def test_routed_forward_composes_router_topk_and_fine_branch():
+    grid, H, d, topk = (8, 8, 16), 2, 16, 3
+    L, nb = 1024, 16
+    s = _rand(L, d)
+    q, k = _rand(H, L, d) + 0.8 * s, _rand(H, L, d) + 0.8 * s
+    q[:, :256] *= 3.0                      # uneven router rows
+    v = _rand(H, L, d)
+    res = orc.vsa2_forward(q, k, v, grid, topk, _rand(L, 8), np.zeros((8, H)), bf16_pooled=True)
+    for h in range(H):
+        p_r = orc.router_scores(q[h], k[h], grid, bf16_pooled=True)
+        assert np.array_equal(res["scores"][h], p_r)
+        assert not np.array_equal(p_r, orc.router_scores(q[h], k[h], grid))     # the rounding matters here
+        m = orc.topk_per_sequence(p_r, topk)[0]
+        assert np.array_equal(res["mask"][h], m)
+        assert m.sum() == nb * topk and len(set(m.sum(axis=1))) > 2               # ragged rows
+        o_f, lse = orc.fine_forward(q[h], k[h], v[h], m)
+        assert np.array_equal(res["o_f"][h], o_f) and np.array_equal(res["lse"][h], lse)
+    # the selection of the pooled key/query roles swapped is a different one
+    assert not np.array_equal(res["mask"][0], orc.topk_per_sequence(
+        orc.router_scores(k[0], q[0], grid, bf16_pooled=True), topk)[0])
+
+
 # ----------------------------------------------------------------------------- cost model
 def test_cost_model_reproduces_printed_sparsities():
     with open(os.path.join(GOLDEN, "cost_model.json")) as f:

@@ -97,6 +97,17 @@ PLANTS = {
         ("        o = o_f.copy()\n        o[:Lv] = merge(g[:, h], oc_hat, o_f[:Lv], block)",
          "        o = o_f.copy()\n        o[:Lv] = merge(g[:, h], oc_hat, o_f[:Lv], block)\n"
          "        o[Lv:] += oc_hat.mean(axis=0)", "text"),
+    # the routed layer forward (router -> TopK -> fine branch)
+    "routed forward with Q and K swapped":
+        ("p_r = router_scores(q[h][:Lv], k[h][:Lv], grid, scale=scale, bf16_pooled=bf16_pooled, block=block)",
+         "p_r = router_scores(k[h][:Lv], q[h][:Lv], grid, scale=scale, bf16_pooled=bf16_pooled, block=block)",
+         "routed"),
+    "routed forward without the bf16 router operands":
+        ("p_r = router_scores(q[h][:Lv], k[h][:Lv], grid, scale=scale, bf16_pooled=bf16_pooled, block=block)",
+         "p_r = router_scores(q[h][:Lv], k[h][:Lv], grid, scale=scale, bf16_pooled=False, block=block)",
+         "routed"),
+    "routed forward with a TopK per row":
+        ("            m = topk_per_sequence(p_r, topk)[0]", "            m = topk_per_row(p_r, topk)[0]", "routed"),
     # the VSA router baseline
     "per-row TopK ties to the higher column":
         ("        order = np.lexsort((np.arange(nb), -scores[i]))", "        order = np.lexsort((-np.arange(nb), -scores[i]))",

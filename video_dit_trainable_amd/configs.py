@@ -172,16 +172,17 @@ def kernel_flops(w: Workload, topk=None):
     }
 
 
-def kernel_bytes(w: Workload, topk=None):
-    """Algorithmic HBM bytes of one launch of each timed kernel.
+def gather_bytes(w: Workload, topk=None):
+    """Bytes one launch of each timed kernel gathers when no tile is reused.
 
-    The fine kernels gather one B-row tile of two operands per selected block
-    pair with no reuse assumed (K and V for the forward and the dQ kernel, Q
-    and dO plus the B rows' (lse, delta) pairs for the dK/dV kernel), plus the
-    index entry, and read or write the per-token tensors that stay with the
-    block once.  The dK/dV and dQ kernels also read the coarse branch's
-    per-block gradient rows.  A router pass reads the pooled Q_r and K_r once and writes
-    the per-row LSE; the score pass also writes the nb x nb cube scores.
+    This is a property of the tile-gathering design, not a floor: the fine
+    kernels gather one B-row tile of two operands per selected block pair (K
+    and V for the forward and the dQ kernel, Q and dO plus the B rows' (lse,
+    delta) pairs for the dK/dV kernel), plus the index entry, and read or
+    write the per-token tensors that stay with the block once.  The dK/dV and
+    dQ kernels also read the coarse branch's per-block gradient rows.  A
+    router pass reads the pooled Q_r and K_r once and writes the per-row LSE;
+    the score pass also writes the nb x nb cube scores.
     """
     k = w.budget(topk)
     bh = w.batch * w.heads
@@ -200,4 +201,60 @@ def kernel_bytes(w: Workload, topk=None):
         "bwd_dq": bh * (k * (2 * tile + 4) + tp * 2 * t64 + 3 * tok + w.rows * 8 + w.nblk * d * 4 + ptr),
         "router_lse": bh * (2 * lr * d * esz + lr * 4),
         "router_scores": bh * (2 * lr * d * esz + lr * 4 + w.nblk * w.nblk * 4),
+    }
+
+
+def compulsory_bytes(w: Workload, topk=None):
+    """Bytes one launch of each timed kernel must move at least: every input
+    read once and every output written once, whatever the tiling.
+
+    Forward: Q, K, V read, O_f and the LSE written, the CSR read.  dK/dV: Q,
+    K, V, dO and the per-row (lse, delta) pairs read, dK and dV written, the
+    CSC and the coarse per-block dK_c, dV_c rows read.  dQ: Q, K, V, dO, O_f
+    and the LSE read, dQ and the per-row pairs written, the CSR and dQ_c read.
+    Router passes as in gather_bytes (they read each pooled operand once).
+    """
+    k = w.budget(topk)
+    bh = w.batch * w.heads
+    d = w.head_dim
+    esz = 2 if w.dtype == "bf16" else 4
+    tok = w.rows * d * esz
+    idx = k * 4 + (w.nblk + 1) * 4
+    crow = w.nblk * d * 4
+    g = gather_bytes(w, topk)
+    return {
+        "fine_fwd": bh * (4 * tok + w.rows * 4 + idx),
+        "bwd_dkdv": bh * (6 * tok + w.rows * 8 + idx + 2 * crow),
+        "bwd_dq": bh * (6 * tok + w.rows * 4 + w.rows * 8 + idx + crow),
+        "router_lse": g["router_lse"],
+        "router_scores": g["router_scores"],
+    }
+
+
+def op_bytes(w: Workload, topk=None):
+    """Bytes the memory-bound calls move, as implemented (each pass counted).
+
+    route: both router passes (gather_bytes of each).  topk: the per-sequence
+    TopK reads the nb x nb fp32 scores five times (three radix histogram
+    passes, the per-row count and the compaction), writes the CSR and the
+    selection bitmap, then reads the bitmap twice and writes the CSC (the
+    per-row TopK of the VSA router baseline also reads every score five times:
+    four 8-bit radix passes per row and the compaction).  pool: Q, K, V read
+    once, the router and coarse operands written.
+    """
+    k = w.budget(topk)
+    bh = w.batch * w.heads
+    d = w.head_dim
+    esz = 2 if w.dtype == "bf16" else 4
+    nb = w.nblk
+    scores = nb * nb * 4
+    bitmap = nb * 2 * ((nb + 63) // 64) * 4
+    lists = 2 * (k * 4 + (nb + 1) * 4)
+    passes = 5
+    g = gather_bytes(w, topk)
+    nbp = -(-nb // 64) * 64
+    return {
+        "route": g["router_lse"] + g["router_scores"],
+        "topk": bh * (passes * scores + 3 * bitmap + lists),
+        "pool": bh * (3 * w.L * d * esz + (2 * (w.L // SUB) + 3 * nbp) * d * esz),
     }

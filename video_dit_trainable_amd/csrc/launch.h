@@ -1,4 +1,4 @@
-// Internal launch interface between the C-ABI layer (api.cpp) and the kernels.
+// Internal launch interface between the C-ABI layer (api.hip) and the kernels.
 #pragma once
 
 #include <hip/hip_runtime.h>

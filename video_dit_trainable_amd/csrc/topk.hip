@@ -259,7 +259,9 @@ __global__ __launch_bounds__(256) void k_compact(const float* __restrict__ score
   }
 }
 
-// Selection given as CSR: bitmap + column counts.
+// Selection given as CSR: bitmap + column counts.  A column that appears
+// twice in a row sets its bit once and is counted once, so the column counts
+// always match the bitmap the CSC is filled from.
 __global__ __launch_bounds__(256) void k_csr_scatter(const int32_t* __restrict__ row_ptr,
                                                      const int32_t* __restrict__ col_idx, uint32_t* __restrict__ bitmap,
                                                      uint32_t* __restrict__ colcnt, int nb, int64_t kph, int words) {
@@ -271,8 +273,9 @@ __global__ __launch_bounds__(256) void k_csr_scatter(const int32_t* __restrict__
   for (int64_t n = n0 + lane; n < n1; n += 64) {
     const int j = ci[n];
     if ((unsigned)j >= (unsigned)nb) continue;   // corrupt entry: ignored
-    atomicOr(&bitmap[((size_t)bh * nb + row) * words + (j >> 5)], 1u << (j & 31));
-    atomicAdd(&colcnt[(size_t)bh * nb + j], 1u);
+    const uint32_t bit = 1u << (j & 31);
+    const uint32_t was = atomicOr(&bitmap[((size_t)bh * nb + row) * words + (j >> 5)], bit);
+    if (!(was & bit)) atomicAdd(&colcnt[(size_t)bh * nb + j], 1u);
   }
 }
 

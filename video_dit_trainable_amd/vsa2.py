@@ -307,12 +307,11 @@ class Layer:
                 f[n1 + n2:n1 + n2 + self.bh * self.L].view(p.batch, p.heads, self.L))
 
     def pooled_views(self):
+        """(Q_r, K_r [B,H,L/8,d], Q_c, K_c, V_c [B,H,nbp,d]) views of the pooled buffer."""
         p = self.p
-        e = torch.empty((), dtype=self.sdt).element_size()
         flat = self.pooled.view(self.sdt)
         lr, nbp, d = self.L // 8, (self.nb + 63) // 64 * 64, p.head_dim
         n_r, n_c = self.bh * lr * d, self.bh * nbp * d
         sh_r, sh_c = (p.batch, p.heads, lr, d), (p.batch, p.heads, nbp, d)
-        del e
         return (flat[:n_r].view(sh_r), flat[n_r:2 * n_r].view(sh_r), flat[2 * n_r:2 * n_r + n_c].view(sh_c),
                 flat[2 * n_r + n_c:2 * n_r + 2 * n_c].view(sh_c), flat[2 * n_r + 2 * n_c:2 * n_r + 3 * n_c].view(sh_c))
