@@ -68,7 +68,8 @@ enum vsa2_status {
                           /* text cubes + 8) x 256 beyond 2^32), head_dim not 64/128*/
   VSA2_E_WORKSPACE = 3,   /* workspace smaller than vsa2_workspace_size() reports     */
   VSA2_E_HIP = 4,         /* a HIP call or kernel launch failed                       */
-  VSA2_E_UNSUPPORTED = 5  /* valid request the library does not implement             */
+  VSA2_E_UNSUPPORTED = 5, /* valid request the library does not implement             */
+  VSA2_E_SCRATCH = 6      /* beyond the fixed scratch of vsa2_route_noalloc           */
 };
 
 enum vsa2_dtype { VSA2_F32 = 0, VSA2_BF16 = 1 };
@@ -163,6 +164,24 @@ int vsa2_topk_per_seq(const vsa2_problem* p, const float* scores, int32_t topk,
  *   ws: vsa2_workspace_size(VSA2_OP_PLAN). */
 int vsa2_plan_from_csr(const vsa2_problem* p, int32_t topk, const int32_t* row_ptr, const int32_t* col_idx,
                        int32_t* col_ptr, int32_t* row_idx, void* ws, size_t ws_bytes, void* stream);
+
+/* vsa2_route for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same kernels and result as vsa2_route, with the router's scratch (the
+ * log-sum-exp of every pooled query and, on padded grids, one key-existence
+ * word per 64 pooled keys: vsa2_workspace_size(VSA2_OP_ROUTE) bytes) taken
+ * from a fixed array in device memory that the library holds on every GPU it
+ * runs on until the process ends, instead of a caller workspace.
+ *   The array holds vsa2_route_noalloc_limit() bytes (8 MiB; at 720p with 20
+ *   heads the router needs 2.2 MB): a larger problem returns VSA2_E_SCRATCH
+ *   before anything is enqueued.  The call allocates and frees nothing.
+ *   Every call on one GPU shares that GPU's array and leaves its scratch
+ *   there; calls that overlap on one GPU (two streams, two host threads)
+ *   race and must be ordered by the caller. */
+int vsa2_route_noalloc(const vsa2_problem* p, const void* pooled, float* scores, void* stream);
+
+/* Size in bytes of vsa2_route_noalloc's fixed device scratch. */
+int vsa2_route_noalloc_limit(size_t* bytes);
 
 /* The VSA router the paper compares against (§1 and Figure 1 left; Eq.(1)-(2)):
  * block scores from the coarse branch's own attention map,

@@ -3,6 +3,7 @@
 // synchronisation; every call enqueues on the caller's stream.
 #include <cmath>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/vsa2.h"
 #include "launch.h"
@@ -237,6 +238,40 @@ void timer_after(int kid, hipStream_t st) {
 }
 }  // namespace vsa2
 
+// Fixed device scratch of the no-allocation router entry point: one copy of
+// this array lives on every GPU the library runs on, for the life of the
+// process.  Host code never passes the array's name to a kernel (on the host
+// it names a stand-in, not device memory): its device address is looked up
+// once per device with hipGetSymbolAddress and that address is used instead.
+constexpr size_t SCRATCH_BYTES = (size_t)8 << 20;
+static __device__ __align__(256) unsigned char scratch[SCRATCH_BYTES];
+
+namespace {
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[MAX_DEVICES] = {};
+
+// Device address of `scratch` on the current device, looked up on the first
+// call for that device.  Returns hipSuccess and the address, or the error of
+// hipGetDevice / hipGetSymbolAddress.
+hipError_t scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= MAX_DEVICES) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!ptr || (uintptr_t)ptr % ALIGN) return hipErrorInvalidValue;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+}  // namespace
+
 extern "C" {
 
 int vsa2_kernel_timer_start(int32_t kernel, int32_t capacity) {
@@ -274,6 +309,7 @@ const char* vsa2_status_string(int s) {
     case VSA2_E_WORKSPACE: return "workspace too small";
     case VSA2_E_HIP: return "HIP launch failed";
     case VSA2_E_UNSUPPORTED: return "unsupported request";
+    case VSA2_E_SCRATCH: return "problem needs more scratch than the no-allocation entry point's fixed device array";
     default: return "unknown status";
   }
 }
@@ -354,6 +390,29 @@ int vsa2_route(const vsa2_problem* p, const void* pooled, float* scores, void* w
   RouteArgs a{pp.qr, pp.kr, (float*)ws, scores, d.bh, d.nc, d.d, d.bf16, d.scale * 1.4426950408889634f, d.pad,
               d.pad.on ? (uint64_t*)((char*)ws + ws_route_lse(d)) : nullptr, d.bs};
   return hip_status(launch_route(a, (hipStream_t)stream));
+}
+
+int vsa2_route_noalloc(const vsa2_problem* p, const void* pooled, float* scores, void* stream) {
+  Dims d;
+  int s = check_problem(p, d);
+  if (s) return s;
+  if (!aligned(pooled) || !aligned(scores)) return VSA2_E_ARG;
+  const size_t need = ws_route(d);
+  if (need > SCRATCH_BYTES) return VSA2_E_SCRATCH;
+  void* ws = nullptr;
+  if (scratch_address(&ws) != hipSuccess) return VSA2_E_HIP;
+  // the router's scratch is written before it is read (the per-row LSE by
+  // pass 1, the key-existence words by their own kernel), so nothing is cleared
+  Pooled pp = pooled_ptrs(d, pooled);
+  RouteArgs a{pp.qr, pp.kr, (float*)ws, scores, d.bh, d.nc, d.d, d.bf16, d.scale * 1.4426950408889634f, d.pad,
+              d.pad.on ? (uint64_t*)((char*)ws + ws_route_lse(d)) : nullptr, d.bs};
+  return hip_status(launch_route(a, (hipStream_t)stream));
+}
+
+int vsa2_route_noalloc_limit(size_t* bytes) {
+  if (!bytes) return VSA2_E_ARG;
+  *bytes = SCRATCH_BYTES;
+  return VSA2_OK;
 }
 
 int vsa2_route_coarse(const vsa2_problem* p, const void* pooled, float* scores, void* ws, size_t ws_bytes,

@@ -14,7 +14,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libvsa2.so")
 
-VSA2_OK, VSA2_E_ARG, VSA2_E_SHAPE, VSA2_E_WORKSPACE, VSA2_E_HIP, VSA2_E_UNSUPPORTED = range(6)
+VSA2_OK, VSA2_E_ARG, VSA2_E_SHAPE, VSA2_E_WORKSPACE, VSA2_E_HIP, VSA2_E_UNSUPPORTED, VSA2_E_SCRATCH = range(7)
 VSA2_F32, VSA2_BF16 = 0, 1
 OP_POOL, OP_ROUTE, OP_TOPK, OP_PLAN, OP_FWD, OP_BWD, OP_COARSE, OP_COARSE_BWD, OP_ROUTE_COARSE, OP_TOPK_ROW = range(10)
 K_FINE_FWD, K_BWD_DKDV, K_BWD_DQ, K_ROUTER_LSE, K_ROUTER_SCORES = range(5)
@@ -48,6 +48,8 @@ _SIGS = {
     "vsa2_budget": (ctypes.c_int, [_PP, _I32, ctypes.POINTER(ctypes.c_int64)]),
     "vsa2_pool": (ctypes.c_int, [_PP, _P, _P, _P, _P, _P]),
     "vsa2_route": (ctypes.c_int, [_PP, _P, _P, _P, _SZ, _P]),
+    "vsa2_route_noalloc": (ctypes.c_int, [_PP, _P, _P, _P]),
+    "vsa2_route_noalloc_limit": (ctypes.c_int, [ctypes.POINTER(_SZ)]),
     "vsa2_topk_per_seq": (ctypes.c_int, [_PP, _P, _I32, _P, _P, _P, _P, _P, _SZ, _P]),
     "vsa2_route_coarse": (ctypes.c_int, [_PP, _P, _P, _P, _SZ, _P]),
     "vsa2_topk_per_row": (ctypes.c_int, [_PP, _P, _I32, _P, _P, _P, _P, _P, _SZ, _P]),
@@ -142,6 +144,17 @@ def vsa2_pool(p, q, k, v, pooled, stream=None):
 def vsa2_route(p, pooled, scores, ws, stream=None):
     _check("vsa2_route", lib().vsa2_route(ctypes.byref(p), _ptr(pooled), _ptr(scores), _ptr(ws),
                                           0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def vsa2_route_noalloc(p, pooled, scores, stream=None):
+    _check("vsa2_route_noalloc", lib().vsa2_route_noalloc(ctypes.byref(p), _ptr(pooled), _ptr(scores),
+                                                          _stream(stream)))
+
+
+def route_noalloc_limit():
+    out = _SZ(0)
+    _check("vsa2_route_noalloc_limit", lib().vsa2_route_noalloc_limit(ctypes.byref(out)))
+    return out.value
 
 
 def vsa2_topk_per_seq(p, scores, topk, row_ptr, col_idx, col_ptr, row_idx, ws, stream=None):
