@@ -214,6 +214,8 @@ def main():
     ap.add_argument("--workload", default="train720")
     ap.add_argument("--topk", type=int, default=None, help="override the workload's average KV blocks per query block")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-sched", action="store_true",
+                    help="run the fine branch one workgroup per cube instead of on the work schedule's pairs")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain copy kernel of known size (for counter scaling)")
     args = ap.parse_args()
@@ -240,6 +242,7 @@ def main():
     names = ["pool", "route", "topk", "fine_fwd", "coarse_gate", "coarse_gate_bwd", "fine_bwd"]
 
     gr = layer.grads()      # allocated once, outside the timed region
+    sched = None if args.no_sched else layer.sched
     torch.cuda.synchronize()
 
     def step_full(ev=None):
@@ -256,12 +259,13 @@ def main():
         mark(2)
         if w.router == "vsa":
             vsa2.vsa2_topk_per_row(p, layer.scores, w.topk, layer.row_ptr, layer.col_idx, layer.col_ptr,
-                                   layer.row_idx, layer.ws)
+                                   layer.row_idx, layer.ws, sched=sched)
         else:
             vsa2.vsa2_topk_per_seq(p, layer.scores, w.topk, layer.row_ptr, layer.col_idx, layer.col_ptr,
-                                   layer.row_idx, layer.ws)
+                                   layer.row_idx, layer.ws, sched=sched)
         mark(3)
-        vsa2.vsa2_sparse_attn_fwd(p, w.topk, q, k, v, layer.row_ptr, layer.col_idx, layer.o_f, layer.lse, layer.ws)
+        vsa2.vsa2_sparse_attn_fwd(p, w.topk, q, k, v, layer.row_ptr, layer.col_idx, layer.o_f, layer.lse, layer.ws,
+                                  sched=sched)
         mark(4)
         vsa2.vsa2_coarse_gate(p, layer.pooled, x, w.d_model, w_g, layer.o_f, layer.o, layer.saved, layer.ws)
         mark(5)
@@ -272,7 +276,7 @@ def main():
         if w.train:
             vsa2.vsa2_sparse_attn_bwd(p, w.topk, q, k, v, layer.o_f, layer.lse, d_o, layer.row_ptr, layer.col_idx,
                                       layer.col_ptr, layer.row_idx, gr["dqkv_c"], gr["dq"], gr["dk"], gr["dv"],
-                                      layer.ws)
+                                      layer.ws, sched=sched)
         mark(7)
 
     log(f"warmup {args.warmup} steps")
@@ -399,7 +403,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": describe(w),
                    "global_batch": w.batch, "seq_len": w.L, "heads": w.heads, "head_dim": w.head_dim,
-                   "topk": w.topk, "parallelism": "single GPU"},
+                   "topk": w.topk, "parallelism": "single GPU",
+                   "fine_work": "per-cube workgroups" if sched is None else "work-schedule pairs"},
         "step_ms": step_dist,
         "cold_ms_per_step": round(float(np.median(cold)), 3),
         "step_flops": step_flops,

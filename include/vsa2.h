@@ -107,6 +107,29 @@ const char* vsa2_status_string(int status);
  * Pure host computation; enqueues nothing. */
 int vsa2_workspace_size(const vsa2_problem* p, int32_t op, int32_t topk, int32_t d_model, size_t* bytes);
 
+/* Bytes of the work schedule of the fine branch for budget `topk` (0 when the
+ * problem needs none).  The schedule answers the question the paper's
+ * per-sequence TopK (§2.2 Eq.(8)-(9)) leaves open: every query cube holds its
+ * own number of KV cubes (and every KV cube is selected by its own number of
+ * query cubes), and the blog's reproduction notes (its §12) leave the
+ * scheduler of these unequal lists to the implementer (its §10 counts the
+ * imbalance and the block-sparse memory traffic among the gap to the ideal
+ * speed-up).  For every (batch, head) it orders the query cubes (forward, dQ)
+ * and the KV cubes (dK/dV) by a min-hash of their lists, so cubes that gather
+ * the same tiles run next to each other on one XCD's L2; cuts the order into
+ * 8 ranges of equal work, one per XCD; and puts each range's long lists
+ * first.  The fine kernels then run as many workgroups as fit on the device,
+ * each taking cubes from its XCD's queue and then from the others, and give
+ * the same results, bit for bit, as with no schedule.
+ * Written by vsa2_topk_per_seq, vsa2_topk_per_row and vsa2_plan_from_csr from
+ * the selection they produce or receive, read by vsa2_sparse_attn_fwd/bwd.
+ * Built for 64-token blocks without text rows; with block_tokens = 128 (each
+ * workgroup already stages every tile for the block's two cubes) or
+ * text_tokens > 0 the size is 0 and the kernels run one workgroup per block.
+ * Layout (opaque to callers): for query cubes, then KV cubes, a 256-byte
+ * header and batch*heads*nb int32 items. */
+int vsa2_sched_size(const vsa2_problem* p, int32_t topk, size_t* bytes);
+
 /* Bytes of the `pooled` buffer written by vsa2_pool (see there). */
 int vsa2_pooled_size(const vsa2_problem* p, size_t* bytes);
 
@@ -148,10 +171,13 @@ int vsa2_route(const vsa2_problem* p, const void* pooled, float* scores,
  *     col_idx[row_ptr[i] .. row_ptr[i+1]), ascending.  row_ptr[nb] = k.
  *   col_ptr, row_idx (written): the same selection by KV cube (CSC), query
  *     cubes ascending; used by the backward pass.
+ *   sched (written): the work schedule of this selection, sched_bytes >=
+ *     vsa2_sched_size() and 256-byte aligned; NULL builds none (the fine
+ *     kernels then run one workgroup per cube).
  *   ws: vsa2_workspace_size(VSA2_OP_TOPK). */
 int vsa2_topk_per_seq(const vsa2_problem* p, const float* scores, int32_t topk,
                       int32_t* row_ptr, int32_t* col_idx, int32_t* col_ptr, int32_t* row_idx,
-                      void* ws, size_t ws_bytes, void* stream);
+                      void* sched, size_t sched_bytes, void* ws, size_t ws_bytes, void* stream);
 
 /* CSC form (col_ptr, row_idx) of a caller-chosen selection given as CSR
  * (row_ptr, col_idx, same layout as vsa2_topk_per_seq, exactly k entries per
@@ -161,9 +187,29 @@ int vsa2_topk_per_seq(const vsa2_problem* p, const float* scores, int32_t topk,
  * CSC slots at the end of the list are never read (col_ptr[nb] is then below
  * k), while the forward and the dQ pass, which read the CSR, take the KV
  * cube's keys twice into that row's softmax.
+ *   sched (written, or NULL): the work schedule, as for vsa2_topk_per_seq.
  *   ws: vsa2_workspace_size(VSA2_OP_PLAN). */
 int vsa2_plan_from_csr(const vsa2_problem* p, int32_t topk, const int32_t* row_ptr, const int32_t* col_idx,
-                       int32_t* col_ptr, int32_t* row_idx, void* ws, size_t ws_bytes, void* stream);
+                       int32_t* col_ptr, int32_t* row_idx, void* sched, size_t sched_bytes,
+                       void* ws, size_t ws_bytes, void* stream);
+
+/* vsa2_route for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same kernels and result as vsa2_route, with the router's scratch (the
+ * log-sum-exp of every pooled query and, on padded grids, one key-existence
+ * word per 64 pooled keys: vsa2_workspace_size(VSA2_OP_ROUTE) bytes) taken
+ * from a fixed array in device memory that the library holds on every GPU it
+ * runs on until the process ends, instead of a caller workspace.
+ *   The array holds vsa2_route_noalloc_limit() bytes (8 MiB; at 720p with 20
+ *   heads the router needs 2.2 MB): a larger problem returns VSA2_E_SCRATCH
+ *   before anything is enqueued.  The call allocates and frees nothing.
+ *   Every call on one GPU shares that GPU's array and leaves its scratch
+ *   there; calls that overlap on one GPU (two streams, two host threads)
+ *   race and must be ordered by the caller. */
+int vsa2_route_noalloc(const vsa2_problem* p, const void* pooled, float* scores, void* stream);
+
+/* Size in bytes of vsa2_route_noalloc's fixed device scratch. */
+int vsa2_route_noalloc_limit(size_t* bytes);
 
 /* vsa2_route for callers that cannot allocate device memory (code under HIP
  * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
@@ -197,21 +243,25 @@ int vsa2_route_coarse(const vsa2_problem* p, const void* pooled, float* scores,
  * budget of Eq.(8)-(9).  Same outputs, sizes and budget (vsa2_budget) as
  * vsa2_topk_per_seq; row_ptr[i] = i min(topk, nb).
  *   scores: fp32 [batch, heads, nb, nb], finite and >= 0.
+ *   sched (written, or NULL): the work schedule, as for vsa2_topk_per_seq.
  *   ws: vsa2_workspace_size(VSA2_OP_TOPK_ROW). */
 int vsa2_topk_per_row(const vsa2_problem* p, const float* scores, int32_t topk, int32_t* row_ptr,
-                      int32_t* col_idx, int32_t* col_ptr, int32_t* row_idx, void* ws, size_t ws_bytes,
-                      void* stream);
+                      int32_t* col_idx, int32_t* col_ptr, int32_t* row_idx, void* sched, size_t sched_bytes,
+                      void* ws, size_t ws_bytes, void* stream);
 
 /* Fine branch forward, Eq.(12): block-sparse attention of every query cube
  * over its selected KV cubes only (-inf mask elsewhere, §2.1).
  *   row_ptr, col_idx: the selection (CSR as above, k = vsa2_budget(topk)).
+ *   sched: the schedule the call that produced this selection wrote, or NULL
+ *     (one workgroup per query cube, results equal).
  *   o_f (written): storage dtype [batch, heads, L, d].
  *   lse (written): fp32 [batch, heads, L], natural-log log-sum-exp of the scaled
  *     scores of each query over its selected keys (kept for the backward).
  *   A query cube with no selected KV cube gets o_f = 0 and lse = -inf.
- *   ws: vsa2_workspace_size(VSA2_OP_FWD), currently 0 bytes (ws may be NULL). */
+ *   ws: vsa2_workspace_size(VSA2_OP_FWD): 256 bytes (the schedule's queue
+ *     counters) when the problem has a schedule, else 0 (ws may be NULL). */
 int vsa2_sparse_attn_fwd(const vsa2_problem* p, int32_t topk, const void* q, const void* k, const void* v,
-                         const int32_t* row_ptr, const int32_t* col_idx, void* o_f, float* lse,
+                         const int32_t* row_ptr, const int32_t* col_idx, const void* sched, void* o_f, float* lse,
                          void* ws, size_t ws_bytes, void* stream);
 
 /* Fine branch backward with the selection held fixed (the router takes no
@@ -220,6 +270,8 @@ int vsa2_sparse_attn_fwd(const vsa2_problem* p, int32_t topk, const void* q, con
  *   q, k, v, o_f, lse: as in / out of vsa2_sparse_attn_fwd; d_o = dL/dO (the
  *     gate adds O_f with weight one, Eq.(14), so dL/dO_f = dL/dO).
  *   row_ptr, col_idx, col_ptr, row_idx: the selection in CSR and CSC form.
+ *   sched: the selection's schedule or NULL (one workgroup per cube); the
+ *     results are the same bit for bit.
  *   dqkv_c: fp32 [3, batch, heads, nb, d] gradients w.r.t. the pooled Q_c, K_c,
  *     V_c (from vsa2_coarse_gate_bwd) or NULL; each token of cube c receives
  *     1/64 of row c (the adjoint of the mean pooling).
@@ -230,8 +282,9 @@ int vsa2_sparse_attn_fwd(const vsa2_problem* p, int32_t topk, const void* q, con
 int vsa2_sparse_attn_bwd(const vsa2_problem* p, int32_t topk, const void* q, const void* k, const void* v,
                          const void* o_f, const float* lse, const void* d_o,
                          const int32_t* row_ptr, const int32_t* col_idx,
-                         const int32_t* col_ptr, const int32_t* row_idx, const float* dqkv_c,
-                         void* dq, void* dk, void* dv, void* ws, size_t ws_bytes, void* stream);
+                         const int32_t* col_ptr, const int32_t* row_idx, const void* sched,
+                         const float* dqkv_c, void* dq, void* dk, void* dv, void* ws, size_t ws_bytes,
+                         void* stream);
 
 /* Coarse branch, Eq.(1)-(4), and gated merge, Eq.(13)-(14).
  *   pooled: from vsa2_pool.  x: storage dtype [batch, L, d_model] hidden states

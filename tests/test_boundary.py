@@ -61,7 +61,8 @@ def test_sizes_and_budget():
     assert vsa2.pooled_size(p) == 2 * (2 * (L // 8) + 3 * nbp) * 64 * 4
     assert vsa2.saved_size(p) == (2 * nb * 64 + 2 * nb + 2 * L) * 4
     assert vsa2.workspace_size(p, vsa2.OP_ROUTE) >= 2 * (L // 8) * 4
-    assert vsa2.workspace_size(p, vsa2.OP_FWD) == 0                       # forward needs no scratch
+    assert vsa2.workspace_size(p, vsa2.OP_FWD) == 256                     # the schedule's 8 queue counters
+    assert vsa2.workspace_size(_prob(block=128, grid=(8, 16, 32)), vsa2.OP_FWD) == 0   # no schedule, no scratch
     assert vsa2.workspace_size(p, vsa2.OP_COARSE_BWD, 8, 128) > 0
 
 
@@ -135,13 +136,13 @@ def test_workspace_checks():
     assert L.vsa2_route(ctypes.byref(p), A, B, None, need, None) == vsa2.VSA2_E_WORKSPACE
     assert L.vsa2_route(ctypes.byref(p), A, B, C + 16, need, None) == vsa2.VSA2_E_ARG   # ws not 256-aligned
     need = vsa2.workspace_size(p, vsa2.OP_TOPK)
-    assert L.vsa2_topk_per_seq(ctypes.byref(p), A, 8, B, C, D, A, B, need - 256, None) == vsa2.VSA2_E_WORKSPACE
+    assert L.vsa2_topk_per_seq(ctypes.byref(p), A, 8, B, C, D, A, None, 0, B, need - 256, None) == vsa2.VSA2_E_WORKSPACE
 
 
 def test_scalar_arguments():
     L, p = vsa2.lib(), _prob()
-    assert L.vsa2_topk_per_seq(ctypes.byref(p), A, 0, B, C, D, A, B, 1 << 30, None) == vsa2.VSA2_E_ARG
-    assert L.vsa2_sparse_attn_fwd(ctypes.byref(p), 0, A, B, C, D, A, B, C, None, 0, None) == vsa2.VSA2_E_ARG
+    assert L.vsa2_topk_per_seq(ctypes.byref(p), A, 0, B, C, D, A, None, 0, B, 1 << 30, None) == vsa2.VSA2_E_ARG
+    assert L.vsa2_sparse_attn_fwd(ctypes.byref(p), 0, A, B, C, D, A, None, B, C, None, 0, None) == vsa2.VSA2_E_ARG
     assert L.vsa2_coarse_gate(ctypes.byref(p), A, B, 100, C, D, A, B, C, 1 << 30, None) == vsa2.VSA2_E_SHAPE
     many = _prob(heads=65)
     assert L.vsa2_coarse_gate(ctypes.byref(many), A, B, 128, C, D, A, B, C, 1 << 30, None) == vsa2.VSA2_E_UNSUPPORTED
@@ -156,3 +157,23 @@ def test_kernel_timer_arguments():
     # armed but never launched: stopping reads no event and reports nothing timed
     assert lib.vsa2_kernel_timer_start(vsa2.K_BWD_DKDV, 4) == vsa2.VSA2_OK
     assert vsa2.kernel_timer_stop(vsa2.K_BWD_DKDV) == (0.0, 0)
+
+
+def test_schedule_size_and_checks():
+    L = vsa2.lib()
+    # 64-token blocks without text rows: for the query cubes and for the KV
+    # cubes, a 256-byte queue header and one int32 item per (head, cube)
+    p = _prob(heads=2, grid=(4, 12, 20))                  # nb = 15
+    up = lambda x: (x + 255) // 256 * 256
+    assert vsa2.sched_size(p, 5) == 2 * (256 + up(2 * 15 * 4))
+    # 128-token blocks and text rows need none
+    assert vsa2.sched_size(_prob(block=128, grid=(8, 16, 32)), 4) == 0
+    txt = vsa2.problem(1, 2, 64, (8, 16, 16), "f32", text=100)
+    assert vsa2.sched_size(txt, 4) == 0
+    need = vsa2.workspace_size(p, vsa2.OP_TOPK)
+    ss = vsa2.sched_size(p, 5)
+    # a schedule buffer that is too small or misaligned is refused before anything runs
+    assert L.vsa2_topk_per_seq(ctypes.byref(p), A, 5, B, C, D, A, B, ss - 1, C, need, None) == vsa2.VSA2_E_WORKSPACE
+    assert L.vsa2_topk_per_seq(ctypes.byref(p), A, 5, B, C, D, A, B + 16, ss, C, need, None) == vsa2.VSA2_E_ARG
+    assert L.vsa2_plan_from_csr(ctypes.byref(p), 5, A, B, C, D, B + 16, ss, C, 1 << 30, None) == vsa2.VSA2_E_ARG
+    assert L.vsa2_sparse_attn_fwd(ctypes.byref(p), 5, A, B, C, D, A, B + 16, C, D, None, 0, None) == vsa2.VSA2_E_ARG

@@ -1,0 +1,192 @@
+"""The work schedule of the fine branch on the GPU.
+
+For each (batch, head) the schedule orders the cubes by a min-hash of their
+lists (query cubes by their CSR rows for the forward and dQ, KV cubes by their
+CSC columns for dK/dV), cuts the order into 8 contiguous ranges of equal work,
+one per XCD, puts the long lists of each range first, and appends the range
+to that XCD's queue.  Checked here:
+  * the queues against a recomputation from the CSR / CSC the schedule was
+    built from: the min-hash keys, the (key, id) order, the equal-work cut,
+    the long-first order inside each range and the queue layout, item for
+    item; every cube appears exactly once;
+  * that the fine branch run through the schedule gives the per-cube launch's
+    results bit for bit (an item is computed the same way whoever takes it)
+    and the oracle's;
+  * that building it and running through it is bitwise reproducible;
+  * odd cube counts, empty lists and padded grids.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import gpu_util as gu
+from oracle import vsa2_oracle as orc
+from video_dit_trainable_amd import vsa2
+from video_dit_trainable_amd.configs import WORKLOADS, Workload
+from video_dit_trainable_amd.inputs import make_grad_out, make_qkv, make_selection
+
+pytestmark = pytest.mark.gpu
+
+MID = Workload("mid", 12, (8, 16, 32), 1, 4, 128, "bf16", 8, "lowrank", train=True)          # nb = 64
+ODD = Workload("odd", 14, (4, 12, 20), 1, 2, 128, "f32", 5, "lowrank", skew=True, train=True)  # nb = 15
+PAD = Workload("pad", 18, (7, 15, 30), 1, 3, 64, "bf16", 6, "lowrank", skew=True, train=True)  # padded, nb = 64
+SHORT = WORKLOADS["short"]                                                                    # nb = 512, 20 heads
+CASES = [MID, ODD, PAD]
+OVH = 4   # the schedule's fixed cost of an item, in list entries
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    vsa2.lib()
+
+
+def _dev():
+    return torch.device("cuda:0")
+
+
+def _up(x):
+    return (x + 255) // 256 * 256
+
+
+def decode(layer):
+    """The schedule buffer as numpy: per side (query cubes, KV cubes) the
+    header (queue starts [8], queue lengths [8]) and the item array."""
+    n_items = layer.bh * layer.nb
+    raw = layer.sched.cpu().numpy()
+    side = 256 + _up(n_items * 4)
+    assert layer.sched.numel() >= 2 * side
+    out = []
+    for off in (0, side):
+        hdr = raw[off:off + 64].view(np.int32)
+        items = raw[off + 256:off + 256 + n_items * 4].view(np.int32)
+        out.append((hdr[:8].copy(), hdr[8:16].copy(), items.copy()))
+    return out
+
+
+def _mh1(j):
+    return (j * 40503 + 12345) & 0xFFFF
+
+
+def _mh2(j):
+    return ((j ^ 0x5A5A) * 52429 + 777) & 0xFFFF
+
+
+def expected_queues(ptr, idx, nb):
+    """The queues, recomputed from the lists of every head (ptr [bh, nb+1],
+    idx [bh, k]) by the rules the schedule states."""
+    queues = [[] for _ in range(8)]
+    for h in range(ptr.shape[0]):
+        lists = [idx[h, ptr[h, c]:ptr[h, c + 1]] for c in range(nb)]
+        keys = [((int(min(_mh1(l))) << 16) | int(min(_mh2(l)))) if len(l) else 0xFFFFFFFF for l in lists]
+        order = sorted(range(nb), key=lambda c: (keys[c], c))
+        w = np.array([len(lists[c]) + OVH for c in order], dtype=np.int64)
+        before = np.concatenate([[0], np.cumsum(w)[:-1]])
+        xcd = np.minimum(7, (8 * (2 * before + w)) // (2 * w.sum()))
+        cls = [int(np.floor(np.log2(len(lists[c]) + 1))) for c in order]
+        for x in range(8):
+            pos = [p for p in range(nb) if xcd[p] == x]
+            pos.sort(key=lambda p: (-cls[p], p))
+            queues[x] += [h * nb + order[p] for p in pos]
+    return queues
+
+
+def check_side(hdr_start, hdr_len, items, ptr, idx, nb):
+    want = expected_queues(ptr, idx, nb)
+    assert list(hdr_len) == [len(q) for q in want]
+    assert list(hdr_start) == list(np.concatenate([[0], np.cumsum(hdr_len)[:-1]]))
+    for x in range(8):
+        got = items[hdr_start[x]:hdr_start[x] + hdr_len[x]]
+        assert got.tolist() == want[x], f"queue {x} differs"
+    assert sorted(items.tolist()) == list(range(ptr.shape[0] * nb)), "every cube exactly once"
+
+
+def _layer(w, dev):
+    p = vsa2.problem(w.batch, w.heads, w.head_dim, w.grid, w.dtype)
+    layer = vsa2.Layer(p, w.topk, w.d_model, device=dev)
+    assert layer.sched is not None
+    return p, layer
+
+
+@pytest.mark.parametrize("w", CASES + [SHORT], ids=lambda w: w.name)
+def test_schedule_queues_from_router_selection(w):
+    dev = _dev()
+    q, k, v = make_qkv(w, device=dev)
+    p, layer = _layer(w, dev)
+    vsa2.vsa2_pool(p, q, k, v, layer.pooled)
+    vsa2.vsa2_route(p, layer.pooled, layer.scores, layer.ws)
+    layer.sched.zero_()      # padding between the parts is never written: start both builds from zero
+    vsa2.vsa2_topk_per_seq(p, layer.scores, w.topk, layer.row_ptr, layer.col_idx, layer.col_ptr, layer.row_idx,
+                           layer.ws, sched=layer.sched)
+    torch.cuda.synchronize()
+    first = layer.sched.clone()
+    (rs, rl, ri), (cs, cl, cidx) = decode(layer)
+    rp, ci, cp, rix = (t[0].cpu().numpy() for t in (layer.row_ptr, layer.col_idx, layer.col_ptr, layer.row_idx))
+    check_side(rs, rl, ri, rp, ci, w.nb)
+    check_side(cs, cl, cidx, cp, rix, w.nb)
+    # the same selection gives the same schedule (built again through the CSR)
+    layer.sched.zero_()
+    vsa2.vsa2_plan_from_csr(p, w.topk, layer.row_ptr, layer.col_idx, layer.col_ptr, layer.row_idx, layer.ws,
+                            sched=layer.sched)
+    torch.cuda.synchronize()
+    assert torch.equal(layer.sched, first)
+
+
+@pytest.mark.parametrize("w", CASES, ids=lambda w: w.name)
+def test_scheduled_fine_branch_matches_per_cube_and_oracle(w):
+    dev = _dev()
+    q, k, v = make_qkv(w, device=dev)
+    d_o = make_grad_out(w, device=dev)
+    p, layer = _layer(w, dev)
+    rp, ci = make_selection(w, device=dev)     # heavy-tailed rows, some empty
+    layer.set_selection(rp, ci)
+    args = (layer.row_ptr, layer.col_idx)
+    lists = (layer.row_ptr, layer.col_idx, layer.col_ptr, layer.row_idx)
+    out = {}
+    for mode, sched in (("per-cube", None), ("scheduled", layer.sched)):
+        o_f, lse = torch.empty_like(layer.o_f), torch.empty_like(layer.lse)
+        vsa2.vsa2_sparse_attn_fwd(p, w.topk, q, k, v, *args, o_f, lse, layer.ws, sched=sched)
+        g = [torch.full_like(q, float("nan")) for _ in range(3)]
+        vsa2.vsa2_sparse_attn_bwd(p, w.topk, q, k, v, o_f, lse, d_o, *lists, None, *g, layer.ws, sched=sched)
+        torch.cuda.synchronize()
+        out[mode] = (o_f, lse, g)
+    (o1, l1, g1), (o2, l2, g2) = out["per-cube"], out["scheduled"]
+    assert torch.equal(o1, o2) and torch.equal(l1, l2), "the scheduled forward differs from the per-cube one"
+    for name, a, b in zip(("dQ", "dK", "dV"), g1, g2):
+        assert torch.equal(a, b), f"{name}: the scheduled backward differs from the per-cube one"
+    real = orc.token_valid(w.grid)
+    for h in range(w.heads):
+        mask = orc.csr_to_mask(rp[0, h].cpu().numpy(), ci[0, h].cpu().numpy(), w.nb)
+        qh, kh, vh, dh = (gu.f64(t[0, h]) for t in (q, k, v, d_o))
+        o, lse = orc.fine_forward(qh, kh, vh, mask, valid=real)
+        if w.dtype == "f32":
+            gu.assert_close_f32(gu.f64(o2[0, h]), o, f"O_f head {h}")
+        else:
+            gu.assert_close_bf16(gu.f64(o2[0, h]), o, f"O_f head {h}")
+        dq, dk, dv = orc.fine_backward(qh, kh, vh, mask, dh, valid=real)
+        for name, got, want in zip(("dQ", "dK", "dV"), g2, (dq, dk, dv)):
+            rr = gu.rel_l2(gu.f64(got[0, h]), want)
+            assert rr <= (1e-4 if w.dtype == "f32" else 2e-2), f"{name} head {h}: rel-L2 {rr:.3g}"
+
+
+def test_scheduled_backward_is_deterministic():
+    w = MID
+    dev = _dev()
+    q, k, v = make_qkv(w, device=dev)
+    d_o = make_grad_out(w, device=dev)
+    p, layer = _layer(w, dev)
+    layer.set_selection(*make_selection(w, device=dev))
+    lists = (layer.row_ptr, layer.col_idx, layer.col_ptr, layer.row_idx)
+    vsa2.vsa2_sparse_attn_fwd(p, w.topk, q, k, v, layer.row_ptr, layer.col_idx, layer.o_f, layer.lse, layer.ws,
+                              sched=layer.sched)
+    runs = []
+    for _ in range(2):
+        g = [torch.empty_like(q) for _ in range(3)]
+        vsa2.vsa2_sparse_attn_bwd(p, w.topk, q, k, v, layer.o_f, layer.lse, d_o, *lists, None, *g, layer.ws,
+                                  sched=layer.sched)
+        torch.cuda.synchronize()
+        runs.append(g)
+    for a, b in zip(*runs):
+        assert torch.equal(a, b)

@@ -14,7 +14,7 @@ OUT = os.path.join(HERE, "libvsa2.so")
 BUILD = os.path.join(HERE, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["api.hip", "pool.hip", "router.hip", "topk.hip", "attn_fwd.hip", "attn_bwd.hip", "gate.hip"]
+SOURCES = ["api.hip", "pool.hip", "router.hip", "topk.hip", "sched.hip", "attn_fwd.hip", "attn_bwd.hip", "gate.hip"]
 
 FLAGS = [
     "--offload-arch=gfx950",

@@ -13,6 +13,7 @@ using namespace vsa2;
 namespace {
 
 constexpr size_t ALIGN = 256;
+constexpr int MAX_DEVICES_GRID = 64;
 
 size_t up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
 
@@ -112,8 +113,22 @@ size_t ws_topk(const Dims& d, TopkWs* w, void* base) {
   const size_t o_take = take((size_t)d.bh * d.nb * 4);
   const size_t o_col = take((size_t)d.bh * d.nb * 4);
   const size_t o_bm = take((size_t)d.bh * d.nb * bitmap_words(d) * 4);
+  const size_t o_sk = take((size_t)d.bh * d.nb * 4);
+  const size_t o_so = take((size_t)d.bh * d.nb * 4);
+  const size_t o_st = take((size_t)d.bh * d.nb * 4);
+  const size_t o_sc = take((size_t)d.bh * 8 * 4);
+  const size_t o_sh = take((size_t)d.bh * 8 * 4);
+  const size_t o_sp = take((size_t)d.bh * d.nb);
+  const size_t o_sr = take((size_t)d.bh * 9 * 4);
   if (w) {
     char* b = (char*)base;
+    w->spx = (uint8_t*)(b + o_sp);
+    w->srng = (int32_t*)(b + o_sr);
+    w->skeys = (uint32_t*)(b + o_sk);
+    w->sorder = (int32_t*)(b + o_so);
+    w->stmp = (int32_t*)(b + o_st);
+    w->scnt = (int32_t*)(b + o_sc);
+    w->shoff = (int32_t*)(b + o_sh);
     w->hist = (uint32_t*)(b + o_hist);
     w->state = (uint32_t*)(b + o_state);
     w->rowcnt = (uint32_t*)(b + o_row);
@@ -128,19 +143,81 @@ size_t ws_topk(const Dims& d, TopkWs* w, void* base) {
 size_t ws_plan(const Dims& d, TopkWs* w, void* base) {
   const size_t o_col = 0;
   const size_t o_bm = up((size_t)d.bh * d.nb * 4);
+  const size_t o_sk = o_bm + up((size_t)d.bh * d.nb * bitmap_words(d) * 4);
+  const size_t o_so = o_sk + up((size_t)d.bh * d.nb * 4);
+  const size_t o_st = o_so + up((size_t)d.bh * d.nb * 4);
+  const size_t o_sc = o_st + up((size_t)d.bh * d.nb * 4);
+  const size_t o_sh = o_sc + up((size_t)d.bh * 8 * 4);
+  const size_t o_sp = o_sh + up((size_t)d.bh * 8 * 4);
+  const size_t o_sr = o_sp + up((size_t)d.bh * d.nb);
   if (w) {
     char* b = (char*)base;
     *w = TopkWs{};
     w->colcnt = (uint32_t*)(b + o_col);
     w->bitmap = (uint32_t*)(b + o_bm);
     w->words = bitmap_words(d);
+    w->skeys = (uint32_t*)(b + o_sk);
+    w->sorder = (int32_t*)(b + o_so);
+    w->stmp = (int32_t*)(b + o_st);
+    w->scnt = (int32_t*)(b + o_sc);
+    w->shoff = (int32_t*)(b + o_sh);
+    w->spx = (uint8_t*)(b + o_sp);
+    w->srng = (int32_t*)(b + o_sr);
   }
-  return o_bm + up((size_t)d.bh * d.nb * bitmap_words(d) * 4);
+  return o_sr + up((size_t)d.bh * 9 * 4);
 }
 
-size_t ws_bwd(const Dims& d) { return up((size_t)d.bh * d.ld * 8); }     // (lse2, delta) per token row
+// The fine branch's work schedule (sched.hip): built for 64-token blocks
+// without text rows, where the fine kernels run one cube per work item; other
+// problems need none.  Layout: for the query cubes, then for the KV cubes, a
+// header of 16 int32 (queue starts and lengths, 256 bytes) and the items
+// [bh * nb] int32.
+bool sched_on(const Dims& d) { return d.bs == 0 && d.ntc == 0; }
+struct SchedPtrs {
+  int32_t *rh, *ri, *ch, *ci;
+};
+size_t sched_layout(const Dims& d, int64_t k, const void* base, SchedPtrs* sp) {
+  (void)k;
+  if (!sched_on(d)) return 0;
+  const size_t side = ALIGN + up((size_t)d.bh * d.nb * 4);
+  if (sp) {
+    char* b = (char*)base;
+    sp->rh = (int32_t*)b;
+    sp->ri = (int32_t*)(b + ALIGN);
+    sp->ch = (int32_t*)(b + side);
+    sp->ci = (int32_t*)(b + side + ALIGN);
+  }
+  return 2 * side;
+}
+size_t ws_fwd(const Dims& d) { return sched_on(d) ? ALIGN : 0; }
 
-size_t ws_fwd(const Dims&) { return 0; }  // the forward needs no scratch
+// Checks a caller's schedule buffer: NULL is allowed (no schedule: one
+// workgroup per cube in the natural order); otherwise aligned and, when its
+// size is known, large enough.
+int check_sched(const Dims& d, int64_t k, const void* sched, const size_t* bytes) {
+  const size_t need = sched_layout(d, k, nullptr, nullptr);
+  if (!sched || need == 0) return VSA2_OK;
+  if ((uintptr_t)sched % ALIGN) return VSA2_E_ARG;
+  if (bytes && *bytes < need) return VSA2_E_WORKSPACE;
+  return VSA2_OK;
+}
+// Builds the schedule into `sched` (when there is one) from the selection's
+// CSR and CSC.
+hipError_t build_sched(const Dims& d, int64_t k, const TopkArgs& a, void* sched, hipStream_t st) {
+  if (!sched || !sched_on(d)) return hipSuccess;
+  SchedPtrs sp;
+  sched_layout(d, k, sched, &sp);
+  SchedArgs s{a.row_ptr, a.col_idx, a.col_ptr, a.row_idx, sp.rh, sp.ri, sp.ch, sp.ci, a.ws.skeys, a.ws.sorder,
+              a.ws.stmp, a.ws.scnt, a.ws.shoff, a.ws.spx, a.ws.srng, d.bh, d.nb, k};
+  return launch_sched(s, st);
+}
+
+// (lse2, delta) per token row, then the schedule's queue counters (8 for the
+// dQ pass, 8 for the dK/dV pass)
+size_t ws_bwd_stats(const Dims& d) { return up((size_t)d.bh * d.ld * 8); }
+size_t ws_bwd(const Dims& d) { return ws_bwd_stats(d) + ALIGN; }
+
+size_t ws_fwd(const Dims& d);  // the schedule's 8 queue counters (below)
 
 
 int pad16(int x) { return (x + 15) / 16 * 16; }
@@ -220,6 +297,29 @@ KernelTimer g_timer[VSA2_K_COUNT];
 }  // namespace
 
 namespace vsa2 {
+int resident_grid(const void* fn, int threads, int items) {
+  static std::mutex mu;
+  static int cus[MAX_DEVICES_GRID] = {};
+  int dev = 0;
+  (void)hipGetDevice(&dev);
+  int n_cu = 0;
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    if (dev >= 0 && dev < MAX_DEVICES_GRID) {
+      if (!cus[dev]) (void)hipDeviceGetAttribute(&cus[dev], hipDeviceAttributeMultiprocessorCount, dev);
+      n_cu = cus[dev];
+    }
+  }
+  int per = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, fn, threads, 0) != hipSuccess || per < 1) per = 1;
+  if (n_cu < 1) n_cu = 8;
+  long g = (long)n_cu * per;
+  const long cap = ((long)items + 7) / 8 * 8;
+  if (g > cap) g = cap;
+  g = (g + 7) / 8 * 8;
+  return (int)(g < 8 ? 8 : g);
+}
+
 void timer_before(int kid, hipStream_t st) {
   KernelTimer& t = g_timer[kid];
   if (!t.armed || t.used >= t.capacity) return;
@@ -320,6 +420,15 @@ int vsa2_budget(const vsa2_problem* p, int32_t topk, int64_t* k) {
   if (s) return s;
   if (!k || topk < 1) return VSA2_E_ARG;
   *k = budget(d, topk);
+  return VSA2_OK;
+}
+
+int vsa2_sched_size(const vsa2_problem* p, int32_t topk, size_t* bytes) {
+  Dims d;
+  int s = check_problem(p, d);
+  if (s) return s;
+  if (!bytes || topk < 1) return VSA2_E_ARG;
+  *bytes = sched_layout(d, budget(d, topk), nullptr, nullptr);
   return VSA2_OK;
 }
 
@@ -429,14 +538,15 @@ int vsa2_route_coarse(const vsa2_problem* p, const void* pooled, float* scores, 
 }
 
 int vsa2_topk_per_row(const vsa2_problem* p, const float* scores, int32_t topk, int32_t* row_ptr,
-                      int32_t* col_idx, int32_t* col_ptr, int32_t* row_idx, void* ws, size_t ws_bytes,
-                      void* stream) {
+                      int32_t* col_idx, int32_t* col_ptr, int32_t* row_idx, void* sched, size_t sched_bytes,
+                      void* ws, size_t ws_bytes, void* stream) {
   Dims d;
   int s = check_problem(p, d);
   if (s) return s;
   if (topk < 1) return VSA2_E_ARG;
   if (!aligned(scores) || !aligned(row_ptr) || !aligned(col_idx) || !aligned(col_ptr) || !aligned(row_idx))
     return VSA2_E_ARG;
+  if ((s = check_sched(d, budget(d, topk), sched, &sched_bytes))) return s;
   if ((s = check_ws(ws, ws_bytes, ws_plan(d, nullptr, nullptr)))) return s;
   TopkArgs a{};
   a.scores = scores;
@@ -448,17 +558,21 @@ int vsa2_topk_per_row(const vsa2_problem* p, const float* scores, int32_t topk, 
   a.nb = d.nb;
   a.k = budget(d, topk);  // nb min(topk, nb)
   ws_plan(d, &a.ws, ws);
-  return hip_status(launch_topk_rows(a, (hipStream_t)stream));
+  hipError_t e = launch_topk_rows(a, (hipStream_t)stream);
+  if (e == hipSuccess) e = build_sched(d, a.k, a, sched, (hipStream_t)stream);
+  return hip_status(e);
 }
 
 int vsa2_topk_per_seq(const vsa2_problem* p, const float* scores, int32_t topk, int32_t* row_ptr, int32_t* col_idx,
-                      int32_t* col_ptr, int32_t* row_idx, void* ws, size_t ws_bytes, void* stream) {
+                      int32_t* col_ptr, int32_t* row_idx, void* sched, size_t sched_bytes, void* ws,
+                      size_t ws_bytes, void* stream) {
   Dims d;
   int s = check_problem(p, d);
   if (s) return s;
   if (topk < 1) return VSA2_E_ARG;
   if (!aligned(scores) || !aligned(row_ptr) || !aligned(col_idx) || !aligned(col_ptr) || !aligned(row_idx))
     return VSA2_E_ARG;
+  if ((s = check_sched(d, budget(d, topk), sched, &sched_bytes))) return s;
   if ((s = check_ws(ws, ws_bytes, ws_topk(d, nullptr, nullptr)))) return s;
   TopkArgs a{};
   a.scores = scores;
@@ -470,16 +584,20 @@ int vsa2_topk_per_seq(const vsa2_problem* p, const float* scores, int32_t topk, 
   a.nb = d.nb;
   a.k = budget(d, topk);
   ws_topk(d, &a.ws, ws);
-  return hip_status(launch_topk(a, (hipStream_t)stream));
+  hipError_t e = launch_topk(a, (hipStream_t)stream);
+  if (e == hipSuccess) e = build_sched(d, a.k, a, sched, (hipStream_t)stream);
+  return hip_status(e);
 }
 
 int vsa2_plan_from_csr(const vsa2_problem* p, int32_t topk, const int32_t* row_ptr, const int32_t* col_idx,
-                       int32_t* col_ptr, int32_t* row_idx, void* ws, size_t ws_bytes, void* stream) {
+                       int32_t* col_ptr, int32_t* row_idx, void* sched, size_t sched_bytes, void* ws,
+                       size_t ws_bytes, void* stream) {
   Dims d;
   int s = check_problem(p, d);
   if (s) return s;
   if (topk < 1) return VSA2_E_ARG;
   if (!aligned(row_ptr) || !aligned(col_idx) || !aligned(col_ptr) || !aligned(row_idx)) return VSA2_E_ARG;
+  if ((s = check_sched(d, budget(d, topk), sched, &sched_bytes))) return s;
   if ((s = check_ws(ws, ws_bytes, ws_plan(d, nullptr, nullptr)))) return s;
   TopkArgs a{};
   a.row_ptr = const_cast<int32_t*>(row_ptr);
@@ -490,12 +608,14 @@ int vsa2_plan_from_csr(const vsa2_problem* p, int32_t topk, const int32_t* row_p
   a.nb = d.nb;
   a.k = budget(d, topk);
   ws_plan(d, &a.ws, ws);
-  return hip_status(launch_plan(a, (hipStream_t)stream));
+  hipError_t e = launch_plan(a, (hipStream_t)stream);
+  if (e == hipSuccess) e = build_sched(d, a.k, a, sched, (hipStream_t)stream);
+  return hip_status(e);
 }
 
 int vsa2_sparse_attn_fwd(const vsa2_problem* p, int32_t topk, const void* q, const void* k, const void* v,
-                         const int32_t* row_ptr, const int32_t* col_idx, void* o_f, float* lse, void* ws,
-                         size_t ws_bytes, void* stream) {
+                         const int32_t* row_ptr, const int32_t* col_idx, const void* sched, void* o_f, float* lse,
+                         void* ws, size_t ws_bytes, void* stream) {
   Dims d;
   int s = check_problem(p, d);
   if (s) return s;
@@ -503,8 +623,16 @@ int vsa2_sparse_attn_fwd(const vsa2_problem* p, int32_t topk, const void* q, con
   if (!aligned(q) || !aligned(k) || !aligned(v) || !aligned(row_ptr) || !aligned(col_idx) || !aligned(o_f) ||
       !aligned(lse))
     return VSA2_E_ARG;
+  if ((s = check_sched(d, budget(d, topk), sched, nullptr))) return s;
   if ((s = check_ws(ws, ws_bytes, ws_fwd(d)))) return s;
   AttnArgs a{};
+  if (sched && sched_on(d)) {
+    SchedPtrs sp;
+    sched_layout(d, budget(d, topk), sched, &sp);
+    a.sq_hdr = sp.rh;
+    a.sq_items = sp.ri;
+    a.sq_ctr = (int32_t*)ws;
+  }
   a.q = q; a.k = k; a.v = v;
   a.row_ptr = row_ptr; a.col_idx = col_idx;
   a.o = o_f; a.lse = lse;
@@ -521,8 +649,9 @@ int vsa2_sparse_attn_fwd(const vsa2_problem* p, int32_t topk, const void* q, con
 
 int vsa2_sparse_attn_bwd(const vsa2_problem* p, int32_t topk, const void* q, const void* k, const void* v,
                          const void* o_f, const float* lse, const void* d_o, const int32_t* row_ptr,
-                         const int32_t* col_idx, const int32_t* col_ptr, const int32_t* row_idx, const float* dqkv_c,
-                         void* dq, void* dk, void* dv, void* ws, size_t ws_bytes, void* stream) {
+                         const int32_t* col_idx, const int32_t* col_ptr, const int32_t* row_idx, const void* sched,
+                         const float* dqkv_c, void* dq, void* dk, void* dv, void* ws, size_t ws_bytes,
+                         void* stream) {
   Dims d;
   int s = check_problem(p, d);
   if (s) return s;
@@ -532,9 +661,19 @@ int vsa2_sparse_attn_bwd(const vsa2_problem* p, int32_t topk, const void* q, con
       !aligned(dk) || !aligned(dv))
     return VSA2_E_ARG;
   if (dqkv_c && !aligned(dqkv_c)) return VSA2_E_ARG;
+  if ((s = check_sched(d, budget(d, topk), sched, nullptr))) return s;
   if ((s = check_ws(ws, ws_bytes, ws_bwd(d)))) return s;
   const hipStream_t st = (hipStream_t)stream;
   AttnBwdArgs a{};
+  if (sched && sched_on(d)) {
+    SchedPtrs sp;
+    sched_layout(d, budget(d, topk), sched, &sp);
+    a.sq_hdr = sp.rh;
+    a.sq_items = sp.ri;
+    a.sk_hdr = sp.ch;
+    a.sk_items = sp.ci;
+    a.sq_ctr = (int32_t*)((char*)ws + ws_bwd_stats(d));
+  }
   a.q = q; a.k = k; a.v = v; a.o = o_f; a.d_o = d_o;
   a.lse = lse;
   a.stats_out = (float*)ws;

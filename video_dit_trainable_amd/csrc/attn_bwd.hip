@@ -140,7 +140,11 @@ __device__ __forceinline__ void dkdv_pair(const T* qs, const T* dos, const float
 // 0, 1 the first cube, 2, 3 the second), which share the block's list; each
 // wave runs both query halves of every staged Q / dO tile itself, so the
 // tiles are staged once for 128 keys and no query-half reduction is needed.
-template <typename T, typename TO, int D, bool DENSE, bool PAD, int BS, bool TEXT, int QB = 1>
+// SCHED (64-token blocks): the grid holds as many workgroups as fit on the
+// device; each takes KV cubes from the work schedule's queues (its XCD's
+// first) until they are empty, and runs each exactly as a one-cube workgroup
+// would.
+template <typename T, typename TO, int D, bool DENSE, bool PAD, int BS, bool TEXT, int QB = 1, bool SCHED = false>
 __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(const T* __restrict__ q, const T* __restrict__ k,
                                                      const T* __restrict__ v, const T* __restrict__ d_o,
                                                      const float* __restrict__ stats,
@@ -150,19 +154,35 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(const T* __restrict__ q, co
                                                      const float* __restrict__ dv_add, TO* __restrict__ dk,
                                                      TO* __restrict__ dv, int nq, int nkv, int seq, int ld,
                                                      int out_rows, int64_t kph, float scale, float c, PadGrid pad,
-                                                     int ntc, int ntext, int nbh) {
+                                                     int ntc, int ntext, int nbh,
+                                                     const int32_t* __restrict__ sk_hdr = nullptr,
+                                                     const int32_t* __restrict__ sk_items = nullptr,
+                                                     int32_t* __restrict__ sk_ctr = nullptr) {
   static_assert(!(DENSE && PAD), "padding applies to the fine branch");
   static_assert(!DENSE || BS == 0, "the dense mode has one cube per block");
   static_assert(!(DENSE && TEXT), "text rows apply to the fine branch");
   static_assert(QB == 1 || (QB == 2 && BS == 1 && !TEXT && !DENSE), "whole-block workgroups for 128-token blocks");
+  static_assert(!SCHED || (QB == 1 && BS == 0 && !TEXT && !DENSE), "the schedule serves 64-token blocks");
   constexpr int TILE = 64 * D;
   __shared__ __align__(16) T tA[2 * TILE];  // stage A: Q tile | dO tile
   __shared__ __align__(16) T tB[2 * TILE];  // stage B
   __shared__ __align__(16) float sA[128];   // stage A row statistics: [row][lse2, delta]
   __shared__ __align__(16) float sB[128];
+  __shared__ int s_item;                    // SCHED: the item the workgroup runs next
+  for (int iter = 0;; ++iter) {
   int bh, j;
   bool textk = false;  // a text KV cube
-  if constexpr (TEXT) {
+  if constexpr (SCHED) {
+    __syncthreads();  // every wave is done with the previous item's tiles and s_item
+    if (threadIdx.x == 0) s_item = sched_take(sk_hdr, sk_items, sk_ctr);
+    __syncthreads();
+    const int code = s_item;
+    if (code < 0) break;
+    bh = code / nkv;
+    j = code - bh * nkv;
+  } else if (iter > 0) {
+    break;
+  } else if constexpr (TEXT) {
     const int tblk = (ntc * nbh + 7) & ~7;  // a multiple of 8 keeps the video blocks' XCD map
     if ((int)blockIdx.x < tblk) {
       if ((int)blockIdx.x >= ntc * nbh) return;
@@ -337,7 +357,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(const T* __restrict__ q, co
         }
   }
   __syncthreads();
-  if (qh == 1) return;
+  if (qh == 1) continue;  // this wave's part is handed over (the next item starts at a barrier)
 #pragma unroll
   for (int db = 0; db < D / 16; ++db)
 #pragma unroll
@@ -393,6 +413,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(const T* __restrict__ q, co
       store4(vrow + 16 * db + 4 * g, b4);
     }
   }
+  }  // items
 }
 
 // One (query cube, KV cube) pair of the dQ kernel for one wave: queries 32qh..
@@ -468,7 +489,10 @@ __device__ __forceinline__ void dq_pair(const T* ks, const T* vs, int brow, int 
 // (waves 0, 1 the first cube, 2, 3 the second); each wave runs both key
 // halves of every staged K / V tile itself, so the tiles are staged once for
 // 128 query rows and no key-half reduction is needed.
-template <typename T, typename TO, int D, bool DENSE, bool STATS, bool PAD, int BS, bool TEXT, int QB = 1>
+// SCHED (64-token blocks): as in the dK/dV kernel, over the schedule's
+// query-cube queues.
+template <typename T, typename TO, int D, bool DENSE, bool STATS, bool PAD, int BS, bool TEXT, int QB = 1,
+          bool SCHED = false>
 __global__ __launch_bounds__(256, 2) void k_bwd_dq(const T* __restrict__ q, const T* __restrict__ k,
                                                    const T* __restrict__ v, const T* __restrict__ d_o,
                                                    const T* __restrict__ o, const float* __restrict__ lse,
@@ -478,17 +502,32 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(const T* __restrict__ q, cons
                                                    const float* __restrict__ dq_add, TO* __restrict__ dq, int nq,
                                                    int nkv, int seq, int ld, int out_rows, int64_t kph, float scale,
                                                    float c, int ct, int cy, int cx, PadGrid pad, int ntc, int ntext,
-                                                   int nbh) {
+                                                   int nbh, const int32_t* __restrict__ sq_hdr = nullptr,
+                                                   const int32_t* __restrict__ sq_items = nullptr,
+                                                   int32_t* __restrict__ sq_ctr = nullptr) {
   static_assert(!PAD || (STATS && !DENSE), "padding applies to the fine branch");
   static_assert(!DENSE || BS == 0, "the dense mode has one cube per block");
   static_assert(!TEXT || (STATS && !DENSE), "text rows apply to the fine branch");
   static_assert(QB == 1 || (QB == 2 && BS == 1 && !TEXT && !DENSE), "whole-block workgroups for 128-token blocks");
+  static_assert(!SCHED || (QB == 1 && BS == 0 && !TEXT && !DENSE && STATS), "the schedule serves 64-token blocks");
   constexpr int TILE = 64 * D;
   __shared__ __align__(16) T tA[2 * TILE];  // stage A: K tile | V tile
   __shared__ __align__(16) T tB[2 * TILE];  // stage B
+  __shared__ int s_item;                    // SCHED: the item the workgroup runs next
+  for (int iter = 0;; ++iter) {
   int bh, i;
   bool textq = false;  // a text query cube
-  if constexpr (TEXT) {
+  if constexpr (SCHED) {
+    __syncthreads();  // every wave is done with the previous item's tiles and s_item
+    if (threadIdx.x == 0) s_item = sched_take(sq_hdr, sq_items, sq_ctr);
+    __syncthreads();
+    const int code = s_item;
+    if (code < 0) break;
+    bh = code / nq;
+    i = code - bh * nq;
+  } else if (iter > 0) {
+    break;
+  } else if constexpr (TEXT) {
     const int tblk = (ntc * nbh + 7) & ~7;  // a multiple of 8 keeps the video blocks' XCD map
     if ((int)blockIdx.x < tblk) {
       if ((int)blockIdx.x >= ntc * nbh) return;
@@ -689,7 +728,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(const T* __restrict__ q, cons
         for (int r = 0; r < 4; ++r) mine[((db * 2 + qb) * 4 + r) * 64 + lane] = dqa[db][qb][r];
   }
   __syncthreads();
-  if (kh == 1) return;
+  if (kh == 1) continue;  // this wave's part is handed over (the next item starts at a barrier)
 #pragma unroll
   for (int db = 0; db < D / 16; ++db)
 #pragma unroll
@@ -730,6 +769,32 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(const T* __restrict__ q, cons
       store4(dst + 16 * db + 4 * g, a4);
     }
   }
+  }  // items
+}
+
+// The fine backward over the work schedule: dQ over the query-cube queues
+// (it writes the row statistics), then dK/dV over the KV-cube queues.
+template <typename T, int D, bool PAD>
+hipError_t launch_bwd_sched(const AttnBwdArgs& a, hipStream_t st) {
+  hipError_t e = launch_fill_u32((uint32_t*)a.sq_ctr, 0u, 16, st);
+  if (e != hipSuccess) return e;
+  const auto fq = k_bwd_dq<T, T, D, false, true, PAD, 0, false, 1, true>;
+  timer_before(TK_BWD_DQ, st);
+  hipLaunchKernelGGL(fq, dim3(resident_grid((const void*)fq, 256, a.bh * a.nq)), dim3(256), 0, st, (const T*)a.q,
+                     (const T*)a.k, (const T*)a.v, (const T*)a.d_o, (const T*)a.o, a.lse, a.stats_out, nullptr,
+                     a.row_ptr, a.col_idx, a.dq_add, (T*)a.dq, a.nq, a.nkv, a.seq, a.ld, a.out_rows, a.kph, a.scale,
+                     a.scale_log2, a.ct, a.cy, a.cx, a.pad, 0, 0, a.bh, a.sq_hdr, a.sq_items, a.sq_ctr);
+  timer_after(TK_BWD_DQ, st);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const auto fk = k_bwd_dkdv<T, T, D, false, PAD, 0, false, 1, true>;
+  timer_before(TK_BWD_DKDV, st);
+  hipLaunchKernelGGL(fk, dim3(resident_grid((const void*)fk, 256, a.bh * a.nkv)), dim3(256), 0, st, (const T*)a.q,
+                     (const T*)a.k, (const T*)a.v, (const T*)a.d_o, a.stats_out, a.col_ptr, a.row_idx, a.dk_add,
+                     a.dv_add, (T*)a.dk, (T*)a.dv, a.nq, a.nkv, a.seq, a.ld, a.out_rows, a.kph, a.scale, a.scale_log2,
+                     a.pad, 0, 0, a.bh, a.sk_hdr, a.sk_items, a.sq_ctr + 8);
+  timer_after(TK_BWD_DKDV, st);
+  return hipGetLastError();
 }
 
 template <typename T, typename TO, int D, bool DENSE, bool PAD, int BS, bool TEXT, int QB = 1>
@@ -762,6 +827,8 @@ hipError_t launch_bwd_tt(const AttnBwdArgs& a, hipStream_t st) {
 template <typename T, int D>
 hipError_t launch_bwd_t(const AttnBwdArgs& a, hipStream_t st) {
   if (a.dense) return launch_bwd_tt<T, float, D, true, false, 0, false>(a, st);
+  if (a.sq_hdr && !a.bs && !a.ntc)  // the work schedule's queues
+    return a.pad.on ? launch_bwd_sched<T, D, true>(a, st) : launch_bwd_sched<T, D, false>(a, st);
 #define VSA2_BWD(PAD, BS)                                                                              \
   return a.ntc ? launch_bwd_tt<T, T, D, false, PAD, BS, true>(a, st)                                  \
                : launch_bwd_tt<T, T, D, false, PAD, BS, false>(a, st)

@@ -40,21 +40,41 @@ namespace vsa2 {
 // a block (waves 0, 1 the first cube, 2, 3 the second), which share the
 // block's KV list, so every gathered K / V tile is staged once for 128 query
 // rows.
-template <typename T, typename TO, int D, bool DENSE, bool PAD, int BS, bool TEXT, int QB = 1>
+// SCHED (64-token blocks): the grid holds as many workgroups as fit on the
+// device; each takes query cubes from the work schedule's queues (its XCD's
+// first) until they are empty, and runs each exactly as a one-cube workgroup
+// would.
+template <typename T, typename TO, int D, bool DENSE, bool PAD, int BS, bool TEXT, int QB = 1, bool SCHED = false>
 __global__ __launch_bounds__(128 * QB, 2) void k_attn_fwd(const T* __restrict__ q, const T* __restrict__ k,
                                                   const T* __restrict__ v, const int32_t* __restrict__ row_ptr,
                                                   const int32_t* __restrict__ col_idx, TO* __restrict__ o,
                                                   float* __restrict__ lse, int nq, int nkv, int seq, int ld,
                                                   int out_rows, int64_t kph, float c, int ct, int cy, int cx,
-                                                  PadGrid pad, int ntc, int ntext, int nbh) {
+                                                  PadGrid pad, int ntc, int ntext, int nbh,
+                                                  const int32_t* __restrict__ sq_hdr = nullptr,
+                                                  const int32_t* __restrict__ sq_items = nullptr,
+                                                  int32_t* __restrict__ sq_ctr = nullptr) {
   static_assert(!(DENSE && PAD), "padding applies to the fine branch");
   static_assert(!(DENSE && TEXT), "text rows apply to the fine branch");
   static_assert(QB == 1 || (QB == 2 && BS == 1 && !TEXT && !DENSE), "whole-block workgroups for 128-token blocks");
+  static_assert(!SCHED || (QB == 1 && BS == 0 && !TEXT && !DENSE), "the schedule serves 64-token blocks");
   __shared__ __align__(16) T ks[64 * D];
   __shared__ __align__(16) T vs[64 * D];
+  __shared__ int s_item;  // SCHED: the item the workgroup runs next
+  for (int iter = 0;; ++iter) {
   int bh, i;
   bool textq = false;  // a text query cube
-  if constexpr (TEXT) {
+  if constexpr (SCHED) {
+    __syncthreads();  // every wave is done with the previous item's tiles and s_item
+    if (threadIdx.x == 0) s_item = sched_take(sq_hdr, sq_items, sq_ctr);
+    __syncthreads();
+    const int code = s_item;
+    if (code < 0) break;
+    bh = code / nq;
+    i = code - bh * nq;
+  } else if (iter > 0) {
+    break;
+  } else if constexpr (TEXT) {
     const int tblk = (ntc * nbh + 7) & ~7;  // a multiple of 8 keeps the video blocks' XCD map
     if ((int)blockIdx.x < tblk) {
       if ((int)blockIdx.x >= ntc * nbh) return;
@@ -262,6 +282,7 @@ __global__ __launch_bounds__(128 * QB, 2) void k_attn_fwd(const T* __restrict__ 
       if (g == 0) lse[(size_t)bh * out_rows + qrow] = lt > 0.f ? (m[qb] * c + __log2f(lt)) * LN2 : -INFINITY;
     }
   }
+  }  // items
 }
 
 template <typename T, int D>
@@ -286,13 +307,26 @@ hipError_t launch_fwd_t(const AttnArgs& a, hipStream_t st) {
   hipLaunchKernelGGL((k_attn_fwd<T, T, D, false, PAD, 1, false, 2>), bgrid, dim3(256), 0, st, (const T*)a.q,    \
                      (const T*)a.k, (const T*)a.v, a.row_ptr, a.col_idx, (T*)a.o, a.lse, a.nq, a.nkv, a.seq, a.ld, \
                      a.out_rows, a.kph, a.scale_log2, a.ct, a.cy, a.cx, a.pad, 0, 0, a.bh)
-    if (a.bs && !a.ntc) {
+#define VSA2_FWD_SCHED(PAD)                                                                                    \
+  {                                                                                                            \
+    const auto fn = k_attn_fwd<T, T, D, false, PAD, 0, false, 1, true>;                                        \
+    hipError_t e_ = launch_fill_u32((uint32_t*)a.sq_ctr, 0u, 8, st);                                           \
+    if (e_ != hipSuccess) return e_;                                                                           \
+    const dim3 pgrid(resident_grid((const void*)fn, 128, a.bh * a.nq));                                        \
+    hipLaunchKernelGGL(fn, pgrid, dim3(128), 0, st, (const T*)a.q, (const T*)a.k, (const T*)a.v, a.row_ptr,     \
+                       a.col_idx, (T*)a.o, a.lse, a.nq, a.nkv, a.seq, a.ld, a.out_rows, a.kph, a.scale_log2,    \
+                       a.ct, a.cy, a.cx, a.pad, 0, 0, a.bh, a.sq_hdr, a.sq_items, a.sq_ctr);                  \
+  }
+    if (a.sq_hdr && !a.bs && !a.ntc) {
+      if (a.pad.on) VSA2_FWD_SCHED(true) else VSA2_FWD_SCHED(false)
+    } else if (a.bs && !a.ntc) {
       if (a.pad.on) { VSA2_FWD_BLOCK(true); } else { VSA2_FWD_BLOCK(false); }
     } else if (a.bs) {  // with text rows: per-cube workgroups
       if (a.pad.on) { VSA2_FWD(true, 1, true); } else { VSA2_FWD(false, 1, true); }
     } else {
       if (a.pad.on) { VSA2_FWD_T(true, 0); } else { VSA2_FWD_T(false, 0); }
     }
+#undef VSA2_FWD_SCHED
 #undef VSA2_FWD_BLOCK
 #undef VSA2_FWD_T
 #undef VSA2_FWD

@@ -527,6 +527,50 @@ __device__ __forceinline__ int cube_count(int c, const PadGrid& p) {
   return vt * vy * vx;
 }
 
+// Exclusive prefix sum over a 1024-thread block (every thread takes part);
+// total gets the block's sum.  sh: 17 words of LDS.
+__device__ inline uint32_t block_scan_1024(uint32_t x, uint32_t& total, uint32_t* sh) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  uint32_t inc = x;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t y = __shfl_up(inc, o);
+    if (lane >= o) inc += y;
+  }
+  if (lane == 63) sh[w] = inc;
+  __syncthreads();
+  if (tid == 0) {
+    uint32_t a = 0;
+    for (int i = 0; i < 16; ++i) {
+      const uint32_t t = sh[i];
+      sh[i] = a;
+      a += t;
+    }
+    sh[16] = a;
+  }
+  __syncthreads();
+  const uint32_t r = sh[w] + inc - x;
+  total = sh[16];
+  __syncthreads();
+  return r;
+}
+
+// Next work item of the schedule for this workgroup: from the queue of its
+// XCD (workgroup b runs on XCD b mod 8), then from the others in turn; -1
+// when every queue is empty.  hdr = {queue starts[8], queue lengths[8]}; ctr
+// = one counter per queue, zero before the launch.  Called by one thread.
+__device__ inline int sched_take(const int32_t* __restrict__ hdr, const int32_t* __restrict__ items, int32_t* ctr) {
+  const int x0 = (int)(blockIdx.x & 7u);
+  for (int s = 0; s < 8; ++s) {
+    const int x = (x0 + s) & 7;
+    const int len = hdr[8 + x];
+    if (__hip_atomic_load(&ctr[x], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= len) continue;
+    const int t = atomicAdd(&ctr[x], 1);
+    if (t < len) return items[hdr[x] + t];
+  }
+  return -1;
+}
+
 __host__ __device__ inline int xcd_grid(int items_per_bh, int bh_total) {
   return 8 * ((items_per_bh + 7) >> 3) * bh_total;
 }

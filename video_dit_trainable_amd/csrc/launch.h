@@ -53,6 +53,13 @@ struct TopkWs {       // carved from the caller workspace
   uint32_t* colcnt;   // [bh, nb]
   uint32_t* bitmap;   // [bh, nb, words]
   int words;          // 32-bit words per bitmap row (multiple of 2)
+  uint32_t* skeys;    // [bh, nb] schedule: min-hash key of every list
+  int32_t* sorder;    // [bh, nb] schedule: cubes in key order
+  int32_t* stmp;      // [bh, nb] schedule: cubes in queue order
+  int32_t* scnt;      // [bh, 8] schedule: items per XCD
+  int32_t* shoff;     // [bh, 8] schedule: queue offsets
+  uint8_t* spx;       // [bh, nb] schedule: XCD and length class of each position
+  int32_t* srng;      // [bh, 9] schedule: XCD range starts
 };
 struct TopkArgs {
   const float* scores;
@@ -67,6 +74,26 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t st);
 hipError_t launch_topk_rows(const TopkArgs& a, hipStream_t st);
 // CSC from a caller CSR (uses ws.colcnt and ws.bitmap)
 hipError_t launch_plan(const TopkArgs& a, hipStream_t st);
+
+// Work schedule of the fine branch (sched.hip), built from the CSR and the
+// CSC.  Per side (query cubes for the forward and dQ, KV cubes for dK/dV):
+// hdr[16] = {start of queue x in items (x < 8), length of queue x}, then
+// items[bh * n], item = bh * n + cube.  Workgroup b of a scheduled kernel
+// takes items from queue b mod 8 through the counter ctr[b mod 8] (zeroed
+// before the launch), then from the other queues.
+constexpr int SCHED_MAXN = 46340;  // cubes per (batch, head) the API admits
+struct SchedArgs {
+  const int32_t *row_ptr, *col_idx, *col_ptr, *row_idx;
+  int32_t *row_hdr, *row_items, *col_hdr, *col_items;
+  uint32_t* keys;             // workspace [bh, n]
+  int32_t *order, *tmp;       // workspace [bh, n]
+  int32_t *cnt, *hoff;        // workspace [bh, 8]
+  uint8_t* px;                // workspace [bh, n]: XCD << 5 | length class of each position
+  int32_t* rng;               // workspace [bh, 9]: XCD range starts
+  int bh, n;
+  int64_t kph;
+};
+hipError_t launch_sched(const SchedArgs& a, hipStream_t st);
 
 struct AttnArgs {
   const void *q, *k, *v;
@@ -87,6 +114,8 @@ struct AttnArgs {
   PadGrid pad;                        // fine branch on a padded grid: pad keys masked, pad rows zero
   int bs;                             // fine: 2^bs cubes per block; the CSR lists blocks (nq, nkv count cubes)
   int ntc, ntext;                     // fine: text cubes after the nq video cubes, and their tokens (0 = none)
+  const int32_t *sq_hdr, *sq_items;   // fine: the schedule's query-cube queues (NULL: one workgroup per cube)
+  int32_t* sq_ctr;                    //   their 8 counters (workspace)
 };
 hipError_t launch_attn_fwd(const AttnArgs& a, hipStream_t st);
 
@@ -108,6 +137,9 @@ struct AttnBwdArgs {
   PadGrid pad;                        // fine branch on a padded grid (per-block terms added as row/n, n real tokens)
   int bs;                             // fine: 2^bs cubes per block; CSR / CSC and the per-block terms are per block
   int ntc, ntext;                     // fine: text cubes after the nq video cubes, and their tokens (0 = none)
+  const int32_t *sq_hdr, *sq_items;   // fine: the schedule's query-cube queues (NULL: one workgroup per cube)
+  const int32_t *sk_hdr, *sk_items;   //   and KV-cube queues
+  int32_t* sq_ctr;                    //   8 counters for the dQ pass and 8 for the dK/dV pass (workspace)
 };
 hipError_t launch_attn_bwd(const AttnBwdArgs& a, hipStream_t st);
 
@@ -155,6 +187,12 @@ struct GateBwdArgs {
 hipError_t launch_gate_bwd(const GateBwdArgs& a, hipStream_t st);
 
 hipError_t launch_fill_u32(uint32_t* p, uint32_t val, size_t n, hipStream_t st);
+
+// Grid of a scheduled kernel: the workgroups of `threads` threads that fit on
+// the current device at once (multiprocessors x resident blocks of fn), a
+// multiple of 8 so every XCD gets the same number, at most `items` rounded up
+// to 8 and at least 8.
+int resident_grid(const void* fn, int threads, int items);
 
 // Diagnostic timer hooks (api.hip): bracket one launch of kernel `kid`.
 enum TimerKernel { TK_FINE_FWD = 0, TK_BWD_DKDV = 1, TK_BWD_DQ = 2, TK_ROUTER_LSE = 3, TK_ROUTER_SCORES = 4 };

@@ -1,0 +1,250 @@
+// Work schedule of the fine branch: in what order, and on which XCD, the
+// per-cube work items of the forward and dQ passes (query cubes) and of the
+// dK/dV pass (KV cubes) run.
+//
+// Per-sequence TopK (paper §2.2 Eq.(8)-(9)) leaves every query cube with its
+// own number of KV cubes, and the blog's reproduction notes (its §12) leave
+// the scheduler of these unequal lists to the implementer; its §10 counts the
+// resulting imbalance and the block-sparse memory traffic among the gap
+// between the ideal and the measured speed-up.  At 720p the lists of one
+// (batch, head) run up to ~220 blocks per query cube and up to ~800 query
+// cubes per KV cube, with a quarter of the lists empty.  The schedule:
+//  * orders the cubes of each (batch, head) by a min-hash of their lists: a
+//    cube's key is the minimum, over its list, of two fixed bijections of the
+//    ids (16 bits each); two cubes share the first half with probability equal
+//    to the Jaccard overlap of their lists, so cubes that gather the same
+//    tiles sit next to each other;
+//  * cuts that order into 8 contiguous ranges of equal work (list length plus
+//    a fixed cost per item), one per XCD, so neighbours in the order share an
+//    L2 and every XCD gets the same work;
+//  * puts the long lists of each range first (by length class, then the
+//    min-hash order), so the short and the empty ones end each XCD's queue;
+//  * appends each (batch, head)'s range for XCD x to queue x, in (batch,
+//    head) order.
+// The kernels run as many workgroups as fit on the device at once; each takes
+// items from the queue of its XCD (workgroup b runs on XCD b mod 8) and, when
+// that queue is empty, from the others.  An item is computed the same way
+// whoever takes it, so results do not depend on the order items are taken.
+#include "common.h"
+#include "launch.h"
+
+namespace vsa2 {
+
+// Two bijections of [0, 2^16) (an odd multiplier is invertible modulo 2^16).
+__device__ __forceinline__ uint32_t mh1(uint32_t j) { return (j * 40503u + 12345u) & 0xFFFFu; }
+__device__ __forceinline__ uint32_t mh2(uint32_t j) { return ((j ^ 0x5A5Au) * 52429u + 777u) & 0xFFFFu; }
+
+__device__ __forceinline__ int list_len(const int32_t* __restrict__ ptr, int c, int64_t kph) {
+  const int64_t s = min<int64_t>(max(ptr[c], 0), kph);
+  const int64_t e = min<int64_t>(max<int64_t>(ptr[c + 1], s), kph);
+  return (int)(e - s);
+}
+
+// Min-hash key of every list: (min mh1 << 16 | min mh2), 0xFFFFFFFF when the
+// list holds no valid id.  One wave per list.
+__global__ __launch_bounds__(256) void k_sched_keys(const int32_t* __restrict__ ptr, const int32_t* __restrict__ idx,
+                                                    uint32_t* __restrict__ keys, int n, int64_t kph) {
+  const int bh = blockIdx.y, c = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (c >= n) return;
+  const int32_t* pb = ptr + (size_t)bh * (n + 1);
+  const int64_t s = min<int64_t>(max(pb[c], 0), kph);
+  const int64_t e = min<int64_t>(max<int64_t>(pb[c + 1], s), kph);
+  const int32_t* li = idx + (size_t)bh * kph;
+  uint32_t a = 0xFFFFu, b = 0xFFFFu;
+  bool any = false;
+  for (int64_t p = s + lane; p < e; p += 64) {
+    const int j = li[p];
+    if ((unsigned)j < (unsigned)n) {
+      a = min(a, mh1((uint32_t)j));
+      b = min(b, mh2((uint32_t)j));
+      any = true;
+    }
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    a = min(a, (uint32_t)__shfl_xor((int)a, o));
+    b = min(b, (uint32_t)__shfl_xor((int)b, o));
+  }
+  any = __ballot(any) != 0ull;
+  if (lane == 0) keys[(size_t)bh * n + c] = any ? ((a << 16) | b) : 0xFFFFFFFFu;
+}
+
+constexpr int SCHED_TILE = 4096;  // keys per LDS tile of the rank count
+constexpr int SCHED_OVH = 4;      // fixed cost of an item, in list entries
+
+// Rank of every cube in (key, id) order, order[rank] = cube.  One thread per
+// cube counts the keys below its own; the keys of the (batch, head) pass
+// through LDS in tiles, read four at a time.
+__global__ __launch_bounds__(256) void k_sched_rank(const uint32_t* __restrict__ keys, int32_t* __restrict__ order,
+                                                    int n) {
+  __shared__ __align__(16) uint32_t kt[SCHED_TILE];
+  const int bh = blockIdx.y, tid = threadIdx.x, e = blockIdx.x * 256 + tid;
+  const uint32_t* kb = keys + (size_t)bh * n;
+  const uint32_t ke = e < n ? kb[e] : 0u;
+  uint32_t rank = 0;
+  for (int f0 = 0; f0 < n; f0 += SCHED_TILE) {
+    const int nt = min(SCHED_TILE, n - f0);
+    __syncthreads();
+    for (int f = tid; f < SCHED_TILE; f += 256) kt[f] = f < nt ? kb[f0 + f] : 0xFFFFFFFFu;
+    __syncthreads();
+    // key f0 + f ranks below ke when smaller, or equal with a lower id; the
+    // pad entries past nt (0xFFFFFFFF, id beyond every cube) never do
+    const int lim = e - f0;  // ids below e, in this tile's numbering
+    const int nt4 = (nt + 3) & ~3;
+#pragma unroll 4
+    for (int f = 0; f < nt4; f += 4) {
+      const uint4 k4 = *reinterpret_cast<const uint4*>(&kt[f]);
+      rank += (k4.x < ke || (k4.x == ke && f < lim)) ? 1u : 0u;
+      rank += (k4.y < ke || (k4.y == ke && f + 1 < lim)) ? 1u : 0u;
+      rank += (k4.z < ke || (k4.z == ke && f + 2 < lim)) ? 1u : 0u;
+      rank += (k4.w < ke || (k4.w == ke && f + 3 < lim)) ? 1u : 0u;
+    }
+  }
+  if (e < n) order[(size_t)bh * n + rank] = e;
+}
+
+// One workgroup per (batch, head): the work of each position of the order
+// (list length + SCHED_OVH), an exclusive scan, and the XCD of a position =
+// the eighth of the total its work's midpoint falls in, so the ranges are
+// contiguous in the order.  px[bh][p] = XCD << 5 | length class, with class
+// floor(log2(length + 1)) + 1 <= 16; rng[bh][0..8] = range starts (rng[8] = n).
+__global__ __launch_bounds__(1024) void k_sched_cut(const int32_t* __restrict__ ptr, const int32_t* __restrict__ order,
+                                                    uint8_t* __restrict__ px, int32_t* __restrict__ rng_out, int n,
+                                                    int64_t kph) {
+  __shared__ uint32_t sh[17];
+  __shared__ int rng[9];
+  const int bh = blockIdx.x, tid = threadIdx.x;
+  const int32_t* pb = ptr + (size_t)bh * (n + 1);
+  const int32_t* ob = order + (size_t)bh * n;
+  uint32_t total = 0;
+  for (int p0 = 0; p0 < n; p0 += 1024) {
+    const int p = p0 + tid;
+    const uint32_t w = p < n ? (uint32_t)(list_len(pb, ob[p], kph) + SCHED_OVH) : 0u;
+    uint32_t tot;
+    (void)block_scan_1024(w, tot, sh);
+    total += tot;
+  }
+  if (tid < 9) rng[tid] = 0;
+  __syncthreads();
+  uint32_t carry = 0;
+  for (int p0 = 0; p0 < n; p0 += 1024) {
+    const int p = p0 + tid;
+    const int len = p < n ? list_len(pb, ob[p], kph) : 0;
+    const uint32_t w = p < n ? (uint32_t)(len + SCHED_OVH) : 0u;
+    uint32_t tot;
+    const uint32_t before = carry + block_scan_1024(w, tot, sh);
+    carry += tot;
+    if (p < n) {
+      const uint64_t mid2 = 2ull * before + w;                        // twice the midpoint
+      const int x = (int)min<uint64_t>(7ull, (8ull * mid2) / (2ull * (uint64_t)total));
+      const int c = 32 - __clz((unsigned)len + 1u);                   // floor(log2(len + 1)) + 1
+      px[(size_t)bh * n + p] = (uint8_t)((x << 5) | c);
+      atomicAdd(&rng[x + 1], 1);
+    }
+  }
+  __syncthreads();
+  if (tid == 0) {
+    for (int x = 0; x < 8; ++x) rng[x + 1] += rng[x];
+  }
+  __syncthreads();
+  if (tid < 9) rng_out[(size_t)bh * 9 + tid] = rng[tid];
+}
+
+// Long lists first inside each XCD's range: the position of p within its
+// range = entries of the range with a higher class, plus those of the same
+// class earlier in the order.  tmp[bh][range start + that] = cube;
+// cnt[bh][x] = items of XCD x.  The head's classes pass through LDS.
+__global__ __launch_bounds__(256) void k_sched_place(const uint8_t* __restrict__ px, const int32_t* __restrict__ rng,
+                                                     const int32_t* __restrict__ order, int32_t* __restrict__ tmp,
+                                                     int32_t* __restrict__ cnt, int n) {
+  __shared__ uint8_t pl[SCHED_MAXN];
+  const int bh = blockIdx.y, tid = threadIdx.x, p = blockIdx.x * 256 + tid;
+  const uint8_t* pxb = px + (size_t)bh * n;
+  for (int q = tid; q < n; q += 256) pl[q] = pxb[q];
+  __syncthreads();
+  if (blockIdx.x == 0 && tid < 8) cnt[(size_t)bh * 8 + tid] = rng[(size_t)bh * 9 + tid + 1] - rng[(size_t)bh * 9 + tid];
+  if (p >= n) return;
+  const int x = pl[p] >> 5, c = pl[p] & 31;
+  const int r0 = rng[(size_t)bh * 9 + x], r1 = rng[(size_t)bh * 9 + x + 1];
+  int pos = 0;
+  for (int q = r0; q < r1; ++q) {
+    const int cq = pl[q] & 31;
+    pos += (cq > c || (cq == c && q < p)) ? 1 : 0;
+  }
+  tmp[(size_t)bh * n + r0 + pos] = order[(size_t)bh * n + p];
+}
+
+// Queue offsets: queue x holds, for every (batch, head) in turn, that head's
+// range for XCD x.  hdr[x] = start of queue x in the item array, hdr[8 + x]
+// its length; hoff[bh][x] = where (batch, head) bh's range starts.
+__global__ __launch_bounds__(64) void k_sched_queues(const int32_t* __restrict__ cnt, int32_t* __restrict__ hdr,
+                                                     int32_t* __restrict__ hoff, int bh) {
+  __shared__ int tot[8];
+  const int x = threadIdx.x;
+  if (x < 8) {
+    int s = 0;
+    for (int h = 0; h < bh; ++h) s += cnt[(size_t)h * 8 + x];
+    tot[x] = s;
+  }
+  __syncthreads();
+  if (x < 8) {
+    int head = 0;
+    for (int y = 0; y < x; ++y) head += tot[y];
+    hdr[x] = head;
+    hdr[8 + x] = tot[x];
+    int o = head;
+    for (int h = 0; h < bh; ++h) {
+      hoff[(size_t)h * 8 + x] = o;
+      o += cnt[(size_t)h * 8 + x];
+    }
+  }
+}
+
+// Items into their queues: item code = bh * n + cube.
+__global__ __launch_bounds__(256) void k_sched_fill(const int32_t* __restrict__ tmp, const int32_t* __restrict__ cnt,
+                                                    const int32_t* __restrict__ hoff, int32_t* __restrict__ items,
+                                                    int n) {
+  const int bh = blockIdx.y, t = blockIdx.x * 256 + threadIdx.x;
+  if (t >= n) return;
+  int s = 0, x = 0;
+  for (; x < 7; ++x) {
+    const int c = cnt[(size_t)bh * 8 + x];
+    if (t < s + c) break;
+    s += c;
+  }
+  items[hoff[(size_t)bh * 8 + x] + (t - s)] = (int32_t)((int64_t)bh * n + tmp[(size_t)bh * n + t]);
+}
+
+// One side of the schedule from lists (ptr, idx): the CSR for the query side,
+// the CSC for the KV side.
+static hipError_t build_side(const int32_t* ptr, const int32_t* idx, int32_t* hdr, int32_t* items,
+                             const SchedArgs& a, hipStream_t st) {
+  const int n = a.n;
+  hipLaunchKernelGGL(k_sched_keys, dim3((n + 3) / 4, a.bh), dim3(256), 0, st, ptr, idx, a.keys, n, a.kph);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_sched_rank, dim3((n + 255) / 256, a.bh), dim3(256), 0, st, a.keys, a.order, n);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_sched_cut, dim3(a.bh), dim3(1024), 0, st, ptr, a.order, a.px, a.rng, n, a.kph);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_sched_place, dim3((n + 255) / 256, a.bh), dim3(256), 0, st, a.px, a.rng, a.order, a.tmp,
+                     a.cnt, n);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_sched_queues, dim3(1), dim3(64), 0, st, a.cnt, hdr, a.hoff, a.bh);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_sched_fill, dim3((n + 255) / 256, a.bh), dim3(256), 0, st, a.tmp, a.cnt, a.hoff, items, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_sched(const SchedArgs& a, hipStream_t st) {
+  if (a.n > SCHED_MAXN) return hipErrorInvalidValue;
+  hipError_t e = build_side(a.row_ptr, a.col_idx, a.row_hdr, a.row_items, a, st);
+  if (e != hipSuccess) return e;
+  return build_side(a.col_ptr, a.row_idx, a.col_hdr, a.col_items, a, st);
+}
+
+}  // namespace vsa2

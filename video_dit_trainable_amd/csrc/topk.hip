@@ -151,32 +151,6 @@ __global__ __launch_bounds__(256) void k_rowcount(const float* __restrict__ scor
 
 // Block-wide exclusive scan of one value per thread (1024 threads); returns
 // the exclusive prefix and sets `total`.
-__device__ uint32_t block_scan_1024(uint32_t x, uint32_t& total, uint32_t* sh) {
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  uint32_t inc = x;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t y = __shfl_up(inc, o);
-    if (lane >= o) inc += y;
-  }
-  if (lane == 63) sh[w] = inc;
-  __syncthreads();
-  if (tid == 0) {
-    uint32_t a = 0;
-    for (int i = 0; i < 16; ++i) {
-      const uint32_t t = sh[i];
-      sh[i] = a;
-      a += t;
-    }
-    sh[16] = a;
-  }
-  __syncthreads();
-  const uint32_t r = sh[w] + inc - x;
-  total = sh[16];
-  __syncthreads();
-  return r;
-}
-
 // Ties at tau go to the lowest flat indices: row i takes
 // clamp(need - (ties in rows < i), 0, ties in row i).  Builds row_ptr.
 __global__ __launch_bounds__(1024) void k_rowalloc(const uint32_t* __restrict__ rowcnt,

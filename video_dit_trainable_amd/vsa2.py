@@ -50,12 +50,13 @@ _SIGS = {
     "vsa2_route": (ctypes.c_int, [_PP, _P, _P, _P, _SZ, _P]),
     "vsa2_route_noalloc": (ctypes.c_int, [_PP, _P, _P, _P]),
     "vsa2_route_noalloc_limit": (ctypes.c_int, [ctypes.POINTER(_SZ)]),
-    "vsa2_topk_per_seq": (ctypes.c_int, [_PP, _P, _I32, _P, _P, _P, _P, _P, _SZ, _P]),
+    "vsa2_sched_size": (ctypes.c_int, [_PP, _I32, ctypes.POINTER(_SZ)]),
+    "vsa2_topk_per_seq": (ctypes.c_int, [_PP, _P, _I32, _P, _P, _P, _P, _P, _SZ, _P, _SZ, _P]),
     "vsa2_route_coarse": (ctypes.c_int, [_PP, _P, _P, _P, _SZ, _P]),
-    "vsa2_topk_per_row": (ctypes.c_int, [_PP, _P, _I32, _P, _P, _P, _P, _P, _SZ, _P]),
-    "vsa2_plan_from_csr": (ctypes.c_int, [_PP, _I32, _P, _P, _P, _P, _P, _SZ, _P]),
-    "vsa2_sparse_attn_fwd": (ctypes.c_int, [_PP, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
-    "vsa2_sparse_attn_bwd": (ctypes.c_int, [_PP, _I32] + [_P] * 15 + [_SZ, _P]),
+    "vsa2_topk_per_row": (ctypes.c_int, [_PP, _P, _I32, _P, _P, _P, _P, _P, _SZ, _P, _SZ, _P]),
+    "vsa2_plan_from_csr": (ctypes.c_int, [_PP, _I32, _P, _P, _P, _P, _P, _SZ, _P, _SZ, _P]),
+    "vsa2_sparse_attn_fwd": (ctypes.c_int, [_PP, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "vsa2_sparse_attn_bwd": (ctypes.c_int, [_PP, _I32] + [_P] * 16 + [_SZ, _P]),
     "vsa2_coarse_gate": (ctypes.c_int, [_PP, _P, _P, _I32, _P, _P, _P, _P, _P, _SZ, _P]),
     "vsa2_coarse_gate_bwd": (ctypes.c_int, [_PP, _P, _P, _I32, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "vsa2_kernel_timer_start": (ctypes.c_int, [_I32, _I32]),
@@ -157,10 +158,20 @@ def route_noalloc_limit():
     return out.value
 
 
-def vsa2_topk_per_seq(p, scores, topk, row_ptr, col_idx, col_ptr, row_idx, ws, stream=None):
+def _nbytes(t):
+    return 0 if t is None else t.numel() * t.element_size()
+
+
+def sched_size(p, topk):
+    out = _SZ(0)
+    _check("vsa2_sched_size", lib().vsa2_sched_size(ctypes.byref(p), topk, ctypes.byref(out)))
+    return out.value
+
+
+def vsa2_topk_per_seq(p, scores, topk, row_ptr, col_idx, col_ptr, row_idx, ws, stream=None, sched=None):
     _check("vsa2_topk_per_seq", lib().vsa2_topk_per_seq(
         ctypes.byref(p), _ptr(scores), topk, _ptr(row_ptr), _ptr(col_idx), _ptr(col_ptr), _ptr(row_idx),
-        _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
+        _ptr(sched), _nbytes(sched), _ptr(ws), _nbytes(ws), _stream(stream)))
 
 
 def vsa2_route_coarse(p, pooled, scores, ws, stream=None):
@@ -169,30 +180,30 @@ def vsa2_route_coarse(p, pooled, scores, ws, stream=None):
                                                         _stream(stream)))
 
 
-def vsa2_topk_per_row(p, scores, topk, row_ptr, col_idx, col_ptr, row_idx, ws, stream=None):
+def vsa2_topk_per_row(p, scores, topk, row_ptr, col_idx, col_ptr, row_idx, ws, stream=None, sched=None):
     _check("vsa2_topk_per_row", lib().vsa2_topk_per_row(
         ctypes.byref(p), _ptr(scores), topk, _ptr(row_ptr), _ptr(col_idx), _ptr(col_ptr), _ptr(row_idx),
-        _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
+        _ptr(sched), _nbytes(sched), _ptr(ws), _nbytes(ws), _stream(stream)))
 
 
-def vsa2_plan_from_csr(p, topk, row_ptr, col_idx, col_ptr, row_idx, ws, stream=None):
+def vsa2_plan_from_csr(p, topk, row_ptr, col_idx, col_ptr, row_idx, ws, stream=None, sched=None):
     _check("vsa2_plan_from_csr", lib().vsa2_plan_from_csr(
         ctypes.byref(p), topk, _ptr(row_ptr), _ptr(col_idx), _ptr(col_ptr), _ptr(row_idx),
-        _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
+        _ptr(sched), _nbytes(sched), _ptr(ws), _nbytes(ws), _stream(stream)))
 
 
-def vsa2_sparse_attn_fwd(p, topk, q, k, v, row_ptr, col_idx, o_f, lse, ws=None, stream=None):
+def vsa2_sparse_attn_fwd(p, topk, q, k, v, row_ptr, col_idx, o_f, lse, ws=None, stream=None, sched=None):
     _check("vsa2_sparse_attn_fwd", lib().vsa2_sparse_attn_fwd(
-        ctypes.byref(p), topk, _ptr(q), _ptr(k), _ptr(v), _ptr(row_ptr), _ptr(col_idx), _ptr(o_f), _ptr(lse),
-        _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
+        ctypes.byref(p), topk, _ptr(q), _ptr(k), _ptr(v), _ptr(row_ptr), _ptr(col_idx), _ptr(sched), _ptr(o_f),
+        _ptr(lse), _ptr(ws), _nbytes(ws), _stream(stream)))
 
 
 def vsa2_sparse_attn_bwd(p, topk, q, k, v, o_f, lse, d_o, row_ptr, col_idx, col_ptr, row_idx, dqkv_c,
-                         dq, dk, dv, ws, stream=None):
+                         dq, dk, dv, ws, stream=None, sched=None):
     _check("vsa2_sparse_attn_bwd", lib().vsa2_sparse_attn_bwd(
         ctypes.byref(p), topk, _ptr(q), _ptr(k), _ptr(v), _ptr(o_f), _ptr(lse), _ptr(d_o), _ptr(row_ptr),
-        _ptr(col_idx), _ptr(col_ptr), _ptr(row_idx), _ptr(dqkv_c), _ptr(dq), _ptr(dk), _ptr(dv),
-        _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
+        _ptr(col_idx), _ptr(col_ptr), _ptr(row_idx), _ptr(sched), _ptr(dqkv_c), _ptr(dq), _ptr(dk), _ptr(dv),
+        _ptr(ws), _nbytes(ws), _stream(stream)))
 
 
 def vsa2_coarse_gate(p, pooled, x, d_model, w_g, o_f, o, saved, ws, stream=None):
@@ -261,6 +272,9 @@ class Layer:
                       for op in (OP_ROUTE, OP_TOPK, OP_PLAN, OP_FWD, OP_BWD, OP_COARSE, OP_COARSE_BWD,
                                  OP_ROUTE_COARSE, OP_TOPK_ROW))
         self.ws = _ws(ws_need, device)
+        # the fine branch's work schedule (None when the problem needs none)
+        ss = sched_size(p, topk)
+        self.sched = _ws(ss, device) if ss else None
         self._grads = None
 
     def forward(self, q, k, v, x, w_g, route=True, stream=None, router="vsa2"):
@@ -271,19 +285,21 @@ class Layer:
         if route and router == "vsa":
             vsa2_route_coarse(p, self.pooled, self.scores, self.ws, stream)
             vsa2_topk_per_row(p, self.scores, self.topk, self.row_ptr, self.col_idx, self.col_ptr,
-                              self.row_idx, self.ws, stream)
+                              self.row_idx, self.ws, stream, sched=self.sched)
         elif route:
             vsa2_route(p, self.pooled, self.scores, self.ws, stream)
             vsa2_topk_per_seq(p, self.scores, self.topk, self.row_ptr, self.col_idx, self.col_ptr,
-                              self.row_idx, self.ws, stream)
-        vsa2_sparse_attn_fwd(p, self.topk, q, k, v, self.row_ptr, self.col_idx, self.o_f, self.lse, self.ws, stream)
+                              self.row_idx, self.ws, stream, sched=self.sched)
+        vsa2_sparse_attn_fwd(p, self.topk, q, k, v, self.row_ptr, self.col_idx, self.o_f, self.lse, self.ws, stream,
+                             sched=self.sched)
         vsa2_coarse_gate(p, self.pooled, x, self.d_model, w_g, self.o_f, self.o, self.saved, self.ws, stream)
         return self.o
 
     def set_selection(self, row_ptr, col_idx, stream=None):
         self.row_ptr.copy_(row_ptr)
         self.col_idx.copy_(col_idx)
-        vsa2_plan_from_csr(self.p, self.topk, self.row_ptr, self.col_idx, self.col_ptr, self.row_idx, self.ws, stream)
+        vsa2_plan_from_csr(self.p, self.topk, self.row_ptr, self.col_idx, self.col_ptr, self.row_idx, self.ws, stream,
+                           sched=self.sched)
 
     def grads(self):
         """Gradient buffers (allocated on first use): dq, dk, dv, dx, dw_g, dqkv_c."""
@@ -307,7 +323,8 @@ class Layer:
         vsa2_coarse_gate_bwd(p, self.pooled, x, self.d_model, w_g, self.saved, d_o, g["dqkv_c"], g["dx"],
                              g["dw_g"], self.ws, stream)
         vsa2_sparse_attn_bwd(p, self.topk, q, k, v, self.o_f, self.lse, d_o, self.row_ptr, self.col_idx,
-                             self.col_ptr, self.row_idx, g["dqkv_c"], g["dq"], g["dk"], g["dv"], self.ws, stream)
+                             self.col_ptr, self.row_idx, g["dqkv_c"], g["dq"], g["dk"], g["dv"], self.ws, stream,
+                             sched=self.sched)
         return g
 
     def saved_views(self):
