@@ -37,9 +37,10 @@ PEAK_HBM = 8.0e12       # MI355X HBM3E, B/s
 TIMED = {"fine_fwd": (vsa2.K_FINE_FWD, "k_attn_fwd"), "bwd_dkdv": (vsa2.K_BWD_DKDV, "k_bwd_dkdv"),
          "bwd_dq": (vsa2.K_BWD_DQ, "k_bwd_dq"), "router_lse": (vsa2.K_ROUTER_LSE, "k_router (pass 1)"),
          "router_scores": (vsa2.K_ROUTER_SCORES, "k_router (pass 2)")}
-# kernel source each timed kernel is built from (hashed to tell whether stored counters are current)
-SOURCES = {"fine_fwd": "attn_fwd.hip", "bwd_dkdv": "attn_bwd.hip", "bwd_dq": "attn_bwd.hip",
-           "router_lse": "router.hip", "router_scores": "router.hip"}
+# kernel sources each timed kernel is built from (hashed to tell whether stored counters are current);
+# the fine kernels' traffic also depends on the work schedule their items come from
+SOURCES = {"fine_fwd": ("attn_fwd.hip", "sched.hip"), "bwd_dkdv": ("attn_bwd.hip", "sched.hip"),
+           "bwd_dq": ("attn_bwd.hip", "sched.hip"), "router_lse": ("router.hip",), "router_scores": ("router.hip",)}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 
 
@@ -143,7 +144,7 @@ def describe(w):
 def source_hash(kernel):
     import hashlib
     h = hashlib.sha256()
-    for name in (SOURCES[kernel], "common.h"):
+    for name in SOURCES[kernel] + ("common.h",):
         with open(os.path.join(ROOT, "video_dit_trainable_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
