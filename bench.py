@@ -305,7 +305,7 @@ def main():
     total_ms = t_start.elapsed_time(t_stop)
     ms_step = total_ms / args.steps
     per = {n: float(np.median([evs[s][i].elapsed_time(evs[s][i + 1]) for s in range(args.steps)]))
-           for i, n in enumerate(names)}
+           for i, n in enumerate(names) if w.train or n not in ("coarse_gate_bwd", "fine_bwd")}
     log("per-call ms: " + ", ".join(f"{n} {t:.3f}" for n, t in per.items()))
     steps_ms = [evs[s][0].elapsed_time(evs[s][7]) for s in range(args.steps)]
     step_dist = {"median": round(float(np.median(steps_ms)), 3), "min": round(float(np.min(steps_ms)), 3),
@@ -370,6 +370,8 @@ def main():
 
     ops = {n: {"ms": round(t, 4)} for n, t in per.items()}
     for n, key in (("fine_fwd", "fine_fwd"), ("fine_bwd", "fine_bwd"), ("route", "router")):
+        if n not in per:        # the backward calls of a forward-only step
+            continue
         ops[n]["tflops"] = round(fl[key] / (per[n] * 1e-3) / 1e12, 2)
         ops[n]["pct_bf16_peak"] = round(100 * fl[key] / (per[n] * 1e-3) / PEAK_BF16, 2)
     # the router and TopK as a fraction of HBM bandwidth, on the bytes they move

@@ -126,8 +126,13 @@ int vsa2_workspace_size(const vsa2_problem* p, int32_t op, int32_t topk, int32_t
  * Built for 64-token blocks without text rows; with block_tokens = 128 (each
  * workgroup already stages every tile for the block's two cubes) or
  * text_tokens > 0 the size is 0 and the kernels run one workgroup per block.
+ * A schedule built for another selection of the same problem is still valid
+ * (it lists every cube once), only balanced for that selection; a buffer that
+ * no build for this problem wrote is recognised by its header, and the fine
+ * kernels then take the cubes in plain order, with the same results.
  * Layout (opaque to callers): for query cubes, then KV cubes, a 256-byte
- * header and batch*heads*nb int32 items. */
+ * header (queue starts and lengths, the item count, a marker) and
+ * batch*heads*nb int32 items. */
 int vsa2_sched_size(const vsa2_problem* p, int32_t topk, size_t* bytes);
 
 /* Bytes of the `pooled` buffer written by vsa2_pool (see there). */
@@ -253,7 +258,7 @@ int vsa2_topk_per_row(const vsa2_problem* p, const float* scores, int32_t topk, 
  * over its selected KV cubes only (-inf mask elsewhere, §2.1).
  *   row_ptr, col_idx: the selection (CSR as above, k = vsa2_budget(topk)).
  *   sched: the schedule the call that produced this selection wrote, or NULL
- *     (one workgroup per query cube, results equal).
+ *     (one workgroup per query cube, results equal); vsa2_sched_size() bytes.
  *   o_f (written): storage dtype [batch, heads, L, d].
  *   lse (written): fp32 [batch, heads, L], natural-log log-sum-exp of the scaled
  *     scores of each query over its selected keys (kept for the backward).

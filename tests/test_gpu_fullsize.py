@@ -52,7 +52,9 @@ def _run(w, topk, train, fine_on="seeded"):
     coarse branch, gate and backward then run on a seeded selection with the
     exact budget (make_selection, fine_on="seeded"), or, as the benchmark
     runs them, on the router's own selection (fine_on="routed"); the oracle is
-    given the same selection."""
+    given the same selection.  The fine kernels run through the work schedule
+    that TopK (or set_selection) built for that selection, as in the
+    benchmark."""
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     dev = _dev()
@@ -63,7 +65,7 @@ def _run(w, topk, train, fine_on="seeded"):
     vsa2.vsa2_pool(p, q, k, v, layer.pooled)
     vsa2.vsa2_route(p, layer.pooled, layer.scores, layer.ws)
     vsa2.vsa2_topk_per_seq(p, layer.scores, topk, layer.row_ptr, layer.col_idx, layer.col_ptr, layer.row_idx,
-                           layer.ws)
+                           layer.ws, sched=layer.sched)
     torch.cuda.synchronize()
     out = dict(w=w, topk=topk, q=q, k=k, v=v, x=x, w_g=w_g, layer=layer,
                routed=[t.clone() for t in (layer.row_ptr, layer.col_idx, layer.col_ptr, layer.row_idx)])
@@ -81,7 +83,8 @@ def _run(w, topk, train, fine_on="seeded"):
                                   g["dw_g"], layer.ws)
         # fine-branch gradients alone (no coarse rows added) for the sampled checks
         vsa2.vsa2_sparse_attn_bwd(p, topk, q, k, v, layer.o_f, layer.lse, d_o, layer.row_ptr, layer.col_idx,
-                                  layer.col_ptr, layer.row_idx, None, g["dq"], g["dk"], g["dv"], layer.ws)
+                                  layer.col_ptr, layer.row_idx, None, g["dq"], g["dk"], g["dv"], layer.ws,
+                                  sched=layer.sched)
         out["d_o"] = d_o
     torch.cuda.synchronize()
     return out

@@ -13,7 +13,9 @@ to that XCD's queue.  Checked here:
     results bit for bit (an item is computed the same way whoever takes it)
     and the oracle's;
   * that building it and running through it is bitwise reproducible;
-  * odd cube counts, empty lists and padded grids.
+  * odd cube counts, empty lists and padded grids;
+  * that a buffer no build wrote (zeros, random bytes) and a schedule built
+    for another selection still give the per-cube results bit for bit.
 """
 
 import numpy as np
@@ -34,6 +36,7 @@ PAD = Workload("pad", 18, (7, 15, 30), 1, 3, 64, "bf16", 6, "lowrank", skew=True
 SHORT = WORKLOADS["short"]                                                                    # nb = 512, 20 heads
 CASES = [MID, ODD, PAD]
 OVH = 4   # the schedule's fixed cost of an item, in list entries
+MAGIC = 0x53434844  # header word 17 of a built side, beside the item count in word 16
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -53,14 +56,16 @@ def _up(x):
 
 def decode(layer):
     """The schedule buffer as numpy: per side (query cubes, KV cubes) the
-    header (queue starts [8], queue lengths [8]) and the item array."""
+    header (queue starts [8], queue lengths [8], item count, marker) and the
+    item array."""
     n_items = layer.bh * layer.nb
     raw = layer.sched.cpu().numpy()
     side = 256 + _up(n_items * 4)
     assert layer.sched.numel() >= 2 * side
     out = []
     for off in (0, side):
-        hdr = raw[off:off + 64].view(np.int32)
+        hdr = raw[off:off + 72].view(np.int32)
+        assert hdr[16] == n_items and hdr[17] == MAGIC, "header count / marker"
         items = raw[off + 256:off + 256 + n_items * 4].view(np.int32)
         out.append((hdr[:8].copy(), hdr[8:16].copy(), items.copy()))
     return out
@@ -190,3 +195,44 @@ def test_scheduled_backward_is_deterministic():
         runs.append(g)
     for a, b in zip(*runs):
         assert torch.equal(a, b)
+
+
+def _fine(p, w, layer, q, k, v, d_o, sched):
+    o_f, lse = torch.empty_like(layer.o_f), torch.empty_like(layer.lse)
+    vsa2.vsa2_sparse_attn_fwd(p, w.topk, q, k, v, layer.row_ptr, layer.col_idx, o_f, lse, layer.ws, sched=sched)
+    g = [torch.full_like(q, float("nan")) for _ in range(3)]
+    vsa2.vsa2_sparse_attn_bwd(p, w.topk, q, k, v, o_f, lse, d_o, layer.row_ptr, layer.col_idx, layer.col_ptr,
+                              layer.row_idx, None, *g, layer.ws, sched=sched)
+    torch.cuda.synchronize()
+    return [o_f, lse] + g
+
+
+@pytest.mark.parametrize("w", [MID, PAD], ids=lambda w: w.name)
+def test_unbuilt_or_stale_schedule_gives_the_same_results(w):
+    """The fine kernels check the header's item count and marker: a buffer
+    that no build wrote makes them take the cubes in plain order, and a
+    schedule of another selection still lists every cube once."""
+    dev = _dev()
+    q, k, v = make_qkv(w, device=dev)
+    d_o = make_grad_out(w, device=dev)
+    p, layer = _layer(w, dev)
+    names = ("O_f", "LSE", "dQ", "dK", "dV")
+    # selection A builds the schedule; selection B (the router's) replaces the
+    # lists without touching it
+    layer.set_selection(*make_selection(w, device=dev))
+    vsa2.vsa2_pool(p, q, k, v, layer.pooled)
+    vsa2.vsa2_route(p, layer.pooled, layer.scores, layer.ws)
+    vsa2.vsa2_topk_per_seq(p, layer.scores, w.topk, layer.row_ptr, layer.col_idx, layer.col_ptr, layer.row_idx,
+                           layer.ws)
+    want = _fine(p, w, layer, q, k, v, d_o, None)
+    got = _fine(p, w, layer, q, k, v, d_o, layer.sched)
+    for nm, a, b in zip(names, want, got):
+        assert torch.equal(a, b), f"{nm}: a schedule of another selection changed the result"
+    gen = torch.Generator().manual_seed(5)
+    for label, fill in (("zeros", torch.zeros(layer.sched.numel(), dtype=torch.uint8)),
+                        ("random bytes", torch.randint(0, 256, (layer.sched.numel(),), generator=gen,
+                                                       dtype=torch.uint8))):
+        layer.sched.copy_(fill.to(dev))
+        got = _fine(p, w, layer, q, k, v, d_o, layer.sched)
+        for nm, a, b in zip(names, want, got):
+            assert torch.equal(a, b), f"{nm}: an unbuilt schedule buffer ({label}) changed the result"

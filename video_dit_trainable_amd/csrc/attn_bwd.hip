@@ -174,7 +174,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(const T* __restrict__ q, co
   bool textk = false;  // a text KV cube
   if constexpr (SCHED) {
     __syncthreads();  // every wave is done with the previous item's tiles and s_item
-    if (threadIdx.x == 0) s_item = sched_take(sk_hdr, sk_items, sk_ctr);
+    if (threadIdx.x == 0) s_item = sched_take(sk_hdr, sk_items, sk_ctr, nbh * nkv);
     __syncthreads();
     const int code = s_item;
     if (code < 0) break;
@@ -519,7 +519,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(const T* __restrict__ q, cons
   bool textq = false;  // a text query cube
   if constexpr (SCHED) {
     __syncthreads();  // every wave is done with the previous item's tiles and s_item
-    if (threadIdx.x == 0) s_item = sched_take(sq_hdr, sq_items, sq_ctr);
+    if (threadIdx.x == 0) s_item = sched_take(sq_hdr, sq_items, sq_ctr, nbh * nq);
     __syncthreads();
     const int code = s_item;
     if (code < 0) break;

@@ -66,7 +66,7 @@ __global__ __launch_bounds__(128 * QB, 2) void k_attn_fwd(const T* __restrict__ 
   bool textq = false;  // a text query cube
   if constexpr (SCHED) {
     __syncthreads();  // every wave is done with the previous item's tiles and s_item
-    if (threadIdx.x == 0) s_item = sched_take(sq_hdr, sq_items, sq_ctr);
+    if (threadIdx.x == 0) s_item = sched_take(sq_hdr, sq_items, sq_ctr, nbh * nq);
     __syncthreads();
     const int code = s_item;
     if (code < 0) break;

@@ -555,18 +555,37 @@ __device__ inline uint32_t block_scan_1024(uint32_t x, uint32_t& total, uint32_t
   return r;
 }
 
+// Written by the schedule build into word 17 of each side's header, beside
+// the item count in word 16.
+constexpr int32_t SCHED_MAGIC = 0x53434844;
+
 // Next work item of the schedule for this workgroup: from the queue of its
 // XCD (workgroup b runs on XCD b mod 8), then from the others in turn; -1
-// when every queue is empty.  hdr = {queue starts[8], queue lengths[8]}; ctr
-// = one counter per queue, zero before the launch.  Called by one thread.
-__device__ inline int sched_take(const int32_t* __restrict__ hdr, const int32_t* __restrict__ items, int32_t* ctr) {
+// when every queue is empty.  hdr = {queue starts[8], queue lengths[8], item
+// count, SCHED_MAGIC}; ctr = one counter per queue, zero before the launch;
+// total = the launch's item count.  A header that no build of this size
+// wrote (a buffer never built, or built for another problem) makes the
+// workgroups take the items 0..total-1 in plain order off ctr[0], so every
+// item still runs once; queue slots and items outside [0, total) are never
+// dereferenced or returned.  Called by one thread.
+__device__ inline int sched_take(const int32_t* __restrict__ hdr, const int32_t* __restrict__ items, int32_t* ctr,
+                                 int total) {
+  if (hdr[16] != total || hdr[17] != SCHED_MAGIC) {
+    const int t = atomicAdd(&ctr[0], 1);
+    return t < total ? t : -1;
+  }
   const int x0 = (int)(blockIdx.x & 7u);
   for (int s = 0; s < 8; ++s) {
     const int x = (x0 + s) & 7;
     const int len = hdr[8 + x];
     if (__hip_atomic_load(&ctr[x], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= len) continue;
     const int t = atomicAdd(&ctr[x], 1);
-    if (t < len) return items[hdr[x] + t];
+    if (t < len) {
+      const int at = hdr[x] + t;
+      if ((unsigned)at >= (unsigned)total) return -1;
+      const int item = items[at];
+      return (unsigned)item < (unsigned)total ? item : -1;
+    }
   }
   return -1;
 }

@@ -176,9 +176,10 @@ __global__ __launch_bounds__(256) void k_sched_place(const uint8_t* __restrict__
 
 // Queue offsets: queue x holds, for every (batch, head) in turn, that head's
 // range for XCD x.  hdr[x] = start of queue x in the item array, hdr[8 + x]
-// its length; hoff[bh][x] = where (batch, head) bh's range starts.
+// its length, hdr[16] the item count bh * n and hdr[17] SCHED_MAGIC;
+// hoff[bh][x] = where (batch, head) bh's range starts.
 __global__ __launch_bounds__(64) void k_sched_queues(const int32_t* __restrict__ cnt, int32_t* __restrict__ hdr,
-                                                     int32_t* __restrict__ hoff, int bh) {
+                                                     int32_t* __restrict__ hoff, int bh, int n) {
   __shared__ int tot[8];
   const int x = threadIdx.x;
   if (x < 8) {
@@ -192,6 +193,10 @@ __global__ __launch_bounds__(64) void k_sched_queues(const int32_t* __restrict__
     for (int y = 0; y < x; ++y) head += tot[y];
     hdr[x] = head;
     hdr[8 + x] = tot[x];
+    if (x == 0) {  // what the fine kernels check before trusting the queues
+      hdr[16] = bh * n;
+      hdr[17] = SCHED_MAGIC;
+    }
     int o = head;
     for (int h = 0; h < bh; ++h) {
       hoff[(size_t)h * 8 + x] = o;
@@ -233,7 +238,7 @@ static hipError_t build_side(const int32_t* ptr, const int32_t* idx, int32_t* hd
                      a.cnt, n);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_sched_queues, dim3(1), dim3(64), 0, st, a.cnt, hdr, a.hoff, a.bh);
+  hipLaunchKernelGGL(k_sched_queues, dim3(1), dim3(64), 0, st, a.cnt, hdr, a.hoff, a.bh, n);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_sched_fill, dim3((n + 255) / 256, a.bh), dim3(256), 0, st, a.tmp, a.cnt, a.hoff, items, n);
