@@ -97,7 +97,20 @@ typedef struct vsa2_problem {
   float softmax_scale;    /* <= 0 selects 1/sqrt(head_dim)                            */
   int32_t block_tokens;   /* attention block B: 64 (0 selects it) or 128, see above   */
   int32_t text_tokens;    /* MMDiT text tokens Nt >= 0 joining the fine branch, above */
+  int32_t router_pool;    /* edge of the router's pooling window, below: 2 (0 selects */
+                          /* it), 1 or 4; anything else is VSA2_E_SHAPE               */
 } vsa2_problem;
+
+/* The router's pooling window (paper §2.2 Eq.(5), R = pool^3 tokens, G = 64 / R
+ * pooled tokens per cube).  2: the 2x2x2 windows the method uses (R = 8, G =
+ * 8).  The two ends exist for the special cases the paper names: 1 (R = 1, G
+ * = 64) makes the router the token-level softmax averaged over each 64 x 64
+ * tile, i.e. the oracle block scores P_oracle of Eq.(10)-(11); 4 (R = 64, G =
+ * 1) makes it the coarse branch's P_c of Eq.(2).  Pools 1 and 4 need 64-token
+ * blocks on an unpadded grid (vsa2_pool and vsa2_route return
+ * VSA2_E_UNSUPPORTED otherwise); they cost more (pool 1 runs the router over
+ * every token, with an nb*8 x nb*8 intermediate in the workspace) and serve
+ * checks, not training. */
 
 /* Human-readable name of a status code (static string). */
 const char* vsa2_status_string(int status);
@@ -146,11 +159,13 @@ int vsa2_saved_size(const vsa2_problem* p, size_t* bytes);
  * sequence). */
 int vsa2_budget(const vsa2_problem* p, int32_t topk, int64_t* k);
 
-/* Mean pooling of the router (Eq.(5), windows of 8 tokens) and of the coarse
- * branch (Eq.(1), cubes of 64 tokens), one read of Q, K, V.
+/* Mean pooling of the router (Eq.(5), windows of R = router_pool^3 tokens) and
+ * of the coarse branch (Eq.(1), cubes of 64 tokens), one read of Q, K, V.
  *   pooled (written), in order, each [batch, heads, rows, d] in the storage dtype:
- *     Q_r, K_r    rows = L/8   (router operands; bf16 storage rounds the fp32 mean
- *                               to nearest-even, the router's stated precision)
+ *     Q_r, K_r    rows = L/R   (router operands; bf16 storage rounds the fp32 mean
+ *                               to nearest-even, the router's stated precision;
+ *                               pool 1 copies the tokens; pool 4 has no rows here,
+ *                               its router operands are Q_c, K_c)
  *     Q_c, K_c, V_c rows = nbp = nb rounded up to a multiple of 64; rows >= nb are 0
  *   Size from vsa2_pooled_size(). */
 int vsa2_pool(const vsa2_problem* p, const void* q, const void* k, const void* v,
@@ -160,9 +175,13 @@ int vsa2_pool(const vsa2_problem* p, const void* q, const void* k, const void* v
  * (log-sum-exp, then softmax + G x G mean pooling), P_hat_r never stored.
  *   pooled: from vsa2_pool.
  *   scores (written): fp32 [batch, heads, nb, nb], P_r[i][j] = mean over the
- *     8 x 8 pooled (query, key) pairs of cubes i, j of softmax_b(q_a.k_b*scale).
- *     Every row sums to 1/8 (padded grids: to the number of the cube's 2x2x2
- *     windows that hold a real token, over 64).
+ *     G x G pooled (query, key) pairs of cubes i, j of softmax_b(q_a.k_b*scale).
+ *     Every row sums to 1/G (padded grids: to the number of the cube's 2x2x2
+ *     windows that hold a real token, over 64).  Pool 1: the passes run over
+ *     the tokens with 8 x 8 means per pair of 2x2x2 sub-cubes, written to the
+ *     workspace, and a third kernel averages each 8 x 8 block of those into
+ *     P_r (the mean of means of equal-sized groups is the 64 x 64 mean).
+ *     Pool 4: P_c, as vsa2_route_coarse computes it.
  *   ws: vsa2_workspace_size(VSA2_OP_ROUTE). */
 int vsa2_route(const vsa2_problem* p, const void* pooled, float* scores,
                void* ws, size_t ws_bytes, void* stream);

@@ -177,3 +177,39 @@ def test_schedule_size_and_checks():
     assert L.vsa2_topk_per_seq(ctypes.byref(p), A, 5, B, C, D, A, B + 16, ss, C, need, None) == vsa2.VSA2_E_ARG
     assert L.vsa2_plan_from_csr(ctypes.byref(p), 5, A, B, C, D, B + 16, ss, C, 1 << 30, None) == vsa2.VSA2_E_ARG
     assert L.vsa2_sparse_attn_fwd(ctypes.byref(p), 5, A, B, C, D, A, B + 16, C, D, None, 0, None) == vsa2.VSA2_E_ARG
+
+
+def test_router_pool_sizes_and_refusals():
+    """Router pools 1 (every token) and 4 (one pooled token per cube, the
+    coarse operands) beside the method's 2: pooled rows, workspace, and the
+    problems they refuse (padded grids, 128-token blocks, other edges)."""
+    L = vsa2.lib()
+    up = lambda x: (x + 255) // 256 * 256
+    grid, bh, d, esz, nb, nbp, tok = (8, 16, 16), 2, 64, 4, 32, 64, 2048
+    pr = {r: vsa2.problem(1, 2, d, grid, "f32", router_pool=r) for r in (1, 2, 4)}
+    assert vsa2.pooled_size(pr[2]) == bh * (2 * (tok // 8) + 3 * nbp) * d * esz
+    assert vsa2.pooled_size(pr[1]) == bh * (2 * tok + 3 * nbp) * d * esz     # the tokens themselves
+    assert vsa2.pooled_size(pr[4]) == bh * (3 * nbp) * d * esz               # no router rows
+    assert vsa2.workspace_size(pr[2], vsa2.OP_ROUTE) == up(bh * (tok // 8) * 4)
+    # pool 1: the LSE of every token, then the means over sub-cube pairs
+    assert vsa2.workspace_size(pr[1], vsa2.OP_ROUTE) == up(bh * tok * 4) + up(bh * (8 * nb) ** 2 * 4)
+    assert vsa2.workspace_size(pr[4], vsa2.OP_ROUTE) == up(bh * nb * 4)
+    # everything the router does not feed is unchanged
+    for op in (vsa2.OP_TOPK, vsa2.OP_FWD, vsa2.OP_BWD):
+        assert vsa2.workspace_size(pr[1], op) == vsa2.workspace_size(pr[2], op) == vsa2.workspace_size(pr[4], op)
+    for bad in (3, 8, -1):
+        with pytest.raises(vsa2.Vsa2Error) as e:
+            vsa2.pooled_size(vsa2.problem(1, 2, d, grid, "f32", router_pool=bad))
+        assert e.value.code == vsa2.VSA2_E_SHAPE
+    # pools 1 and 4 need 64-token blocks on an unpadded grid; refused before anything runs
+    for r in (1, 4):
+        for p in (vsa2.problem(1, 2, d, (7, 13, 14), "f32", router_pool=r),
+                  vsa2.problem(1, 2, d, (8, 16, 32), "f32", block=128, router_pool=r)):
+            assert L.vsa2_pool(ctypes.byref(p), A, B, C, D, None) == vsa2.VSA2_E_UNSUPPORTED
+            assert L.vsa2_route(ctypes.byref(p), A, B, C, 1 << 40, None) == vsa2.VSA2_E_UNSUPPORTED
+            assert L.vsa2_route_noalloc(ctypes.byref(p), A, B, None) == vsa2.VSA2_E_UNSUPPORTED
+    # pool 1 keeps its sub-cube intermediate within int32 indices: 8 nb <= 46,340
+    big = vsa2.problem(1, 1, d, (48, 52, 144), "f32", router_pool=1)      # 5,616 cubes: allowed
+    assert L.vsa2_route(ctypes.byref(big), A, B, C, 0, None) == vsa2.VSA2_E_WORKSPACE
+    huge = vsa2.problem(1, 1, d, (100, 100, 100), "f32", router_pool=1)   # 15,625 cubes: refused
+    assert L.vsa2_route(ctypes.byref(huge), A, B, C, 1 << 40, None) == vsa2.VSA2_E_UNSUPPORTED

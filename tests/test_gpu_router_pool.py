@@ -1,0 +1,113 @@
+"""The router's two special cases on the GPU, through the C-ABI.
+
+[VSA2] §2.2: with a pooling window of one token (R = 1, G = 64) the router's
+block scores are the token-level softmax averaged over each 64 x 64 tile,
+P_oracle of Eq.(10)-(11); with a window of a whole cube (R = 64, G = 1) they
+are the coarse branch's P_c of Eq.(2).  `vsa2_problem.router_pool` selects
+the window, and both ends are checked here against the textbook dense
+computation in fp64 (oracle_block_scores: one softmax over all tokens, then
+64 x 64 means), against the oracle's router at the same window, through the
+row sums 1/G, and (R = 64) bit for bit against `vsa2_route_coarse`.  The
+selection TopK makes from the R = 1 scores is the exact top k of P_oracle
+outside the 1e-3 band.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import gpu_util as gu
+from oracle import vsa2_oracle as orc
+from video_dit_trainable_amd import vsa2
+from video_dit_trainable_amd.configs import Workload
+from video_dit_trainable_amd.inputs import make_qkv
+
+pytestmark = pytest.mark.gpu
+
+SMALL = Workload("pool-small", 41, (8, 8, 16), 1, 2, 64, "f32", 4, "lowrank")       # 16 cubes
+SMALLB = Workload("pool-small-b", 42, (8, 8, 16), 1, 2, 64, "bf16", 4, "lowrank")
+ODD = Workload("pool-odd", 43, (4, 12, 20), 1, 2, 128, "bf16", 5, "lowrank", skew=True)  # 15 cubes
+CASES = [SMALL, SMALLB, ODD]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    vsa2.lib()
+
+
+def _dev():
+    return torch.device("cuda:0")
+
+
+def _route(w, pool, q, k, v):
+    """Pool + route with router window ``pool``; returns (scores, problem, buffers)."""
+    dev = _dev()
+    p = vsa2.problem(w.batch, w.heads, w.head_dim, w.grid, w.dtype, router_pool=pool)
+    pooled = torch.empty(vsa2.pooled_size(p), dtype=torch.uint8, device=dev)
+    ws = torch.empty(max(vsa2.workspace_size(p, vsa2.OP_ROUTE), 256), dtype=torch.uint8, device=dev)
+    scores = torch.full((w.batch, w.heads, w.nb, w.nb), float("nan"), dtype=torch.float32, device=dev)
+    vsa2.vsa2_pool(p, q, k, v, pooled)
+    vsa2.vsa2_route(p, pooled, scores, ws)
+    torch.cuda.synchronize()
+    return scores, p, pooled
+
+
+@pytest.mark.parametrize("w", CASES, ids=lambda w: w.name)
+def test_pool1_router_is_the_token_level_block_mean(w):
+    q, k, v = make_qkv(w, device=_dev())
+    scores, _, _ = _route(w, 1, q, k, v)
+    got = scores[0].double().cpu().numpy()
+    assert np.all(np.isfinite(got))
+    # every row of a cube holds 64 queries whose softmaxes each sum to 1: 64 / 64^2
+    np.testing.assert_allclose(got.sum(axis=2), 1.0 / 64.0, rtol=1e-5)
+    for h in range(w.heads):
+        qh, kh = gu.f64(q[0, h]), gu.f64(k[0, h])
+        want = orc.oracle_block_scores(qh, kh, w.grid)               # dense softmax, then 64 x 64 means
+        for i in range(w.nb):
+            assert gu.rel_l2(got[h, i], want[i]) <= 1e-4, f"head {h} row {i}"
+        # the oracle's router at the same window agrees (pooling one token is the identity)
+        np.testing.assert_allclose(orc.router_scores(qh, kh, w.grid, pool=(1, 1, 1)), want, rtol=1e-10, atol=1e-15)
+
+
+@pytest.mark.parametrize("w", CASES, ids=lambda w: w.name)
+def test_pool4_router_is_the_coarse_softmax(w):
+    q, k, v = make_qkv(w, device=_dev())
+    scores, _, _ = _route(w, 4, q, k, v)
+    got = scores[0].double().cpu().numpy()
+    np.testing.assert_allclose(got.sum(axis=2), 1.0, rtol=1e-5)      # G = 1: each row is a softmax
+    bf16 = w.dtype == "bf16"
+    for h in range(w.heads):
+        want = orc.router_scores(gu.f64(q[0, h]), gu.f64(k[0, h]), w.grid, pool=(4, 4, 4), bf16_pooled=bf16)
+        for i in range(w.nb):
+            assert gu.rel_l2(got[h, i], want[i]) <= 1e-4, f"head {h} row {i}"
+    # the same numbers as the VSA router baseline's P_c, from the method's own pooled buffer
+    p2 = vsa2.problem(w.batch, w.heads, w.head_dim, w.grid, w.dtype)
+    pooled = torch.empty(vsa2.pooled_size(p2), dtype=torch.uint8, device=_dev())
+    ws = torch.empty(max(vsa2.workspace_size(p2, vsa2.OP_ROUTE_COARSE), 256), dtype=torch.uint8, device=_dev())
+    pc = torch.empty_like(scores)
+    vsa2.vsa2_pool(p2, q, k, v, pooled)
+    vsa2.vsa2_route_coarse(p2, pooled, pc, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(pc, scores)
+
+
+def test_topk_on_pool1_scores_is_the_oracle_selection():
+    w = ODD
+    dev = _dev()
+    q, k, v = make_qkv(w, device=dev)
+    scores, p, _ = _route(w, 1, q, k, v)
+    kk = vsa2.budget(p, w.topk)
+    i32 = dict(dtype=torch.int32, device=dev)
+    rp, cp = (torch.empty((1, w.heads, w.nb + 1), **i32) for _ in range(2))
+    ci, ri = (torch.empty((1, w.heads, kk), **i32) for _ in range(2))
+    ws = torch.empty(vsa2.workspace_size(p, vsa2.OP_TOPK), dtype=torch.uint8, device=dev)
+    vsa2.vsa2_topk_per_seq(p, scores, w.topk, rp, ci, cp, ri, ws)
+    torch.cuda.synchronize()
+    gu.check_csr_csc(rp[0], ci[0], cp[0], ri[0], w.nb, kk)
+    for h in range(w.heads):
+        want = orc.oracle_block_scores(gu.f64(q[0, h]), gu.f64(k[0, h]), w.grid)
+        mask = orc.csr_to_mask(rp[0, h].cpu().numpy(), ci[0, h].cpu().numpy(), w.nb)
+        outside, band, _ = gu.band_compare(mask, want, kk)
+        assert outside == 0, f"head {h}: {outside} mismatches outside the band ({band} pairs in it)"

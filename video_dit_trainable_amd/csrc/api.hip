@@ -21,7 +21,8 @@ size_t up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
 // of the selection, the coarse tokens), nc the 4x4x4 cubes the kernels tile
 // over; nb = nc >> bs with 2^bs cubes per block.
 struct Dims {
-  int batch, heads, bh, d, L, nb, nbp, Lr;
+  int batch, heads, bh, d, L, nb, nbp, Lr;  // Lr: router rows per head in the pooled buffer
+  int rp;                                    // router pool edge: 1, 2 or 4
   int nc, bs;
   int nt, ntc, ld;  // MMDiT text tokens, their 64-row cubes, token rows per head (L + 64 ntc)
   bool bf16;
@@ -39,6 +40,7 @@ int check_problem(const vsa2_problem* p, Dims& o) {
   if (p->dtype != VSA2_F32 && p->dtype != VSA2_BF16) return VSA2_E_ARG;
   if (p->block_tokens != 0 && p->block_tokens != 64 && p->block_tokens != 128) return VSA2_E_SHAPE;
   if (p->text_tokens < 0 || p->text_tokens > (1 << 20)) return VSA2_E_SHAPE;
+  if (p->router_pool != 0 && p->router_pool != 1 && p->router_pool != 2 && p->router_pool != 4) return VSA2_E_SHAPE;
   const int bs = p->block_tokens == 128 ? 1 : 0;  // a 128-token block is two x-adjacent cubes
   // a grid that is not a whole number of blocks is padded up to one
   const int64_t xs = 4 << bs;
@@ -67,7 +69,8 @@ int check_problem(const vsa2_problem* p, Dims& o) {
   o.nt = p->text_tokens;
   o.ntc = (p->text_tokens + 63) / 64;
   o.ld = o.L + 64 * o.ntc;
-  o.Lr = (int)(L / 8);
+  o.rp = p->router_pool ? p->router_pool : 2;
+  o.Lr = o.rp == 1 ? (int)L : (o.rp == 2 ? (int)(L / 8) : 0);  // pool 4 routes on Q_c, K_c
   o.bf16 = p->dtype == VSA2_BF16;
   o.esz = o.bf16 ? 2 : 4;
   o.scale = p->softmax_scale > 0.f ? p->softmax_scale : 1.0f / std::sqrt((float)p->head_dim);
@@ -95,8 +98,11 @@ int bitmap_words(const Dims& d) { return 2 * ((d.nb + 63) / 64); }
 
 // Workspace layouts --------------------------------------------------------
 // per-row LSE, then (padded grids) one existence word per 64 pooled keys
-size_t ws_route_lse(const Dims& d) { return up((size_t)d.bh * d.Lr * 4); }
+// pool 1: then the 8 x 8 sub-cube means [bh, 8 nc, 8 nc]; pool 4: the LSE of the
+// coarse rows (as vsa2_route_coarse)
+size_t ws_route_lse(const Dims& d) { return up((size_t)d.bh * (d.rp == 4 ? d.nb : d.Lr) * 4); }
 size_t ws_route(const Dims& d) {
+  if (d.rp == 1) return ws_route_lse(d) + up((size_t)d.bh * 64 * d.nc * d.nc * 4);
   return ws_route_lse(d) + (d.pad.on ? up((size_t)(d.Lr + 63) / 64 * 8) : 0);
 }
 
@@ -283,6 +289,34 @@ Pooled pooled_ptrs(const Dims& d, const void* base) {
   const size_t r = (size_t)d.bh * d.Lr * d.d * d.esz;
   const size_t c = (size_t)d.bh * d.nbp * d.d * d.esz;
   return Pooled{b, b + r, b + 2 * r, b + 2 * r + c, b + 2 * r + 2 * c};
+}
+
+// Pools 1 and 4 serve 64-token blocks on unpadded grids; pool 1's sub-cube
+// intermediate has (8 nc)^2 entries per head, kept within int32 indices.
+bool route_supported(const Dims& d) {
+  if (d.rp == 2) return true;
+  if (d.pad.on || d.bs) return false;
+  return d.rp == 4 || 8 * (int64_t)d.nc <= 46340;
+}
+
+// The router launches of vsa2_route / vsa2_route_noalloc for every pool.
+hipError_t route_launch(const Dims& d, const void* pooled, float* scores, void* ws, hipStream_t st) {
+  Pooled pp = pooled_ptrs(d, pooled);
+  const float sl2 = d.scale * 1.4426950408889634f;
+  if (d.rp == 4) {  // one pooled token per cube: the coarse operands, and P_r = P_c
+    RouteArgs a{pp.qc, pp.kc, (float*)ws, scores, d.bh, d.nb, d.d, d.bf16, sl2, PadGrid{}, nullptr, 0, 1, d.nbp};
+    return launch_route(a, st);
+  }
+  if (d.rp == 1) {  // every token: 8 x 8 means over sub-cube pairs, then 8 x 8 blocks of those
+    float* sub = (float*)((char*)ws + ws_route_lse(d));
+    RouteArgs a{pp.qr, pp.kr, (float*)ws, sub, d.bh, 8 * d.nc, d.d, d.bf16, sl2, PadGrid{}, nullptr, 0};
+    hipError_t e = launch_route(a, st);
+    if (e != hipSuccess) return e;
+    return launch_route_fold(sub, scores, d.bh, d.nc, st);
+  }
+  RouteArgs a{pp.qr, pp.kr, (float*)ws, scores, d.bh, d.nc, d.d, d.bf16, sl2, d.pad,
+              d.pad.on ? (uint64_t*)((char*)ws + ws_route_lse(d)) : nullptr, d.bs};
+  return launch_route(a, st);
 }
 
 // Diagnostic kernel timer ----------------------------------------------------
@@ -482,10 +516,11 @@ int vsa2_pool(const vsa2_problem* p, const void* q, const void* k, const void* v
   Dims d;
   int s = check_problem(p, d);
   if (s) return s;
+  if (!route_supported(d)) return VSA2_E_UNSUPPORTED;
   if (!aligned(q) || !aligned(k) || !aligned(v) || !aligned(pooled)) return VSA2_E_ARG;
   Pooled pp = pooled_ptrs(d, pooled);
   PoolArgs a{q, k, v, (void*)pp.qr, (void*)pp.kr, (void*)pp.qc, (void*)pp.kc, (void*)pp.vc, d.bh, d.nc, d.nbp, d.d,
-             d.bf16, d.pad, d.bs, d.ld};
+             d.bf16, d.pad, d.bs, d.ld, d.rp};
   return hip_status(launch_pool(a, (hipStream_t)stream));
 }
 
@@ -493,12 +528,10 @@ int vsa2_route(const vsa2_problem* p, const void* pooled, float* scores, void* w
   Dims d;
   int s = check_problem(p, d);
   if (s) return s;
+  if (!route_supported(d)) return VSA2_E_UNSUPPORTED;
   if (!aligned(pooled) || !aligned(scores)) return VSA2_E_ARG;
   if ((s = check_ws(ws, ws_bytes, ws_route(d)))) return s;
-  Pooled pp = pooled_ptrs(d, pooled);
-  RouteArgs a{pp.qr, pp.kr, (float*)ws, scores, d.bh, d.nc, d.d, d.bf16, d.scale * 1.4426950408889634f, d.pad,
-              d.pad.on ? (uint64_t*)((char*)ws + ws_route_lse(d)) : nullptr, d.bs};
-  return hip_status(launch_route(a, (hipStream_t)stream));
+  return hip_status(route_launch(d, pooled, scores, ws, (hipStream_t)stream));
 }
 
 int vsa2_route_noalloc(const vsa2_problem* p, const void* pooled, float* scores, void* stream) {
@@ -506,16 +539,15 @@ int vsa2_route_noalloc(const vsa2_problem* p, const void* pooled, float* scores,
   int s = check_problem(p, d);
   if (s) return s;
   if (!aligned(pooled) || !aligned(scores)) return VSA2_E_ARG;
+  if (!route_supported(d)) return VSA2_E_UNSUPPORTED;
   const size_t need = ws_route(d);
   if (need > SCRATCH_BYTES) return VSA2_E_SCRATCH;
   void* ws = nullptr;
   if (scratch_address(&ws) != hipSuccess) return VSA2_E_HIP;
   // the router's scratch is written before it is read (the per-row LSE by
-  // pass 1, the key-existence words by their own kernel), so nothing is cleared
-  Pooled pp = pooled_ptrs(d, pooled);
-  RouteArgs a{pp.qr, pp.kr, (float*)ws, scores, d.bh, d.nc, d.d, d.bf16, d.scale * 1.4426950408889634f, d.pad,
-              d.pad.on ? (uint64_t*)((char*)ws + ws_route_lse(d)) : nullptr, d.bs};
-  return hip_status(launch_route(a, (hipStream_t)stream));
+  // pass 1, the key-existence words by their own kernel, pool 1's sub-cube
+  // means by pass 2), so nothing is cleared
+  return hip_status(route_launch(d, pooled, scores, ws, (hipStream_t)stream));
 }
 
 int vsa2_route_noalloc_limit(size_t* bytes) {

@@ -27,6 +27,7 @@ struct PoolArgs {
   PadGrid pad;
   int bs;                 // 2^bs cubes per attention block (coarse token)
   int ld;                 // token rows per head in q/k/v (video slots, then text rows)
+  int rp;                 // router pool edge: 2 (sub-cube means), 1 (the tokens), 4 (no router rows)
 };
 hipError_t launch_pool(const PoolArgs& a, hipStream_t st);
 
@@ -44,6 +45,9 @@ struct RouteArgs {
   int hstride;        //   blocks, and the scores are P_c itself
 };
 hipError_t launch_route(const RouteArgs& a, hipStream_t st);
+// Router pool 1: scores[bh][c][g] = mean of the 8 x 8 block of sub[bh][8c..][8g..]
+// (sub: [bh, 8 nc, 8 nc] means over sub-cube pairs).
+hipError_t launch_route_fold(const float* sub, float* scores, int bh, int nc, hipStream_t st);
 
 struct TopkWs {       // carved from the caller workspace
   uint32_t* hist;     // [bh, 4096]

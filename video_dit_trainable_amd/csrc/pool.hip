@@ -1,5 +1,6 @@
 // Mean pooling for the router (paper §2.2 Eq.(5): 2x2x2 windows = 8
-// contiguous tokens in cube-tiled order) and for the coarse branch (Eq.(1):
+// contiguous tokens in cube-tiled order; router pool 1 copies the tokens,
+// pool 4 leaves the router to the coarse operands) and for the coarse branch (Eq.(1):
 // attention blocks, 4x4x4 cubes = 64 contiguous tokens or 4x4x8 pairs = 128),
 // one pass over Q, K and V.  On a padded grid (§2.2 "Kernel Implementation")
 // windows average their real tokens.
@@ -18,7 +19,7 @@ template <typename T, int D>
 __global__ __launch_bounds__(256) void k_pool(const T* __restrict__ q, const T* __restrict__ k,
                                               const T* __restrict__ v, T* __restrict__ qr, T* __restrict__ kr,
                                               T* __restrict__ qc, T* __restrict__ kc, T* __restrict__ vc, int nb,
-                                              int nbp, PadGrid pad, int bs, int ld) {
+                                              int nbp, PadGrid pad, int bs, int ld, int rp) {
   __shared__ float sub[3][8][D];
   const int blk = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
   const int nblk = nb >> bs;
@@ -39,6 +40,8 @@ __global__ __launch_bounds__(256) void k_pool(const T* __restrict__ q, const T* 
 #pragma unroll
       for (int r = 0; r < 8; ++r) {
         Vec8<T> x = load8(src + (tok0 + 8 * s + r) * D + 8 * cg);
+        if (rp == 1 && tensor < 2)  // router pool 1: the router's rows are the tokens (64 per cube)
+          store8((tensor == 0 ? qr : kr) + ((size_t)bh * nb * 64 + (size_t)c * 64 + 8 * s + r) * D + 8 * cg, x);
         const bool ok = (sreal >> r) & 1;
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[e] += ok ? to_f32(x.v[e]) : 0.f;
@@ -53,7 +56,7 @@ __global__ __launch_bounds__(256) void k_pool(const T* __restrict__ q, const T* 
         sub[tensor][s][8 * cg + e] = cb ? sub[tensor][s][8 * cg + e] + part : part;
         m.v[e] = from_f32<T>(n == 8 ? acc[e] * 0.125f : (n > 0 ? acc[e] / (float)n : 0.f));
       }
-      if (tensor < 2) {
+      if (rp == 2 && tensor < 2) {
         T* dst = tensor == 0 ? qr : kr;
         store8(dst + ((size_t)bh * nb * 8 + (size_t)c * 8 + s) * D + 8 * cg, m);
       }
@@ -82,7 +85,7 @@ template <typename T, int D>
 hipError_t launch_pool_t(const PoolArgs& a, hipStream_t st) {
   dim3 grid(a.nb >> a.bs, a.bh);
   hipLaunchKernelGGL((k_pool<T, D>), grid, dim3(256), 0, st, (const T*)a.q, (const T*)a.k, (const T*)a.v,
-                     (T*)a.qr, (T*)a.kr, (T*)a.qc, (T*)a.kc, (T*)a.vc, a.nb, a.nbp, a.pad, a.bs, a.ld);
+                     (T*)a.qr, (T*)a.kr, (T*)a.qc, (T*)a.kc, (T*)a.vc, a.nb, a.nbp, a.pad, a.bs, a.ld, a.rp);
   return hipGetLastError();
 }
 

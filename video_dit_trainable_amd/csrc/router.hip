@@ -384,6 +384,30 @@ hipError_t launch_route_t(const RouteArgs& a, hipStream_t st) {
   return (8 * a.nb) % RK ? launch_route_tt<T, D, true, false>(a, st) : launch_route_tt<T, D, false, false>(a, st);
 }
 
+// Router pool 1: the passes ran over the tokens with sub-cubes as their
+// groups, writing the mean over each (query sub-cube, key sub-cube) pair; the
+// score of a cube pair is the mean of its 8 x 8 such means (groups of equal
+// size).  One workgroup per (query cube, batch*head), fixed summation order.
+__global__ __launch_bounds__(256) void k_route_fold(const float* __restrict__ sub, float* __restrict__ scores,
+                                                    int nc) {
+  const int c = blockIdx.x, bh = blockIdx.y;
+  const size_t n8 = 8 * (size_t)nc;
+  const float* rows = sub + ((size_t)bh * n8 + 8 * (size_t)c) * n8;
+  float* out = scores + ((size_t)bh * nc + c) * nc;
+  for (int j = threadIdx.x; j < nc; j += 256) {
+    float acc = 0.f;
+    for (int s1 = 0; s1 < 8; ++s1)
+#pragma unroll
+      for (int s2 = 0; s2 < 8; ++s2) acc += rows[s1 * n8 + 8 * (size_t)j + s2];
+    out[j] = acc * (1.0f / 64.0f);
+  }
+}
+
+hipError_t launch_route_fold(const float* sub, float* scores, int bh, int nc, hipStream_t st) {
+  hipLaunchKernelGGL(k_route_fold, dim3(nc, bh), dim3(256), 0, st, sub, scores, nc);
+  return hipGetLastError();
+}
+
 hipError_t launch_route(const RouteArgs& a, hipStream_t st) {
   if (a.bf16) return a.d == 128 ? launch_route_t<bf16, 128>(a, st) : launch_route_t<bf16, 64>(a, st);
   return a.d == 128 ? launch_route_t<float, 128>(a, st) : launch_route_t<float, 64>(a, st);

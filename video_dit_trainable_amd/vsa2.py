@@ -32,6 +32,7 @@ class Problem(ctypes.Structure):
         ("softmax_scale", ctypes.c_float),
         ("block_tokens", ctypes.c_int32),
         ("text_tokens", ctypes.c_int32),
+        ("router_pool", ctypes.c_int32),
     ]
 
 
@@ -92,10 +93,10 @@ def _check(fn, code):
         raise Vsa2Error(fn, code)
 
 
-def problem(batch, heads, head_dim, grid, dtype, softmax_scale=0.0, block=64, text=0):
+def problem(batch, heads, head_dim, grid, dtype, softmax_scale=0.0, block=64, text=0, router_pool=2):
     t, y, x = grid
     dt = {"bf16": VSA2_BF16, "f32": VSA2_F32, torch.bfloat16: VSA2_BF16, torch.float32: VSA2_F32}[dtype]
-    return Problem(batch, heads, head_dim, t, y, x, dt, softmax_scale, block, text)
+    return Problem(batch, heads, head_dim, t, y, x, dt, softmax_scale, block, text, router_pool)
 
 
 def _ptr(t):
