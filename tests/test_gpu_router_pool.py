@@ -111,3 +111,18 @@ def test_topk_on_pool1_scores_is_the_oracle_selection():
         mask = orc.csr_to_mask(rp[0, h].cpu().numpy(), ci[0, h].cpu().numpy(), w.nb)
         outside, band, _ = gu.band_compare(mask, want, kk)
         assert outside == 0, f"head {h}: {outside} mismatches outside the band ({band} pairs in it)"
+
+
+@pytest.mark.parametrize("pool", [1, 4])
+def test_noalloc_router_takes_every_pool(pool):
+    """The no-allocation router dispatches the pools as vsa2_route does, on
+    its fixed scratch: the same scores bit for bit, twice in a row."""
+    w = ODD
+    q, k, v = make_qkv(w, device=_dev())
+    want, p, pooled = _route(w, pool, q, k, v)
+    assert vsa2.workspace_size(p, vsa2.OP_ROUTE) <= vsa2.route_noalloc_limit()
+    for _ in range(2):
+        got = torch.full_like(want, float("nan"))
+        vsa2.vsa2_route_noalloc(p, pooled, got)
+        torch.cuda.synchronize()
+        assert torch.equal(got, want)

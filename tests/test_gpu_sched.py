@@ -236,3 +236,22 @@ def test_unbuilt_or_stale_schedule_gives_the_same_results(w):
         got = _fine(p, w, layer, q, k, v, d_o, layer.sched)
         for nm, a, b in zip(names, want, got):
             assert torch.equal(a, b), f"{nm}: an unbuilt schedule buffer ({label}) changed the result"
+
+
+# the schedule build sorts in LDS up to 8192 lists per (batch, head) and counts
+# ranks beyond: one case past 4096 (the largest sort) and one past 8192
+SORT_MID = Workload("sort-mid", 61, (48, 80, 84), 1, 2, 64, "bf16", 4, "lowrank")     # nb = 5,040
+SORT_BIG = Workload("sort-big", 62, (64, 64, 132), 1, 2, 64, "bf16", 4, "lowrank")    # nb = 8,448
+
+
+@pytest.mark.parametrize("w", [SORT_MID, SORT_BIG], ids=lambda w: w.name)
+def test_schedule_queues_on_both_sides_of_the_lds_sort(w):
+    dev = _dev()
+    p, layer = _layer(w, dev)
+    layer.sched.zero_()
+    layer.set_selection(*make_selection(w, device=dev))      # the plan call builds the schedule
+    torch.cuda.synchronize()
+    (rs, rl, ri), (cs, cl, cidx) = decode(layer)
+    rp, ci, cp, rix = (t[0].cpu().numpy() for t in (layer.row_ptr, layer.col_idx, layer.col_ptr, layer.row_idx))
+    check_side(rs, rl, ri, rp, ci, w.nb)
+    check_side(cs, cl, cidx, cp, rix, w.nb)

@@ -69,8 +69,49 @@ __global__ __launch_bounds__(256) void k_sched_keys(const int32_t* __restrict__ 
   if (lane == 0) keys[(size_t)bh * n + c] = any ? ((a << 16) | b) : 0xFFFFFFFFu;
 }
 
-constexpr int SCHED_TILE = 4096;  // keys per LDS tile of the rank count
-constexpr int SCHED_OVH = 4;      // fixed cost of an item, in list entries
+constexpr int SCHED_TILE = 4096;   // keys per LDS tile of the rank count
+constexpr int SCHED_OVH = 4;       // fixed cost of an item, in list entries
+constexpr int SCHED_FASTN = 8192;  // lists per (batch, head) the in-LDS sorts take
+
+// Ascending bitonic sort of m 64-bit values in LDS (m a power of two, at most
+// SCHED_FASTN) by one 1024-thread workgroup; the caller has synchronised
+// after writing them.  Values equal to each other end up adjacent, so with
+// distinct values (an id in the low bits) the order is unique.
+__device__ void lds_bitonic(uint64_t* a, int m) {
+  for (int k = 2; k <= m; k <<= 1)
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int i = threadIdx.x; i < m; i += 1024) {
+        const int l = i ^ j;
+        if (l > i) {
+          const uint64_t x = a[i], y = a[l];
+          if ((x > y) == ((i & k) == 0)) {
+            a[i] = y;
+            a[l] = x;
+          }
+        }
+      }
+      __syncthreads();
+    }
+}
+
+__device__ __forceinline__ int pow2_at_least(int n) {
+  int m = 2;
+  while (m < n) m <<= 1;
+  return m;
+}
+
+// The (key, id) order of up to SCHED_FASTN lists, one workgroup per (batch,
+// head): (key << 32 | id) sorted in LDS, order[rank] = id.
+__global__ __launch_bounds__(1024) void k_sched_sort(const uint32_t* __restrict__ keys, int32_t* __restrict__ order,
+                                                     int n) {
+  __shared__ uint64_t a[SCHED_FASTN];
+  const int bh = blockIdx.x, m = pow2_at_least(n);
+  for (int i = threadIdx.x; i < m; i += 1024)
+    a[i] = i < n ? ((uint64_t)keys[(size_t)bh * n + i] << 32 | (uint32_t)i) : ~0ull;
+  __syncthreads();
+  lds_bitonic(a, m);
+  for (int r = threadIdx.x; r < n; r += 1024) order[(size_t)bh * n + r] = (int32_t)(uint32_t)a[r];
+}
 
 // Rank of every cube in (key, id) order, order[rank] = cube.  One thread per
 // cube counts the keys below its own; the keys of the (batch, head) pass
@@ -174,6 +215,32 @@ __global__ __launch_bounds__(256) void k_sched_place(const uint8_t* __restrict__
   tmp[(size_t)bh * n + r0 + pos] = order[(size_t)bh * n + p];
 }
 
+// The placement of k_sched_place for up to SCHED_FASTN lists, one workgroup
+// per (batch, head): positions sorted by (XCD, class descending, position) put
+// each XCD's range at its start in the order (the ranges are contiguous) and
+// the range long-first, which is the same placement.
+__global__ __launch_bounds__(1024) void k_sched_place_sort(const uint8_t* __restrict__ px,
+                                                           const int32_t* __restrict__ rng,
+                                                           const int32_t* __restrict__ order,
+                                                           int32_t* __restrict__ tmp, int32_t* __restrict__ cnt,
+                                                           int n) {
+  __shared__ uint64_t a[SCHED_FASTN];
+  const int bh = blockIdx.x, tid = threadIdx.x, m = pow2_at_least(n);
+  const uint8_t* pxb = px + (size_t)bh * n;
+  for (int p = tid; p < m; p += 1024) {
+    if (p < n) {
+      const uint32_t x = pxb[p] >> 5, c = pxb[p] & 31;
+      a[p] = (uint64_t)((x << 5) | (31u - c)) << 32 | (uint32_t)p;
+    } else {
+      a[p] = ~0ull;
+    }
+  }
+  if (tid < 8) cnt[(size_t)bh * 8 + tid] = rng[(size_t)bh * 9 + tid + 1] - rng[(size_t)bh * 9 + tid];
+  __syncthreads();
+  lds_bitonic(a, m);
+  for (int i = tid; i < n; i += 1024) tmp[(size_t)bh * n + i] = order[(size_t)bh * n + (int)(uint32_t)a[i]];
+}
+
 // Queue offsets: queue x holds, for every (batch, head) in turn, that head's
 // range for XCD x.  hdr[x] = start of queue x in the item array, hdr[8 + x]
 // its length, hdr[16] the item count bh * n and hdr[17] SCHED_MAGIC;
@@ -228,14 +295,21 @@ static hipError_t build_side(const int32_t* ptr, const int32_t* idx, int32_t* hd
   hipLaunchKernelGGL(k_sched_keys, dim3((n + 3) / 4, a.bh), dim3(256), 0, st, ptr, idx, a.keys, n, a.kph);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_sched_rank, dim3((n + 255) / 256, a.bh), dim3(256), 0, st, a.keys, a.order, n);
+  const bool fast = n <= SCHED_FASTN;  // the in-LDS sorts; beyond, the counting kernels
+  if (fast)
+    hipLaunchKernelGGL(k_sched_sort, dim3(a.bh), dim3(1024), 0, st, a.keys, a.order, n);
+  else
+    hipLaunchKernelGGL(k_sched_rank, dim3((n + 255) / 256, a.bh), dim3(256), 0, st, a.keys, a.order, n);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_sched_cut, dim3(a.bh), dim3(1024), 0, st, ptr, a.order, a.px, a.rng, n, a.kph);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_sched_place, dim3((n + 255) / 256, a.bh), dim3(256), 0, st, a.px, a.rng, a.order, a.tmp,
-                     a.cnt, n);
+  if (fast)
+    hipLaunchKernelGGL(k_sched_place_sort, dim3(a.bh), dim3(1024), 0, st, a.px, a.rng, a.order, a.tmp, a.cnt, n);
+  else
+    hipLaunchKernelGGL(k_sched_place, dim3((n + 255) / 256, a.bh), dim3(256), 0, st, a.px, a.rng, a.order, a.tmp,
+                       a.cnt, n);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_sched_queues, dim3(1), dim3(64), 0, st, a.cnt, hdr, a.hoff, a.bh, n);
