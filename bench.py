@@ -244,6 +244,8 @@ def main():
 
     gr = layer.grads()      # allocated once, outside the timed region
     sched = None if args.no_sched else layer.sched
+    # the CSC (and the KV-cube side of the schedule) feeds only the backward
+    csc = (layer.col_ptr, layer.row_idx) if w.train else (None, None)
     torch.cuda.synchronize()
 
     def step_full(ev=None):
@@ -259,11 +261,11 @@ def main():
             vsa2.vsa2_route(p, layer.pooled, layer.scores, layer.ws)
         mark(2)
         if w.router == "vsa":
-            vsa2.vsa2_topk_per_row(p, layer.scores, w.topk, layer.row_ptr, layer.col_idx, layer.col_ptr,
-                                   layer.row_idx, layer.ws, sched=sched)
+            vsa2.vsa2_topk_per_row(p, layer.scores, w.topk, layer.row_ptr, layer.col_idx, *csc, layer.ws,
+                                   sched=sched)
         else:
-            vsa2.vsa2_topk_per_seq(p, layer.scores, w.topk, layer.row_ptr, layer.col_idx, layer.col_ptr,
-                                   layer.row_idx, layer.ws, sched=sched)
+            vsa2.vsa2_topk_per_seq(p, layer.scores, w.topk, layer.row_ptr, layer.col_idx, *csc, layer.ws,
+                                   sched=sched)
         mark(3)
         vsa2.vsa2_sparse_attn_fwd(p, w.topk, q, k, v, layer.row_ptr, layer.col_idx, layer.o_f, layer.lse, layer.ws,
                                   sched=sched)

@@ -194,7 +194,10 @@ int vsa2_route(const vsa2_problem* p, const void* pooled, float* scores,
  *     [batch, heads, k]: selected KV cubes of query cube i are
  *     col_idx[row_ptr[i] .. row_ptr[i+1]), ascending.  row_ptr[nb] = k.
  *   col_ptr, row_idx (written): the same selection by KV cube (CSC), query
- *     cubes ascending; used by the backward pass.
+ *     cubes ascending; used by the backward pass.  Both NULL for a selection
+ *     only the forward runs on (inference): no CSC is built, and the schedule
+ *     gets only its query-cube side.  One NULL without the other is
+ *     VSA2_E_ARG.
  *   sched (written): the work schedule of this selection, sched_bytes >=
  *     vsa2_sched_size() and 256-byte aligned; NULL builds none (the fine
  *     kernels then run one workgroup per cube).
@@ -267,6 +270,7 @@ int vsa2_route_coarse(const vsa2_problem* p, const void* pooled, float* scores,
  * budget of Eq.(8)-(9).  Same outputs, sizes and budget (vsa2_budget) as
  * vsa2_topk_per_seq; row_ptr[i] = i min(topk, nb).
  *   scores: fp32 [batch, heads, nb, nb], finite and >= 0.
+ *   col_ptr, row_idx: as for vsa2_topk_per_seq (both NULL: forward only).
  *   sched (written, or NULL): the work schedule, as for vsa2_topk_per_seq.
  *   ws: vsa2_workspace_size(VSA2_OP_TOPK_ROW). */
 int vsa2_topk_per_row(const vsa2_problem* p, const float* scores, int32_t topk, int32_t* row_ptr,

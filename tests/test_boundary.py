@@ -174,6 +174,10 @@ def test_schedule_size_and_checks():
     ss = vsa2.sched_size(p, 5)
     # a schedule buffer that is too small or misaligned is refused before anything runs
     assert L.vsa2_topk_per_seq(ctypes.byref(p), A, 5, B, C, D, A, B, ss - 1, C, need, None) == vsa2.VSA2_E_WORKSPACE
+    # the CSC outputs come both or neither (forward-only selections leave both NULL)
+    assert L.vsa2_topk_per_seq(ctypes.byref(p), A, 5, B, C, None, A, B, ss, C, need, None) == vsa2.VSA2_E_ARG
+    assert L.vsa2_topk_per_seq(ctypes.byref(p), A, 5, B, C, D, None, B, ss, C, need, None) == vsa2.VSA2_E_ARG
+    assert L.vsa2_topk_per_row(ctypes.byref(p), A, 5, B, C, None, A, B, ss, C, 1 << 30, None) == vsa2.VSA2_E_ARG
     assert L.vsa2_topk_per_seq(ctypes.byref(p), A, 5, B, C, D, A, B + 16, ss, C, need, None) == vsa2.VSA2_E_ARG
     assert L.vsa2_plan_from_csr(ctypes.byref(p), 5, A, B, C, D, B + 16, ss, C, 1 << 30, None) == vsa2.VSA2_E_ARG
     assert L.vsa2_sparse_attn_fwd(ctypes.byref(p), 5, A, B, C, D, A, B + 16, C, D, None, 0, None) == vsa2.VSA2_E_ARG

@@ -255,3 +255,38 @@ def test_schedule_queues_on_both_sides_of_the_lds_sort(w):
     rp, ci, cp, rix = (t[0].cpu().numpy() for t in (layer.row_ptr, layer.col_idx, layer.col_ptr, layer.row_idx))
     check_side(rs, rl, ri, rp, ci, w.nb)
     check_side(cs, cl, cidx, cp, rix, w.nb)
+
+
+@pytest.mark.parametrize("w", [MID, SHORT], ids=lambda w: w.name)
+def test_forward_only_topk_builds_the_query_side(w):
+    """TopK without the CSC (a selection only the forward runs on): the same
+    CSR, the same query-cube side of the schedule byte for byte, the KV-cube
+    side left alone, and the same forward through it."""
+    dev = _dev()
+    q, k, v = make_qkv(w, device=dev)
+    p, layer = _layer(w, dev)
+    vsa2.vsa2_pool(p, q, k, v, layer.pooled)
+    vsa2.vsa2_route(p, layer.pooled, layer.scores, layer.ws)
+    layer.sched.zero_()
+    vsa2.vsa2_topk_per_seq(p, layer.scores, w.topk, layer.row_ptr, layer.col_idx, layer.col_ptr, layer.row_idx,
+                           layer.ws, sched=layer.sched)
+    want = [t.clone() for t in (layer.row_ptr, layer.col_idx, layer.sched)]
+    o1, l1 = torch.empty_like(layer.o_f), torch.empty_like(layer.lse)
+    vsa2.vsa2_sparse_attn_fwd(p, w.topk, q, k, v, layer.row_ptr, layer.col_idx, o1, l1, layer.ws, sched=layer.sched)
+    torch.cuda.synchronize()
+    layer.row_ptr.fill_(-1)
+    layer.col_idx.fill_(-1)
+    layer.sched.fill_(7)
+    vsa2.vsa2_topk_per_seq(p, layer.scores, w.topk, layer.row_ptr, layer.col_idx, None, None, layer.ws,
+                           sched=layer.sched)
+    torch.cuda.synchronize()
+    assert torch.equal(layer.row_ptr, want[0]) and torch.equal(layer.col_idx, want[1])
+    side = 256 + _up(layer.bh * layer.nb * 4)
+    raw, ref = layer.sched.cpu().numpy(), want[2].cpu().numpy()
+    # the query side: header words and items as with the CSC (the bytes between them are never written)
+    assert np.array_equal(raw[:72], ref[:72]) and np.array_equal(raw[256:side], ref[256:side])
+    assert np.all(raw[side:2 * side] == 7), "the KV-cube side was written"
+    o2, l2 = torch.empty_like(layer.o_f), torch.empty_like(layer.lse)
+    vsa2.vsa2_sparse_attn_fwd(p, w.topk, q, k, v, layer.row_ptr, layer.col_idx, o2, l2, layer.ws, sched=layer.sched)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)

@@ -88,6 +88,13 @@ int check_problem(const vsa2_problem* p, Dims& o) {
 
 bool aligned(const void* ptr) { return ptr && ((uintptr_t)ptr % 16 == 0); }
 
+// The CSC outputs of the TopK calls: both given (aligned), or both NULL for a
+// forward-only selection (no CSC, and only the query side of the schedule).
+bool csc_args_ok(const int32_t* col_ptr, const int32_t* row_idx) {
+  if (!col_ptr && !row_idx) return true;
+  return aligned(col_ptr) && aligned(row_idx);
+}
+
 int64_t budget(const Dims& d, int32_t topk) {
   const int64_t all = (int64_t)d.nb * d.nb;
   const int64_t k = (int64_t)d.nb * topk;
@@ -576,8 +583,8 @@ int vsa2_topk_per_row(const vsa2_problem* p, const float* scores, int32_t topk, 
   int s = check_problem(p, d);
   if (s) return s;
   if (topk < 1) return VSA2_E_ARG;
-  if (!aligned(scores) || !aligned(row_ptr) || !aligned(col_idx) || !aligned(col_ptr) || !aligned(row_idx))
-    return VSA2_E_ARG;
+  if (!aligned(scores) || !aligned(row_ptr) || !aligned(col_idx)) return VSA2_E_ARG;
+  if (!csc_args_ok(col_ptr, row_idx)) return VSA2_E_ARG;
   if ((s = check_sched(d, budget(d, topk), sched, &sched_bytes))) return s;
   if ((s = check_ws(ws, ws_bytes, ws_plan(d, nullptr, nullptr)))) return s;
   TopkArgs a{};
@@ -602,8 +609,8 @@ int vsa2_topk_per_seq(const vsa2_problem* p, const float* scores, int32_t topk, 
   int s = check_problem(p, d);
   if (s) return s;
   if (topk < 1) return VSA2_E_ARG;
-  if (!aligned(scores) || !aligned(row_ptr) || !aligned(col_idx) || !aligned(col_ptr) || !aligned(row_idx))
-    return VSA2_E_ARG;
+  if (!aligned(scores) || !aligned(row_ptr) || !aligned(col_idx)) return VSA2_E_ARG;
+  if (!csc_args_ok(col_ptr, row_idx)) return VSA2_E_ARG;
   if ((s = check_sched(d, budget(d, topk), sched, &sched_bytes))) return s;
   if ((s = check_ws(ws, ws_bytes, ws_topk(d, nullptr, nullptr)))) return s;
   TopkArgs a{};

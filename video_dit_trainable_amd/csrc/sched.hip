@@ -322,7 +322,7 @@ static hipError_t build_side(const int32_t* ptr, const int32_t* idx, int32_t* hd
 hipError_t launch_sched(const SchedArgs& a, hipStream_t st) {
   if (a.n > SCHED_MAXN) return hipErrorInvalidValue;
   hipError_t e = build_side(a.row_ptr, a.col_idx, a.row_hdr, a.row_items, a, st);
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || !a.col_ptr) return e;  // no CSC (forward only): the query side alone
   return build_side(a.col_ptr, a.row_idx, a.col_hdr, a.col_items, a, st);
 }
 

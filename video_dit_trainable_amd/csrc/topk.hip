@@ -180,11 +180,13 @@ __global__ __launch_bounds__(1024) void k_rowalloc(const uint32_t* __restrict__ 
   if (tid == 0) row_ptr[(size_t)bh * (nb + 1) + nb] = (int32_t)carry_sel;
 }
 
-// Compact each row in ascending column order; record bitmap and column counts.
+// Compact each row in ascending column order; with csc, record the bitmap and
+// the column counts the CSC is built from.
 __global__ __launch_bounds__(256) void k_compact(const float* __restrict__ scores, const uint32_t* __restrict__ state,
                                                  const uint32_t* __restrict__ take, const int32_t* __restrict__ row_ptr,
                                                  int32_t* __restrict__ col_idx, uint32_t* __restrict__ bitmap,
-                                                 uint32_t* __restrict__ colcnt, int nb, int64_t kph, int words) {
+                                                 uint32_t* __restrict__ colcnt, int nb, int64_t kph, int words,
+                                                 int csc) {
   const int bh = blockIdx.y, row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (row >= nb) return;
   const uint32_t tau = state[bh * 4 + 0];
@@ -222,9 +224,9 @@ __global__ __launch_bounds__(256) void k_compact(const float* __restrict__ score
       const uint32_t before = __popcll(selm & lt);
       if (sel && row0 + written + before < kph) {
         out[written + before] = j;
-        atomicAdd(&colcnt[(size_t)bh * nb + j], 1u);
+        if (csc) atomicAdd(&colcnt[(size_t)bh * nb + j], 1u);
       }
-      if (lane < 2) bm[(j0 >> 5) + lane] = (uint32_t)(selm >> (32 * lane));
+      if (csc && lane < 2) bm[(j0 >> 5) + lane] = (uint32_t)(selm >> (32 * lane));
       eq_seen += __popcll(eqm);
       written += __popcll(selm);
     }
@@ -360,11 +362,12 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t st) {
   VSA2_CHECK(hipGetLastError());
   hipLaunchKernelGGL(k_rowalloc, dim3(a.bh), dim3(1024), 0, st, a.ws.rowcnt, a.ws.state, a.ws.take, a.row_ptr, a.nb);
   VSA2_CHECK(hipGetLastError());
-  VSA2_CHECK(launch_fill_u32(a.ws.colcnt, 0u, (size_t)a.bh * a.nb, st));
+  const int csc = a.col_ptr != nullptr;  // forward-only callers need no CSC
+  if (csc) VSA2_CHECK(launch_fill_u32(a.ws.colcnt, 0u, (size_t)a.bh * a.nb, st));
   hipLaunchKernelGGL(k_compact, rgrid, dim3(256), 0, st, a.scores, a.ws.state, a.ws.take, a.row_ptr, a.col_idx,
-                     a.ws.bitmap, a.ws.colcnt, a.nb, a.k, a.ws.words);
+                     a.ws.bitmap, a.ws.colcnt, a.nb, a.k, a.ws.words, csc);
   VSA2_CHECK(hipGetLastError());
-  return csc_from_bitmap(a, st);
+  return csc ? csc_from_bitmap(a, st) : hipSuccess;
 }
 
 // The VSA router baseline's selection (paper §1, Figure 1 left): every query
@@ -447,7 +450,7 @@ hipError_t launch_topk_rows(const TopkArgs& a, hipStream_t st) {
   const int kr = (int)(a.k / a.nb);
   hipLaunchKernelGGL(k_row_topk, dim3(a.nb, a.bh), dim3(256), 0, st, a.scores, a.row_ptr, a.col_idx, a.nb, kr);
   VSA2_CHECK(hipGetLastError());
-  return launch_plan(a, st);
+  return a.col_ptr ? launch_plan(a, st) : hipSuccess;  // forward-only callers need no CSC
 }
 
 hipError_t launch_plan(const TopkArgs& a, hipStream_t st) {
