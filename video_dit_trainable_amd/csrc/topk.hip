@@ -180,13 +180,12 @@ __global__ __launch_bounds__(1024) void k_rowalloc(const uint32_t* __restrict__ 
   if (tid == 0) row_ptr[(size_t)bh * (nb + 1) + nb] = (int32_t)carry_sel;
 }
 
-// Compact each row in ascending column order; with csc, record the bitmap and
-// the column counts the CSC is built from.
+// Compact each row in ascending column order; with csc, record the bitmap the
+// CSC is built from.
 __global__ __launch_bounds__(256) void k_compact(const float* __restrict__ scores, const uint32_t* __restrict__ state,
                                                  const uint32_t* __restrict__ take, const int32_t* __restrict__ row_ptr,
                                                  int32_t* __restrict__ col_idx, uint32_t* __restrict__ bitmap,
-                                                 uint32_t* __restrict__ colcnt, int nb, int64_t kph, int words,
-                                                 int csc) {
+                                                 int nb, int64_t kph, int words, int csc) {
   const int bh = blockIdx.y, row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (row >= nb) return;
   const uint32_t tau = state[bh * 4 + 0];
@@ -222,10 +221,7 @@ __global__ __launch_bounds__(256) void k_compact(const float* __restrict__ score
       const bool sel = j < nb && (u > tau || (is_eq && rank < tk));
       const uint64_t selm = __ballot(sel);
       const uint32_t before = __popcll(selm & lt);
-      if (sel && row0 + written + before < kph) {
-        out[written + before] = j;
-        if (csc) atomicAdd(&colcnt[(size_t)bh * nb + j], 1u);
-      }
+      if (sel && row0 + written + before < kph) out[written + before] = j;
       if (csc && lane < 2) bm[(j0 >> 5) + lane] = (uint32_t)(selm >> (32 * lane));
       eq_seen += __popcll(eqm);
       written += __popcll(selm);
@@ -268,6 +264,44 @@ __global__ __launch_bounds__(1024) void k_colptr(const uint32_t* __restrict__ co
     if (i < nb) col_ptr[(size_t)bh * (nb + 1) + i] = (int32_t)pos;
   }
   if (tid == 0) col_ptr[(size_t)bh * (nb + 1) + nb] = (int32_t)carry;
+}
+
+// Column counts of the selection from its bitmap: block = (64-column strip,
+// bh), wave w counts rows [w*R, (w+1)*R), lane = column; fixed order, no
+// atomics.
+__global__ __launch_bounds__(1024) void k_colcount(const uint32_t* __restrict__ bitmap,
+                                                   uint32_t* __restrict__ colcnt, int nb, int words) {
+  constexpr int NW = 16;
+  __shared__ uint32_t cnt[NW][64];
+  const int bh = blockIdx.y, strip = blockIdx.x, w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int j = strip * 64 + lane;
+  const int R = (nb + NW - 1) / NW;
+  const int r0 = min(nb, w * R), r1 = min(nb, r0 + R);
+  const uint32_t* bm = bitmap + (size_t)bh * nb * words + 2 * strip;
+  const bool hi_half = lane >= 32;
+  const uint32_t bit = 1u << (lane & 31);
+  uint32_t c = 0;
+  for (int rb = r0; rb < r1; rb += 64) {
+    // lane l loads the strip's two words of row rb + l; readlane hands them to every lane
+    const int r = rb + lane;
+    uint32_t lo = 0u, hi = 0u;
+    if (r < r1) {
+      lo = bm[(size_t)r * words];
+      hi = bm[(size_t)r * words + 1];
+    }
+    const int n = min(64, r1 - rb);
+    for (int i = 0; i < n; ++i) {
+      const uint32_t a = __builtin_amdgcn_readlane(lo, i), b = __builtin_amdgcn_readlane(hi, i);
+      c += ((hi_half ? b : a) & bit) ? 1u : 0u;
+    }
+  }
+  cnt[w][lane] = c;
+  __syncthreads();
+  if (w == 0 && j < nb) {
+    uint32_t t = 0;
+    for (int ww = 0; ww < NW; ++ww) t += cnt[ww][lane];
+    colcnt[(size_t)bh * nb + j] = t;
+  }
 }
 
 // CSC rows in ascending order from the bitmap: block = (64-column strip, bh),
@@ -363,11 +397,14 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t st) {
   hipLaunchKernelGGL(k_rowalloc, dim3(a.bh), dim3(1024), 0, st, a.ws.rowcnt, a.ws.state, a.ws.take, a.row_ptr, a.nb);
   VSA2_CHECK(hipGetLastError());
   const int csc = a.col_ptr != nullptr;  // forward-only callers need no CSC
-  if (csc) VSA2_CHECK(launch_fill_u32(a.ws.colcnt, 0u, (size_t)a.bh * a.nb, st));
   hipLaunchKernelGGL(k_compact, rgrid, dim3(256), 0, st, a.scores, a.ws.state, a.ws.take, a.row_ptr, a.col_idx,
-                     a.ws.bitmap, a.ws.colcnt, a.nb, a.k, a.ws.words, csc);
+                     a.ws.bitmap, a.nb, a.k, a.ws.words, csc);
   VSA2_CHECK(hipGetLastError());
-  return csc ? csc_from_bitmap(a, st) : hipSuccess;
+  if (!csc) return hipSuccess;
+  hipLaunchKernelGGL(k_colcount, dim3(a.ws.words / 2, a.bh), dim3(1024), 0, st, a.ws.bitmap, a.ws.colcnt, a.nb,
+                     a.ws.words);
+  VSA2_CHECK(hipGetLastError());
+  return csc_from_bitmap(a, st);
 }
 
 // The VSA router baseline's selection (paper §1, Figure 1 left): every query
