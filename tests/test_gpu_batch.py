@@ -1,0 +1,87 @@
+"""The layer over a batch of more than one sequence, on the GPU.
+
+Every other GPU test runs one sequence.  Here batch 2 (bf16, skewed query
+scales, on the work schedule) and batch 3 (fp32) run the whole layer: the
+router and per-sequence TopK of every (batch, head) against the oracle, then,
+on the oracle's selection, the merged output and every gradient against the
+oracle's layer for each batch element, with dW_g summed over the batch
+([VSA2] §2.2 Eq.(8)-(9) keep one budget per sequence and head; the gate of
+Eq.(13)-(14) shares W_g across the batch).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import gpu_util as gu
+from oracle import vsa2_oracle as orc
+from video_dit_trainable_amd import vsa2
+from video_dit_trainable_amd.configs import Workload
+from video_dit_trainable_amd.inputs import make_gate_inputs, make_grad_out, make_qkv
+
+pytestmark = pytest.mark.gpu
+
+BATCH2 = Workload("batch2", 19, (8, 8, 16), 2, 2, 64, "bf16", 4, "lowrank", skew=True, train=True)      # nb = 16
+BATCH3 = Workload("batch3", 20, (4, 12, 20), 3, 2, 64, "f32", 3, "sinusoid", alpha=1.0, train=True)     # nb = 15
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    vsa2.lib()
+
+
+@pytest.mark.parametrize("w", [BATCH2, BATCH3], ids=lambda w: w.name)
+def test_layer_over_a_batch(w):
+    dev = torch.device("cuda:0")
+    q, k, v = make_qkv(w)
+    x, w_g = make_gate_inputs(w, zero_gate=False)
+    d_o = make_grad_out(w)
+    p = vsa2.problem(w.batch, w.heads, w.head_dim, w.grid, w.dtype)
+    layer = vsa2.Layer(p, w.topk, w.d_model, device=dev)
+    qd, kd, vd, xd, wd, dod = (t.to(dev) for t in (q, k, v, x, w_g, d_o))
+    bf = w.dtype == "bf16"
+    tol = 1e-4 if w.dtype == "f32" else 2e-2
+
+    # router and per-sequence TopK of every (batch, head)
+    layer.forward(qd, kd, vd, xd, wd)
+    torch.cuda.synchronize()
+    masks = np.empty((w.batch, w.heads, w.nb, w.nb), dtype=bool)
+    for b in range(w.batch):
+        gu.check_csr_csc(layer.row_ptr[b], layer.col_idx[b], layer.col_ptr[b], layer.row_idx[b], w.nb, layer.k)
+        for h in range(w.heads):
+            want = orc.router_scores(gu.f64(q[b, h]), gu.f64(k[b, h]), w.grid, bf16_pooled=bf)
+            got = gu.f64(layer.scores[b, h])
+            for i in range(w.nb):
+                assert gu.rel_l2(got[i], want[i]) <= 1e-4, f"scores batch {b} head {h} row {i}"
+            mask = orc.csr_to_mask(layer.row_ptr[b, h].cpu().numpy(), layer.col_idx[b, h].cpu().numpy(), w.nb)
+            outside, band, _ = gu.band_compare(mask, want, layer.k)
+            assert outside == 0, f"batch {b} head {h}: {outside} mismatches outside the band ({band} in it)"
+            masks[b, h] = orc.topk_per_sequence(want, w.topk)[0]
+
+    # outputs and gradients on the oracle's selection
+    rp = np.stack([[orc.mask_to_csr_csc(m)[0] for m in mb] for mb in masks])
+    ci = np.stack([[orc.mask_to_csr_csc(m)[1] for m in mb] for mb in masks])
+    layer.set_selection(torch.tensor(rp, dtype=torch.int32, device=dev),
+                        torch.tensor(ci, dtype=torch.int32, device=dev))
+    o = layer.forward(qd, kd, vd, xd, wd, route=False)
+    g = layer.backward(qd, kd, vd, xd, wd, dod)
+    torch.cuda.synchronize()
+    dw_sum = 0.0
+    for b in range(w.batch):
+        a = [gu.f64(t[b]) for t in (q, k, v)]
+        ref = orc.vsa2_forward(*a, w.grid, w.topk, gu.f64(x[b]), gu.f64(w_g), bf16_pooled=bf, mask=masks[b])
+        for h in range(w.heads):
+            if w.dtype == "f32":
+                gu.assert_close_f32(gu.f64(o[b, h]), ref["o"][h], f"O batch {b} head {h}")
+            else:
+                gu.assert_close_bf16(gu.f64(o[b, h]), ref["o"][h], f"O batch {b} head {h}", rounding=2.0 ** -8)
+        dq, dk, dv, dx, dw = orc.vsa2_backward(*a, w.grid, masks[b], gu.f64(x[b]), gu.f64(w_g), gu.f64(d_o[b]))
+        for name, want in (("dq", dq), ("dk", dk), ("dv", dv), ("dx", dx)):
+            got = gu.f64(g[name][b])
+            r = gu.rel_l2(got, want.reshape(got.shape))
+            assert r <= tol, f"{name} batch {b}: rel-L2 {r:.3g} > {tol}"
+        dw_sum = dw_sum + dw
+    r = gu.rel_l2(gu.f64(g["dw_g"]), dw_sum)
+    assert r <= tol, f"dW_g (summed over the batch): rel-L2 {r:.3g} > {tol}"
