@@ -1,4 +1,5 @@
-"""The layer over a batch of more than one sequence, on the GPU.
+"""The layer over a batch of more than one sequence, and with a given softmax
+scale, on the GPU.
 
 Every other GPU test runs one sequence.  Here batch 2 (bf16, skewed query
 scales, on the work schedule) and batch 3 (fp32) run the whole layer: the
@@ -6,7 +7,8 @@ router and per-sequence TopK of every (batch, head) against the oracle, then,
 on the oracle's selection, the merged output and every gradient against the
 oracle's layer for each batch element, with dW_g summed over the batch
 ([VSA2] §2.2 Eq.(8)-(9) keep one budget per sequence and head; the gate of
-Eq.(13)-(14) shares W_g across the batch).
+Eq.(13)-(14) shares W_g across the batch).  The last test sets
+vsa2_problem.softmax_scale, which every other test leaves at 1/sqrt(d).
 """
 
 import numpy as np
@@ -85,3 +87,43 @@ def test_layer_over_a_batch(w):
         dw_sum = dw_sum + dw
     r = gu.rel_l2(gu.f64(g["dw_g"]), dw_sum)
     assert r <= tol, f"dW_g (summed over the batch): rel-L2 {r:.3g} > {tol}"
+
+
+SCALED = Workload("scaled", 21, (8, 8, 16), 1, 2, 128, "bf16", 4, "lowrank", train=True)   # nb = 16
+
+
+def test_layer_with_a_given_softmax_scale():
+    """vsa2_problem.softmax_scale replaces 1/sqrt(d) in the router, the fine
+    and the coarse attention alike (Eq.(2), (6), (12))."""
+    w, scale = SCALED, 0.21
+    dev = torch.device("cuda:0")
+    q, k, v = make_qkv(w)
+    x, w_g = make_gate_inputs(w, zero_gate=False)
+    d_o = make_grad_out(w)
+    p = vsa2.problem(w.batch, w.heads, w.head_dim, w.grid, w.dtype, softmax_scale=scale)
+    layer = vsa2.Layer(p, w.topk, w.d_model, device=dev)
+    qd, kd, vd, xd, wd, dod = (t.to(dev) for t in (q, k, v, x, w_g, d_o))
+    layer.forward(qd, kd, vd, xd, wd)
+    torch.cuda.synchronize()
+    a = [gu.f64(t[0]) for t in (q, k, v)]
+    masks = []
+    for h in range(w.heads):
+        want = orc.router_scores(a[0][h], a[1][h], w.grid, scale=scale, bf16_pooled=True)
+        got = gu.f64(layer.scores[0, h])
+        for i in range(w.nb):
+            assert gu.rel_l2(got[i], want[i]) <= 1e-4, f"scores head {h} row {i}"
+        masks.append(orc.topk_per_sequence(want, w.topk)[0])
+    masks = np.stack(masks)
+    layer.set_selection(*gu.csr_tensors(masks, dev))
+    o = layer.forward(qd, kd, vd, xd, wd, route=False)
+    g = layer.backward(qd, kd, vd, xd, wd, dod)
+    torch.cuda.synchronize()
+    ref = orc.vsa2_forward(*a, w.grid, w.topk, gu.f64(x[0]), gu.f64(w_g), scale=scale, bf16_pooled=True, mask=masks)
+    for h in range(w.heads):
+        gu.assert_close_bf16(gu.f64(o[0, h]), ref["o"][h], f"O head {h}", rounding=2.0 ** -8)
+        np.testing.assert_allclose(gu.f64(layer.lse[0, h]), ref["lse"][h], atol=2e-3)
+    dq, dk, dv, dx, dw = orc.vsa2_backward(*a, w.grid, masks, gu.f64(x[0]), gu.f64(w_g), gu.f64(d_o[0]), scale=scale)
+    for name, want in (("dq", dq), ("dk", dk), ("dv", dv), ("dx", dx), ("dw_g", dw)):
+        got = gu.f64(g[name][0] if name != "dw_g" else g[name])
+        r = gu.rel_l2(got, want.reshape(got.shape))
+        assert r <= 2e-2, f"{name}: rel-L2 {r:.3g}"
