@@ -7,8 +7,9 @@ router and per-sequence TopK of every (batch, head) against the oracle, then,
 on the oracle's selection, the merged output and every gradient against the
 oracle's layer for each batch element, with dW_g summed over the batch
 ([VSA2] §2.2 Eq.(8)-(9) keep one budget per sequence and head; the gate of
-Eq.(13)-(14) shares W_g across the batch).  The last test sets
-vsa2_problem.softmax_scale, which every other test leaves at 1/sqrt(d).
+Eq.(13)-(14) shares W_g across the batch).  One test sets
+vsa2_problem.softmax_scale, which every other test leaves at 1/sqrt(d), and
+one runs the layer on a stream other than the default one.
 """
 
 import numpy as np
@@ -127,3 +128,26 @@ def test_layer_with_a_given_softmax_scale():
         got = gu.f64(g[name][0] if name != "dw_g" else g[name])
         r = gu.rel_l2(got, want.reshape(got.shape))
         assert r <= 2e-2, f"{name}: rel-L2 {r:.3g}"
+
+
+def test_layer_on_a_side_stream():
+    """Every call enqueues on the stream it is given: the layer run on a side
+    stream (default priority) gives the default stream's results bit for bit."""
+    w = BATCH2
+    dev = torch.device("cuda:0")
+    q, k, v = (t.to(dev) for t in make_qkv(w))
+    x, w_g = (t.to(dev) for t in make_gate_inputs(w, zero_gate=False))
+    d_o = make_grad_out(w).to(dev)
+    p = vsa2.problem(w.batch, w.heads, w.head_dim, w.grid, w.dtype)
+    runs = []
+    for side in (False, True):
+        layer = vsa2.Layer(p, w.topk, w.d_model, device=dev)
+        torch.cuda.synchronize()
+        st = torch.cuda.Stream(device=dev) if side else None
+        raw = st.cuda_stream if side else None
+        o = layer.forward(q, k, v, x, w_g, stream=raw)
+        g = layer.backward(q, k, v, x, w_g, d_o, stream=raw)
+        (st or torch.cuda.current_stream()).synchronize()
+        runs.append([t.clone() for t in (o, layer.col_idx, g["dq"], g["dk"], g["dv"], g["dx"], g["dw_g"])])
+    for a, b in zip(*runs):
+        assert torch.equal(a, b)
