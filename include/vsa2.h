@@ -136,8 +136,8 @@ int vsa2_workspace_size(const vsa2_problem* p, int32_t op, int32_t topk, int32_t
  * the same results, bit for bit, as with no schedule.
  * Written by vsa2_topk_per_seq, vsa2_topk_per_row and vsa2_plan_from_csr from
  * the selection they produce or receive, read by vsa2_sparse_attn_fwd/bwd.
- * Built for 64-token blocks without text rows; with block_tokens = 128 (each
- * workgroup already stages every tile for the block's two cubes) or
+ * Built for problems without text rows, by attention block (a cube, or with
+ * block_tokens = 128 a pair of cubes that one workgroup runs whole); with
  * text_tokens > 0 the size is 0 and the kernels run one workgroup per block.
  * A schedule built for another selection of the same problem is still valid
  * (it lists every cube once), only balanced for that selection; a buffer that

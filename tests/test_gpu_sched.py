@@ -290,3 +290,48 @@ def test_forward_only_topk_builds_the_query_side(w):
     vsa2.vsa2_sparse_attn_fwd(p, w.topk, q, k, v, layer.row_ptr, layer.col_idx, o2, l2, layer.ws, sched=layer.sched)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+# 128-token blocks: one item per block, run by a whole-block workgroup
+B128 = Workload("b128", 32, (8, 16, 32), 1, 3, 128, "bf16", 4, "lowrank", skew=True, train=True, block=128)
+B128_PAD = Workload("b128-pad", 33, (5, 6, 9), 1, 2, 64, "bf16", 3, "lowrank", train=True, block=128)
+
+
+@pytest.mark.parametrize("w", [B128, B128_PAD], ids=lambda w: w.name)
+def test_block128_schedule(w):
+    dev = _dev()
+    q, k, v = make_qkv(w, device=dev)
+    d_o = make_grad_out(w, device=dev)
+    p = vsa2.problem(w.batch, w.heads, w.head_dim, w.grid, w.dtype, block=128)
+    layer = vsa2.Layer(p, w.topk, w.d_model, device=dev)
+    assert layer.sched is not None and layer.nb == w.nblk
+    rp, ci = make_selection(w, device=dev)
+    layer.sched.zero_()
+    layer.set_selection(rp, ci)
+    torch.cuda.synchronize()
+    (rs, rl, ri), (cs, cl, cidx) = decode(layer)
+    rpn, cin, cpn, rin = (t[0].cpu().numpy() for t in (layer.row_ptr, layer.col_idx, layer.col_ptr, layer.row_idx))
+    check_side(rs, rl, ri, rpn, cin, w.nblk)
+    check_side(cs, cl, cidx, cpn, rin, w.nblk)
+    lists = (layer.row_ptr, layer.col_idx, layer.col_ptr, layer.row_idx)
+    out = {}
+    for mode, sched in (("per-block", None), ("scheduled", layer.sched)):
+        o_f, lse = torch.empty_like(layer.o_f), torch.empty_like(layer.lse)
+        vsa2.vsa2_sparse_attn_fwd(p, w.topk, q, k, v, layer.row_ptr, layer.col_idx, o_f, lse, layer.ws, sched=sched)
+        g = [torch.full_like(q, float("nan")) for _ in range(3)]
+        vsa2.vsa2_sparse_attn_bwd(p, w.topk, q, k, v, o_f, lse, d_o, *lists, None, *g, layer.ws, sched=sched)
+        torch.cuda.synchronize()
+        out[mode] = [o_f, lse] + g
+    for name, a, b in zip(("O_f", "LSE", "dQ", "dK", "dV"), out["per-block"], out["scheduled"]):
+        assert torch.equal(a, b), f"{name}: the scheduled run differs from the per-block one"
+    real = orc.token_valid(w.grid, 128)
+    o2, _, dq2, dk2, dv2 = out["scheduled"]
+    for h in range(w.heads):
+        mask = orc.csr_to_mask(rp[0, h].cpu().numpy(), ci[0, h].cpu().numpy(), w.nblk)
+        qh, kh, vh, dh = (gu.f64(t[0, h]) for t in (q, k, v, d_o))
+        o, _ = orc.fine_forward(qh, kh, vh, mask, valid=real, block=128)
+        gu.assert_close_bf16(gu.f64(o2[0, h]), o, f"O_f head {h}")
+        for name, got, want in zip(("dQ", "dK", "dV"), (dq2, dk2, dv2),
+                                   orc.fine_backward(qh, kh, vh, mask, dh, valid=real, block=128)):
+            rr = gu.rel_l2(gu.f64(got[0, h]), want)
+            assert rr <= 2e-2, f"{name} head {h}: rel-L2 {rr:.3g}"

@@ -180,12 +180,13 @@ size_t ws_plan(const Dims& d, TopkWs* w, void* base) {
   return o_sr + up((size_t)d.bh * 9 * 4);
 }
 
-// The fine branch's work schedule (sched.hip): built for 64-token blocks
-// without text rows, where the fine kernels run one cube per work item; other
-// problems need none.  Layout: for the query cubes, then for the KV cubes, a
-// header of 16 int32 (queue starts and lengths, 256 bytes) and the items
-// [bh * nb] int32.
-bool sched_on(const Dims& d) { return d.bs == 0 && d.ntc == 0; }
+// The fine branch's work schedule (sched.hip): built for problems without
+// text rows, where the fine kernels run one attention block (a cube, or a
+// whole 128-token block) per work item; with text rows there is none.
+// Layout: for the query blocks, then for the KV blocks, a 256-byte header
+// (queue starts and lengths, item count, marker) and the items [bh * nb]
+// int32 (nb attention blocks).
+bool sched_on(const Dims& d) { return d.ntc == 0; }
 struct SchedPtrs {
   int32_t *rh, *ri, *ch, *ci;
 };

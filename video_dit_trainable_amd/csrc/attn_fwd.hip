@@ -40,10 +40,10 @@ namespace vsa2 {
 // a block (waves 0, 1 the first cube, 2, 3 the second), which share the
 // block's KV list, so every gathered K / V tile is staged once for 128 query
 // rows.
-// SCHED (64-token blocks): the grid holds as many workgroups as fit on the
-// device; each takes query cubes from the work schedule's queues (its XCD's
-// first) until they are empty, and runs each exactly as a one-cube workgroup
-// would.
+// SCHED (no text rows): the grid holds as many workgroups as fit on the
+// device; each takes query cubes (QB = 2: query blocks) from the work
+// schedule's queues (its XCD's first) until they are empty, and runs each
+// exactly as a workgroup of the one-item launch would.
 template <typename T, typename TO, int D, bool DENSE, bool PAD, int BS, bool TEXT, int QB = 1, bool SCHED = false>
 __global__ __launch_bounds__(128 * QB, 2) void k_attn_fwd(const T* __restrict__ q, const T* __restrict__ k,
                                                   const T* __restrict__ v, const int32_t* __restrict__ row_ptr,
@@ -57,7 +57,7 @@ __global__ __launch_bounds__(128 * QB, 2) void k_attn_fwd(const T* __restrict__ 
   static_assert(!(DENSE && PAD), "padding applies to the fine branch");
   static_assert(!(DENSE && TEXT), "text rows apply to the fine branch");
   static_assert(QB == 1 || (QB == 2 && BS == 1 && !TEXT && !DENSE), "whole-block workgroups for 128-token blocks");
-  static_assert(!SCHED || (QB == 1 && BS == 0 && !TEXT && !DENSE), "the schedule serves 64-token blocks");
+  static_assert(!SCHED || (((QB == 1 && BS == 0) || QB == 2) && !TEXT && !DENSE), "no schedule with text rows");
   __shared__ __align__(16) T ks[64 * D];
   __shared__ __align__(16) T vs[64 * D];
   __shared__ int s_item;  // SCHED: the item the workgroup runs next
@@ -66,12 +66,14 @@ __global__ __launch_bounds__(128 * QB, 2) void k_attn_fwd(const T* __restrict__ 
   bool textq = false;  // a text query cube
   if constexpr (SCHED) {
     __syncthreads();  // every wave is done with the previous item's tiles and s_item
-    if (threadIdx.x == 0) s_item = sched_take(sq_hdr, sq_items, sq_ctr, nbh * nq);
+    constexpr int per_item = QB;  // query cubes per item
+    const int nitem = nq / per_item;
+    if (threadIdx.x == 0) s_item = sched_take(sq_hdr, sq_items, sq_ctr, nbh * nitem);
     __syncthreads();
     const int code = s_item;
     if (code < 0) break;
-    bh = code / nq;
-    i = code - bh * nq;
+    bh = code / nitem;
+    i = code - bh * nitem;  // QB = 2: the block
   } else if (iter > 0) {
     break;
   } else if constexpr (TEXT) {
@@ -317,8 +319,20 @@ hipError_t launch_fwd_t(const AttnArgs& a, hipStream_t st) {
                        a.col_idx, (T*)a.o, a.lse, a.nq, a.nkv, a.seq, a.ld, a.out_rows, a.kph, a.scale_log2,    \
                        a.ct, a.cy, a.cx, a.pad, 0, 0, a.bh, a.sq_hdr, a.sq_items, a.sq_ctr);                  \
   }
+#define VSA2_FWD_BLOCK_SCHED(PAD)                                                                              \
+  {                                                                                                            \
+    const auto fn = k_attn_fwd<T, T, D, false, PAD, 1, false, 2, true>;                                        \
+    hipError_t e_ = launch_fill_u32((uint32_t*)a.sq_ctr, 0u, 8, st);                                           \
+    if (e_ != hipSuccess) return e_;                                                                           \
+    const dim3 pgrid(resident_grid((const void*)fn, 256, a.bh * (a.nq >> 1)));                                 \
+    hipLaunchKernelGGL(fn, pgrid, dim3(256), 0, st, (const T*)a.q, (const T*)a.k, (const T*)a.v, a.row_ptr,     \
+                       a.col_idx, (T*)a.o, a.lse, a.nq, a.nkv, a.seq, a.ld, a.out_rows, a.kph, a.scale_log2,    \
+                       a.ct, a.cy, a.cx, a.pad, 0, 0, a.bh, a.sq_hdr, a.sq_items, a.sq_ctr);                  \
+  }
     if (a.sq_hdr && !a.bs && !a.ntc) {
       if (a.pad.on) VSA2_FWD_SCHED(true) else VSA2_FWD_SCHED(false)
+    } else if (a.sq_hdr && !a.ntc) {  // whole 128-token blocks on the schedule
+      if (a.pad.on) VSA2_FWD_BLOCK_SCHED(true) else VSA2_FWD_BLOCK_SCHED(false)
     } else if (a.bs && !a.ntc) {
       if (a.pad.on) { VSA2_FWD_BLOCK(true); } else { VSA2_FWD_BLOCK(false); }
     } else if (a.bs) {  // with text rows: per-cube workgroups
@@ -327,6 +341,7 @@ hipError_t launch_fwd_t(const AttnArgs& a, hipStream_t st) {
       if (a.pad.on) { VSA2_FWD_T(true, 0); } else { VSA2_FWD_T(false, 0); }
     }
 #undef VSA2_FWD_SCHED
+#undef VSA2_FWD_BLOCK_SCHED
 #undef VSA2_FWD_BLOCK
 #undef VSA2_FWD_T
 #undef VSA2_FWD
