@@ -136,16 +136,18 @@ int vsa2_workspace_size(const vsa2_problem* p, int32_t op, int32_t topk, int32_t
  * the same results, bit for bit, as with no schedule.
  * Written by vsa2_topk_per_seq, vsa2_topk_per_row and vsa2_plan_from_csr from
  * the selection they produce or receive, read by vsa2_sparse_attn_fwd/bwd.
- * Built for problems without text rows, by attention block (a cube, or with
- * block_tokens = 128 a pair of cubes that one workgroup runs whole); with
- * text_tokens > 0 the size is 0 and the kernels run one workgroup per block.
+ * Built by attention block (a cube, or with block_tokens = 128 a pair of
+ * cubes that one workgroup runs whole).  With text_tokens > 0 and 64-token
+ * blocks every text cube is one more item (its list is every cube), and the
+ * text items of all heads open the queues; with text_tokens > 0 and
+ * block_tokens = 128 the size is 0 and the kernels run one workgroup per cube.
  * A schedule built for another selection of the same problem is still valid
- * (it lists every cube once), only balanced for that selection; a buffer that
+ * (it lists every block once), only balanced for that selection; a buffer that
  * no build for this problem wrote is recognised by its header, and the fine
- * kernels then take the cubes in plain order, with the same results.
- * Layout (opaque to callers): for query cubes, then KV cubes, a 256-byte
+ * kernels then take the blocks in plain order, with the same results.
+ * Layout (opaque to callers): for query blocks, then KV blocks, a 256-byte
  * header (queue starts and lengths, the item count, a marker) and
- * batch*heads*nb int32 items. */
+ * batch*heads*(nb + ntc) int32 items (ntc text cubes). */
 int vsa2_sched_size(const vsa2_problem* p, int32_t topk, size_t* bytes);
 
 /* Bytes of the `pooled` buffer written by vsa2_pool (see there). */

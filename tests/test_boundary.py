@@ -64,7 +64,9 @@ def test_sizes_and_budget():
     assert vsa2.workspace_size(p, vsa2.OP_FWD) == 256                     # the schedule's 8 queue counters
     assert vsa2.workspace_size(_prob(block=128, grid=(8, 16, 32)), vsa2.OP_FWD) == 256  # 128-token blocks: same
     txt = vsa2.problem(1, 2, 64, (8, 16, 16), "f32", text=100)
-    assert vsa2.workspace_size(txt, vsa2.OP_FWD) == 0                                     # text rows: no schedule
+    assert vsa2.workspace_size(txt, vsa2.OP_FWD) == 256                                   # text rows: same
+    txt128 = vsa2.problem(1, 2, 64, (8, 16, 32), "f32", text=100, block=128)
+    assert vsa2.workspace_size(txt128, vsa2.OP_FWD) == 0                 # text rows with 128-token blocks: none
     assert vsa2.workspace_size(p, vsa2.OP_COARSE_BWD, 8, 128) > 0
 
 
@@ -168,10 +170,13 @@ def test_schedule_size_and_checks():
     p = _prob(heads=2, grid=(4, 12, 20))                  # nb = 15
     up = lambda x: (x + 255) // 256 * 256
     assert vsa2.sched_size(p, 5) == 2 * (256 + up(2 * 15 * 4))
-    # 128-token blocks: one item per block (8x16x32: 64 cubes, 32 blocks); text rows need none
+    # 128-token blocks: one item per block (8x16x32: 64 cubes, 32 blocks)
     assert vsa2.sched_size(_prob(block=128, grid=(8, 16, 32)), 4) == 2 * (256 + up(2 * 32 * 4))
-    txt = vsa2.problem(1, 2, 64, (8, 16, 16), "f32", text=100)
-    assert vsa2.sched_size(txt, 4) == 0
+    # text rows (100 tokens: 2 text cubes) add one item per text cube; with
+    # 128-token blocks the kernels run per cube and there is no schedule
+    txt = vsa2.problem(1, 2, 64, (8, 16, 16), "f32", text=100)     # nb = 32
+    assert vsa2.sched_size(txt, 4) == 2 * (256 + up(2 * (32 + 2) * 4))
+    assert vsa2.sched_size(vsa2.problem(1, 2, 64, (8, 16, 32), "f32", text=100, block=128), 4) == 0
     need = vsa2.workspace_size(p, vsa2.OP_TOPK)
     ss = vsa2.sched_size(p, 5)
     # a schedule buffer that is too small or misaligned is refused before anything runs

@@ -15,7 +15,9 @@ to that XCD's queue.  Checked here:
   * that building it and running through it is bitwise reproducible;
   * odd cube counts, empty lists and padded grids;
   * that a buffer no build wrote (zeros, random bytes) and a schedule built
-    for another selection still give the per-cube results bit for bit.
+    for another selection still give the per-cube results bit for bit;
+  * MMDiT text rows: each text cube is one more item, its list every cube, and
+    queue x takes the text cubes t with t mod 8 = x of every head first.
 """
 
 import numpy as np
@@ -58,7 +60,7 @@ def decode(layer):
     """The schedule buffer as numpy: per side (query cubes, KV cubes) the
     header (queue starts [8], queue lengths [8], item count, marker) and the
     item array."""
-    n_items = layer.bh * layer.nb
+    n_items = layer.bh * (layer.nb + layer.ntc)
     raw = layer.sched.cpu().numpy()
     side = 256 + _up(n_items * 4)
     assert layer.sched.numel() >= 2 * side
@@ -79,10 +81,15 @@ def _mh2(j):
     return ((j ^ 0x5A5A) * 52429 + 777) & 0xFFFF
 
 
-def expected_queues(ptr, idx, nb):
+def expected_queues(ptr, idx, nb, ntc=0):
     """The queues, recomputed from the lists of every head (ptr [bh, nb+1],
-    idx [bh, k]) by the rules the schedule states."""
+    idx [bh, k]) by the rules the schedule states; ntc text cubes per head
+    are items nb .. nb + ntc - 1 of it."""
     queues = [[] for _ in range(8)]
+    n = nb + ntc
+    for h in range(ptr.shape[0]):
+        for t in range(ntc):
+            queues[t % 8].append(h * n + nb + t)
     for h in range(ptr.shape[0]):
         lists = [idx[h, ptr[h, c]:ptr[h, c + 1]] for c in range(nb)]
         keys = [((int(min(_mh1(l))) << 16) | int(min(_mh2(l)))) if len(l) else 0xFFFFFFFF for l in lists]
@@ -94,18 +101,18 @@ def expected_queues(ptr, idx, nb):
         for x in range(8):
             pos = [p for p in range(nb) if xcd[p] == x]
             pos.sort(key=lambda p: (-cls[p], p))
-            queues[x] += [h * nb + order[p] for p in pos]
+            queues[x] += [h * n + order[p] for p in pos]
     return queues
 
 
-def check_side(hdr_start, hdr_len, items, ptr, idx, nb):
-    want = expected_queues(ptr, idx, nb)
+def check_side(hdr_start, hdr_len, items, ptr, idx, nb, ntc=0):
+    want = expected_queues(ptr, idx, nb, ntc)
     assert list(hdr_len) == [len(q) for q in want]
     assert list(hdr_start) == list(np.concatenate([[0], np.cumsum(hdr_len)[:-1]]))
     for x in range(8):
         got = items[hdr_start[x]:hdr_start[x] + hdr_len[x]]
         assert got.tolist() == want[x], f"queue {x} differs"
-    assert sorted(items.tolist()) == list(range(ptr.shape[0] * nb)), "every cube exactly once"
+    assert sorted(items.tolist()) == list(range(ptr.shape[0] * (nb + ntc))), "every cube exactly once"
 
 
 def _layer(w, dev):
@@ -335,3 +342,48 @@ def test_block128_schedule(w):
                                    orc.fine_backward(qh, kh, vh, mask, dh, valid=real, block=128)):
             rr = gu.rel_l2(gu.f64(got[0, h]), want)
             assert rr <= 2e-2, f"{name} head {h}: rel-L2 {rr:.3g}"
+
+
+# MMDiT text rows with 64-token blocks: every text cube is one more item
+TXT_SCHED = Workload("txt-sched", 45, (8, 16, 32), 1, 3, 128, "bf16", 4, "lowrank", skew=True, train=True,
+                     text=600)                                                   # nb = 64, 10 text cubes
+TXT_SCHED_PAD = Workload("txt-sched-pad", 46, (7, 13, 15), 1, 2, 64, "f32", 6, "lowrank", train=True, text=77)
+
+
+@pytest.mark.parametrize("w", [TXT_SCHED, TXT_SCHED_PAD], ids=lambda w: w.name)
+def test_text_rows_on_the_schedule(w):
+    dev = _dev()
+    q, k, v = make_qkv(w, device=dev)
+    d_o = make_grad_out(w, device=dev)
+    p = vsa2.problem(w.batch, w.heads, w.head_dim, w.grid, w.dtype, text=w.text)
+    layer = vsa2.Layer(p, w.topk, w.d_model, device=dev)
+    ntc = -(-w.text // 64)
+    assert layer.sched is not None and layer.ntc == ntc
+    rp, ci = make_selection(w, device=dev)     # heavy-tailed rows, some empty
+    layer.sched.zero_()
+    layer.set_selection(rp, ci)
+    torch.cuda.synchronize()
+    (rs, rl, ri), (cs, cl, cidx) = decode(layer)
+    rpn, cin, cpn, rin = (t[0].cpu().numpy() for t in (layer.row_ptr, layer.col_idx, layer.col_ptr, layer.row_idx))
+    check_side(rs, rl, ri, rpn, cin, w.nb, ntc)
+    check_side(cs, cl, cidx, cpn, rin, w.nb, ntc)
+    out = {}
+    for mode, sched in (("per-cube", None), ("scheduled", layer.sched)):
+        out[mode] = _fine(p, w, layer, q, k, v, d_o, sched)
+    for name, a, b in zip(("O_f", "LSE", "dQ", "dK", "dV"), out["per-cube"], out["scheduled"]):
+        assert torch.equal(a, b), f"{name}: the scheduled run differs from the per-cube one"
+    real = orc.token_valid(w.grid)
+    o2, lse2, dq2, dk2, dv2 = out["scheduled"]
+    tol = 1e-4 if w.dtype == "f32" else 2e-2
+    for h in range(w.heads):
+        mask = orc.csr_to_mask(rp[0, h].cpu().numpy(), ci[0, h].cpu().numpy(), w.nb)
+        qh, kh, vh, dh = (gu.f64(t[0, h]) for t in (q, k, v, d_o))
+        o, _ = orc.fine_forward(qh, kh, vh, mask, valid=real, n_text=w.text)
+        if w.dtype == "f32":
+            gu.assert_close_f32(gu.f64(o2[0, h]), o, f"O_f head {h}")
+        else:
+            gu.assert_close_bf16(gu.f64(o2[0, h]), o, f"O_f head {h}")
+        for name, got, want in zip(("dQ", "dK", "dV"), (dq2, dk2, dv2),
+                                   orc.fine_backward(qh, kh, vh, mask, dh, valid=real, n_text=w.text)):
+            rr = gu.rel_l2(gu.f64(got[0, h]), want)
+            assert rr <= tol, f"{name} head {h}: rel-L2 {rr:.3g}"

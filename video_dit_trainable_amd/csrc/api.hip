@@ -180,20 +180,21 @@ size_t ws_plan(const Dims& d, TopkWs* w, void* base) {
   return o_sr + up((size_t)d.bh * 9 * 4);
 }
 
-// The fine branch's work schedule (sched.hip): built for problems without
-// text rows, where the fine kernels run one attention block (a cube, or a
-// whole 128-token block) per work item; with text rows there is none.
-// Layout: for the query blocks, then for the KV blocks, a 256-byte header
-// (queue starts and lengths, item count, marker) and the items [bh * nb]
-// int32 (nb attention blocks).
-bool sched_on(const Dims& d) { return d.ntc == 0; }
+// The fine branch's work schedule (sched.hip): the fine kernels run one
+// attention block (a cube, or a whole 128-token block) per work item, and
+// with text rows one text cube per further item (64-token blocks only: with
+// 128-token blocks and text rows the kernels run per cube, and there is no
+// schedule).  Layout: for the query blocks, then for the KV blocks, a 256-byte
+// header (queue starts and lengths, item count, marker) and the items
+// [bh * (nb + ntc)] int32 (nb attention blocks, ntc text cubes).
+bool sched_on(const Dims& d) { return d.ntc == 0 || d.bs == 0; }
 struct SchedPtrs {
   int32_t *rh, *ri, *ch, *ci;
 };
 size_t sched_layout(const Dims& d, int64_t k, const void* base, SchedPtrs* sp) {
   (void)k;
   if (!sched_on(d)) return 0;
-  const size_t side = ALIGN + up((size_t)d.bh * d.nb * 4);
+  const size_t side = ALIGN + up((size_t)d.bh * (d.nb + d.ntc) * 4);
   if (sp) {
     char* b = (char*)base;
     sp->rh = (int32_t*)b;
@@ -222,7 +223,7 @@ hipError_t build_sched(const Dims& d, int64_t k, const TopkArgs& a, void* sched,
   SchedPtrs sp;
   sched_layout(d, k, sched, &sp);
   SchedArgs s{a.row_ptr, a.col_idx, a.col_ptr, a.row_idx, sp.rh, sp.ri, sp.ch, sp.ci, a.ws.skeys, a.ws.sorder,
-              a.ws.stmp, a.ws.scnt, a.ws.shoff, a.ws.spx, a.ws.srng, d.bh, d.nb, k};
+              a.ws.stmp, a.ws.scnt, a.ws.shoff, a.ws.spx, a.ws.srng, d.bh, d.nb, k, d.ntc};
   return launch_sched(s, st);
 }
 

@@ -162,7 +162,8 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(const T* __restrict__ q, co
   static_assert(!DENSE || BS == 0, "the dense mode has one cube per block");
   static_assert(!(DENSE && TEXT), "text rows apply to the fine branch");
   static_assert(QB == 1 || (QB == 2 && BS == 1 && !TEXT && !DENSE), "whole-block workgroups for 128-token blocks");
-  static_assert(!SCHED || (((QB == 1 && BS == 0) || QB == 2) && !TEXT && !DENSE), "no schedule with text rows");
+  static_assert(!SCHED || (((QB == 1 && BS == 0) || (QB == 2 && !TEXT)) && !DENSE),
+                "the schedule serves cubes (text cubes too) or whole 128-token blocks");
   constexpr int TILE = 64 * D;
   __shared__ __align__(16) T tA[2 * TILE];  // stage A: Q tile | dO tile
   __shared__ __align__(16) T tB[2 * TILE];  // stage B
@@ -174,14 +175,15 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(const T* __restrict__ q, co
   bool textk = false;  // a text KV cube
   if constexpr (SCHED) {
     __syncthreads();  // every wave is done with the previous item's tiles and s_item
-    const int nitem = nkv / QB;  // KV cubes (QB = 2: KV blocks)
+    const int nitem = nkv / QB + (TEXT ? ntc : 0);  // KV cubes (QB = 2: KV blocks), then text cubes
     if (threadIdx.x == 0) s_item = sched_take(sk_hdr, sk_items, sk_ctr, nbh * nitem);
     __syncthreads();
     const int code = s_item;
     if (code < 0) break;
     bh = code / nitem;
-    j = code - bh * nitem;
+    j = code - bh * nitem;  // text cube t: nkv + t, as in the row numbering
     if constexpr (QB == 2) j = (j << 1) + ((int)threadIdx.x >> 7);  // this wave's KV cube
+    if constexpr (TEXT) textk = j >= nkv;
   } else if (iter > 0) {
     break;
   } else if constexpr (TEXT) {
@@ -511,7 +513,8 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(const T* __restrict__ q, cons
   static_assert(!DENSE || BS == 0, "the dense mode has one cube per block");
   static_assert(!TEXT || (STATS && !DENSE), "text rows apply to the fine branch");
   static_assert(QB == 1 || (QB == 2 && BS == 1 && !TEXT && !DENSE), "whole-block workgroups for 128-token blocks");
-  static_assert(!SCHED || (((QB == 1 && BS == 0) || QB == 2) && !TEXT && !DENSE && STATS), "no schedule with text");
+  static_assert(!SCHED || (((QB == 1 && BS == 0) || (QB == 2 && !TEXT)) && !DENSE && STATS),
+                "the schedule serves cubes (text cubes too) or whole 128-token blocks");
   constexpr int TILE = 64 * D;
   __shared__ __align__(16) T tA[2 * TILE];  // stage A: K tile | V tile
   __shared__ __align__(16) T tB[2 * TILE];  // stage B
@@ -521,14 +524,15 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(const T* __restrict__ q, cons
   bool textq = false;  // a text query cube
   if constexpr (SCHED) {
     __syncthreads();  // every wave is done with the previous item's tiles and s_item
-    const int nitem = nq / QB;  // query cubes (QB = 2: query blocks)
+    const int nitem = nq / QB + (TEXT ? ntc : 0);  // query cubes (QB = 2: query blocks), then text cubes
     if (threadIdx.x == 0) s_item = sched_take(sq_hdr, sq_items, sq_ctr, nbh * nitem);
     __syncthreads();
     const int code = s_item;
     if (code < 0) break;
     bh = code / nitem;
-    i = code - bh * nitem;
+    i = code - bh * nitem;  // text cube t: nq + t, as in the row numbering
     if constexpr (QB == 2) i = (i << 1) + ((int)threadIdx.x >> 7);  // this wave's query cube
+    if constexpr (TEXT) textq = i >= nq;
   } else if (iter > 0) {
     break;
   } else if constexpr (TEXT) {
@@ -779,26 +783,29 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(const T* __restrict__ q, cons
 // The fine backward over the work schedule: dQ over the query-cube queues
 // (it writes the row statistics), then dK/dV over the KV-cube queues; with
 // 128-token blocks (BS = 1) the items are blocks and the workgroups whole-block.
-template <typename T, int D, bool PAD, int BS>
+template <typename T, int D, bool PAD, int BS, bool TEXT = false>
 hipError_t launch_bwd_sched(const AttnBwdArgs& a, hipStream_t st) {
   constexpr int QB = BS ? 2 : 1;
+  static_assert(!(TEXT && BS), "text rows with 128-token blocks run per cube, off the schedule");
+  const int ntc = TEXT ? a.ntc : 0;
   hipError_t e = launch_fill_u32((uint32_t*)a.sq_ctr, 0u, 16, st);
   if (e != hipSuccess) return e;
-  const auto fq = k_bwd_dq<T, T, D, false, true, PAD, BS, false, QB, true>;
+  const auto fq = k_bwd_dq<T, T, D, false, true, PAD, BS, TEXT, QB, true>;
   timer_before(TK_BWD_DQ, st);
-  hipLaunchKernelGGL(fq, dim3(resident_grid((const void*)fq, 256, a.bh * (a.nq / QB))), dim3(256), 0, st,
+  hipLaunchKernelGGL(fq, dim3(resident_grid((const void*)fq, 256, a.bh * (a.nq / QB + ntc))), dim3(256), 0, st,
                      (const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.d_o, (const T*)a.o, a.lse, a.stats_out,
                      nullptr, a.row_ptr, a.col_idx, a.dq_add, (T*)a.dq, a.nq, a.nkv, a.seq, a.ld, a.out_rows, a.kph,
-                     a.scale, a.scale_log2, a.ct, a.cy, a.cx, a.pad, 0, 0, a.bh, a.sq_hdr, a.sq_items, a.sq_ctr);
+                     a.scale, a.scale_log2, a.ct, a.cy, a.cx, a.pad, ntc, a.ntext, a.bh, a.sq_hdr, a.sq_items,
+                     a.sq_ctr);
   timer_after(TK_BWD_DQ, st);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const auto fk = k_bwd_dkdv<T, T, D, false, PAD, BS, false, QB, true>;
+  const auto fk = k_bwd_dkdv<T, T, D, false, PAD, BS, TEXT, QB, true>;
   timer_before(TK_BWD_DKDV, st);
-  hipLaunchKernelGGL(fk, dim3(resident_grid((const void*)fk, 256, a.bh * (a.nkv / QB))), dim3(256), 0, st,
+  hipLaunchKernelGGL(fk, dim3(resident_grid((const void*)fk, 256, a.bh * (a.nkv / QB + ntc))), dim3(256), 0, st,
                      (const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.d_o, a.stats_out, a.col_ptr, a.row_idx,
                      a.dk_add, a.dv_add, (T*)a.dk, (T*)a.dv, a.nq, a.nkv, a.seq, a.ld, a.out_rows, a.kph, a.scale,
-                     a.scale_log2, a.pad, 0, 0, a.bh, a.sk_hdr, a.sk_items, a.sq_ctr + 8);
+                     a.scale_log2, a.pad, ntc, a.ntext, a.bh, a.sk_hdr, a.sk_items, a.sq_ctr + 8);
   timer_after(TK_BWD_DKDV, st);
   return hipGetLastError();
 }
@@ -833,8 +840,10 @@ hipError_t launch_bwd_tt(const AttnBwdArgs& a, hipStream_t st) {
 template <typename T, int D>
 hipError_t launch_bwd_t(const AttnBwdArgs& a, hipStream_t st) {
   if (a.dense) return launch_bwd_tt<T, float, D, true, false, 0, false>(a, st);
-  if (a.sq_hdr && !a.ntc) {  // the work schedule's queues
+  if (a.sq_hdr && !(a.bs && a.ntc)) {  // the work schedule's queues
     if (a.bs) return a.pad.on ? launch_bwd_sched<T, D, true, 1>(a, st) : launch_bwd_sched<T, D, false, 1>(a, st);
+    if (a.ntc)
+      return a.pad.on ? launch_bwd_sched<T, D, true, 0, true>(a, st) : launch_bwd_sched<T, D, false, 0, true>(a, st);
     return a.pad.on ? launch_bwd_sched<T, D, true, 0>(a, st) : launch_bwd_sched<T, D, false, 0>(a, st);
   }
 #define VSA2_BWD(PAD, BS)                                                                              \

@@ -57,7 +57,8 @@ __global__ __launch_bounds__(128 * QB, 2) void k_attn_fwd(const T* __restrict__ 
   static_assert(!(DENSE && PAD), "padding applies to the fine branch");
   static_assert(!(DENSE && TEXT), "text rows apply to the fine branch");
   static_assert(QB == 1 || (QB == 2 && BS == 1 && !TEXT && !DENSE), "whole-block workgroups for 128-token blocks");
-  static_assert(!SCHED || (((QB == 1 && BS == 0) || QB == 2) && !TEXT && !DENSE), "no schedule with text rows");
+  static_assert(!SCHED || (((QB == 1 && BS == 0) || (QB == 2 && !TEXT)) && !DENSE),
+                "the schedule serves cubes (text cubes too) or whole 128-token blocks");
   __shared__ __align__(16) T ks[64 * D];
   __shared__ __align__(16) T vs[64 * D];
   __shared__ int s_item;  // SCHED: the item the workgroup runs next
@@ -66,14 +67,14 @@ __global__ __launch_bounds__(128 * QB, 2) void k_attn_fwd(const T* __restrict__ 
   bool textq = false;  // a text query cube
   if constexpr (SCHED) {
     __syncthreads();  // every wave is done with the previous item's tiles and s_item
-    constexpr int per_item = QB;  // query cubes per item
-    const int nitem = nq / per_item;
+    const int nitem = nq / QB + (TEXT ? ntc : 0);  // query cubes (QB = 2: blocks), then text cubes
     if (threadIdx.x == 0) s_item = sched_take(sq_hdr, sq_items, sq_ctr, nbh * nitem);
     __syncthreads();
     const int code = s_item;
     if (code < 0) break;
     bh = code / nitem;
-    i = code - bh * nitem;  // QB = 2: the block
+    i = code - bh * nitem;  // QB = 2: the block; text cube t: nq + t, as in the row numbering
+    if constexpr (TEXT) textq = i >= nq;
   } else if (iter > 0) {
     break;
   } else if constexpr (TEXT) {
@@ -309,15 +310,15 @@ hipError_t launch_fwd_t(const AttnArgs& a, hipStream_t st) {
   hipLaunchKernelGGL((k_attn_fwd<T, T, D, false, PAD, 1, false, 2>), bgrid, dim3(256), 0, st, (const T*)a.q,    \
                      (const T*)a.k, (const T*)a.v, a.row_ptr, a.col_idx, (T*)a.o, a.lse, a.nq, a.nkv, a.seq, a.ld, \
                      a.out_rows, a.kph, a.scale_log2, a.ct, a.cy, a.cx, a.pad, 0, 0, a.bh)
-#define VSA2_FWD_SCHED(PAD)                                                                                    \
+#define VSA2_FWD_SCHED(PAD, TEXT)                                                                              \
   {                                                                                                            \
-    const auto fn = k_attn_fwd<T, T, D, false, PAD, 0, false, 1, true>;                                        \
+    const auto fn = k_attn_fwd<T, T, D, false, PAD, 0, TEXT, 1, true>;                                         \
     hipError_t e_ = launch_fill_u32((uint32_t*)a.sq_ctr, 0u, 8, st);                                           \
     if (e_ != hipSuccess) return e_;                                                                           \
-    const dim3 pgrid(resident_grid((const void*)fn, 128, a.bh * a.nq));                                        \
+    const dim3 pgrid(resident_grid((const void*)fn, 128, a.bh * (a.nq + a.ntc)));                              \
     hipLaunchKernelGGL(fn, pgrid, dim3(128), 0, st, (const T*)a.q, (const T*)a.k, (const T*)a.v, a.row_ptr,     \
                        a.col_idx, (T*)a.o, a.lse, a.nq, a.nkv, a.seq, a.ld, a.out_rows, a.kph, a.scale_log2,    \
-                       a.ct, a.cy, a.cx, a.pad, 0, 0, a.bh, a.sq_hdr, a.sq_items, a.sq_ctr);                  \
+                       a.ct, a.cy, a.cx, a.pad, a.ntc, a.ntext, a.bh, a.sq_hdr, a.sq_items, a.sq_ctr);        \
   }
 #define VSA2_FWD_BLOCK_SCHED(PAD)                                                                              \
   {                                                                                                            \
@@ -329,8 +330,12 @@ hipError_t launch_fwd_t(const AttnArgs& a, hipStream_t st) {
                        a.col_idx, (T*)a.o, a.lse, a.nq, a.nkv, a.seq, a.ld, a.out_rows, a.kph, a.scale_log2,    \
                        a.ct, a.cy, a.cx, a.pad, 0, 0, a.bh, a.sq_hdr, a.sq_items, a.sq_ctr);                  \
   }
-    if (a.sq_hdr && !a.bs && !a.ntc) {
-      if (a.pad.on) VSA2_FWD_SCHED(true) else VSA2_FWD_SCHED(false)
+    if (a.sq_hdr && !a.bs) {
+      if (a.ntc) {
+        if (a.pad.on) VSA2_FWD_SCHED(true, true) else VSA2_FWD_SCHED(false, true)
+      } else {
+        if (a.pad.on) VSA2_FWD_SCHED(true, false) else VSA2_FWD_SCHED(false, false)
+      }
     } else if (a.sq_hdr && !a.ntc) {  // whole 128-token blocks on the schedule
       if (a.pad.on) VSA2_FWD_BLOCK_SCHED(true) else VSA2_FWD_BLOCK_SCHED(false)
     } else if (a.bs && !a.ntc) {

@@ -96,6 +96,7 @@ struct SchedArgs {
   int32_t* rng;               // workspace [bh, 9]: XCD range starts
   int bh, n;
   int64_t kph;
+  int ntc;                    // text cubes: items n .. n + ntc - 1 of every (batch, head), ahead of its range
 };
 hipError_t launch_sched(const SchedArgs& a, hipStream_t st);
 

@@ -241,16 +241,23 @@ __global__ __launch_bounds__(1024) void k_sched_place_sort(const uint8_t* __rest
   for (int i = tid; i < n; i += 1024) tmp[(size_t)bh * n + i] = order[(size_t)bh * n + (int)(uint32_t)a[i]];
 }
 
-// Queue offsets: queue x holds, for every (batch, head) in turn, that head's
-// range for XCD x.  hdr[x] = start of queue x in the item array, hdr[8 + x]
-// its length, hdr[16] the item count bh * n and hdr[17] SCHED_MAGIC;
-// hoff[bh][x] = where (batch, head) bh's range starts.
+// Text cubes t of a (batch, head) with t mod 8 = x: the text items of queue x.
+__device__ __forceinline__ int sched_text_items(int ntc, int x) { return x < ntc ? (ntc - x + 7) >> 3 : 0; }
+
+// Queue offsets: queue x holds first the text cubes t with t mod 8 = x of
+// every (batch, head) (MMDiT text rows: each of their lists holds every cube,
+// tens of times a video list, so all of them start at once), then, for every
+// (batch, head) in turn, that head's range for XCD x.  hdr[x] = start of queue
+// x in the item array, hdr[8 + x] its length, hdr[16] the item count
+// bh (n + ntc) and hdr[17] SCHED_MAGIC; hoff[bh][x] = where (batch, head) bh's
+// range starts.
 __global__ __launch_bounds__(64) void k_sched_queues(const int32_t* __restrict__ cnt, int32_t* __restrict__ hdr,
-                                                     int32_t* __restrict__ hoff, int bh, int n) {
+                                                     int32_t* __restrict__ hoff, int bh, int n, int ntc) {
   __shared__ int tot[8];
   const int x = threadIdx.x;
+  const int tx = x < 8 ? sched_text_items(ntc, x) : 0;
   if (x < 8) {
-    int s = 0;
+    int s = bh * tx;
     for (int h = 0; h < bh; ++h) s += cnt[(size_t)h * 8 + x];
     tot[x] = s;
   }
@@ -261,10 +268,10 @@ __global__ __launch_bounds__(64) void k_sched_queues(const int32_t* __restrict__
     hdr[x] = head;
     hdr[8 + x] = tot[x];
     if (x == 0) {  // what the fine kernels check before trusting the queues
-      hdr[16] = bh * n;
+      hdr[16] = bh * (n + ntc);
       hdr[17] = SCHED_MAGIC;
     }
-    int o = head;
+    int o = head + bh * tx;
     for (int h = 0; h < bh; ++h) {
       hoff[(size_t)h * 8 + x] = o;
       o += cnt[(size_t)h * 8 + x];
@@ -272,11 +279,20 @@ __global__ __launch_bounds__(64) void k_sched_queues(const int32_t* __restrict__
   }
 }
 
-// Items into their queues: item code = bh * n + cube.
+// Items into their queues: item code = bh (n + ntc) + cube, text cube t being
+// item n + t; the text items of queue x sit head-major before hoff[0][x].
 __global__ __launch_bounds__(256) void k_sched_fill(const int32_t* __restrict__ tmp, const int32_t* __restrict__ cnt,
                                                     const int32_t* __restrict__ hoff, int32_t* __restrict__ items,
-                                                    int n) {
+                                                    int n, int ntc) {
   const int bh = blockIdx.y, t = blockIdx.x * 256 + threadIdx.x;
+  const int64_t base = (int64_t)bh * (n + ntc);
+  if (blockIdx.x == 0) {
+    for (int u = threadIdx.x; u < ntc; u += 256) {
+      const int x = u & 7;
+      const int tx = sched_text_items(ntc, x);
+      items[hoff[x] - (int)gridDim.y * tx + bh * tx + (u >> 3)] = (int32_t)(base + n + u);
+    }
+  }
   if (t >= n) return;
   int s = 0, x = 0;
   for (; x < 7; ++x) {
@@ -284,7 +300,7 @@ __global__ __launch_bounds__(256) void k_sched_fill(const int32_t* __restrict__ 
     if (t < s + c) break;
     s += c;
   }
-  items[hoff[(size_t)bh * 8 + x] + (t - s)] = (int32_t)((int64_t)bh * n + tmp[(size_t)bh * n + t]);
+  items[hoff[(size_t)bh * 8 + x] + (t - s)] = (int32_t)(base + tmp[(size_t)bh * n + t]);
 }
 
 // One side of the schedule from lists (ptr, idx): the CSR for the query side,
@@ -312,10 +328,11 @@ static hipError_t build_side(const int32_t* ptr, const int32_t* idx, int32_t* hd
                        a.cnt, n);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_sched_queues, dim3(1), dim3(64), 0, st, a.cnt, hdr, a.hoff, a.bh, n);
+  hipLaunchKernelGGL(k_sched_queues, dim3(1), dim3(64), 0, st, a.cnt, hdr, a.hoff, a.bh, n, a.ntc);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_sched_fill, dim3((n + 255) / 256, a.bh), dim3(256), 0, st, a.tmp, a.cnt, a.hoff, items, n);
+  hipLaunchKernelGGL(k_sched_fill, dim3((n + 255) / 256, a.bh), dim3(256), 0, st, a.tmp, a.cnt, a.hoff, items, n,
+                     a.ntc);
   return hipGetLastError();
 }
 

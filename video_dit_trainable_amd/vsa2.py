@@ -255,6 +255,7 @@ class Layer:
         self.L, self.nb, self.bh, self.block = L, nb, bh, block
         # MMDiT text rows follow the video slots of every per-token attention tensor
         self.rows = L + 64 * -(-p.text_tokens // 64)
+        self.ntc = (self.rows - L) // 64  # text cubes
         self.k = budget(p, topk)
         self.sdt = torch.bfloat16 if p.dtype == VSA2_BF16 else torch.float32
         i32 = dict(dtype=torch.int32, device=device)
