@@ -132,8 +132,9 @@ int vsa2_workspace_size(const vsa2_problem* p, int32_t op, int32_t topk, int32_t
  * the same tiles run next to each other on one XCD's L2; cuts the order into
  * 8 ranges of equal work, one per XCD; and puts each range's long lists
  * first.  The fine kernels then run as many workgroups as fit on the device,
- * each taking cubes from its XCD's queue and then from the others, and give
- * the same results, bit for bit, as with no schedule.
+ * each taking cubes from its XCD's queue and then from the others (the
+ * forward two consecutive cubes at a time, staging each KV cube of their two
+ * lists once), and give the same results, bit for bit, as with no schedule.
  * Written by vsa2_topk_per_seq, vsa2_topk_per_row and vsa2_plan_from_csr from
  * the selection they produce or receive, read by vsa2_sparse_attn_fwd/bwd.
  * Built by attention block (a cube, or with block_tokens = 128 a pair of

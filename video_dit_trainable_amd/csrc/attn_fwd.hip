@@ -19,6 +19,7 @@
 // V^T A operand is read in the same order by transposing LDS reads.  The O
 // rescale is lazy: the running max is only moved when a tile exceeds it by
 // more than 2^8, which keeps every exponential <= 256 and the result exact.
+#include <climits>
 #include <cmath>
 
 #include "common.h"
@@ -40,10 +41,16 @@ namespace vsa2 {
 // a block (waves 0, 1 the first cube, 2, 3 the second), which share the
 // block's KV list, so every gathered K / V tile is staged once for 128 query
 // rows.
-// SCHED (no text rows): the grid holds as many workgroups as fit on the
-// device; each takes query cubes (QB = 2: query blocks) from the work
-// schedule's queues (its XCD's first) until they are empty, and runs each
-// exactly as a workgroup of the one-item launch would.
+// SCHED: the grid holds as many workgroups as fit on the device; each takes
+// query cubes (QB = 2: query blocks) from the work schedule's queues (its
+// XCD's first) until they are empty, and runs each exactly as a workgroup of
+// the one-item launch would.
+// QB = 2 with BS = 0 (pairs, on the schedule, no text rows): a workgroup takes
+// two consecutive items of a queue, two query cubes of one head with lists of
+// their own (waves 0, 1 the first, 2, 3 the second).  It walks the merge of
+// the two lists, staging each KV cube in either list once; the waves of a cube
+// compute the tiles of its own list, in the list's order, so each cube's
+// result is the one-cube workgroup's bit for bit.
 template <typename T, typename TO, int D, bool DENSE, bool PAD, int BS, bool TEXT, int QB = 1, bool SCHED = false>
 __global__ __launch_bounds__(128 * QB, 2) void k_attn_fwd(const T* __restrict__ q, const T* __restrict__ k,
                                                   const T* __restrict__ v, const int32_t* __restrict__ row_ptr,
@@ -56,24 +63,50 @@ __global__ __launch_bounds__(128 * QB, 2) void k_attn_fwd(const T* __restrict__ 
                                                   int32_t* __restrict__ sq_ctr = nullptr) {
   static_assert(!(DENSE && PAD), "padding applies to the fine branch");
   static_assert(!(DENSE && TEXT), "text rows apply to the fine branch");
-  static_assert(QB == 1 || (QB == 2 && BS == 1 && !TEXT && !DENSE), "whole-block workgroups for 128-token blocks");
+  static_assert(QB == 1 || (QB == 2 && (BS == 1 || SCHED) && !TEXT && !DENSE),
+                "whole-block workgroups for 128-token blocks, pairs of cubes on the schedule");
+  constexpr bool PAIR = QB == 2 && BS == 0;  // two query cubes with lists of their own
   static_assert(!SCHED || (((QB == 1 && BS == 0) || (QB == 2 && !TEXT)) && !DENSE),
                 "the schedule serves cubes (text cubes too) or whole 128-token blocks");
-  __shared__ __align__(16) T ks[64 * D];
-  __shared__ __align__(16) T vs[64 * D];
+  constexpr int TILE = 64 * D;
+  // the K and V tiles; PAIR: two stages, ks = stage A (K | V), vs = stage B
+  __shared__ __align__(16) T ks[PAIR ? 2 * TILE : TILE];
+  __shared__ __align__(16) T vs[PAIR ? 2 * TILE : TILE];
   __shared__ int s_item;  // SCHED: the item the workgroup runs next
+  __shared__ int s_item2;  // PAIR: the second query cube's item, or -1
+  __shared__ int s_pend;   // PAIR: an item taken with one of another head, run next
+  if (PAIR && threadIdx.x == 0) s_pend = -1;
   for (int iter = 0;; ++iter) {
-  int bh, i;
+  int bh, i, i2 = -1;
   bool textq = false;  // a text query cube
   if constexpr (SCHED) {
     __syncthreads();  // every wave is done with the previous item's tiles and s_item
-    const int nitem = nq / QB + (TEXT ? ntc : 0);  // query cubes (QB = 2: blocks), then text cubes
-    if (threadIdx.x == 0) s_item = sched_take(sq_hdr, sq_items, sq_ctr, nbh * nitem);
+    // query cubes (QB = 2: blocks, PAIR: cubes), then text cubes
+    const int nitem = (PAIR ? nq : nq / QB) + (TEXT ? ntc : 0);
+    if (threadIdx.x == 0) {
+      if constexpr (PAIR) {
+        int c0 = s_pend, c1 = -1;
+        if (c0 >= 0) {
+          s_pend = -1;
+        } else {
+          c0 = sched_take2(sq_hdr, sq_items, sq_ctr, nbh * nitem, c1);
+          if (c0 >= 0 && c1 >= 0 && c1 / nitem != c0 / nitem) {  // heads differ: one at a time
+            s_pend = c1;
+            c1 = -1;
+          }
+        }
+        s_item = c0;
+        s_item2 = c1;
+      } else {
+        s_item = sched_take(sq_hdr, sq_items, sq_ctr, nbh * nitem);
+      }
+    }
     __syncthreads();
     const int code = s_item;
     if (code < 0) break;
     bh = code / nitem;
     i = code - bh * nitem;  // QB = 2: the block; text cube t: nq + t, as in the row numbering
+    if constexpr (PAIR) i2 = s_item2 < 0 ? -1 : s_item2 - bh * nitem;
     if constexpr (TEXT) textq = i >= nq;
   } else if (iter > 0) {
     break;
@@ -88,7 +121,7 @@ __global__ __launch_bounds__(128 * QB, 2) void k_attn_fwd(const T* __restrict__ 
       if (!xcd_work(blockIdx.x - tblk, nq, bh, i)) return;
       if (ct > 0) i = blocked_cube(i, ct, cy, cx);
     }
-  } else if constexpr (QB == 2) {
+  } else if constexpr (QB == 2 && !PAIR) {
     if (!xcd_work(blockIdx.x, nq >> 1, bh, i)) return;  // i: the block
     if (ct > 0) i = blocked_cube(i, ct, cy, cx >> 1);
   } else {
@@ -96,8 +129,10 @@ __global__ __launch_bounds__(128 * QB, 2) void k_attn_fwd(const T* __restrict__ 
     if (ct > 0) i = blocked_cube(i, ct, cy, cx);
   }
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, cc = lane & 15;
-  const int qcube = QB == 2 ? (i << 1) + (w >> 1) : i;  // this wave's query cube
-  const int wq = QB == 2 ? (w & 1) : w;                // and its 32-row half
+  const int wu = __builtin_amdgcn_readfirstlane(w);  // the wave index, known to be uniform
+  // this wave's query cube (PAIR: -1 for the waves of an absent second cube)
+  const int qcube = PAIR ? ((wu >> 1) ? i2 : i) : (QB == 2 ? (i << 1) + (w >> 1) : i);
+  const int wq = QB == 2 ? (w & 1) : w;  // and its 32-row half
   const size_t hoff = (size_t)bh * ld * D;
   const T* kbase = k + hoff;
   const T* vbase = v + hoff;
@@ -109,7 +144,7 @@ __global__ __launch_bounds__(128 * QB, 2) void k_attn_fwd(const T* __restrict__ 
   } else if (TEXT && textq) {
     cnt = nkv + ntc;
   } else {
-    const int blk = QB == 2 ? i : (i >> BS);
+    const int blk = QB == 2 && !PAIR ? i : (i >> BS);
     const int32_t* rp = row_ptr + (size_t)bh * ((nq >> BS) + 1);
     const int64_t start = min<int64_t>(max(rp[blk], 0), kph);
     const int64_t end = min<int64_t>(max<int64_t>(rp[blk + 1], start), kph);
@@ -117,6 +152,17 @@ __global__ __launch_bounds__(128 * QB, 2) void k_attn_fwd(const T* __restrict__ 
     cols = col_idx + (size_t)bh * kph + start;
     nsel = cnt;
     if constexpr (TEXT) cnt += ntc;
+  }
+  int cnt2 = 0;  // PAIR: the second cube's list
+  const int32_t* cols2 = col_idx;
+  if constexpr (PAIR) {
+    if (i2 >= 0) {
+      const int32_t* rp = row_ptr + (size_t)bh * (nq + 1);
+      const int64_t start = min<int64_t>(max(rp[i2], 0), kph);
+      const int64_t end = min<int64_t>(max<int64_t>(rp[i2 + 1], start), kph);
+      cnt2 = (int)(end - start);
+      cols2 = col_idx + (size_t)bh * kph + start;
+    }
   }
   // cube id of list position n; out-of-range ids (corrupt lists) become -1 = masked tile
   auto cube_at = [&](int n) -> int {
@@ -141,17 +187,155 @@ __global__ __launch_bounds__(128 * QB, 2) void k_attn_fwd(const T* __restrict__ 
   for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
     for (int s = 0; s < D / 32; ++s)
-      qf[qb][s] = frag_global<T, D>(q + hoff, qcube * 64 + 32 * wq + 16 * qb + cc, s, g);
+      qf[qb][s] = frag_global<T, D>(q + hoff, max(qcube, 0) * 64 + 32 * wq + 16 * qb + cc, s, g);
 
   f32x4 oacc[D / 16][2];
 #pragma unroll
   for (int db = 0; db < D / 16; ++db) oacc[db][0] = oacc[db][1] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};
 
-  if (cnt > 0) {
+  int vtr = 0;  // bf16: this lane's part of the transposed V reads (rows 4g + c/4 of key half 0)
+  if constexpr (sizeof(T) == 2) vtr = sw_tr_base<T, D>(0, g, cc);
+  // one staged K / V tile (kst, vst) into this wave's running softmax and O;
+  // keys at or beyond lim are masked (PAD: and keys whose bit in km is clear)
+  auto tile = [&](const T* kst, const T* vst, int lim, uint64_t km) {
+    // S^T = K Q^T: acc[kb][qb] holds keys 16kb + 4g + r of query 16qb + cc (of this wave)
+    f32x4 acc[4][2];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      const Frag<T> a = sw_frag<T, D>(kst, 16 * kb + cc, 0, g);
+      acc[kb][0] = mma0(a, qf[0][0]);
+      acc[kb][1] = mma0(a, qf[1][0]);
+    }
+#pragma unroll
+    for (int s = 1; s < D / 32; ++s)
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        const Frag<T> a = sw_frag<T, D>(kst, 16 * kb + cc, s, g);
+        mma(acc[kb][0], a, qf[0][s]);
+        mma(acc[kb][1], a, qf[1][s]);
+      }
+    if (lim < 64) {
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (16 * kb + 4 * g + r >= lim) acc[kb][0][r] = acc[kb][1][r] = -INFINITY;
+    }
+    if constexpr (PAD) {
+      if (km != ~0ull) {
+        const uint64_t mine = km >> (4 * g);
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (!((mine >> (16 * kb + r)) & 1)) acc[kb][0][r] = acc[kb][1][r] = -INFINITY;
+      }
+    }
+    // lane-local maxima; the 4-lane reduction only runs when a lane asks to
+    // move its reference maximum (lazy rescale, exponentials stay <= 2^8)
+    float mt[2];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      float x = acc[0][qb][0];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) x = fmaxf(x, acc[kb][qb][r]);
+      mt[qb] = x;
+    }
+    if (__ballot(mt[0] * c > m[0] * c + 8.f || mt[1] * c > m[1] * c + 8.f)) {
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        const float gm = group_max(mt[qb]);
+        if (gm * c > m[qb] * c + 8.f) {
+          const float alpha = fast_exp2((m[qb] - gm) * c);
+          m[qb] = gm;
+          l[qb] *= alpha;
+#pragma unroll
+          for (int db = 0; db < D / 16; ++db) oacc[db][qb] *= alpha;
+        }
+      }
+    }
+    Frag<T> pf[2][2];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      const float mc = m[qb] == -INFINITY ? 0.f : -m[qb] * c;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float p = fast_exp2(fmaf(acc[kb][qb][r], c, mc));
+          acc[kb][qb][r] = p;
+          l[qb] += p;
+        }
+      pf[qb][0] = frag_from_acc<T>(acc[0][qb], acc[1][qb]);
+      pf[qb][1] = frag_from_acc<T>(acc[2][qb], acc[3][qb]);
+    }
+    // O^T += V^T P^T
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        Frag<T> a;
+        if constexpr (sizeof(T) == 2) a = sw_frag_tr_at<T, D>(vst, vtr + 32 * h * D, 16 * db);
+        else a = sw_frag_tr<T, D>(vst, 32 * h, 16 * db, g, cc);
+        mma(oacc[db][0], a, pf[0][h]);
+        mma(oacc[db][1], a, pf[1][h]);
+      }
+  };
+  if constexpr (PAIR) {
+    // the merge of the two lists: the head of each (a corrupt entry reads as
+    // -1, a masked tile, like the one-cube kernel's), the smaller goes next,
+    // and a KV cube in both lists is staged once for both cubes
+    auto head = [&](const int32_t* cl, int p, int n) -> int {
+      if (p >= n) return INT_MAX;
+      const int jj = cl[p];
+      return (unsigned)jj < (unsigned)nkv ? jj : -1;
+    };
+    int pa = 0, pb = 0;
+    int ha = head(cols, 0, cnt), hb = head(cols2, 0, cnt2);
+    // the next KV cube of the merge and which lists hold it; false at the end
+    auto step = [&](int& jj, bool& in_a, bool& in_b) -> bool {
+      if (ha == INT_MAX && hb == INT_MAX) return false;
+      jj = min(ha, hb);
+      in_a = ha == jj;
+      in_b = hb == jj;
+      if (in_a) ha = head(cols, ++pa, cnt);
+      if (in_b) hb = head(cols2, ++pb, cnt2);
+      return true;
+    };
+    auto fetch = [&](int jj, T* st) {  // LDS-direct copy of K and V cube jj into a stage
+      dma_tile<64, D, T, 256>(kbase + (size_t)max(jj, 0) * TILE, st, tid);
+      dma_tile<64, D, T, 256>(vbase + (size_t)max(jj, 0) * TILE, st + TILE, tid);
+    };
+    auto run = [&](const T* st, int jj, bool in_a, bool in_b) {
+      if (!((wu >> 1) ? in_b : in_a)) return;  // not in this wave's list
+      uint64_t km = ~0ull;
+      if constexpr (PAD) km = jj < 0 ? 0ull : cube_slots(jj, pad);
+      tile(st, st + TILE, jj >= 0 ? 64 : 0, km);
+    };
+    // stage A takes the even steps of the merge, stage B the odd ones; the
+    // copy into one stage runs while the other is computed
+    int ja = 0, jb = 0;
+    bool aa = false, ab = false, ba = false, bb = false;
+    bool has_a = step(ja, aa, ab);
+    if (has_a) fetch(ja, ks);
+    while (has_a) {
+      wait_vm0();
+      __syncthreads();  // stage A holds its tile; every wave is done with stage B
+      const bool has_b = step(jb, ba, bb);
+      if (has_b) fetch(jb, vs);
+      run(ks, ja, aa, ab);
+      if (!has_b) break;
+      wait_vm0();
+      __syncthreads();  // stage B holds its tile; every wave is done with stage A
+      has_a = step(ja, aa, ab);
+      if (has_a) fetch(ja, ks);
+      run(vs, jb, ba, bb);
+    }
+  } else if (cnt > 0) {
     SwRegs<64, D, T, 128 * QB> kr, vr;
-    int vtr = 0;  // bf16: this lane's part of the transposed V reads (rows 4g + c/4 of key half 0)
-    if constexpr (sizeof(T) == 2) vtr = sw_tr_base<T, D>(0, g, cc);
     int j = cube_at(0);
     sw_load(kr, kbase + (size_t)max(j, 0) * 64 * D, tid);
     sw_load(vr, vbase + (size_t)max(j, 0) * 64 * D, tid);
@@ -167,90 +351,7 @@ __global__ __launch_bounds__(128 * QB, 2) void k_attn_fwd(const T* __restrict__ 
         sw_load(kr, kbase + (size_t)max(j, 0) * 64 * D, tid);
         sw_load(vr, vbase + (size_t)max(j, 0) * 64 * D, tid);
       }
-      // S^T = K Q^T: acc[kb][qb] holds keys 16kb + 4g + r of query 16qb + cc (of this wave)
-      f32x4 acc[4][2];
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        const Frag<T> a = sw_frag<T, D>(ks, 16 * kb + cc, 0, g);
-        acc[kb][0] = mma0(a, qf[0][0]);
-        acc[kb][1] = mma0(a, qf[1][0]);
-      }
-#pragma unroll
-      for (int s = 1; s < D / 32; ++s)
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-          const Frag<T> a = sw_frag<T, D>(ks, 16 * kb + cc, s, g);
-          mma(acc[kb][0], a, qf[0][s]);
-          mma(acc[kb][1], a, qf[1][s]);
-        }
-      if (lim < 64) {
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            if (16 * kb + 4 * g + r >= lim) acc[kb][0][r] = acc[kb][1][r] = -INFINITY;
-      }
-      if constexpr (PAD) {
-        if (km != ~0ull) {
-          const uint64_t mine = km >> (4 * g);
-#pragma unroll
-          for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-              if (!((mine >> (16 * kb + r)) & 1)) acc[kb][0][r] = acc[kb][1][r] = -INFINITY;
-        }
-      }
-      // lane-local maxima; the 4-lane reduction only runs when a lane asks to
-      // move its reference maximum (lazy rescale, exponentials stay <= 2^8)
-      float mt[2];
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        float x = acc[0][qb][0];
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) x = fmaxf(x, acc[kb][qb][r]);
-        mt[qb] = x;
-      }
-      if (__ballot(mt[0] * c > m[0] * c + 8.f || mt[1] * c > m[1] * c + 8.f)) {
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-          const float gm = group_max(mt[qb]);
-          if (gm * c > m[qb] * c + 8.f) {
-            const float alpha = fast_exp2((m[qb] - gm) * c);
-            m[qb] = gm;
-            l[qb] *= alpha;
-#pragma unroll
-            for (int db = 0; db < D / 16; ++db) oacc[db][qb] *= alpha;
-          }
-        }
-      }
-      Frag<T> pf[2][2];
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        const float mc = m[qb] == -INFINITY ? 0.f : -m[qb] * c;
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float p = fast_exp2(fmaf(acc[kb][qb][r], c, mc));
-            acc[kb][qb][r] = p;
-            l[qb] += p;
-          }
-        pf[qb][0] = frag_from_acc<T>(acc[0][qb], acc[1][qb]);
-        pf[qb][1] = frag_from_acc<T>(acc[2][qb], acc[3][qb]);
-      }
-      // O^T += V^T P^T
-#pragma unroll
-      for (int db = 0; db < D / 16; ++db)
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          Frag<T> a;
-          if constexpr (sizeof(T) == 2) a = sw_frag_tr_at<T, D>(vs, vtr + 32 * h * D, 16 * db);
-          else a = sw_frag_tr<T, D>(vs, 32 * h, 16 * db, g, cc);
-          mma(oacc[db][0], a, pf[0][h]);
-          mma(oacc[db][1], a, pf[1][h]);
-        }
+      tile(ks, vs, lim, km);
       __syncthreads();
     }
   }
@@ -262,6 +363,7 @@ __global__ __launch_bounds__(128 * QB, 2) void k_attn_fwd(const T* __restrict__ 
       qm = nr >= 64 ? ~0ull : (1ull << nr) - 1;
     }
   }
+  if (PAIR && qcube < 0) continue;  // the waves of an absent second cube (the next item starts at a barrier)
   if constexpr (PAD) {
     if (!textq) qm = cube_slots(qcube, pad);
   }
@@ -320,6 +422,16 @@ hipError_t launch_fwd_t(const AttnArgs& a, hipStream_t st) {
                        a.col_idx, (T*)a.o, a.lse, a.nq, a.nkv, a.seq, a.ld, a.out_rows, a.kph, a.scale_log2,    \
                        a.ct, a.cy, a.cx, a.pad, a.ntc, a.ntext, a.bh, a.sq_hdr, a.sq_items, a.sq_ctr);        \
   }
+#define VSA2_FWD_PAIR_SCHED(PAD)                                                                               \
+  {                                                                                                            \
+    const auto fn = k_attn_fwd<T, T, D, false, PAD, 0, false, 2, true>;                                        \
+    hipError_t e_ = launch_fill_u32((uint32_t*)a.sq_ctr, 0u, 8, st);                                           \
+    if (e_ != hipSuccess) return e_;                                                                           \
+    const dim3 pgrid(resident_grid((const void*)fn, 256, a.bh * ((a.nq + 1) >> 1)));                           \
+    hipLaunchKernelGGL(fn, pgrid, dim3(256), 0, st, (const T*)a.q, (const T*)a.k, (const T*)a.v, a.row_ptr,     \
+                       a.col_idx, (T*)a.o, a.lse, a.nq, a.nkv, a.seq, a.ld, a.out_rows, a.kph, a.scale_log2,    \
+                       a.ct, a.cy, a.cx, a.pad, 0, 0, a.bh, a.sq_hdr, a.sq_items, a.sq_ctr);                  \
+  }
 #define VSA2_FWD_BLOCK_SCHED(PAD)                                                                              \
   {                                                                                                            \
     const auto fn = k_attn_fwd<T, T, D, false, PAD, 1, false, 2, true>;                                        \
@@ -334,7 +446,7 @@ hipError_t launch_fwd_t(const AttnArgs& a, hipStream_t st) {
       if (a.ntc) {
         if (a.pad.on) VSA2_FWD_SCHED(true, true) else VSA2_FWD_SCHED(false, true)
       } else {
-        if (a.pad.on) VSA2_FWD_SCHED(true, false) else VSA2_FWD_SCHED(false, false)
+        if (a.pad.on) VSA2_FWD_PAIR_SCHED(true) else VSA2_FWD_PAIR_SCHED(false)
       }
     } else if (a.sq_hdr && !a.ntc) {  // whole 128-token blocks on the schedule
       if (a.pad.on) VSA2_FWD_BLOCK_SCHED(true) else VSA2_FWD_BLOCK_SCHED(false)
@@ -346,6 +458,7 @@ hipError_t launch_fwd_t(const AttnArgs& a, hipStream_t st) {
       if (a.pad.on) { VSA2_FWD_T(true, 0); } else { VSA2_FWD_T(false, 0); }
     }
 #undef VSA2_FWD_SCHED
+#undef VSA2_FWD_PAIR_SCHED
 #undef VSA2_FWD_BLOCK_SCHED
 #undef VSA2_FWD_BLOCK
 #undef VSA2_FWD_T

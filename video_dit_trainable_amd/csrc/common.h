@@ -590,6 +590,41 @@ __device__ inline int sched_take(const int32_t* __restrict__ hdr, const int32_t*
   return -1;
 }
 
+// Two consecutive items of one queue (pairs of query cubes): returns the first
+// (-1 when every queue is empty) and sets `second` to the one after it in the
+// same queue, or -1.  Each queue is taken two items at a time, so the pairs
+// are the same whichever workgroup takes them; an unbuilt schedule gives the
+// pairs (2t, 2t + 1) of the plain order.
+__device__ inline int sched_take2(const int32_t* __restrict__ hdr, const int32_t* __restrict__ items, int32_t* ctr,
+                                  int total, int& second) {
+  second = -1;
+  if (hdr[16] != total || hdr[17] != SCHED_MAGIC) {
+    const int t = atomicAdd(&ctr[0], 2);
+    if (t >= total) return -1;
+    if (t + 1 < total) second = t + 1;
+    return t;
+  }
+  const int x0 = (int)(blockIdx.x & 7u);
+  for (int s = 0; s < 8; ++s) {
+    const int x = (x0 + s) & 7;
+    const int len = hdr[8 + x];
+    if (__hip_atomic_load(&ctr[x], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= len) continue;
+    const int t = atomicAdd(&ctr[x], 2);
+    if (t < len) {
+      const int at = hdr[x] + t;
+      if ((unsigned)at >= (unsigned)total) return -1;
+      const int item = items[at];
+      if ((unsigned)item >= (unsigned)total) return -1;
+      if (t + 1 < len && (unsigned)(at + 1) < (unsigned)total) {
+        const int it2 = items[at + 1];
+        if ((unsigned)it2 < (unsigned)total) second = it2;
+      }
+      return item;
+    }
+  }
+  return -1;
+}
+
 __host__ __device__ inline int xcd_grid(int items_per_bh, int bh_total) {
   return 8 * ((items_per_bh + 7) >> 3) * bh_total;
 }
