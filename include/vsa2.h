@@ -140,7 +140,8 @@ int vsa2_workspace_size(const vsa2_problem* p, int32_t op, int32_t topk, int32_t
  * Built by attention block (a cube, or with block_tokens = 128 a pair of
  * cubes that one workgroup runs whole).  With text_tokens > 0 and 64-token
  * blocks every text cube is one more item (its list is every cube), and the
- * text items of all heads open the queues; with text_tokens > 0 and
+ * text items of all heads open the queues (text cubes 2u, 2u + 1 of a head
+ * side by side, for the forward's pairs); with text_tokens > 0 and
  * block_tokens = 128 the size is 0 and the kernels run one workgroup per cube.
  * A schedule built for another selection of the same problem is still valid
  * (it lists every block once), only balanced for that selection; a buffer that

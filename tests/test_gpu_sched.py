@@ -16,8 +16,9 @@ to that XCD's queue.  Checked here:
   * odd cube counts, empty lists and padded grids;
   * that a buffer no build wrote (zeros, random bytes) and a schedule built
     for another selection still give the per-cube results bit for bit;
-  * MMDiT text rows: each text cube is one more item, its list every cube, and
-    queue x takes the text cubes t with t mod 8 = x of every head first.
+  * MMDiT text rows: each text cube is one more item, its list every cube;
+    every queue opens with its text items, head by head, text cubes 2u and
+    2u + 1 of head h side by side in queue (h ceil(ntc / 2) + u) mod 8.
 """
 
 import numpy as np
@@ -89,7 +90,7 @@ def expected_queues(ptr, idx, nb, ntc=0):
     n = nb + ntc
     for h in range(ptr.shape[0]):
         for t in range(ntc):
-            queues[t % 8].append(h * n + nb + t)
+            queues[(h * ((ntc + 1) // 2) + t // 2) % 8].append(h * n + nb + t)
     for h in range(ptr.shape[0]):
         lists = [idx[h, ptr[h, c]:ptr[h, c + 1]] for c in range(nb)]
         keys = [((int(min(_mh1(l))) << 16) | int(min(_mh2(l)))) if len(l) else 0xFFFFFFFF for l in lists]
@@ -347,7 +348,7 @@ def test_block128_schedule(w):
 # MMDiT text rows with 64-token blocks: every text cube is one more item
 TXT_SCHED = Workload("txt-sched", 45, (8, 16, 32), 1, 3, 128, "bf16", 4, "lowrank", skew=True, train=True,
                      text=600)                                                   # nb = 64, 10 text cubes
-TXT_SCHED_PAD = Workload("txt-sched-pad", 46, (7, 13, 15), 1, 2, 64, "f32", 6, "lowrank", train=True, text=77)
+TXT_SCHED_PAD = Workload("txt-sched-pad", 46, (7, 13, 15), 1, 2, 64, "f32", 6, "lowrank", train=True, text=150)
 
 
 @pytest.mark.parametrize("w", [TXT_SCHED, TXT_SCHED_PAD], ids=lambda w: w.name)

@@ -63,15 +63,16 @@ __global__ __launch_bounds__(128 * QB, 2) void k_attn_fwd(const T* __restrict__ 
                                                   int32_t* __restrict__ sq_ctr = nullptr) {
   static_assert(!(DENSE && PAD), "padding applies to the fine branch");
   static_assert(!(DENSE && TEXT), "text rows apply to the fine branch");
-  static_assert(QB == 1 || (QB == 2 && (BS == 1 || SCHED) && !TEXT && !DENSE),
+  static_assert(QB == 1 || (QB == 2 && (BS == 1 || SCHED) && !(TEXT && BS) && !DENSE),
                 "whole-block workgroups for 128-token blocks, pairs of cubes on the schedule");
   constexpr bool PAIR = QB == 2 && BS == 0;  // two query cubes with lists of their own
-  static_assert(!SCHED || (((QB == 1 && BS == 0) || (QB == 2 && !TEXT)) && !DENSE),
+  constexpr bool STAGED = QB == 2;           // two LDS-direct stages (pairs and whole blocks)
+  static_assert(!SCHED || (((QB == 1 && BS == 0) || (QB == 2 && !(TEXT && BS))) && !DENSE),
                 "the schedule serves cubes (text cubes too) or whole 128-token blocks");
   constexpr int TILE = 64 * D;
-  // the K and V tiles; PAIR: two stages, ks = stage A (K | V), vs = stage B
-  __shared__ __align__(16) T ks[PAIR ? 2 * TILE : TILE];
-  __shared__ __align__(16) T vs[PAIR ? 2 * TILE : TILE];
+  // the K and V tiles; STAGED: two stages, ks = stage A (K | V), vs = stage B
+  __shared__ __align__(16) T ks[STAGED ? 2 * TILE : TILE];
+  __shared__ __align__(16) T vs[STAGED ? 2 * TILE : TILE];
   __shared__ int s_item;  // SCHED: the item the workgroup runs next
   __shared__ int s_item2;  // PAIR: the second query cube's item, or -1
   __shared__ int s_pend;   // PAIR: an item taken with one of another head, run next
@@ -133,6 +134,7 @@ __global__ __launch_bounds__(128 * QB, 2) void k_attn_fwd(const T* __restrict__ 
   // this wave's query cube (PAIR: -1 for the waves of an absent second cube)
   const int qcube = PAIR ? ((wu >> 1) ? i2 : i) : (QB == 2 ? (i << 1) + (w >> 1) : i);
   const int wq = QB == 2 ? (w & 1) : w;  // and its 32-row half
+  if constexpr (PAIR && TEXT) textq = qcube >= nq;  // this wave's cube is a text cube
   const size_t hoff = (size_t)bh * ld * D;
   const T* kbase = k + hoff;
   const T* vbase = v + hoff;
@@ -141,10 +143,12 @@ __global__ __launch_bounds__(128 * QB, 2) void k_attn_fwd(const T* __restrict__ 
   const int32_t* cols = nullptr;
   if constexpr (DENSE) {
     cnt = nkv;
+  } else if constexpr (PAIR) {
+    cnt = 0;  // the two lists are walked as a merge (below)
   } else if (TEXT && textq) {
     cnt = nkv + ntc;
   } else {
-    const int blk = QB == 2 && !PAIR ? i : (i >> BS);
+    const int blk = QB == 2 ? i : (i >> BS);
     const int32_t* rp = row_ptr + (size_t)bh * ((nq >> BS) + 1);
     const int64_t start = min<int64_t>(max(rp[blk], 0), kph);
     const int64_t end = min<int64_t>(max<int64_t>(rp[blk + 1], start), kph);
@@ -153,17 +157,23 @@ __global__ __launch_bounds__(128 * QB, 2) void k_attn_fwd(const T* __restrict__ 
     nsel = cnt;
     if constexpr (TEXT) cnt += ntc;
   }
-  int cnt2 = 0;  // PAIR: the second cube's list
-  const int32_t* cols2 = col_idx;
-  if constexpr (PAIR) {
-    if (i2 >= 0) {
-      const int32_t* rp = row_ptr + (size_t)bh * (nq + 1);
-      const int64_t start = min<int64_t>(max(rp[i2], 0), kph);
-      const int64_t end = min<int64_t>(max<int64_t>(rp[i2 + 1], start), kph);
-      cnt2 = (int)(end - start);
-      cols2 = col_idx + (size_t)bh * kph + start;
-    }
-  }
+  // PAIR: the lists of the two cubes x = i, i2 as sequences of KV cubes: a
+  // video cube's selected cubes, then (TEXT) the text cubes nkv ..; a text
+  // cube's list is every cube 0 .. nkv + ntc - 1; an absent cube's is empty
+  struct PList {
+    const int32_t* cl;  // the selected entries
+    int ns, tot;        // how many of them, and the whole length
+    bool all;           // every cube in order (a text query cube)
+  };
+  auto plist = [&](int x) -> PList {
+    if (x < 0) return PList{col_idx, 0, 0, false};
+    if (TEXT && x >= nq) return PList{col_idx, 0, nkv + ntc, true};
+    const int32_t* rp = row_ptr + (size_t)bh * (nq + 1);
+    const int64_t start = min<int64_t>(max(rp[x], 0), kph);
+    const int64_t end = min<int64_t>(max<int64_t>(rp[x + 1], start), kph);
+    const int ns = (int)(end - start);
+    return PList{col_idx + (size_t)bh * kph + start, ns, ns + (TEXT ? ntc : 0), false};
+  };
   // cube id of list position n; out-of-range ids (corrupt lists) become -1 = masked tile
   auto cube_at = [&](int n) -> int {
     if constexpr (DENSE) return n;
@@ -284,25 +294,41 @@ __global__ __launch_bounds__(128 * QB, 2) void k_attn_fwd(const T* __restrict__ 
         mma(oacc[db][1], a, pf[1][h]);
       }
   };
-  if constexpr (PAIR) {
-    // the merge of the two lists: the head of each (a corrupt entry reads as
-    // -1, a masked tile, like the one-cube kernel's), the smaller goes next,
-    // and a KV cube in both lists is staged once for both cubes
-    auto head = [&](const int32_t* cl, int p, int n) -> int {
-      if (p >= n) return INT_MAX;
-      const int jj = cl[p];
+  if constexpr (STAGED) {
+    // PAIR: the merge of the two lists: the head of each (a corrupt entry
+    // reads as -1, a masked tile, like the one-cube kernel's), the smaller
+    // goes next, and a KV cube in both lists is staged once for both cubes.
+    // Whole blocks: the block's list in order, every tile for all four waves.
+    auto head = [&](const PList& L, int p) -> int {
+      if (p >= L.tot) return INT_MAX;
+      if (TEXT && L.all) return p;
+      if (TEXT && p >= L.ns) return nkv + (p - L.ns);
+      const int jj = L.cl[p];
       return (unsigned)jj < (unsigned)nkv ? jj : -1;
     };
+    PList la{col_idx, 0, 0, false}, lb{col_idx, 0, 0, false};
     int pa = 0, pb = 0;
-    int ha = head(cols, 0, cnt), hb = head(cols2, 0, cnt2);
-    // the next KV cube of the merge and which lists hold it; false at the end
+    int ha = 0, hb = 0;
+    if constexpr (PAIR) {
+      la = plist(i);
+      lb = plist(i2);
+      ha = head(la, 0);
+      hb = head(lb, 0);
+    }
+    // the next KV cube and which of the two cubes take it; false at the end
     auto step = [&](int& jj, bool& in_a, bool& in_b) -> bool {
-      if (ha == INT_MAX && hb == INT_MAX) return false;
-      jj = min(ha, hb);
-      in_a = ha == jj;
-      in_b = hb == jj;
-      if (in_a) ha = head(cols, ++pa, cnt);
-      if (in_b) hb = head(cols2, ++pb, cnt2);
+      if constexpr (PAIR) {
+        if (ha == INT_MAX && hb == INT_MAX) return false;
+        jj = min(ha, hb);
+        in_a = ha == jj;
+        in_b = hb == jj;
+        if (in_a) ha = head(la, ++pa);
+        if (in_b) hb = head(lb, ++pb);
+      } else {
+        if (pa >= cnt) return false;
+        jj = cube_at(pa++);
+        in_a = in_b = true;
+      }
       return true;
     };
     auto fetch = [&](int jj, T* st) {  // LDS-direct copy of K and V cube jj into a stage
@@ -311,12 +337,12 @@ __global__ __launch_bounds__(128 * QB, 2) void k_attn_fwd(const T* __restrict__ 
     };
     auto run = [&](const T* st, int jj, bool in_a, bool in_b) {
       if (!((wu >> 1) ? in_b : in_a)) return;  // not in this wave's list
-      uint64_t km = ~0ull;
-      if constexpr (PAD) km = jj < 0 ? 0ull : cube_slots(jj, pad);
-      tile(st, st + TILE, jj >= 0 ? 64 : 0, km);
+      uint64_t km = ~0ull;  // text cubes: their tail goes by the limit
+      if constexpr (PAD) km = jj < 0 ? 0ull : ((TEXT && jj >= nkv) ? ~0ull : cube_slots(jj, pad));
+      tile(st, st + TILE, kv_limit(jj), km);
     };
-    // stage A takes the even steps of the merge, stage B the odd ones; the
-    // copy into one stage runs while the other is computed
+    // stage A takes the even steps, stage B the odd ones; the copy into one
+    // stage runs while the other is computed
     int ja = 0, jb = 0;
     bool aa = false, ab = false, ba = false, bb = false;
     bool has_a = step(ja, aa, ab);
@@ -359,7 +385,7 @@ __global__ __launch_bounds__(128 * QB, 2) void k_attn_fwd(const T* __restrict__ 
   uint64_t qm = ~0ull;  // PAD / TEXT: real rows of query cube i
   if constexpr (TEXT) {
     if (textq) {
-      const int nr = ntext - 64 * (i - nq);
+      const int nr = ntext - 64 * (qcube - nq);
       qm = nr >= 64 ? ~0ull : (1ull << nr) - 1;
     }
   }
@@ -412,25 +438,15 @@ hipError_t launch_fwd_t(const AttnArgs& a, hipStream_t st) {
   hipLaunchKernelGGL((k_attn_fwd<T, T, D, false, PAD, 1, false, 2>), bgrid, dim3(256), 0, st, (const T*)a.q,    \
                      (const T*)a.k, (const T*)a.v, a.row_ptr, a.col_idx, (T*)a.o, a.lse, a.nq, a.nkv, a.seq, a.ld, \
                      a.out_rows, a.kph, a.scale_log2, a.ct, a.cy, a.cx, a.pad, 0, 0, a.bh)
-#define VSA2_FWD_SCHED(PAD, TEXT)                                                                              \
+#define VSA2_FWD_PAIR_SCHED(PAD, TEXT)                                                                         \
   {                                                                                                            \
-    const auto fn = k_attn_fwd<T, T, D, false, PAD, 0, TEXT, 1, true>;                                         \
+    const auto fn = k_attn_fwd<T, T, D, false, PAD, 0, TEXT, 2, true>;                                         \
     hipError_t e_ = launch_fill_u32((uint32_t*)a.sq_ctr, 0u, 8, st);                                           \
     if (e_ != hipSuccess) return e_;                                                                           \
-    const dim3 pgrid(resident_grid((const void*)fn, 128, a.bh * (a.nq + a.ntc)));                              \
-    hipLaunchKernelGGL(fn, pgrid, dim3(128), 0, st, (const T*)a.q, (const T*)a.k, (const T*)a.v, a.row_ptr,     \
-                       a.col_idx, (T*)a.o, a.lse, a.nq, a.nkv, a.seq, a.ld, a.out_rows, a.kph, a.scale_log2,    \
-                       a.ct, a.cy, a.cx, a.pad, a.ntc, a.ntext, a.bh, a.sq_hdr, a.sq_items, a.sq_ctr);        \
-  }
-#define VSA2_FWD_PAIR_SCHED(PAD)                                                                               \
-  {                                                                                                            \
-    const auto fn = k_attn_fwd<T, T, D, false, PAD, 0, false, 2, true>;                                        \
-    hipError_t e_ = launch_fill_u32((uint32_t*)a.sq_ctr, 0u, 8, st);                                           \
-    if (e_ != hipSuccess) return e_;                                                                           \
-    const dim3 pgrid(resident_grid((const void*)fn, 256, a.bh * ((a.nq + 1) >> 1)));                           \
+    const dim3 pgrid(resident_grid((const void*)fn, 256, a.bh * ((a.nq + a.ntc + 1) >> 1)));                   \
     hipLaunchKernelGGL(fn, pgrid, dim3(256), 0, st, (const T*)a.q, (const T*)a.k, (const T*)a.v, a.row_ptr,     \
                        a.col_idx, (T*)a.o, a.lse, a.nq, a.nkv, a.seq, a.ld, a.out_rows, a.kph, a.scale_log2,    \
-                       a.ct, a.cy, a.cx, a.pad, 0, 0, a.bh, a.sq_hdr, a.sq_items, a.sq_ctr);                  \
+                       a.ct, a.cy, a.cx, a.pad, a.ntc, a.ntext, a.bh, a.sq_hdr, a.sq_items, a.sq_ctr);        \
   }
 #define VSA2_FWD_BLOCK_SCHED(PAD)                                                                              \
   {                                                                                                            \
@@ -444,9 +460,9 @@ hipError_t launch_fwd_t(const AttnArgs& a, hipStream_t st) {
   }
     if (a.sq_hdr && !a.bs) {
       if (a.ntc) {
-        if (a.pad.on) VSA2_FWD_SCHED(true, true) else VSA2_FWD_SCHED(false, true)
+        if (a.pad.on) VSA2_FWD_PAIR_SCHED(true, true) else VSA2_FWD_PAIR_SCHED(false, true)
       } else {
-        if (a.pad.on) VSA2_FWD_PAIR_SCHED(true) else VSA2_FWD_PAIR_SCHED(false)
+        if (a.pad.on) VSA2_FWD_PAIR_SCHED(true, false) else VSA2_FWD_PAIR_SCHED(false, false)
       }
     } else if (a.sq_hdr && !a.ntc) {  // whole 128-token blocks on the schedule
       if (a.pad.on) VSA2_FWD_BLOCK_SCHED(true) else VSA2_FWD_BLOCK_SCHED(false)
@@ -457,7 +473,6 @@ hipError_t launch_fwd_t(const AttnArgs& a, hipStream_t st) {
     } else {
       if (a.pad.on) { VSA2_FWD_T(true, 0); } else { VSA2_FWD_T(false, 0); }
     }
-#undef VSA2_FWD_SCHED
 #undef VSA2_FWD_PAIR_SCHED
 #undef VSA2_FWD_BLOCK_SCHED
 #undef VSA2_FWD_BLOCK

@@ -241,23 +241,33 @@ __global__ __launch_bounds__(1024) void k_sched_place_sort(const uint8_t* __rest
   for (int i = tid; i < n; i += 1024) tmp[(size_t)bh * n + i] = order[(size_t)bh * n + (int)(uint32_t)a[i]];
 }
 
-// Text cubes t of a (batch, head) with t mod 8 = x: the text items of queue x.
-__device__ __forceinline__ int sched_text_items(int ntc, int x) { return x < ntc ? (ntc - x + 7) >> 3 : 0; }
+// MMDiT text cubes: text cubes 2u, 2u + 1 of (batch, head) h go next to each
+// other into queue (h ceil(ntc / 2) + u) mod 8, so the forward, which takes
+// two consecutive items at a time, runs them together.
+__device__ __forceinline__ int sched_text_queue(int h, int t, int ntc) {
+  return (h * ((ntc + 1) >> 1) + (t >> 1)) & 7;
+}
+// Text items of heads 0 .. nh - 1 in queue x.
+__device__ inline int sched_text_count(int nh, int ntc, int x) {
+  int c = 0;
+  for (int h = 0; h < nh; ++h)
+    for (int t = 0; t < ntc; ++t) c += sched_text_queue(h, t, ntc) == x;
+  return c;
+}
 
-// Queue offsets: queue x holds first the text cubes t with t mod 8 = x of
-// every (batch, head) (MMDiT text rows: each of their lists holds every cube,
-// tens of times a video list, so all of them start at once), then, for every
-// (batch, head) in turn, that head's range for XCD x.  hdr[x] = start of queue
-// x in the item array, hdr[8 + x] its length, hdr[16] the item count
-// bh (n + ntc) and hdr[17] SCHED_MAGIC; hoff[bh][x] = where (batch, head) bh's
-// range starts.
+// Queue offsets: queue x holds first its text items, head by head (MMDiT text
+// rows: each of their lists holds every cube, tens of times a video list, so
+// all of them start at once), then, for every (batch, head) in turn, that
+// head's range for XCD x.  hdr[x] = start of queue x in the item array,
+// hdr[8 + x] its length, hdr[16] the item count bh (n + ntc) and hdr[17]
+// SCHED_MAGIC; hoff[bh][x] = where (batch, head) bh's range starts.
 __global__ __launch_bounds__(64) void k_sched_queues(const int32_t* __restrict__ cnt, int32_t* __restrict__ hdr,
                                                      int32_t* __restrict__ hoff, int bh, int n, int ntc) {
   __shared__ int tot[8];
   const int x = threadIdx.x;
-  const int tx = x < 8 ? sched_text_items(ntc, x) : 0;
+  const int tx = x < 8 ? sched_text_count(bh, ntc, x) : 0;
   if (x < 8) {
-    int s = bh * tx;
+    int s = tx;
     for (int h = 0; h < bh; ++h) s += cnt[(size_t)h * 8 + x];
     tot[x] = s;
   }
@@ -271,7 +281,7 @@ __global__ __launch_bounds__(64) void k_sched_queues(const int32_t* __restrict__
       hdr[16] = bh * (n + ntc);
       hdr[17] = SCHED_MAGIC;
     }
-    int o = head + bh * tx;
+    int o = head + tx;
     for (int h = 0; h < bh; ++h) {
       hoff[(size_t)h * 8 + x] = o;
       o += cnt[(size_t)h * 8 + x];
@@ -280,7 +290,8 @@ __global__ __launch_bounds__(64) void k_sched_queues(const int32_t* __restrict__
 }
 
 // Items into their queues: item code = bh (n + ntc) + cube, text cube t being
-// item n + t; the text items of queue x sit head-major before hoff[0][x].
+// item n + t; the text items of queue x sit before hoff[0][x], head by head
+// and in the order of t.
 __global__ __launch_bounds__(256) void k_sched_fill(const int32_t* __restrict__ tmp, const int32_t* __restrict__ cnt,
                                                     const int32_t* __restrict__ hoff, int32_t* __restrict__ items,
                                                     int n, int ntc) {
@@ -288,9 +299,10 @@ __global__ __launch_bounds__(256) void k_sched_fill(const int32_t* __restrict__ 
   const int64_t base = (int64_t)bh * (n + ntc);
   if (blockIdx.x == 0) {
     for (int u = threadIdx.x; u < ntc; u += 256) {
-      const int x = u & 7;
-      const int tx = sched_text_items(ntc, x);
-      items[hoff[x] - (int)gridDim.y * tx + bh * tx + (u >> 3)] = (int32_t)(base + n + u);
+      const int x = sched_text_queue(bh, u, ntc);
+      int at = hoff[x] - sched_text_count((int)gridDim.y, ntc, x) + sched_text_count(bh, ntc, x);
+      for (int v = 0; v < u; ++v) at += sched_text_queue(bh, v, ntc) == x;
+      items[at] = (int32_t)(base + n + u);
     }
   }
   if (t >= n) return;
