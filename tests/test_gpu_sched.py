@@ -388,3 +388,46 @@ def test_text_rows_on_the_schedule(w):
                                    orc.fine_backward(qh, kh, vh, mask, dh, valid=real, n_text=w.text)):
             rr = gu.rel_l2(gu.f64(got[0, h]), want)
             assert rr <= tol, f"{name} head {h}: rel-L2 {rr:.3g}"
+
+
+def test_pair_forward_takes_each_list_in_its_own_order():
+    """The forward's pairs walk the merge of two lists but give each cube its
+    own list's tiles in that list's order: with rows whose columns are out of
+    order or repeat a cube (caller errors the header lets stay memory-safe),
+    the scheduled forward still equals the one-cube forward bit for bit, and
+    with columns merely out of order it still matches the oracle."""
+    w = MID
+    dev = _dev()
+    q, k, v = make_qkv(w, device=dev)
+    p, layer = _layer(w, dev)
+    rp, ci = make_selection(w, device=dev)
+    rpn, cin = rp.cpu().numpy(), ci.cpu().numpy().copy()
+    gen = np.random.default_rng(7)
+    shuffled = cin.copy()
+    for h in range(w.heads):
+        for i in range(w.nb):
+            a, b = rpn[0, h, i], rpn[0, h, i + 1]
+            shuffled[0, h, a:b] = gen.permutation(shuffled[0, h, a:b])
+    repeated = shuffled.copy()
+    for h in range(w.heads):
+        for i in range(0, w.nb, 3):  # every third row repeats its first cube in place of its last
+            a, b = rpn[0, h, i], rpn[0, h, i + 1]
+            if b - a >= 2:
+                repeated[0, h, b - 1] = repeated[0, h, a]
+    for label, cols in (("shuffled", shuffled), ("repeated", repeated)):
+        layer.set_selection(rp, torch.tensor(cols, dtype=torch.int32, device=dev))
+        out = {}
+        for mode, sched in (("one cube", None), ("pairs", layer.sched)):
+            o_f, lse = torch.empty_like(layer.o_f), torch.empty_like(layer.lse)
+            vsa2.vsa2_sparse_attn_fwd(p, w.topk, q, k, v, layer.row_ptr, layer.col_idx, o_f, lse, layer.ws,
+                                      sched=sched)
+            torch.cuda.synchronize()
+            out[mode] = (o_f, lse)
+        assert torch.equal(out["one cube"][0], out["pairs"][0]), f"{label}: O_f differs"
+        assert torch.equal(out["one cube"][1], out["pairs"][1]), f"{label}: LSE differs"
+        if label == "shuffled":
+            real = orc.token_valid(w.grid)
+            for h in range(w.heads):
+                mask = orc.csr_to_mask(rpn[0, h], cin[0, h], w.nb)
+                o, _ = orc.fine_forward(*(gu.f64(t[0, h]) for t in (q, k, v)), mask, valid=real)
+                gu.assert_close_bf16(gu.f64(out["pairs"][0][0, h]), o, f"O_f head {h}")
