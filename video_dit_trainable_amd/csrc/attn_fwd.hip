@@ -37,20 +37,22 @@ namespace vsa2 {
 // selected cubes and then to every text cube; a text query cube attends to
 // every video and text cube.  The text query cubes take the first blocks of
 // the grid, so their long lists start first.
-// QB = 2 (128-token blocks): a 256-thread workgroup takes both query cubes of
-// a block (waves 0, 1 the first cube, 2, 3 the second), which share the
-// block's KV list, so every gathered K / V tile is staged once for 128 query
-// rows.
+// QB = 2 with BS = 1 (128-token blocks): a 256-thread workgroup takes both
+// query cubes of a block (waves 0, 1 the first cube, 2, 3 the second), which
+// share the block's KV list, so every gathered K / V tile is staged once for
+// 128 query rows.
 // SCHED: the grid holds as many workgroups as fit on the device; each takes
-// query cubes (QB = 2: query blocks) from the work schedule's queues (its
-// XCD's first) until they are empty, and runs each exactly as a workgroup of
-// the one-item launch would.
-// QB = 2 with BS = 0 (pairs, on the schedule, no text rows): a workgroup takes
+// items from the work schedule's queues (its XCD's first) until they are
+// empty, and runs each exactly as a workgroup of the one-item launch would.
+// QB = 2 with BS = 0 (PAIR, on the schedule, text rows too): a workgroup takes
 // two consecutive items of a queue, two query cubes of one head with lists of
 // their own (waves 0, 1 the first, 2, 3 the second).  It walks the merge of
 // the two lists, staging each KV cube in either list once; the waves of a cube
 // compute the tiles of its own list, in the list's order, so each cube's
 // result is the one-cube workgroup's bit for bit.
+// QB = 2 stages K / V tiles LDS-direct into two stages (the copy of the next
+// step runs while this one is computed); the one-cube kernel stages the next
+// tile through registers into a single LDS tile.
 template <typename T, typename TO, int D, bool DENSE, bool PAD, int BS, bool TEXT, int QB = 1, bool SCHED = false>
 __global__ __launch_bounds__(128 * QB, 2) void k_attn_fwd(const T* __restrict__ q, const T* __restrict__ k,
                                                   const T* __restrict__ v, const int32_t* __restrict__ row_ptr,
