@@ -126,13 +126,13 @@ size_t ws_topk(const Dims& d, TopkWs* w, void* base) {
   const size_t o_take = take((size_t)d.bh * d.nb * 4);
   const size_t o_col = take((size_t)d.bh * d.nb * 4);
   const size_t o_bm = take((size_t)d.bh * d.nb * bitmap_words(d) * 4);
-  const size_t o_sk = take((size_t)d.bh * d.nb * 4);
-  const size_t o_so = take((size_t)d.bh * d.nb * 4);
-  const size_t o_st = take((size_t)d.bh * d.nb * 4);
-  const size_t o_sc = take((size_t)d.bh * 8 * 4);
-  const size_t o_sh = take((size_t)d.bh * 8 * 4);
-  const size_t o_sp = take((size_t)d.bh * d.nb);
-  const size_t o_sr = take((size_t)d.bh * 9 * 4);
+  const size_t o_sk = take((size_t)2 * d.bh * d.nb * 4);  // the schedule's arrays: both sides
+  const size_t o_so = take((size_t)2 * d.bh * d.nb * 4);
+  const size_t o_st = take((size_t)2 * d.bh * d.nb * 4);
+  const size_t o_sc = take((size_t)2 * d.bh * 8 * 4);
+  const size_t o_sh = take((size_t)2 * d.bh * 8 * 4);
+  const size_t o_sp = take((size_t)2 * d.bh * d.nb);
+  const size_t o_sr = take((size_t)2 * d.bh * 9 * 4);
   if (w) {
     char* b = (char*)base;
     w->spx = (uint8_t*)(b + o_sp);
@@ -156,13 +156,13 @@ size_t ws_topk(const Dims& d, TopkWs* w, void* base) {
 size_t ws_plan(const Dims& d, TopkWs* w, void* base) {
   const size_t o_col = 0;
   const size_t o_bm = up((size_t)d.bh * d.nb * 4);
-  const size_t o_sk = o_bm + up((size_t)d.bh * d.nb * bitmap_words(d) * 4);
-  const size_t o_so = o_sk + up((size_t)d.bh * d.nb * 4);
-  const size_t o_st = o_so + up((size_t)d.bh * d.nb * 4);
-  const size_t o_sc = o_st + up((size_t)d.bh * d.nb * 4);
-  const size_t o_sh = o_sc + up((size_t)d.bh * 8 * 4);
-  const size_t o_sp = o_sh + up((size_t)d.bh * 8 * 4);
-  const size_t o_sr = o_sp + up((size_t)d.bh * d.nb);
+  const size_t o_sk = o_bm + up((size_t)d.bh * d.nb * bitmap_words(d) * 4);  // the schedule's: both sides
+  const size_t o_so = o_sk + up((size_t)2 * d.bh * d.nb * 4);
+  const size_t o_st = o_so + up((size_t)2 * d.bh * d.nb * 4);
+  const size_t o_sc = o_st + up((size_t)2 * d.bh * d.nb * 4);
+  const size_t o_sh = o_sc + up((size_t)2 * d.bh * 8 * 4);
+  const size_t o_sp = o_sh + up((size_t)2 * d.bh * 8 * 4);
+  const size_t o_sr = o_sp + up((size_t)2 * d.bh * d.nb);
   if (w) {
     char* b = (char*)base;
     *w = TopkWs{};
@@ -177,7 +177,7 @@ size_t ws_plan(const Dims& d, TopkWs* w, void* base) {
     w->spx = (uint8_t*)(b + o_sp);
     w->srng = (int32_t*)(b + o_sr);
   }
-  return o_sr + up((size_t)d.bh * 9 * 4);
+  return o_sr + up((size_t)2 * d.bh * 9 * 4);
 }
 
 // The fine branch's work schedule (sched.hip): the fine kernels run one

@@ -57,13 +57,14 @@ struct TopkWs {       // carved from the caller workspace
   uint32_t* colcnt;   // [bh, nb]
   uint32_t* bitmap;   // [bh, nb, words]
   int words;          // 32-bit words per bitmap row (multiple of 2)
-  uint32_t* skeys;    // [bh, nb] schedule: min-hash key of every list
-  int32_t* sorder;    // [bh, nb] schedule: cubes in key order
-  int32_t* stmp;      // [bh, nb] schedule: cubes in queue order
-  int32_t* scnt;      // [bh, 8] schedule: items per XCD
-  int32_t* shoff;     // [bh, 8] schedule: queue offsets
-  uint8_t* spx;       // [bh, nb] schedule: XCD and length class of each position
-  int32_t* srng;      // [bh, 9] schedule: XCD range starts
+  // schedule, both sides (query-cube lists, then KV-cube lists): 2 bh entries
+  uint32_t* skeys;    // [2 bh, nb] min-hash key of every list
+  int32_t* sorder;    // [2 bh, nb] cubes in key order
+  int32_t* stmp;      // [2 bh, nb] cubes in queue order
+  int32_t* scnt;      // [2 bh, 8] items per XCD
+  int32_t* shoff;     // [2 bh, 8] queue offsets
+  uint8_t* spx;       // [2 bh, nb] XCD and length class of each position
+  int32_t* srng;      // [2 bh, 9] XCD range starts
 };
 struct TopkArgs {
   const float* scores;
@@ -89,11 +90,12 @@ constexpr int SCHED_MAXN = 46340;  // cubes per (batch, head) the API admits
 struct SchedArgs {
   const int32_t *row_ptr, *col_idx, *col_ptr, *row_idx;
   int32_t *row_hdr, *row_items, *col_hdr, *col_items;
-  uint32_t* keys;             // workspace [bh, n]
-  int32_t *order, *tmp;       // workspace [bh, n]
-  int32_t *cnt, *hoff;        // workspace [bh, 8]
-  uint8_t* px;                // workspace [bh, n]: XCD << 5 | length class of each position
-  int32_t* rng;               // workspace [bh, 9]: XCD range starts
+  // workspace, for the query side's lists then the KV side's (2 bh entries)
+  uint32_t* keys;             // [2 bh, n]
+  int32_t *order, *tmp;       // [2 bh, n]
+  int32_t *cnt, *hoff;        // [2 bh, 8]
+  uint8_t* px;                // [2 bh, n]: XCD << 5 | length class of each position
+  int32_t* rng;               // [2 bh, 9]: XCD range starts
   int bh, n;
   int64_t kph;
   int ntc;                    // text cubes: items n .. n + ntc - 1 of every (batch, head), ahead of its range

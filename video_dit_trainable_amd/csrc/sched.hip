@@ -21,6 +21,9 @@
 //    min-hash order), so the short and the empty ones end each XCD's queue;
 //  * appends each (batch, head)'s range for XCD x to queue x, in (batch,
 //    head) order.
+// Both sides are built in the same launches, as 2 x (batch x head) lists of
+// lists: (batch, head) entry v < nbh is the query side of v, entry nbh + v
+// the KV side of v.
 // The kernels run as many workgroups as fit on the device at once; each takes
 // items from the queue of its XCD (workgroup b runs on XCD b mod 8) and, when
 // that queue is empty, from the others.  An item is computed the same way
@@ -40,16 +43,23 @@ __device__ __forceinline__ int list_len(const int32_t* __restrict__ ptr, int c, 
   return (int)(e - s);
 }
 
+// The lists of side entry v (see above): (ptr0, idx0) for v < nbh (the CSR),
+// (ptr1, idx1) for the others (the CSC).
+__device__ __forceinline__ const int32_t* side_ptr(const int32_t* ptr0, const int32_t* ptr1, int v, int nbh, int n) {
+  return v < nbh ? ptr0 + (size_t)v * (n + 1) : ptr1 + (size_t)(v - nbh) * (n + 1);
+}
+
 // Min-hash key of every list: (min mh1 << 16 | min mh2), 0xFFFFFFFF when the
 // list holds no valid id.  One wave per list.
-__global__ __launch_bounds__(256) void k_sched_keys(const int32_t* __restrict__ ptr, const int32_t* __restrict__ idx,
-                                                    uint32_t* __restrict__ keys, int n, int64_t kph) {
+__global__ __launch_bounds__(256) void k_sched_keys(const int32_t* __restrict__ ptr0, const int32_t* __restrict__ idx0,
+                                                    const int32_t* __restrict__ ptr1, const int32_t* __restrict__ idx1,
+                                                    uint32_t* __restrict__ keys, int n, int64_t kph, int nbh) {
   const int bh = blockIdx.y, c = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (c >= n) return;
-  const int32_t* pb = ptr + (size_t)bh * (n + 1);
+  const int32_t* pb = side_ptr(ptr0, ptr1, bh, nbh, n);
   const int64_t s = min<int64_t>(max(pb[c], 0), kph);
   const int64_t e = min<int64_t>(max<int64_t>(pb[c + 1], s), kph);
-  const int32_t* li = idx + (size_t)bh * kph;
+  const int32_t* li = bh < nbh ? idx0 + (size_t)bh * kph : idx1 + (size_t)(bh - nbh) * kph;
   uint32_t a = 0xFFFFu, b = 0xFFFFu;
   bool any = false;
   for (int64_t p = s + lane; p < e; p += 64) {
@@ -149,13 +159,13 @@ __global__ __launch_bounds__(256) void k_sched_rank(const uint32_t* __restrict__
 // the eighth of the total its work's midpoint falls in, so the ranges are
 // contiguous in the order.  px[bh][p] = XCD << 5 | length class, with class
 // floor(log2(length + 1)) + 1 <= 16; rng[bh][0..8] = range starts (rng[8] = n).
-__global__ __launch_bounds__(1024) void k_sched_cut(const int32_t* __restrict__ ptr, const int32_t* __restrict__ order,
-                                                    uint8_t* __restrict__ px, int32_t* __restrict__ rng_out, int n,
-                                                    int64_t kph) {
+__global__ __launch_bounds__(1024) void k_sched_cut(const int32_t* __restrict__ ptr0, const int32_t* __restrict__ ptr1,
+                                                    const int32_t* __restrict__ order, uint8_t* __restrict__ px,
+                                                    int32_t* __restrict__ rng_out, int n, int64_t kph, int nbh) {
   __shared__ uint32_t sh[17];
   __shared__ int rng[9];
   const int bh = blockIdx.x, tid = threadIdx.x;
-  const int32_t* pb = ptr + (size_t)bh * (n + 1);
+  const int32_t* pb = side_ptr(ptr0, ptr1, bh, nbh, n);
   const int32_t* ob = order + (size_t)bh * n;
   uint32_t total = 0;
   for (int p0 = 0; p0 < n; p0 += 1024) {
@@ -260,11 +270,16 @@ __device__ inline int sched_text_count(int nh, int ntc, int x) {
 // all of them start at once), then, for every (batch, head) in turn, that
 // head's range for XCD x.  hdr[x] = start of queue x in the item array,
 // hdr[8 + x] its length, hdr[16] the item count bh (n + ntc) and hdr[17]
-// SCHED_MAGIC; hoff[bh][x] = where (batch, head) bh's range starts.
-__global__ __launch_bounds__(64) void k_sched_queues(const int32_t* __restrict__ cnt, int32_t* __restrict__ hdr,
-                                                     int32_t* __restrict__ hoff, int bh, int n, int ntc) {
+// SCHED_MAGIC; hoff[bh][x] = where (batch, head) bh's range starts.  One
+// workgroup per side (hdr0 the query side's header, hdr1 the KV side's).
+__global__ __launch_bounds__(64) void k_sched_queues(const int32_t* __restrict__ cnt_, int32_t* __restrict__ hdr0,
+                                                     int32_t* __restrict__ hdr1, int32_t* __restrict__ hoff_, int bh,
+                                                     int n, int ntc) {
   __shared__ int tot[8];
   const int x = threadIdx.x;
+  const int32_t* cnt = cnt_ + (size_t)blockIdx.x * bh * 8;
+  int32_t* hoff = hoff_ + (size_t)blockIdx.x * bh * 8;
+  int32_t* hdr = blockIdx.x ? hdr1 : hdr0;
   const int tx = x < 8 ? sched_text_count(bh, ntc, x) : 0;
   if (x < 8) {
     int s = tx;
@@ -293,15 +308,18 @@ __global__ __launch_bounds__(64) void k_sched_queues(const int32_t* __restrict__
 // item n + t; the text items of queue x sit before hoff[0][x], head by head
 // and in the order of t.
 __global__ __launch_bounds__(256) void k_sched_fill(const int32_t* __restrict__ tmp, const int32_t* __restrict__ cnt,
-                                                    const int32_t* __restrict__ hoff, int32_t* __restrict__ items,
-                                                    int n, int ntc) {
-  const int bh = blockIdx.y, t = blockIdx.x * 256 + threadIdx.x;
-  const int64_t base = (int64_t)bh * (n + ntc);
+                                                    const int32_t* __restrict__ hoff, int32_t* __restrict__ items0,
+                                                    int32_t* __restrict__ items1, int n, int ntc, int nbh) {
+  const int bh = blockIdx.y, t = blockIdx.x * 256 + threadIdx.x;  // bh: the side entry
+  const int side = bh >= nbh ? 1 : 0, h = bh - side * nbh;        // h: the (batch, head)
+  int32_t* items = side ? items1 : items0;
+  const int64_t base = (int64_t)h * (n + ntc);
   if (blockIdx.x == 0) {
+    const int32_t* hoff0 = hoff + (size_t)side * nbh * 8;  // the side's head 0
     for (int u = threadIdx.x; u < ntc; u += 256) {
-      const int x = sched_text_queue(bh, u, ntc);
-      int at = hoff[x] - sched_text_count((int)gridDim.y, ntc, x) + sched_text_count(bh, ntc, x);
-      for (int v = 0; v < u; ++v) at += sched_text_queue(bh, v, ntc) == x;
+      const int x = sched_text_queue(h, u, ntc);
+      int at = hoff0[x] - sched_text_count(nbh, ntc, x) + sched_text_count(h, ntc, x);
+      for (int v = 0; v < u; ++v) at += sched_text_queue(h, v, ntc) == x;
       items[at] = (int32_t)(base + n + u);
     }
   }
@@ -315,44 +333,42 @@ __global__ __launch_bounds__(256) void k_sched_fill(const int32_t* __restrict__ 
   items[hoff[(size_t)bh * 8 + x] + (t - s)] = (int32_t)(base + tmp[(size_t)bh * n + t]);
 }
 
-// One side of the schedule from lists (ptr, idx): the CSR for the query side,
-// the CSC for the KV side.
-static hipError_t build_side(const int32_t* ptr, const int32_t* idx, int32_t* hdr, int32_t* items,
-                             const SchedArgs& a, hipStream_t st) {
+// The schedule from the CSR (query side) and, with a CSC, the KV side, both in
+// the same launches.
+hipError_t launch_sched(const SchedArgs& a, hipStream_t st) {
+  if (a.n > SCHED_MAXN) return hipErrorInvalidValue;
   const int n = a.n;
-  hipLaunchKernelGGL(k_sched_keys, dim3((n + 3) / 4, a.bh), dim3(256), 0, st, ptr, idx, a.keys, n, a.kph);
+  const int sides = a.col_ptr ? 2 : 1;  // no CSC (forward only): the query side alone
+  const int nv = sides * a.bh;           // side entries
+  hipLaunchKernelGGL(k_sched_keys, dim3((n + 3) / 4, nv), dim3(256), 0, st, a.row_ptr, a.col_idx, a.col_ptr,
+                     a.row_idx, a.keys, n, a.kph, a.bh);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const bool fast = n <= SCHED_FASTN;  // the in-LDS sorts; beyond, the counting kernels
   if (fast)
-    hipLaunchKernelGGL(k_sched_sort, dim3(a.bh), dim3(1024), 0, st, a.keys, a.order, n);
+    hipLaunchKernelGGL(k_sched_sort, dim3(nv), dim3(1024), 0, st, a.keys, a.order, n);
   else
-    hipLaunchKernelGGL(k_sched_rank, dim3((n + 255) / 256, a.bh), dim3(256), 0, st, a.keys, a.order, n);
+    hipLaunchKernelGGL(k_sched_rank, dim3((n + 255) / 256, nv), dim3(256), 0, st, a.keys, a.order, n);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_sched_cut, dim3(a.bh), dim3(1024), 0, st, ptr, a.order, a.px, a.rng, n, a.kph);
+  hipLaunchKernelGGL(k_sched_cut, dim3(nv), dim3(1024), 0, st, a.row_ptr, a.col_ptr, a.order, a.px, a.rng, n, a.kph,
+                     a.bh);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (fast)
-    hipLaunchKernelGGL(k_sched_place_sort, dim3(a.bh), dim3(1024), 0, st, a.px, a.rng, a.order, a.tmp, a.cnt, n);
+    hipLaunchKernelGGL(k_sched_place_sort, dim3(nv), dim3(1024), 0, st, a.px, a.rng, a.order, a.tmp, a.cnt, n);
   else
-    hipLaunchKernelGGL(k_sched_place, dim3((n + 255) / 256, a.bh), dim3(256), 0, st, a.px, a.rng, a.order, a.tmp,
+    hipLaunchKernelGGL(k_sched_place, dim3((n + 255) / 256, nv), dim3(256), 0, st, a.px, a.rng, a.order, a.tmp,
                        a.cnt, n);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_sched_queues, dim3(1), dim3(64), 0, st, a.cnt, hdr, a.hoff, a.bh, n, a.ntc);
+  hipLaunchKernelGGL(k_sched_queues, dim3(sides), dim3(64), 0, st, a.cnt, a.row_hdr, a.col_hdr, a.hoff, a.bh, n,
+                     a.ntc);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_sched_fill, dim3((n + 255) / 256, a.bh), dim3(256), 0, st, a.tmp, a.cnt, a.hoff, items, n,
-                     a.ntc);
+  hipLaunchKernelGGL(k_sched_fill, dim3((n + 255) / 256, nv), dim3(256), 0, st, a.tmp, a.cnt, a.hoff, a.row_items,
+                     a.col_items, n, a.ntc, a.bh);
   return hipGetLastError();
-}
-
-hipError_t launch_sched(const SchedArgs& a, hipStream_t st) {
-  if (a.n > SCHED_MAXN) return hipErrorInvalidValue;
-  hipError_t e = build_side(a.row_ptr, a.col_idx, a.row_hdr, a.row_items, a, st);
-  if (e != hipSuccess || !a.col_ptr) return e;  // no CSC (forward only): the query side alone
-  return build_side(a.col_ptr, a.row_idx, a.col_hdr, a.col_items, a, st);
 }
 
 }  // namespace vsa2
