@@ -110,6 +110,59 @@ def cpu_baseline(w, q, k, v, d_o, budget_s=20.0):
             "seconds": round(secs, 2), "cpu": cpu_model(), "host_cpus": os.cpu_count()}
 
 
+def dense_attention(w, q, k, v, d_o, fwd_ms, step_ms):
+    """Context for the pages' own headline (an attention speedup over a dense
+    flash attention at about 220K tokens, [VSA2] §3.4 Fig. 8): the dense
+    softmax attention over all L tokens that PyTorch-ROCm ships (torch SDPA,
+    memory-efficient backend), on the same Q, K, V and dO, timed with torch
+    events (1 warm-up, then the median of 3 forwards and of 2 forward +
+    backward calls).  Not a part of this library, and not `value`."""
+    if w.text or w.padded or w.batch != 1:
+        return {"skipped": "timed on unpadded video-only workloads of batch 1"}
+    from torch.nn.attention import SDPBackend, sdpa_kernel
+    import torch.nn.functional as F
+
+    def med(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return float(np.median(ts))
+
+    fl = 4.0 * w.L * w.L * w.head_dim * w.heads      # QK^T and PV over every pair, all heads
+    out = {"what": "torch.nn.functional.scaled_dot_product_attention over all L tokens (PyTorch-ROCm, "
+                   "memory-efficient backend), the same Q, K, V and dO; dense, no router",
+           "dense_flops_fwd": fl}
+    try:
+        with sdpa_kernel([SDPBackend.EFFICIENT_ATTENTION]):
+            fms = med(lambda: F.scaled_dot_product_attention(q, k, v), 3)
+            out["fwd_ms"] = round(fms, 2)
+            out["fwd_tflops"] = round(fl / (fms * 1e-3) / 1e12, 1)
+            out["vsa2_fwd_ms"] = round(fwd_ms, 3)
+            out["speedup_fwd"] = round(fms / fwd_ms, 2)
+            if w.train:
+                qg, kg, vg = (t.detach().clone().requires_grad_(True) for t in (q, k, v))
+
+                def fb():
+                    F.scaled_dot_product_attention(qg, kg, vg).backward(d_o)
+                bms = med(fb, 2)
+                del qg, kg, vg
+                out["fwd_bwd_ms"] = round(bms, 2)
+                out["fwd_bwd_tflops"] = round(3.5 * fl / (bms * 1e-3) / 1e12, 1)
+                out["speedup_step"] = round(bms / step_ms, 2)
+    except Exception as e:          # a backend this PyTorch build lacks: no context figure
+        out["skipped"] = f"{type(e).__name__}: {str(e)[:200]}"
+    torch.cuda.empty_cache()
+    log(f"dense attention (torch SDPA): {out}")
+    return out
+
+
 def cpu_model():
     try:
         with open("/proc/cpuinfo") as f:
@@ -215,6 +268,8 @@ def main():
     ap.add_argument("--workload", default="train720")
     ap.add_argument("--topk", type=int, default=None, help="override the workload's average KV blocks per query block")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-dense", action="store_true",
+                    help="skip the dense-attention context figure (torch SDPA over all tokens)")
     ap.add_argument("--no-sched", action="store_true",
                     help="run the fine branch one workgroup per cube instead of on the work schedule's pairs")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -387,6 +442,10 @@ def main():
     if args.copy_calibration:
         copy_calibration(dev)
     peaks = measured_peaks(dev)
+    dense = None
+    if not args.no_dense:
+        fwd_ms = sum(per[n] for n in ("pool", "route", "topk", "fine_fwd", "coarse_gate"))
+        dense = dense_attention(w, q, k, v, d_o, fwd_ms, ms_step)
 
     cpu = None
     if not args.no_cpu:
@@ -417,6 +476,7 @@ def main():
         "kernels": kernels,
         "roofline": roof,
         "measured_peaks": peaks,
+        "dense_attention": dense,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

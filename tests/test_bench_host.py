@@ -92,3 +92,11 @@ def test_every_workload_is_described_with_its_grid(name):
     t, y, x = w.grid
     assert f"{t}x{y}x{x}" in text
     assert f"d={w.head_dim}" in text
+
+
+def test_dense_context_figure_only_on_plain_video_workloads():
+    # the dense-attention context runs over all L tokens of Q, K, V; text rows
+    # and pad slots are not tokens of that attention, so those workloads skip
+    for name in ("train720text", "train720pad"):
+        out = bench.dense_attention(WORKLOADS[name], None, None, None, None, 1.0, 1.0)
+        assert set(out) == {"skipped"}
