@@ -85,6 +85,16 @@ def test_topk_bytes_count_every_pass():
     assert five < op_bytes(w)["topk"] < 1.05 * five
 
 
+def test_forward_only_topk_bytes_leave_out_the_csc():
+    # forward-only workloads call TopK with no CSC: no selection bitmap and
+    # no column lists, only the five score passes and the CSR
+    w = WORKLOADS["infer720"]
+    five = 20 * 5 * 3432 * 3432 * 4
+    csr = 20 * (219648 * 4 + 3433 * 4)
+    assert op_bytes(w)["topk"] == five + csr
+    assert op_bytes(w)["topk"] < op_bytes(WORKLOADS["train720"])["topk"]
+
+
 @pytest.mark.parametrize("name", sorted(WORKLOADS))
 def test_every_workload_is_described_with_its_grid(name):
     w = WORKLOADS[name]

@@ -239,8 +239,10 @@ def op_bytes(w: Workload, topk=None):
     passes, the per-row count and the compaction), writes the CSR and the
     selection bitmap, then reads the bitmap twice and writes the CSC (the
     per-row TopK of the VSA router baseline also reads every score five times:
-    four 8-bit radix passes per row and the compaction).  pool: Q, K, V read
-    once, the router and coarse operands written.
+    four 8-bit radix passes per row and the compaction).  A forward-only
+    workload calls TopK without the CSC, which then builds no bitmap and no
+    CSC: the five score passes and the CSR only.  pool: Q, K, V read once,
+    the router and coarse operands written.
     """
     k = w.budget(topk)
     bh = w.batch * w.heads
@@ -248,8 +250,9 @@ def op_bytes(w: Workload, topk=None):
     esz = 2 if w.dtype == "bf16" else 4
     nb = w.nblk
     scores = nb * nb * 4
-    bitmap = nb * 2 * ((nb + 63) // 64) * 4
-    lists = 2 * (k * 4 + (nb + 1) * 4)
+    csc = w.train  # the CSC side (bitmap, column lists) feeds only the backward
+    bitmap = nb * 2 * ((nb + 63) // 64) * 4 if csc else 0
+    lists = (2 if csc else 1) * (k * 4 + (nb + 1) * 4)
     passes = 5
     g = gather_bytes(w, topk)
     nbp = -(-nb // 64) * 64
