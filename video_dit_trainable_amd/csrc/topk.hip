@@ -196,6 +196,64 @@ __global__ __launch_bounds__(256) void k_compact(const float* __restrict__ score
   uint32_t eq_seen = 0, written = 0;
   const uint64_t lt = lanemask_lt(lane);
   const int64_t row0 = row_ptr[(size_t)bh * (nb + 1) + row];
+  if ((nb & 3) == 0) {
+    // 16-byte rows: lane l reads columns 4l .. 4l + 3 of each 256-column
+    // step in one load (the next step's load is issued before this one is
+    // ranked).  Ranks in column order: the entries of lower lanes, then the
+    // lane's own lower columns.
+    float4 cur = make_float4(0.f, 0.f, 0.f, 0.f), nxt = cur;
+    if (4 * lane < nb) cur = *reinterpret_cast<const float4*>(s + 4 * lane);
+    for (int j1 = 0; j1 < nb; j1 += 256) {
+      const int j = j1 + 4 * lane;
+      if (j + 256 < nb) nxt = *reinterpret_cast<const float4*>(s + j + 256);
+      const bool in = j < nb;  // nb % 4 == 0: all four columns or none
+      const uint32_t u[4] = {score_bits(cur.x), score_bits(cur.y), score_bits(cur.z), score_bits(cur.w)};
+      bool is_eq[4], sel[4];
+      uint64_t eqm[4], selm[4];
+      uint32_t eq_lower = 0;  // equal entries of the lower lanes of this step
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        is_eq[e] = in && u[e] == tau;
+        eqm[e] = __ballot(is_eq[e]);
+        eq_lower += __popcll(eqm[e] & lt);
+      }
+      uint32_t rank = eq_seen + eq_lower, sel_lower = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        sel[e] = in && (u[e] > tau || (is_eq[e] && rank < tk));
+        rank += is_eq[e];
+        selm[e] = __ballot(sel[e]);
+        sel_lower += __popcll(selm[e] & lt);
+      }
+      uint32_t pos = written + sel_lower;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (sel[e] && row0 + pos < kph) out[pos] = j + e;
+        pos += sel[e];
+      }
+      // bitmap word k of the step (columns j1 + 32k ..) holds lanes 8k .. 8k + 7,
+      // four columns each: bit 4i + e is element e of lane 8k + i
+      if (csc && lane < 8 && j1 + 64 * (lane >> 1) < nb) {
+        uint32_t word = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          uint32_t x = (uint32_t)(selm[e] >> (8 * lane)) & 0xFFu;  // spread bit i to bit 4i
+          x = (x | (x << 12)) & 0x000F000Fu;
+          x = (x | (x << 6)) & 0x03030303u;
+          x = (x | (x << 3)) & 0x11111111u;
+          word |= x << e;
+        }
+        bm[(j1 >> 5) + lane] = word;
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        eq_seen += __popcll(eqm[e]);
+        written += __popcll(selm[e]);
+      }
+      cur = nxt;
+    }
+    return;
+  }
   // four 64-column chunks per step, compacted in column order; the next
   // step's four are loaded while this step's are ranked
   uint32_t uu[4], un[4];
