@@ -154,8 +154,11 @@ def _topk_on(scores_np, topk, grid_nb):
     return rp[0], ci[0], cp[0], ri[0], k
 
 
+# nb % 4 == 0 rows are compacted 256 columns per step (one float4 per lane),
+# others 64 at a time; 520 and 1028 carry tie ranks and list offsets across
+# several steps, the last one ragged
 @pytest.mark.parametrize("nb,topk,levels", [(32, 8, 5), (64, 3, 3), (10, 4, 2), (200, 17, 7), (15, 15, 4),
-                                           (33, 40, 3), (130, 1, 1000)])
+                                           (33, 40, 3), (130, 1, 1000), (520, 9, 6), (1028, 5, 11)])
 def test_topk_exact_with_ties(nb, topk, levels):
     rng = np.random.default_rng(nb * 1000 + topk)
     H = 3
